@@ -1,0 +1,6 @@
+"""MI355X byte-level BPE encode/decode behind a C ABI (libbpe.so).
+
+Python side: ``Model`` marshals torch device tensors into the C calls.
+"""
+from .api import BPEError, Model  # noqa: F401
+from . import _lib  # noqa: F401

@@ -1,0 +1,163 @@
+"""Python binding over libbpe's C ABI (argument marshalling only).
+
+PyTorch supplies device memory and the current HIP stream; every step of
+encode and decode runs in the library's HIP kernels.  There is no CPU path:
+without libbpe.so or a GPU, these calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _lib
+
+
+class BPEError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        msg = _lib.load().bpe_strerror(code).decode()
+        super().__init__(f"{what}: {msg} ({code})")
+        self.code = code
+
+
+def _stream_handle(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+class Model:
+    """A merge table resident on the current GPU (bpe_load_merges)."""
+
+    def __init__(self, merges, id_map=None, stream=None):
+        if not torch.cuda.is_available():
+            raise RuntimeError("libbpe needs a HIP device; none is visible")
+        L = _lib.load()
+        m = np.ascontiguousarray(np.asarray(merges, dtype=np.int32).reshape(-1, 2))
+        im = None if id_map is None else np.ascontiguousarray(np.asarray(id_map, dtype=np.int32))
+        if im is not None and im.size != 256 + m.shape[0]:
+            raise ValueError("id_map must have 256 + n_merges entries")
+        h = C.c_void_p()
+        rc = L.bpe_load_merges(m.ctypes.data_as(C.c_void_p) if m.size else None, m.shape[0],
+                               im.ctypes.data_as(C.c_void_p) if im is not None else None,
+                               C.c_void_p(_stream_handle(stream)), C.byref(h))
+        if rc != _lib.BPE_OK:
+            raise BPEError(rc, "bpe_load_merges")
+        self._h = h
+        self.n_merges = int(m.shape[0])
+        self.device = torch.device("cuda", torch.cuda.current_device())
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.load().bpe_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def vocab_size(self) -> int:
+        return int(_lib.load().bpe_vocab_size(self._h))
+
+    @property
+    def max_token_bytes(self) -> int:
+        return int(_lib.load().bpe_max_token_bytes(self._h))
+
+    # ---- encode -------------------------------------------------------------
+    def encode_workspace_bytes(self, n_bytes: int, n_docs: int) -> int:
+        return int(_lib.load().bpe_encode_workspace_bytes(self._h, n_bytes, n_docs))
+
+    def encode_batch_into(self, data: torch.Tensor, doc_off: torch.Tensor, ids: torch.Tensor,
+                          id_off: torch.Tensor, workspace: torch.Tensor | None,
+                          status: torch.Tensor, stream=None) -> None:
+        """bpe_encode_batch on caller-owned device buffers (no allocation, no
+        synchronization)."""
+        n_bytes = int(data.numel())
+        n_docs = int(doc_off.numel()) - 1
+        if data.dtype != torch.uint8 or doc_off.dtype != torch.int64 or ids.dtype != torch.int32 \
+                or id_off.dtype != torch.int64 or status.dtype != torch.int32:
+            raise TypeError("dtypes: data uint8, doc_off int64, ids int32, id_off int64, status int32")
+        if n_docs < 0 or id_off.numel() != n_docs + 1:
+            raise ValueError("doc_off and id_off need n_docs + 1 entries")
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = _lib.load().bpe_encode_batch(
+            self._h, _dptr(data) if n_bytes else None, n_bytes, _dptr(doc_off), n_docs,
+            _dptr(ids) if ids.numel() else None, int(ids.numel()), _dptr(id_off),
+            _dptr(workspace) if ws_bytes else None, ws_bytes, _dptr(status),
+            C.c_void_p(_stream_handle(stream)))
+        if rc != _lib.BPE_OK:
+            raise BPEError(rc, "bpe_encode_batch")
+
+    def encode_batch(self, data: torch.Tensor, doc_off: torch.Tensor, ids_capacity: int | None = None,
+                     stream=None):
+        """Allocate outputs, encode, synchronize, and return (ids[:T], id_off)."""
+        dev = data.device
+        n_bytes = int(data.numel())
+        n_docs = int(doc_off.numel()) - 1
+        cap = n_bytes if ids_capacity is None else ids_capacity
+        ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)[:cap]
+        id_off = torch.empty(n_docs + 1, dtype=torch.int64, device=dev)
+        ws = torch.empty(max(1, self.encode_workspace_bytes(n_bytes, n_docs)), dtype=torch.uint8,
+                         device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.encode_batch_into(data, doc_off, ids, id_off, ws, status, stream)
+        st = int(status.item())
+        if st:
+            raise RuntimeError(f"bpe_encode_batch device status {st:#x}")
+        T = int(id_off[-1].item())
+        return ids[:T], id_off
+
+    # ---- decode -------------------------------------------------------------
+    def decode_workspace_bytes(self, n_ids: int, n_docs: int) -> int:
+        return int(_lib.load().bpe_decode_workspace_bytes(self._h, n_ids, n_docs))
+
+    def decode_batch_into(self, ids: torch.Tensor, id_off: torch.Tensor, out: torch.Tensor,
+                          byte_off: torch.Tensor, workspace: torch.Tensor | None,
+                          status: torch.Tensor, stream=None) -> None:
+        n_ids = int(ids.numel())
+        n_docs = int(id_off.numel()) - 1
+        if ids.dtype != torch.int32 or id_off.dtype != torch.int64 or out.dtype != torch.uint8 \
+                or byte_off.dtype != torch.int64 or status.dtype != torch.int32:
+            raise TypeError("dtypes: ids int32, id_off int64, out uint8, byte_off int64, status int32")
+        if n_docs < 0 or byte_off.numel() != n_docs + 1:
+            raise ValueError("id_off and byte_off need n_docs + 1 entries")
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = _lib.load().bpe_decode_batch(
+            self._h, _dptr(ids) if n_ids else None, n_ids, _dptr(id_off), n_docs,
+            _dptr(out) if out.numel() else None, int(out.numel()), _dptr(byte_off),
+            _dptr(workspace) if ws_bytes else None, ws_bytes, _dptr(status),
+            C.c_void_p(_stream_handle(stream)))
+        if rc != _lib.BPE_OK:
+            raise BPEError(rc, "bpe_decode_batch")
+
+    def decode_batch(self, ids: torch.Tensor, id_off: torch.Tensor, bytes_capacity: int | None = None,
+                     stream=None):
+        """Allocate outputs, decode, synchronize, and return (bytes[:N], byte_off)."""
+        dev = ids.device
+        n_ids = int(ids.numel())
+        n_docs = int(id_off.numel()) - 1
+        cap = n_ids * max(1, self.max_token_bytes) if bytes_capacity is None else bytes_capacity
+        out = torch.empty(max(cap, 1), dtype=torch.uint8, device=dev)[:cap]
+        byte_off = torch.empty(n_docs + 1, dtype=torch.int64, device=dev)
+        ws = torch.empty(max(1, self.decode_workspace_bytes(n_ids, n_docs)), dtype=torch.uint8,
+                         device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.decode_batch_into(ids, id_off, out, byte_off, ws, status, stream)
+        st = int(status.item())
+        if st:
+            raise RuntimeError(f"bpe_decode_batch device status {st:#x}")
+        N = int(byte_off[-1].item())
+        return out[:N], byte_off

@@ -1,0 +1,322 @@
+// bpe_api.cpp -- host side of libbpe: model building, checks, launches.
+//
+// The model is the merge table of "Tokenization LLM: ... C++"
+// (glitch4techs.com), sections "BPE algorithm" and "Vocabulary lookup",
+// uploaded once to the device as "Hugging Face Tokenizers v1" (dothoosh.com)
+// section "Road to 1.0.0" proposes for GPU batch encoding.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/bpe.h"
+#include "bpe_internal.h"
+
+using namespace bpe;
+
+struct bpe_model {
+  int64_t R = 0, V = 0;
+  int device = 0;
+  uint64_t *d_table = nullptr;
+  int table_bits = 0;
+  int32_t *d_id_map = nullptr;
+  // decode tables
+  bool decode_ok = false;
+  int64_t max_token = 1;
+  int64_t *d_exp_off = nullptr;
+  uint8_t *d_exp_bytes = nullptr;
+  int32_t *d_inv_map = nullptr;
+  int64_t inv_size = 0;
+};
+
+namespace {
+
+void free_model(bpe_model *m) {
+  if (!m) return;
+  if (m->d_table) (void)hipFree(m->d_table);
+  if (m->d_id_map) (void)hipFree(m->d_id_map);
+  if (m->d_exp_off) (void)hipFree(m->d_exp_off);
+  if (m->d_exp_bytes) (void)hipFree(m->d_exp_bytes);
+  if (m->d_inv_map) (void)hipFree(m->d_inv_map);
+  delete m;
+}
+
+template <typename T>
+int upload(T **dst, const T *src, size_t count, hipStream_t stream) {
+  if (count == 0) count = 1;
+  if (hipMalloc((void **)dst, count * sizeof(T)) != hipSuccess) {
+    *dst = nullptr;
+    return BPE_ENOMEM;
+  }
+  if (src && hipMemcpyAsync(*dst, src, count * sizeof(T), hipMemcpyHostToDevice, stream) !=
+                 hipSuccess)
+    return BPE_EHIP;
+  return BPE_OK;
+}
+
+bool on_model_device(const bpe_model *m) {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev == m->device;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_map,
+                    void *hip_stream, bpe_model **out) {
+  if (!out || n_merges < 0 || n_merges > BPE_MAX_MERGES || (n_merges > 0 && !merges))
+    return BPE_EINVAL;
+  const int64_t R = n_merges, V = 256 + n_merges;
+  hipStream_t stream = (hipStream_t)hip_stream;
+
+  // operands in range, pairs distinct
+  std::vector<uint64_t> keys((size_t)R);
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t l = merges[2 * r], rt = merges[2 * r + 1];
+    if (l < 0 || l >= V || rt < 0 || rt >= V) return BPE_EMERGES;
+    keys[(size_t)r] = pair_key((uint32_t)l, (uint32_t)rt);
+  }
+  {
+    std::vector<uint64_t> sorted(keys);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return BPE_EMERGES;
+  }
+
+  // Operands before the symbols built from them (Kahn's order); symbols left
+  // unordered lie on a cycle.  Byte lengths follow in the same order.
+  std::vector<int64_t> len((size_t)V, 1);
+  std::vector<int64_t> order;
+  order.reserve((size_t)R);
+  {
+    std::vector<int32_t> indeg((size_t)R, 0);
+    std::vector<int64_t> ustart((size_t)V + 1, 0);
+    for (int64_t r = 0; r < R; ++r)
+      for (int k = 0; k < 2; ++k) {
+        const int32_t u = merges[2 * r + k];
+        if (u >= 256) {
+          ++indeg[(size_t)r];
+          ++ustart[(size_t)u + 1];
+        }
+      }
+    for (int64_t v = 0; v < V; ++v) ustart[(size_t)v + 1] += ustart[(size_t)v];
+    std::vector<int32_t> users((size_t)ustart[(size_t)V]);
+    std::vector<int64_t> fill(ustart.begin(), ustart.end() - 1);
+    for (int64_t r = 0; r < R; ++r)
+      for (int k = 0; k < 2; ++k) {
+        const int32_t u = merges[2 * r + k];
+        if (u >= 256) users[(size_t)fill[(size_t)u]++] = (int32_t)(256 + r);
+      }
+    std::vector<int64_t> queue;
+    queue.reserve((size_t)R);
+    for (int64_t r = 0; r < R; ++r)
+      if (indeg[(size_t)r] == 0) queue.push_back(256 + r);
+    const int64_t cap = (int64_t)1 << 62;
+    for (size_t qi = 0; qi < queue.size(); ++qi) {
+      const int64_t v = queue[qi];
+      const int64_t r = v - 256;
+      len[(size_t)v] = std::min(cap, len[(size_t)merges[2 * r]] + len[(size_t)merges[2 * r + 1]]);
+      order.push_back(v);
+      for (int64_t k = ustart[(size_t)v]; k < ustart[(size_t)v + 1]; ++k) {
+        const int32_t w = users[(size_t)k];
+        if (--indeg[(size_t)(w - 256)] == 0) queue.push_back(w);
+      }
+    }
+    if ((int64_t)order.size() != R) return BPE_EMERGES;
+  }
+
+  // id_map: distinct values in [0, BPE_MAX_ID]
+  int64_t max_id = V - 1;
+  if (id_map) {
+    std::vector<uint8_t> seen((size_t)BPE_MAX_ID + 1, 0);
+    max_id = 0;
+    for (int64_t v = 0; v < V; ++v) {
+      const int32_t x = id_map[v];
+      if (x < 0 || x > BPE_MAX_ID || seen[(size_t)x]) return BPE_EIDMAP;
+      seen[(size_t)x] = 1;
+      max_id = std::max<int64_t>(max_id, x);
+    }
+  }
+
+  // rank table: power-of-two capacity >= 2R, linear probing
+  int bits = 8;
+  while (((int64_t)1 << bits) < 2 * R) ++bits;
+  std::vector<uint64_t> table((size_t)1 << bits, kEmptySlot);
+  const uint64_t mask = ((uint64_t)1 << bits) - 1;
+  for (int64_t r = 0; r < R; ++r) {
+    uint64_t h = pair_hash(keys[(size_t)r], bits);
+    while (table[(size_t)h] != kEmptySlot) h = (h + 1) & mask;
+    table[(size_t)h] = (keys[(size_t)r] << kSymBits) | (uint64_t)r;
+  }
+
+  bpe_model *m = new (std::nothrow) bpe_model;
+  if (!m) return BPE_ENOMEM;
+  m->R = R;
+  m->V = V;
+  m->table_bits = bits;
+  if (hipGetDevice(&m->device) != hipSuccess) {
+    delete m;
+    return BPE_EHIP;
+  }
+  int rc = upload(&m->d_table, table.data(), table.size(), stream);
+  if (rc == BPE_OK && id_map) rc = upload(&m->d_id_map, id_map, (size_t)V, stream);
+
+  // decode tables: byte expansion of every symbol, and the ID -> symbol map
+  int64_t total = 0;
+  for (int64_t v = 0; v < V && total <= BPE_MAX_EXPANSION; ++v) total += len[(size_t)v];
+  std::vector<int64_t> exp_off;
+  std::vector<uint8_t> exp_bytes;
+  std::vector<int32_t> inv;
+  if (rc == BPE_OK && total <= BPE_MAX_EXPANSION) {
+    exp_off.resize((size_t)V + 1);
+    exp_off[0] = 0;
+    for (int64_t v = 0; v < V; ++v) exp_off[(size_t)v + 1] = exp_off[(size_t)v] + len[(size_t)v];
+    exp_bytes.resize((size_t)std::max<int64_t>(1, total));
+    for (int64_t b = 0; b < 256; ++b) exp_bytes[(size_t)exp_off[(size_t)b]] = (uint8_t)b;
+    for (int64_t v : order) {
+      const int64_t r = v - 256;
+      const int32_t l = merges[2 * r], rt = merges[2 * r + 1];
+      uint8_t *dst = &exp_bytes[(size_t)exp_off[(size_t)v]];
+      std::memcpy(dst, &exp_bytes[(size_t)exp_off[(size_t)l]], (size_t)len[(size_t)l]);
+      std::memcpy(dst + len[(size_t)l], &exp_bytes[(size_t)exp_off[(size_t)rt]],
+                  (size_t)len[(size_t)rt]);
+    }
+    m->max_token = *std::max_element(len.begin(), len.end());
+    rc = upload(&m->d_exp_off, exp_off.data(), exp_off.size(), stream);
+    if (rc == BPE_OK) rc = upload(&m->d_exp_bytes, exp_bytes.data(), exp_bytes.size(), stream);
+    if (rc == BPE_OK && id_map) {
+      inv.assign((size_t)max_id + 1, -1);
+      for (int64_t v = 0; v < V; ++v) inv[(size_t)id_map[v]] = (int32_t)v;
+      m->inv_size = max_id + 1;
+      rc = upload(&m->d_inv_map, inv.data(), inv.size(), stream);
+    }
+    m->decode_ok = rc == BPE_OK;
+  }
+  if (rc == BPE_OK && hipStreamSynchronize(stream) != hipSuccess) rc = BPE_EHIP;
+  if (rc != BPE_OK) {
+    (void)hipStreamSynchronize(stream);
+    free_model(m);
+    return rc;
+  }
+  *out = m;
+  return BPE_OK;
+}
+
+void bpe_free(bpe_model *model) { free_model(model); }
+
+int64_t bpe_vocab_size(const bpe_model *model) { return model ? model->V : -1; }
+
+int64_t bpe_max_token_bytes(const bpe_model *model) {
+  return (model && model->decode_ok) ? model->max_token : -1;
+}
+
+size_t bpe_encode_workspace_bytes(const bpe_model *model, int64_t n_bytes, int64_t n_docs) {
+  (void)model;
+  (void)n_docs;
+  return n_bytes > 0 ? enc_layout(n_bytes).total : 0;
+}
+
+int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
+                     const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids,
+                     int64_t ids_capacity, int64_t *d_id_off, void *d_workspace,
+                     size_t workspace_bytes, int32_t *d_status, void *hip_stream) {
+  if (!model || n_bytes < 0 || n_docs < 0 || ids_capacity < 0 || !d_doc_off || !d_id_off ||
+      !d_status || (ids_capacity > 0 && !d_ids) || (n_bytes > 0 && (!d_bytes || !d_workspace)))
+    return BPE_EINVAL;
+  if (enc_chunks(n_bytes) > INT32_MAX) return BPE_EINVAL;
+  if (!on_model_device(model)) return BPE_EINVAL;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (n_bytes == 0)
+    return launch_empty(d_doc_off, n_docs, BPE_STATUS_BAD_DOC_OFFSETS, d_id_off, d_status,
+                        stream) == hipSuccess
+               ? BPE_OK
+               : BPE_EHIP;
+  const EncLayout L = enc_layout(n_bytes);
+  if (workspace_bytes < L.total) return BPE_EWORKSPACE;
+  uint8_t *ws = (uint8_t *)d_workspace;
+  EncodeArgs a;
+  a.bytes = d_bytes;
+  a.n_bytes = n_bytes;
+  a.doc_off = d_doc_off;
+  a.n_docs = n_docs;
+  a.ids = d_ids;
+  a.ids_cap = ids_capacity;
+  a.id_off = d_id_off;
+  a.table = model->d_table;
+  a.table_bits = model->table_bits;
+  a.id_map = model->d_id_map;
+  a.ticket = (uint32_t *)(ws + L.ticket);
+  a.flags = (uint64_t *)(ws + L.flags);
+  a.gsym = (int32_t *)(ws + L.gsym);
+  a.grank = (int32_t *)(ws + L.grank);
+  a.status = d_status;
+  a.n_chunks = enc_chunks(n_bytes);
+  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, stream) != hipSuccess) return BPE_EHIP;
+  if (launch_encode(a, stream) != hipSuccess) return BPE_EHIP;
+  return BPE_OK;
+}
+
+size_t bpe_decode_workspace_bytes(const bpe_model *model, int64_t n_ids, int64_t n_docs) {
+  (void)model;
+  (void)n_docs;
+  return n_ids > 0 ? dec_layout(n_ids).total : 0;
+}
+
+int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids,
+                     const int64_t *d_id_off, int64_t n_docs, uint8_t *d_bytes,
+                     int64_t bytes_capacity, int64_t *d_byte_off, void *d_workspace,
+                     size_t workspace_bytes, int32_t *d_status, void *hip_stream) {
+  if (!model || n_ids < 0 || n_docs < 0 || bytes_capacity < 0 || !d_id_off || !d_byte_off ||
+      !d_status || (bytes_capacity > 0 && !d_bytes) || (n_ids > 0 && (!d_ids || !d_workspace)))
+    return BPE_EINVAL;
+  if (!model->decode_ok) return BPE_ENOTSUP;
+  if (dec_chunks(n_ids) > INT32_MAX) return BPE_EINVAL;
+  if (!on_model_device(model)) return BPE_EINVAL;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (n_ids == 0)
+    return launch_empty(d_id_off, n_docs, BPE_STATUS_BAD_ID_OFFSETS, d_byte_off, d_status,
+                        stream) == hipSuccess
+               ? BPE_OK
+               : BPE_EHIP;
+  const DecLayout L = dec_layout(n_ids);
+  if (workspace_bytes < L.total) return BPE_EWORKSPACE;
+  uint8_t *ws = (uint8_t *)d_workspace;
+  DecodeArgs a;
+  a.ids = d_ids;
+  a.n_ids = n_ids;
+  a.id_off = d_id_off;
+  a.n_docs = n_docs;
+  a.out = d_bytes;
+  a.out_cap = bytes_capacity;
+  a.byte_off = d_byte_off;
+  a.exp_off = model->d_exp_off;
+  a.exp_bytes = model->d_exp_bytes;
+  a.inv_map = model->d_inv_map;
+  a.inv_size = model->inv_size;
+  a.vocab = model->V;
+  a.ticket = (uint32_t *)(ws + L.ticket);
+  a.flags = (uint64_t *)(ws + L.flags);
+  a.status = d_status;
+  a.n_chunks = dec_chunks(n_ids);
+  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, stream) != hipSuccess) return BPE_EHIP;
+  if (launch_decode(a, stream) != hipSuccess) return BPE_EHIP;
+  return BPE_OK;
+}
+
+const char *bpe_strerror(int code) {
+  switch (code) {
+    case BPE_OK: return "success";
+    case BPE_EINVAL: return "invalid argument";
+    case BPE_EMERGES: return "merge table rejected (repeated pair, operand out of range, or cycle)";
+    case BPE_EIDMAP: return "id_map rejected (negative, repeated or too large ID)";
+    case BPE_EWORKSPACE: return "workspace too small";
+    case BPE_EHIP: return "HIP runtime error";
+    case BPE_ENOMEM: return "out of memory";
+    case BPE_ENOTSUP: return "decode unsupported: byte expansions of this table are too large";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

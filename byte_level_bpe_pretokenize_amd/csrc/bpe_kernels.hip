@@ -1,0 +1,826 @@
+// bpe_kernels.hip -- byte-level BPE encode and decode kernels for gfx950.
+//
+// Encode is one pass over the input.  A workgroup owns a 4 KiB chunk of the
+// concatenated documents: every pre-token whose first byte lies in the chunk.
+//   1. scan: the chunk (plus a 64-byte halo after it and 2 bytes before) is
+//      read once, coalesced, into LDS; each byte gets its class and a start
+//      bit from a 3-byte window, and the start bits are packed 16 per lane.
+//   2. merge: each lane merges the short pre-tokens that start in its 16
+//      bytes, in place in LDS, with ranks probed in the device hash table;
+//      longer ones are merged by the whole workgroup (LDS, or global scratch
+//      for a pre-token that runs past the halo).
+//   3. compaction: surviving symbols are counted per lane, scanned, the
+//      chunk's total is chained to the previous chunks by a decoupled
+//      look-back over 64-bit flags, and the IDs are written at their final
+//      positions together with the per-document offsets.
+// Decode uses the same chained-prefix pattern over per-ID byte lengths.
+//
+// Sources: "Tokenization LLM: ... C++" (glitch4techs.com), sections
+// "Technical analysis", "Byte-level encoding", "BPE algorithm", "Vocabulary
+// lookup"; "Characters, bytes and subwords" (tokenwerk.deckle.io), section
+// "BPE step by step" ([a,a,a] -> [aa,a]); "Hugging Face Tokenizers v1"
+// (dothoosh.com), sections "How v1 works", "Bitcannon" (boundaries from
+// bit-parallel class masks), "Merge-loop rewrite" (flat symbol arrays,
+// 'no merge' as the largest value, batches) and "Road to 1.0.0" (GPU batch
+// encode/decode, output positions in parallel).
+#include <limits.h>
+#include <stdint.h>
+
+#include "bpe_internal.h"
+#include "../../include/bpe.h"
+
+namespace bpe {
+namespace {
+
+constexpr int WG = kEncThreads;
+constexpr int WIN = kChunk + kHalo;        // window positions [0, WIN)
+constexpr int SB_HALF = WIN / 16 + 1;      // 16-bit start masks for positions [0, WIN]
+constexpr int SB_WORDS = (SB_HALF + 1) / 2 + 1;
+constexpr int DB_OFF = 32;                 // doc-start bit of position p is bit p + DB_OFF
+constexpr int DB_WORDS = (WIN + DB_OFF) / 32 + 2;
+constexpr int kMaxLong = kChunk / (kLaneMax + 1) + 4;
+constexpr int kTile = WG * 16;
+constexpr int32_t kDead = -1;
+constexpr int kNoStart = INT_MAX;
+
+// Byte classes (the fixed split rule): letters (A-Z, a-z and every byte from
+// 0x80 up), digits, whitespace (0x09-0x0D, 0x20), punctuation (the rest).
+enum : uint32_t { kL = 0, kD = 1, kW = 2, kP = 3 };
+
+__device__ __forceinline__ uint32_t byte_class(uint32_t b) {
+  const uint32_t lo = b | 0x20u;
+  if ((lo - 'a' <= 'z' - 'a') || b >= 0x80u) return kL;
+  if (b - '0' <= 9u) return kD;
+  if (b - 9u <= 4u || b == 0x20u) return kW;
+  return kP;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Rank of the pair (l, r), or kRankInf.  Linear probing from the pair's hash.
+__device__ __forceinline__ int32_t rank_of(const uint64_t *__restrict__ tab, int bits, uint32_t l,
+                                           uint32_t r) {
+  const uint64_t key = pair_key(l, r);
+  const uint64_t mask = (1ull << bits) - 1;
+  uint64_t h = pair_hash(key, bits);
+  for (;;) {
+    const uint64_t s = tab[h];
+    if ((s >> kSymBits) == key) return (int32_t)(s & ((1u << kSymBits) - 1));
+    if (s == kEmptySlot) return kRankInf;
+    h = (h + 1) & mask;
+  }
+}
+
+// ---- wave / workgroup reductions and scans --------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_sum(T v) {
+  const int lane = lane_id();
+  for (int d = 1; d < 64; d <<= 1) {
+    const T o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over the workgroup; *total gets the sum.  Barriers
+// inside: every thread must call it.
+template <typename T, int NT>
+__device__ T block_excl_sum(T v, T *red, T *total) {
+  const T inc = wave_incl_sum(v);
+  if (lane_id() == 63) red[wave_id()] = inc;
+  __syncthreads();
+  T wp = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const T x = red[w];
+    if (w < wave_id()) wp += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return wp + inc - v;
+}
+
+template <int NT>
+__device__ int32_t block_min(int32_t v, int32_t *red) {
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  int32_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) m = min(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+template <int NT>
+__device__ int32_t block_max(int32_t v, int32_t *red) {
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 64));
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  int32_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) m = max(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+// Exclusive running maximum over the workgroup (identity `lowest`);
+// *total gets the maximum of all values.
+template <int NT>
+__device__ int64_t block_excl_max64(int64_t v, int64_t lowest, int64_t *red, int64_t *total) {
+  const int lane = lane_id();
+  int64_t inc = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc = max(inc, o);
+  }
+  int64_t ex = __shfl_up(inc, 1, 64);
+  if (lane == 0) ex = lowest;
+  if (lane == 63) red[wave_id()] = inc;
+  __syncthreads();
+  int64_t wp = lowest, tot = lowest;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int64_t x = red[w];
+    if (w < wave_id()) wp = max(wp, x);
+    tot = max(tot, x);
+  }
+  __syncthreads();
+  *total = tot;
+  return max(wp, ex);
+}
+
+// First index i in [0, n) with a[i] >= key (n if none), for a sorted array.
+// Called by all 64 lanes of one wave; 64-way split per step.  For an array
+// that is not sorted the result is still in [0, n].
+__device__ int64_t wave_lower_bound(const int64_t *a, int64_t n, int64_t key) {
+  const int lane = lane_id();
+  int64_t lo = 0, hi = n;  // a[i] < key for i < lo; answer <= hi
+  while (hi - lo > 64) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t idx = lo + (int64_t)lane * step;
+    const bool ge = idx < hi ? (a[idx] >= key) : true;
+    const uint64_t m = __ballot(ge);
+    const int first = m ? __ffsll((unsigned long long)m) - 1 : 64;
+    const int64_t nlo = first == 0 ? lo : lo + (int64_t)(first - 1) * step + 1;
+    const int64_t nhi = first == 64 ? hi : min(hi, lo + (int64_t)first * step);
+    lo = nlo;
+    hi = max(nhi, nlo);
+  }
+  const int64_t idx = lo + lane;
+  const bool ge = idx < hi ? (a[idx] >= key) : true;
+  const uint64_t m = __ballot(ge);
+  return m ? lo + (__ffsll((unsigned long long)m) - 1) : hi;
+}
+
+// Decoupled look-back over per-chunk flags (called by all lanes of one wave).
+// Publishes this chunk's own count, then sums the counts of earlier chunks
+// until one with a published running total, publishes its own running total
+// and returns the exclusive prefix.
+__device__ int64_t wave_lookback(uint64_t *flags, int64_t c, int64_t agg) {
+  const int lane = lane_id();
+  if (c == 0) {
+    if (lane == 0)
+      __hip_atomic_store(&flags[0], kFlagPrefix | (uint64_t)agg, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    return 0;
+  }
+  if (lane == 0)
+    __hip_atomic_store(&flags[c], kFlagAgg | (uint64_t)agg, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  int64_t excl = 0;
+  int64_t top = c - 1;
+  for (;;) {
+    const int64_t idx = top - lane;
+    const uint64_t f = idx >= 0 ? __hip_atomic_load(&flags[idx], __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                : kFlagPrefix;
+    const uint64_t state = f & ~kFlagValue;
+    const uint64_t not_ready = __ballot(state == 0);
+    const uint64_t pfx = __ballot(state == kFlagPrefix);
+    const int kp = pfx ? __ffsll((unsigned long long)pfx) - 1 : 64;
+    const uint64_t upto = kp >= 63 ? ~0ull : ((1ull << (kp + 1)) - 1);
+    if (not_ready & upto) {
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    const int64_t v = lane <= kp ? (int64_t)(f & kFlagValue) : 0;
+    excl += wave_sum(v);
+    if (kp < 64) break;
+    top -= 64;
+  }
+  if (lane == 0)
+    __hip_atomic_store(&flags[c], kFlagPrefix | (uint64_t)(excl + agg), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return excl;
+}
+
+// ---- encode ---------------------------------------------------------------
+struct EncShared {
+  int32_t Y[WIN];     // symbols at their byte positions (kDead: no symbol)
+  int32_t RK[WIN];    // RK[p] = rank of the pair starting at p
+  alignas(16) uint8_t B[16 + WIN];  // B[16 + p] = byte at window position p
+  uint32_t SB[SB_WORDS];            // pre-token start bits, positions [0, WIN]
+  uint32_t DB[DB_WORDS];            // document start bits, positions [-32, WIN)
+  int32_t excl[WG];                 // per-lane exclusive token counts
+  int32_t mflag[WG];
+  int32_t red[8];
+  int64_t red64[8];
+  int32_t longs[kMaxLong];
+  int32_t n_long;
+  int64_t chunk;
+  int64_t d_lo, o_lo, o_hi;
+  int64_t base;
+  int64_t ov_start, ov_ntok;
+};
+
+__device__ __forceinline__ uint32_t sb16(const EncShared &s, int g) {
+  return reinterpret_cast<const uint16_t *>(s.SB)[g];
+}
+
+__device__ __forceinline__ bool db_bit(const EncShared &s, int p) {
+  const int q = p + DB_OFF;
+  return (s.DB[q >> 5] >> (q & 31)) & 1u;
+}
+
+// Smallest start position in [from, to] (to <= WIN), or -1.
+__device__ __forceinline__ int next_start_bounded(const EncShared &s, int from, int to) {
+  if (from > to) return -1;
+  int w = from >> 5;
+  uint32_t bits = s.SB[w] & (~0u << (from & 31));
+  const int wl = to >> 5;
+  while (bits == 0 && w < wl) bits = s.SB[++w];
+  if (bits == 0) return -1;
+  const int p = (w << 5) + __ffs(bits) - 1;
+  return p <= to ? p : -1;
+}
+
+// Smallest start position in [from, WIN], or kNoStart.  Whole workgroup.
+__device__ int block_next_start(EncShared &s, int from) {
+  int cand = kNoStart;
+  if (from <= WIN) {
+    const int w = (from >> 5) + (int)threadIdx.x;
+    if (w <= (WIN >> 5)) {
+      uint32_t bits = s.SB[w];
+      if (w == (from >> 5)) bits &= ~0u << (from & 31);
+      if (bits) {
+        const int p = (w << 5) + __ffs(bits) - 1;
+        if (p <= WIN) cand = p;
+      }
+    }
+  }
+  return block_min<WG>(cand, s.red);
+}
+
+// Merge one short pre-token of n symbols in place at Y[0..n), RK[0..n) (one
+// lane).  Each round takes the lowest rank r present and rewrites the
+// sequence left to right, merging every pair whose rank is r unless its left
+// symbol was just consumed; then only pairs touching the new symbol are
+// probed again.  Leaves kDead after the result.
+__device__ void lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_t *tab,
+                           const int bits) {
+  for (int i = 0; i + 1 < len; ++i) RK[i] = rank_of(tab, bits, Y[i], Y[i + 1]);
+  RK[len - 1] = kRankInf;
+  int n = len;
+  for (;;) {
+    int32_t r = kRankInf;
+    for (int i = 0; i + 1 < n; ++i) r = min(r, RK[i]);
+    if (r == kRankInf) break;
+    const int32_t z = 256 + r;
+    int o = 0;
+    for (int i = 0; i < n; ++o) {
+      if (RK[i] == r) {
+        Y[o] = z;
+        i += 2;
+      } else {
+        Y[o] = Y[i];
+        RK[o] = RK[i];
+        i += 1;
+      }
+    }
+    n = o;
+    for (int j = 0; j + 1 < n; ++j)
+      if (Y[j] == z || Y[j + 1] == z) RK[j] = rank_of(tab, bits, Y[j], Y[j + 1]);
+    RK[n - 1] = kRankInf;
+  }
+  for (int j = n; j < len; ++j) Y[j] = kDead;
+}
+
+// Merge one pre-token of n symbols at Y[0..n) with the whole workgroup; RK is
+// scratch of n entries.  Y and RK are LDS or global (position-indexed
+// scratch).  Same rounds as lane_merge: the lowest rank r is found by a
+// workgroup minimum, runs of consecutive pairs with rank r (only possible for
+// a pair (x, x)) merge at even offsets from the run start, and survivors are
+// compacted in place tile by tile.  Returns the final symbol count.
+__device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const uint64_t *tab, int bits,
+                            EncShared &s) {
+  const int tid = threadIdx.x;
+  for (int64_t i = tid; i < n; i += WG)
+    RK[i] = (i + 1 < n) ? rank_of(tab, bits, Y[i], Y[i + 1]) : kRankInf;
+  __syncthreads();
+  for (;;) {
+    int32_t r = kRankInf;
+    for (int64_t i = tid; i < n; i += WG) r = min(r, RK[i]);
+    r = block_min<WG>(r, s.red);
+    if (r == kRankInf) break;
+    const int32_t z = 256 + r;
+    int64_t out_base = 0;
+    int64_t anchor = -1;  // last position before the tile whose pair rank is not r
+    bool prev_m = false;  // the pair just before the tile merged
+    for (int64_t t0 = 0; t0 < n; t0 += kTile) {
+      const int64_t p0 = t0 + 16 * (int64_t)tid;
+      int32_t y[16], rk[16];
+      bool f[16];
+      int64_t my_anchor = -1;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t p = p0 + j;
+        const bool v = p < n;
+        rk[j] = v ? RK[p] : kRankInf;
+        y[j] = v ? Y[p] : kDead;
+        f[j] = v && rk[j] == r;
+        if (!f[j]) my_anchor = p;
+      }
+      int64_t tile_anchor;
+      int64_t za = block_excl_max64<WG>(my_anchor, -1, s.red64, &tile_anchor);
+      za = max(za, anchor);
+      bool m[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t p = p0 + j;
+        if (!f[j]) {
+          m[j] = false;
+          za = p;
+        } else {
+          m[j] = ((p - 1 - za) & 1) == 0;
+        }
+      }
+      s.mflag[tid] = m[15];
+      __syncthreads();
+      const bool mprev = tid ? (s.mflag[tid - 1] != 0) : prev_m;
+      const bool tile_last_m = s.mflag[WG - 1] != 0;
+      bool keep[16];
+      int kc = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool consumed = j == 0 ? mprev : m[j - 1];
+        keep[j] = (p0 + j < n) && !consumed;
+        kc += keep[j];
+      }
+      int tile_kept;
+      const int kex = block_excl_sum<int, WG>(kc, s.red, &tile_kept);
+      int64_t o = out_base + kex;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (keep[j]) {
+          Y[o] = m[j] ? z : y[j];
+          RK[o] = rk[j];
+          ++o;
+        }
+      }
+      anchor = max(anchor, tile_anchor);
+      prev_m = tile_last_m;
+      out_base += tile_kept;
+      __syncthreads();
+    }
+    n = out_base;
+    for (int64_t i = tid; i < n; i += WG) {
+      if (i + 1 < n) {
+        const int32_t a = Y[i], b = Y[i + 1];
+        if (a == z || b == z) RK[i] = rank_of(tab, bits, a, b);
+      } else {
+        RK[i] = kRankInf;
+      }
+    }
+    __syncthreads();
+  }
+  return n;
+}
+
+__device__ __forceinline__ int32_t out_id(const int32_t *id_map, int32_t sym) {
+  return id_map ? id_map[sym] : sym;
+}
+
+// End (exclusive, global) of the pre-token that starts at gs and has no start
+// in the window, scanning bytes from `from` on.  Whole workgroup.
+__device__ int64_t block_global_end(const EncodeArgs &a, EncShared &s, int64_t gs, int64_t from) {
+  const int tid = threadIdx.x;
+  if (wave_id() == 0) {
+    const int64_t d = wave_lower_bound(a.doc_off, a.n_docs + 1, gs + 1);
+    if (lane_id() == 0) {
+      int64_t dn = d <= a.n_docs ? a.doc_off[d] : a.n_bytes;
+      dn = min(max(dn, gs + 1), a.n_bytes);
+      s.red64[4] = dn;
+    }
+  }
+  __syncthreads();
+  const int64_t limit = s.red64[4];
+  __syncthreads();
+  const uint8_t *b = a.bytes;
+  // from > gs + 1 always (the pre-token fills the window), so q - 1 > gs is
+  // inside the document and is not a document start
+  for (int64_t q0 = max(from, gs + 2); q0 < limit; q0 += kTile) {
+    int cand = kNoStart;
+    for (int j = 0; j < 16; ++j) {
+      const int64_t q = q0 + 16 * (int64_t)tid + j;
+      if (q >= limit) break;
+      const uint32_t c0 = byte_class(b[q]), b1 = b[q - 1], c1 = byte_class(b1);
+      const bool attach = c0 == kL && b1 == 0x20u && byte_class(b[q - 2]) != kW;
+      if (c0 != c1 && !attach) {
+        cand = 16 * tid + j;
+        break;
+      }
+    }
+    const int first = block_min<WG>(cand, s.red);
+    if (first != kNoStart) return q0 + first;
+  }
+  return limit;
+}
+
+__global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
+  __shared__ EncShared s;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+
+  // Offsets check, spread over the grid by launch index.
+  {
+    const int64_t per = (a.n_docs + 1 + gridDim.x - 1) / gridDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * per;
+    bool bad = false;
+    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += WG) {
+      const int64_t v = a.doc_off[i];
+      if (i == 0 && v != 0) bad = true;
+      if (i == a.n_docs && v != a.n_bytes) bad = true;
+      if (i < a.n_docs && a.doc_off[i + 1] < v) bad = true;
+    }
+    if (bad) atomicOr(a.status, (int32_t)BPE_STATUS_BAD_DOC_OFFSETS);
+  }
+
+  if (tid == 0) {
+    s.chunk = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.n_long = 0;
+    s.ov_start = -1;
+    s.ov_ntok = 0;
+  }
+  for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
+  __syncthreads();
+  const int64_t c = s.chunk;
+  const int64_t c0 = c * kChunk;
+  const int64_t n = a.n_bytes;
+  const int nwin = (int)min<int64_t>(WIN, n - c0);
+  const int nown = (int)min<int64_t>(kChunk, n - c0);
+  const bool win_reaches_end = (c0 + nwin == n);
+
+  // 1. documents touching the window; bytes into LDS
+  if (wave == 0) {
+    const int64_t dlo = wave_lower_bound(a.doc_off, a.n_docs + 1, c0 - 1);
+    const int64_t olo = wave_lower_bound(a.doc_off, a.n_docs + 1, c0);
+    const int64_t ohi = wave_lower_bound(a.doc_off, a.n_docs + 1, c0 + nown);
+    if (lane == 0) {
+      s.d_lo = dlo;
+      s.o_lo = olo;
+      s.o_hi = ohi;
+    }
+  }
+  {
+    const bool aligned = (((uintptr_t)a.bytes) & 15u) == 0;
+    for (int g = tid - 1; g < WIN / 16; g += WG) {
+      const int64_t gp = c0 + 16 * (int64_t)g;
+      uint8_t *dst = &s.B[16 + 16 * g];
+      if (aligned && gp >= 0 && gp + 16 <= n) {
+        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(a.bytes + gp);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int64_t q = gp + k;
+          dst[k] = (q >= 0 && q < n) ? a.bytes[q] : 0;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int64_t d = s.d_lo + tid; d < a.n_docs; d += WG) {
+    const int64_t p = a.doc_off[d] - c0;
+    if (p >= nwin) break;
+    if (p >= -1) atomicOr(&s.DB[(p + DB_OFF) >> 5], 1u << ((p + DB_OFF) & 31));
+  }
+  __syncthreads();
+
+  // 2. start bits: a document start, or a class change unless a single space
+  //    that follows a non-whitespace byte (or opens the document) leads a
+  //    letter run.  Positions past the input end read as starts.
+  for (int g = tid; g < SB_HALF; g += WG) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int p = 16 * g + k;
+      bool st;
+      if (p >= nwin) {
+        st = win_reaches_end;
+      } else if (db_bit(s, p)) {
+        st = true;
+      } else {
+        const uint32_t b0 = s.B[16 + p], b1 = s.B[16 + p - 1], b2 = s.B[16 + p - 2];
+        const uint32_t k0 = byte_class(b0), k1 = byte_class(b1);
+        const bool attach = k0 == kL && b1 == 0x20u && (db_bit(s, p - 1) || byte_class(b2) != kW);
+        st = k0 != k1 && !attach;
+      }
+      m |= (uint32_t)st << k;
+    }
+    reinterpret_cast<uint16_t *>(s.SB)[g] = (uint16_t)m;
+  }
+  __syncthreads();
+
+  // first and last owned start; end of the last owned pre-token
+  int fs = kNoStart, ls = -1;
+  if (16 * tid < nown) {
+    uint32_t m = sb16(s, tid);
+    const int lim = nown - 16 * tid;
+    if (lim < 16) m &= (1u << lim) - 1;
+    if (m) {
+      fs = 16 * tid + __ffs(m) - 1;
+      ls = 16 * tid + 31 - __clz(m);
+    }
+  }
+  fs = block_min<WG>(fs, s.red);
+  ls = block_max<WG>(ls, s.red);
+  const int e_last = ls >= 0 ? block_next_start(s, ls + 1) : -1;  // kNoStart: runs past WIN
+  const bool overhang = ls >= 0 && e_last == kNoStart;
+  const int own_end = ls < 0 ? 0 : (overhang ? ls : e_last);
+  for (int p = tid; p < WIN; p += WG) {
+    s.Y[p] = (p >= fs && p < own_end) ? (int32_t)s.B[16 + p] : kDead;
+    s.RK[p] = kRankInf;
+  }
+  __syncthreads();
+
+  // 3. lane tier: pre-tokens that start in this lane's 16 bytes
+  if (16 * tid < nown) {
+    uint32_t m = sb16(s, tid);
+    const int lim = nown - 16 * tid;
+    if (lim < 16) m &= (1u << lim) - 1;
+    while (m) {
+      const int st = 16 * tid + __ffs(m) - 1;
+      m &= m - 1;
+      if (overhang && st == ls) continue;
+      const int e = next_start_bounded(s, st + 1, min(st + kLaneMax, WIN));
+      if (e < 0) {
+        const int k = atomicAdd(&s.n_long, 1);
+        s.longs[k] = st;
+        continue;
+      }
+      lane_merge(s.Y + st, s.RK + st, e - st, a.table, a.table_bits);
+    }
+  }
+  __syncthreads();
+
+  // 4. workgroup tier: longer pre-tokens inside the window, then the one that
+  //    runs past it (in the position-indexed global scratch)
+  const int n_long = s.n_long;
+  for (int k = 0; k < n_long; ++k) {
+    const int st = s.longs[k];
+    const int e = block_next_start(s, st + 1);
+    const int64_t len = e - st;
+    const int64_t nt = wg_merge(s.Y + st, s.RK + st, len, a.table, a.table_bits, s);
+    for (int64_t j = nt + tid; j < len; j += WG) s.Y[st + j] = kDead;
+    __syncthreads();
+  }
+  if (overhang) {
+    const int64_t gs = c0 + ls;
+    const int64_t ge = block_global_end(a, s, gs, c0 + WIN);
+    for (int64_t q = gs + tid; q < ge; q += WG) a.gsym[q] = a.bytes[q];
+    __syncthreads();
+    const int64_t nt = wg_merge(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits, s);
+    if (tid == 0) {
+      s.ov_start = gs;
+      s.ov_ntok = nt;
+    }
+    __syncthreads();
+  }
+
+  // 5. counts, chained prefix, writes
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cnt += s.Y[16 * tid + k] != kDead;
+  int main_total;
+  const int ex = block_excl_sum<int, WG>(cnt, s.red, &main_total);
+  s.excl[tid] = ex;
+  int halo_rank = 0, halo_total = 0;
+  bool halo_valid = false;
+  if (wave == 0) {
+    halo_valid = s.Y[kChunk + lane] != kDead;
+    const uint64_t hb = __ballot(halo_valid);
+    halo_total = __popcll(hb);
+    halo_rank = __popcll(hb & ((1ull << lane) - 1));
+    const int64_t agg = (int64_t)main_total + halo_total + s.ov_ntok;
+    const int64_t base = wave_lookback(a.flags, c, agg);
+    if (lane == 0) s.base = base;
+  }
+  __syncthreads();
+  const int64_t base = s.base;
+  bool overflow = false;
+  {
+    int64_t w = base + ex;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int32_t y = s.Y[16 * tid + k];
+      if (y != kDead) {
+        if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, y);
+        else overflow = true;
+        ++w;
+      }
+    }
+  }
+  if (wave == 0 && halo_valid) {
+    const int64_t w = base + main_total + halo_rank;
+    if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, s.Y[kChunk + lane]);
+    else overflow = true;
+  }
+  // halo count for every wave (wave 0 computed it)
+  if (tid == 0) s.red[6] = halo_total;
+  __syncthreads();
+  const int halo_all = s.red[6];
+  if (s.ov_start >= 0) {
+    const int64_t w0 = base + main_total + halo_all;
+    for (int64_t j = tid; j < s.ov_ntok; j += WG) {
+      const int64_t w = w0 + j;
+      if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, a.gsym[s.ov_start + j]);
+      else overflow = true;
+    }
+  }
+  if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
+
+  // per-document offsets: a document starting at p begins after every token
+  // of the pre-tokens that start before p
+  for (int64_t d = s.o_lo + tid; d < s.o_hi; d += WG) {
+    const int64_t p64 = a.doc_off[d] - c0;
+    const int p = (int)min<int64_t>(max<int64_t>(p64, 0), kChunk - 1);
+    const int t = p >> 4;
+    int before = s.excl[t];
+    for (int q = 16 * t; q < p; ++q) before += s.Y[q] != kDead;
+    a.id_off[d] = base + before;
+  }
+  if (c == a.n_chunks - 1) {
+    const int64_t total = base + main_total + halo_all + s.ov_ntok;
+    for (int64_t d = s.o_hi + tid; d <= a.n_docs; d += WG) a.id_off[d] = total;
+  }
+}
+
+// Clears the ticket, the status word and the look-back flags.
+__global__ void k_clear(uint32_t *ticket, uint64_t *flags, int64_t n_flags, int32_t *status) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if (gid == 0) {
+    *ticket = 0;
+    *status = 0;
+  }
+  for (int64_t i = gid; i < n_flags; i += stride) flags[i] = 0;
+}
+
+// Empty input (one workgroup): clear the status, then check that every
+// offset is zero and write zero offsets.
+__global__ void k_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, int64_t *out_off,
+                        int32_t *status) {
+  if (threadIdx.x == 0) *status = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int64_t i = threadIdx.x; i <= n_docs; i += blockDim.x) {
+    if (offs[i] != 0) bad = true;
+    out_off[i] = 0;
+  }
+  if (bad) atomicOr(status, (int32_t)bad_bit);
+}
+
+// ---- decode ---------------------------------------------------------------
+constexpr int DWG = kDecThreads;
+constexpr int DPT = kDecPerThread;
+
+struct DecShared {
+  int32_t len[kDecChunk];
+  int32_t sym[kDecChunk];
+  int64_t excl[DWG];
+  int64_t red64[8];
+  int64_t chunk;
+  int64_t o_lo, o_hi;
+  int64_t base;
+};
+
+__global__ void __launch_bounds__(DWG) k_decode(DecodeArgs a) {
+  __shared__ DecShared s;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  {
+    const int64_t per = (a.n_docs + 1 + gridDim.x - 1) / gridDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * per;
+    bool bad = false;
+    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += DWG) {
+      const int64_t v = a.id_off[i];
+      if (i == 0 && v != 0) bad = true;
+      if (i == a.n_docs && v != a.n_ids) bad = true;
+      if (i < a.n_docs && a.id_off[i + 1] < v) bad = true;
+    }
+    if (bad) atomicOr(a.status, (int32_t)BPE_STATUS_BAD_ID_OFFSETS);
+  }
+  if (tid == 0)
+    s.chunk = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int64_t c = s.chunk;
+  const int64_t i0 = c * kDecChunk;
+  const int cnt = (int)min<int64_t>(kDecChunk, a.n_ids - i0);
+  if (wave == 0) {
+    const int64_t olo = wave_lower_bound(a.id_off, a.n_docs + 1, i0);
+    const int64_t ohi = wave_lower_bound(a.id_off, a.n_docs + 1, i0 + cnt);
+    if (lane == 0) {
+      s.o_lo = olo;
+      s.o_hi = ohi;
+    }
+  }
+  bool bad_id = false;
+  int64_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int k = tid * DPT + j;
+    int32_t sym = -1, len = 0;
+    if (k < cnt) {
+      const int32_t id = a.ids[i0 + k];
+      if (a.inv_map) sym = (id >= 0 && id < a.inv_size) ? a.inv_map[id] : -1;
+      else sym = (id >= 0 && id < a.vocab) ? id : -1;
+      if (sym < 0) bad_id = true;
+      else len = (int32_t)(a.exp_off[sym + 1] - a.exp_off[sym]);
+    }
+    s.sym[k] = sym;
+    s.len[k] = len;
+    mine += len;
+  }
+  if (bad_id) atomicOr(a.status, (int32_t)BPE_STATUS_BAD_ID);
+  int64_t total;
+  const int64_t ex = block_excl_sum<int64_t, DWG>(mine, s.red64, &total);
+  s.excl[tid] = ex;
+  if (wave == 0) {
+    const int64_t base = wave_lookback(a.flags, c, total);
+    if (lane == 0) s.base = base;
+  }
+  __syncthreads();
+  const int64_t base = s.base;
+  bool overflow = false;
+  int64_t w = base + ex;
+  for (int j = 0; j < DPT; ++j) {
+    const int k = tid * DPT + j;
+    const int32_t sym = s.sym[k];
+    const int32_t len = s.len[k];
+    if (sym >= 0) {
+      const uint8_t *src = a.exp_bytes + a.exp_off[sym];
+      for (int q = 0; q < len; ++q) {
+        if (w + q < a.out_cap) a.out[w + q] = src[q];
+        else overflow = true;
+      }
+    }
+    w += len;
+  }
+  if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_BYTES_CAPACITY);
+  for (int64_t d = s.o_lo + tid; d < s.o_hi; d += DWG) {
+    const int64_t k64 = a.id_off[d] - i0;
+    const int k = (int)min<int64_t>(max<int64_t>(k64, 0), kDecChunk - 1);
+    const int t = k / DPT;
+    int64_t before = s.excl[t];
+    for (int q = t * DPT; q < k; ++q) before += s.len[q];
+    a.byte_off[d] = base + before;
+  }
+  if (c == a.n_chunks - 1)
+    for (int64_t d = s.o_hi + tid; d <= a.n_docs; d += DWG) a.byte_off[d] = base + total;
+}
+
+}  // namespace
+
+hipError_t launch_clear(uint32_t *ticket, uint64_t *flags, int64_t n_flags, int32_t *status,
+                        hipStream_t stream) {
+  int64_t blocks = (n_flags + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+  hipLaunchKernelGGL(k_clear, dim3((unsigned)blocks), dim3(256), 0, stream, ticket, flags, n_flags,
+                     status);
+  return hipGetLastError();
+}
+
+hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, int64_t *out_off,
+                        int32_t *status, hipStream_t stream) {
+  hipLaunchKernelGGL(k_empty, dim3(1), dim3(256), 0, stream, offs, n_docs, bad_bit, out_off,
+                     status);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_encode, dim3((unsigned)a.n_chunks), dim3(WG), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_decode, dim3((unsigned)a.n_chunks), dim3(DWG), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bpe

@@ -1,0 +1,168 @@
+/*
+ * bpe.h -- C ABI of the MI355X byte-level BPE library (libbpe.so).
+ *
+ * The operation (sources named by page title and section):
+ *  - "Tokenization LLM: details of building an inference engine in C++"
+ *    (glitch4techs.com), sections "Technical analysis" (a fixed pattern splits
+ *    text into words, numbers, punctuation and whitespace, each piece handled
+ *    on its own), "Byte-level encoding" (text is UTF-8 bytes), "BPE algorithm"
+ *    (repeatedly merge the adjacent pair with the lowest rank until no ranked
+ *    pair is left) and "Vocabulary lookup" (merged symbols become integer IDs).
+ *  - "Characters, bytes and subwords" (tokenwerk.deckle.io), section "BPE step
+ *    by step": a merge acts on the current sequence from the left without
+ *    overlap, so [a,a,a] with (a,a) gives [aa,a]; section "Check the round
+ *    trip first": decode(encode(x)) == x.
+ *  - "Hugging Face Tokenizers v1: encoding up to 30x faster" (dothoosh.com),
+ *    sections "How v1 works" (a merge never crosses a pre-token boundary),
+ *    "Merge-loop rewrite" (caller-managed scratch, batches of pre-tokens) and
+ *    "Road to 1.0.0" (batch encode/decode on the GPU with the vocabulary
+ *    uploaded once, output positions computed in parallel, bytes gathered on
+ *    the device; IDs-only output).
+ *
+ * Fixed readings of what the pages leave open:
+ *  - Byte classes: L = A-Z, a-z and every byte >= 0x80; D = 0-9;
+ *    W = 0x09-0x0D and 0x20; P = every other byte.
+ *  - Split: the leftmost-first alternation of greedy runs
+ *    ` ?L+ | D+ | P+ | W+` (only the space 0x20 may lead a letter run).
+ *    Every document start is a pre-token start.
+ *  - One merge step takes the smallest rank r* among all adjacent pairs of the
+ *    pre-token and replaces every occurrence of pair(r*) in one left-to-right,
+ *    non-overlapping pass; steps repeat until no adjacent pair is ranked.
+ *  - Bytes are symbols 0..255; the merge of rank r creates symbol 256 + r.
+ *    The output ID of a symbol is the symbol, or id_map[symbol].
+ *
+ * Conventions for every call:
+ *  - Arguments named d_* are device pointers on the device that was current
+ *    when the model was loaded; every other pointer is host memory.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t, or NULL for the null
+ *    stream).  Encode and decode never synchronize the host; they return as
+ *    soon as their kernels are queued.
+ *  - Host-checkable problems return a negative BPE_E* code and enqueue
+ *    nothing.  Problems only the device can see are reported in *d_status (an
+ *    int32 in device memory that the call first clears) as BPE_STATUS_* bits;
+ *    read it after synchronizing the stream.  When *d_status != 0 the outputs
+ *    are not valid.
+ *  - The caller owns all device buffers, including the workspace, which must
+ *    not be shared by calls that may run at the same time.  A model is
+ *    read-only after loading and may be used from several streams at once.
+ */
+#ifndef BPE_H
+#define BPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define BPE_OK 0
+#define BPE_EINVAL (-1)      /* null pointer, negative size, unsupported size, wrong device */
+#define BPE_EMERGES (-2)     /* merge table: repeated pair, operand out of range, or a cycle */
+#define BPE_EIDMAP (-3)      /* id_map: negative, repeated, or above BPE_MAX_ID */
+#define BPE_EWORKSPACE (-4)  /* workspace_bytes below what the *_workspace_bytes call gives */
+#define BPE_EHIP (-5)        /* a HIP runtime call failed */
+#define BPE_ENOMEM (-6)      /* host or device allocation failed while loading */
+#define BPE_ENOTSUP (-7)     /* decode: this table's byte expansions exceed BPE_MAX_EXPANSION */
+
+/* bits of *d_status */
+#define BPE_STATUS_BAD_DOC_OFFSETS 1u   /* encode: offsets not 0 = d[0] <= ... <= d[n_docs] = n_bytes */
+#define BPE_STATUS_IDS_CAPACITY 2u      /* encode: more IDs than ids_capacity (extra IDs dropped) */
+#define BPE_STATUS_BAD_ID 4u            /* decode: an ID that no symbol maps to */
+#define BPE_STATUS_BYTES_CAPACITY 8u    /* decode: more bytes than bytes_capacity (extra dropped) */
+#define BPE_STATUS_BAD_ID_OFFSETS 16u   /* decode: offsets not 0 = o[0] <= ... <= o[n_docs] = n_ids */
+
+/* limits */
+#define BPE_MAX_MERGES (1 << 20)               /* merges per table */
+#define BPE_MAX_ID ((1 << 24) - 1)             /* largest value an id_map may hold */
+#define BPE_MAX_EXPANSION ((int64_t)1 << 30)   /* total decoded bytes of all symbols, for decode */
+
+typedef struct bpe_model bpe_model;
+
+/*
+ * Load a merge table ("merges.txt" of the C++ engine page, as integers).
+ *  merges   host int32 [n_merges][2]: row r is the pair (left, right) whose
+ *           merge has rank r and creates symbol 256 + r.  Operands are
+ *           symbols in [0, 256 + n_merges).  Pairs must be distinct and no
+ *           symbol may depend on itself through its operands.  Ranks need not
+ *           follow creation order.  May be NULL when n_merges == 0.
+ *  n_merges 0 <= n_merges <= BPE_MAX_MERGES.
+ *  id_map   host int32 [256 + n_merges] or NULL (identity): the output ID of
+ *           each symbol; values distinct, in [0, BPE_MAX_ID].
+ *  out      receives the model; free it with bpe_free.
+ * The tables are copied to the current device on hip_stream, and the call
+ * waits for the copies.  Returns BPE_OK, BPE_EINVAL, BPE_EMERGES,
+ * BPE_EIDMAP, BPE_ENOMEM or BPE_EHIP; *out is set only on success.
+ */
+int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_map,
+                    void *hip_stream, bpe_model **out);
+
+/* Release a model and its device tables (the caller makes sure no queued
+ * work still uses it).  NULL is ignored. */
+void bpe_free(bpe_model *model);
+
+/* 256 + n_merges, or -1 for NULL. */
+int64_t bpe_vocab_size(const bpe_model *model);
+
+/* Largest token length in bytes (1 if there are no merges), or -1 for NULL or
+ * when decode is unsupported for this table. */
+int64_t bpe_max_token_bytes(const bpe_model *model);
+
+/* Workspace bytes bpe_encode_batch needs for this input size (0 for
+ * n_bytes <= 0). */
+size_t bpe_encode_workspace_bytes(const bpe_model *model, int64_t n_bytes, int64_t n_docs);
+
+/*
+ * Encode a batch of documents into token IDs.
+ *  d_bytes       uint8 [n_bytes]: the documents back to back (UTF-8 or any
+ *                bytes; no byte is special).
+ *  d_doc_off     int64 [n_docs + 1]: document d is d_bytes[d_doc_off[d] ..
+ *                d_doc_off[d+1]); must satisfy 0 = d_doc_off[0] <= ... <=
+ *                d_doc_off[n_docs] = n_bytes, else BPE_STATUS_BAD_DOC_OFFSETS
+ *                and nothing is written.  Empty documents are allowed.
+ *  d_ids         int32 [ids_capacity]: receives the IDs of all documents in
+ *                order.  The count never exceeds n_bytes, so ids_capacity >=
+ *                n_bytes always suffices; with less, IDs at index >=
+ *                ids_capacity are dropped and BPE_STATUS_IDS_CAPACITY is set.
+ *  d_id_off      int64 [n_docs + 1]: receives the offsets of each document's
+ *                IDs; d_id_off[n_docs] is the total ID count.
+ *  d_workspace   device scratch of workspace_bytes >=
+ *                bpe_encode_workspace_bytes(model, n_bytes, n_docs).
+ *  d_status      int32 [1]: cleared, then receives BPE_STATUS_* bits.
+ * Returns BPE_OK, BPE_EINVAL, BPE_EWORKSPACE or BPE_EHIP.
+ */
+int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
+                     const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids,
+                     int64_t ids_capacity, int64_t *d_id_off, void *d_workspace,
+                     size_t workspace_bytes, int32_t *d_status, void *hip_stream);
+
+/* Workspace bytes bpe_decode_batch needs (0 for n_ids <= 0). */
+size_t bpe_decode_workspace_bytes(const bpe_model *model, int64_t n_ids, int64_t n_docs);
+
+/*
+ * Decode token IDs back to bytes (the inverse of encode, byte for byte).
+ *  d_ids         int32 [n_ids]; an ID that is not the output ID of any symbol
+ *                sets BPE_STATUS_BAD_ID (it contributes no bytes).
+ *  d_id_off      int64 [n_docs + 1] with 0 = o[0] <= ... <= o[n_docs] = n_ids,
+ *                else BPE_STATUS_BAD_ID_OFFSETS and nothing is written.
+ *  d_bytes       uint8 [bytes_capacity]: receives the bytes of all documents;
+ *                bytes past the capacity are dropped and
+ *                BPE_STATUS_BYTES_CAPACITY is set.  n_ids * bpe_max_token_bytes
+ *                always suffices.
+ *  d_byte_off    int64 [n_docs + 1]: receives the byte offsets per document.
+ * Returns BPE_OK, BPE_EINVAL, BPE_EWORKSPACE, BPE_ENOTSUP or BPE_EHIP.
+ */
+int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids,
+                     const int64_t *d_id_off, int64_t n_docs, uint8_t *d_bytes,
+                     int64_t bytes_capacity, int64_t *d_byte_off, void *d_workspace,
+                     size_t workspace_bytes, int32_t *d_status, void *hip_stream);
+
+/* A static English description of a BPE_E* code. */
+const char *bpe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPE_H */

@@ -1,0 +1,260 @@
+"""GPU encode/decode against the oracle, element by element (bit-exact).
+
+Every test calls the HIP path through the C ABI (libbpe.so) and compares
+with the plain CPU oracle on the same seeded inputs.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from byte_level_bpe_pretokenize_amd import Model, _lib
+from workloads import CONFIGS, make_lexicon, small_batch
+
+from gpu_util import (batch_from_docs, check_encode, device, gpu_decode, gpu_encode,
+                      merges_for)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = device()
+    torch.cuda.set_device(d)
+    return d
+
+
+_models = {}
+
+
+def model_pair(k):
+    if k not in _models:
+        m = merges_for(k)
+        _models[k] = (Model(m), O.Table(m))
+    return _models[k]
+
+
+# ------------------------------------------------------ workload shapes ----
+
+SMALL = {1: (4, 20000), 2: (16, 8192), 3: (12, 8192), 4: (6, 16384), 5: (300, 0)}
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_workload_style_small(dev, k):
+    cfg = CONFIGS[k]
+    model, table = model_pair(k)
+    nd, sz = SMALL[k]
+    b = small_batch(cfg, n_docs=nd, doc_bytes=sz, seed=1000 + k, lex=make_lexicon(cfg))
+    ids, off = check_encode(model, table, b.data, b.doc_off)
+    out, boff, st = gpu_decode(model, ids, off)
+    assert st == 0 and np.array_equal(out, b.data) and np.array_equal(boff, b.doc_off)
+
+
+def test_config1_full_document(dev):
+    from workloads import encode_batch_input
+    cfg = CONFIGS[1]
+    model, table = model_pair(1)
+    b = encode_batch_input(cfg, make_lexicon(cfg))
+    assert b.n_docs == 1 and b.n_bytes == 1 << 20
+    ids, off = check_encode(model, table, b.data, b.doc_off)
+    out, boff, st = gpu_decode(model, ids, off)
+    assert st == 0 and np.array_equal(out, b.data)
+
+
+# ------------------------------------------------------------ edge cases ----
+
+EDGE_DOCS = [b"", b"a", b" ", b"  ", b"\t a", b" a", b"a b", b"a  b", b"!!", b"12 34",
+             b"Hello world!", b" \n", b"\x00\x00a\x00", b"\xff\xfe\x80", b"caf\xc3\xa9 \xe4\xbd\xa0",
+             "Grüße 🐈".encode(), b"x" * 40, b" " * 70, b"9" * 50, b"<assistant>"]
+
+
+@pytest.mark.parametrize("k", [1, 4])
+def test_edge_documents(dev, k):
+    model, table = model_pair(k)
+    data, off = batch_from_docs(EDGE_DOCS)
+    ids, ioff = check_encode(model, table, data, off)
+    out, boff, st = gpu_decode(model, ids, ioff)
+    assert st == 0 and np.array_equal(out, data)
+
+
+@pytest.mark.parametrize("n_docs", [0, 1, 5])
+def test_empty_input(dev, n_docs):
+    model, table = model_pair(1)
+    data, off = batch_from_docs([b""] * n_docs)
+    if n_docs == 0:
+        off = np.zeros(1, np.int64)
+    ids, ioff, st = gpu_encode(model, data, off)
+    assert st == 0 and ids.size == 0 and np.all(ioff == 0)
+    out, boff, st = gpu_decode(model, ids, ioff)
+    assert st == 0 and out.size == 0 and np.all(boff == 0)
+
+
+def test_random_bytes_many_docs(dev):
+    model, table = model_pair(3)
+    rng = np.random.default_rng(21)
+    docs = [rng.integers(0, 256, int(rng.integers(0, 900))).astype(np.uint8).tobytes()
+            for _ in range(300)]
+    data, off = batch_from_docs(docs)
+    ids, ioff = check_encode(model, table, data, off)
+    out, _, st = gpu_decode(model, ids, ioff)
+    assert st == 0 and np.array_equal(out, data)
+
+
+def test_chunk_boundaries(dev):
+    # documents and pre-tokens that start, end or straddle 4096-byte chunk
+    # edges, including a single space before a letter run at the edge
+    model, table = model_pair(2)
+    rng = np.random.default_rng(5)
+    base = small_batch(CONFIGS[2], 1, 40000, seed=77).data.tobytes()
+    docs = []
+    for cut in [4095, 4096, 4097, 4094, 8191, 8192, 1, 2, 3]:
+        docs.append(base[:cut])
+    docs.append(b"a" * 4094 + b" bcd" + b" " * 10)
+    docs.append(b"a" * 4095 + b" bcd")
+    docs.append(b"x" * 4096 + b" y")
+    docs.append(b"\t" * 4095 + b" z")
+    for _ in range(20):
+        docs.append(base[: int(rng.integers(1, 12000))])
+    data, off = batch_from_docs(docs)
+    check_encode(model, table, data, off)
+
+
+def test_pathological_runs(dev):
+    # letter runs around every tier limit, and runs longer than the window so
+    # the pre-token continues into later chunks
+    model, table = model_pair(4)
+    lens = [1, 2, 31, 32, 33, 63, 64, 65, 66, 100, 1000, 4095, 4096, 4097, 4160, 4161, 5000,
+            8192, 20000, 70000]
+    docs = [b"a" * n for n in lens] + [b" " + b"q" * n for n in lens]
+    rng = np.random.default_rng(9)
+    for n in [33, 100, 2048, 5000, 30000]:
+        docs.append(rng.integers(48, 58, n).astype(np.uint8).tobytes())
+    docs.append(b"lead " + b"z" * 12000 + b" tail")
+    data, off = batch_from_docs(docs)
+    ids, ioff = check_encode(model, table, data, off)
+    out, _, st = gpu_decode(model, ids, ioff)
+    assert st == 0 and np.array_equal(out, data)
+
+
+def test_same_pair_runs(dev):
+    # [a,a,a] -> [aa,a]: runs of one pair merge left to right without overlap
+    for merges in ([[97, 97]], [[97, 97], [256, 256], [257, 257]], [[97, 97], [256, 97]]):
+        model, table = Model(merges), O.Table(merges)
+        docs = [b"a" * n for n in range(1, 80)] + [b"a" * n for n in (127, 128, 129, 4100, 9001)]
+        data, off = batch_from_docs(docs)
+        ids, ioff = check_encode(model, table, data, off)
+        if merges == [[97, 97]]:
+            for d, n in enumerate(range(1, 80)):
+                assert ids[ioff[d]:ioff[d + 1]].tolist() == [256] * (n // 2) + [97] * (n % 2)
+
+
+def _random_acyclic_table(rng, n, alphabet=(97, 98, 99)):
+    # operands may be symbols made by later ranks (ranks out of creation order)
+    syms = list(alphabet)
+    pairs = []
+    seen = set()
+    while len(pairs) < n:
+        l, r = int(rng.choice(syms)), int(rng.choice(syms))
+        if (l, r) in seen:
+            continue
+        seen.add((l, r))
+        pairs.append((l, r))
+        syms.append(256 + len(pairs) - 1)
+    perm = rng.permutation(n)              # new rank of creation step i
+    remap = {256 + i: 256 + int(perm[i]) for i in range(n)}
+    merges = [None] * n
+    for i, (l, r) in enumerate(pairs):
+        merges[int(perm[i])] = [remap.get(l, l), remap.get(r, r)]
+    return merges
+
+
+def test_out_of_order_tables(dev):
+    # all-occurrences rounds must match the oracle on tables whose ranks are
+    # not in creation order
+    rng = np.random.default_rng(13)
+    strings = [bytes(s) for n in range(1, 8) for s in itertools.product(b"abc", repeat=n)]
+    for trial in range(6):
+        merges = _random_acyclic_table(rng, int(rng.integers(2, 9)))
+        assert O.validate(merges) == O.ORA_OK
+        model, table = Model(merges), O.Table(merges)
+        docs = strings + [b"".join(rng.choice([b"a", b"b", b"c"], 200)) for _ in range(20)]
+        data, off = batch_from_docs(docs)
+        check_encode(model, table, data, off)
+
+
+def test_id_map_permutation(dev):
+    m = merges_for(1)
+    V = 256 + m.shape[0]
+    perm = np.random.default_rng(3).permutation(V).astype(np.int32)
+    model, table = Model(m, perm), O.Table(m, perm)
+    b = small_batch(CONFIGS[1], 3, 5000, seed=4)
+    ids, off = check_encode(model, table, b.data, b.doc_off)
+    base, _ = table.encode_batch(b.data, b.doc_off)
+    out, _, st = gpu_decode(model, ids, off)
+    assert st == 0 and np.array_equal(out, b.data)
+    # sparse, non-contiguous IDs
+    sparse = (np.arange(V, dtype=np.int64) * 37 + 11).astype(np.int32)
+    model2, table2 = Model(m, sparse), O.Table(m, sparse)
+    ids2, off2 = check_encode(model2, table2, b.data, b.doc_off)
+    out2, _, st2 = gpu_decode(model2, ids2, off2)
+    assert st2 == 0 and np.array_equal(out2, b.data)
+
+
+def test_unaligned_input(dev):
+    model, table = model_pair(2)
+    b = small_batch(CONFIGS[2], 4, 9000, seed=8)
+    want, want_off = table.encode_batch(b.data, b.doc_off)
+    for shift in (1, 3, 8, 15):
+        got, off, st = gpu_encode(model, b.data, b.doc_off, data_offset=shift)
+        assert st == 0 and np.array_equal(got, want) and np.array_equal(off, want_off)
+
+
+def test_ids_capacity_overflow(dev):
+    model, table = model_pair(1)
+    b = small_batch(CONFIGS[1], 3, 6000, seed=2)
+    want, _ = table.encode_batch(b.data, b.doc_off)
+    cap = want.size // 2
+    got, _, st = gpu_encode(model, b.data, b.doc_off, cap=cap)
+    assert st & _lib.STATUS_IDS_CAPACITY
+    assert np.array_equal(got[:cap], want[:cap])
+
+
+@pytest.mark.parametrize("bad", ["first", "order", "last"])
+def test_bad_doc_offsets(dev, bad):
+    model, _ = model_pair(1)
+    data, off = batch_from_docs([b"hello there", b"abc", b"more text here"])
+    off = off.copy()
+    if bad == "first":
+        off[0] = 1
+    elif bad == "order":
+        off[1], off[2] = off[2], off[1]
+    else:
+        off[-1] -= 1
+    _, _, st = gpu_encode(model, data, off)
+    assert st & _lib.STATUS_BAD_DOC_OFFSETS
+
+
+def test_decode_bad_ids_and_capacity(dev):
+    model, table = model_pair(1)
+    V = model.vocab_size
+    ids = np.array([104, 105, V, 32, -1, 256], dtype=np.int32)
+    _, _, st = gpu_decode(model, ids, np.array([0, ids.size], np.int64))
+    assert st & _lib.STATUS_BAD_ID
+    good = np.array([104, 105, 300, 301], dtype=np.int32)
+    want = table.decode(good)
+    out, _, st = gpu_decode(model, good, np.array([0, 4], np.int64), cap=len(want) - 1)
+    assert st & _lib.STATUS_BYTES_CAPACITY
+    out, boff, st = gpu_decode(model, good, np.array([0, 2, 2, 4], np.int64))
+    assert st == 0 and out.tobytes() == want
+    wb, wboff = table.decode_batch(good, np.array([0, 2, 2, 4], np.int64))
+    assert np.array_equal(boff, wboff)
+
+
+def test_determinism(dev):
+    model, table = model_pair(2)
+    b = small_batch(CONFIGS[2], 64, 16384, seed=12)
+    a1, o1, s1 = gpu_encode(model, b.data, b.doc_off)
+    a2, o2, s2 = gpu_encode(model, b.data, b.doc_off)
+    assert s1 == 0 and s2 == 0 and np.array_equal(a1, a2) and np.array_equal(o1, o2)
