@@ -1,0 +1,202 @@
+"""Benchmark: byte-level BPE encode throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload throughput] [--gpus 1]
+
+One step is one bpe_encode_batch call over the whole batch (byte-class scan,
+pre-token merge, ID compaction and per-document offsets), with the input
+already resident in HBM.  Prints one JSON line.  The default workload is the
+throughput workload: 4,096 documents of 64 KiB (256 MiB) with the
+32,000-merge table.  The CPU baseline is the oracle, single-threaded, on the
+first documents of the same batch; its IDs are checked against the GPU's.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="throughput",
+                    choices=["tiny", "throughput", "multilingual", "adversarial", "serving"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(merges, batch, ids_gpu, id_off_gpu, target_s):
+    """The oracle, as it stands, on a bounded prefix of the batch's documents;
+    also checks those documents' GPU IDs element by element."""
+    import oracle as O
+    table = O.Table(merges)
+    # size the sample from a short calibration run
+    nd = batch.n_docs
+    probe = max(1, min(nd, 4))
+    t0 = time.perf_counter()
+    table.encode_batch(batch.data[:batch.doc_off[probe]], batch.doc_off[:probe + 1])
+    dt = max(1e-6, time.perf_counter() - t0)
+    rate = batch.doc_off[probe] / dt
+    want_bytes = rate * target_s
+    k = int(np.searchsorted(batch.doc_off, want_bytes, side="right"))
+    k = max(1, min(nd, k))
+    n = int(batch.doc_off[k])
+    t0 = time.perf_counter()
+    ids, off = table.encode_batch(batch.data[:n], batch.doc_off[:k + 1])
+    dt = time.perf_counter() - t0
+    ok = bool(np.array_equal(ids, ids_gpu[:ids.size]) and np.array_equal(off, id_off_gpu[:k + 1]))
+    return {
+        "value": round(n / dt / 1e6, 3),
+        "unit": "MB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {k} of {nd} documents ({n} bytes) of the same batch, {dt:.1f} s, "
+                  f"one thread; IDs equal to the GPU's: {ok}",
+        "tokens_per_s": round(ids.size / dt, 1),
+        "parity_ok": ok,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(documents shard independently across GPUs, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from byte_level_bpe_pretokenize_amd import Model
+    from workloads import WORKLOADS, encode_batch_input, make_lexicon
+
+    cfg = WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    batch = encode_batch_input(cfg, make_lexicon(cfg))
+    t_gen = time.perf_counter() - t_gen
+    merges = np.load(os.path.join(ROOT, "assets", f"merges_{args.workload}.npy"), allow_pickle=False)
+    print(f"# generated {batch.n_bytes} bytes in {batch.n_docs} documents in {t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    model = Model(merges)
+    N, D = batch.n_bytes, batch.n_docs
+    data = torch.from_numpy(batch.data).to(dev)
+    doc_off = torch.from_numpy(batch.doc_off).to(dev)
+    ids = torch.empty(N, dtype=torch.int32, device=dev)
+    id_off = torch.empty(D + 1, dtype=torch.int64, device=dev)
+    ws = torch.empty(model.encode_workspace_bytes(N, D), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        model.encode_batch_into(data, doc_off, ids, id_off, ws, status, stream)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    st = int(status.item())
+    if st:
+        raise SystemExit(f"device status {st:#x} after warm-up")
+    T = int(id_off[-1].item())
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    st = int(status.item())
+    if st:
+        raise SystemExit(f"device status {st:#x} in the timed region")
+
+    sec = ms / 1e3
+    alg_bytes = N + 4 * T + 16 * (D + 1)
+    achieved = alg_bytes / sec / 1e9
+
+    # decode of the same IDs (round trip), timed the same way
+    dec = {}
+    mtb = model.max_token_bytes
+    if mtb > 0:
+        out = torch.empty(N + 64, dtype=torch.uint8, device=dev)
+        byte_off = torch.empty(D + 1, dtype=torch.int64, device=dev)
+        dws = torch.empty(max(1, model.decode_workspace_bytes(T, D)), dtype=torch.uint8, device=dev)
+        dstat = torch.zeros(1, dtype=torch.int32, device=dev)
+        ids_t = ids[:T]
+        for _ in range(2):
+            model.decode_batch_into(ids_t, id_off, out, byte_off, dws, dstat, stream)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            model.decode_batch_into(ids_t, id_off, out, byte_off, dws, dstat, stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        dms = start.elapsed_time(stop) / args.steps
+        rt = bool(int(dstat.item()) == 0 and torch.equal(out[:N], data)
+                  and torch.equal(byte_off, doc_off))
+        dec = {"ms": round(dms, 4), "output_MB_per_s": round(N / (dms / 1e3) / 1e6, 1),
+               "achieved_GB_per_s": round((4 * T + N + 16 * (D + 1)) / (dms / 1e3) / 1e9, 1),
+               "round_trip_ok": rt}
+
+    ids_np = ids[:T].cpu().numpy()
+    id_off_np = id_off.cpu().numpy()
+    import hashlib
+    cpu, fnv = None, None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(merges, batch, ids_np, id_off_np, args.cpu_seconds)
+        import oracle as O
+        fnv = f"{O.ids_fnv(ids_np):016x}"
+
+    line = {
+        "metric": "BPE encode input MB/s and tokens/s on 1 MI355X; % of HBM roofline",
+        "value": round(N / sec / 1e6, 1),
+        "unit": "MB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {D} documents, {N} bytes, {merges.shape[0]} merges",
+            "n_bytes": N, "n_docs": D, "n_merges": int(merges.shape[0]), "tokens": T,
+        },
+        "tokens_per_s": round(T / sec, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": alg_bytes,
+        },
+        "cpu_baseline": cpu,
+        "ids_fnv1a64": fnv,
+        "decode": dec,
+        "ids_sha256": hashlib.sha256(ids_np.tobytes()).hexdigest()[:16],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

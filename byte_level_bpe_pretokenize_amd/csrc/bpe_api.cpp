@@ -22,6 +22,10 @@ struct bpe_model {
   uint64_t *d_table = nullptr;
   int table_bits = 0;
   int32_t *d_id_map = nullptr;
+  int32_t *d_pair_rank = nullptr;   // [65536] ranks of byte pairs
+  uint4 *d_words = nullptr;         // word table (2 uint4 per slot), or nullptr
+  int word_bits = 0;
+  int64_t n_words = 0;
   // decode tables
   bool decode_ok = false;
   int64_t max_token = 1;
@@ -37,6 +41,8 @@ void free_model(bpe_model *m) {
   if (!m) return;
   if (m->d_table) (void)hipFree(m->d_table);
   if (m->d_id_map) (void)hipFree(m->d_id_map);
+  if (m->d_pair_rank) (void)hipFree(m->d_pair_rank);
+  if (m->d_words) (void)hipFree(m->d_words);
   if (m->d_exp_off) (void)hipFree(m->d_exp_off);
   if (m->d_exp_bytes) (void)hipFree(m->d_exp_bytes);
   if (m->d_inv_map) (void)hipFree(m->d_inv_map);
@@ -59,6 +65,138 @@ int upload(T **dst, const T *src, size_t count, hipStream_t stream) {
 bool on_model_device(const bpe_model *m) {
   int dev = -1;
   return hipGetDevice(&dev) == hipSuccess && dev == m->device;
+}
+
+// Queue the encode kernels.  `words` selects the word table (nullptr: every
+// pre-token runs the merge loop); `id_map` the output mapping.
+int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
+                   const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids, int64_t ids_capacity,
+                   int64_t *d_id_off, void *d_workspace, int32_t *d_status, const uint4 *words,
+                   const int32_t *id_map, hipStream_t stream) {
+  if (n_bytes == 0)
+    return launch_empty(d_doc_off, n_docs, BPE_STATUS_BAD_DOC_OFFSETS, d_id_off, d_status,
+                        stream) == hipSuccess
+               ? BPE_OK
+               : BPE_EHIP;
+  const EncLayout L = enc_layout(n_bytes);
+  uint8_t *ws = (uint8_t *)d_workspace;
+  EncodeArgs a;
+  a.bytes = d_bytes;
+  a.n_bytes = n_bytes;
+  a.doc_off = d_doc_off;
+  a.n_docs = n_docs;
+  a.ids = d_ids;
+  a.ids_cap = ids_capacity;
+  a.id_off = d_id_off;
+  a.table = model->d_table;
+  a.table_bits = model->table_bits;
+  a.id_map = id_map;
+  a.pair_rank = model->d_pair_rank;
+  a.words = words;
+  a.word_bits = model->word_bits;
+  a.ticket = (uint32_t *)(ws + L.ticket);
+  a.flags = (uint64_t *)(ws + L.flags);
+  a.gsym = (int32_t *)(ws + L.gsym);
+  a.grank = (int32_t *)(ws + L.grank);
+  a.status = d_status;
+  a.n_chunks = enc_chunks(n_bytes);
+  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, stream) != hipSuccess) return BPE_EHIP;
+  if (launch_encode(a, stream) != hipSuccess) return BPE_EHIP;
+  return BPE_OK;
+}
+
+// The word table: every symbol whose byte expansion (2..kWordMax bytes)
+// encodes to exactly that symbol.  The expansions are encoded on the device
+// by the same kernels, with the merge loop for every pre-token; the host only
+// arranges the results into the hash table.
+int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
+                     const std::vector<uint8_t> &exp_bytes, hipStream_t stream) {
+  std::vector<int32_t> cand;
+  std::vector<int64_t> doc_off(1, 0);
+  for (int64_t v = 256; v < m->V; ++v) {
+    const int64_t n = exp_off[(size_t)v + 1] - exp_off[(size_t)v];
+    if (n >= 2 && n <= kWordMax) {
+      cand.push_back((int32_t)v);
+      doc_off.push_back(doc_off.back() + n);
+    }
+  }
+  if (cand.empty()) return BPE_OK;
+  const int64_t N = doc_off.back(), D = (int64_t)cand.size();
+  std::vector<uint8_t> text((size_t)N);
+  for (int64_t k = 0; k < D; ++k) {
+    const int64_t v = cand[(size_t)k];
+    std::memcpy(&text[(size_t)doc_off[(size_t)k]], &exp_bytes[(size_t)exp_off[(size_t)v]],
+                (size_t)(doc_off[(size_t)k + 1] - doc_off[(size_t)k]));
+  }
+  const EncLayout L = enc_layout(N);
+  uint8_t *d_text = nullptr, *d_ws = nullptr;
+  int64_t *d_doc = nullptr, *d_ioff = nullptr;
+  int32_t *d_ids = nullptr, *d_status = nullptr;
+  int rc = BPE_OK;
+  if (hipMalloc((void **)&d_text, (size_t)N) != hipSuccess ||
+      hipMalloc((void **)&d_doc, sizeof(int64_t) * (size_t)(D + 1)) != hipSuccess ||
+      hipMalloc((void **)&d_ioff, sizeof(int64_t) * (size_t)(D + 1)) != hipSuccess ||
+      hipMalloc((void **)&d_ids, sizeof(int32_t) * (size_t)N) != hipSuccess ||
+      hipMalloc((void **)&d_status, sizeof(int32_t)) != hipSuccess ||
+      hipMalloc((void **)&d_ws, L.total) != hipSuccess)
+    rc = BPE_ENOMEM;
+  std::vector<int64_t> ioff((size_t)D + 1);
+  std::vector<int32_t> ids((size_t)N);
+  int32_t status = -1;
+  if (rc == BPE_OK &&
+      (hipMemcpyAsync(d_text, text.data(), (size_t)N, hipMemcpyHostToDevice, stream) != hipSuccess ||
+       hipMemcpyAsync(d_doc, doc_off.data(), sizeof(int64_t) * (size_t)(D + 1),
+                      hipMemcpyHostToDevice, stream) != hipSuccess))
+    rc = BPE_EHIP;
+  if (rc == BPE_OK)
+    rc = enqueue_encode(m, d_text, N, d_doc, D, d_ids, N, d_ioff, d_ws, d_status, nullptr,
+                        nullptr, stream);
+  if (rc == BPE_OK &&
+      (hipMemcpyAsync(ioff.data(), d_ioff, sizeof(int64_t) * (size_t)(D + 1), hipMemcpyDeviceToHost,
+                      stream) != hipSuccess ||
+       hipMemcpyAsync(ids.data(), d_ids, sizeof(int32_t) * (size_t)N, hipMemcpyDeviceToHost,
+                      stream) != hipSuccess ||
+       hipMemcpyAsync(&status, d_status, sizeof(int32_t), hipMemcpyDeviceToHost, stream) !=
+           hipSuccess ||
+       hipStreamSynchronize(stream) != hipSuccess))
+    rc = BPE_EHIP;
+  (void)hipFree(d_text);
+  (void)hipFree(d_doc);
+  (void)hipFree(d_ioff);
+  (void)hipFree(d_ids);
+  (void)hipFree(d_status);
+  (void)hipFree(d_ws);
+  if (rc != BPE_OK) return rc;
+  if (status != 0) return BPE_EHIP;
+
+  int64_t n_keep = 0;
+  for (int64_t k = 0; k < D; ++k)
+    n_keep += ioff[(size_t)k + 1] - ioff[(size_t)k] == 1 && ids[(size_t)ioff[(size_t)k]] == cand[(size_t)k];
+  int bits = 8;
+  while (((int64_t)1 << bits) < 2 * n_keep) ++bits;
+  const uint32_t mask = (1u << bits) - 1u;
+  std::vector<uint32_t> slots((size_t)8 << bits, 0u);
+  for (int64_t k = 0; k < D; ++k) {
+    if (!(ioff[(size_t)k + 1] - ioff[(size_t)k] == 1 && ids[(size_t)ioff[(size_t)k]] == cand[(size_t)k]))
+      continue;
+    const int len = (int)(doc_off[(size_t)k + 1] - doc_off[(size_t)k]);
+    uint32_t w[kWordWords] = {0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < len; ++j)
+      w[j >> 2] |= (uint32_t)text[(size_t)doc_off[(size_t)k] + j] << (8 * (j & 3));
+    const uint32_t h = word_hash(w, len);
+    uint32_t i = h & mask;
+    while (slots[(size_t)8 * i] != 0u) i = (i + 1) & mask;
+    uint32_t *slot = &slots[(size_t)8 * i];
+    slot[0] = word_tag(h, len);
+    slot[1] = (uint32_t)cand[(size_t)k];
+    for (int j = 0; j < kWordWords; ++j) slot[2 + j] = w[j];
+  }
+  rc = upload(reinterpret_cast<uint32_t **>(&m->d_words), slots.data(), slots.size(), stream);
+  if (rc == BPE_OK) {
+    m->word_bits = bits;
+    m->n_words = n_keep;
+  }
+  return rc;
 }
 
 }  // namespace
@@ -162,6 +300,13 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
   }
   int rc = upload(&m->d_table, table.data(), table.size(), stream);
   if (rc == BPE_OK && id_map) rc = upload(&m->d_id_map, id_map, (size_t)V, stream);
+  if (rc == BPE_OK) {
+    std::vector<int32_t> pr((size_t)65536, kRankInf);
+    for (int64_t r = 0; r < R; ++r)
+      if (merges[2 * r] < 256 && merges[2 * r + 1] < 256)
+        pr[(size_t)(merges[2 * r] * 256 + merges[2 * r + 1])] = (int32_t)r;
+    rc = upload(&m->d_pair_rank, pr.data(), pr.size(), stream);
+  }
 
   // decode tables: byte expansion of every symbol, and the ID -> symbol map
   int64_t total = 0;
@@ -193,6 +338,7 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
       rc = upload(&m->d_inv_map, inv.data(), inv.size(), stream);
     }
     m->decode_ok = rc == BPE_OK;
+    if (rc == BPE_OK) rc = build_word_table(m, exp_off, exp_bytes, stream);
   }
   if (rc == BPE_OK && hipStreamSynchronize(stream) != hipSuccess) rc = BPE_EHIP;
   if (rc != BPE_OK) {
@@ -228,34 +374,9 @@ int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_b
   if (enc_chunks(n_bytes) > INT32_MAX) return BPE_EINVAL;
   if (!on_model_device(model)) return BPE_EINVAL;
   hipStream_t stream = (hipStream_t)hip_stream;
-  if (n_bytes == 0)
-    return launch_empty(d_doc_off, n_docs, BPE_STATUS_BAD_DOC_OFFSETS, d_id_off, d_status,
-                        stream) == hipSuccess
-               ? BPE_OK
-               : BPE_EHIP;
-  const EncLayout L = enc_layout(n_bytes);
-  if (workspace_bytes < L.total) return BPE_EWORKSPACE;
-  uint8_t *ws = (uint8_t *)d_workspace;
-  EncodeArgs a;
-  a.bytes = d_bytes;
-  a.n_bytes = n_bytes;
-  a.doc_off = d_doc_off;
-  a.n_docs = n_docs;
-  a.ids = d_ids;
-  a.ids_cap = ids_capacity;
-  a.id_off = d_id_off;
-  a.table = model->d_table;
-  a.table_bits = model->table_bits;
-  a.id_map = model->d_id_map;
-  a.ticket = (uint32_t *)(ws + L.ticket);
-  a.flags = (uint64_t *)(ws + L.flags);
-  a.gsym = (int32_t *)(ws + L.gsym);
-  a.grank = (int32_t *)(ws + L.grank);
-  a.status = d_status;
-  a.n_chunks = enc_chunks(n_bytes);
-  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, stream) != hipSuccess) return BPE_EHIP;
-  if (launch_encode(a, stream) != hipSuccess) return BPE_EHIP;
-  return BPE_OK;
+  if (n_bytes > 0 && workspace_bytes < enc_layout(n_bytes).total) return BPE_EWORKSPACE;
+  return enqueue_encode(model, d_bytes, n_bytes, d_doc_off, n_docs, d_ids, ids_capacity, d_id_off,
+                        d_workspace, d_status, model->d_words, model->d_id_map, stream);
 }
 
 size_t bpe_decode_workspace_bytes(const bpe_model *model, int64_t n_ids, int64_t n_docs) {

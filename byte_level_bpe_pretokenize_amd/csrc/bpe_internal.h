@@ -26,6 +26,28 @@ __host__ __device__ inline uint64_t pair_hash(uint64_t key, int bits) {
   return (key * 0x9E3779B97F4A7C15ull) >> (64 - bits);
 }
 
+// ---- word table -----------------------------------------------------------
+// Read-only table built at load time: a pre-token whose bytes equal the
+// expansion of symbol s (2..kWordMax bytes), where encoding that expansion
+// yields exactly [s], encodes to [s] without running the merge loop.  One
+// 32-byte slot per entry: {tag, symbol, key[6]}; tag = (hash & ~0xff) | len
+// (0 = empty); key = the bytes as six little-endian words, zero padded.
+constexpr int kWordMax = 24;
+constexpr int kWordWords = kWordMax / 4;
+
+__host__ __device__ inline uint32_t word_hash(const uint32_t *w, int len) {
+  uint32_t h = 0x811C9DC5u ^ ((uint32_t)len * 0x01000193u);
+  for (int i = 0; i < kWordWords; ++i) {
+    h = (h ^ w[i]) * 0x9E3779B1u;
+    h ^= h >> 16;
+  }
+  return h;
+}
+
+__host__ __device__ inline uint32_t word_tag(uint32_t h, int len) {
+  return (h & 0xFFFFFF00u) | (uint32_t)len;
+}
+
 // ---- look-back flags ----------------------------------------------------
 // One 64-bit word per chunk: bits 62..63 state, bits 0..61 value.
 constexpr uint64_t kFlagAgg = 1ull << 62;     // value = this chunk's count
@@ -87,6 +109,9 @@ struct EncodeArgs {
   const uint64_t *table;
   int table_bits;
   const int32_t *id_map;  // nullptr = identity
+  const int32_t *pair_rank;  // [65536]: rank of the byte pair (a, b) at a * 256 + b
+  const uint4 *words;        // word table: 2 uint4 per slot; nullptr = none
+  int word_bits;
   uint32_t *ticket;
   uint64_t *flags;
   int32_t *gsym;

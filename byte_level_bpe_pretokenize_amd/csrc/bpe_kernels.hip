@@ -227,7 +227,7 @@ __device__ int64_t wave_lookback(uint64_t *flags, int64_t c, int64_t agg) {
 struct EncShared {
   int32_t Y[WIN];     // symbols at their byte positions (kDead: no symbol)
   int32_t RK[WIN];    // RK[p] = rank of the pair starting at p
-  alignas(16) uint8_t B[16 + WIN];  // B[16 + p] = byte at window position p
+  alignas(16) uint8_t B[16 + WIN + 32];  // B[16 + p] = byte at window position p
   uint32_t SB[SB_WORDS];            // pre-token start bits, positions [0, WIN]
   uint32_t DB[DB_WORDS];            // document start bits, positions [-32, WIN)
   int32_t excl[WG];                 // per-lane exclusive token counts
@@ -236,6 +236,8 @@ struct EncShared {
   int64_t red64[8];
   int32_t longs[kMaxLong];
   int32_t n_long;
+  uint32_t miss[kChunk / 2 + 4];    // pre-tokens for the merge loop: start | len << 16
+  int32_t n_miss;
   int64_t chunk;
   int64_t d_lo, o_lo, o_hi;
   int64_t base;
@@ -280,14 +282,53 @@ __device__ int block_next_start(EncShared &s, int from) {
   return block_min<WG>(cand, s.red);
 }
 
+// The bytes of the pre-token at window position st (len <= kWordMax) as six
+// little-endian words, zero padded.
+__device__ __forceinline__ void pretoken_words(const EncShared &s, int st, int len,
+                                               uint32_t w[kWordWords]) {
+  const int b0 = 16 + st;
+  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
+  const int q = b0 >> 2;
+  const uint32_t sh = (uint32_t)(b0 & 3);
+  uint32_t raw[kWordWords + 1];
+#pragma unroll
+  for (int i = 0; i <= kWordWords; ++i) raw[i] = B32[q + i];
+#pragma unroll
+  for (int i = 0; i < kWordWords; ++i) {
+    const uint32_t v = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
+    const int valid = len - 4 * i;
+    const uint32_t m = valid >= 4 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : ((1u << (8 * valid)) - 1u));
+    w[i] = v & m;
+  }
+}
+
+// Symbol stored for these bytes in the word table, or -1.
+__device__ __forceinline__ int32_t word_lookup(const uint4 *__restrict__ tab, int bits,
+                                               const uint32_t w[kWordWords], int len) {
+  const uint32_t h = word_hash(w, len);
+  const uint32_t tag = word_tag(h, len);
+  const uint32_t mask = (1u << bits) - 1u;
+  uint32_t i = h & mask;
+  for (;;) {
+    const uint4 a = tab[2 * i];
+    if (a.x == 0) return -1;
+    if (a.x == tag && a.z == w[0] && a.w == w[1]) {
+      const uint4 b = tab[2 * i + 1];
+      if (b.x == w[2] && b.y == w[3] && b.z == w[4] && b.w == w[5]) return (int32_t)a.y;
+    }
+    i = (i + 1) & mask;
+  }
+}
+
 // Merge one short pre-token of n symbols in place at Y[0..n), RK[0..n) (one
 // lane).  Each round takes the lowest rank r present and rewrites the
 // sequence left to right, merging every pair whose rank is r unless its left
 // symbol was just consumed; then only pairs touching the new symbol are
 // probed again.  Leaves kDead after the result.
 __device__ void lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_t *tab,
-                           const int bits) {
-  for (int i = 0; i + 1 < len; ++i) RK[i] = rank_of(tab, bits, Y[i], Y[i + 1]);
+                           const int bits, const int32_t *__restrict__ pair_rank) {
+  // the symbols are still bytes: their ranks come from the direct table
+  for (int i = 0; i + 1 < len; ++i) RK[i] = pair_rank[(Y[i] << 8) | Y[i + 1]];
   RK[len - 1] = kRankInf;
   int n = len;
   for (;;) {
@@ -321,10 +362,10 @@ __device__ void lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_
 // a pair (x, x)) merge at even offsets from the run start, and survivors are
 // compacted in place tile by tile.  Returns the final symbol count.
 __device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const uint64_t *tab, int bits,
-                            EncShared &s) {
+                            const int32_t *__restrict__ pair_rank, EncShared &s) {
   const int tid = threadIdx.x;
   for (int64_t i = tid; i < n; i += WG)
-    RK[i] = (i + 1 < n) ? rank_of(tab, bits, Y[i], Y[i + 1]) : kRankInf;
+    RK[i] = (i + 1 < n) ? pair_rank[(Y[i] << 8) | Y[i + 1]] : kRankInf;
   __syncthreads();
   for (;;) {
     int32_t r = kRankInf;
@@ -560,7 +601,12 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   }
   __syncthreads();
 
-  // 3. lane tier: pre-tokens that start in this lane's 16 bytes
+  // 3. lane tier: pre-tokens that start in this lane's 16 bytes.  A single
+  //    byte is its own token; a pre-token found in the word table takes its
+  //    symbol; the rest go to a list that all lanes then share for the merge
+  //    loop, so busy lanes are packed together.
+  if (tid == 0) s.n_miss = 0;
+  __syncthreads();
   if (16 * tid < nown) {
     uint32_t m = sb16(s, tid);
     const int lim = nown - 16 * tid;
@@ -572,22 +618,43 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
       const int e = next_start_bounded(s, st + 1, min(st + kLaneMax, WIN));
       if (e < 0) {
         const int k = atomicAdd(&s.n_long, 1);
-        s.longs[k] = st;
+        if (k < kMaxLong) s.longs[k] = st;
         continue;
       }
-      lane_merge(s.Y + st, s.RK + st, e - st, a.table, a.table_bits);
+      const int len = e - st;
+      if (len == 1) continue;
+      if (a.words && len <= kWordMax) {
+        uint32_t w[kWordWords];
+        pretoken_words(s, st, len, w);
+        const int32_t sym = word_lookup(a.words, a.word_bits, w, len);
+        if (sym >= 0) {
+          s.Y[st] = sym;
+          for (int j = 1; j < len; ++j) s.Y[st + j] = kDead;
+          continue;
+        }
+      }
+      const int k = atomicAdd(&s.n_miss, 1);
+      s.miss[k] = (uint32_t)st | ((uint32_t)len << 16);
+    }
+  }
+  __syncthreads();
+  {
+    const int n_miss = s.n_miss;
+    for (int k = tid; k < n_miss; k += WG) {
+      const int st = (int)(s.miss[k] & 0xFFFFu), len = (int)(s.miss[k] >> 16);
+      lane_merge(s.Y + st, s.RK + st, len, a.table, a.table_bits, a.pair_rank);
     }
   }
   __syncthreads();
 
   // 4. workgroup tier: longer pre-tokens inside the window, then the one that
   //    runs past it (in the position-indexed global scratch)
-  const int n_long = s.n_long;
+  const int n_long = min(s.n_long, kMaxLong);
   for (int k = 0; k < n_long; ++k) {
     const int st = s.longs[k];
     const int e = block_next_start(s, st + 1);
     const int64_t len = e - st;
-    const int64_t nt = wg_merge(s.Y + st, s.RK + st, len, a.table, a.table_bits, s);
+    const int64_t nt = wg_merge(s.Y + st, s.RK + st, len, a.table, a.table_bits, a.pair_rank, s);
     for (int64_t j = nt + tid; j < len; j += WG) s.Y[st + j] = kDead;
     __syncthreads();
   }
@@ -596,7 +663,7 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
     const int64_t ge = block_global_end(a, s, gs, c0 + WIN);
     for (int64_t q = gs + tid; q < ge; q += WG) a.gsym[q] = a.bytes[q];
     __syncthreads();
-    const int64_t nt = wg_merge(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits, s);
+    const int64_t nt = wg_merge(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits, a.pair_rank, s);
     if (tid == 0) {
       s.ov_start = gs;
       s.ov_ntok = nt;

@@ -12,8 +12,8 @@ from byte_level_bpe_pretokenize_amd import Model, _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def merges_for(k: int) -> np.ndarray:
-    return np.load(os.path.join(ROOT, "assets", f"merges_c{k}.npy"), allow_pickle=False)
+def merges_for(name: str) -> np.ndarray:
+    return np.load(os.path.join(ROOT, "assets", f"merges_{name}.npy"), allow_pickle=False)
 
 
 def device() -> torch.device:

@@ -11,7 +11,7 @@ import torch
 
 import oracle as O
 from byte_level_bpe_pretokenize_amd import Model, _lib
-from workloads import CONFIGS, make_lexicon, small_batch
+from workloads import WORKLOADS, make_lexicon, small_batch
 
 from gpu_util import (batch_from_docs, check_encode, device, gpu_decode, gpu_encode,
                       merges_for)
@@ -38,24 +38,26 @@ def model_pair(k):
 
 # ------------------------------------------------------ workload shapes ----
 
-SMALL = {1: (4, 20000), 2: (16, 8192), 3: (12, 8192), 4: (6, 16384), 5: (300, 0)}
+SMALL = {"tiny": (4, 20000), "throughput": (16, 8192), "multilingual": (12, 8192),
+         "adversarial": (6, 16384), "serving": (300, 0)}
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", list(SMALL))
 def test_workload_style_small(dev, k):
-    cfg = CONFIGS[k]
+    cfg = WORKLOADS[k]
     model, table = model_pair(k)
     nd, sz = SMALL[k]
-    b = small_batch(cfg, n_docs=nd, doc_bytes=sz, seed=1000 + k, lex=make_lexicon(cfg))
+    b = small_batch(cfg, n_docs=nd, doc_bytes=sz, seed=1000 + list(SMALL).index(k),
+                    lex=make_lexicon(cfg))
     ids, off = check_encode(model, table, b.data, b.doc_off)
     out, boff, st = gpu_decode(model, ids, off)
     assert st == 0 and np.array_equal(out, b.data) and np.array_equal(boff, b.doc_off)
 
 
-def test_config1_full_document(dev):
+def test_tiny_full_document(dev):
     from workloads import encode_batch_input
-    cfg = CONFIGS[1]
-    model, table = model_pair(1)
+    cfg = WORKLOADS["tiny"]
+    model, table = model_pair("tiny")
     b = encode_batch_input(cfg, make_lexicon(cfg))
     assert b.n_docs == 1 and b.n_bytes == 1 << 20
     ids, off = check_encode(model, table, b.data, b.doc_off)
@@ -70,7 +72,7 @@ EDGE_DOCS = [b"", b"a", b" ", b"  ", b"\t a", b" a", b"a b", b"a  b", b"!!", b"1
              "Grüße 🐈".encode(), b"x" * 40, b" " * 70, b"9" * 50, b"<assistant>"]
 
 
-@pytest.mark.parametrize("k", [1, 4])
+@pytest.mark.parametrize("k", ["tiny", "adversarial"])
 def test_edge_documents(dev, k):
     model, table = model_pair(k)
     data, off = batch_from_docs(EDGE_DOCS)
@@ -81,7 +83,7 @@ def test_edge_documents(dev, k):
 
 @pytest.mark.parametrize("n_docs", [0, 1, 5])
 def test_empty_input(dev, n_docs):
-    model, table = model_pair(1)
+    model, table = model_pair("tiny")
     data, off = batch_from_docs([b""] * n_docs)
     if n_docs == 0:
         off = np.zeros(1, np.int64)
@@ -92,7 +94,7 @@ def test_empty_input(dev, n_docs):
 
 
 def test_random_bytes_many_docs(dev):
-    model, table = model_pair(3)
+    model, table = model_pair("multilingual")
     rng = np.random.default_rng(21)
     docs = [rng.integers(0, 256, int(rng.integers(0, 900))).astype(np.uint8).tobytes()
             for _ in range(300)]
@@ -105,9 +107,9 @@ def test_random_bytes_many_docs(dev):
 def test_chunk_boundaries(dev):
     # documents and pre-tokens that start, end or straddle 4096-byte chunk
     # edges, including a single space before a letter run at the edge
-    model, table = model_pair(2)
+    model, table = model_pair("throughput")
     rng = np.random.default_rng(5)
-    base = small_batch(CONFIGS[2], 1, 40000, seed=77).data.tobytes()
+    base = small_batch(WORKLOADS["throughput"], 1, 40000, seed=77).data.tobytes()
     docs = []
     for cut in [4095, 4096, 4097, 4094, 8191, 8192, 1, 2, 3]:
         docs.append(base[:cut])
@@ -124,7 +126,7 @@ def test_chunk_boundaries(dev):
 def test_pathological_runs(dev):
     # letter runs around every tier limit, and runs longer than the window so
     # the pre-token continues into later chunks
-    model, table = model_pair(4)
+    model, table = model_pair("adversarial")
     lens = [1, 2, 31, 32, 33, 63, 64, 65, 66, 100, 1000, 4095, 4096, 4097, 4160, 4161, 5000,
             8192, 20000, 70000]
     docs = [b"a" * n for n in lens] + [b" " + b"q" * n for n in lens]
@@ -185,11 +187,11 @@ def test_out_of_order_tables(dev):
 
 
 def test_id_map_permutation(dev):
-    m = merges_for(1)
+    m = merges_for("tiny")
     V = 256 + m.shape[0]
     perm = np.random.default_rng(3).permutation(V).astype(np.int32)
     model, table = Model(m, perm), O.Table(m, perm)
-    b = small_batch(CONFIGS[1], 3, 5000, seed=4)
+    b = small_batch(WORKLOADS["tiny"], 3, 5000, seed=4)
     ids, off = check_encode(model, table, b.data, b.doc_off)
     base, _ = table.encode_batch(b.data, b.doc_off)
     out, _, st = gpu_decode(model, ids, off)
@@ -203,8 +205,8 @@ def test_id_map_permutation(dev):
 
 
 def test_unaligned_input(dev):
-    model, table = model_pair(2)
-    b = small_batch(CONFIGS[2], 4, 9000, seed=8)
+    model, table = model_pair("throughput")
+    b = small_batch(WORKLOADS["throughput"], 4, 9000, seed=8)
     want, want_off = table.encode_batch(b.data, b.doc_off)
     for shift in (1, 3, 8, 15):
         got, off, st = gpu_encode(model, b.data, b.doc_off, data_offset=shift)
@@ -212,8 +214,8 @@ def test_unaligned_input(dev):
 
 
 def test_ids_capacity_overflow(dev):
-    model, table = model_pair(1)
-    b = small_batch(CONFIGS[1], 3, 6000, seed=2)
+    model, table = model_pair("tiny")
+    b = small_batch(WORKLOADS["tiny"], 3, 6000, seed=2)
     want, _ = table.encode_batch(b.data, b.doc_off)
     cap = want.size // 2
     got, _, st = gpu_encode(model, b.data, b.doc_off, cap=cap)
@@ -223,7 +225,7 @@ def test_ids_capacity_overflow(dev):
 
 @pytest.mark.parametrize("bad", ["first", "order", "last"])
 def test_bad_doc_offsets(dev, bad):
-    model, _ = model_pair(1)
+    model, _ = model_pair("tiny")
     data, off = batch_from_docs([b"hello there", b"abc", b"more text here"])
     off = off.copy()
     if bad == "first":
@@ -237,7 +239,7 @@ def test_bad_doc_offsets(dev, bad):
 
 
 def test_decode_bad_ids_and_capacity(dev):
-    model, table = model_pair(1)
+    model, table = model_pair("tiny")
     V = model.vocab_size
     ids = np.array([104, 105, V, 32, -1, 256], dtype=np.int32)
     _, _, st = gpu_decode(model, ids, np.array([0, ids.size], np.int64))
@@ -253,8 +255,8 @@ def test_decode_bad_ids_and_capacity(dev):
 
 
 def test_determinism(dev):
-    model, table = model_pair(2)
-    b = small_batch(CONFIGS[2], 64, 16384, seed=12)
+    model, table = model_pair("throughput")
+    b = small_batch(WORKLOADS["throughput"], 64, 16384, seed=12)
     a1, o1, s1 = gpu_encode(model, b.data, b.doc_off)
     a2, o2, s2 = gpu_encode(model, b.data, b.doc_off)
     assert s1 == 0 and s2 == 0 and np.array_equal(a1, a2) and np.array_equal(o1, o2)

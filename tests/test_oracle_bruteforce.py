@@ -172,8 +172,8 @@ def test_b2_merge_order_enumeration():
 
 @pytest.fixture(scope="module")
 def tiny_corpus():
-    from workloads import CONFIGS, make_lexicon, training_corpus
-    cfg = CONFIGS[1]
+    from workloads import WORKLOADS, make_lexicon, training_corpus
+    cfg = WORKLOADS["tiny"]
     return cfg, training_corpus(cfg, make_lexicon(cfg))
 
 

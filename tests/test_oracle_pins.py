@@ -189,8 +189,8 @@ def test_validate_id_map():
 # ------------------------------------------------------ batch semantics ----
 
 def _trained_tiny():
-    from workloads import CONFIGS, make_lexicon, training_corpus
-    cfg = CONFIGS[1]
+    from workloads import WORKLOADS, make_lexicon, training_corpus
+    cfg = WORKLOADS["tiny"]
     tc = training_corpus(cfg, make_lexicon(cfg))
     merges, _ = O.train(tc.data, tc.doc_off, cfg.n_merges)
     return merges

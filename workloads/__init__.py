@@ -5,7 +5,7 @@ arithmetic (no splitting, no merging, no ID mapping), so both the oracle and
 the GPU path may consume its output.
 """
 from .synth import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     WorkloadConfig,
     Batch,
     make_lexicon,

@@ -1,7 +1,7 @@
 """Seeded synthetic text for the five byte-level BPE workloads.
 
 Every random draw comes from numpy's PCG64 generator, seeded from the table
-in ``CONFIGS``.  The output is raw bytes plus document offsets; nothing here
+in ``WORKLOADS``.  The output is raw bytes plus document offsets; nothing here
 splits, merges or maps tokens.
 
 Recipe (one reading of the workload descriptions, stated once here):
@@ -55,16 +55,16 @@ class WorkloadConfig:
     patho_frac: float = 0.0
 
 
-CONFIGS = {
-    1: WorkloadConfig("tiny", 512, 64 * KiB, 2000, 1.10, "ascii_lower", 0.0,
+WORKLOADS = {
+    "tiny": WorkloadConfig("tiny", 512, 64 * KiB, 2000, 1.10, "ascii_lower", 0.0,
                       101, 201, 301, "fixed", 1, 1 * MiB),
-    2: WorkloadConfig("throughput", 32000, 16 * MiB, 50000, 1.05, "ascii_lower", 0.10,
+    "throughput": WorkloadConfig("throughput", 32000, 16 * MiB, 50000, 1.05, "ascii_lower", 0.10,
                       102, 202, 302, "fixed", 4096, 64 * KiB),
-    3: WorkloadConfig("multilingual", 50000, 32 * MiB, 50000, 1.05, "multilingual", 0.0,
+    "multilingual": WorkloadConfig("multilingual", 50000, 32 * MiB, 50000, 1.05, "multilingual", 0.0,
                       103, 203, 303, "fixed", 16384, 64 * KiB),
-    4: WorkloadConfig("adversarial", 128000, 64 * MiB, 50000, 1.05, "multilingual", 0.0,
+    "adversarial": WorkloadConfig("adversarial", 128000, 64 * MiB, 50000, 1.05, "multilingual", 0.0,
                       104, 204, 304, "fixed", 16384, 64 * KiB, patho_frac=0.01),
-    5: WorkloadConfig("serving", 100000, 64 * MiB, 50000, 1.05, "multilingual", 0.0,
+    "serving": WorkloadConfig("serving", 100000, 64 * MiB, 50000, 1.05, "multilingual", 0.0,
                       105, 205, 305, "lognormal", 65536, 0),
 }
 
