@@ -96,11 +96,14 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.word_bits = model->word_bits;
   a.ticket = (uint32_t *)(ws + L.ticket);
   a.flags = (uint64_t *)(ws + L.flags);
+  a.first_doc = (const int64_t *)(ws + L.first_doc);
   a.gsym = (int32_t *)(ws + L.gsym);
   a.grank = (int32_t *)(ws + L.grank);
   a.status = d_status;
   a.n_chunks = enc_chunks(n_bytes);
-  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, stream) != hipSuccess) return BPE_EHIP;
+  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, (int64_t *)(ws + L.first_doc),
+                   d_doc_off, n_docs, stream) != hipSuccess)
+    return BPE_EHIP;
   if (launch_encode(a, stream) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }
@@ -421,7 +424,9 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
   a.flags = (uint64_t *)(ws + L.flags);
   a.status = d_status;
   a.n_chunks = dec_chunks(n_ids);
-  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, stream) != hipSuccess) return BPE_EHIP;
+  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, nullptr, nullptr, 0, stream) !=
+      hipSuccess)
+    return BPE_EHIP;
   if (launch_decode(a, stream) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }

@@ -70,18 +70,19 @@ inline int64_t dec_chunks(int64_t n_ids) { return (n_ids + kDecChunk - 1) / kDec
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Encode workspace: [ticket 256 B][flags 8*G][symbols 4*N][ranks 4*N].
-// The symbol/rank regions hold pre-tokens that run past a workgroup's
-// window, each at its own byte position, so no two overlap.
+// Encode workspace: [ticket 256 B][flags 8*G][first doc 8*G][symbols 4*N]
+// [ranks 4*N].  The symbol/rank regions hold the pre-tokens that run the
+// merge loop, each at its own byte position, so no two overlap.
 struct EncLayout {
-  size_t ticket, flags, gsym, grank, total;
+  size_t ticket, flags, first_doc, gsym, grank, total;
 };
 inline EncLayout enc_layout(int64_t n_bytes) {
   EncLayout L;
   int64_t G = enc_chunks(n_bytes);
   L.ticket = 0;
   L.flags = 256;
-  L.gsym = L.flags + align256(8 * (size_t)G);
+  L.first_doc = L.flags + align256(8 * (size_t)G);
+  L.gsym = L.first_doc + align256(8 * (size_t)G);
   L.grank = L.gsym + align256(4 * (size_t)n_bytes);
   L.total = L.grank + align256(4 * (size_t)n_bytes);
   return L;
@@ -114,6 +115,7 @@ struct EncodeArgs {
   int word_bits;
   uint32_t *ticket;
   uint64_t *flags;
+  const int64_t *first_doc;  // [n_chunks]
   int32_t *gsym;
   int32_t *grank;
   int32_t *status;
@@ -140,8 +142,10 @@ struct DecodeArgs {
 };
 
 // Launchers (bpe_kernels.hip).
-// Clears the ticket, the status word and n_flags look-back flags.
+// Clears the ticket, the status word and n_flags look-back flags; with
+// first_doc, also records each chunk's first document (encode).
 hipError_t launch_clear(uint32_t *ticket, uint64_t *flags, int64_t n_flags, int32_t *status,
+                        int64_t *first_doc, const int64_t *doc_off, int64_t n_docs,
                         hipStream_t stream);
 // Empty input: clears the status, checks that offs[0..n_docs] are all zero
 // (else sets bad_bit) and writes zeros to out_off[0..n_docs].

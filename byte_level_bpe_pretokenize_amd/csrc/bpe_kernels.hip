@@ -224,24 +224,28 @@ __device__ int64_t wave_lookback(uint64_t *flags, int64_t c, int64_t agg) {
 }
 
 // ---- encode ---------------------------------------------------------------
+constexpr int kMissCap = 512;   // shared merge-loop work list per workgroup
+constexpr int kPool = 2048;     // LDS ints for merge-loop symbols and ranks
+
 struct EncShared {
-  int32_t Y[WIN];     // symbols at their byte positions (kDead: no symbol)
-  int32_t RK[WIN];    // RK[p] = rank of the pair starting at p
   alignas(16) uint8_t B[16 + WIN + 32];  // B[16 + p] = byte at window position p
-  uint32_t SB[SB_WORDS];            // pre-token start bits, positions [0, WIN]
-  uint32_t DB[DB_WORDS];            // document start bits, positions [-32, WIN)
-  int32_t excl[WG];                 // per-lane exclusive token counts
+  uint32_t SB[SB_WORDS];                 // pre-token start bits, positions [0, WIN]
+  uint32_t DB[DB_WORDS];                 // document start bits, positions [-32, WIN)
+  uint16_t PS[kChunk + 2];               // owned pre-token starts in order, then the end
+  int32_t pool[kPool];                   // merge-loop scratch: symbols, then ranks
+  uint32_t miss[kMissCap];               // pool offset | len << 16, then | ntok << 16
+  int32_t long_st[kMaxLong];             // long pre-tokens inside the window
+  int32_t long_e[kMaxLong];
+  int32_t long_nt[kMaxLong];
+  int32_t pool_used;
   int32_t mflag[WG];
   int32_t red[8];
   int64_t red64[8];
-  int32_t longs[kMaxLong];
-  int32_t n_long;
-  uint32_t miss[kChunk / 2 + 4];    // pre-tokens for the merge loop: start | len << 16
-  int32_t n_miss;
+  int32_t n_miss, n_long;
   int64_t chunk;
-  int64_t d_lo, o_lo, o_hi;
+  int64_t o_lo, o_hi;
   int64_t base;
-  int64_t ov_start, ov_ntok;
+  int64_t ov_ntok;
 };
 
 __device__ __forceinline__ uint32_t sb16(const EncShared &s, int g) {
@@ -320,13 +324,14 @@ __device__ __forceinline__ int32_t word_lookup(const uint4 *__restrict__ tab, in
   }
 }
 
-// Merge one short pre-token of n symbols in place at Y[0..n), RK[0..n) (one
-// lane).  Each round takes the lowest rank r present and rewrites the
-// sequence left to right, merging every pair whose rank is r unless its left
-// symbol was just consumed; then only pairs touching the new symbol are
-// probed again.  Leaves kDead after the result.
-__device__ void lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_t *tab,
-                           const int bits, const int32_t *__restrict__ pair_rank) {
+// Merge one short pre-token of len symbols in place at Y[0..len), with RK
+// as scratch (one lane; Y and RK are the position-indexed global scratch).
+// Each round takes the lowest rank r present and rewrites the sequence left
+// to right, merging every pair whose rank is r unless its left symbol was
+// just consumed; then only pairs touching the new symbol are probed again.
+// Returns the final symbol count.
+__device__ int lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_t *tab,
+                          const int bits, const int32_t *__restrict__ pair_rank) {
   // the symbols are still bytes: their ranks come from the direct table
   for (int i = 0; i + 1 < len; ++i) RK[i] = pair_rank[(Y[i] << 8) | Y[i + 1]];
   RK[len - 1] = kRankInf;
@@ -352,15 +357,18 @@ __device__ void lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_
       if (Y[j] == z || Y[j + 1] == z) RK[j] = rank_of(tab, bits, Y[j], Y[j + 1]);
     RK[n - 1] = kRankInf;
   }
-  for (int j = n; j < len; ++j) Y[j] = kDead;
+  return n;
 }
 
+constexpr int kWgPer = 4;                // positions per thread per tile
+constexpr int kWgTile = WG * kWgPer;
+
 // Merge one pre-token of n symbols at Y[0..n) with the whole workgroup; RK is
-// scratch of n entries.  Y and RK are LDS or global (position-indexed
-// scratch).  Same rounds as lane_merge: the lowest rank r is found by a
-// workgroup minimum, runs of consecutive pairs with rank r (only possible for
-// a pair (x, x)) merge at even offsets from the run start, and survivors are
-// compacted in place tile by tile.  Returns the final symbol count.
+// scratch of n entries (position-indexed global scratch).  Same rounds as
+// lane_merge: the lowest rank r is a workgroup minimum, runs of consecutive
+// pairs with rank r (only possible for a pair (x, x)) merge at even offsets
+// from the run start, and survivors are compacted in place tile by tile.
+// Returns the final symbol count.
 __device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const uint64_t *tab, int bits,
                             const int32_t *__restrict__ pair_rank, EncShared &s) {
   const int tid = threadIdx.x;
@@ -376,53 +384,47 @@ __device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const uint64_t *
     int64_t out_base = 0;
     int64_t anchor = -1;  // last position before the tile whose pair rank is not r
     bool prev_m = false;  // the pair just before the tile merged
-    for (int64_t t0 = 0; t0 < n; t0 += kTile) {
-      const int64_t p0 = t0 + 16 * (int64_t)tid;
-      int32_t y[16], rk[16];
-      bool f[16];
+    for (int64_t t0 = 0; t0 < n; t0 += kWgTile) {
+      const int64_t p0 = t0 + kWgPer * (int64_t)tid;
+      int32_t y[kWgPer], rk[kWgPer];
+      uint32_t f = 0;
       int64_t my_anchor = -1;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < kWgPer; ++j) {
         const int64_t p = p0 + j;
         const bool v = p < n;
         rk[j] = v ? RK[p] : kRankInf;
         y[j] = v ? Y[p] : kDead;
-        f[j] = v && rk[j] == r;
-        if (!f[j]) my_anchor = p;
+        if (v && rk[j] == r) f |= 1u << j;
+        else my_anchor = p;
       }
       int64_t tile_anchor;
       int64_t za = block_excl_max64<WG>(my_anchor, -1, s.red64, &tile_anchor);
       za = max(za, anchor);
-      bool m[16];
+      uint32_t m = 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < kWgPer; ++j) {
         const int64_t p = p0 + j;
-        if (!f[j]) {
-          m[j] = false;
-          za = p;
-        } else {
-          m[j] = ((p - 1 - za) & 1) == 0;
-        }
+        if (!((f >> j) & 1u)) za = p;
+        else if (((p - 1 - za) & 1) == 0) m |= 1u << j;
       }
-      s.mflag[tid] = m[15];
+      s.mflag[tid] = (m >> (kWgPer - 1)) & 1u;
       __syncthreads();
-      const bool mprev = tid ? (s.mflag[tid - 1] != 0) : prev_m;
+      const uint32_t mprev = tid ? (uint32_t)s.mflag[tid - 1] : (uint32_t)prev_m;
       const bool tile_last_m = s.mflag[WG - 1] != 0;
-      bool keep[16];
-      int kc = 0;
+      // position p is consumed when the pair at p - 1 merged
+      const uint32_t consumed = ((m << 1) | mprev) & ((1u << kWgPer) - 1u);
+      uint32_t keep = 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bool consumed = j == 0 ? mprev : m[j - 1];
-        keep[j] = (p0 + j < n) && !consumed;
-        kc += keep[j];
-      }
+      for (int j = 0; j < kWgPer; ++j)
+        if (p0 + j < n && !((consumed >> j) & 1u)) keep |= 1u << j;
       int tile_kept;
-      const int kex = block_excl_sum<int, WG>(kc, s.red, &tile_kept);
+      const int kex = block_excl_sum<int, WG>(__popc(keep), s.red, &tile_kept);
       int64_t o = out_base + kex;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (keep[j]) {
-          Y[o] = m[j] ? z : y[j];
+      for (int j = 0; j < kWgPer; ++j) {
+        if ((keep >> j) & 1u) {
+          Y[o] = ((m >> j) & 1u) ? z : y[j];
           RK[o] = rk[j];
           ++o;
         }
@@ -486,6 +488,13 @@ __device__ int64_t block_global_end(const EncodeArgs &a, EncShared &s, int64_t g
   return limit;
 }
 
+// Per-start state a lane keeps in registers between the phases:
+//   >= 0             the pre-token is this one symbol
+//   [-kPendBase, -1] its -v symbols are in the global scratch at its start
+//   -kPendBase - 1 - k   pending merge-loop list entry k
+//   -2 * kPendBase - 1 - k   pending long-list entry k
+constexpr int32_t kPendBase = 1 << 20;
+
 __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   __shared__ EncShared s;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -507,7 +516,7 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   if (tid == 0) {
     s.chunk = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s.n_long = 0;
-    s.ov_start = -1;
+    s.n_miss = 0;
     s.ov_ntok = 0;
   }
   for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
@@ -519,13 +528,23 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   const int nown = (int)min<int64_t>(kChunk, n - c0);
   const bool win_reaches_end = (c0 + nwin == n);
 
-  // 1. documents touching the window; bytes into LDS
+  // 1. document starts in the window (wave 0, from the chunk's first
+  //    document onwards, 64 offsets per load); bytes into LDS (all waves)
   if (wave == 0) {
-    const int64_t dlo = wave_lower_bound(a.doc_off, a.n_docs + 1, c0 - 1);
-    const int64_t olo = wave_lower_bound(a.doc_off, a.n_docs + 1, c0);
-    const int64_t ohi = wave_lower_bound(a.doc_off, a.n_docs + 1, c0 + nown);
+    int64_t d0 = a.first_doc[c];
+    d0 = min(max(d0, (int64_t)0), a.n_docs);
+    int64_t olo = d0, ohi = d0;
+    for (;;) {
+      const int64_t d = d0 + lane;
+      const int64_t v = d < a.n_docs ? a.doc_off[d] : INT64_MAX;
+      const int64_t p = v - c0;
+      if (p >= -1 && p < nwin) atomicOr(&s.DB[(p + DB_OFF) >> 5], 1u << ((p + DB_OFF) & 31));
+      olo += __popcll(__ballot(v < c0));
+      ohi += __popcll(__ballot(v < c0 + nown));
+      if (!(__shfl(v, 63, 64) < c0 + nwin)) break;
+      d0 += 64;
+    }
     if (lane == 0) {
-      s.d_lo = dlo;
       s.o_lo = olo;
       s.o_hi = ohi;
     }
@@ -545,12 +564,6 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
         }
       }
     }
-  }
-  __syncthreads();
-  for (int64_t d = s.d_lo + tid; d < a.n_docs; d += WG) {
-    const int64_t p = a.doc_off[d] - c0;
-    if (p >= nwin) break;
-    if (p >= -1) atomicOr(&s.DB[(p + DB_OFF) >> 5], 1u << ((p + DB_OFF) & 31));
   }
   __syncthreads();
 
@@ -579,114 +592,163 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   }
   __syncthreads();
 
-  // first and last owned start; end of the last owned pre-token
-  int fs = kNoStart, ls = -1;
+  // last owned start and whether its pre-token runs past the window
+  uint32_t own = 0;
   if (16 * tid < nown) {
-    uint32_t m = sb16(s, tid);
+    own = sb16(s, tid);
     const int lim = nown - 16 * tid;
-    if (lim < 16) m &= (1u << lim) - 1;
-    if (m) {
-      fs = 16 * tid + __ffs(m) - 1;
-      ls = 16 * tid + 31 - __clz(m);
-    }
+    if (lim < 16) own &= (1u << lim) - 1;
   }
-  fs = block_min<WG>(fs, s.red);
-  ls = block_max<WG>(ls, s.red);
-  const int e_last = ls >= 0 ? block_next_start(s, ls + 1) : -1;  // kNoStart: runs past WIN
+  const int ls = block_max<WG>(own ? 16 * tid + 31 - __clz(own) : -1, s.red);
+  const int e_last = ls >= 0 ? block_next_start(s, ls + 1) : -1;
   const bool overhang = ls >= 0 && e_last == kNoStart;
-  const int own_end = ls < 0 ? 0 : (overhang ? ls : e_last);
-  for (int p = tid; p < WIN; p += WG) {
-    s.Y[p] = (p >= fs && p < own_end) ? (int32_t)s.B[16 + p] : kDead;
-    s.RK[p] = kRankInf;
+
+  // 3. the owned pre-token starts as one ordered list (prefix popcount), and
+  //    the end of the last one (past the window: the global tier finds it)
+  int n_pt;
+  {
+    const int pex = block_excl_sum<int, WG>(__popc(own), s.red, &n_pt);
+    uint32_t m = own;
+    for (int k = pex; m; ++k, m &= m - 1) s.PS[k] = (uint16_t)(16 * tid + __ffs(m) - 1);
+    if (tid == 0) {
+      s.PS[n_pt] = (uint16_t)(overhang ? WIN : (ls >= 0 ? e_last : 0));
+      s.pool_used = 0;
+    }
   }
   __syncthreads();
 
-  // 3. lane tier: pre-tokens that start in this lane's 16 bytes.  A single
-  //    byte is its own token; a pre-token found in the word table takes its
-  //    symbol; the rest go to a list that all lanes then share for the merge
-  //    loop, so busy lanes are packed together.
-  if (tid == 0) s.n_miss = 0;
-  __syncthreads();
-  if (16 * tid < nown) {
-    uint32_t m = sb16(s, tid);
-    const int lim = nown - 16 * tid;
-    if (lim < 16) m &= (1u << lim) - 1;
-    while (m) {
-      const int st = 16 * tid + __ffs(m) - 1;
-      m &= m - 1;
-      if (overhang && st == ls) continue;
-      const int e = next_start_bounded(s, st + 1, min(st + kLaneMax, WIN));
-      if (e < 0) {
-        const int k = atomicAdd(&s.n_long, 1);
-        if (k < kMaxLong) s.longs[k] = st;
+  // 4. each thread takes a contiguous block of the list.  A single byte is its
+  //    own token; a pre-token found in the word table takes its symbol; the
+  //    rest go to a shared list for the merge loop, with their symbols in an
+  //    LDS pool (or, when the pool is full, merged at once in the global
+  //    scratch at the pre-token's position).
+  const int per = (n_pt + WG - 1) / WG;     // <= 16: a chunk has <= 4096 starts
+  const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
+  int32_t* gsym = a.gsym + c0;
+  int32_t* grank = a.grank + c0;
+  int32_t v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = 0;
+    if (i >= per) continue;                 // uniform
+    const int k = k0 + i;
+    if (k >= k1) continue;
+    const int st = s.PS[k];
+    if (overhang && k == n_pt - 1) {
+      v[i] = -2 * kPendBase - 1 - kMaxLong;  // resolved below
+      continue;
+    }
+    const int len = (int)s.PS[k + 1] - st;
+    if (len > kLaneMax) {
+      const int q = atomicAdd(&s.n_long, 1);  // < kMaxLong: long ones are > kLaneMax bytes
+      s.long_st[q] = st;
+      s.long_e[q] = st + len;
+      v[i] = -2 * kPendBase - 1 - q;
+      continue;
+    }
+    if (len == 1) {
+      v[i] = s.B[16 + st];
+      continue;
+    }
+    if (a.words && len <= kWordMax) {
+      uint32_t w[kWordWords];
+      pretoken_words(s, st, len, w);
+      const int32_t sym = word_lookup(a.words, a.word_bits, w, len);
+      if (sym >= 0) {
+        v[i] = sym;
         continue;
       }
-      const int len = e - st;
-      if (len == 1) continue;
-      if (a.words && len <= kWordMax) {
-        uint32_t w[kWordWords];
-        pretoken_words(s, st, len, w);
-        const int32_t sym = word_lookup(a.words, a.word_bits, w, len);
-        if (sym >= 0) {
-          s.Y[st] = sym;
-          for (int j = 1; j < len; ++j) s.Y[st + j] = kDead;
-          continue;
-        }
-      }
-      const int k = atomicAdd(&s.n_miss, 1);
-      s.miss[k] = (uint32_t)st | ((uint32_t)len << 16);
+    }
+    const int off = atomicAdd(&s.pool_used, 2 * len);
+    const int q = off + 2 * len <= kPool ? atomicAdd(&s.n_miss, 1) : kMissCap;
+    if (q < kMissCap) {
+      for (int j = 0; j < len; ++j) s.pool[off + j] = s.B[16 + st + j];
+      s.miss[q] = (uint32_t)off | ((uint32_t)len << 16);
+      v[i] = -kPendBase - 1 - q;
+    } else {
+      for (int j = 0; j < len; ++j) gsym[st + j] = s.B[16 + st + j];
+      v[i] = -lane_merge(gsym + st, grank + st, len, a.table, a.table_bits, a.pair_rank);
     }
   }
   __syncthreads();
   {
-    const int n_miss = s.n_miss;
-    for (int k = tid; k < n_miss; k += WG) {
-      const int st = (int)(s.miss[k] & 0xFFFFu), len = (int)(s.miss[k] >> 16);
-      lane_merge(s.Y + st, s.RK + st, len, a.table, a.table_bits, a.pair_rank);
+    const int n_miss = min(s.n_miss, kMissCap);
+    for (int q = tid; q < n_miss; q += WG) {
+      const int off = (int)(s.miss[q] & 0xFFFFu), len = (int)(s.miss[q] >> 16);
+      const int nt = lane_merge(s.pool + off, s.pool + off + len, len, a.table, a.table_bits,
+                                a.pair_rank);
+      s.miss[q] = (uint32_t)off | ((uint32_t)nt << 16);
     }
   }
-  __syncthreads();
 
-  // 4. workgroup tier: longer pre-tokens inside the window, then the one that
-  //    runs past it (in the position-indexed global scratch)
-  const int n_long = min(s.n_long, kMaxLong);
-  for (int k = 0; k < n_long; ++k) {
-    const int st = s.longs[k];
-    const int e = block_next_start(s, st + 1);
-    const int64_t len = e - st;
-    const int64_t nt = wg_merge(s.Y + st, s.RK + st, len, a.table, a.table_bits, a.pair_rank, s);
-    for (int64_t j = nt + tid; j < len; j += WG) s.Y[st + j] = kDead;
+  // 5. workgroup tier: longer pre-tokens inside the window, then the one that
+  //    runs past it (both in the global scratch at their positions)
+  const int n_long = s.n_long;
+  for (int q = 0; q < n_long; ++q) {
+    const int st = s.long_st[q], e = s.long_e[q];
+    for (int p = st + tid; p < e; p += WG) gsym[p] = s.B[16 + p];
     __syncthreads();
+    const int64_t nt = wg_merge(gsym + st, grank + st, e - st, a.table, a.table_bits, a.pair_rank, s);
+    if (tid == 0) s.long_nt[q] = (int32_t)nt;
   }
   if (overhang) {
     const int64_t gs = c0 + ls;
     const int64_t ge = block_global_end(a, s, gs, c0 + WIN);
     for (int64_t q = gs + tid; q < ge; q += WG) a.gsym[q] = a.bytes[q];
     __syncthreads();
-    const int64_t nt = wg_merge(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits, a.pair_rank, s);
-    if (tid == 0) {
-      s.ov_start = gs;
-      s.ov_ntok = nt;
-    }
-    __syncthreads();
+    const int64_t nt = wg_merge(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits,
+                                a.pair_rank, s);
+    if (tid == 0) s.ov_ntok = nt;
   }
+  __syncthreads();
 
-  // 5. counts, chained prefix, writes
-  int cnt = 0;
+  // 6. token counts per thread, chained prefix over the chunks, writes.
+  //    v[i] becomes: >= 0 one symbol; -kPendBase - 1 - q pool entry q;
+  //    [-kPendBase, -1] that many symbols in the global scratch.
+  int64_t cnt = 0;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) cnt += s.Y[16 * tid + k] != kDead;
-  int main_total;
-  const int ex = block_excl_sum<int, WG>(cnt, s.red, &main_total);
-  s.excl[tid] = ex;
-  int halo_rank = 0, halo_total = 0;
-  bool halo_valid = false;
+  for (int i = 0; i < 16; ++i) {
+    if (i >= per || k0 + i >= k1) continue;
+    int32_t x = v[i];
+    int64_t nt;
+    if (x >= 0) {
+      nt = 1;
+    } else if (x < -2 * kPendBase) {
+      const int q = -2 * kPendBase - 1 - x;
+      if (q == kMaxLong) {
+        nt = s.ov_ntok;
+        x = 0;
+      } else {
+        nt = s.long_nt[q];
+        x = -(int32_t)nt;
+      }
+    } else if (x < -kPendBase) {
+      nt = s.miss[-kPendBase - 1 - x] >> 16;
+    } else {
+      nt = -x;
+    }
+    v[i] = x;
+    cnt += nt;
+  }
+  int64_t total;
+  const int64_t ex = block_excl_sum<int64_t, WG>(cnt, s.red64, &total);
+  {
+    // local token offset at each document start, kept at that position in
+    // the rank scratch (free again by now) for the offsets written below
+    int64_t run = ex;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i >= per || k0 + i >= k1) continue;
+      const int k = k0 + i;
+      const int st = s.PS[k];
+      if (db_bit(s, st)) grank[st] = (int32_t)run;
+      const int32_t x = v[i];
+      run += x >= 0 ? (overhang && k == n_pt - 1 ? s.ov_ntok : 1)
+                    : (x < -kPendBase ? (int64_t)(s.miss[-kPendBase - 1 - x] >> 16) : -(int64_t)x);
+    }
+  }
   if (wave == 0) {
-    halo_valid = s.Y[kChunk + lane] != kDead;
-    const uint64_t hb = __ballot(halo_valid);
-    halo_total = __popcll(hb);
-    halo_rank = __popcll(hb & ((1ull << lane) - 1));
-    const int64_t agg = (int64_t)main_total + halo_total + s.ov_ntok;
-    const int64_t base = wave_lookback(a.flags, c, agg);
+    const int64_t base = wave_lookback(a.flags, c, total);
     if (lane == 0) s.base = base;
   }
   __syncthreads();
@@ -695,29 +757,36 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   {
     int64_t w = base + ex;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int32_t y = s.Y[16 * tid + k];
-      if (y != kDead) {
-        if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, y);
+    for (int i = 0; i < 16; ++i) {
+      if (i >= per || k0 + i >= k1) continue;
+      const int k = k0 + i;
+      if (overhang && k == n_pt - 1) continue;  // written below by all threads
+      const int32_t x = v[i];
+      if (x >= 0) {
+        if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, x);
         else overflow = true;
         ++w;
+      } else if (x < -kPendBase) {
+        const uint32_t e = s.miss[-kPendBase - 1 - x];
+        const int off = (int)(e & 0xFFFFu), nt = (int)(e >> 16);
+        for (int q = 0; q < nt; ++q, ++w) {
+          if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, s.pool[off + q]);
+          else overflow = true;
+        }
+      } else {
+        const int st = s.PS[k];
+        for (int q = 0; q < -x; ++q, ++w) {
+          if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, gsym[st + q]);
+          else overflow = true;
+        }
       }
     }
   }
-  if (wave == 0 && halo_valid) {
-    const int64_t w = base + main_total + halo_rank;
-    if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, s.Y[kChunk + lane]);
-    else overflow = true;
-  }
-  // halo count for every wave (wave 0 computed it)
-  if (tid == 0) s.red[6] = halo_total;
-  __syncthreads();
-  const int halo_all = s.red[6];
-  if (s.ov_start >= 0) {
-    const int64_t w0 = base + main_total + halo_all;
-    for (int64_t j = tid; j < s.ov_ntok; j += WG) {
-      const int64_t w = w0 + j;
-      if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, a.gsym[s.ov_start + j]);
+  if (overhang) {
+    const int64_t w0 = base + total - s.ov_ntok;
+    for (int64_t q = tid; q < s.ov_ntok; q += WG) {
+      const int64_t w = w0 + q;
+      if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, gsym[ls + q]);
       else overflow = true;
     }
   }
@@ -726,28 +795,36 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   // per-document offsets: a document starting at p begins after every token
   // of the pre-tokens that start before p
   for (int64_t d = s.o_lo + tid; d < s.o_hi; d += WG) {
-    const int64_t p64 = a.doc_off[d] - c0;
-    const int p = (int)min<int64_t>(max<int64_t>(p64, 0), kChunk - 1);
-    const int t = p >> 4;
-    int before = s.excl[t];
-    for (int q = 16 * t; q < p; ++q) before += s.Y[q] != kDead;
-    a.id_off[d] = base + before;
+    const int64_t p = min(max(a.doc_off[d] - c0, (int64_t)0), (int64_t)kChunk - 1);
+    a.id_off[d] = base + grank[p];
   }
-  if (c == a.n_chunks - 1) {
-    const int64_t total = base + main_total + halo_all + s.ov_ntok;
-    for (int64_t d = s.o_hi + tid; d <= a.n_docs; d += WG) a.id_off[d] = total;
-  }
+  if (c == a.n_chunks - 1)
+    for (int64_t d = s.o_hi + tid; d <= a.n_docs; d += WG) a.id_off[d] = base + total;
 }
 
-// Clears the ticket, the status word and the look-back flags.
-__global__ void k_clear(uint32_t *ticket, uint64_t *flags, int64_t n_flags, int32_t *status) {
+// Clears the ticket, the status word and the look-back flags, and finds each
+// chunk's first document: the first d with doc_off[d] >= chunk start - 1.
+__global__ void k_clear(uint32_t *ticket, uint64_t *flags, int64_t n_flags, int32_t *status,
+                        int64_t *first_doc, const int64_t *doc_off, int64_t n_docs, int64_t chunk) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (gid == 0) {
     *ticket = 0;
     *status = 0;
   }
-  for (int64_t i = gid; i < n_flags; i += stride) flags[i] = 0;
+  for (int64_t i = gid; i < n_flags; i += stride) {
+    flags[i] = 0;
+    if (first_doc) {
+      const int64_t key = i * chunk - 1;
+      int64_t lo = 0, hi = n_docs + 1;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (doc_off[mid] < key) lo = mid + 1;
+        else hi = mid;
+      }
+      first_doc[i] = lo;
+    }
+  }
 }
 
 // Empty input (one workgroup): clear the status, then check that every
@@ -865,11 +942,12 @@ __global__ void __launch_bounds__(DWG) k_decode(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_clear(uint32_t *ticket, uint64_t *flags, int64_t n_flags, int32_t *status,
+                        int64_t *first_doc, const int64_t *doc_off, int64_t n_docs,
                         hipStream_t stream) {
   int64_t blocks = (n_flags + 255) / 256;
   blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
   hipLaunchKernelGGL(k_clear, dim3((unsigned)blocks), dim3(256), 0, stream, ticket, flags, n_flags,
-                     status);
+                     status, first_doc, doc_off, n_docs, (int64_t)kChunk);
   return hipGetLastError();
 }
 
