@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of the input (for counter scaling)")
     return ap.parse_args()
 
 
@@ -105,6 +107,12 @@ def main():
     def step():
         model.encode_batch_into(data, doc_off, ids, id_off, ws, status, stream)
 
+    if args.copy_calibration:
+        # a plain copy kernel of known size: reads and writes n_bytes once
+        copy = torch.empty_like(data)
+        copy.copy_(data)
+        torch.cuda.synchronize()
+        del copy
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()

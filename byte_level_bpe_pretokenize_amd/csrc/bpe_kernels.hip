@@ -47,6 +47,8 @@ constexpr int kNoStart = INT_MAX;
 // 0x80 up), digits, whitespace (0x09-0x0D, 0x20), punctuation (the rest).
 enum : uint32_t { kL = 0, kD = 1, kW = 2, kP = 3 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint32_t byte_class(uint32_t b) {
   const uint32_t lo = b | 0x20u;
   if ((lo - 'a' <= 'z' - 'a') || b >= 0x80u) return kL;
@@ -224,25 +226,25 @@ __device__ int64_t wave_lookback(uint64_t *flags, int64_t c, int64_t agg) {
 }
 
 // ---- encode ---------------------------------------------------------------
-constexpr int kMissCap = 512;   // shared merge-loop work list per workgroup
-constexpr int kPool = 2048;     // LDS ints for merge-loop symbols and ranks
+constexpr int kPool = 768;  // LDS ints for the merge loop of 17..32-byte pre-tokens
 
 struct EncShared {
   alignas(16) uint8_t B[16 + WIN + 32];  // B[16 + p] = byte at window position p
   uint32_t SB[SB_WORDS];                 // pre-token start bits, positions [0, WIN]
   uint32_t DB[DB_WORDS];                 // document start bits, positions [-32, WIN)
   uint16_t PS[kChunk + 2];               // owned pre-token starts in order, then the end
-  int32_t pool[kPool];                   // merge-loop scratch: symbols, then ranks
-  uint32_t miss[kMissCap];               // pool offset | len << 16, then | ntok << 16
+  int32_t PV[kChunk + 2];                // result of each pre-token (see kPendBase)
+  uint16_t miss[kChunk / 2 + 2];         // pre-tokens for the merge loop (list indices)
+  int32_t pool[kPool];                   // merge-loop scratch for 17..32-byte pre-tokens
+  int32_t pool_used;
   int32_t long_st[kMaxLong];             // long pre-tokens inside the window
   int32_t long_e[kMaxLong];
   int32_t long_nt[kMaxLong];
-  int32_t pool_used;
-  int32_t mflag[WG];
+  uint8_t mflag[WG];
   int32_t red[8];
   int64_t red64[8];
   int32_t n_miss, n_long;
-  int64_t chunk;
+  uint32_t ticket;
   int64_t o_lo, o_hi;
   int64_t base;
   int64_t ov_ntok;
@@ -255,18 +257,6 @@ __device__ __forceinline__ uint32_t sb16(const EncShared &s, int g) {
 __device__ __forceinline__ bool db_bit(const EncShared &s, int p) {
   const int q = p + DB_OFF;
   return (s.DB[q >> 5] >> (q & 31)) & 1u;
-}
-
-// Smallest start position in [from, to] (to <= WIN), or -1.
-__device__ __forceinline__ int next_start_bounded(const EncShared &s, int from, int to) {
-  if (from > to) return -1;
-  int w = from >> 5;
-  uint32_t bits = s.SB[w] & (~0u << (from & 31));
-  const int wl = to >> 5;
-  while (bits == 0 && w < wl) bits = s.SB[++w];
-  if (bits == 0) return -1;
-  const int p = (w << 5) + __ffs(bits) - 1;
-  return p <= to ? p : -1;
 }
 
 // Smallest start position in [from, WIN], or kNoStart.  Whole workgroup.
@@ -357,6 +347,98 @@ __device__ int lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_t
       if (Y[j] == z || Y[j + 1] == z) RK[j] = rank_of(tab, bits, Y[j], Y[j + 1]);
     RK[n - 1] = kRankInf;
   }
+  return n;
+}
+
+// Rank of (l, r) continuing the linear probe after slot h (rare path).
+__device__ __noinline__ int32_t rank_probe_from(const uint64_t *__restrict__ tab, int bits,
+                                                uint64_t key, uint64_t h) {
+  const uint64_t mask = (1ull << bits) - 1;
+  for (;;) {
+    h = (h + 1) & mask;
+    const uint64_t s = tab[h];
+    if ((s >> kSymBits) == key) return (int32_t)(s & ((1u << kSymBits) - 1));
+    if (s == kEmptySlot) return kRankInf;
+  }
+}
+
+// Merge one pre-token of len <= W bytes (read from LDS at b) in registers
+// and write its symbols to out; returns their count.  Same rounds as
+// lane_merge, but positions never move: a consumed position is marked dead
+// and every pair joins a live position to the next live one, so all
+// indexing is static and the arrays stay in registers.  The rank probes of
+// a round are issued together, so a round costs one table round trip.
+template <int W>
+__device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const uint64_t *tab,
+                         const int bits, const int32_t *__restrict__ pair_rank) {
+  int32_t sym[W], rk[W];
+  uint32_t alive = len >= 32 ? ~0u : ((1u << len) - 1u);
+#pragma unroll
+  for (int i = 0; i < W; ++i) sym[i] = i < len ? (int32_t)b[i] : 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    rk[i] = (i + 1 < len) ? pair_rank[(sym[i] << 8) | sym[i + 1]] : kRankInf;
+  const uint64_t mask = (1ull << bits) - 1;
+  for (;;) {
+    int32_t r = kRankInf;
+#pragma unroll
+    for (int i = 0; i < W; ++i) r = min(r, rk[i]);   // dead and last positions hold kRankInf
+    if (r == kRankInf) break;
+    const int32_t z = 256 + r;
+    bool carry = false;  // the previous live position merged: this one is consumed
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const bool live = (alive >> i) & 1u;
+      const bool consumed = live && carry;
+      const bool merge = live && !carry && rk[i] == r;
+      if (consumed) {
+        alive &= ~(1u << i);
+        rk[i] = kRankInf;
+      }
+      if (merge) sym[i] = z;
+      carry = live ? merge : carry;
+    }
+    // pairs touching z get new ranks.  Groups of 8 positions from the top:
+    // the next live symbol of each position, then the group's first probes
+    // issued together, then examined.
+    int32_t ns = -1;  // next live symbol above the current group
+#pragma unroll
+    for (int g = W / 8 - 1; g >= 0; --g) {
+      int32_t nx[8];
+      uint32_t need = 0;
+#pragma unroll
+      for (int j = 7; j >= 0; --j) {
+        const int i = 8 * g + j;
+        nx[j] = ns;
+        const bool live = (alive >> i) & 1u;
+        if (live && ns >= 0 && (sym[i] == z || ns == z)) need |= 1u << j;
+        if (live && ns < 0) rk[i] = kRankInf;
+        if (live) ns = sym[i];
+      }
+      if (need) {
+        uint64_t slot[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          slot[j] = kEmptySlot;
+          if ((need >> j) & 1u) slot[j] = tab[pair_hash(pair_key(sym[8 * g + j], nx[j]), bits)];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if ((need >> j) & 1u) {
+            const int i = 8 * g + j;
+            const uint64_t key = pair_key(sym[i], nx[j]);
+            if ((slot[j] >> kSymBits) == key) rk[i] = (int32_t)(slot[j] & ((1u << kSymBits) - 1));
+            else if (slot[j] == kEmptySlot) rk[i] = kRankInf;
+            else rk[i] = rank_probe_from(tab, bits, key, pair_hash(key, bits) & mask);
+          }
+        }
+      }
+    }
+  }
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    if ((alive >> i) & 1u) out[n++] = sym[i];
   return n;
 }
 
@@ -488,40 +570,33 @@ __device__ int64_t block_global_end(const EncodeArgs &a, EncShared &s, int64_t g
   return limit;
 }
 
-// Per-start state a lane keeps in registers between the phases:
-//   >= 0             the pre-token is this one symbol
-//   [-kPendBase, -1] its -v symbols are in the global scratch at its start
-//   -kPendBase - 1 - k   pending merge-loop list entry k
-//   -2 * kPendBase - 1 - k   pending long-list entry k
+// Result of one pre-token, kept in LDS (PV) between the phases:
+//   >= 0                    the pre-token is this one symbol
+//   [-kPendBase, -1]        its -v symbols are in the global scratch at its start
+//   -2 * kPendBase - 1 - q  long-list entry q (q == kMaxLong: the pre-token past the window)
 constexpr int32_t kPendBase = 1 << 20;
 
-__global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
-  __shared__ EncShared s;
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-
-  // Offsets check, spread over the grid by launch index.
-  {
-    const int64_t per = (a.n_docs + 1 + gridDim.x - 1) / gridDim.x;
-    const int64_t i0 = (int64_t)blockIdx.x * per;
-    bool bad = false;
-    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += WG) {
-      const int64_t v = a.doc_off[i];
-      if (i == 0 && v != 0) bad = true;
-      if (i == a.n_docs && v != a.n_bytes) bad = true;
-      if (i < a.n_docs && a.doc_off[i + 1] < v) bad = true;
-    }
-    if (bad) atomicOr(a.status, (int32_t)BPE_STATUS_BAD_DOC_OFFSETS);
+// Token count of pre-token k from its PV entry (after the merge phases).
+__device__ __forceinline__ int64_t pv_ntok(const EncShared &s, int32_t x) {
+  if (x >= 0) return 1;
+  if (x < -2 * kPendBase) {
+    const int q = -2 * kPendBase - 1 - x;
+    return q == kMaxLong ? s.ov_ntok : (int64_t)s.long_nt[q];
   }
+  return -(int64_t)x;
+}
 
+// One chunk: every pre-token whose first byte lies in [c * kChunk, +kChunk).
+__device__ void encode_chunk(const EncodeArgs &a, EncShared &s, const int64_t c) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   if (tid == 0) {
-    s.chunk = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s.n_long = 0;
     s.n_miss = 0;
     s.ov_ntok = 0;
+    s.pool_used = 0;
   }
   for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
   __syncthreads();
-  const int64_t c = s.chunk;
   const int64_t c0 = c * kChunk;
   const int64_t n = a.n_bytes;
   const int nwin = (int)min<int64_t>(WIN, n - c0);
@@ -555,9 +630,10 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
       const int64_t gp = c0 + 16 * (int64_t)g;
       uint8_t *dst = &s.B[16 + 16 * g];
       if (aligned && gp >= 0 && gp + 16 <= n) {
-        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(a.bytes + gp);
+        // streamed once: keep it out of the way of the tables in L2
+        *reinterpret_cast<u32x4 *>(dst) =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.bytes + gp));
       } else {
-#pragma unroll
         for (int k = 0; k < 16; ++k) {
           const int64_t q = gp + k;
           dst[k] = (q >= 0 && q < n) ? a.bytes[q] : 0;
@@ -604,80 +680,80 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   const bool overhang = ls >= 0 && e_last == kNoStart;
 
   // 3. the owned pre-token starts as one ordered list (prefix popcount), and
-  //    the end of the last one (past the window: the global tier finds it)
+  //    the end of the last one
   int n_pt;
   {
     const int pex = block_excl_sum<int, WG>(__popc(own), s.red, &n_pt);
     uint32_t m = own;
     for (int k = pex; m; ++k, m &= m - 1) s.PS[k] = (uint16_t)(16 * tid + __ffs(m) - 1);
-    if (tid == 0) {
-      s.PS[n_pt] = (uint16_t)(overhang ? WIN : (ls >= 0 ? e_last : 0));
-      s.pool_used = 0;
-    }
+    if (tid == 0) s.PS[n_pt] = (uint16_t)(overhang ? WIN : (ls >= 0 ? e_last : 0));
   }
   __syncthreads();
 
   // 4. each thread takes a contiguous block of the list.  A single byte is its
   //    own token; a pre-token found in the word table takes its symbol; the
   //    rest go to a shared list for the merge loop, with their symbols in an
-  //    LDS pool (or, when the pool is full, merged at once in the global
-  //    scratch at the pre-token's position).
-  const int per = (n_pt + WG - 1) / WG;     // <= 16: a chunk has <= 4096 starts
+  //    LDS pool (or in the global scratch at the pre-token's position).
+  const int per = (n_pt + WG - 1) / WG;
   const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
-  int32_t* gsym = a.gsym + c0;
-  int32_t* grank = a.grank + c0;
-  int32_t v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = 0;
-    if (i >= per) continue;                 // uniform
-    const int k = k0 + i;
-    if (k >= k1) continue;
+  int32_t *gsym = a.gsym + c0;
+  int32_t *grank = a.grank + c0;
+  for (int k = k0; k < k1; ++k) {
     const int st = s.PS[k];
+    int32_t res = -1;
     if (overhang && k == n_pt - 1) {
-      v[i] = -2 * kPendBase - 1 - kMaxLong;  // resolved below
-      continue;
-    }
-    const int len = (int)s.PS[k + 1] - st;
-    if (len > kLaneMax) {
-      const int q = atomicAdd(&s.n_long, 1);  // < kMaxLong: long ones are > kLaneMax bytes
-      s.long_st[q] = st;
-      s.long_e[q] = st + len;
-      v[i] = -2 * kPendBase - 1 - q;
-      continue;
-    }
-    if (len == 1) {
-      v[i] = s.B[16 + st];
-      continue;
-    }
-    if (a.words && len <= kWordMax) {
-      uint32_t w[kWordWords];
-      pretoken_words(s, st, len, w);
-      const int32_t sym = word_lookup(a.words, a.word_bits, w, len);
-      if (sym >= 0) {
-        v[i] = sym;
-        continue;
+      res = -2 * kPendBase - 1 - kMaxLong;
+    } else {
+      const int len = (int)s.PS[k + 1] - st;
+      if (len > kLaneMax) {
+        const int q = atomicAdd(&s.n_long, 1);  // < kMaxLong: each is > kLaneMax bytes
+        s.long_st[q] = st;
+        s.long_e[q] = st + len;
+        res = -2 * kPendBase - 1 - q;
+      } else if (len == 1) {
+        res = s.B[16 + st];
+      } else {
+        if (a.words && len <= kWordMax) {
+          uint32_t w[kWordWords];
+          pretoken_words(s, st, len, w);
+          res = word_lookup(a.words, a.word_bits, w, len);
+        }
+        if (res < 0) {
+          s.miss[atomicAdd(&s.n_miss, 1)] = (uint16_t)k;  // < kChunk / 2: each is >= 2 bytes
+          res = -1;                                       // set by the merge below
+        }
       }
     }
-    const int off = atomicAdd(&s.pool_used, 2 * len);
-    const int q = off + 2 * len <= kPool ? atomicAdd(&s.n_miss, 1) : kMissCap;
-    if (q < kMissCap) {
-      for (int j = 0; j < len; ++j) s.pool[off + j] = s.B[16 + st + j];
-      s.miss[q] = (uint32_t)off | ((uint32_t)len << 16);
-      v[i] = -kPendBase - 1 - q;
-    } else {
-      for (int j = 0; j < len; ++j) gsym[st + j] = s.B[16 + st + j];
-      v[i] = -lane_merge(gsym + st, grank + st, len, a.table, a.table_bits, a.pair_rank);
-    }
+    s.PV[k] = res;
   }
   __syncthreads();
   {
-    const int n_miss = min(s.n_miss, kMissCap);
-    for (int q = tid; q < n_miss; q += WG) {
-      const int off = (int)(s.miss[q] & 0xFFFFu), len = (int)(s.miss[q] >> 16);
-      const int nt = lane_merge(s.pool + off, s.pool + off + len, len, a.table, a.table_bits,
-                                a.pair_rank);
-      s.miss[q] = (uint32_t)off | ((uint32_t)nt << 16);
+    // the merge loop for the list, one pre-token per lane, symbols in registers
+    // entry q goes to lane q / 4 of wave q % 4: every wave (SIMD) gets a share
+    const int n_miss = s.n_miss;
+    const int slot = 4 * lane + wave;
+    for (int q = slot; q < n_miss; q += WG) {
+      const int k = s.miss[q];
+      const int st = s.PS[k], len = (int)s.PS[k + 1] - st;
+      int nt;
+      if (len <= 8) {
+        nt = reg_merge<8>(&s.B[16 + st], len, gsym + st, a.table, a.table_bits, a.pair_rank);
+      } else if (len <= 16) {
+        nt = reg_merge<16>(&s.B[16 + st], len, gsym + st, a.table, a.table_bits, a.pair_rank);
+      } else {
+        // 17..32 bytes: symbols and ranks in the LDS pool when it has room
+        const int off = atomicAdd(&s.pool_used, 2 * len);
+        int32_t *Y = gsym + st, *RK = grank + st;
+        if (off + 2 * len <= kPool) {
+          Y = s.pool + off;
+          RK = Y + len;
+        }
+        for (int j = 0; j < len; ++j) Y[j] = s.B[16 + st + j];
+        nt = lane_merge(Y, RK, len, a.table, a.table_bits, a.pair_rank);
+        if (Y != gsym + st)
+          for (int j = 0; j < nt; ++j) gsym[st + j] = Y[j];
+      }
+      s.PV[k] = -nt;
     }
   }
 
@@ -702,49 +778,19 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   }
   __syncthreads();
 
-  // 6. token counts per thread, chained prefix over the chunks, writes.
-  //    v[i] becomes: >= 0 one symbol; -kPendBase - 1 - q pool entry q;
-  //    [-kPendBase, -1] that many symbols in the global scratch.
+  // 6. token counts per thread, chained prefix over the chunks, writes
   int64_t cnt = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i >= per || k0 + i >= k1) continue;
-    int32_t x = v[i];
-    int64_t nt;
-    if (x >= 0) {
-      nt = 1;
-    } else if (x < -2 * kPendBase) {
-      const int q = -2 * kPendBase - 1 - x;
-      if (q == kMaxLong) {
-        nt = s.ov_ntok;
-        x = 0;
-      } else {
-        nt = s.long_nt[q];
-        x = -(int32_t)nt;
-      }
-    } else if (x < -kPendBase) {
-      nt = s.miss[-kPendBase - 1 - x] >> 16;
-    } else {
-      nt = -x;
-    }
-    v[i] = x;
-    cnt += nt;
-  }
+  for (int k = k0; k < k1; ++k) cnt += pv_ntok(s, s.PV[k]);
   int64_t total;
   const int64_t ex = block_excl_sum<int64_t, WG>(cnt, s.red64, &total);
   {
     // local token offset at each document start, kept at that position in
     // the rank scratch (free again by now) for the offsets written below
     int64_t run = ex;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i >= per || k0 + i >= k1) continue;
-      const int k = k0 + i;
+    for (int k = k0; k < k1; ++k) {
       const int st = s.PS[k];
       if (db_bit(s, st)) grank[st] = (int32_t)run;
-      const int32_t x = v[i];
-      run += x >= 0 ? (overhang && k == n_pt - 1 ? s.ov_ntok : 1)
-                    : (x < -kPendBase ? (int64_t)(s.miss[-kPendBase - 1 - x] >> 16) : -(int64_t)x);
+      run += pv_ntok(s, s.PV[k]);
     }
   }
   if (wave == 0) {
@@ -756,29 +802,23 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   bool overflow = false;
   {
     int64_t w = base + ex;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i >= per || k0 + i >= k1) continue;
-      const int k = k0 + i;
-      if (overhang && k == n_pt - 1) continue;  // written below by all threads
-      const int32_t x = v[i];
+    for (int k = k0; k < k1; ++k) {
+      const int32_t x = s.PV[k];
       if (x >= 0) {
-        if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, x);
+        if (w < a.ids_cap) __builtin_nontemporal_store(out_id(a.id_map, x), &a.ids[w]);
         else overflow = true;
         ++w;
-      } else if (x < -kPendBase) {
-        const uint32_t e = s.miss[-kPendBase - 1 - x];
-        const int off = (int)(e & 0xFFFFu), nt = (int)(e >> 16);
-        for (int q = 0; q < nt; ++q, ++w) {
-          if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, s.pool[off + q]);
-          else overflow = true;
-        }
-      } else {
-        const int st = s.PS[k];
-        for (int q = 0; q < -x; ++q, ++w) {
-          if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, gsym[st + q]);
-          else overflow = true;
-        }
+        continue;
+      }
+      if (x < -2 * kPendBase && -2 * kPendBase - 1 - x == kMaxLong) continue;  // below
+      const int st = s.PS[k];
+      const int32_t *src = gsym + st;
+      int nt;
+      if (x < -2 * kPendBase) nt = s.long_nt[-2 * kPendBase - 1 - x];
+      else nt = -x;
+      for (int q = 0; q < nt; ++q, ++w) {
+        if (w < a.ids_cap) __builtin_nontemporal_store(out_id(a.id_map, src[q]), &a.ids[w]);
+        else overflow = true;
       }
     }
   }
@@ -786,7 +826,7 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
     const int64_t w0 = base + total - s.ov_ntok;
     for (int64_t q = tid; q < s.ov_ntok; q += WG) {
       const int64_t w = w0 + q;
-      if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, gsym[ls + q]);
+      if (w < a.ids_cap) __builtin_nontemporal_store(out_id(a.id_map, gsym[ls + q]), &a.ids[w]);
       else overflow = true;
     }
   }
@@ -800,6 +840,31 @@ __global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
   }
   if (c == a.n_chunks - 1)
     for (int64_t d = s.o_hi + tid; d <= a.n_docs; d += WG) a.id_off[d] = base + total;
+  __syncthreads();
+}
+
+// One workgroup per chunk.  Chunks are numbered in the order workgroups
+// start (an atomic ticket), so the chunk a look-back waits for always belongs
+// to a workgroup that is already running.
+__global__ void __launch_bounds__(WG) k_encode(EncodeArgs a) {
+  __shared__ EncShared s;
+  const int tid = threadIdx.x;
+  {
+    const int64_t per = (a.n_docs + 1 + gridDim.x - 1) / gridDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * per;
+    bool bad = false;
+    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += WG) {
+      const int64_t v = a.doc_off[i];
+      if (i == 0 && v != 0) bad = true;
+      if (i == a.n_docs && v != a.n_bytes) bad = true;
+      if (i < a.n_docs && a.doc_off[i + 1] < v) bad = true;
+    }
+    if (bad) atomicOr(a.status, (int32_t)BPE_STATUS_BAD_DOC_OFFSETS);
+  }
+  if (tid == 0)
+    s.ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  encode_chunk(a, s, (int64_t)s.ticket);
 }
 
 // Clears the ticket, the status word and the look-back flags, and finds each
