@@ -78,7 +78,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
                         stream) == hipSuccess
                ? BPE_OK
                : BPE_EHIP;
-  const EncLayout L = enc_layout(n_bytes);
+  const EncLayout L = enc_layout(n_bytes, n_docs);
   uint8_t *ws = (uint8_t *)d_workspace;
   EncodeArgs a;
   a.bytes = d_bytes;
@@ -94,16 +94,18 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.pair_rank = model->d_pair_rank;
   a.words = words;
   a.word_bits = model->word_bits;
-  a.ticket = (uint32_t *)(ws + L.ticket);
-  a.flags = (uint64_t *)(ws + L.flags);
-  a.first_doc = (const int64_t *)(ws + L.first_doc);
+  a.meta = (int32_t *)(ws + L.meta);
+  a.tot = (int64_t *)(ws + L.tot);
+  a.off = (int64_t *)(ws + L.off);
+  a.doc_rng = (int64_t *)(ws + L.doc_rng);
+  a.doc_pt = (int32_t *)(ws + L.doc_pt);
+  a.pv = (int32_t *)(ws + L.pv);
+  a.miss = (uint32_t *)(ws + L.miss);
+  a.mt = (int32_t *)(ws + L.mt);
   a.gsym = (int32_t *)(ws + L.gsym);
   a.grank = (int32_t *)(ws + L.grank);
   a.status = d_status;
   a.n_chunks = enc_chunks(n_bytes);
-  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, (int64_t *)(ws + L.first_doc),
-                   d_doc_off, n_docs, stream) != hipSuccess)
-    return BPE_EHIP;
   if (launch_encode(a, stream) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }
@@ -131,7 +133,7 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
     std::memcpy(&text[(size_t)doc_off[(size_t)k]], &exp_bytes[(size_t)exp_off[(size_t)v]],
                 (size_t)(doc_off[(size_t)k + 1] - doc_off[(size_t)k]));
   }
-  const EncLayout L = enc_layout(N);
+  const EncLayout L = enc_layout(N, D);
   uint8_t *d_text = nullptr, *d_ws = nullptr;
   int64_t *d_doc = nullptr, *d_ioff = nullptr;
   int32_t *d_ids = nullptr, *d_status = nullptr;
@@ -363,8 +365,7 @@ int64_t bpe_max_token_bytes(const bpe_model *model) {
 
 size_t bpe_encode_workspace_bytes(const bpe_model *model, int64_t n_bytes, int64_t n_docs) {
   (void)model;
-  (void)n_docs;
-  return n_bytes > 0 ? enc_layout(n_bytes).total : 0;
+  return n_bytes > 0 ? enc_layout(n_bytes, n_docs).total : 0;
 }
 
 int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
@@ -374,10 +375,11 @@ int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_b
   if (!model || n_bytes < 0 || n_docs < 0 || ids_capacity < 0 || !d_doc_off || !d_id_off ||
       !d_status || (ids_capacity > 0 && !d_ids) || (n_bytes > 0 && (!d_bytes || !d_workspace)))
     return BPE_EINVAL;
-  if (enc_chunks(n_bytes) > INT32_MAX) return BPE_EINVAL;
+  // a launch holds at most 2^32 - 1 work-items
+  if (enc_chunks(n_bytes) * kEncThreads > (int64_t)UINT32_MAX) return BPE_EINVAL;
   if (!on_model_device(model)) return BPE_EINVAL;
   hipStream_t stream = (hipStream_t)hip_stream;
-  if (n_bytes > 0 && workspace_bytes < enc_layout(n_bytes).total) return BPE_EWORKSPACE;
+  if (n_bytes > 0 && workspace_bytes < enc_layout(n_bytes, n_docs).total) return BPE_EWORKSPACE;
   return enqueue_encode(model, d_bytes, n_bytes, d_doc_off, n_docs, d_ids, ids_capacity, d_id_off,
                         d_workspace, d_status, model->d_words, model->d_id_map, stream);
 }
@@ -396,7 +398,7 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
       !d_status || (bytes_capacity > 0 && !d_bytes) || (n_ids > 0 && (!d_ids || !d_workspace)))
     return BPE_EINVAL;
   if (!model->decode_ok) return BPE_ENOTSUP;
-  if (dec_chunks(n_ids) > INT32_MAX) return BPE_EINVAL;
+  if (dec_chunks(n_ids) * kDecThreads > (int64_t)UINT32_MAX) return BPE_EINVAL;
   if (!on_model_device(model)) return BPE_EINVAL;
   hipStream_t stream = (hipStream_t)hip_stream;
   if (n_ids == 0)
@@ -420,13 +422,11 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
   a.inv_map = model->d_inv_map;
   a.inv_size = model->inv_size;
   a.vocab = model->V;
-  a.ticket = (uint32_t *)(ws + L.ticket);
-  a.flags = (uint64_t *)(ws + L.flags);
+  a.tot = (int64_t *)(ws + L.tot);
+  a.off = (int64_t *)(ws + L.off);
+  a.flag = (int32_t *)(ws + L.flag);
   a.status = d_status;
   a.n_chunks = dec_chunks(n_ids);
-  if (launch_clear(a.ticket, a.flags, a.n_chunks, d_status, nullptr, nullptr, 0, stream) !=
-      hipSuccess)
-    return BPE_EHIP;
   if (launch_decode(a, stream) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }

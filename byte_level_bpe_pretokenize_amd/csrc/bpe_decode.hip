@@ -1,0 +1,157 @@
+// bpe_decode.hip -- byte-level BPE decode for gfx950.
+//
+// Decode maps every ID back to its symbol and writes the symbol's byte
+// expansion; the concatenation is the original text.  IDs are cut into
+// chunks of kDecChunk; three kernels, none of which waits on another
+// workgroup:
+//   k_dec_len    per chunk: the byte count of its IDs and its status bits
+//                (an ID outside the vocabulary, bad document offsets).
+//   k_dec_scan   exclusive scan of the chunk byte counts; the status word.
+//   k_dec_write  per chunk: the byte offset of each ID in the chunk, the
+//                bytes, and the per-document byte offsets.
+//
+// Sources: "Tokenization LLM: ... C++" (glitch4techs.com), sections
+// "Byte-level encoding" (every byte sequence has a representation, so
+// decoding returns the exact input bytes) and "Vocabulary lookup" (ID back
+// to token); "Hugging Face Tokenizers v1" (dothoosh.com), section "Road to
+// 1.0.0" (GPU batch decode).
+#include "../../include/bpe.h"
+#include "bpe_device.cuh"
+
+namespace bpe {
+namespace {
+
+constexpr int DWG = kDecThreads;
+constexpr int DPT = kDecPerThread;
+constexpr int SWG = 1024;
+
+// Symbol of an ID, or -1 for an ID with no symbol.
+__device__ __forceinline__ int32_t dec_sym(const DecodeArgs &a, int32_t id) {
+  if (a.inv_map) return (id >= 0 && id < a.inv_size) ? a.inv_map[id] : -1;
+  return (id >= 0 && id < a.vocab) ? id : -1;
+}
+
+__global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
+  __shared__ int64_t red64[DWG / 64];
+  const int tid = threadIdx.x;
+  bool bad_off = false;
+  {
+    const int64_t per = (a.n_docs + 1 + gridDim.x - 1) / gridDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * per;
+    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += DWG) {
+      const int64_t v = a.id_off[i];
+      if (i == 0 && v != 0) bad_off = true;
+      if (i == a.n_docs && v != a.n_ids) bad_off = true;
+      if (i < a.n_docs && a.id_off[i + 1] < v) bad_off = true;
+    }
+  }
+  const int64_t c = blockIdx.x;
+  const int64_t i0 = c * kDecChunk;
+  const int cnt = (int)min<int64_t>(kDecChunk, a.n_ids - i0);
+  bool bad_id = false;
+  int64_t mine = 0;
+  // consecutive threads read consecutive IDs
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int k = j * DWG + tid;
+    if (k < cnt) {
+      const int32_t sym = dec_sym(a, a.ids[i0 + k]);
+      if (sym < 0) bad_id = true;
+      else mine += a.exp_off[sym + 1] - a.exp_off[sym];
+    }
+  }
+  int64_t total;
+  (void)block_excl_sum<int64_t, DWG>(mine, red64, &total);
+  const int bits = (__syncthreads_or(bad_id) ? (int)BPE_STATUS_BAD_ID : 0) |
+                   (__syncthreads_or(bad_off) ? (int)BPE_STATUS_BAD_ID_OFFSETS : 0);
+  if (tid == 0) {
+    a.tot[c] = total;
+    a.flag[c] = bits;
+  }
+}
+
+__global__ void __launch_bounds__(SWG) k_dec_scan(DecodeArgs a) {
+  __shared__ int64_t red64[SWG / 64];
+  chunk_offsets<SWG>(a.tot, a.off, a.flag, 1, a.n_chunks, a.status, red64);
+}
+
+struct WriteShared {
+  int32_t len[kDecChunk];
+  int64_t excl[DWG];
+  int64_t red64[DWG / 64];
+  int64_t o_lo, o_hi;
+};
+
+__global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
+  __shared__ WriteShared s;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int64_t c = blockIdx.x;
+  const int64_t i0 = c * kDecChunk;
+  const int cnt = (int)min<int64_t>(kDecChunk, a.n_ids - i0);
+  const int64_t base = a.off[c];
+  if (wave == 0) {
+    const int64_t olo = wave_lower_bound(a.id_off, a.n_docs + 1, i0);
+    const int64_t ohi = wave_lower_bound(a.id_off, a.n_docs + 1, i0 + cnt);
+    if (lane == 0) {
+      s.o_lo = olo;
+      s.o_hi = max(olo, ohi);
+    }
+  }
+  // lengths read coalesced into LDS, then each thread takes DPT in a row
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int k = j * DWG + tid;
+    int32_t len = 0;
+    if (k < cnt) {
+      const int32_t sym = dec_sym(a, a.ids[i0 + k]);
+      if (sym >= 0) len = (int32_t)(a.exp_off[sym + 1] - a.exp_off[sym]);
+    }
+    s.len[k] = len;
+  }
+  __syncthreads();
+  int64_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) mine += s.len[tid * DPT + j];
+  int64_t total;
+  const int64_t ex = block_excl_sum<int64_t, DWG>(mine, s.red64, &total);
+  s.excl[tid] = ex;
+  bool overflow = false;
+  int64_t w = base + ex;
+  for (int j = 0; j < DPT; ++j) {
+    const int k = tid * DPT + j;
+    const int32_t len = s.len[k];
+    if (len > 0) {
+      const int32_t sym = dec_sym(a, a.ids[i0 + k]);
+      const uint8_t *src = a.exp_bytes + a.exp_off[sym];
+      for (int q = 0; q < len; ++q) {
+        if (w + q < a.out_cap) a.out[w + q] = src[q];
+        else overflow = true;
+      }
+    }
+    w += len;
+  }
+  if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_BYTES_CAPACITY);
+  __syncthreads();
+  for (int64_t d = s.o_lo + tid; d < s.o_hi; d += DWG) {
+    const int64_t k64 = a.id_off[d] - i0;
+    const int k = (int)min<int64_t>(max<int64_t>(k64, 0), kDecChunk - 1);
+    const int t = k / DPT;
+    int64_t before = s.excl[t];
+    for (int q = t * DPT; q < k; ++q) before += s.len[q];
+    a.byte_off[d] = base + before;
+  }
+  if (c == a.n_chunks - 1)
+    for (int64_t d = s.o_hi + tid; d <= a.n_docs; d += DWG) a.byte_off[d] = base + total;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  const unsigned G = (unsigned)a.n_chunks;
+  hipLaunchKernelGGL(k_dec_len, dim3(G), dim3(DWG), 0, stream, a);
+  hipLaunchKernelGGL(k_dec_scan, dim3(1), dim3(SWG), 0, stream, a);
+  hipLaunchKernelGGL(k_dec_write, dim3(G), dim3(DWG), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bpe

@@ -1,0 +1,200 @@
+// bpe_device.cuh -- device helpers shared by the encode and decode kernels:
+// byte classes, rank probes, wave / workgroup reductions and scans, a wave-wide
+// binary search and the per-chunk offset scan.
+#pragma once
+
+#include <limits.h>
+#include <stdint.h>
+
+#include "bpe_internal.h"
+
+namespace bpe {
+namespace {
+
+// Byte classes (the fixed split rule): letters (A-Z, a-z and every byte from
+// 0x80 up), digits, whitespace (0x09-0x0D, 0x20), punctuation (the rest).
+enum : uint32_t { kL = 0, kD = 1, kW = 2, kP = 3 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kNoStart = INT_MAX;
+
+__device__ __forceinline__ uint32_t byte_class(uint32_t b) {
+  const uint32_t lo = b | 0x20u;
+  if ((lo - 'a' <= 'z' - 'a') || b >= 0x80u) return kL;
+  if (b - '0' <= 9u) return kD;
+  if (b - 9u <= 4u || b == 0x20u) return kW;
+  return kP;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Rank of the pair (l, r), or kRankInf.  Linear probing from the pair's hash.
+__device__ __forceinline__ int32_t rank_of(const uint64_t *__restrict__ tab, int bits, uint32_t l,
+                                           uint32_t r) {
+  const uint64_t key = pair_key(l, r);
+  const uint64_t mask = (1ull << bits) - 1;
+  uint64_t h = pair_hash(key, bits);
+  for (;;) {
+    const uint64_t s = tab[h];
+    if ((s >> kSymBits) == key) return (int32_t)(s & ((1u << kSymBits) - 1));
+    if (s == kEmptySlot) return kRankInf;
+    h = (h + 1) & mask;
+  }
+}
+
+// ---- wave / workgroup reductions and scans --------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_sum(T v) {
+  const int lane = lane_id();
+  for (int d = 1; d < 64; d <<= 1) {
+    const T o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over the workgroup; *total gets the sum.  Barriers
+// inside: every thread must call it.
+template <typename T, int NT>
+__device__ T block_excl_sum(T v, T *red, T *total) {
+  const T inc = wave_incl_sum(v);
+  if (lane_id() == 63) red[wave_id()] = inc;
+  __syncthreads();
+  T wp = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const T x = red[w];
+    if (w < wave_id()) wp += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return wp + inc - v;
+}
+
+template <int NT>
+__device__ int32_t block_min(int32_t v, int32_t *red) {
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  int32_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) m = min(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+template <int NT>
+__device__ int32_t block_max(int32_t v, int32_t *red) {
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 64));
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  int32_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) m = max(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+// Exclusive running maximum over the workgroup (identity `lowest`);
+// *total gets the maximum of all values.
+template <int NT>
+__device__ int64_t block_excl_max64(int64_t v, int64_t lowest, int64_t *red, int64_t *total) {
+  const int lane = lane_id();
+  int64_t inc = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc = max(inc, o);
+  }
+  int64_t ex = __shfl_up(inc, 1, 64);
+  if (lane == 0) ex = lowest;
+  if (lane == 63) red[wave_id()] = inc;
+  __syncthreads();
+  int64_t wp = lowest, tot = lowest;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int64_t x = red[w];
+    if (w < wave_id()) wp = max(wp, x);
+    tot = max(tot, x);
+  }
+  __syncthreads();
+  *total = tot;
+  return max(wp, ex);
+}
+
+// First index i in [0, n) with a[i] >= key (n if none), for a sorted array.
+// Called by all 64 lanes of one wave; 64-way split per step.  For an array
+// that is not sorted the result is still in [0, n].
+__device__ int64_t wave_lower_bound(const int64_t *a, int64_t n, int64_t key) {
+  const int lane = lane_id();
+  int64_t lo = 0, hi = n;  // a[i] < key for i < lo; answer <= hi
+  while (hi - lo > 64) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t idx = lo + (int64_t)lane * step;
+    const bool ge = idx < hi ? (a[idx] >= key) : true;
+    const uint64_t m = __ballot(ge);
+    const int first = m ? __ffsll((unsigned long long)m) - 1 : 64;
+    const int64_t nlo = first == 0 ? lo : lo + (int64_t)(first - 1) * step + 1;
+    const int64_t nhi = first == 64 ? hi : min(hi, lo + (int64_t)first * step);
+    lo = nlo;
+    hi = max(nhi, nlo);
+  }
+  const int64_t idx = lo + lane;
+  const bool ge = idx < hi ? (a[idx] >= key) : true;
+  const uint64_t m = __ballot(ge);
+  return m ? lo + (__ffsll((unsigned long long)m) - 1) : hi;
+}
+
+// Exclusive prefix of the per-chunk counts tot[0..n) into off, and the OR of
+// the per-chunk status bits flag[c * fstride] into *status.  One workgroup of
+// NT threads; red64 holds NT / 64 values.
+template <int NT>
+__device__ void chunk_offsets(const int64_t *__restrict__ tot, int64_t *__restrict__ off,
+                              const int32_t *__restrict__ flag, int fstride, int64_t n,
+                              int32_t *status, int64_t *red64) {
+  constexpr int PER = 8;
+  int64_t carry = 0;
+  int32_t bits = 0;
+  for (int64_t t0 = 0; t0 < n; t0 += (int64_t)NT * PER) {
+    const int64_t b0 = t0 + (int64_t)threadIdx.x * PER;
+    int64_t v[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool in = b0 + j < n;
+      v[j] = in ? tot[b0 + j] : 0;
+      if (in) bits |= flag[(b0 + j) * fstride];
+      sum += v[j];
+    }
+    int64_t total;
+    int64_t run = carry + block_excl_sum<int64_t, NT>(sum, red64, &total);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (b0 + j < n) off[b0 + j] = run;
+      run += v[j];
+    }
+    carry += total;
+  }
+  for (int d = 32; d >= 1; d >>= 1) bits |= __shfl_xor(bits, d, 64);
+  int32_t *red = reinterpret_cast<int32_t *>(red64);
+  if (lane_id() == 0) red[wave_id()] = bits;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t all = 0;
+    for (int w = 0; w < NT / 64; ++w) all |= red[w];
+    *status = all;
+  }
+}
+
+__device__ __forceinline__ int32_t out_id(const int32_t *id_map, int32_t sym) {
+  return id_map ? id_map[sym] : sym;
+}
+
+}  // namespace
+}  // namespace bpe

@@ -1,0 +1,772 @@
+// bpe_encode.hip -- byte-level BPE encode for gfx950.
+//
+// The input is cut into 4 KiB chunks; a chunk owns every pre-token whose
+// first byte lies in it.  Four kernels, none of which waits on another
+// workgroup:
+//   k_find    scan a chunk (coalesced bytes into LDS, a byte class and a
+//             start bit per byte from a 3-byte window), list its pre-tokens
+//             in order (prefix popcount), and resolve each one that is a
+//             single byte or a whole entry of the word table; the others go
+//             to the chunk's ordered merge-loop list.
+//   k_merge   one wave per chunk runs the merge loop for the list: one
+//             pre-token per lane in registers for <= kLaneMax bytes, the
+//             whole wave for longer ones; writes token counts and tokens.
+//   k_offsets exclusive scan of the per-chunk token counts.
+//   k_emit    writes each chunk's IDs at its offset, and the per-document
+//             offsets.
+//
+// Sources: "Tokenization LLM: ... C++" (glitch4techs.com), sections
+// "Technical analysis" (the split into words, numbers, punctuation and
+// whitespace), "Byte-level encoding", "BPE algorithm" (lowest rank merges
+// first, repeat until no ranked pair) and "Vocabulary lookup";
+// "Characters, bytes and subwords" (tokenwerk.deckle.io), section "BPE step
+// by step" (left to right without overlap: [a,a,a] -> [aa,a]); "Hugging Face
+// Tokenizers v1" (dothoosh.com), sections "How v1 works" (merges stay inside
+// a pre-token), "Bitcannon" (pre-token boundaries from bit-parallel class
+// masks), "Word caching" (a pre-token seen as a whole skips the merge loop),
+// "Merge-loop rewrite" (flat arrays, 'no merge' as the largest value,
+// batches) and "Road to 1.0.0" (GPU batch encode, output positions in
+// parallel).
+#include "../../include/bpe.h"
+#include "bpe_device.cuh"
+
+namespace bpe {
+namespace {
+
+constexpr int WG = kEncThreads;             // k_find, k_emit: 4 waves
+constexpr int MWG = 64;                     // k_merge: one wave per chunk
+constexpr int OWG = 1024;                   // k_offsets: one workgroup
+constexpr int WIN = kChunk + kHalo;         // window positions [0, WIN)
+constexpr int SB_HALF = WIN / 16 + 1;       // 16-bit start masks for positions [0, WIN]
+constexpr int SB_WORDS = (SB_HALF + 1) / 2 + 1;
+constexpr int DB_OFF = 32;                  // document-start bit of position p is bit p + DB_OFF
+constexpr int DB_WORDS = (WIN + DB_OFF) / 32 + 2;
+constexpr int kMaxLong = kChunk / (kLaneMax + 1) + 4;  // longer pre-tokens per chunk, + the last
+
+// merge-loop list entry: start (13 bits) | length (13 bits) << 13 | kind << 26
+enum : uint32_t { kShort = 0, kLong = 1, kOver = 2 };
+__device__ __forceinline__ uint32_t miss_entry(int st, int len, uint32_t kind) {
+  return (uint32_t)st | ((uint32_t)len << 13) | (kind << 26);
+}
+__device__ __forceinline__ int me_start(uint32_t e) { return (int)(e & 0x1FFFu); }
+__device__ __forceinline__ int me_len(uint32_t e) { return (int)((e >> 13) & 0x1FFFu); }
+__device__ __forceinline__ uint32_t me_kind(uint32_t e) { return e >> 26; }
+
+// Scratch for the workgroup reductions and the workgroup merge.
+template <int NT>
+struct Red {
+  int32_t red[NT / 64 + 4];
+  int64_t red64[NT / 64 + 4];
+  uint8_t mflag[NT];
+};
+
+// ---- merge loops ----------------------------------------------------------
+
+// Rank of (l, r) continuing the linear probe after slot h (rare path).
+__device__ __noinline__ int32_t rank_probe_from(const uint64_t *__restrict__ tab, int bits,
+                                                uint64_t key, uint64_t h) {
+  const uint64_t mask = (1ull << bits) - 1;
+  for (;;) {
+    h = (h + 1) & mask;
+    const uint64_t s = tab[h];
+    if ((s >> kSymBits) == key) return (int32_t)(s & ((1u << kSymBits) - 1));
+    if (s == kEmptySlot) return kRankInf;
+  }
+}
+
+
+// Merge one pre-token of len <= W bytes in registers and write its symbols
+// to out; returns their count.  Each round takes the lowest rank r among the
+// adjacent pairs and rewrites left to right: a pair of rank r merges into
+// symbol 256 + r unless its left symbol was just consumed.  Positions never
+// move: a consumed position is marked dead and each pair joins a live
+// position to the next live one, so all indexing is static.  The rank probes
+// of a round are issued together, eight positions at a time.
+template <int W>
+__device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const uint64_t *tab,
+                         const int bits, const int32_t *__restrict__ pair_rank) {
+  int32_t sym[W], rk[W];
+  uint32_t alive = len >= 32 ? ~0u : ((1u << len) - 1u);
+#pragma unroll
+  for (int i = 0; i < W; ++i) sym[i] = i < len ? (int32_t)b[i] : 0;
+  // the symbols are still bytes: their ranks come from the direct table
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    rk[i] = (i + 1 < len) ? pair_rank[(sym[i] << 8) | sym[i + 1]] : kRankInf;
+  const uint64_t mask = (1ull << bits) - 1;
+  for (;;) {
+    int32_t r = kRankInf;
+#pragma unroll
+    for (int i = 0; i < W; ++i) r = min(r, rk[i]);  // dead and last positions hold kRankInf
+    if (r == kRankInf) break;
+    const int32_t z = 256 + r;
+    bool carry = false;  // the previous live position merged: this one is consumed
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const bool live = (alive >> i) & 1u;
+      const bool consumed = live && carry;
+      const bool merge = live && !carry && rk[i] == r;
+      if (consumed) {
+        alive &= ~(1u << i);
+        rk[i] = kRankInf;
+      }
+      if (merge) sym[i] = z;
+      carry = live ? merge : carry;
+    }
+    // new ranks for the pairs that touch z, groups of 8 from the top
+    int32_t ns = -1;  // next live symbol above the current group
+#pragma unroll
+    for (int g = W / 8 - 1; g >= 0; --g) {
+      int32_t nx[8];
+      uint32_t need = 0;
+#pragma unroll
+      for (int j = 7; j >= 0; --j) {
+        const int i = 8 * g + j;
+        nx[j] = ns;
+        const bool live = (alive >> i) & 1u;
+        if (live && ns >= 0 && (sym[i] == z || ns == z)) need |= 1u << j;
+        if (live && ns < 0) rk[i] = kRankInf;
+        if (live) ns = sym[i];
+      }
+      if (need) {
+        uint64_t slot[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          slot[j] = kEmptySlot;
+          if ((need >> j) & 1u) slot[j] = tab[pair_hash(pair_key(sym[8 * g + j], nx[j]), bits)];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if ((need >> j) & 1u) {
+            const int i = 8 * g + j;
+            const uint64_t key = pair_key(sym[i], nx[j]);
+            if ((slot[j] >> kSymBits) == key) rk[i] = (int32_t)(slot[j] & ((1u << kSymBits) - 1));
+            else if (slot[j] == kEmptySlot) rk[i] = kRankInf;
+            else rk[i] = rank_probe_from(tab, bits, key, pair_hash(key, bits) & mask);
+          }
+        }
+      }
+    }
+  }
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    if ((alive >> i) & 1u) out[n++] = sym[i];
+  return n;
+}
+
+// The same rounds on arrays (one lane): Y[0..len) symbols, RK scratch;
+// survivors are compacted in place.  Returns the final symbol count.
+__device__ int lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_t *tab,
+                          const int bits, const int32_t *__restrict__ pair_rank) {
+  for (int i = 0; i + 1 < len; ++i) RK[i] = pair_rank[(Y[i] << 8) | Y[i + 1]];
+  RK[len - 1] = kRankInf;
+  int n = len;
+  for (;;) {
+    int32_t r = kRankInf;
+    for (int i = 0; i + 1 < n; ++i) r = min(r, RK[i]);
+    if (r == kRankInf) break;
+    const int32_t z = 256 + r;
+    int o = 0;
+    for (int i = 0; i < n; ++o) {
+      if (RK[i] == r) {
+        Y[o] = z;
+        i += 2;
+      } else {
+        Y[o] = Y[i];
+        RK[o] = RK[i];
+        i += 1;
+      }
+    }
+    n = o;
+    for (int j = 0; j + 1 < n; ++j)
+      if (Y[j] == z || Y[j + 1] == z) RK[j] = rank_of(tab, bits, Y[j], Y[j + 1]);
+    RK[n - 1] = kRankInf;
+  }
+  return n;
+}
+
+// The same rounds with the whole workgroup (NT threads) on Y[0..n), RK
+// scratch (global, position-indexed).  The lowest rank r is a workgroup
+// minimum; runs of consecutive pairs with rank r (only possible for a pair
+// (x, x)) merge at even offsets from the run start; survivors are compacted
+// in place tile by tile.  Returns the final symbol count.
+template <int NT>
+__device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const uint64_t *tab, int bits,
+                            const int32_t *__restrict__ pair_rank, Red<NT> &s) {
+  constexpr int PER = 4;
+  constexpr int TILE = NT * PER;
+  const int tid = threadIdx.x;
+  for (int64_t i = tid; i < n; i += NT)
+    RK[i] = (i + 1 < n) ? pair_rank[(Y[i] << 8) | Y[i + 1]] : kRankInf;
+  __syncthreads();
+  for (;;) {
+    int32_t r = kRankInf;
+    for (int64_t i = tid; i < n; i += NT) r = min(r, RK[i]);
+    r = block_min<NT>(r, s.red);
+    if (r == kRankInf) break;
+    const int32_t z = 256 + r;
+    int64_t out_base = 0;
+    int64_t anchor = -1;  // last position before the tile whose pair rank is not r
+    bool prev_m = false;  // the pair just before the tile merged
+    for (int64_t t0 = 0; t0 < n; t0 += TILE) {
+      const int64_t p0 = t0 + PER * (int64_t)tid;
+      int32_t y[PER], rk[PER];
+      uint32_t f = 0;
+      int64_t my_anchor = -1;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int64_t p = p0 + j;
+        const bool v = p < n;
+        rk[j] = v ? RK[p] : kRankInf;
+        y[j] = v ? Y[p] : 0;
+        if (v && rk[j] == r) f |= 1u << j;
+        else my_anchor = p;
+      }
+      int64_t tile_anchor;
+      int64_t za = block_excl_max64<NT>(my_anchor, -1, s.red64, &tile_anchor);
+      za = max(za, anchor);
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int64_t p = p0 + j;
+        if (!((f >> j) & 1u)) za = p;
+        else if (((p - 1 - za) & 1) == 0) m |= 1u << j;
+      }
+      s.mflag[tid] = (m >> (PER - 1)) & 1u;
+      __syncthreads();
+      const uint32_t mprev = tid ? (uint32_t)s.mflag[tid - 1] : (uint32_t)prev_m;
+      const bool tile_last_m = s.mflag[NT - 1] != 0;
+      // position p is consumed when the pair at p - 1 merged
+      const uint32_t consumed = ((m << 1) | mprev) & ((1u << PER) - 1u);
+      uint32_t keep = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (p0 + j < n && !((consumed >> j) & 1u)) keep |= 1u << j;
+      int tile_kept;
+      const int kex = block_excl_sum<int, NT>(__popc(keep), s.red, &tile_kept);
+      int64_t o = out_base + kex;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if ((keep >> j) & 1u) {
+          Y[o] = ((m >> j) & 1u) ? z : y[j];
+          RK[o] = rk[j];
+          ++o;
+        }
+      }
+      anchor = max(anchor, tile_anchor);
+      prev_m = tile_last_m;
+      out_base += tile_kept;
+      __syncthreads();
+    }
+    n = out_base;
+    for (int64_t i = tid; i < n; i += NT) {
+      if (i + 1 < n) {
+        const int32_t l = Y[i], rr = Y[i + 1];
+        if (l == z || rr == z) RK[i] = rank_of(tab, bits, l, rr);
+      } else {
+        RK[i] = kRankInf;
+      }
+    }
+    __syncthreads();
+  }
+  return n;
+}
+
+// ---- k_find -------------------------------------------------------------------
+
+struct FindShared {
+  alignas(16) uint8_t B[16 + WIN + 32];  // B[16 + p] = byte at window position p
+  uint32_t SB[SB_WORDS];                 // pre-token start bits, positions [0, WIN]
+  uint32_t DB[DB_WORDS];                 // document start bits, positions [-32, WIN)
+  uint16_t PS[kChunk + 2];               // owned pre-token starts in order, then the end
+  Red<WG> r;
+  int64_t o_lo, o_hi;
+};
+
+__device__ __forceinline__ uint32_t sb16(const FindShared &s, int g) {
+  return reinterpret_cast<const uint16_t *>(s.SB)[g];
+}
+
+__device__ __forceinline__ bool db_bit(const FindShared &s, int p) {
+  const int q = p + DB_OFF;
+  return (s.DB[q >> 5] >> (q & 31)) & 1u;
+}
+
+// Smallest start position in [from, WIN], or kNoStart.  Whole workgroup.
+__device__ int block_next_start(FindShared &s, int from) {
+  int cand = kNoStart;
+  if (from <= WIN) {
+    const int w = (from >> 5) + (int)threadIdx.x;
+    if (w <= (WIN >> 5)) {
+      uint32_t bits = s.SB[w];
+      if (w == (from >> 5)) bits &= ~0u << (from & 31);
+      if (bits) {
+        const int p = (w << 5) + __ffs(bits) - 1;
+        if (p <= WIN) cand = p;
+      }
+    }
+  }
+  return block_min<WG>(cand, s.r.red);
+}
+
+// The bytes of the pre-token at window position st (len <= kWordMax) as six
+// little-endian words, zero padded.
+__device__ __forceinline__ void pretoken_words(const FindShared &s, int st, int len,
+                                               uint32_t w[kWordWords]) {
+  const int b0 = 16 + st;
+  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
+  const int q = b0 >> 2;
+  const uint32_t sh = (uint32_t)(b0 & 3);
+  uint32_t raw[kWordWords + 1];
+#pragma unroll
+  for (int i = 0; i <= kWordWords; ++i) raw[i] = B32[q + i];
+#pragma unroll
+  for (int i = 0; i < kWordWords; ++i) {
+    const uint32_t v = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
+    const int valid = len - 4 * i;
+    const uint32_t m = valid >= 4 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : ((1u << (8 * valid)) - 1u));
+    w[i] = v & m;
+  }
+}
+
+// Symbol stored for these bytes in the word table, or -1.
+__device__ __forceinline__ int32_t word_lookup(const uint4 *__restrict__ tab, int bits,
+                                               const uint32_t w[kWordWords], int len) {
+  const uint32_t h = word_hash(w, len);
+  const uint32_t tag = word_tag(h, len);
+  const uint32_t mask = (1u << bits) - 1u;
+  uint32_t i = h & mask;
+  for (;;) {
+    const uint4 x = tab[2 * i];
+    if (x.x == 0) return -1;
+    if (x.x == tag && x.z == w[0] && x.w == w[1]) {
+      const uint4 y = tab[2 * i + 1];
+      if (y.x == w[2] && y.y == w[3] && y.z == w[4] && y.w == w[5]) return (int32_t)x.y;
+    }
+    i = (i + 1) & mask;
+  }
+}
+
+__global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
+  __shared__ FindShared s;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+
+  // document offsets check, spread over the grid
+  bool bad = false;
+  {
+    const int64_t per = (a.n_docs + 1 + gridDim.x - 1) / gridDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * per;
+    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += WG) {
+      const int64_t v = a.doc_off[i];
+      if (i == 0 && v != 0) bad = true;
+      if (i == a.n_docs && v != a.n_bytes) bad = true;
+      if (i < a.n_docs && a.doc_off[i + 1] < v) bad = true;
+    }
+  }
+
+  const int64_t c = blockIdx.x;
+  const int64_t c0 = c * kChunk;
+  const int64_t n = a.n_bytes;
+  const int nwin = (int)min<int64_t>(WIN, n - c0);
+  const int nown = (int)min<int64_t>(kChunk, n - c0);
+  const bool win_reaches_end = (c0 + nwin == n);
+  for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
+  __syncthreads();
+
+  // 1. document starts in the window (wave 0: a 64-way search for the first
+  //    document at or after the byte before the chunk, then 64 offsets per
+  //    load); bytes into LDS (all waves)
+  if (wave == 0) {
+    int64_t d0 = wave_lower_bound(a.doc_off, a.n_docs + 1, c0 - 1);
+    d0 = min(d0, a.n_docs);
+    int64_t olo = d0, ohi = d0;
+    for (;;) {
+      const int64_t d = d0 + lane;
+      const int64_t v = d < a.n_docs ? a.doc_off[d] : INT64_MAX;
+      const int64_t p = v - c0;
+      if (p >= -1 && p < nwin) atomicOr(&s.DB[(p + DB_OFF) >> 5], 1u << ((p + DB_OFF) & 31));
+      olo += __popcll(__ballot(v < c0));
+      ohi += __popcll(__ballot(v < c0 + nown));
+      if (!(__shfl(v, 63, 64) < c0 + nwin)) break;
+      d0 += 64;
+    }
+    if (lane == 0) {
+      s.o_lo = olo;
+      s.o_hi = ohi;
+    }
+  }
+  {
+    const bool aligned = (((uintptr_t)a.bytes) & 15u) == 0;
+    for (int g = tid - 1; g < WIN / 16; g += WG) {
+      const int64_t gp = c0 + 16 * (int64_t)g;
+      uint8_t *dst = &s.B[16 + 16 * g];
+      if (aligned && gp >= 0 && gp + 16 <= n) {
+        // streamed once: keep it out of the way of the tables in L2
+        *reinterpret_cast<u32x4 *>(dst) =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.bytes + gp));
+      } else {
+        for (int k = 0; k < 16; ++k) {
+          const int64_t q = gp + k;
+          dst[k] = (q >= 0 && q < n) ? a.bytes[q] : 0;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. start bits: a document start, or a class change unless a single space
+  //    that follows a non-whitespace byte (or opens the document) leads a
+  //    letter run.  Positions past the input end read as starts.
+  for (int g = tid; g < SB_HALF; g += WG) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int p = 16 * g + k;
+      bool st;
+      if (p >= nwin) {
+        st = win_reaches_end;
+      } else if (db_bit(s, p)) {
+        st = true;
+      } else {
+        const uint32_t b0 = s.B[16 + p], b1 = s.B[16 + p - 1], b2 = s.B[16 + p - 2];
+        const uint32_t k0 = byte_class(b0), k1 = byte_class(b1);
+        const bool attach = k0 == kL && b1 == 0x20u && (db_bit(s, p - 1) || byte_class(b2) != kW);
+        st = k0 != k1 && !attach;
+      }
+      m |= (uint32_t)st << k;
+    }
+    reinterpret_cast<uint16_t *>(s.SB)[g] = (uint16_t)m;
+  }
+  __syncthreads();
+
+  // last owned start and whether its pre-token runs past the window
+  uint32_t own = 0;
+  if (16 * tid < nown) {
+    own = sb16(s, tid);
+    const int lim = nown - 16 * tid;
+    if (lim < 16) own &= (1u << lim) - 1;
+  }
+  const int ls = block_max<WG>(own ? 16 * tid + 31 - __clz(own) : -1, s.r.red);
+  const int e_last = ls >= 0 ? block_next_start(s, ls + 1) : -1;
+  const bool overhang = ls >= 0 && e_last == kNoStart;
+
+  // 3. the owned pre-token starts as one ordered list, and the end of the last
+  int n_pt;
+  {
+    const int pex = block_excl_sum<int, WG>(__popc(own), s.r.red, &n_pt);
+    uint32_t m = own;
+    for (int k = pex; m; ++k, m &= m - 1) s.PS[k] = (uint16_t)(16 * tid + __ffs(m) - 1);
+    if (tid == 0) s.PS[n_pt] = (uint16_t)(overhang ? WIN : (ls >= 0 ? e_last : 0));
+  }
+  __syncthreads();
+
+  // 4. each thread resolves a contiguous block of the list: a single byte is
+  //    its own token; a pre-token that is a whole word-table entry takes its
+  //    symbol; the others (-1) go to the merge-loop list, in order
+  const int per = (n_pt + WG - 1) / WG;  // <= 16
+  const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
+  int32_t *pv = a.pv + c * kChunk;
+  uint32_t mbits = 0;
+  for (int k = k0; k < k1; ++k) {
+    const int st = s.PS[k];
+    int32_t res = -1;
+    if (!(overhang && k == n_pt - 1)) {
+      const int len = (int)s.PS[k + 1] - st;
+      if (len == 1) {
+        res = s.B[16 + st];
+      } else if (a.words && len <= kWordMax) {
+        uint32_t w[kWordWords];
+        pretoken_words(s, st, len, w);
+        res = word_lookup(a.words, a.word_bits, w, len);
+      }
+    }
+    pv[k] = res;
+    if (res < 0) mbits |= 1u << (k - k0);
+  }
+  int n_miss;
+  const int mex = block_excl_sum<int, WG>(__popc(mbits), s.r.red, &n_miss);
+  {
+    uint32_t *ml = a.miss + c * kMissMax;
+    int q = mex;
+    for (uint32_t m = mbits; m; m &= m - 1) {
+      const int k = k0 + __ffs(m) - 1;
+      const int st = s.PS[k];
+      if (overhang && k == n_pt - 1) {
+        ml[q++] = miss_entry(st, 0, kOver);
+      } else {
+        const int len = (int)s.PS[k + 1] - st;
+        ml[q++] = miss_entry(st, len, len > kLaneMax ? kLong : kShort);
+      }
+    }
+  }
+  const bool any_bad = __syncthreads_or(bad);
+  if (tid == 0) {
+    a.meta[4 * c] = n_pt;
+    a.meta[4 * c + 1] = n_miss;
+    a.meta[4 * c + 2] = any_bad ? (int32_t)BPE_STATUS_BAD_DOC_OFFSETS : 0;
+    a.doc_rng[2 * c] = s.o_lo;
+    a.doc_rng[2 * c + 1] = s.o_hi;
+  }
+  // each document that starts here: the index of its first pre-token
+  for (int64_t d = s.o_lo + tid; d < s.o_hi; d += WG) {
+    const int p = (int)min(max(a.doc_off[d] - c0, (int64_t)0), (int64_t)kChunk - 1);
+    int lo = 0, hi = n_pt;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)s.PS[mid] < p) lo = mid + 1;
+      else hi = mid;
+    }
+    a.doc_pt[d] = lo;
+  }
+}
+
+// ---- k_merge ------------------------------------------------------------------
+
+constexpr int kMidSlots = 16;  // lanes that merge a 17..kLaneMax-byte pre-token in LDS at once
+
+struct MergeShared {
+  int32_t y[kMidSlots][kLaneMax + 1];  // symbols and ranks of the array merge
+  int32_t rk[kMidSlots][kLaneMax + 1];
+  int32_t longs[kMaxLong];
+  int32_t n_long;
+  Red<MWG> r;
+};
+
+// End (exclusive, global) of the pre-token that starts at gs and has no start
+// in the window, scanning bytes from `from` on (one wave).
+__device__ int64_t wave_global_end(const EncodeArgs &a, int64_t gs, int64_t from) {
+  const int lane = lane_id();
+  const int64_t d = wave_lower_bound(a.doc_off, a.n_docs + 1, gs + 1);
+  int64_t limit = d <= a.n_docs ? a.doc_off[d] : a.n_bytes;
+  limit = min(max(limit, gs + 1), a.n_bytes);
+  const uint8_t *b = a.bytes;
+  // from > gs + 1 always (the pre-token fills the window), so q - 1 > gs is
+  // inside the document and is not a document start
+  for (int64_t q0 = max(from, gs + 2); q0 < limit; q0 += 64 * 16) {
+    int cand = kNoStart;
+    for (int j = 0; j < 16; ++j) {
+      const int64_t q = q0 + 16 * (int64_t)lane + j;
+      if (q >= limit) break;
+      const uint32_t c0 = byte_class(b[q]), b1 = b[q - 1], c1 = byte_class(b1);
+      const bool attach = c0 == kL && b1 == 0x20u && byte_class(b[q - 2]) != kW;
+      if (c0 != c1 && !attach) {
+        cand = 16 * lane + j;
+        break;
+      }
+    }
+    for (int dd = 32; dd >= 1; dd >>= 1) cand = min(cand, __shfl_xor(cand, dd, 64));
+    if (cand != kNoStart) return q0 + cand;
+  }
+  return limit;
+}
+
+// Merge-loop list of one chunk (one wave).  The tokens of the pre-token at
+// global position g go to gsym[g ..]: never more tokens than bytes, so the
+// pre-tokens' regions do not overlap.  mt[i] gets each entry's token count,
+// tot[c] the chunk's.
+__global__ void __launch_bounds__(MWG) k_merge(EncodeArgs a) {
+  __shared__ MergeShared s;
+  const int lane = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  const int64_t c0 = c * kChunk;
+  const int n_pt = a.meta[4 * c], n_miss = a.meta[4 * c + 1];
+  const uint32_t *ml = a.miss + c * kMissMax;
+  int32_t *mt = a.mt + c * kMissMax;
+  const uint8_t *bytes = a.bytes + c0;
+  int32_t *gsym = a.gsym + c0;
+  if (lane == 0) s.n_long = 0;
+  __syncthreads();
+
+  // entries of <= kLaneMax bytes: one per lane, in registers up to 16 bytes
+  int tok = 0;
+  for (int i0 = 0; i0 < n_miss; i0 += MWG) {
+    const int i = i0 + lane;
+    uint32_t e = 0;
+    int nt = 0;
+    bool mid = false;
+    if (i < n_miss) {
+      e = ml[i];
+      const int st = me_start(e), len = me_len(e);
+      if (me_kind(e) != kShort)
+        s.longs[atomicAdd(&s.n_long, 1)] = i;
+      else if (len <= 8)
+        nt = reg_merge<8>(bytes + st, len, gsym + st, a.table, a.table_bits, a.pair_rank);
+      else if (len <= 16)
+        nt = reg_merge<16>(bytes + st, len, gsym + st, a.table, a.table_bits, a.pair_rank);
+      else
+        mid = true;
+    }
+    // 17..kLaneMax bytes: arrays in LDS, kMidSlots lanes at a time
+    const uint64_t mm = __ballot(mid);
+    if (mm) {
+      const int rank = __popcll(mm & ((1ull << lane) - 1));
+      for (int p0 = 0; p0 < __popcll(mm); p0 += kMidSlots) {
+        if (mid && rank >= p0 && rank < p0 + kMidSlots) {
+          const int slot = rank - p0;
+          const int st = me_start(e), len = me_len(e);
+          int32_t *y = s.y[slot];
+          for (int j = 0; j < len; ++j) y[j] = bytes[st + j];
+          nt = lane_merge(y, s.rk[slot], len, a.table, a.table_bits, a.pair_rank);
+          for (int j = 0; j < nt; ++j) gsym[st + j] = y[j];
+        }
+      }
+    }
+    if (i < n_miss && me_kind(e) == kShort) mt[i] = nt;
+    tok += nt;
+  }
+  tok = wave_sum(tok);
+  int64_t tot = (int64_t)(n_pt - n_miss) + tok;  // every other pre-token is one token
+  __syncthreads();
+
+  // longer entries: the whole wave, in place in the position-indexed scratch
+  const int n_long = s.n_long;
+  for (int q = 0; q < n_long; ++q) {
+    const int i = s.longs[q];
+    const uint32_t e = ml[i];
+    const int64_t gs = c0 + me_start(e);
+    const int64_t ge = me_kind(e) == kLong ? gs + me_len(e) : wave_global_end(a, gs, c0 + WIN);
+    for (int64_t p = gs + lane; p < ge; p += MWG) a.gsym[p] = a.bytes[p];
+    __syncthreads();
+    const int64_t nt =
+        wg_merge<MWG>(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits, a.pair_rank, s.r);
+    if (lane == 0) mt[i] = (int32_t)nt;
+    tot += nt;
+    __syncthreads();
+  }
+  if (lane == 0) a.tot[c] = tot;
+}
+
+// ---- k_offsets ---------------------------------------------------------------
+
+// Exclusive prefix of the per-chunk token counts, and the status word from
+// the chunks' status bits (one workgroup).
+__global__ void __launch_bounds__(OWG) k_offsets(EncodeArgs a) {
+  __shared__ int64_t red64[OWG / 64];
+  chunk_offsets<OWG>(a.tot, a.off, a.meta + 2, 4, a.n_chunks, a.status, red64);
+}
+
+// ---- k_emit -------------------------------------------------------------------
+
+struct EmitShared {
+  int32_t tokoff[kChunk + 1];  // token offset of each pre-token within the chunk
+  int64_t lw[kMaxLong];        // longer entries: output position, symbols, count
+  int64_t lsrc[kMaxLong];
+  int64_t lnt[kMaxLong];
+  int32_t n_long;
+  Red<WG> r;
+};
+
+__global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
+  __shared__ EmitShared s;
+  const int tid = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  const int64_t c0 = c * kChunk;
+  const int n_pt = a.meta[4 * c];
+  const int64_t base = a.off[c];
+  const int32_t *pv = a.pv + c * kChunk;
+  const uint32_t *ml = a.miss + c * kMissMax;
+  const int32_t *mt = a.mt + c * kMissMax;
+  const int32_t *gsym = a.gsym + c0;
+  if (tid == 0) s.n_long = 0;
+
+  const int per = (n_pt + WG - 1) / WG;
+  const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
+  uint32_t mbits = 0;
+  for (int k = k0; k < k1; ++k)
+    if (pv[k] < 0) mbits |= 1u << (k - k0);
+  int n_miss;
+  const int mex = block_excl_sum<int, WG>(__popc(mbits), s.r.red, &n_miss);
+  int64_t cnt = k1 - k0 - __popc(mbits);
+  for (int q = mex; q < mex + __popc(mbits); ++q) cnt += mt[q];
+  int64_t total;
+  const int64_t ex = block_excl_sum<int64_t, WG>(cnt, s.r.red64, &total);
+  if (tid == 0) s.tokoff[n_pt] = (int32_t)total;
+  bool overflow = false;
+  {
+    int64_t w = base + ex;
+    int q = mex;
+    for (int k = k0; k < k1; ++k) {
+      s.tokoff[k] = (int32_t)(w - base);
+      const int32_t x = pv[k];
+      if (x >= 0) {
+        if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, x);
+        else overflow = true;
+        ++w;
+        continue;
+      }
+      const uint32_t e = ml[q];
+      const int64_t nt = mt[q];
+      if (me_kind(e) == kShort) {
+        const int32_t *src = gsym + me_start(e);
+        for (int j = 0; j < nt; ++j, ++w) {
+          if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, src[j]);
+          else overflow = true;
+        }
+      } else {
+        const int slot = atomicAdd(&s.n_long, 1);
+        s.lw[slot] = w;
+        s.lsrc[slot] = c0 + me_start(e);
+        s.lnt[slot] = nt;
+        w += nt;
+      }
+      ++q;
+    }
+  }
+  __syncthreads();
+  // longer entries' symbols, copied by the whole workgroup
+  for (int q = 0; q < s.n_long; ++q) {
+    const int64_t w0 = s.lw[q], src = s.lsrc[q], nt = s.lnt[q];
+    for (int64_t j = tid; j < nt; j += WG) {
+      const int64_t w = w0 + j;
+      if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, a.gsym[src + j]);
+      else overflow = true;
+    }
+  }
+  if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
+  // per-document offsets: a document starting at pre-token k begins after
+  // every token of the pre-tokens before k
+  const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
+  for (int64_t d = dlo + tid; d < dhi; d += WG) {
+    const int k = min(max(a.doc_pt[d], 0), n_pt);
+    a.id_off[d] = base + s.tokoff[k];
+  }
+  if (c == a.n_chunks - 1) {
+    const int64_t end = base + a.tot[c];
+    for (int64_t d = dhi + tid; d <= a.n_docs; d += WG) a.id_off[d] = end;
+  }
+}
+
+// Empty input (one workgroup): clear the status, then check that every
+// offset is zero and write zero offsets.
+__global__ void k_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, int64_t *out_off,
+                        int32_t *status) {
+  if (threadIdx.x == 0) *status = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int64_t i = threadIdx.x; i <= n_docs; i += blockDim.x) {
+    if (offs[i] != 0) bad = true;
+    out_off[i] = 0;
+  }
+  if (bad) atomicOr(status, (int32_t)bad_bit);
+}
+
+}  // namespace
+
+hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, int64_t *out_off,
+                        int32_t *status, hipStream_t stream) {
+  hipLaunchKernelGGL(k_empty, dim3(1), dim3(256), 0, stream, offs, n_docs, bad_bit, out_off,
+                     status);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream) {
+  const unsigned G = (unsigned)a.n_chunks;
+  hipLaunchKernelGGL(k_find, dim3(G), dim3(WG), 0, stream, a);
+  hipLaunchKernelGGL(k_merge, dim3(G), dim3(MWG), 0, stream, a);
+  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(OWG), 0, stream, a);
+  hipLaunchKernelGGL(k_emit, dim3(G), dim3(WG), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bpe

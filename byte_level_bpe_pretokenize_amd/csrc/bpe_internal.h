@@ -48,12 +48,6 @@ __host__ __device__ inline uint32_t word_tag(uint32_t h, int len) {
   return (h & 0xFFFFFF00u) | (uint32_t)len;
 }
 
-// ---- look-back flags ----------------------------------------------------
-// One 64-bit word per chunk: bits 62..63 state, bits 0..61 value.
-constexpr uint64_t kFlagAgg = 1ull << 62;     // value = this chunk's count
-constexpr uint64_t kFlagPrefix = 2ull << 62;  // value = count up to and including this chunk
-constexpr uint64_t kFlagValue = (1ull << 62) - 1;
-
 // ---- encode geometry ----------------------------------------------------
 constexpr int kEncThreads = 256;     // one workgroup = 4 wave64
 constexpr int kChunk = 4096;         // bytes whose pre-token starts a workgroup owns
@@ -70,32 +64,57 @@ inline int64_t dec_chunks(int64_t n_ids) { return (n_ids + kDecChunk - 1) / kDec
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Encode workspace: [ticket 256 B][flags 8*G][first doc 8*G][symbols 4*N]
-// [ranks 4*N].  The symbol/rank regions hold the pre-tokens that run the
-// merge loop, each at its own byte position, so no two overlap.
+// Per-chunk record size of the encode pipeline.
+constexpr int kMissMax = kChunk / 2 + 16;  // merge-loop pre-tokens per chunk (each >= 2 bytes)
+
+// Encode workspace, all regions 256-byte aligned:
+//   meta      [G][4] i32  pre-tokens, merge-loop pre-tokens, status bits, 0
+//   tot, off  [G] i64   token count per chunk, then its exclusive prefix
+//   doc_rng   [G][2] i64  documents that start in the chunk
+//   doc_pt    [D] i32   index of each document's first pre-token in its chunk
+//   pv        [G][kChunk] i32    result per pre-token (symbol, or -1: see the list)
+//   miss      [G][kMissMax] u32  merge-loop list: start | len << 13 | kind << 26
+//   mt        [G][kMissMax] i32  token count of each list entry
+//   gsym      [N] i32   tokens of the list entry that starts at byte g, from gsym[g] on
+//   grank     [N] i32   pair ranks of the workgroup merge, position-indexed
 struct EncLayout {
-  size_t ticket, flags, first_doc, gsym, grank, total;
+  size_t meta, tot, off, doc_rng, doc_pt, pv, miss, mt, gsym, grank, total;
 };
-inline EncLayout enc_layout(int64_t n_bytes) {
+inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   EncLayout L;
-  int64_t G = enc_chunks(n_bytes);
-  L.ticket = 0;
-  L.flags = 256;
-  L.first_doc = L.flags + align256(8 * (size_t)G);
-  L.gsym = L.first_doc + align256(8 * (size_t)G);
-  L.grank = L.gsym + align256(4 * (size_t)n_bytes);
-  L.total = L.grank + align256(4 * (size_t)n_bytes);
+  const size_t G = (size_t)enc_chunks(n_bytes);
+  size_t o = 0;
+  auto take = [&o](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.meta = take(16 * G);
+  L.tot = take(8 * G);
+  L.off = take(8 * G);
+  L.doc_rng = take(16 * G);
+  L.doc_pt = take(4 * (size_t)(n_docs + 1));
+  L.pv = take(4 * (size_t)kChunk * G);
+  L.miss = take(4 * (size_t)kMissMax * G);
+  L.mt = take(4 * (size_t)kMissMax * G);
+  L.gsym = take(4 * (size_t)n_bytes);
+  L.grank = take(4 * (size_t)n_bytes);
+  L.total = o;
   return L;
 }
 
+// Decode workspace: tot, off [G] i64 (byte count per chunk of IDs, then its
+// exclusive prefix), flag [G] i32 (status bits found by the chunk).
 struct DecLayout {
-  size_t ticket, flags, total;
+  size_t tot, off, flag, total;
 };
 inline DecLayout dec_layout(int64_t n_ids) {
   DecLayout L;
-  L.ticket = 0;
-  L.flags = 256;
-  L.total = L.flags + align256(8 * (size_t)dec_chunks(n_ids));
+  const size_t G = (size_t)dec_chunks(n_ids);
+  L.tot = 0;
+  L.off = align256(8 * G);
+  L.flag = L.off + align256(8 * G);
+  L.total = L.flag + align256(4 * G);
   return L;
 }
 
@@ -109,13 +128,18 @@ struct EncodeArgs {
   int64_t *id_off;
   const uint64_t *table;
   int table_bits;
-  const int32_t *id_map;  // nullptr = identity
+  const int32_t *id_map;     // nullptr = identity
   const int32_t *pair_rank;  // [65536]: rank of the byte pair (a, b) at a * 256 + b
   const uint4 *words;        // word table: 2 uint4 per slot; nullptr = none
   int word_bits;
-  uint32_t *ticket;
-  uint64_t *flags;
-  const int64_t *first_doc;  // [n_chunks]
+  int32_t *meta;
+  int64_t *tot;
+  int64_t *off;
+  int64_t *doc_rng;
+  int32_t *doc_pt;
+  int32_t *pv;
+  uint32_t *miss;
+  int32_t *mt;
   int32_t *gsym;
   int32_t *grank;
   int32_t *status;
@@ -135,23 +159,21 @@ struct DecodeArgs {
   const int32_t *inv_map;    // nullptr = identity; else [inv_size], -1 = no symbol
   int64_t inv_size;
   int64_t vocab;
-  uint32_t *ticket;
-  uint64_t *flags;
+  int64_t *tot;
+  int64_t *off;
+  int32_t *flag;
   int32_t *status;
   int64_t n_chunks;
 };
 
-// Launchers (bpe_kernels.hip).
-// Clears the ticket, the status word and n_flags look-back flags; with
-// first_doc, also records each chunk's first document (encode).
-hipError_t launch_clear(uint32_t *ticket, uint64_t *flags, int64_t n_flags, int32_t *status,
-                        int64_t *first_doc, const int64_t *doc_off, int64_t n_docs,
-                        hipStream_t stream);
+// Launchers.
 // Empty input: clears the status, checks that offs[0..n_docs] are all zero
-// (else sets bad_bit) and writes zeros to out_off[0..n_docs].
+// (else sets bad_bit) and writes zeros to out_off[0..n_docs]  (bpe_encode.hip).
 hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, int64_t *out_off,
                         int32_t *status, hipStream_t stream);
+// The encode pipeline for n_bytes > 0 (bpe_encode.hip).
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
+// The decode pipeline for n_ids > 0 (bpe_decode.hip).
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace bpe
