@@ -8,10 +8,21 @@ already resident in HBM.  Prints one JSON line.  The default workload is the
 throughput workload: 4,096 documents of 64 KiB (256 MiB) with the
 32,000-merge table.  The CPU baseline is the oracle, single-threaded, on the
 first documents of the same batch; its IDs are checked against the GPU's.
+
+The roofline object covers one encode call: its four kernels run back to
+back on one stream, and the library's stage timing (HIP events recorded
+between them during the timed steps) gives each kernel's average duration.
+Algorithmic bytes are the call's: the input read once, the IDs and the
+per-document offsets written once (N + 4T + 16(D + 1)).  Measured HBM
+traffic comes from profiles/traffic_<workload>.json (rocprofv3 FETCH_SIZE and
+WRITE_SIZE per call, scaled by a plain copy's counts) and is reported only
+while the kernel sources still hash to the value recorded there.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +34,31 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of every source the kernels are built from."""
+    files = sorted(glob.glob(os.path.join(ROOT, "byte_level_bpe_pretokenize_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "bpe.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per encode call from the committed counter summary, or None
+    when it is missing or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return int(rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"])
 
 
 def parse():
@@ -107,6 +143,19 @@ def main():
     def step():
         model.encode_batch_into(data, doc_off, ids, id_off, ws, status, stream)
 
+    # device-to-device copy bandwidth of this machine, for context
+    copy = torch.empty_like(data)
+    for _ in range(3):
+        copy.copy_(data)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        copy.copy_(data)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * N * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del copy
+
     if args.copy_calibration:
         # a plain copy kernel of known size: reads and writes n_bytes once
         copy = torch.empty_like(data)
@@ -121,22 +170,30 @@ def main():
         raise SystemExit(f"device status {st:#x} after warm-up")
     T = int(id_off[-1].item())
 
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    start, stop = evs[0], evs[-1]
+    model.stage_timing(True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        evs[k].record(stream)
         step()
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
+    per_step = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
+    stage_ms, calls = model.stage_times("encode")
+    model.stage_timing(False)
     st = int(status.item())
     if st:
         raise SystemExit(f"device status {st:#x} in the timed region")
+    kern = {k: v / max(1, calls) for k, v in stage_ms.items()}
+    path_ms = sum(kern.values())
+    dominant = max(kern, key=kern.get)
 
     sec = ms / 1e3
     alg_bytes = N + 4 * T + 16 * (D + 1)
-    achieved = alg_bytes / sec / 1e9
+    achieved = alg_bytes / (path_ms / 1e3) / 1e9
+    traffic = measured_traffic(args.workload)
 
     # decode of the same IDs (round trip), timed the same way
     dec = {}
@@ -164,7 +221,6 @@ def main():
 
     ids_np = ids[:T].cpu().numpy()
     id_off_np = id_off.cpu().numpy()
-    import hashlib
     cpu, fnv = None, None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(merges, batch, ids_np, id_off_np, args.cpu_seconds)
@@ -189,14 +245,22 @@ def main():
             "n_bytes": N, "n_docs": D, "n_merges": int(merges.shape[0]), "tokens": T,
         },
         "tokens_per_s": round(T / sec, 1),
+        "ms_median": round(per_step[len(per_step) // 2], 4),
+        "ms_min": round(per_step[0], 4),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "scope": "one encode call: " + " + ".join(kern),
             "algorithmic_bytes": alg_bytes,
+            "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+            "dominant": dominant,
+            "timed_calls": calls,
+            "copy_GBps": round(copy_gbs, 1),
+            "frac_of_copy": round(achieved / copy_gbs, 4),
         },
         "cpu_baseline": cpu,
         "ids_fnv1a64": fnv,

@@ -11,13 +11,16 @@ LIB_PATH = os.path.join(PKG, "libbpe.so")
 SYMBOLS = (
     "bpe_load_merges", "bpe_free", "bpe_vocab_size", "bpe_max_token_bytes",
     "bpe_encode_workspace_bytes", "bpe_encode_batch",
-    "bpe_decode_workspace_bytes", "bpe_decode_batch", "bpe_strerror",
+    "bpe_decode_workspace_bytes", "bpe_decode_batch",
+    "bpe_stage_timing", "bpe_stage_count", "bpe_stage_name", "bpe_stage_times",
+    "bpe_strerror",
 )
 
 BPE_OK, BPE_EINVAL, BPE_EMERGES, BPE_EIDMAP, BPE_EWORKSPACE, BPE_EHIP, BPE_ENOMEM, BPE_ENOTSUP = \
     0, -1, -2, -3, -4, -5, -6, -7
 STATUS_BAD_DOC_OFFSETS, STATUS_IDS_CAPACITY, STATUS_BAD_ID, STATUS_BYTES_CAPACITY, \
     STATUS_BAD_ID_OFFSETS = 1, 2, 4, 8, 16
+OP_ENCODE, OP_DECODE = 0, 1
 MAX_MERGES = 1 << 20
 MAX_ID = (1 << 24) - 1
 
@@ -50,6 +53,14 @@ def load() -> C.CDLL:
     L.bpe_decode_workspace_bytes.restype = sz
     L.bpe_decode_batch.argtypes = [p, p, i64, p, i64, p, i64, p, p, sz, p, p]
     L.bpe_decode_batch.restype = i32
+    L.bpe_stage_timing.argtypes = [p, i32]
+    L.bpe_stage_timing.restype = i32
+    L.bpe_stage_count.argtypes = [i32]
+    L.bpe_stage_count.restype = i32
+    L.bpe_stage_name.argtypes = [i32, i32]
+    L.bpe_stage_name.restype = C.c_char_p
+    L.bpe_stage_times.argtypes = [p, i32, C.POINTER(C.c_double), i32, C.POINTER(C.c_int64)]
+    L.bpe_stage_times.restype = i32
     L.bpe_strerror.argtypes = [i32]
     L.bpe_strerror.restype = C.c_char_p
     _lib = L

@@ -76,6 +76,25 @@ class Model:
     def max_token_bytes(self) -> int:
         return int(_lib.load().bpe_max_token_bytes(self._h))
 
+    # ---- stage timing (bpe_stage_timing / bpe_stage_times) -------------------
+    def stage_timing(self, enable: bool = True) -> None:
+        rc = _lib.load().bpe_stage_timing(self._h, 1 if enable else 0)
+        if rc != _lib.BPE_OK:
+            raise BPEError(rc, "bpe_stage_timing")
+
+    def stage_times(self, op: str = "encode") -> tuple[dict[str, float], int]:
+        """Total milliseconds per kernel over the timed calls since the last
+        read, and the number of those calls (waits for their events)."""
+        L = _lib.load()
+        code = {"encode": _lib.OP_ENCODE, "decode": _lib.OP_DECODE}[op]
+        n = L.bpe_stage_count(code)
+        ms = (C.c_double * n)()
+        calls = C.c_int64()
+        rc = L.bpe_stage_times(self._h, code, ms, n, C.byref(calls))
+        if rc != _lib.BPE_OK:
+            raise BPEError(rc, "bpe_stage_times")
+        return {L.bpe_stage_name(code, k).decode(): float(ms[k]) for k in range(n)}, int(calls.value)
+
     # ---- encode -------------------------------------------------------------
     def encode_workspace_bytes(self, n_bytes: int, n_docs: int) -> int:
         return int(_lib.load().bpe_encode_workspace_bytes(self._h, n_bytes, n_docs))

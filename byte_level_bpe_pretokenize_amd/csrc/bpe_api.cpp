@@ -33,12 +33,49 @@ struct bpe_model {
   uint8_t *d_exp_bytes = nullptr;
   int32_t *d_inv_map = nullptr;
   int64_t inv_size = 0;
+  // stage timing (bpe_stage_timing): events of the calls not yet read, per
+  // op, stages + 1 per call; spare events for reuse
+  bool timing = false;
+  mutable std::vector<hipEvent_t> rec[2];
+  mutable std::vector<hipEvent_t> spare;
 };
 
 namespace {
 
+constexpr int kStages[2] = {kEncStages, kDecStages};
+
+void drop_events(bpe_model *m) {
+  for (auto &r : m->rec) {
+    m->spare.insert(m->spare.end(), r.begin(), r.end());
+    r.clear();
+  }
+}
+
+// Events for one timed call of op (nullptr when timing is off or events run out).
+hipEvent_t *call_events(const bpe_model *m, int op) {
+  if (!m->timing) return nullptr;
+  const int n = kStages[op] + 1;
+  std::vector<hipEvent_t> &r = m->rec[op];
+  for (int i = 0; i < n; ++i) {
+    hipEvent_t e = nullptr;
+    if (!m->spare.empty()) {
+      e = m->spare.back();
+      m->spare.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+      // give back what this call took
+      m->spare.insert(m->spare.end(), r.end() - i, r.end());
+      r.resize(r.size() - i);
+      return nullptr;
+    }
+    r.push_back(e);
+  }
+  return r.data() + r.size() - n;
+}
+
 void free_model(bpe_model *m) {
   if (!m) return;
+  drop_events(m);
+  for (hipEvent_t e : m->spare) (void)hipEventDestroy(e);
   if (m->d_table) (void)hipFree(m->d_table);
   if (m->d_id_map) (void)hipFree(m->d_id_map);
   if (m->d_pair_rank) (void)hipFree(m->d_pair_rank);
@@ -60,6 +97,29 @@ int upload(T **dst, const T *src, size_t count, hipStream_t stream) {
                  hipSuccess)
     return BPE_EHIP;
   return BPE_OK;
+}
+
+// Place every (key, rank) in one of its two slots; false if some key cannot
+// be placed within a bounded number of displacements (the caller retries
+// with twice the capacity).
+bool build_cuckoo(const std::vector<uint64_t> &keys, int bits, std::vector<uint64_t> &table) {
+  table.assign((size_t)1 << bits, kEmptySlot);
+  const int64_t max_kicks = 64 + 4 * (int64_t)bits;
+  for (size_t r = 0; r < keys.size(); ++r) {
+    uint64_t item = (keys[r] << kSymBits) | (uint64_t)r;
+    uint64_t h = pair_slot0(keys[r], bits);
+    for (int64_t kick = 0;; ++kick) {
+      const uint64_t key = item >> kSymBits;
+      const uint64_t a = pair_slot0(key, bits), b = pair_slot1(key, bits);
+      if (table[(size_t)a] == kEmptySlot) { table[(size_t)a] = item; break; }
+      if (table[(size_t)b] == kEmptySlot) { table[(size_t)b] = item; break; }
+      if (kick == max_kicks) return false;
+      // evict the occupant of the slot this item did not come from
+      h = (h == a) ? b : a;
+      std::swap(item, table[(size_t)h]);
+    }
+  }
+  return true;
 }
 
 bool on_model_device(const bpe_model *m) {
@@ -106,7 +166,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.grank = (int32_t *)(ws + L.grank);
   a.status = d_status;
   a.n_chunks = enc_chunks(n_bytes);
-  if (launch_encode(a, stream) != hipSuccess) return BPE_EHIP;
+  if (launch_encode(a, stream, call_events(model, BPE_OP_ENCODE)) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }
 
@@ -283,15 +343,13 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
     }
   }
 
-  // rank table: power-of-two capacity >= 2R, linear probing
+  // rank table: two-choice cuckoo hashing, power-of-two capacity >= 2.5R
   int bits = 8;
-  while (((int64_t)1 << bits) < 2 * R) ++bits;
-  std::vector<uint64_t> table((size_t)1 << bits, kEmptySlot);
-  const uint64_t mask = ((uint64_t)1 << bits) - 1;
-  for (int64_t r = 0; r < R; ++r) {
-    uint64_t h = pair_hash(keys[(size_t)r], bits);
-    while (table[(size_t)h] != kEmptySlot) h = (h + 1) & mask;
-    table[(size_t)h] = (keys[(size_t)r] << kSymBits) | (uint64_t)r;
+  while (((int64_t)1 << bits) < 5 * R / 2) ++bits;
+  std::vector<uint64_t> table;
+  for (;; ++bits) {
+    if (bits > 40) return BPE_ENOMEM;
+    if (build_cuckoo(keys, bits, table)) break;
   }
 
   bpe_model *m = new (std::nothrow) bpe_model;
@@ -424,11 +482,47 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
   a.vocab = model->V;
   a.tot = (int64_t *)(ws + L.tot);
   a.off = (int64_t *)(ws + L.off);
-  a.flag = (int32_t *)(ws + L.flag);
   a.status = d_status;
   a.n_chunks = dec_chunks(n_ids);
-  if (launch_decode(a, stream) != hipSuccess) return BPE_EHIP;
+  if (launch_decode(a, stream, call_events(model, BPE_OP_DECODE)) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
+}
+
+int bpe_stage_timing(bpe_model *model, int enable) {
+  if (!model) return BPE_EINVAL;
+  drop_events(model);
+  model->timing = enable != 0;
+  return BPE_OK;
+}
+
+int bpe_stage_count(int op) { return (op == BPE_OP_ENCODE || op == BPE_OP_DECODE) ? kStages[op] : -1; }
+
+const char *bpe_stage_name(int op, int stage) {
+  if (op == BPE_OP_ENCODE && stage >= 0 && stage < kEncStages) return kEncStageNames[stage];
+  if (op == BPE_OP_DECODE && stage >= 0 && stage < kDecStages) return kDecStageNames[stage];
+  return nullptr;
+}
+
+int bpe_stage_times(bpe_model *model, int op, double *ms, int max_stages, int64_t *n_calls) {
+  if (!model || (op != BPE_OP_ENCODE && op != BPE_OP_DECODE) || !ms || !n_calls ||
+      max_stages < kStages[op])
+    return BPE_EINVAL;
+  const int n = kStages[op] + 1;
+  std::vector<hipEvent_t> &r = model->rec[op];
+  for (int k = 0; k < kStages[op]; ++k) ms[k] = 0.0;
+  int rc = BPE_OK;
+  for (size_t c = 0; c + n <= r.size(); c += n) {
+    if (hipEventSynchronize(r[c + n - 1]) != hipSuccess) rc = BPE_EHIP;
+    for (int k = 0; k < kStages[op] && rc == BPE_OK; ++k) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, r[c + k], r[c + k + 1]) != hipSuccess) rc = BPE_EHIP;
+      ms[k] += t;
+    }
+  }
+  *n_calls = (int64_t)(r.size() / n);
+  model->spare.insert(model->spare.end(), r.begin(), r.end());
+  r.clear();
+  return rc;
 }
 
 const char *bpe_strerror(int code) {

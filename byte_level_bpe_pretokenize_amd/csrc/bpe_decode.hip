@@ -64,15 +64,12 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   (void)block_excl_sum<int64_t, DWG>(mine, red64, &total);
   const int bits = (__syncthreads_or(bad_id) ? (int)BPE_STATUS_BAD_ID : 0) |
                    (__syncthreads_or(bad_off) ? (int)BPE_STATUS_BAD_ID_OFFSETS : 0);
-  if (tid == 0) {
-    a.tot[c] = total;
-    a.flag[c] = bits;
-  }
+  if (tid == 0) a.tot[c] = total | ((int64_t)bits << kCountBits);
 }
 
 __global__ void __launch_bounds__(SWG) k_dec_scan(DecodeArgs a) {
   __shared__ int64_t red64[SWG / 64];
-  chunk_offsets<SWG>(a.tot, a.off, a.flag, 1, a.n_chunks, a.status, red64);
+  chunk_offsets<SWG>(a.tot, a.off, a.n_chunks, a.status, red64);
 }
 
 struct WriteShared {
@@ -146,11 +143,17 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+const char *const kDecStageNames[kDecStages] = {"k_dec_len", "k_dec_scan", "k_dec_write"};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t *ev) {
   const unsigned G = (unsigned)a.n_chunks;
+  if (ev) (void)hipEventRecord(ev[0], stream);
   hipLaunchKernelGGL(k_dec_len, dim3(G), dim3(DWG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[1], stream);
   hipLaunchKernelGGL(k_dec_scan, dim3(1), dim3(SWG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[2], stream);
   hipLaunchKernelGGL(k_dec_write, dim3(G), dim3(DWG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[3], stream);
   return hipGetLastError();
 }
 

@@ -29,18 +29,18 @@ __device__ __forceinline__ uint32_t byte_class(uint32_t b) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-// Rank of the pair (l, r), or kRankInf.  Linear probing from the pair's hash.
+// Rank held by a loaded slot pair for key, or kRankInf.
+__device__ __forceinline__ int32_t rank_in(uint64_t s0, uint64_t s1, uint64_t key) {
+  if ((s0 >> kSymBits) == key) return (int32_t)(s0 & ((1u << kSymBits) - 1));
+  if ((s1 >> kSymBits) == key) return (int32_t)(s1 & ((1u << kSymBits) - 1));
+  return kRankInf;
+}
+
+// Rank of the pair (l, r), or kRankInf: both choices loaded at once.
 __device__ __forceinline__ int32_t rank_of(const uint64_t *__restrict__ tab, int bits, uint32_t l,
                                            uint32_t r) {
   const uint64_t key = pair_key(l, r);
-  const uint64_t mask = (1ull << bits) - 1;
-  uint64_t h = pair_hash(key, bits);
-  for (;;) {
-    const uint64_t s = tab[h];
-    if ((s >> kSymBits) == key) return (int32_t)(s & ((1u << kSymBits) - 1));
-    if (s == kEmptySlot) return kRankInf;
-    h = (h + 1) & mask;
-  }
+  return rank_in(tab[pair_slot0(key, bits)], tab[pair_slot1(key, bits)], key);
 }
 
 // ---- wave / workgroup reductions and scans --------------------------------
@@ -152,38 +152,61 @@ __device__ int64_t wave_lower_bound(const int64_t *a, int64_t n, int64_t key) {
   return m ? lo + (__ffsll((unsigned long long)m) - 1) : hi;
 }
 
-// Exclusive prefix of the per-chunk counts tot[0..n) into off, and the OR of
-// the per-chunk status bits flag[c * fstride] into *status.  One workgroup of
-// NT threads; red64 holds NT / 64 values.
+// Per-chunk totals carry the chunk's status bits above bit kCountBits.
+constexpr int kCountBits = 56;
+constexpr int kScanSeg = 16;
+constexpr int64_t kCountMask = (1ll << kCountBits) - 1;
+
+// Exclusive prefix of the per-chunk counts tot[0..n) (low kCountBits bits)
+// into off, and the OR of their status bits into *status.  One workgroup of
+// NT threads; thread t owns kScanSeg consecutive chunks of each tile, read
+// and written with 16-byte accesses: tot and off are 256-byte aligned and
+// hold n rounded up to kScanSeg entries (the extra ones are ignored).
+// red64 holds NT / 64 values.
 template <int NT>
 __device__ void chunk_offsets(const int64_t *__restrict__ tot, int64_t *__restrict__ off,
-                              const int32_t *__restrict__ flag, int fstride, int64_t n,
-                              int32_t *status, int64_t *red64) {
-  constexpr int PER = 8;
+                              int64_t n, int32_t *status, int64_t *red64) {
+  constexpr int64_t TILE = (int64_t)NT * kScanSeg;
+  typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
   int64_t carry = 0;
-  int32_t bits = 0;
-  for (int64_t t0 = 0; t0 < n; t0 += (int64_t)NT * PER) {
-    const int64_t b0 = t0 + (int64_t)threadIdx.x * PER;
-    int64_t v[PER], sum = 0;
+  int64_t bits = 0;
+  for (int64_t t0 = 0; t0 < n; t0 += TILE) {
+    const int64_t b0 = t0 + (int64_t)threadIdx.x * kScanSeg;
+    i64x2 v[kScanSeg / 2];
+    int64_t sum = 0;
+    if (b0 < n) {
+      const i64x2 *p = reinterpret_cast<const i64x2 *>(tot + b0);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool in = b0 + j < n;
-      v[j] = in ? tot[b0 + j] : 0;
-      if (in) bits |= flag[(b0 + j) * fstride];
-      sum += v[j];
+      for (int j = 0; j < kScanSeg / 2; ++j) v[j] = p[j];
+#pragma unroll
+      for (int j = 0; j < kScanSeg / 2; ++j) {
+        if (b0 + 2 * j >= n) v[j].x = 0;
+        if (b0 + 2 * j + 1 >= n) v[j].y = 0;
+        bits |= v[j].x | v[j].y;
+        v[j].x &= kCountMask;
+        v[j].y &= kCountMask;
+        sum += v[j].x + v[j].y;
+      }
     }
     int64_t total;
     int64_t run = carry + block_excl_sum<int64_t, NT>(sum, red64, &total);
+    if (b0 < n) {
+      i64x2 *q = reinterpret_cast<i64x2 *>(off + b0);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (b0 + j < n) off[b0 + j] = run;
-      run += v[j];
+      for (int j = 0; j < kScanSeg / 2; ++j) {
+        i64x2 x;
+        x.x = run;
+        x.y = run + v[j].x;
+        run = x.y + v[j].y;
+        q[j] = x;
+      }
     }
     carry += total;
   }
-  for (int d = 32; d >= 1; d >>= 1) bits |= __shfl_xor(bits, d, 64);
+  int32_t b32 = (int32_t)(bits >> kCountBits);
+  for (int d = 32; d >= 1; d >>= 1) b32 |= __shfl_xor(b32, d, 64);
   int32_t *red = reinterpret_cast<int32_t *>(red64);
-  if (lane_id() == 0) red[wave_id()] = bits;
+  if (lane_id() == 0) red[wave_id()] = b32;
   __syncthreads();
   if (threadIdx.x == 0) {
     int32_t all = 0;

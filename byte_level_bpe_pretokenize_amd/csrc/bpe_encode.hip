@@ -43,14 +43,28 @@ constexpr int DB_OFF = 32;                  // document-start bit of position p 
 constexpr int DB_WORDS = (WIN + DB_OFF) / 32 + 2;
 constexpr int kMaxLong = kChunk / (kLaneMax + 1) + 4;  // longer pre-tokens per chunk, + the last
 
-// merge-loop list entry: start (13 bits) | length (13 bits) << 13 | kind << 26
-enum : uint32_t { kShort = 0, kLong = 1, kOver = 2 };
-__device__ __forceinline__ uint32_t miss_entry(int st, int len, uint32_t kind) {
-  return (uint32_t)st | ((uint32_t)len << 13) | (kind << 26);
+// Merge-loop list entry: start (13 bits) | length (13 bits) << 13 | overhang
+// << 26.  An overhang entry is a chunk's last pre-token that runs past the
+// window; its length is found by the merge kernel.
+__device__ __forceinline__ uint32_t miss_entry(int st, int len, bool over) {
+  return (uint32_t)st | ((uint32_t)len << 13) | ((uint32_t)over << 26);
 }
 __device__ __forceinline__ int me_start(uint32_t e) { return (int)(e & 0x1FFFu); }
 __device__ __forceinline__ int me_len(uint32_t e) { return (int)((e >> 13) & 0x1FFFu); }
-__device__ __forceinline__ uint32_t me_kind(uint32_t e) { return e >> 26; }
+__device__ __forceinline__ bool me_over(uint32_t e) { return (e >> 26) & 1u; }
+
+// Length buckets of the merge-loop list: a chunk's list holds bucket 0
+// entries first, then 1, 2, 3, each in text order.  Buckets 0-2 are merged
+// one pre-token per lane (registers for 0-1, LDS arrays for 2); bucket 3 by a
+// whole wave.
+constexpr int kBuckets = 4;
+__device__ __forceinline__ int bucket_of(int len, bool over) {
+  return over ? 3 : (len <= 8 ? 0 : (len <= 16 ? 1 : (len <= kLaneMax ? 2 : 3)));
+}
+// Four 16-bit bucket counts packed in one int64, for one workgroup scan.
+__device__ __forceinline__ int bfield(int64_t packed, int b) {
+  return (int)((packed >> (16 * b)) & 0xFFFF);
+}
 
 // Scratch for the workgroup reductions and the workgroup merge.
 template <int NT>
@@ -62,26 +76,13 @@ struct Red {
 
 // ---- merge loops ----------------------------------------------------------
 
-// Rank of (l, r) continuing the linear probe after slot h (rare path).
-__device__ __noinline__ int32_t rank_probe_from(const uint64_t *__restrict__ tab, int bits,
-                                                uint64_t key, uint64_t h) {
-  const uint64_t mask = (1ull << bits) - 1;
-  for (;;) {
-    h = (h + 1) & mask;
-    const uint64_t s = tab[h];
-    if ((s >> kSymBits) == key) return (int32_t)(s & ((1u << kSymBits) - 1));
-    if (s == kEmptySlot) return kRankInf;
-  }
-}
-
-
 // Merge one pre-token of len <= W bytes in registers and write its symbols
 // to out; returns their count.  Each round takes the lowest rank r among the
 // adjacent pairs and rewrites left to right: a pair of rank r merges into
 // symbol 256 + r unless its left symbol was just consumed.  Positions never
 // move: a consumed position is marked dead and each pair joins a live
-// position to the next live one, so all indexing is static.  The rank probes
-// of a round are issued together, eight positions at a time.
+// position to the next live one, so all indexing is static.  The rank
+// probes of a round are issued together, 8 positions at a time.
 template <int W>
 __device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const uint64_t *tab,
                          const int bits, const int32_t *__restrict__ pair_rank) {
@@ -93,7 +94,6 @@ __device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const ui
 #pragma unroll
   for (int i = 0; i < W; ++i)
     rk[i] = (i + 1 < len) ? pair_rank[(sym[i] << 8) | sym[i + 1]] : kRankInf;
-  const uint64_t mask = (1ull << bits) - 1;
   for (;;) {
     int32_t r = kRankInf;
 #pragma unroll
@@ -113,15 +113,17 @@ __device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const ui
       if (merge) sym[i] = z;
       carry = live ? merge : carry;
     }
-    // new ranks for the pairs that touch z, groups of 8 from the top
+    // the pairs that touch z get new ranks: the next live symbol of each
+    // position, from the top, in probe groups of PG positions
+    constexpr int PG = W < 8 ? W : 8;
     int32_t ns = -1;  // next live symbol above the current group
 #pragma unroll
-    for (int g = W / 8 - 1; g >= 0; --g) {
-      int32_t nx[8];
+    for (int g = W / PG - 1; g >= 0; --g) {
+      int32_t nx[PG];
       uint32_t need = 0;
 #pragma unroll
-      for (int j = 7; j >= 0; --j) {
-        const int i = 8 * g + j;
+      for (int j = PG - 1; j >= 0; --j) {
+        const int i = PG * g + j;
         nx[j] = ns;
         const bool live = (alive >> i) & 1u;
         if (live && ns >= 0 && (sym[i] == z || ns == z)) need |= 1u << j;
@@ -129,22 +131,19 @@ __device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const ui
         if (live) ns = sym[i];
       }
       if (need) {
-        uint64_t slot[8];
+        uint64_t s0[PG], s1[PG];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          slot[j] = kEmptySlot;
-          if ((need >> j) & 1u) slot[j] = tab[pair_hash(pair_key(sym[8 * g + j], nx[j]), bits)];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < PG; ++j) {
+          s0[j] = s1[j] = kEmptySlot;
           if ((need >> j) & 1u) {
-            const int i = 8 * g + j;
-            const uint64_t key = pair_key(sym[i], nx[j]);
-            if ((slot[j] >> kSymBits) == key) rk[i] = (int32_t)(slot[j] & ((1u << kSymBits) - 1));
-            else if (slot[j] == kEmptySlot) rk[i] = kRankInf;
-            else rk[i] = rank_probe_from(tab, bits, key, pair_hash(key, bits) & mask);
+            const uint64_t key = pair_key(sym[PG * g + j], nx[j]);
+            s0[j] = tab[pair_slot0(key, bits)];
+            s1[j] = tab[pair_slot1(key, bits)];
           }
         }
+#pragma unroll
+        for (int j = 0; j < PG; ++j)
+          if ((need >> j) & 1u) rk[PG * g + j] = rank_in(s0[j], s1[j], pair_key(sym[PG * g + j], nx[j]));
       }
     }
   }
@@ -152,37 +151,6 @@ __device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const ui
 #pragma unroll
   for (int i = 0; i < W; ++i)
     if ((alive >> i) & 1u) out[n++] = sym[i];
-  return n;
-}
-
-// The same rounds on arrays (one lane): Y[0..len) symbols, RK scratch;
-// survivors are compacted in place.  Returns the final symbol count.
-__device__ int lane_merge(int32_t *Y, int32_t *RK, const int len, const uint64_t *tab,
-                          const int bits, const int32_t *__restrict__ pair_rank) {
-  for (int i = 0; i + 1 < len; ++i) RK[i] = pair_rank[(Y[i] << 8) | Y[i + 1]];
-  RK[len - 1] = kRankInf;
-  int n = len;
-  for (;;) {
-    int32_t r = kRankInf;
-    for (int i = 0; i + 1 < n; ++i) r = min(r, RK[i]);
-    if (r == kRankInf) break;
-    const int32_t z = 256 + r;
-    int o = 0;
-    for (int i = 0; i < n; ++o) {
-      if (RK[i] == r) {
-        Y[o] = z;
-        i += 2;
-      } else {
-        Y[o] = Y[i];
-        RK[o] = RK[i];
-        i += 1;
-      }
-    }
-    n = o;
-    for (int j = 0; j + 1 < n; ++j)
-      if (Y[j] == z || Y[j + 1] == z) RK[j] = rank_of(tab, bits, Y[j], Y[j + 1]);
-    RK[n - 1] = kRankInf;
-  }
   return n;
 }
 
@@ -330,20 +298,20 @@ __device__ __forceinline__ void pretoken_words(const FindShared &s, int st, int 
   }
 }
 
-// Symbol stored for these bytes in the word table, or -1.
-__device__ __forceinline__ int32_t word_lookup(const uint4 *__restrict__ tab, int bits,
+// Symbol stored for these bytes in the word table, or -1.  Both halves of
+// a slot are loaded together.
+__device__ __forceinline__ int32_t word_lookup(const uint4 *__restrict__ tab, uint32_t mask,
                                                const uint32_t w[kWordWords], int len) {
   const uint32_t h = word_hash(w, len);
   const uint32_t tag = word_tag(h, len);
-  const uint32_t mask = (1u << bits) - 1u;
   uint32_t i = h & mask;
   for (;;) {
     const uint4 x = tab[2 * i];
+    const uint4 y = tab[2 * i + 1];
     if (x.x == 0) return -1;
-    if (x.x == tag && x.z == w[0] && x.w == w[1]) {
-      const uint4 y = tab[2 * i + 1];
-      if (y.x == w[2] && y.y == w[3] && y.z == w[4] && y.w == w[5]) return (int32_t)x.y;
-    }
+    if (x.x == tag && x.z == w[0] && x.w == w[1] && y.x == w[2] && y.y == w[3] && y.z == w[4] &&
+        y.w == w[5])
+      return (int32_t)x.y;
     i = (i + 1) & mask;
   }
 }
@@ -372,11 +340,27 @@ __global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
   const int nown = (int)min<int64_t>(kChunk, n - c0);
   const bool win_reaches_end = (c0 + nwin == n);
   for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
+
+  // 1. the window's bytes, 16 per load (group g covers positions 16g ..
+  //    16g + 15; group -1 is the two bytes before the chunk), issued first so
+  //    that their latency overlaps the document search
+  const bool aligned = (((uintptr_t)a.bytes) & 15u) == 0;
+  constexpr int NG = WIN / 16 + 1;  // groups -1 .. WIN / 16 - 1
+  u32x4 reg[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int g = tid - 1 + r * WG;
+    reg[r] = u32x4{0, 0, 0, 0};
+    const int64_t gp = c0 + 16 * (int64_t)g;
+    if (g + 1 < NG && aligned && gp >= 0 && gp + 16 <= n)
+      // streamed once: keep it out of the way of the tables in L2
+      reg[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.bytes + gp));
+  }
   __syncthreads();
 
-  // 1. document starts in the window (wave 0: a 64-way search for the first
+  //    document starts in the window (wave 0: a 64-way search for the first
   //    document at or after the byte before the chunk, then 64 offsets per
-  //    load); bytes into LDS (all waves)
+  //    load)
   if (wave == 0) {
     int64_t d0 = wave_lower_bound(a.doc_off, a.n_docs + 1, c0 - 1);
     d0 = min(d0, a.n_docs);
@@ -396,20 +380,18 @@ __global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
       s.o_hi = ohi;
     }
   }
-  {
-    const bool aligned = (((uintptr_t)a.bytes) & 15u) == 0;
-    for (int g = tid - 1; g < WIN / 16; g += WG) {
-      const int64_t gp = c0 + 16 * (int64_t)g;
-      uint8_t *dst = &s.B[16 + 16 * g];
-      if (aligned && gp >= 0 && gp + 16 <= n) {
-        // streamed once: keep it out of the way of the tables in L2
-        *reinterpret_cast<u32x4 *>(dst) =
-            __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.bytes + gp));
-      } else {
-        for (int k = 0; k < 16; ++k) {
-          const int64_t q = gp + k;
-          dst[k] = (q >= 0 && q < n) ? a.bytes[q] : 0;
-        }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int g = tid - 1 + r * WG;
+    if (g + 1 >= NG) continue;
+    const int64_t gp = c0 + 16 * (int64_t)g;
+    uint8_t *dst = &s.B[16 + 16 * g];
+    if (aligned && gp >= 0 && gp + 16 <= n) {
+      *reinterpret_cast<u32x4 *>(dst) = reg[r];
+    } else {
+      for (int k = 0; k < 16; ++k) {
+        const int64_t q = gp + k;
+        dst[k] = (q >= 0 && q < n) ? a.bytes[q] : 0;
       }
     }
   }
@@ -463,48 +445,66 @@ __global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
 
   // 4. each thread resolves a contiguous block of the list: a single byte is
   //    its own token; a pre-token that is a whole word-table entry takes its
-  //    symbol; the others (-1) go to the merge-loop list, in order
+  //    symbol; the others go to the merge-loop list (pv = -1 - bucket)
   const int per = (n_pt + WG - 1) / WG;  // <= 16
   const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
   int32_t *pv = a.pv + c * kChunk;
-  uint32_t mbits = 0;
+  int64_t bcnt = 0;    // this thread's misses per bucket, packed
+  uint64_t codes = 0;  // 3 bits per pre-token k0 + j: 0 resolved, 1 + bucket otherwise
+  const uint32_t wmask = (1u << a.word_bits) - 1u;
   for (int k = k0; k < k1; ++k) {
+    int32_t v = -1;
+    const bool over = overhang && k == n_pt - 1;
     const int st = s.PS[k];
-    int32_t res = -1;
-    if (!(overhang && k == n_pt - 1)) {
-      const int len = (int)s.PS[k + 1] - st;
-      if (len == 1) {
-        res = s.B[16 + st];
-      } else if (a.words && len <= kWordMax) {
-        uint32_t w[kWordWords];
-        pretoken_words(s, st, len, w);
-        res = word_lookup(a.words, a.word_bits, w, len);
-      }
+    const int len = over ? 0 : (int)s.PS[k + 1] - st;
+    if (len == 1) {
+      v = s.B[16 + st];
+    } else if (!over && a.words && len <= kWordMax) {
+      uint32_t w[kWordWords];
+      pretoken_words(s, st, len, w);
+      v = word_lookup(a.words, wmask, w, len);
     }
-    pv[k] = res;
-    if (res < 0) mbits |= 1u << (k - k0);
+    if (v < 0) {
+      const int b = bucket_of(len, over);
+      v = -1 - b;
+      bcnt += (int64_t)1 << (16 * b);
+      codes |= (uint64_t)(1 + b) << (3 * (k - k0));
+    }
+    pv[k] = v;
   }
-  int n_miss;
-  const int mex = block_excl_sum<int, WG>(__popc(mbits), s.r.red, &n_miss);
+  int64_t btot;
+  const int64_t bex = block_excl_sum<int64_t, WG>(bcnt, s.r.red64, &btot);
   {
     uint32_t *ml = a.miss + c * kMissMax;
-    int q = mex;
-    for (uint32_t m = mbits; m; m &= m - 1) {
-      const int k = k0 + __ffs(m) - 1;
-      const int st = s.PS[k];
-      if (overhang && k == n_pt - 1) {
-        ml[q++] = miss_entry(st, 0, kOver);
-      } else {
-        const int len = (int)s.PS[k + 1] - st;
-        ml[q++] = miss_entry(st, len, len > kLaneMax ? kLong : kShort);
+    int64_t at = 0;  // next list index per bucket, packed
+    int base = 0;
+#pragma unroll
+    for (int b = 0; b < kBuckets; ++b) {
+      at += (int64_t)(base + bfield(bex, b)) << (16 * b);
+      base += bfield(btot, b);
+    }
+    for (int k = k0; codes; ++k, codes >>= 3) {
+      if (codes & 7u) {
+        const int b = (int)(codes & 7u) - 1;
+        const int st = s.PS[k];
+        const bool over = overhang && k == n_pt - 1;
+        ml[bfield(at, b)] = miss_entry(st, over ? 0 : (int)s.PS[k + 1] - st, over);
+        at += (int64_t)1 << (16 * b);
       }
     }
   }
   const bool any_bad = __syncthreads_or(bad);
   if (tid == 0) {
-    a.meta[4 * c] = n_pt;
-    a.meta[4 * c + 1] = n_miss;
-    a.meta[4 * c + 2] = any_bad ? (int32_t)BPE_STATUS_BAD_DOC_OFFSETS : 0;
+    int32_t *m = a.meta + kMetaInts * c;
+    int n_miss = 0;
+#pragma unroll
+    for (int b = 0; b < kBuckets; ++b) {
+      m[kMetaBucket + b] = bfield(btot, b);
+      n_miss += bfield(btot, b);
+    }
+    m[kMetaPretokens] = n_pt;
+    m[kMetaMisses] = n_miss;
+    m[kMetaStatus] = any_bad ? (int32_t)BPE_STATUS_BAD_DOC_OFFSETS : 0;
     a.doc_rng[2 * c] = s.o_lo;
     a.doc_rng[2 * c + 1] = s.o_hi;
   }
@@ -521,17 +521,55 @@ __global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
   }
 }
 
-// ---- k_merge ------------------------------------------------------------------
+// ---- k_merge, k_merge_wide ---------------------------------------------------
 
-constexpr int kMidSlots = 16;  // lanes that merge a 17..kLaneMax-byte pre-token in LDS at once
+constexpr int kGroup = 4;  // chunks per merge wave: batches of one bucket span them
 
 struct MergeShared {
-  int32_t y[kMidSlots][kLaneMax + 1];  // symbols and ranks of the array merge
-  int32_t rk[kMidSlots][kLaneMax + 1];
-  int32_t longs[kMaxLong];
-  int32_t n_long;
+  int32_t meta[kGroup][kMetaInts];
+  int32_t tok[kGroup];
   Red<MWG> r;
 };
+
+// Entry g (0-based) of bucket b across the group's chunks: chunk index f and
+// list index; meta counts are in LDS.
+__device__ __forceinline__ void group_entry(const MergeShared &s, int b, int g, int &f, int &idx) {
+  int pre = 0;
+  f = 0;
+  while (g >= pre + s.meta[f][kMetaBucket + b]) pre += s.meta[f++][kMetaBucket + b];
+  idx = g - pre;
+  for (int bb = 0; bb < b; ++bb) idx += s.meta[f][kMetaBucket + bb];
+}
+
+// Bucket b (one pre-token per lane, W-wide registers) of the group's lists,
+// 64 entries per batch; adds the token counts into s.tok.
+template <int W>
+__device__ void merge_bucket(const EncodeArgs &a, MergeShared &s, int64_t cg, int nf, int b) {
+  const int lane = lane_id();
+  int total = 0;
+  for (int f = 0; f < nf; ++f) total += s.meta[f][kMetaBucket + b];
+  for (int s0 = 0; s0 < total; s0 += MWG) {
+    const int g = s0 + lane;
+    if (g < total) {
+      int f, idx;
+      group_entry(s, b, g, f, idx);
+      const int64_t c0 = (cg + f) * kChunk;
+      const uint32_t e = a.miss[(cg + f) * kMissMax + idx];
+      const int st = me_start(e);
+      const int nt = reg_merge<W>(a.bytes + c0 + st, me_len(e), a.gsym + c0 + st, a.table,
+                                  a.table_bits, a.pair_rank);
+      a.mt[(cg + f) * kMissMax + idx] = nt;
+      atomicAdd(&s.tok[f], nt);
+    }
+  }
+}
+
+__device__ void load_group(const EncodeArgs &a, MergeShared &s, int64_t cg, int nf) {
+  const int lane = lane_id();
+  if (lane < kMetaInts * nf) (&s.meta[0][0])[lane] = a.meta[kMetaInts * cg + lane];
+  if (lane < kGroup) s.tok[lane] = 0;
+  __syncthreads();
+}
 
 // End (exclusive, global) of the pre-token that starts at gs and has no start
 // in the window, scanning bytes from `from` on (one wave).
@@ -561,80 +599,63 @@ __device__ int64_t wave_global_end(const EncodeArgs &a, int64_t gs, int64_t from
   return limit;
 }
 
-// Merge-loop list of one chunk (one wave).  The tokens of the pre-token at
-// global position g go to gsym[g ..]: never more tokens than bytes, so the
-// pre-tokens' regions do not overlap.  mt[i] gets each entry's token count,
-// tot[c] the chunk's.
+// Merge-loop lists of kGroup consecutive chunks, buckets 0 and 1 (one wave).
+// The entries of one bucket are taken 64 at a time across the chunks, so
+// every lane of a batch runs the same merge width.  The tokens of the
+// pre-token at global position g go to gsym[g ..]: never more tokens than
+// bytes, so the pre-tokens' regions do not overlap.  mt gets each entry's
+// token count; tot[c] the chunk's count so far (its resolved pre-tokens and
+// these buckets) with its status bits on top.
 __global__ void __launch_bounds__(MWG) k_merge(EncodeArgs a) {
   __shared__ MergeShared s;
+  const int64_t cg = (int64_t)blockIdx.x * kGroup;
+  const int nf = (int)min<int64_t>(kGroup, a.n_chunks - cg);
+  load_group(a, s, cg, nf);
+  merge_bucket<8>(a, s, cg, nf, 0);
+  merge_bucket<16>(a, s, cg, nf, 1);
+  __syncthreads();
   const int lane = threadIdx.x;
-  const int64_t c = blockIdx.x;
-  const int64_t c0 = c * kChunk;
-  const int n_pt = a.meta[4 * c], n_miss = a.meta[4 * c + 1];
-  const uint32_t *ml = a.miss + c * kMissMax;
-  int32_t *mt = a.mt + c * kMissMax;
-  const uint8_t *bytes = a.bytes + c0;
-  int32_t *gsym = a.gsym + c0;
-  if (lane == 0) s.n_long = 0;
-  __syncthreads();
+  if (lane < nf) {
+    const int32_t *m = s.meta[lane];
+    const int64_t tot = (int64_t)(m[kMetaPretokens] - m[kMetaMisses]) + s.tok[lane];
+    a.tot[cg + lane] = tot | ((int64_t)m[kMetaStatus] << kCountBits);
+  }
+}
 
-  // entries of <= kLaneMax bytes: one per lane, in registers up to 16 bytes
-  int tok = 0;
-  for (int i0 = 0; i0 < n_miss; i0 += MWG) {
-    const int i = i0 + lane;
-    uint32_t e = 0;
-    int nt = 0;
-    bool mid = false;
-    if (i < n_miss) {
-      e = ml[i];
-      const int st = me_start(e), len = me_len(e);
-      if (me_kind(e) != kShort)
-        s.longs[atomicAdd(&s.n_long, 1)] = i;
-      else if (len <= 8)
-        nt = reg_merge<8>(bytes + st, len, gsym + st, a.table, a.table_bits, a.pair_rank);
-      else if (len <= 16)
-        nt = reg_merge<16>(bytes + st, len, gsym + st, a.table, a.table_bits, a.pair_rank);
-      else
-        mid = true;
-    }
-    // 17..kLaneMax bytes: arrays in LDS, kMidSlots lanes at a time
-    const uint64_t mm = __ballot(mid);
-    if (mm) {
-      const int rank = __popcll(mm & ((1ull << lane) - 1));
-      for (int p0 = 0; p0 < __popcll(mm); p0 += kMidSlots) {
-        if (mid && rank >= p0 && rank < p0 + kMidSlots) {
-          const int slot = rank - p0;
-          const int st = me_start(e), len = me_len(e);
-          int32_t *y = s.y[slot];
-          for (int j = 0; j < len; ++j) y[j] = bytes[st + j];
-          nt = lane_merge(y, s.rk[slot], len, a.table, a.table_bits, a.pair_rank);
-          for (int j = 0; j < nt; ++j) gsym[st + j] = y[j];
-        }
+// Buckets 2 (one pre-token per lane, 32-wide registers) and 3 (the whole
+// wave per entry, in place in the position-indexed scratch) of the same
+// groups; adds their token counts to tot.
+__global__ void __launch_bounds__(MWG) k_merge_wide(EncodeArgs a) {
+  __shared__ MergeShared s;
+  const int64_t cg = (int64_t)blockIdx.x * kGroup;
+  const int nf = (int)min<int64_t>(kGroup, a.n_chunks - cg);
+  load_group(a, s, cg, nf);
+  int any = 0;
+  for (int f = 0; f < nf; ++f) any += s.meta[f][kMetaBucket + 2] + s.meta[f][kMetaBucket + 3];
+  if (any == 0) return;
+  const int lane = threadIdx.x;
+  merge_bucket<32>(a, s, cg, nf, 2);
+  __syncthreads();
+  for (int f = 0; f < nf; ++f) {
+    const int n3 = s.meta[f][kMetaBucket + 3];
+    const int base = s.meta[f][kMetaMisses] - n3;
+    const int64_t c = cg + f, c0 = c * kChunk;
+    for (int q = 0; q < n3; ++q) {
+      const uint32_t e = a.miss[c * kMissMax + base + q];
+      const int64_t gs = c0 + me_start(e);
+      const int64_t ge = me_over(e) ? wave_global_end(a, gs, c0 + WIN) : gs + me_len(e);
+      for (int64_t p = gs + lane; p < ge; p += MWG) a.gsym[p] = a.bytes[p];
+      __syncthreads();
+      const int64_t nt = wg_merge<MWG>(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits,
+                                       a.pair_rank, s.r);
+      if (lane == 0) {
+        a.mt[c * kMissMax + base + q] = (int32_t)nt;
+        s.tok[f] += (int32_t)nt;
       }
+      __syncthreads();
     }
-    if (i < n_miss && me_kind(e) == kShort) mt[i] = nt;
-    tok += nt;
   }
-  tok = wave_sum(tok);
-  int64_t tot = (int64_t)(n_pt - n_miss) + tok;  // every other pre-token is one token
-  __syncthreads();
-
-  // longer entries: the whole wave, in place in the position-indexed scratch
-  const int n_long = s.n_long;
-  for (int q = 0; q < n_long; ++q) {
-    const int i = s.longs[q];
-    const uint32_t e = ml[i];
-    const int64_t gs = c0 + me_start(e);
-    const int64_t ge = me_kind(e) == kLong ? gs + me_len(e) : wave_global_end(a, gs, c0 + WIN);
-    for (int64_t p = gs + lane; p < ge; p += MWG) a.gsym[p] = a.bytes[p];
-    __syncthreads();
-    const int64_t nt =
-        wg_merge<MWG>(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits, a.pair_rank, s.r);
-    if (lane == 0) mt[i] = (int32_t)nt;
-    tot += nt;
-    __syncthreads();
-  }
-  if (lane == 0) a.tot[c] = tot;
+  if (lane < nf && s.tok[lane] != 0) a.tot[cg + lane] += s.tok[lane];
 }
 
 // ---- k_offsets ---------------------------------------------------------------
@@ -643,7 +664,7 @@ __global__ void __launch_bounds__(MWG) k_merge(EncodeArgs a) {
 // the chunks' status bits (one workgroup).
 __global__ void __launch_bounds__(OWG) k_offsets(EncodeArgs a) {
   __shared__ int64_t red64[OWG / 64];
-  chunk_offsets<OWG>(a.tot, a.off, a.meta + 2, 4, a.n_chunks, a.status, red64);
+  chunk_offsets<OWG>(a.tot, a.off, a.n_chunks, a.status, red64);
 }
 
 // ---- k_emit -------------------------------------------------------------------
@@ -662,7 +683,17 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
   const int tid = threadIdx.x;
   const int64_t c = blockIdx.x;
   const int64_t c0 = c * kChunk;
-  const int n_pt = a.meta[4 * c];
+  const int32_t *meta = a.meta + kMetaInts * c;
+  const int n_pt = meta[kMetaPretokens];
+  int64_t at = 0;  // first list index of each bucket, packed
+  {
+    int base = 0;
+#pragma unroll
+    for (int b = 0; b < kBuckets; ++b) {
+      at += (int64_t)base << (16 * b);
+      base += meta[kMetaBucket + b];
+    }
+  }
   const int64_t base = a.off[c];
   const int32_t *pv = a.pv + c * kChunk;
   const uint32_t *ml = a.miss + c * kMissMax;
@@ -670,22 +701,36 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
   const int32_t *gsym = a.gsym + c0;
   if (tid == 0) s.n_long = 0;
 
+  // this thread's pre-tokens: results, and the list index of each miss
   const int per = (n_pt + WG - 1) / WG;
   const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
-  uint32_t mbits = 0;
-  for (int k = k0; k < k1; ++k)
-    if (pv[k] < 0) mbits |= 1u << (k - k0);
-  int n_miss;
-  const int mex = block_excl_sum<int, WG>(__popc(mbits), s.r.red, &n_miss);
-  int64_t cnt = k1 - k0 - __popc(mbits);
-  for (int q = mex; q < mex + __popc(mbits); ++q) cnt += mt[q];
+  int64_t bcnt = 0;
+  for (int k = k0; k < k1; ++k) {
+    const int32_t v = pv[k];
+    if (v < 0) bcnt += (int64_t)1 << (16 * (-1 - v));
+  }
+  int64_t btot;
+  at += block_excl_sum<int64_t, WG>(bcnt, s.r.red64, &btot);
+  int64_t cnt = 0;
+  {
+    int64_t q = at;
+    for (int k = k0; k < k1; ++k) {
+      const int32_t v = pv[k];
+      if (v >= 0) {
+        ++cnt;
+      } else {
+        const int b = -1 - v;
+        cnt += mt[bfield(q, b)];
+        q += (int64_t)1 << (16 * b);
+      }
+    }
+  }
   int64_t total;
   const int64_t ex = block_excl_sum<int64_t, WG>(cnt, s.r.red64, &total);
   if (tid == 0) s.tokoff[n_pt] = (int32_t)total;
   bool overflow = false;
   {
     int64_t w = base + ex;
-    int q = mex;
     for (int k = k0; k < k1; ++k) {
       s.tokoff[k] = (int32_t)(w - base);
       const int32_t x = pv[k];
@@ -695,9 +740,12 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
         ++w;
         continue;
       }
-      const uint32_t e = ml[q];
-      const int64_t nt = mt[q];
-      if (me_kind(e) == kShort) {
+      const int b = -1 - x;
+      const int i = bfield(at, b);
+      at += (int64_t)1 << (16 * b);
+      const uint32_t e = ml[i];
+      const int64_t nt = mt[i];
+      if (b < 3) {
         const int32_t *src = gsym + me_start(e);
         for (int j = 0; j < nt; ++j, ++w) {
           if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, src[j]);
@@ -710,7 +758,6 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
         s.lnt[slot] = nt;
         w += nt;
       }
-      ++q;
     }
   }
   __syncthreads();
@@ -732,7 +779,7 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
     a.id_off[d] = base + s.tokoff[k];
   }
   if (c == a.n_chunks - 1) {
-    const int64_t end = base + a.tot[c];
+    const int64_t end = base + (a.tot[c] & kCountMask);
     for (int64_t d = dhi + tid; d <= a.n_docs; d += WG) a.id_off[d] = end;
   }
 }
@@ -760,12 +807,22 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
   return hipGetLastError();
 }
 
-hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream) {
+const char *const kEncStageNames[kEncStages] = {"k_find", "k_merge", "k_merge_wide", "k_offsets",
+                                                "k_emit"};
+
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev) {
   const unsigned G = (unsigned)a.n_chunks;
+  if (ev) (void)hipEventRecord(ev[0], stream);
   hipLaunchKernelGGL(k_find, dim3(G), dim3(WG), 0, stream, a);
-  hipLaunchKernelGGL(k_merge, dim3(G), dim3(MWG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[1], stream);
+  hipLaunchKernelGGL(k_merge, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[2], stream);
+  hipLaunchKernelGGL(k_merge_wide, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[3], stream);
   hipLaunchKernelGGL(k_offsets, dim3(1), dim3(OWG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[4], stream);
   hipLaunchKernelGGL(k_emit, dim3(G), dim3(WG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[5], stream);
   return hipGetLastError();
 }
 

@@ -7,13 +7,14 @@
 namespace bpe {
 
 // ---- rank table --------------------------------------------------------
-// Open-addressing hash table in device memory, one 64-bit slot per entry:
+// Two-choice cuckoo hash table in device memory, one 64-bit slot per entry:
 //   bits 42..62  left symbol, bits 21..41 right symbol, bits 0..20 rank.
 // A key is (left << 21) | right, so (slot >> 21) is the key; the empty slot
-// is all ones, whose upper bits can equal no key.  Capacity is a power of
-// two >= 2 * merges (load <= 1/2), probed linearly from a multiplicative hash
-// of the key.  ("Tokenization LLM: ... C++", section "Vocabulary lookup":
-// a pair-keyed map from the pair of units to its rank.)
+// is all ones, whose upper bits can equal no key.  Every key sits in one of
+// its two slots pair_slot(key, 0 or 1), so a lookup is two independent loads
+// and never a chain.  Capacity is a power of two >= 2.5 * merges (load
+// <= 0.4).  ("Tokenization LLM: ... C++", section "Vocabulary lookup": a
+// pair-keyed map from the pair of units to its rank.)
 constexpr int kSymBits = 21;
 constexpr uint64_t kEmptySlot = ~0ull;
 constexpr int32_t kRankInf = 0x7fffffff;  // "no merge here" compares largest
@@ -22,8 +23,15 @@ __host__ __device__ inline uint64_t pair_key(uint32_t l, uint32_t r) {
   return ((uint64_t)l << kSymBits) | (uint64_t)r;
 }
 
-__host__ __device__ inline uint64_t pair_hash(uint64_t key, int bits) {
+// Slot of choice 0 or 1 for a key (two multiplicative hashes; the second is
+// moved off the first when they coincide).
+__host__ __device__ inline uint64_t pair_slot0(uint64_t key, int bits) {
   return (key * 0x9E3779B97F4A7C15ull) >> (64 - bits);
+}
+__host__ __device__ inline uint64_t pair_slot1(uint64_t key, int bits) {
+  const uint64_t h0 = pair_slot0(key, bits);
+  const uint64_t h1 = (key * 0xC2B2AE3D27D4EB4Full) >> (64 - bits);
+  return h1 == h0 ? h0 ^ 1u : h1;
 }
 
 // ---- word table -----------------------------------------------------------
@@ -64,16 +72,25 @@ inline int64_t dec_chunks(int64_t n_ids) { return (n_ids + kDecChunk - 1) / kDec
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Per-chunk record size of the encode pipeline.
+// Per-chunk records of the encode pipeline.
 constexpr int kMissMax = kChunk / 2 + 16;  // merge-loop pre-tokens per chunk (each >= 2 bytes)
+// meta: 8 int32 per chunk
+constexpr int kMetaInts = 8;
+constexpr int kMetaPretokens = 0;  // pre-tokens that start in the chunk
+constexpr int kMetaMisses = 1;     // of which on the merge-loop list
+constexpr int kMetaStatus = 2;     // status bits found by the chunk
+constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
 
 // Encode workspace, all regions 256-byte aligned:
-//   meta      [G][4] i32  pre-tokens, merge-loop pre-tokens, status bits, 0
-//   tot, off  [G] i64   token count per chunk, then its exclusive prefix
+//   meta      [G][8] i32  pre-tokens, merge-loop pre-tokens, status bits, -,
+//                         list entries per length bucket
+//   tot, off  [G] i64   token count per chunk with its status bits on top,
+//                       then the counts' exclusive prefix
 //   doc_rng   [G][2] i64  documents that start in the chunk
 //   doc_pt    [D] i32   index of each document's first pre-token in its chunk
 //   pv        [G][kChunk] i32    result per pre-token (symbol, or -1: see the list)
-//   miss      [G][kMissMax] u32  merge-loop list: start | len << 13 | kind << 26
+//   miss      [G][kMissMax] u32  merge-loop list by length bucket:
+//                                start | len << 13 | overhang << 26
 //   mt        [G][kMissMax] i32  token count of each list entry
 //   gsym      [N] i32   tokens of the list entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the workgroup merge, position-indexed
@@ -89,9 +106,9 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
     o += align256(bytes);
     return at;
   };
-  L.meta = take(16 * G);
-  L.tot = take(8 * G);
-  L.off = take(8 * G);
+  L.meta = take(4 * kMetaInts * G);
+  L.tot = take(8 * (G + 16));  // the offset scan reads whole groups of 16
+  L.off = take(8 * (G + 16));
   L.doc_rng = take(16 * G);
   L.doc_pt = take(4 * (size_t)(n_docs + 1));
   L.pv = take(4 * (size_t)kChunk * G);
@@ -103,18 +120,17 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   return L;
 }
 
-// Decode workspace: tot, off [G] i64 (byte count per chunk of IDs, then its
-// exclusive prefix), flag [G] i32 (status bits found by the chunk).
+// Decode workspace: tot, off [G] i64 (byte count per chunk of IDs with the
+// chunk's status bits on top, then the counts' exclusive prefix).
 struct DecLayout {
-  size_t tot, off, flag, total;
+  size_t tot, off, total;
 };
 inline DecLayout dec_layout(int64_t n_ids) {
   DecLayout L;
   const size_t G = (size_t)dec_chunks(n_ids);
-  L.tot = 0;
-  L.off = align256(8 * G);
-  L.flag = L.off + align256(8 * G);
-  L.total = L.flag + align256(4 * G);
+  L.tot = 0;  // the offset scan reads whole groups of 16
+  L.off = align256(8 * (G + 16));
+  L.total = L.off + align256(8 * (G + 16));
   return L;
 }
 
@@ -161,7 +177,6 @@ struct DecodeArgs {
   int64_t vocab;
   int64_t *tot;
   int64_t *off;
-  int32_t *flag;
   int32_t *status;
   int64_t n_chunks;
 };
@@ -171,9 +186,14 @@ struct DecodeArgs {
 // (else sets bad_bit) and writes zeros to out_off[0..n_docs]  (bpe_encode.hip).
 hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, int64_t *out_off,
                         int32_t *status, hipStream_t stream);
-// The encode pipeline for n_bytes > 0 (bpe_encode.hip).
-hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
-// The decode pipeline for n_ids > 0 (bpe_decode.hip).
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// The encode pipeline for n_bytes > 0 (bpe_encode.hip).  ev: nullptr, or
+// kEncStages + 1 events recorded before the first kernel and after each.
+constexpr int kEncStages = 5;
+extern const char *const kEncStageNames[kEncStages];
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
+// The decode pipeline for n_ids > 0 (bpe_decode.hip), events as for encode.
+constexpr int kDecStages = 3;
+extern const char *const kDecStageNames[kDecStages];
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t *ev);
 
 }  // namespace bpe

@@ -120,7 +120,8 @@ size_t bpe_encode_workspace_bytes(const bpe_model *model, int64_t n_bytes, int64
  *  d_doc_off     int64 [n_docs + 1]: document d is d_bytes[d_doc_off[d] ..
  *                d_doc_off[d+1]); must satisfy 0 = d_doc_off[0] <= ... <=
  *                d_doc_off[n_docs] = n_bytes, else BPE_STATUS_BAD_DOC_OFFSETS
- *                and nothing is written.  Empty documents are allowed.
+ *                is set and the outputs are not valid (every write still stays
+ *                inside the caller's buffers).  Empty documents are allowed.
  *  d_ids         int32 [ids_capacity]: receives the IDs of all documents in
  *                order.  The count never exceeds n_bytes, so ids_capacity >=
  *                n_bytes always suffices; with less, IDs at index >=
@@ -145,7 +146,8 @@ size_t bpe_decode_workspace_bytes(const bpe_model *model, int64_t n_ids, int64_t
  *  d_ids         int32 [n_ids]; an ID that is not the output ID of any symbol
  *                sets BPE_STATUS_BAD_ID (it contributes no bytes).
  *  d_id_off      int64 [n_docs + 1] with 0 = o[0] <= ... <= o[n_docs] = n_ids,
- *                else BPE_STATUS_BAD_ID_OFFSETS and nothing is written.
+ *                else BPE_STATUS_BAD_ID_OFFSETS is set and the outputs are not
+ *                valid (every write still stays inside the caller's buffers).
  *  d_bytes       uint8 [bytes_capacity]: receives the bytes of all documents;
  *                bytes past the capacity are dropped and
  *                BPE_STATUS_BYTES_CAPACITY is set.  n_ids * bpe_max_token_bytes
@@ -157,6 +159,30 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
                      const int64_t *d_id_off, int64_t n_docs, uint8_t *d_bytes,
                      int64_t bytes_capacity, int64_t *d_byte_off, void *d_workspace,
                      size_t workspace_bytes, int32_t *d_status, void *hip_stream);
+
+/*
+ * Stage timing, for benchmarks and profilers.  While it is enabled on a
+ * model, each bpe_encode_batch / bpe_decode_batch call with input records a
+ * HIP event on its stream before its first kernel and after each kernel
+ * (event records only: the call still never synchronizes).  While enabled,
+ * calls on the model must come from one host thread.
+ *  bpe_stage_timing   enable (1) or disable (0); either way, events not yet
+ *                     read are dropped.  Returns BPE_OK, BPE_EINVAL or BPE_EHIP.
+ *  bpe_stage_count    number of kernels (stages) of op, or -1.
+ *  bpe_stage_name     static name of a stage, or NULL.
+ *  bpe_stage_times    waits for the recorded events of op, writes each
+ *                     stage's total milliseconds over the calls since the
+ *                     last read to ms[0 .. bpe_stage_count(op)), and the
+ *                     number of those calls to *n_calls; then forgets them.
+ *                     max_stages is the length of ms.  Returns BPE_OK,
+ *                     BPE_EINVAL or BPE_EHIP.
+ */
+#define BPE_OP_ENCODE 0
+#define BPE_OP_DECODE 1
+int bpe_stage_timing(bpe_model *model, int enable);
+int bpe_stage_count(int op);
+const char *bpe_stage_name(int op, int stage);
+int bpe_stage_times(bpe_model *model, int op, double *ms, int max_stages, int64_t *n_calls);
 
 /* A static English description of a BPE_E* code. */
 const char *bpe_strerror(int code);

@@ -92,6 +92,21 @@ def test_workspace_sizes():
     assert L.bpe_decode_workspace_bytes(None, 5000, 3) > 0
 
 
+def test_stage_timing_queries():
+    L = _lib.load()
+    assert L.bpe_stage_count(_lib.OP_ENCODE) == 5
+    assert L.bpe_stage_count(_lib.OP_DECODE) == 3
+    assert L.bpe_stage_count(7) == -1
+    names = [L.bpe_stage_name(_lib.OP_ENCODE, k).decode() for k in range(5)]
+    assert names == ["k_find", "k_merge", "k_merge_wide", "k_offsets", "k_emit"]
+    assert L.bpe_stage_name(_lib.OP_ENCODE, 5) is None
+    assert L.bpe_stage_name(_lib.OP_DECODE, -1) is None
+    assert L.bpe_stage_timing(None, 1) == _lib.BPE_EINVAL
+    ms = (C.c_double * 5)()
+    n = C.c_int64()
+    assert L.bpe_stage_times(None, _lib.OP_ENCODE, ms, 5, C.byref(n)) == _lib.BPE_EINVAL
+
+
 def test_strerror():
     L = _lib.load()
     for code in range(-7, 1):
