@@ -162,6 +162,8 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.pv = (int32_t *)(ws + L.pv);
   a.miss = (uint32_t *)(ws + L.miss);
   a.mt = (int32_t *)(ws + L.mt);
+  a.mbytes = ws + L.mbytes;
+  a.res = (int32_t *)(ws + L.res);
   a.gsym = (int32_t *)(ws + L.gsym);
   a.grank = (int32_t *)(ws + L.grank);
   a.status = d_status;

@@ -43,9 +43,11 @@ constexpr int DB_OFF = 32;                  // document-start bit of position p 
 constexpr int DB_WORDS = (WIN + DB_OFF) / 32 + 2;
 constexpr int kMaxLong = kChunk / (kLaneMax + 1) + 4;  // longer pre-tokens per chunk, + the last
 
-// Merge-loop list entry: start (13 bits) | length (13 bits) << 13 | overhang
-// << 26.  An overhang entry is a chunk's last pre-token that runs past the
-// window; its length is found by the merge kernel.
+// Merge-loop list entry: where (13 bits) | length (13 bits) << 13 | overhang
+// << 26.  `where` is the pre-token's start in the chunk for bucket 3, and its
+// offset in the chunk's mbytes / res regions for buckets 0-2.  An overhang
+// entry is a chunk's last pre-token that runs past the window; its length is
+// found by the merge kernel.
 __device__ __forceinline__ uint32_t miss_entry(int st, int len, bool over) {
   return (uint32_t)st | ((uint32_t)len << 13) | ((uint32_t)over << 26);
 }
@@ -450,6 +452,7 @@ __global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
   const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
   int32_t *pv = a.pv + c * kChunk;
   int64_t bcnt = 0;    // this thread's misses per bucket, packed
+  int64_t blen = 0;    // and their bytes, buckets 0-2
   uint64_t codes = 0;  // 3 bits per pre-token k0 + j: 0 resolved, 1 + bucket otherwise
   const uint32_t wmask = (1u << a.word_bits) - 1u;
   for (int k = k0; k < k1; ++k) {
@@ -468,27 +471,44 @@ __global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
       const int b = bucket_of(len, over);
       v = -1 - b;
       bcnt += (int64_t)1 << (16 * b);
+      if (b < 3) blen += (int64_t)len << (16 * b);
       codes |= (uint64_t)(1 + b) << (3 * (k - k0));
     }
     pv[k] = v;
   }
-  int64_t btot;
+  int64_t btot, ltot;
   const int64_t bex = block_excl_sum<int64_t, WG>(bcnt, s.r.red64, &btot);
+  const int64_t lex = block_excl_sum<int64_t, WG>(blen, s.r.red64, &ltot);
   {
     uint32_t *ml = a.miss + c * kMissMax;
+    uint8_t *mb = a.mbytes + c * kMissBytes;
     int64_t at = 0;  // next list index per bucket, packed
-    int base = 0;
+    int64_t bo = 0;  // next byte offset per bucket (0-2), packed
+    int base = 0, lbase = 0;
 #pragma unroll
     for (int b = 0; b < kBuckets; ++b) {
       at += (int64_t)(base + bfield(bex, b)) << (16 * b);
       base += bfield(btot, b);
+      if (b < 3) {
+        bo += (int64_t)(lbase + bfield(lex, b)) << (16 * b);
+        lbase += bfield(ltot, b);
+      }
     }
     for (int k = k0; codes; ++k, codes >>= 3) {
       if (codes & 7u) {
         const int b = (int)(codes & 7u) - 1;
         const int st = s.PS[k];
         const bool over = overhang && k == n_pt - 1;
-        ml[bfield(at, b)] = miss_entry(st, over ? 0 : (int)s.PS[k + 1] - st, over);
+        const int len = over ? 0 : (int)s.PS[k + 1] - st;
+        if (b < 3) {
+          // lane-merged entries: their bytes go to the dense region
+          const int o = bfield(bo, b);
+          for (int j = 0; j < len; ++j) mb[o + j] = s.B[16 + st + j];
+          ml[bfield(at, b)] = miss_entry(o, len, false);
+          bo += (int64_t)len << (16 * b);
+        } else {
+          ml[bfield(at, b)] = miss_entry(st, len, over);
+        }
         at += (int64_t)1 << (16 * b);
       }
     }
@@ -553,11 +573,11 @@ __device__ void merge_bucket(const EncodeArgs &a, MergeShared &s, int64_t cg, in
     if (g < total) {
       int f, idx;
       group_entry(s, b, g, f, idx);
-      const int64_t c0 = (cg + f) * kChunk;
-      const uint32_t e = a.miss[(cg + f) * kMissMax + idx];
-      const int st = me_start(e);
-      const int nt = reg_merge<W>(a.bytes + c0 + st, me_len(e), a.gsym + c0 + st, a.table,
-                                  a.table_bits, a.pair_rank);
+      const int64_t c = cg + f;
+      const uint32_t e = a.miss[c * kMissMax + idx];
+      const int o = me_start(e);
+      const int nt = reg_merge<W>(a.mbytes + c * kMissBytes + o, me_len(e),
+                                  a.res + c * kMissBytes + o, a.table, a.table_bits, a.pair_rank);
       a.mt[(cg + f) * kMissMax + idx] = nt;
       atomicAdd(&s.tok[f], nt);
     }
@@ -601,11 +621,11 @@ __device__ int64_t wave_global_end(const EncodeArgs &a, int64_t gs, int64_t from
 
 // Merge-loop lists of kGroup consecutive chunks, buckets 0 and 1 (one wave).
 // The entries of one bucket are taken 64 at a time across the chunks, so
-// every lane of a batch runs the same merge width.  The tokens of the
-// pre-token at global position g go to gsym[g ..]: never more tokens than
-// bytes, so the pre-tokens' regions do not overlap.  mt gets each entry's
-// token count; tot[c] the chunk's count so far (its resolved pre-tokens and
-// these buckets) with its status bits on top.
+// every lane of a batch runs the same merge width.  An entry's bytes are read
+// from the chunk's dense mbytes region and its tokens written to res at the
+// same offset: never more tokens than bytes, so entries do not overlap.  mt
+// gets each entry's token count; tot[c] the chunk's count so far (its
+// resolved pre-tokens and these buckets) with its status bits on top.
 __global__ void __launch_bounds__(MWG) k_merge(EncodeArgs a) {
   __shared__ MergeShared s;
   const int64_t cg = (int64_t)blockIdx.x * kGroup;
@@ -622,9 +642,9 @@ __global__ void __launch_bounds__(MWG) k_merge(EncodeArgs a) {
   }
 }
 
-// Buckets 2 (one pre-token per lane, 32-wide registers) and 3 (the whole
-// wave per entry, in place in the position-indexed scratch) of the same
-// groups; adds their token counts to tot.
+// Buckets 2 (one pre-token per lane, 32-wide registers, as above) and 3 (the
+// whole wave per entry, in place in the position-indexed gsym / grank) of the
+// same groups; adds their token counts to tot.
 __global__ void __launch_bounds__(MWG) k_merge_wide(EncodeArgs a) {
   __shared__ MergeShared s;
   const int64_t cg = (int64_t)blockIdx.x * kGroup;
@@ -698,7 +718,7 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
   const int32_t *pv = a.pv + c * kChunk;
   const uint32_t *ml = a.miss + c * kMissMax;
   const int32_t *mt = a.mt + c * kMissMax;
-  const int32_t *gsym = a.gsym + c0;
+  const int32_t *res = a.res + c * kMissBytes;
   if (tid == 0) s.n_long = 0;
 
   // this thread's pre-tokens: results, and the list index of each miss
@@ -746,7 +766,7 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
       const uint32_t e = ml[i];
       const int64_t nt = mt[i];
       if (b < 3) {
-        const int32_t *src = gsym + me_start(e);
+        const int32_t *src = res + me_start(e);
         for (int j = 0; j < nt; ++j, ++w) {
           if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, src[j]);
           else overflow = true;

@@ -74,6 +74,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Per-chunk records of the encode pipeline.
 constexpr int kMissMax = kChunk / 2 + 16;  // merge-loop pre-tokens per chunk (each >= 2 bytes)
+constexpr int kMissBytes = kChunk + kHalo;  // bytes of a chunk's lane-merged pre-tokens, at most
 // meta: 8 int32 per chunk
 constexpr int kMetaInts = 8;
 constexpr int kMetaPretokens = 0;  // pre-tokens that start in the chunk
@@ -92,10 +93,12 @@ constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
 //   miss      [G][kMissMax] u32  merge-loop list by length bucket:
 //                                start | len << 13 | overhang << 26
 //   mt        [G][kMissMax] i32  token count of each list entry
-//   gsym      [N] i32   tokens of the list entry that starts at byte g, from gsym[g] on
-//   grank     [N] i32   pair ranks of the workgroup merge, position-indexed
+//   mbytes    [G][kMissBytes] u8   bytes of the lane-merged entries, back to back
+//   res       [G][kMissBytes] i32  their tokens, each entry's at its byte offset
+//   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
+//   grank     [N] i32   pair ranks of the wave merge, position-indexed
 struct EncLayout {
-  size_t meta, tot, off, doc_rng, doc_pt, pv, miss, mt, gsym, grank, total;
+  size_t meta, tot, off, doc_rng, doc_pt, pv, miss, mt, mbytes, res, gsym, grank, total;
 };
 inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   EncLayout L;
@@ -114,6 +117,8 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.pv = take(4 * (size_t)kChunk * G);
   L.miss = take(4 * (size_t)kMissMax * G);
   L.mt = take(4 * (size_t)kMissMax * G);
+  L.mbytes = take((size_t)kMissBytes * G);
+  L.res = take(4 * (size_t)kMissBytes * G);
   L.gsym = take(4 * (size_t)n_bytes);
   L.grank = take(4 * (size_t)n_bytes);
   L.total = o;
@@ -156,6 +161,8 @@ struct EncodeArgs {
   int32_t *pv;
   uint32_t *miss;
   int32_t *mt;
+  uint8_t *mbytes;
+  int32_t *res;
   int32_t *gsym;
   int32_t *grank;
   int32_t *status;
