@@ -33,6 +33,7 @@ struct bpe_model {
   uint8_t *d_exp_bytes = nullptr;
   int32_t *d_inv_map = nullptr;
   int64_t inv_size = 0;
+  int32_t win_d[4] = {0, 0, 0, 0};  // window radii by pre-token class (EncodeArgs::win_d)
   // stage timing (bpe_stage_timing): events of the calls not yet read, per
   // op, stages + 1 per call; spare events for reuse
   bool timing = false;
@@ -122,6 +123,45 @@ bool build_cuckoo(const std::vector<uint64_t> &keys, int bits, std::vector<uint6
   return true;
 }
 
+// Window radii for the long-pre-token merge, by pre-token class.  A pair
+// whose rank is the lowest among all pairs within D symbols on each side is
+// merged by the rank-ordered rounds before any other merge touches its
+// symbols, provided every merge's operands come from lower ranks (so the
+// rounds run in increasing rank) and D is at least the longest token that
+// can form inside the pre-token: a merge chain reaching the pair from
+// further away would build a longer token.  Merges stay inside a pre-token
+// ("Hugging Face Tokenizers v1", section "How v1 works"), so that token's
+// bytes belong to the pre-token: digits only, whitespace only, punctuation
+// only, or letters after an optional space.  D = 0 where the table is not
+// in rank order or a radius exceeds kWinMax.
+void window_radii(const int32_t *merges, int64_t R, const std::vector<int64_t> &len,
+                  const std::vector<int64_t> &order, int32_t win_d[4]) {
+  bool ordered = true;
+  for (int64_t r = 0; r < R; ++r)
+    if (merges[2 * r] >= 256 + r || merges[2 * r + 1] >= 256 + r) ordered = false;
+  const size_t V = (size_t)(256 + R);
+  std::vector<uint8_t> first(V), all(V), rest(V);  // first byte; class bits of all / later bytes
+  for (uint32_t b = 0; b < 256; ++b) {
+    first[b] = (uint8_t)b;
+    all[b] = (uint8_t)(1u << byte_class(b));
+    rest[b] = 0;
+  }
+  for (int64_t v : order) {
+    const int32_t l = merges[2 * (v - 256)], rt = merges[2 * (v - 256) + 1];
+    first[(size_t)v] = first[(size_t)l];
+    all[(size_t)v] = all[(size_t)l] | all[(size_t)rt];
+    rest[(size_t)v] = rest[(size_t)l] | all[(size_t)rt];
+  }
+  int64_t d[4] = {1, 1, 1, 1};
+  for (size_t v = 0; v < V; ++v) {
+    const int64_t n = len[v];
+    for (uint32_t c = 0; c < 4; ++c)
+      if (all[v] == (1u << c)) d[c] = std::max(d[c], n);
+    if (first[v] == 0x20 && (rest[v] & ~(1u << kL)) == 0) d[kL] = std::max(d[kL], n);
+  }
+  for (int c = 0; c < 4; ++c) win_d[c] = (ordered && d[c] <= kWinMax) ? (int32_t)d[c] : 0;
+}
+
 bool on_model_device(const bpe_model *m) {
   int dev = -1;
   return hipGetDevice(&dev) == hipSuccess && dev == m->device;
@@ -168,6 +208,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.grank = (int32_t *)(ws + L.grank);
   a.status = d_status;
   a.n_chunks = enc_chunks(n_bytes);
+  for (int k = 0; k < 4; ++k) a.win_d[k] = model->win_d[k];
   if (launch_encode(a, stream, call_events(model, BPE_OP_ENCODE)) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }
@@ -358,6 +399,7 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
   if (!m) return BPE_ENOMEM;
   m->R = R;
   m->V = V;
+  window_radii(merges, R, len, order, m->win_d);
   m->table_bits = bits;
   if (hipGetDevice(&m->device) != hipSuccess) {
     delete m;

@@ -11,20 +11,8 @@
 namespace bpe {
 namespace {
 
-// Byte classes (the fixed split rule): letters (A-Z, a-z and every byte from
-// 0x80 up), digits, whitespace (0x09-0x0D, 0x20), punctuation (the rest).
-enum : uint32_t { kL = 0, kD = 1, kW = 2, kP = 3 };
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNoStart = INT_MAX;
-
-__device__ __forceinline__ uint32_t byte_class(uint32_t b) {
-  const uint32_t lo = b | 0x20u;
-  if ((lo - 'a' <= 'z' - 'a') || b >= 0x80u) return kL;
-  if (b - '0' <= 9u) return kD;
-  if (b - 9u <= 4u || b == 0x20u) return kW;
-  return kP;
-}
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }

@@ -642,40 +642,205 @@ __global__ void __launch_bounds__(MWG) k_merge(EncodeArgs a) {
   }
 }
 
-// Buckets 2 (one pre-token per lane, 32-wide registers, as above) and 3 (the
-// whole wave per entry, in place in the position-indexed gsym / grank) of the
-// same groups; adds their token counts to tot.
+// Bucket 2 (one pre-token per lane, 32-wide registers, as above) of the same
+// groups; adds its token counts to tot.
 __global__ void __launch_bounds__(MWG) k_merge_wide(EncodeArgs a) {
   __shared__ MergeShared s;
   const int64_t cg = (int64_t)blockIdx.x * kGroup;
   const int nf = (int)min<int64_t>(kGroup, a.n_chunks - cg);
   load_group(a, s, cg, nf);
   int any = 0;
-  for (int f = 0; f < nf; ++f) any += s.meta[f][kMetaBucket + 2] + s.meta[f][kMetaBucket + 3];
+  for (int f = 0; f < nf; ++f) any += s.meta[f][kMetaBucket + 2];
   if (any == 0) return;
-  const int lane = threadIdx.x;
   merge_bucket<32>(a, s, cg, nf, 2);
   __syncthreads();
+  const int lane = threadIdx.x;
+  if (lane < nf && s.tok[lane] != 0) a.tot[cg + lane] += s.tok[lane];
+}
+
+// ---- k_merge_long -------------------------------------------------------------
+
+constexpr int kLdsLong = 2048;    // longest bucket-3 pre-token merged in LDS
+constexpr int kProbeGroups = 8;   // groups of 64 positions whose rank probes go together
+
+struct LongShared {
+  int32_t y[kLdsLong];              // symbols
+  int32_t r[kLdsLong];              // rank of the pair (y[i], y[i + 1]); -1 = to be found
+  uint32_t cand[kLdsLong / 32];     // bit i: the pair is the lowest in its window
+};
+
+// The rounds for one pre-token of n <= kLdsLong symbols (bytes on entry) in
+// LDS, by one wave; returns the final count, the symbols left in y.
+//  D > 0: each round merges every pair whose rank is the lowest among the
+//    pairs within D positions on each side (window_radii on the host gives
+//    why the rank-ordered rounds merge it the same way).  A run of one pair
+//    (x, x) merges at even offsets from its first pair, and only if that
+//    first pair is such a lowest pair: the run's start then cannot move
+//    before its round.
+//  D == 0: each round merges the lowest rank of the whole pre-token, every
+//    occurrence left to right without overlap.
+// Position i belongs to lane i % 64; scans run 64 positions at a time with
+// a carry.  One wave does all the work, so LDS accesses stay in program
+// order and the arrays are rewritten in place.
+__device__ int lds_merge(LongShared &L, int n, int D, const uint64_t *__restrict__ tab, int bits,
+                         const int32_t *__restrict__ pair_rank) {
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1;
+#pragma unroll 8
+  for (int i = lane; i < n; i += MWG)
+    L.r[i] = (i + 1 < n) ? pair_rank[(L.y[i] << 8) | L.y[i + 1]] : kRankInf;
+  while (n > 1) {
+    int32_t gmin = kRankInf;
+    if (D == 0) {
+      for (int i = lane; i < n; i += MWG) gmin = min(gmin, L.r[i]);
+      for (int d = 32; d >= 1; d >>= 1) gmin = min(gmin, __shfl_xor(gmin, d, 64));
+      if (gmin == kRankInf) break;
+    }
+    // 1. the lowest pairs of their windows
+    for (int i0 = 0; i0 < n; i0 += MWG) {
+      const int i = i0 + lane;
+      bool c = false;
+      if (i < n) {
+        const int32_t r = L.r[i];
+        int32_t w = gmin;
+        if (D > 0) {
+          w = r;
+          const int j1 = min(n - 1, i + D);
+          for (int j = max(0, i - D); j <= j1; ++j) w = min(w, L.r[j]);
+        }
+        c = r < kRankInf && r == w;
+      }
+      const uint64_t bc = __ballot(c);
+      if (lane == 0) {
+        L.cand[i0 >> 5] = (uint32_t)bc;
+        L.cand[(i0 >> 5) + 1] = (uint32_t)(bc >> 32);
+      }
+    }
+    // 2. merge flags (run starts by a running maximum) and compaction: a
+    //    symbol whose left neighbour merged is consumed
+    int run = 0;                // run start in force before this group
+    bool prevm = false;         // the position before this group merged
+    int32_t prevr = kRankInf;   // and its rank (its slot may already be rewritten)
+    int out = 0;                // symbols kept so far
+    bool any = false;
+    for (int i0 = 0; i0 < n; i0 += MWG) {
+      const int i = i0 + lane;
+      const bool in = i < n;
+      const int32_t r = in ? L.r[i] : kRankInf;
+      const int32_t y = in ? L.y[i] : 0;
+      int32_t rl = __shfl_up(r, 1, 64);
+      if (lane == 0) rl = prevr;
+      const bool bnd = in && (i == 0 || rl != r);
+      int st = bnd ? i : -1;
+      for (int d = 1; d < 64; d <<= 1) st = max(st, __shfl_up(st, d, 64) | (lane >= d ? 0 : -1));
+      st = max(st, run);
+      const bool c = in && ((L.cand[i >> 5] >> (i & 31)) & 1u);
+      const bool cs = (L.cand[st >> 5] >> (st & 31)) & 1u;
+      const bool m = c && cs && ((i - st) & 1) == 0;
+      const uint64_t bm = __ballot(m);
+      const bool cons = lane == 0 ? prevm : ((bm >> (lane - 1)) & 1u);
+      const bool keep = in && !cons;
+      const uint64_t bk = __ballot(keep);
+      const int o = out + __popcll(bk & below);
+      if (keep) {
+        L.y[o] = m ? 256 + r : y;
+        L.r[o] = m ? -1 : r;
+      }
+      any |= bm != 0;
+      out += __popcll(bk);
+      prevm = (bm >> 63) & 1u;
+      prevr = __shfl(r, 63, 64);
+      run = __shfl(st, 63, 64);
+    }
+    if (!any) break;
+    n = out;
+    // 3. ranks of the pairs that touch a new symbol, the probes of kProbeGroups
+    //    groups of 64 positions issued together
+    for (int i0 = 0; i0 < n; i0 += MWG * kProbeGroups) {
+      int32_t nv[kProbeGroups];
+      uint64_t key[kProbeGroups], s0[kProbeGroups], s1[kProbeGroups];
+      uint32_t need = 0;
+#pragma unroll
+      for (int g = 0; g < kProbeGroups; ++g) {
+        const int i = i0 + MWG * g + lane;
+        nv[g] = kRankInf;
+        key[g] = 0;
+        s0[g] = s1[g] = kEmptySlot;
+        if (i + 1 < n) {
+          const int32_t r = L.r[i];
+          nv[g] = r;
+          if (r == -1 || L.r[i + 1] == -1) {
+            need |= 1u << g;
+            key[g] = pair_key(L.y[i], L.y[i + 1]);
+            s0[g] = tab[pair_slot0(key[g], bits)];
+            s1[g] = tab[pair_slot1(key[g], bits)];
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < kProbeGroups; ++g) {
+        const int i = i0 + MWG * g + lane;
+        if ((need >> g) & 1u) nv[g] = rank_in(s0[g], s1[g], key[g]);
+        if (i < n) L.r[i] = nv[g];
+      }
+    }
+  }
+  return n;
+}
+
+struct LongGroupShared {
+  MergeShared g;
+  LongShared L;
+};
+
+// Bucket 3 of the same groups: one wave per entry, in turn.  An entry of at
+// most kLdsLong bytes is merged in LDS (lds_merge) with the window radius of
+// its class; a longer one in place in the position-indexed gsym / grank
+// (wg_merge).  The tokens end in gsym at the entry's position; adds the
+// token counts to tot.
+__global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
+  __shared__ LongGroupShared s;
+  const int64_t cg = (int64_t)blockIdx.x * kGroup;
+  const int nf = (int)min<int64_t>(kGroup, a.n_chunks - cg);
+  load_group(a, s.g, cg, nf);
+  int any = 0;
+  for (int f = 0; f < nf; ++f) any += s.g.meta[f][kMetaBucket + 3];
+  if (any == 0) return;
+  const int lane = threadIdx.x;
   for (int f = 0; f < nf; ++f) {
-    const int n3 = s.meta[f][kMetaBucket + 3];
-    const int base = s.meta[f][kMetaMisses] - n3;
+    const int n3 = s.g.meta[f][kMetaBucket + 3];
+    const int base = s.g.meta[f][kMetaMisses] - n3;
     const int64_t c = cg + f, c0 = c * kChunk;
     for (int q = 0; q < n3; ++q) {
       const uint32_t e = a.miss[c * kMissMax + base + q];
       const int64_t gs = c0 + me_start(e);
       const int64_t ge = me_over(e) ? wave_global_end(a, gs, c0 + WIN) : gs + me_len(e);
-      for (int64_t p = gs + lane; p < ge; p += MWG) a.gsym[p] = a.bytes[p];
-      __syncthreads();
-      const int64_t nt = wg_merge<MWG>(a.gsym + gs, a.grank + gs, ge - gs, a.table, a.table_bits,
-                                       a.pair_rank, s.r);
+      const int64_t len = ge - gs;
+      int64_t nt;
+      if (len <= kLdsLong) {
+#pragma unroll 8
+        for (int i = lane; i < len; i += MWG) s.L.y[i] = a.bytes[gs + i];
+        __syncthreads();
+        // the pre-token's class: its first byte, or the letter after a leading space
+        uint32_t b = (uint32_t)s.L.y[0];
+        if (b == 0x20u && len > 1) b = (uint32_t)s.L.y[1];
+        nt = lds_merge(s.L, (int)len, a.win_d[byte_class(b)], a.table, a.table_bits,
+                       a.pair_rank);
+        for (int i = lane; i < nt; i += MWG) a.gsym[gs + i] = s.L.y[i];
+      } else {
+        for (int64_t p = gs + lane; p < ge; p += MWG) a.gsym[p] = a.bytes[p];
+        __syncthreads();
+        nt = wg_merge<MWG>(a.gsym + gs, a.grank + gs, len, a.table, a.table_bits, a.pair_rank,
+                           s.g.r);
+      }
       if (lane == 0) {
         a.mt[c * kMissMax + base + q] = (int32_t)nt;
-        s.tok[f] += (int32_t)nt;
+        s.g.tok[f] += (int32_t)nt;
       }
       __syncthreads();
     }
   }
-  if (lane < nf && s.tok[lane] != 0) a.tot[cg + lane] += s.tok[lane];
+  if (lane < nf && s.g.tok[lane] != 0) a.tot[cg + lane] += s.g.tok[lane];
 }
 
 // ---- k_offsets ---------------------------------------------------------------
@@ -827,8 +992,8 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
   return hipGetLastError();
 }
 
-const char *const kEncStageNames[kEncStages] = {"k_find", "k_merge", "k_merge_wide", "k_offsets",
-                                                "k_emit"};
+const char *const kEncStageNames[kEncStages] = {"k_find",       "k_merge",   "k_merge_wide",
+                                                "k_merge_long", "k_offsets", "k_emit"};
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev) {
   const unsigned G = (unsigned)a.n_chunks;
@@ -839,10 +1004,12 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
   if (ev) (void)hipEventRecord(ev[2], stream);
   hipLaunchKernelGGL(k_merge_wide, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[3], stream);
-  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(OWG), 0, stream, a);
+  hipLaunchKernelGGL(k_merge_long, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[4], stream);
-  hipLaunchKernelGGL(k_emit, dim3(G), dim3(WG), 0, stream, a);
+  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(OWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[5], stream);
+  hipLaunchKernelGGL(k_emit, dim3(G), dim3(WG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[6], stream);
   return hipGetLastError();
 }
 

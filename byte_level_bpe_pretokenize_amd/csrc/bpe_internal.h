@@ -6,6 +6,21 @@
 
 namespace bpe {
 
+// ---- byte classes ---------------------------------------------------------
+// The fixed split rule's classes: letters (A-Z, a-z and every byte from 0x80
+// up), digits, whitespace (0x09-0x0D, 0x20), punctuation (the rest).
+// ("Tokenization LLM: ... C++", section "Technical analysis": words,
+// numbers, punctuation and whitespace.)
+enum : uint32_t { kL = 0, kD = 1, kW = 2, kP = 3 };
+
+__host__ __device__ inline uint32_t byte_class(uint32_t b) {
+  const uint32_t lo = b | 0x20u;
+  if ((lo - 'a' <= 'z' - 'a') || b >= 0x80u) return kL;
+  if (b - '0' <= 9u) return kD;
+  if (b - 9u <= 4u || b == 0x20u) return kW;
+  return kP;
+}
+
 // ---- rank table --------------------------------------------------------
 // Two-choice cuckoo hash table in device memory, one 64-bit slot per entry:
 //   bits 42..62  left symbol, bits 21..41 right symbol, bits 0..20 rank.
@@ -71,6 +86,9 @@ inline int64_t enc_chunks(int64_t n_bytes) { return (n_bytes + kChunk - 1) / kCh
 inline int64_t dec_chunks(int64_t n_ids) { return (n_ids + kDecChunk - 1) / kDecChunk; }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Largest window radius of the multi-rank rounds (longer: one rank per round).
+constexpr int kWinMax = 64;
 
 // Per-chunk records of the encode pipeline.
 constexpr int kMissMax = kChunk / 2 + 16;  // merge-loop pre-tokens per chunk (each >= 2 bytes)
@@ -167,6 +185,10 @@ struct EncodeArgs {
   int32_t *grank;
   int32_t *status;
   int64_t n_chunks;
+  // Window radius of the multi-rank rounds for long pre-tokens, by the class
+  // of the pre-token's first letter/digit/space/punctuation byte: the longest
+  // token whose bytes can occur in such a pre-token; 0 = one rank per round.
+  int32_t win_d[4];
 };
 
 struct DecodeArgs {
@@ -195,7 +217,7 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
                         int32_t *status, hipStream_t stream);
 // The encode pipeline for n_bytes > 0 (bpe_encode.hip).  ev: nullptr, or
 // kEncStages + 1 events recorded before the first kernel and after each.
-constexpr int kEncStages = 5;
+constexpr int kEncStages = 6;
 extern const char *const kEncStageNames[kEncStages];
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
 // The decode pipeline for n_ids > 0 (bpe_decode.hip), events as for encode.
