@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -277,28 +278,55 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
   if (rc != BPE_OK) return rc;
   if (status != 0) return BPE_EHIP;
 
-  int64_t n_keep = 0;
-  for (int64_t k = 0; k < D; ++k)
-    n_keep += ioff[(size_t)k + 1] - ioff[(size_t)k] == 1 && ids[(size_t)ioff[(size_t)k]] == cand[(size_t)k];
-  int bits = 8;
-  while (((int64_t)1 << bits) < 2 * n_keep) ++bits;
-  const uint32_t mask = (1u << bits) - 1u;
-  std::vector<uint32_t> slots((size_t)8 << bits, 0u);
+  // the entries: {tag, symbol, key[6]} and both hashes
+  std::vector<std::array<uint32_t, 8>> items;
+  std::vector<uint32_t> h0s, h1s;
   for (int64_t k = 0; k < D; ++k) {
     if (!(ioff[(size_t)k + 1] - ioff[(size_t)k] == 1 && ids[(size_t)ioff[(size_t)k]] == cand[(size_t)k]))
       continue;
     const int len = (int)(doc_off[(size_t)k + 1] - doc_off[(size_t)k]);
-    uint32_t w[kWordWords] = {0, 0, 0, 0, 0, 0};
+    std::array<uint32_t, 8> it{};
+    uint32_t *w = &it[2];
     for (int j = 0; j < len; ++j)
       w[j >> 2] |= (uint32_t)text[(size_t)doc_off[(size_t)k] + j] << (8 * (j & 3));
-    const uint32_t h = word_hash(w, len);
-    uint32_t i = h & mask;
-    while (slots[(size_t)8 * i] != 0u) i = (i + 1) & mask;
-    uint32_t *slot = &slots[(size_t)8 * i];
-    slot[0] = word_tag(h, len);
-    slot[1] = (uint32_t)cand[(size_t)k];
-    for (int j = 0; j < kWordWords; ++j) slot[2 + j] = w[j];
+    uint32_t h0, h1;
+    word_hashes(w, len, h0, h1);
+    it[0] = word_tag(h0, len);
+    it[1] = (uint32_t)cand[(size_t)k];
+    items.push_back(it);
+    h0s.push_back(h0);
+    h1s.push_back(h1);
   }
+  const int64_t n_keep = (int64_t)items.size();
+  // two-choice cuckoo placement, capacity a power of two >= 2.5 entries,
+  // doubled until every entry has a slot
+  int bits = 8;
+  while (((int64_t)1 << bits) < 5 * n_keep / 2) ++bits;
+  std::vector<int32_t> at;
+  for (;; ++bits) {
+    if (bits > 30) return BPE_ENOMEM;
+    const uint32_t mask = (1u << bits) - 1u;
+    at.assign((size_t)1 << bits, -1);
+    const int max_kicks = 64 + 4 * bits;
+    bool ok = true;
+    for (int32_t e = 0; e < (int32_t)n_keep && ok; ++e) {
+      int32_t item = e;
+      uint32_t from = word_slot0(h0s[(size_t)e], mask);
+      for (int kick = 0;; ++kick) {
+        const uint32_t a = word_slot0(h0s[(size_t)item], mask);
+        const uint32_t b = word_slot1(h0s[(size_t)item], h1s[(size_t)item], mask);
+        if (at[a] < 0) { at[a] = item; break; }
+        if (at[b] < 0) { at[b] = item; break; }
+        if (kick == max_kicks) { ok = false; break; }
+        from = (from == a) ? b : a;  // the occupant of the other slot moves on
+        std::swap(item, at[from]);
+      }
+    }
+    if (ok) break;
+  }
+  std::vector<uint32_t> slots((size_t)8 << bits, 0u);
+  for (size_t i = 0; i < at.size(); ++i)
+    if (at[i] >= 0) std::memcpy(&slots[8 * i], items[(size_t)at[i]].data(), 32);
   rc = upload(reinterpret_cast<uint32_t **>(&m->d_words), slots.data(), slots.size(), stream);
   if (rc == BPE_OK) {
     m->word_bits = bits;

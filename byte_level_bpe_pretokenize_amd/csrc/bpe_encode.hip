@@ -300,25 +300,28 @@ __device__ __forceinline__ void pretoken_words(const FindShared &s, int st, int 
   }
 }
 
-// Symbol stored for these bytes in the word table, or -1.  Both halves of
-// a slot are loaded together.
+// Symbol stored for these bytes in the word table, or -1: both slots of
+// the key are loaded at once (two-choice cuckoo table).
 __device__ __forceinline__ int32_t word_lookup(const uint4 *__restrict__ tab, uint32_t mask,
                                                const uint32_t w[kWordWords], int len) {
-  const uint32_t h = word_hash(w, len);
-  const uint32_t tag = word_tag(h, len);
-  uint32_t i = h & mask;
-  for (;;) {
-    const uint4 x = tab[2 * i];
-    const uint4 y = tab[2 * i + 1];
-    if (x.x == 0) return -1;
-    if (x.x == tag && x.z == w[0] && x.w == w[1] && y.x == w[2] && y.y == w[3] && y.z == w[4] &&
-        y.w == w[5])
-      return (int32_t)x.y;
-    i = (i + 1) & mask;
-  }
+  uint32_t h0, h1;
+  word_hashes(w, len, h0, h1);
+  const uint32_t tag = word_tag(h0, len);
+  const uint32_t i0 = word_slot0(h0, mask), i1 = word_slot1(h0, h1, mask);
+  const uint4 x0 = tab[2 * i0], y0 = tab[2 * i0 + 1];
+  const uint4 x1 = tab[2 * i1], y1 = tab[2 * i1 + 1];
+  if (x0.x == tag && x0.z == w[0] && x0.w == w[1] && y0.x == w[2] && y0.y == w[3] &&
+      y0.z == w[4] && y0.w == w[5])
+    return (int32_t)x0.y;
+  if (x1.x == tag && x1.z == w[0] && x1.w == w[1] && y1.x == w[2] && y1.y == w[3] &&
+      y1.z == w[4] && y1.w == w[5])
+    return (int32_t)x1.y;
+  return -1;
 }
 
-__global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
+// Eight waves per SIMD (latency-bound: occupancy pays for the few registers
+// this spills).
+__global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   __shared__ FindShared s;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
 
@@ -403,21 +406,26 @@ __global__ void __launch_bounds__(WG) k_find(EncodeArgs a) {
   //    that follows a non-whitespace byte (or opens the document) leads a
   //    letter run.  Positions past the input end read as starts.
   for (int g = tid; g < SB_HALF; g += WG) {
+    // this thread's 16 bytes, the 4 before them, and the document-start bits
+    // of positions 16g - 1 .. 16g + 15, from LDS in four reads
+    const u32x4 cur = *reinterpret_cast<const u32x4 *>(&s.B[16 + 16 * g]);
+    const uint32_t before = *reinterpret_cast<const uint32_t *>(&s.B[16 + 16 * g - 4]);
+    const int q = 16 * g - 1 + DB_OFF;
+    const uint64_t dw = (uint64_t)s.DB[q >> 5] | ((uint64_t)s.DB[(q >> 5) + 1] << 32);
+    const uint32_t doc = (uint32_t)(dw >> (q & 31));  // bit k + 1: position 16g + k
+    uint32_t bytes[5] = {before, cur.x, cur.y, cur.z, cur.w};
     uint32_t m = 0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int p = 16 * g + k;
-      bool st;
-      if (p >= nwin) {
-        st = win_reaches_end;
-      } else if (db_bit(s, p)) {
-        st = true;
-      } else {
-        const uint32_t b0 = s.B[16 + p], b1 = s.B[16 + p - 1], b2 = s.B[16 + p - 2];
-        const uint32_t k0 = byte_class(b0), k1 = byte_class(b1);
-        const bool attach = k0 == kL && b1 == 0x20u && (db_bit(s, p - 1) || byte_class(b2) != kW);
-        st = k0 != k1 && !attach;
-      }
+      // byte at offset k + 4 of the 20-byte window
+      const uint32_t b0 = (bytes[(k + 4) >> 2] >> (8 * ((k + 4) & 3))) & 0xFFu;
+      const uint32_t b1 = (bytes[(k + 3) >> 2] >> (8 * ((k + 3) & 3))) & 0xFFu;
+      const uint32_t b2 = (bytes[(k + 2) >> 2] >> (8 * ((k + 2) & 3))) & 0xFFu;
+      const bool d0 = (doc >> (k + 1)) & 1u, d1 = (doc >> k) & 1u;
+      const uint32_t k0 = byte_class(b0), k1 = byte_class(b1);
+      const bool attach = k0 == kL && b1 == 0x20u && (d1 || byte_class(b2) != kW);
+      const bool st = p >= nwin ? win_reaches_end : (d0 || (k0 != k1 && !attach));
       m |= (uint32_t)st << k;
     }
     reinterpret_cast<uint16_t *>(s.SB)[g] = (uint16_t)m;
