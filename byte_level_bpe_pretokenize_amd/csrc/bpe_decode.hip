@@ -72,11 +72,14 @@ __global__ void __launch_bounds__(SWG) k_dec_scan(DecodeArgs a) {
   chunk_offsets<SWG>(a.tot, a.off, a.n_chunks, a.status, red64);
 }
 
+constexpr int kDecStage = 16384;  // output bytes a chunk may stage in LDS
+
 struct WriteShared {
   int32_t len[kDecChunk];
   int64_t excl[DWG];
   int64_t red64[DWG / 64];
   int64_t o_lo, o_hi;
+  alignas(16) uint8_t stage[kDecStage + 16];
 };
 
 __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
@@ -113,19 +116,51 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
   const int64_t ex = block_excl_sum<int64_t, DWG>(mine, s.red64, &total);
   s.excl[tid] = ex;
   bool overflow = false;
-  int64_t w = base + ex;
-  for (int j = 0; j < DPT; ++j) {
-    const int k = tid * DPT + j;
-    const int32_t len = s.len[k];
-    if (len > 0) {
-      const int32_t sym = dec_sym(a, a.ids[i0 + k]);
-      const uint8_t *src = a.exp_bytes + a.exp_off[sym];
-      for (int q = 0; q < len; ++q) {
-        if (w + q < a.out_cap) a.out[w + q] = src[q];
-        else overflow = true;
+  if (total <= kDecStage) {
+    // stage the bytes in LDS at the output's 16-byte phase, then write whole
+    // aligned 16-byte blocks (bytes at the two ends)
+    const int lead = (int)(((uintptr_t)(a.out + base)) & 15u);
+    int w = lead + (int)ex;
+    for (int j = 0; j < DPT; ++j) {
+      const int k = tid * DPT + j;
+      const int32_t len = s.len[k];
+      if (len > 0) {
+        const int32_t sym = dec_sym(a, a.ids[i0 + k]);
+        const uint8_t *src = a.exp_bytes + a.exp_off[sym];
+        for (int q = 0; q < len; ++q) s.stage[w + q] = src[q];
+      }
+      w += len;
+    }
+    __syncthreads();
+    const int nblk = (lead + (int)total + 15) >> 4;
+    uint8_t *g0 = a.out + base - lead;  // 16-byte aligned
+    for (int blk = tid; blk < nblk; blk += DWG) {
+      const int lo = 16 * blk;
+      const int64_t gpos = base - lead + lo;  // output index of stage[lo]
+      if (lo >= lead && lo + 16 <= lead + (int)total && gpos + 16 <= a.out_cap) {
+        *reinterpret_cast<u32x4 *>(g0 + lo) = *reinterpret_cast<const u32x4 *>(&s.stage[lo]);
+      } else {
+        for (int q = max(lo, lead); q < min(lo + 16, lead + (int)total); ++q) {
+          if (base - lead + q < a.out_cap) g0[q] = s.stage[q];
+          else overflow = true;
+        }
       }
     }
-    w += len;
+  } else {
+    int64_t w = base + ex;
+    for (int j = 0; j < DPT; ++j) {
+      const int k = tid * DPT + j;
+      const int32_t len = s.len[k];
+      if (len > 0) {
+        const int32_t sym = dec_sym(a, a.ids[i0 + k]);
+        const uint8_t *src = a.exp_bytes + a.exp_off[sym];
+        for (int q = 0; q < len; ++q) {
+          if (w + q < a.out_cap) a.out[w + q] = src[q];
+          else overflow = true;
+        }
+      }
+      w += len;
+    }
   }
   if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_BYTES_CAPACITY);
   __syncthreads();

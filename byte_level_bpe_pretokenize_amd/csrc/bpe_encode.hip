@@ -455,7 +455,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
 
   // 4. each thread resolves a contiguous block of the list: a single byte is
   //    its own token; a pre-token that is a whole word-table entry takes its
-  //    symbol; the others go to the merge-loop list (pv = -1 - bucket)
+  //    symbol; the others go to the merge-loop list (pv = -1 - list index)
   const int per = (n_pt + WG - 1) / WG;  // <= 16
   const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
   int32_t *pv = a.pv + c * kChunk;
@@ -477,12 +477,12 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     }
     if (v < 0) {
       const int b = bucket_of(len, over);
-      v = -1 - b;
       bcnt += (int64_t)1 << (16 * b);
       if (b < 3) blen += (int64_t)len << (16 * b);
       codes |= (uint64_t)(1 + b) << (3 * (k - k0));
+    } else {
+      pv[k] = v;
     }
-    pv[k] = v;
   }
   int64_t btot, ltot;
   const int64_t bex = block_excl_sum<int64_t, WG>(bcnt, s.r.red64, &btot);
@@ -508,15 +508,17 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
         const int st = s.PS[k];
         const bool over = overhang && k == n_pt - 1;
         const int len = over ? 0 : (int)s.PS[k + 1] - st;
+        const int idx = bfield(at, b);
         if (b < 3) {
           // lane-merged entries: their bytes go to the dense region
           const int o = bfield(bo, b);
           for (int j = 0; j < len; ++j) mb[o + j] = s.B[16 + st + j];
-          ml[bfield(at, b)] = miss_entry(o, len, false);
+          ml[idx] = miss_entry(o, len, false);
           bo += (int64_t)len << (16 * b);
         } else {
-          ml[bfield(at, b)] = miss_entry(st, len, over);
+          ml[idx] = miss_entry(st, len, over);
         }
+        pv[k] = -1 - idx;
         at += (int64_t)1 << (16 * b);
       }
     }
@@ -878,15 +880,7 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
   const int64_t c0 = c * kChunk;
   const int32_t *meta = a.meta + kMetaInts * c;
   const int n_pt = meta[kMetaPretokens];
-  int64_t at = 0;  // first list index of each bucket, packed
-  {
-    int base = 0;
-#pragma unroll
-    for (int b = 0; b < kBuckets; ++b) {
-      at += (int64_t)base << (16 * b);
-      base += meta[kMetaBucket + b];
-    }
-  }
+  const int first3 = meta[kMetaMisses] - meta[kMetaBucket + 3];  // list index of bucket 3
   const int64_t base = a.off[c];
   const int32_t *pv = a.pv + c * kChunk;
   const uint32_t *ml = a.miss + c * kMissMax;
@@ -894,29 +888,13 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
   const int32_t *res = a.res + c * kMissBytes;
   if (tid == 0) s.n_long = 0;
 
-  // this thread's pre-tokens: results, and the list index of each miss
+  // this thread's pre-tokens: a symbol, or -1 - the index of a list entry
   const int per = (n_pt + WG - 1) / WG;
   const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
-  int64_t bcnt = 0;
+  int64_t cnt = 0;
   for (int k = k0; k < k1; ++k) {
     const int32_t v = pv[k];
-    if (v < 0) bcnt += (int64_t)1 << (16 * (-1 - v));
-  }
-  int64_t btot;
-  at += block_excl_sum<int64_t, WG>(bcnt, s.r.red64, &btot);
-  int64_t cnt = 0;
-  {
-    int64_t q = at;
-    for (int k = k0; k < k1; ++k) {
-      const int32_t v = pv[k];
-      if (v >= 0) {
-        ++cnt;
-      } else {
-        const int b = -1 - v;
-        cnt += mt[bfield(q, b)];
-        q += (int64_t)1 << (16 * b);
-      }
-    }
+    cnt += v >= 0 ? 1 : mt[-1 - v];
   }
   int64_t total;
   const int64_t ex = block_excl_sum<int64_t, WG>(cnt, s.r.red64, &total);
@@ -933,12 +911,10 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
         ++w;
         continue;
       }
-      const int b = -1 - x;
-      const int i = bfield(at, b);
-      at += (int64_t)1 << (16 * b);
+      const int i = -1 - x;
       const uint32_t e = ml[i];
       const int64_t nt = mt[i];
-      if (b < 3) {
+      if (i < first3) {
         const int32_t *src = res + me_start(e);
         for (int j = 0; j < nt; ++j, ++w) {
           if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, src[j]);
