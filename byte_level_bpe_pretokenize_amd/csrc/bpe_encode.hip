@@ -33,7 +33,7 @@
 namespace bpe {
 namespace {
 
-constexpr int WG = kEncThreads;             // k_find, k_emit: 4 waves
+constexpr int WG = kEncThreads;             // k_find: 4 waves
 constexpr int MWG = 64;                     // k_merge: one wave per chunk
 constexpr int OWG = 1024;                   // k_offsets: one workgroup
 constexpr int WIN = kChunk + kHalo;         // window positions [0, WIN)
@@ -864,16 +864,21 @@ __global__ void __launch_bounds__(OWG) k_offsets(EncodeArgs a) {
 
 // ---- k_emit -------------------------------------------------------------------
 
+constexpr int EWG = 256;  // k_emit threads per chunk
+
 struct EmitShared {
-  int32_t tokoff[kChunk + 1];  // token offset of each pre-token within the chunk
-  int64_t lw[kMaxLong];        // longer entries: output position, symbols, count
+  int64_t ex[EWG];        // each thread's first token, relative to the chunk
+  int64_t lw[kMaxLong];   // longer entries: output position, symbols, count
   int64_t lsrc[kMaxLong];
   int64_t lnt[kMaxLong];
   int32_t n_long;
-  Red<WG> r;
+  Red<EWG> r;
 };
 
-__global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
+// Writes a chunk's IDs at its offset, and the offsets of the documents that
+// start in it.  Each thread takes a contiguous block of the chunk's
+// pre-tokens.
+__global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   __shared__ EmitShared s;
   const int tid = threadIdx.x;
   const int64_t c = blockIdx.x;
@@ -889,7 +894,7 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
   if (tid == 0) s.n_long = 0;
 
   // this thread's pre-tokens: a symbol, or -1 - the index of a list entry
-  const int per = (n_pt + WG - 1) / WG;
+  const int per = (n_pt + EWG - 1) / EWG;
   const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
   int64_t cnt = 0;
   for (int k = k0; k < k1; ++k) {
@@ -897,13 +902,12 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
     cnt += v >= 0 ? 1 : mt[-1 - v];
   }
   int64_t total;
-  const int64_t ex = block_excl_sum<int64_t, WG>(cnt, s.r.red64, &total);
-  if (tid == 0) s.tokoff[n_pt] = (int32_t)total;
+  const int64_t ex = block_excl_sum<int64_t, EWG>(cnt, s.r.red64, &total);
+  s.ex[tid] = ex;
   bool overflow = false;
   {
     int64_t w = base + ex;
     for (int k = k0; k < k1; ++k) {
-      s.tokoff[k] = (int32_t)(w - base);
       const int32_t x = pv[k];
       if (x >= 0) {
         if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, x);
@@ -933,7 +937,7 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
   // longer entries' symbols, copied by the whole workgroup
   for (int q = 0; q < s.n_long; ++q) {
     const int64_t w0 = s.lw[q], src = s.lsrc[q], nt = s.lnt[q];
-    for (int64_t j = tid; j < nt; j += WG) {
+    for (int64_t j = tid; j < nt; j += EWG) {
       const int64_t w = w0 + j;
       if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, a.gsym[src + j]);
       else overflow = true;
@@ -941,15 +945,25 @@ __global__ void __launch_bounds__(WG) k_emit(EncodeArgs a) {
   }
   if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
   // per-document offsets: a document starting at pre-token k begins after
-  // every token of the pre-tokens before k
+  // every token of the pre-tokens before k (those of k's thread before k are
+  // counted again)
   const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
-  for (int64_t d = dlo + tid; d < dhi; d += WG) {
+  for (int64_t d = dlo + tid; d < dhi; d += EWG) {
     const int k = min(max(a.doc_pt[d], 0), n_pt);
-    a.id_off[d] = base + s.tokoff[k];
+    int64_t o = total;
+    if (k < n_pt) {
+      const int t = k / per;
+      o = s.ex[t];
+      for (int kk = t * per; kk < k; ++kk) {
+        const int32_t v = pv[kk];
+        o += v >= 0 ? 1 : mt[-1 - v];
+      }
+    }
+    a.id_off[d] = base + o;
   }
   if (c == a.n_chunks - 1) {
     const int64_t end = base + (a.tot[c] & kCountMask);
-    for (int64_t d = dhi + tid; d <= a.n_docs; d += WG) a.id_off[d] = end;
+    for (int64_t d = dhi + tid; d <= a.n_docs; d += EWG) a.id_off[d] = end;
   }
 }
 
@@ -992,7 +1006,7 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
   if (ev) (void)hipEventRecord(ev[4], stream);
   hipLaunchKernelGGL(k_offsets, dim3(1), dim3(OWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[5], stream);
-  hipLaunchKernelGGL(k_emit, dim3(G), dim3(WG), 0, stream, a);
+  hipLaunchKernelGGL(k_emit, dim3(G), dim3(EWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[6], stream);
   return hipGetLastError();
 }
