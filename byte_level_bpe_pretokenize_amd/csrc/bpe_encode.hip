@@ -243,6 +243,57 @@ __device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const uint64_t *
   return n;
 }
 
+// ---- start bits, four bytes per operation --------------------------------------
+// Per-byte flags live in the high bit of each byte of a 32-bit word.
+
+__device__ __forceinline__ uint32_t spread4(uint32_t nib) {  // bit k -> bit 8k + 7
+  return (nib * 0x10204080u) & 0x80808080u;
+}
+__device__ __forceinline__ uint32_t pack4(uint32_t m) {  // bit 8k + 7 -> bit k
+  return ((((m >> 7) & 0x01010101u) * 0x01020408u) >> 24) & 0xFu;
+}
+
+// Pre-token start bits of the positions 16g .. 16g + 15 (bit k: position
+// 16g + k) from the 20 bytes at positions 16g - 4 .. 16g + 15 (w[0]: the four
+// before) and the document-start bits doc (bit k + 1: position 16g + k, bit
+// 0: position 16g - 1).  A position starts a pre-token when it starts a
+// document, or when its class differs from the byte before's, unless it is a
+// letter after a single space that follows a non-whitespace byte (or starts
+// its document).  Classes: letters A-Z, a-z and bytes >= 0x80; digits;
+// whitespace 0x09-0x0D and 0x20; punctuation, the rest.
+__device__ __forceinline__ uint32_t start_bits16(const uint32_t w[5], uint32_t doc) {
+  constexpr uint32_t H = 0x80808080u, M7 = 0x7F7F7F7Fu;
+  uint32_t L[5], D[5], W[5], P[5], S[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const uint32_t x = w[k], hi = x & H, z = x & M7;
+    const uint32_t y = (x | 0x20202020u) & M7;  // ASCII letters folded to lower case
+    L[k] = hi | ((y + 0x1F1F1F1Fu) & ~(y + 0x05050505u) & H);      // 'a' <= y <= 'z'
+    D[k] = (z + 0x50505050u) & ~(z + 0x46464646u) & H & ~hi;        // '0' <= z <= '9'
+    const uint32_t tb = (z + 0x77777777u) & ~(z + 0x72727272u) & H & ~hi;  // 0x09..0x0D
+    const uint32_t v = x ^ 0x20202020u;
+    S[k] = ~(((v & M7) + M7) | v) & H;  // byte == 0x20
+    W[k] = tb | S[k];
+    P[k] = H & ~(L[k] | D[k] | W[k]);
+  }
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 1; k < 5; ++k) {
+    // the same flags one and two bytes earlier
+#define PREV1(m) (((m)[k] << 8) | ((m)[k - 1] >> 24))
+#define PREV2(m) (((m)[k] << 16) | ((m)[k - 1] >> 16))
+    const uint32_t eq = (L[k] & PREV1(L)) | (D[k] & PREV1(D)) | (W[k] & PREV1(W)) |
+                        (P[k] & PREV1(P));
+    const uint32_t d0 = spread4((doc >> (4 * (k - 1) + 1)) & 0xFu);
+    const uint32_t d1 = spread4((doc >> (4 * (k - 1))) & 0xFu);
+    const uint32_t attach = L[k] & PREV1(S) & (d1 | (~PREV2(W) & H));
+#undef PREV1
+#undef PREV2
+    out |= pack4(d0 | (~eq & ~attach & H)) << (4 * (k - 1));
+  }
+  return out;
+}
+
 // ---- k_find -------------------------------------------------------------------
 
 struct FindShared {
@@ -413,20 +464,13 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     const int q = 16 * g - 1 + DB_OFF;
     const uint64_t dw = (uint64_t)s.DB[q >> 5] | ((uint64_t)s.DB[(q >> 5) + 1] << 32);
     const uint32_t doc = (uint32_t)(dw >> (q & 31));  // bit k + 1: position 16g + k
-    uint32_t bytes[5] = {before, cur.x, cur.y, cur.z, cur.w};
-    uint32_t m = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int p = 16 * g + k;
-      // byte at offset k + 4 of the 20-byte window
-      const uint32_t b0 = (bytes[(k + 4) >> 2] >> (8 * ((k + 4) & 3))) & 0xFFu;
-      const uint32_t b1 = (bytes[(k + 3) >> 2] >> (8 * ((k + 3) & 3))) & 0xFFu;
-      const uint32_t b2 = (bytes[(k + 2) >> 2] >> (8 * ((k + 2) & 3))) & 0xFFu;
-      const bool d0 = (doc >> (k + 1)) & 1u, d1 = (doc >> k) & 1u;
-      const uint32_t k0 = byte_class(b0), k1 = byte_class(b1);
-      const bool attach = k0 == kL && b1 == 0x20u && (d1 || byte_class(b2) != kW);
-      const bool st = p >= nwin ? win_reaches_end : (d0 || (k0 != k1 && !attach));
-      m |= (uint32_t)st << k;
+    const uint32_t w[5] = {before, cur.x, cur.y, cur.z, cur.w};
+    uint32_t m = start_bits16(w, doc);
+    // positions at or past the window's end read as starts only at the input's end
+    const int lim = nwin - 16 * g;
+    if (lim < 16) {
+      const uint32_t past = lim <= 0 ? 0xFFFFu : (0xFFFFu << lim) & 0xFFFFu;
+      m = (m & ~past) | (win_reaches_end ? past : 0u);
     }
     reinterpret_cast<uint16_t *>(s.SB)[g] = (uint16_t)m;
   }

@@ -260,3 +260,37 @@ def test_determinism(dev):
     a1, o1, s1 = gpu_encode(model, b.data, b.doc_off)
     a2, o2, s2 = gpu_encode(model, b.data, b.doc_off)
     assert s1 == 0 and s2 == 0 and np.array_equal(a1, a2) and np.array_equal(o1, o2)
+
+
+def test_long_pretokens_windowed_rounds(dev):
+    # pre-tokens longer than 32 bytes go to the wave merge (multi-rank rounds
+    # for tables in rank order): random digit runs up to 2048, single-letter
+    # runs on both sides of the in-LDS limit, mixed-script letter runs, and
+    # whitespace / punctuation runs
+    model, table = model_pair("adversarial")
+    rng = np.random.default_rng(31)
+    docs = []
+    for n in [33, 64, 200, 1000, 2047, 2048, 2049, 3000]:
+        docs.append(rng.integers(48, 58, n).astype(np.uint8).tobytes())
+    for n in [40, 2047, 2048, 2049, 4096, 6000]:
+        docs.append(bytes([int(rng.integers(97, 123))]) * n)
+        docs.append(b" " + bytes([int(rng.integers(65, 91))]) * n)
+    alphabet = "abcdefXYZéüßжщ中文字节的🐈🌍"
+    for n in [20, 60, 300, 900]:
+        docs.append(" ".join("".join(rng.choice(list(alphabet), int(rng.integers(30, 90))))
+                             for _ in range(n // 30 + 1)).encode())
+    docs.append(b" " * 100 + b"\t\n" * 40 + b"!?" * 300)
+    data, off = batch_from_docs(docs)
+    ids, ioff = check_encode(model, table, data, off)
+    out, _, st = gpu_decode(model, ids, ioff)
+    assert st == 0 and np.array_equal(out, data)
+
+
+def test_long_pretokens_out_of_order_table(dev):
+    # a table whose ranks are not in creation order: one rank per round
+    rng = np.random.default_rng(17)
+    merges = _random_acyclic_table(rng, 12, alphabet=(48, 49, 50))
+    model, table = Model(merges), O.Table(merges)
+    docs = [bytes(rng.choice([48, 49, 50], int(n)).astype(np.uint8)) for n in (40, 300, 2048, 2500)]
+    data, off = batch_from_docs(docs)
+    check_encode(model, table, data, off)
