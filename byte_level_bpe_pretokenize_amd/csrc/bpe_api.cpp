@@ -26,6 +26,7 @@ struct bpe_model {
   int32_t *d_pair_rank = nullptr;   // [65536] ranks of byte pairs
   uint4 *d_words = nullptr;         // word table (2 uint4 per slot), or nullptr
   int word_bits = 0;
+  uint32_t word_seed = 0;
   int64_t n_words = 0;
   // decode tables
   bool decode_ok = false;
@@ -195,6 +196,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.pair_rank = model->d_pair_rank;
   a.words = words;
   a.word_bits = model->word_bits;
+  a.word_seed = model->word_seed;
   a.meta = (int32_t *)(ws + L.meta);
   a.tot = (int64_t *)(ws + L.tot);
   a.off = (int64_t *)(ws + L.off);
@@ -278,9 +280,8 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
   if (rc != BPE_OK) return rc;
   if (status != 0) return BPE_EHIP;
 
-  // the entries: {tag, symbol, key[6]} and both hashes
+  // the entries: {key length, symbol, key[6]}
   std::vector<std::array<uint32_t, 8>> items;
-  std::vector<uint32_t> h0s, h1s;
   for (int64_t k = 0; k < D; ++k) {
     if (!(ioff[(size_t)k + 1] - ioff[(size_t)k] == 1 && ids[(size_t)ioff[(size_t)k]] == cand[(size_t)k]))
       continue;
@@ -289,32 +290,33 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
     uint32_t *w = &it[2];
     for (int j = 0; j < len; ++j)
       w[j >> 2] |= (uint32_t)text[(size_t)doc_off[(size_t)k] + j] << (8 * (j & 3));
-    uint32_t h0, h1;
-    word_hashes(w, len, h0, h1);
-    it[0] = word_tag(h0, len);
+    it[0] = (uint32_t)len;
     it[1] = (uint32_t)cand[(size_t)k];
     items.push_back(it);
-    h0s.push_back(h0);
-    h1s.push_back(h1);
   }
   const int64_t n_keep = (int64_t)items.size();
-  // two-choice cuckoo placement, capacity a power of two >= 2.5 entries,
-  // doubled until every entry has a slot
+  // two-choice cuckoo placement, capacity a power of two >= 2.5 entries;
+  // on failure another seed, then twice the capacity
   int bits = 8;
   while (((int64_t)1 << bits) < 5 * n_keep / 2) ++bits;
   std::vector<int32_t> at;
-  for (;; ++bits) {
+  std::vector<uint32_t> hs((size_t)n_keep);
+  uint32_t seed = 0;
+  for (int attempt = 0;; ++attempt) {
     if (bits > 30) return BPE_ENOMEM;
+    seed = 0x9E3779B9u * (uint32_t)(attempt + 1);
+    for (int64_t e = 0; e < n_keep; ++e)
+      hs[(size_t)e] = word_hash(&items[(size_t)e][2], (int)items[(size_t)e][0], seed);
     const uint32_t mask = (1u << bits) - 1u;
     at.assign((size_t)1 << bits, -1);
     const int max_kicks = 64 + 4 * bits;
     bool ok = true;
     for (int32_t e = 0; e < (int32_t)n_keep && ok; ++e) {
       int32_t item = e;
-      uint32_t from = word_slot0(h0s[(size_t)e], mask);
+      uint32_t from = word_slot0(hs[(size_t)e], mask);
       for (int kick = 0;; ++kick) {
-        const uint32_t a = word_slot0(h0s[(size_t)item], mask);
-        const uint32_t b = word_slot1(h0s[(size_t)item], h1s[(size_t)item], mask);
+        const uint32_t a = word_slot0(hs[(size_t)item], mask);
+        const uint32_t b = word_slot1(hs[(size_t)item], mask);
         if (at[a] < 0) { at[a] = item; break; }
         if (at[b] < 0) { at[b] = item; break; }
         if (kick == max_kicks) { ok = false; break; }
@@ -323,13 +325,17 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
       }
     }
     if (ok) break;
+    if (attempt % 2 == 1) ++bits;
   }
+  for (int64_t e = 0; e < n_keep; ++e)
+    items[(size_t)e][0] = word_tag(hs[(size_t)e], (int)items[(size_t)e][0]);
   std::vector<uint32_t> slots((size_t)8 << bits, 0u);
   for (size_t i = 0; i < at.size(); ++i)
     if (at[i] >= 0) std::memcpy(&slots[8 * i], items[(size_t)at[i]].data(), 32);
   rc = upload(reinterpret_cast<uint32_t **>(&m->d_words), slots.data(), slots.size(), stream);
   if (rc == BPE_OK) {
     m->word_bits = bits;
+    m->word_seed = seed;
     m->n_words = n_keep;
   }
   return rc;

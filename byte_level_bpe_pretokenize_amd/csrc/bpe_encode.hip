@@ -354,11 +354,11 @@ __device__ __forceinline__ void pretoken_words(const FindShared &s, int st, int 
 // Symbol stored for these bytes in the word table, or -1: both slots of
 // the key are loaded at once (two-choice cuckoo table).
 __device__ __forceinline__ int32_t word_lookup(const uint4 *__restrict__ tab, uint32_t mask,
-                                               const uint32_t w[kWordWords], int len) {
-  uint32_t h0, h1;
-  word_hashes(w, len, h0, h1);
-  const uint32_t tag = word_tag(h0, len);
-  const uint32_t i0 = word_slot0(h0, mask), i1 = word_slot1(h0, h1, mask);
+                                               uint32_t seed, const uint32_t w[kWordWords],
+                                               int len) {
+  const uint32_t h = word_hash(w, len, seed);
+  const uint32_t tag = word_tag(h, len);
+  const uint32_t i0 = word_slot0(h, mask), i1 = word_slot1(h, mask);
   const uint4 x0 = tab[2 * i0], y0 = tab[2 * i0 + 1];
   const uint4 x1 = tab[2 * i1], y1 = tab[2 * i1 + 1];
   if (x0.x == tag && x0.z == w[0] && x0.w == w[1] && y0.x == w[2] && y0.y == w[3] &&
@@ -517,7 +517,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     } else if (!over && a.words && len <= kWordMax) {
       uint32_t w[kWordWords];
       pretoken_words(s, st, len, w);
-      v = word_lookup(a.words, wmask, w, len);
+      v = word_lookup(a.words, wmask, a.word_seed, w, len);
     }
     if (v < 0) {
       const int b = bucket_of(len, over);

@@ -55,35 +55,32 @@ __host__ __device__ inline uint64_t pair_slot1(uint64_t key, int bits) {
 // yields exactly [s], encodes to [s] without running the merge loop.  One
 // 32-byte slot per entry: {tag, symbol, key[6]}; tag = (h0 & ~0xff) | len
 // (0 = empty); key = the bytes as six little-endian words, zero padded.
-// Two-choice cuckoo hashing: an entry sits in slot h0 or slot h1 (both
-// masked to the capacity), so a lookup loads both slots at once and never
-// follows a chain.
+// Two-choice cuckoo hashing: an entry sits in one of two slots, both
+// derived from one seeded 32-bit hash h, so a lookup loads both slots at
+// once and never follows a chain.  Keys that share h share both slots; the
+// table's seed is chosen at load so that every key finds a slot.
 constexpr int kWordMax = 24;
 constexpr int kWordWords = kWordMax / 4;
 
-// Two independent 32-bit hashes of a key.
-__host__ __device__ inline void word_hashes(const uint32_t *w, int len, uint32_t &h0,
-                                            uint32_t &h1) {
-  uint32_t a = 0x811C9DC5u ^ ((uint32_t)len * 0x01000193u);
-  uint32_t b = 0x2545F491u + (uint32_t)len;
+__host__ __device__ inline uint32_t word_hash(const uint32_t *w, int len, uint32_t seed) {
+  uint32_t h = 0x811C9DC5u ^ ((uint32_t)len * 0x01000193u) ^ seed;
   for (int i = 0; i < kWordWords; ++i) {
-    a = (a ^ w[i]) * 0x9E3779B1u;
-    a ^= a >> 16;
-    b = (b + w[i]) * 0x85EBCA77u;
-    b ^= b >> 13;
+    h = (h ^ w[i]) * 0x9E3779B1u;
+    h ^= h >> 16;
   }
-  h0 = a;
-  h1 = b;
+  return h;
 }
 
-__host__ __device__ inline uint32_t word_tag(uint32_t h0, int len) {
-  return (h0 & 0xFFFFFF00u) | (uint32_t)len;
+__host__ __device__ inline uint32_t word_tag(uint32_t h, int len) {
+  return (h & 0xFFFFFF00u) | (uint32_t)len;
 }
 
 // The two slots of a key; the second moves off the first when they coincide.
-__host__ __device__ inline uint32_t word_slot0(uint32_t h0, uint32_t mask) { return h0 & mask; }
-__host__ __device__ inline uint32_t word_slot1(uint32_t h0, uint32_t h1, uint32_t mask) {
-  const uint32_t s0 = h0 & mask, s1 = h1 & mask;
+__host__ __device__ inline uint32_t word_slot0(uint32_t h, uint32_t mask) { return h & mask; }
+__host__ __device__ inline uint32_t word_slot1(uint32_t h, uint32_t mask) {
+  uint32_t g = h * 0x2C1B3C6Du;
+  g ^= g >> 15;
+  const uint32_t s0 = h & mask, s1 = g & mask;
   return s1 == s0 ? s0 ^ 1u : s1;
 }
 
@@ -187,6 +184,7 @@ struct EncodeArgs {
   const int32_t *pair_rank;  // [65536]: rank of the byte pair (a, b) at a * 256 + b
   const uint4 *words;        // word table: 2 uint4 per slot; nullptr = none
   int word_bits;
+  uint32_t word_seed;
   int32_t *meta;
   int64_t *tot;
   int64_t *off;
