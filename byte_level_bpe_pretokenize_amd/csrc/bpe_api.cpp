@@ -20,8 +20,8 @@ using namespace bpe;
 struct bpe_model {
   int64_t R = 0, V = 0;
   int device = 0;
-  uint64_t *d_table = nullptr;
-  int table_bits = 0;
+  uint64_t *d_table = nullptr;     // rank table, 2 slots per bucket
+  uint32_t table_mask = 0, table_seed = 0;
   int32_t *d_id_map = nullptr;
   int32_t *d_pair_rank = nullptr;   // [65536] ranks of byte pairs
   uint4 *d_words = nullptr;         // word table (2 uint4 per slot), or nullptr
@@ -102,26 +102,66 @@ int upload(T **dst, const T *src, size_t count, hipStream_t stream) {
   return BPE_OK;
 }
 
-// Place every (key, rank) in one of its two slots; false if some key cannot
-// be placed within a bounded number of displacements (the caller retries
-// with twice the capacity).
-bool build_cuckoo(const std::vector<uint64_t> &keys, int bits, std::vector<uint64_t> &table) {
-  table.assign((size_t)1 << bits, kEmptySlot);
-  const int64_t max_kicks = 64 + 4 * (int64_t)bits;
+// Place every (key, rank) in its first or second bucket (two slots each):
+// lower ranks first, each into its first bucket when there is room, else its
+// second, else by displacing an occupant to that occupant's other bucket
+// (a bounded random walk).  Then set the flag of the first bucket of every
+// key that ended in its second.  False if some key found no place.
+bool build_rank_table(const std::vector<uint64_t> &keys, uint32_t mask, uint32_t seed,
+                      std::vector<uint64_t> &slots) {
+  const size_t nb = (size_t)mask + 1;
+  slots.assign(2 * nb, kEmptySlot);
+  auto place = [&](size_t b, uint64_t item) {
+    for (int k = 0; k < 2; ++k)
+      if (slots[2 * b + k] == kEmptySlot) {
+        slots[2 * b + k] = item;
+        return true;
+      }
+    return false;
+  };
+  auto buckets = [&](uint64_t item, uint32_t &b0, uint32_t &b1) {
+    const uint64_t key = item >> kSymBits;
+    const uint32_t x = pair_mix((uint32_t)(key >> kSymBits), (uint32_t)(key & ((1u << kSymBits) - 1)), seed);
+    b0 = pair_bucket0(x, mask);
+    b1 = pair_bucket1(x, mask);
+  };
+  uint64_t rng = 0x2545F4914F6CDD1Dull ^ seed;
+  const int max_kicks = 500;
   for (size_t r = 0; r < keys.size(); ++r) {
     uint64_t item = (keys[r] << kSymBits) | (uint64_t)r;
-    uint64_t h = pair_slot0(keys[r], bits);
-    for (int64_t kick = 0;; ++kick) {
-      const uint64_t key = item >> kSymBits;
-      const uint64_t a = pair_slot0(key, bits), b = pair_slot1(key, bits);
-      if (table[(size_t)a] == kEmptySlot) { table[(size_t)a] = item; break; }
-      if (table[(size_t)b] == kEmptySlot) { table[(size_t)b] = item; break; }
-      if (kick == max_kicks) return false;
-      // evict the occupant of the slot this item did not come from
-      h = (h == a) ? b : a;
-      std::swap(item, table[(size_t)h]);
+    uint32_t b0, b1;
+    buckets(item, b0, b1);
+    if (place(b0, item) || place(b1, item)) continue;
+    uint32_t at = b1;  // bucket the walk evicts from
+    bool ok = false;
+    for (int kick = 0; kick < max_kicks && !ok; ++kick) {
+      rng = rng * 6364136223846793005ull + 1442695040888963407ull;
+      const int k = (int)((rng >> 33) & 1u);
+      std::swap(item, slots[2 * (size_t)at + k]);
+      buckets(item, b0, b1);
+      const uint32_t other = (at == b0) ? b1 : b0;
+      if (place(other, item)) ok = true;
+      else at = other;
     }
+    if (!ok) return false;
   }
+  // keys in their second bucket move to the first where it has room
+  for (size_t b = 0; b < nb; ++b)
+    for (int k = 0; k < 2; ++k) {
+      const uint64_t item = slots[2 * b + k];
+      if (item == kEmptySlot) continue;
+      uint32_t b0, b1;
+      buckets(item, b0, b1);
+      if (b0 != b && place(b0, item)) slots[2 * b + k] = kEmptySlot;
+    }
+  for (size_t b = 0; b < nb; ++b)
+    for (int k = 0; k < 2; ++k) {
+      const uint64_t item = slots[2 * b + k];
+      if (item == kEmptySlot || item == (kEmptySlot | kSlotFlag)) continue;
+      uint32_t b0, b1;
+      buckets(item & ~kSlotFlag, b0, b1);
+      if (b0 != b) slots[2 * (size_t)b0] |= kSlotFlag;
+    }
   return true;
 }
 
@@ -191,7 +231,8 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.ids_cap = ids_capacity;
   a.id_off = d_id_off;
   a.table = model->d_table;
-  a.table_bits = model->table_bits;
+  a.table_mask = model->table_mask;
+  a.table_seed = model->table_seed;
   a.id_map = id_map;
   a.pair_rank = model->d_pair_rank;
   a.words = words;
@@ -420,13 +461,17 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
     }
   }
 
-  // rank table: two-choice cuckoo hashing, power-of-two capacity >= 2.5R
-  int bits = 8;
-  while (((int64_t)1 << bits) < 5 * R / 2) ++bits;
+  // rank table: buckets of two slots, a power-of-two count >= R (load <= 1/2);
+  // on failure another seed, then twice the buckets
+  uint32_t tmask = 1;
+  while ((int64_t)tmask + 1 < R) tmask = 2 * tmask + 1;
   std::vector<uint64_t> table;
-  for (;; ++bits) {
-    if (bits > 40) return BPE_ENOMEM;
-    if (build_cuckoo(keys, bits, table)) break;
+  uint32_t tseed = 0;
+  for (int attempt = 0;; ++attempt) {
+    if (tmask >= (1u << 30)) return BPE_ENOMEM;
+    tseed = 0x9E3779B9u * (uint32_t)(attempt + 1);
+    if (build_rank_table(keys, tmask, tseed, table)) break;
+    if (attempt % 2 == 1) tmask = 2 * tmask + 1;
   }
 
   bpe_model *m = new (std::nothrow) bpe_model;
@@ -434,7 +479,8 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
   m->R = R;
   m->V = V;
   window_radii(merges, R, len, order, m->win_d);
-  m->table_bits = bits;
+  m->table_mask = tmask;
+  m->table_seed = tseed;
   if (hipGetDevice(&m->device) != hipSuccess) {
     delete m;
     return BPE_EHIP;

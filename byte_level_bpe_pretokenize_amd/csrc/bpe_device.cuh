@@ -17,18 +17,34 @@ constexpr int kNoStart = INT_MAX;
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-// Rank held by a loaded slot pair for key, or kRankInf.
-__device__ __forceinline__ int32_t rank_in(uint64_t s0, uint64_t s1, uint64_t key) {
-  if ((s0 >> kSymBits) == key) return (int32_t)(s0 & ((1u << kSymBits) - 1));
-  if ((s1 >> kSymBits) == key) return (int32_t)(s1 & ((1u << kSymBits) - 1));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+// The rank table as seen by the kernels.
+struct RankTable {
+  const u64x2 *b;  // buckets
+  uint32_t mask;   // buckets - 1
+  uint32_t seed;
+};
+
+// Rank held by a loaded bucket for key, or kRankInf.
+__device__ __forceinline__ int32_t bucket_rank(u64x2 b, uint64_t key) {
+  if ((b.x >> kSymBits) == key) return (int32_t)((uint32_t)b.x & kRankMask);
+  if ((b.y >> kSymBits) == key) return (int32_t)((uint32_t)b.y & kRankMask);
   return kRankInf;
 }
 
-// Rank of the pair (l, r), or kRankInf: both choices loaded at once.
-__device__ __forceinline__ int32_t rank_of(const uint64_t *__restrict__ tab, int bits, uint32_t l,
-                                           uint32_t r) {
+// Whether a lookup that missed in this first bucket must load the second.
+__device__ __forceinline__ bool bucket_flag(u64x2 b) { return ((uint32_t)b.x & kSlotFlag) != 0; }
+
+// Rank of the pair (l, r), or kRankInf: the first bucket, then the second
+// only if the first bucket's flag asks for it.
+__device__ __forceinline__ int32_t rank_of(const RankTable &t, uint32_t l, uint32_t r) {
+  const uint32_t x = pair_mix(l, r, t.seed);
   const uint64_t key = pair_key(l, r);
-  return rank_in(tab[pair_slot0(key, bits)], tab[pair_slot1(key, bits)], key);
+  const u64x2 b0 = t.b[pair_bucket0(x, t.mask)];
+  int32_t rk = bucket_rank(b0, key);
+  if (rk == kRankInf && bucket_flag(b0)) rk = bucket_rank(t.b[pair_bucket1(x, t.mask)], key);
+  return rk;
 }
 
 // ---- wave / workgroup reductions and scans --------------------------------

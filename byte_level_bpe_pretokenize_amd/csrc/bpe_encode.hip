@@ -78,82 +78,130 @@ struct Red {
 
 // ---- merge loops ----------------------------------------------------------
 
-// Merge one pre-token of len <= W bytes in registers and write its symbols
-// to out; returns their count.  Each round takes the lowest rank r among the
-// adjacent pairs and rewrites left to right: a pair of rank r merges into
-// symbol 256 + r unless its left symbol was just consumed.  Positions never
-// move: a consumed position is marked dead and each pair joins a live
-// position to the next live one, so all indexing is static.  The rank
-// probes of a round are issued together, 8 positions at a time.
+// Pair keys of the lane merge: rank << 5 | position, so that the smallest
+// key is the leftmost pair of the lowest rank.  A pair made during a round
+// with a rank below the round's (possible only when ranks are not in
+// creation order) carries kKeyDef until the round ends; keys at or above
+// kKeyDone stand for no pair.
+constexpr uint32_t kKeyDef = 1u << 25;
+constexpr uint32_t kKeyDone = 1u << 26;
+constexpr uint32_t kKeyNone = 0xFFFFFFFFu;
+
+// One wave's per-lane arrays in LDS, lane-major: element j of lane l at
+// [j][l], so that lanes hit distinct banks whatever their indexes.
 template <int W>
-__device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const uint64_t *tab,
-                         const int bits, const int32_t *__restrict__ pair_rank) {
-  int32_t sym[W], rk[W];
+struct LaneCols {
+  uint32_t s[W][64];      // symbol at each position (bytes at the start)
+  uint32_t k[W - 1][64];  // key of the pair (position, next live position)
+};
+
+// Merge one pre-token of len <= W bytes (little-endian words w) by one lane
+// and write its symbols to out; returns their count.  A round takes the
+// lowest rank r and merges its pairs left to right without overlap; here the
+// round's merges are made one at a time, always the leftmost pair of rank r:
+// merging (x, y) into 256 + r leaves no pair of rank r that overlaps it (a
+// merge never takes its own symbol as an operand), so the pairs of rank r
+// still present are exactly the rest of the round's.  Positions never move:
+// a consumed position leaves the live mask, and each pair joins a live
+// position to the next live one.
+template <int W>
+__device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, const RankTable &t,
+                          const int32_t *__restrict__ pair_rank, int32_t *out) {
+  const int lane = lane_id();
+  uint32_t *S = &L.s[0][lane];
+  uint32_t *K = &L.k[0][lane];
+  uint32_t b[W];
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    b[j] = (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    S[64 * j] = b[j];
+  }
+  // the symbols are still bytes: their pair ranks come from the direct table
+  int32_t r0[W - 1];
+#pragma unroll
+  for (int j = 0; j + 1 < W; ++j)
+    r0[j] = (j + 1 < len) ? pair_rank[(b[j] << 8) | b[j + 1]] : kRankInf;
+#pragma unroll
+  for (int j = 0; j + 1 < W; ++j)
+    K[64 * j] = r0[j] == kRankInf ? kKeyNone : (((uint32_t)r0[j] << 5) | (uint32_t)j);
   uint32_t alive = len >= 32 ? ~0u : ((1u << len) - 1u);
-#pragma unroll
-  for (int i = 0; i < W; ++i) sym[i] = i < len ? (int32_t)b[i] : 0;
-  // the symbols are still bytes: their ranks come from the direct table
-#pragma unroll
-  for (int i = 0; i < W; ++i)
-    rk[i] = (i + 1 < len) ? pair_rank[(sym[i] << 8) | sym[i + 1]] : kRankInf;
+  uint32_t rcur = kKeyNone;  // rank of the round in progress
+  bool def = false;          // some key carries kKeyDef
   for (;;) {
-    int32_t r = kRankInf;
+    uint32_t m = kKeyNone;
 #pragma unroll
-    for (int i = 0; i < W; ++i) r = min(r, rk[i]);  // dead and last positions hold kRankInf
-    if (r == kRankInf) break;
-    const int32_t z = 256 + r;
-    bool carry = false;  // the previous live position merged: this one is consumed
+    for (int j = 0; j + 1 < W; ++j) m = min(m, K[64 * j]);
+    if (m >= kKeyDone) break;
+    const uint32_t r = m >> 5;
+    if (def && r != rcur) {
+      // the round is over: pairs it made join the next one
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
-      const bool live = (alive >> i) & 1u;
-      const bool consumed = live && carry;
-      const bool merge = live && !carry && rk[i] == r;
-      if (consumed) {
-        alive &= ~(1u << i);
-        rk[i] = kRankInf;
-      }
-      if (merge) sym[i] = z;
-      carry = live ? merge : carry;
+      for (int j = 0; j + 1 < W; ++j) K[64 * j] &= ~kKeyDef;
+      def = false;
+      continue;
     }
-    // the pairs that touch z get new ranks: the next live symbol of each
-    // position, from the top, in probe groups of PG positions
-    constexpr int PG = W < 8 ? W : 8;
-    int32_t ns = -1;  // next live symbol above the current group
-#pragma unroll
-    for (int g = W / PG - 1; g >= 0; --g) {
-      int32_t nx[PG];
-      uint32_t need = 0;
-#pragma unroll
-      for (int j = PG - 1; j >= 0; --j) {
-        const int i = PG * g + j;
-        nx[j] = ns;
-        const bool live = (alive >> i) & 1u;
-        if (live && ns >= 0 && (sym[i] == z || ns == z)) need |= 1u << j;
-        if (live && ns < 0) rk[i] = kRankInf;
-        if (live) ns = sym[i];
-      }
-      if (need) {
-        uint64_t s0[PG], s1[PG];
-#pragma unroll
-        for (int j = 0; j < PG; ++j) {
-          s0[j] = s1[j] = kEmptySlot;
-          if ((need >> j) & 1u) {
-            const uint64_t key = pair_key(sym[PG * g + j], nx[j]);
-            s0[j] = tab[pair_slot0(key, bits)];
-            s1[j] = tab[pair_slot1(key, bits)];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < PG; ++j)
-          if ((need >> j) & 1u) rk[PG * g + j] = rank_in(s0[j], s1[j], pair_key(sym[PG * g + j], nx[j]));
-      }
+    rcur = r;
+    const int i = (int)(m & 31u);
+    const uint32_t above = alive & (0xFFFFFFFEu << i);  // the pair's right symbol first
+    const int q = __builtin_ctz(above);
+    const uint32_t rest = above & (above - 1u);
+    const uint32_t below = alive & ((1u << i) - 1u);
+    alive ^= 1u << q;
+    const uint32_t z = 256u + r;
+    const bool hp = below != 0, ht = rest != 0;
+    const int p = hp ? 31 - __builtin_clz(below) : i;
+    const int tt = ht ? __builtin_ctz(rest) : i;
+    const uint32_t sp = S[64 * p], st = S[64 * tt];
+    S[64 * i] = z;
+    if (q < W - 1) K[64 * q] = kKeyNone;  // the last position starts no pair
+    // ranks of the new pairs (S[p], z) and (z, S[t]): both first buckets at once
+    const uint32_t xl = pair_mix(sp, z, t.seed), xr = pair_mix(z, st, t.seed);
+    const uint64_t kl = pair_key(sp, z), kr = pair_key(z, st);
+    u64x2 bl = {kEmptySlot, kEmptySlot}, br = {kEmptySlot, kEmptySlot};
+    if (hp) bl = t.b[pair_bucket0(xl, t.mask)];
+    if (ht) br = t.b[pair_bucket0(xr, t.mask)];
+    int32_t rl = bucket_rank(bl, kl), rr = bucket_rank(br, kr);
+    const bool nl = hp && rl == kRankInf && bucket_flag(bl);
+    const bool nr = ht && rr == kRankInf && bucket_flag(br);
+    if (nl || nr) {
+      if (nl) bl = t.b[pair_bucket1(xl, t.mask)];
+      if (nr) br = t.b[pair_bucket1(xr, t.mask)];
+      if (nl) rl = bucket_rank(bl, kl);
+      if (nr) rr = bucket_rank(br, kr);
     }
+    uint32_t vl = rl == kRankInf ? kKeyNone : (((uint32_t)rl << 5) | (uint32_t)p);
+    uint32_t vr = rr == kRankInf ? kKeyNone : (((uint32_t)rr << 5) | (uint32_t)i);
+    if ((uint32_t)rl < r) {
+      vl |= kKeyDef;
+      def = true;
+    }
+    if ((uint32_t)rr < r) {
+      vr |= kKeyDef;
+      def = true;
+    }
+    if (hp) K[64 * p] = vl;
+    K[64 * i] = vr;  // i < q <= W - 1
   }
   int n = 0;
 #pragma unroll
-  for (int i = 0; i < W; ++i)
-    if ((alive >> i) & 1u) out[n++] = sym[i];
+  for (int j = 0; j < W; ++j)
+    if ((alive >> j) & 1u) out[n++] = (int32_t)S[64 * j];
   return n;
+}
+
+// The len <= 4 * NW bytes at p as NW little-endian words (bytes past len are
+// whatever follows in memory): aligned 4-byte loads and byte shifts.  Reads
+// up to 3 bytes before p and 4 after the last word.
+template <int NW>
+__device__ __forceinline__ void load_words(const uint8_t *p, uint32_t *w) {
+  const uintptr_t ad = (uintptr_t)p;
+  const uint32_t *q = reinterpret_cast<const uint32_t *>(ad & ~(uintptr_t)3);
+  const uint32_t sh = (uint32_t)(ad & 3);
+  uint32_t raw[NW + 1];
+#pragma unroll
+  for (int i = 0; i <= NW; ++i) raw[i] = q[i];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) w[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
 }
 
 // The same rounds with the whole workgroup (NT threads) on Y[0..n), RK
@@ -162,7 +210,7 @@ __device__ int reg_merge(const uint8_t *b, const int len, int32_t *out, const ui
 // (x, x)) merge at even offsets from the run start; survivors are compacted
 // in place tile by tile.  Returns the final symbol count.
 template <int NT>
-__device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const uint64_t *tab, int bits,
+__device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const RankTable &tab,
                             const int32_t *__restrict__ pair_rank, Red<NT> &s) {
   constexpr int PER = 4;
   constexpr int TILE = NT * PER;
@@ -233,7 +281,7 @@ __device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const uint64_t *
     for (int64_t i = tid; i < n; i += NT) {
       if (i + 1 < n) {
         const int32_t l = Y[i], rr = Y[i + 1];
-        if (l == z || rr == z) RK[i] = rank_of(tab, bits, l, rr);
+        if (l == z || rr == z) RK[i] = rank_of(tab, l, rr);
       } else {
         RK[i] = kRankInf;
       }
@@ -597,7 +645,8 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
 
 // ---- k_merge, k_merge_wide ---------------------------------------------------
 
-constexpr int kGroup = 4;  // chunks per merge wave: batches of one bucket span them
+constexpr int kGroup = 4;       // chunks per merge wave: batches of one bucket span them
+constexpr int kMergeWaves = 4;  // waves per merge workgroup, each on its own group
 
 struct MergeShared {
   int32_t meta[kGroup][kMetaInts];
@@ -615,34 +664,121 @@ __device__ __forceinline__ void group_entry(const MergeShared &s, int b, int g, 
   for (int bb = 0; bb < b; ++bb) idx += s.meta[f][kMetaBucket + bb];
 }
 
-// Bucket b (one pre-token per lane, W-wide registers) of the group's lists,
-// 64 entries per batch; adds the token counts into s.tok.
-template <int W>
-__device__ void merge_bucket(const EncodeArgs &a, MergeShared &s, int64_t cg, int nf, int b) {
-  const int lane = lane_id();
-  int total = 0;
-  for (int f = 0; f < nf; ++f) total += s.meta[f][kMetaBucket + b];
-  for (int s0 = 0; s0 < total; s0 += MWG) {
-    const int g = s0 + lane;
-    if (g < total) {
-      int f, idx;
-      group_entry(s, b, g, f, idx);
-      const int64_t c = cg + f;
-      const uint32_t e = a.miss[c * kMissMax + idx];
-      const int o = me_start(e);
-      const int nt = reg_merge<W>(a.mbytes + c * kMissBytes + o, me_len(e),
-                                  a.res + c * kMissBytes + o, a.table, a.table_bits, a.pair_rank);
-      a.mt[(cg + f) * kMissMax + idx] = nt;
-      atomicAdd(&s.tok[f], nt);
-    }
-  }
-}
-
 __device__ void load_group(const EncodeArgs &a, MergeShared &s, int64_t cg, int nf) {
   const int lane = lane_id();
   if (lane < kMetaInts * nf) (&s.meta[0][0])[lane] = a.meta[kMetaInts * cg + lane];
   if (lane < kGroup) s.tok[lane] = 0;
   __syncthreads();
+}
+
+// The group of one wave of a lane-merge workgroup: its chunk meta read with
+// scalar loads.
+struct LaneGroup {
+  int64_t cg;  // first chunk
+  int nf;      // chunks in the group
+  int cnt[kGroup][kBuckets];
+};
+
+__device__ __forceinline__ bool lane_group(const EncodeArgs &a, LaneGroup &G) {
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+  G.cg = ((int64_t)blockIdx.x * kMergeWaves + wv) * kGroup;
+  if (G.cg >= a.n_chunks) return false;
+  G.nf = (int)min<int64_t>(kGroup, a.n_chunks - G.cg);
+#pragma unroll
+  for (int f = 0; f < kGroup; ++f)
+#pragma unroll
+    for (int b = 0; b < kBuckets; ++b)
+      G.cnt[f][b] = f < G.nf ? a.meta[kMetaInts * (G.cg + f) + kMetaBucket + b] : 0;
+  return true;
+}
+
+// Bucket b of the group's lists, one pre-token per lane with W-wide LDS
+// columns, 64 entries per batch.  An entry's bytes are read from its chunk's
+// dense mbytes region and its tokens written to res at the same offset: never
+// more tokens than bytes, so entries do not overlap.  mt gets each entry's
+// token count; the return value holds the tokens per chunk, 16 bits each.
+template <int W>
+__device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b, LaneCols<W> &L) {
+  const int lane = lane_id();
+  const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
+  // per chunk: entries of the bucket before the chunk's, and the bucket's
+  // first list index in the chunk (uniform across the wave)
+  int pre[kGroup], first[kGroup];
+  int total = 0;
+#pragma unroll
+  for (int f = 0; f < kGroup; ++f) {
+    pre[f] = total;
+    total += G.cnt[f][b];
+    first[f] = 0;
+#pragma unroll
+    for (int bb = 0; bb < kBuckets; ++bb)
+      if (bb < b) first[f] += G.cnt[f][bb];
+  }
+  uint64_t tok = 0;
+  for (int s0 = 0; s0 < total; s0 += 64) {
+    const int g = s0 + lane;
+    if (g >= total) break;
+    int f = 0, idx = g + first[0];
+#pragma unroll
+    for (int k = 1; k < kGroup; ++k)
+      if (g >= pre[k]) {
+        f = k;
+        idx = g - pre[k] + first[k];
+      }
+    const int64_t c = G.cg + f;
+    const uint32_t e = a.miss[c * kMissMax + idx];
+    const int o = me_start(e);
+    uint32_t w[W / 4];
+    load_words<W / 4>(a.mbytes + c * kMissBytes + o, w);
+    const int nt = lane_merge<W>(w, me_len(e), L, t, a.pair_rank, a.res + c * kMissBytes + o);
+    a.mt[c * kMissMax + idx] = nt;
+    tok += (uint64_t)nt << (16 * f);
+  }
+  return tok;
+}
+
+// Per-chunk token sums of the wave (16 bits each in tok).
+__device__ __forceinline__ uint64_t wave_tok_sum(uint64_t tok) {
+  return wave_sum(tok);
+}
+
+// Merge-loop lists of kGroup consecutive chunks per wave, buckets 0 (2-8
+// bytes) and 1 (9-16 bytes).  The entries of one bucket are taken 64 at a
+// time across the chunks, so every lane of a batch runs the same merge width.
+// tot[c] gets the chunk's count so far (its resolved pre-tokens and these
+// buckets) with its status bits on top.
+__global__ void __launch_bounds__(MWG *kMergeWaves) k_merge(EncodeArgs a) {
+  __shared__ LaneCols<16> cols[kMergeWaves];
+  LaneGroup G;
+  if (!lane_group(a, G)) return;
+  LaneCols<16> &L = cols[wave_id()];
+  uint64_t tok = merge_bucket<8>(a, G, 0, *reinterpret_cast<LaneCols<8> *>(&L));
+  tok += merge_bucket<16>(a, G, 1, L);
+  tok = wave_tok_sum(tok);
+  const int lane = lane_id();
+  if (lane < G.nf) {
+    const int64_t c = G.cg + lane;
+    const int32_t *m = a.meta + kMetaInts * c;
+    const int64_t t = (int64_t)(m[kMetaPretokens] - m[kMetaMisses]) + (int64_t)((tok >> (16 * lane)) & 0xFFFFu);
+    a.tot[c] = t | ((int64_t)m[kMetaStatus] << kCountBits);
+  }
+}
+
+// Bucket 2 (17-32 bytes) of the same groups; adds its token counts to tot.
+__global__ void __launch_bounds__(MWG *kMergeWaves) k_merge_wide(EncodeArgs a) {
+  __shared__ LaneCols<32> cols[kMergeWaves];
+  LaneGroup G;
+  if (!lane_group(a, G)) return;
+  int any = 0;
+#pragma unroll
+  for (int f = 0; f < kGroup; ++f) any += G.cnt[f][2];
+  if (any == 0) return;
+  uint64_t tok = wave_tok_sum(merge_bucket<32>(a, G, 2, cols[wave_id()]));
+  const int lane = lane_id();
+  if (lane < G.nf) {
+    const int32_t add = (int32_t)((tok >> (16 * lane)) & 0xFFFFu);
+    if (add) a.tot[G.cg + lane] += add;
+  }
 }
 
 // End (exclusive, global) of the pre-token that starts at gs and has no start
@@ -673,45 +809,6 @@ __device__ int64_t wave_global_end(const EncodeArgs &a, int64_t gs, int64_t from
   return limit;
 }
 
-// Merge-loop lists of kGroup consecutive chunks, buckets 0 and 1 (one wave).
-// The entries of one bucket are taken 64 at a time across the chunks, so
-// every lane of a batch runs the same merge width.  An entry's bytes are read
-// from the chunk's dense mbytes region and its tokens written to res at the
-// same offset: never more tokens than bytes, so entries do not overlap.  mt
-// gets each entry's token count; tot[c] the chunk's count so far (its
-// resolved pre-tokens and these buckets) with its status bits on top.
-__global__ void __launch_bounds__(MWG) k_merge(EncodeArgs a) {
-  __shared__ MergeShared s;
-  const int64_t cg = (int64_t)blockIdx.x * kGroup;
-  const int nf = (int)min<int64_t>(kGroup, a.n_chunks - cg);
-  load_group(a, s, cg, nf);
-  merge_bucket<8>(a, s, cg, nf, 0);
-  merge_bucket<16>(a, s, cg, nf, 1);
-  __syncthreads();
-  const int lane = threadIdx.x;
-  if (lane < nf) {
-    const int32_t *m = s.meta[lane];
-    const int64_t tot = (int64_t)(m[kMetaPretokens] - m[kMetaMisses]) + s.tok[lane];
-    a.tot[cg + lane] = tot | ((int64_t)m[kMetaStatus] << kCountBits);
-  }
-}
-
-// Bucket 2 (one pre-token per lane, 32-wide registers, as above) of the same
-// groups; adds its token counts to tot.
-__global__ void __launch_bounds__(MWG) k_merge_wide(EncodeArgs a) {
-  __shared__ MergeShared s;
-  const int64_t cg = (int64_t)blockIdx.x * kGroup;
-  const int nf = (int)min<int64_t>(kGroup, a.n_chunks - cg);
-  load_group(a, s, cg, nf);
-  int any = 0;
-  for (int f = 0; f < nf; ++f) any += s.meta[f][kMetaBucket + 2];
-  if (any == 0) return;
-  merge_bucket<32>(a, s, cg, nf, 2);
-  __syncthreads();
-  const int lane = threadIdx.x;
-  if (lane < nf && s.tok[lane] != 0) a.tot[cg + lane] += s.tok[lane];
-}
-
 // ---- k_merge_long -------------------------------------------------------------
 
 constexpr int kLdsLong = 2048;    // longest bucket-3 pre-token merged in LDS
@@ -736,7 +833,7 @@ struct LongShared {
 // Position i belongs to lane i % 64; scans run 64 positions at a time with
 // a carry.  One wave does all the work, so LDS accesses stay in program
 // order and the arrays are rewritten in place.
-__device__ int lds_merge(LongShared &L, int n, int D, const uint64_t *__restrict__ tab, int bits,
+__device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
                          const int32_t *__restrict__ pair_rank) {
   const int lane = lane_id();
   const uint64_t below = (1ull << lane) - 1;
@@ -812,29 +909,48 @@ __device__ int lds_merge(LongShared &L, int n, int D, const uint64_t *__restrict
     //    groups of 64 positions issued together
     for (int i0 = 0; i0 < n; i0 += MWG * kProbeGroups) {
       int32_t nv[kProbeGroups];
-      uint64_t key[kProbeGroups], s0[kProbeGroups], s1[kProbeGroups];
+      uint32_t xs[kProbeGroups];
+      uint64_t key[kProbeGroups];
+      u64x2 bk[kProbeGroups];
       uint32_t need = 0;
 #pragma unroll
       for (int g = 0; g < kProbeGroups; ++g) {
         const int i = i0 + MWG * g + lane;
         nv[g] = kRankInf;
         key[g] = 0;
-        s0[g] = s1[g] = kEmptySlot;
+        xs[g] = 0;
+        bk[g] = u64x2{kEmptySlot, kEmptySlot};
         if (i + 1 < n) {
           const int32_t r = L.r[i];
           nv[g] = r;
           if (r == -1 || L.r[i + 1] == -1) {
             need |= 1u << g;
-            key[g] = pair_key(L.y[i], L.y[i + 1]);
-            s0[g] = tab[pair_slot0(key[g], bits)];
-            s1[g] = tab[pair_slot1(key[g], bits)];
+            const uint32_t l = (uint32_t)L.y[i], rt = (uint32_t)L.y[i + 1];
+            key[g] = pair_key(l, rt);
+            xs[g] = pair_mix(l, rt, tab.seed);
+            bk[g] = tab.b[pair_bucket0(xs[g], tab.mask)];
           }
         }
+      }
+      uint32_t need2 = 0;
+#pragma unroll
+      for (int g = 0; g < kProbeGroups; ++g) {
+        if ((need >> g) & 1u) {
+          nv[g] = bucket_rank(bk[g], key[g]);
+          if (nv[g] == kRankInf && bucket_flag(bk[g])) need2 |= 1u << g;
+        }
+      }
+      if (need2) {
+#pragma unroll
+        for (int g = 0; g < kProbeGroups; ++g)
+          if ((need2 >> g) & 1u) bk[g] = tab.b[pair_bucket1(xs[g], tab.mask)];
+#pragma unroll
+        for (int g = 0; g < kProbeGroups; ++g)
+          if ((need2 >> g) & 1u) nv[g] = bucket_rank(bk[g], key[g]);
       }
 #pragma unroll
       for (int g = 0; g < kProbeGroups; ++g) {
         const int i = i0 + MWG * g + lane;
-        if ((need >> g) & 1u) nv[g] = rank_in(s0[g], s1[g], key[g]);
         if (i < n) L.r[i] = nv[g];
       }
     }
@@ -861,6 +977,7 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
   for (int f = 0; f < nf; ++f) any += s.g.meta[f][kMetaBucket + 3];
   if (any == 0) return;
   const int lane = threadIdx.x;
+  const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
   for (int f = 0; f < nf; ++f) {
     const int n3 = s.g.meta[f][kMetaBucket + 3];
     const int base = s.g.meta[f][kMetaMisses] - n3;
@@ -878,14 +995,12 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
         // the pre-token's class: its first byte, or the letter after a leading space
         uint32_t b = (uint32_t)s.L.y[0];
         if (b == 0x20u && len > 1) b = (uint32_t)s.L.y[1];
-        nt = lds_merge(s.L, (int)len, a.win_d[byte_class(b)], a.table, a.table_bits,
-                       a.pair_rank);
+        nt = lds_merge(s.L, (int)len, a.win_d[byte_class(b)], t, a.pair_rank);
         for (int i = lane; i < nt; i += MWG) a.gsym[gs + i] = s.L.y[i];
       } else {
         for (int64_t p = gs + lane; p < ge; p += MWG) a.gsym[p] = a.bytes[p];
         __syncthreads();
-        nt = wg_merge<MWG>(a.gsym + gs, a.grank + gs, len, a.table, a.table_bits, a.pair_rank,
-                           s.g.r);
+        nt = wg_merge<MWG>(a.gsym + gs, a.grank + gs, len, t, a.pair_rank, s.g.r);
       }
       if (lane == 0) {
         a.mt[c * kMissMax + base + q] = (int32_t)nt;
@@ -1042,9 +1157,10 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
   if (ev) (void)hipEventRecord(ev[0], stream);
   hipLaunchKernelGGL(k_find, dim3(G), dim3(WG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[1], stream);
-  hipLaunchKernelGGL(k_merge, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
+  const unsigned LG = (G + kGroup * kMergeWaves - 1) / (kGroup * kMergeWaves);
+  hipLaunchKernelGGL(k_merge, dim3(LG), dim3(MWG * kMergeWaves), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[2], stream);
-  hipLaunchKernelGGL(k_merge_wide, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
+  hipLaunchKernelGGL(k_merge_wide, dim3(LG), dim3(MWG * kMergeWaves), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[3], stream);
   hipLaunchKernelGGL(k_merge_long, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[4], stream);

@@ -22,31 +22,47 @@ __host__ __device__ inline uint32_t byte_class(uint32_t b) {
 }
 
 // ---- rank table --------------------------------------------------------
-// Two-choice cuckoo hash table in device memory, one 64-bit slot per entry:
-//   bits 42..62  left symbol, bits 21..41 right symbol, bits 0..20 rank.
-// A key is (left << 21) | right, so (slot >> 21) is the key; the empty slot
-// is all ones, whose upper bits can equal no key.  Every key sits in one of
-// its two slots pair_slot(key, 0 or 1), so a lookup is two independent loads
-// and never a chain.  Capacity is a power of two >= 2.5 * merges (load
-// <= 0.4).  ("Tokenization LLM: ... C++", section "Vocabulary lookup": a
-// pair-keyed map from the pair of units to its rank.)
+// Pair-keyed map from a pair of units to its rank ("Tokenization LLM: ...
+// C++" (glitch4techs.com), section "Vocabulary lookup"), as a hash table in
+// device memory of 16-byte buckets, each two 64-bit slots, so that a bucket
+// is one load.  A slot holds key << 21 | rank with key = (left << 21) | right;
+// ranks stay below 2^20 (BPE_MAX_MERGES), so bit 20 is free, and bit 20 of a
+// bucket's first slot is the bucket's flag: a key whose first bucket this is
+// sits in its second bucket.  An empty slot has every bit set but bit 20, so
+// its upper bits equal no key.  Every key sits in its first or its second
+// bucket: a lookup loads the first bucket, and the second only when the key
+// is not in the first and the flag is set.
 constexpr int kSymBits = 21;
-constexpr uint64_t kEmptySlot = ~0ull;
+constexpr uint64_t kSlotFlag = 1ull << 20;
+constexpr uint64_t kEmptySlot = ~0ull ^ kSlotFlag;
+constexpr uint32_t kRankMask = (1u << 20) - 1;
 constexpr int32_t kRankInf = 0x7fffffff;  // "no merge here" compares largest
 
 __host__ __device__ inline uint64_t pair_key(uint32_t l, uint32_t r) {
   return ((uint64_t)l << kSymBits) | (uint64_t)r;
 }
 
-// Slot of choice 0 or 1 for a key (two multiplicative hashes; the second is
-// moved off the first when they coincide).
-__host__ __device__ inline uint64_t pair_slot0(uint64_t key, int bits) {
-  return (key * 0x9E3779B97F4A7C15ull) >> (64 - bits);
+// Products of two values below 2^24 (one full-rate multiply on the device).
+__host__ __device__ inline uint32_t mul24(uint32_t a, uint32_t b) {
+  return (a & 0xFFFFFFu) * (b & 0xFFFFFFu);
 }
-__host__ __device__ inline uint64_t pair_slot1(uint64_t key, int bits) {
-  const uint64_t h0 = pair_slot0(key, bits);
-  const uint64_t h1 = (key * 0xC2B2AE3D27D4EB4Full) >> (64 - bits);
-  return h1 == h0 ? h0 ^ 1u : h1;
+
+// 32-bit mix of a pair of symbols (both below 2^21) and the table's seed.
+__host__ __device__ inline uint32_t pair_mix(uint32_t l, uint32_t r, uint32_t seed) {
+  uint32_t x = mul24(l, 0x9E3779u) ^ r ^ seed;
+  x ^= x >> 16;
+  x = mul24(x, 0x85EBCBu);
+  x ^= x >> 13;
+  return x;
+}
+
+// First and second bucket of a mix, for a table of mask + 1 buckets (a power
+// of two, at least 2); the second differs from the first.
+__host__ __device__ inline uint32_t pair_bucket0(uint32_t x, uint32_t mask) { return x & mask; }
+__host__ __device__ inline uint32_t pair_bucket1(uint32_t x, uint32_t mask) {
+  const uint32_t y = mul24(x >> 8, 0xC2B2AFu) ^ (x >> 21);
+  const uint32_t b0 = x & mask, b1 = y & mask;
+  return b1 == b0 ? b0 ^ 1u : b1;
 }
 
 // ---- word table -----------------------------------------------------------
@@ -178,8 +194,9 @@ struct EncodeArgs {
   int32_t *ids;
   int64_t ids_cap;
   int64_t *id_off;
-  const uint64_t *table;
-  int table_bits;
+  const uint64_t *table;     // rank table: 2 slots per bucket
+  uint32_t table_mask;       // buckets - 1
+  uint32_t table_seed;
   const int32_t *id_map;     // nullptr = identity
   const int32_t *pair_rank;  // [65536]: rank of the byte pair (a, b) at a * 256 + b
   const uint4 *words;        // word table: 2 uint4 per slot; nullptr = none
