@@ -24,8 +24,10 @@ struct bpe_model {
   uint32_t table_mask = 0, table_seed = 0;
   int32_t *d_id_map = nullptr;
   int32_t *d_pair_rank = nullptr;   // [65536] ranks of byte pairs
-  uint4 *d_words = nullptr;         // word table (2 uint4 per slot), or nullptr
-  int word_bits = 0;
+  uint4 *d_words = nullptr;         // short word table (one uint4 per slot), or nullptr
+  uint32_t word_mask = 0;
+  uint4 *d_lwords = nullptr;        // long word table (two uint4 per slot), or nullptr
+  uint32_t lword_mask = 0, lword_seed = 0;
   uint32_t word_seed = 0;
   int64_t n_words = 0;
   // decode tables
@@ -83,6 +85,7 @@ void free_model(bpe_model *m) {
   if (m->d_id_map) (void)hipFree(m->d_id_map);
   if (m->d_pair_rank) (void)hipFree(m->d_pair_rank);
   if (m->d_words) (void)hipFree(m->d_words);
+  if (m->d_lwords) (void)hipFree(m->d_lwords);
   if (m->d_exp_off) (void)hipFree(m->d_exp_off);
   if (m->d_exp_bytes) (void)hipFree(m->d_exp_bytes);
   if (m->d_inv_map) (void)hipFree(m->d_inv_map);
@@ -209,11 +212,11 @@ bool on_model_device(const bpe_model *m) {
   return hipGetDevice(&dev) == hipSuccess && dev == m->device;
 }
 
-// Queue the encode kernels.  `words` selects the word table (nullptr: every
+// Queue the encode kernels.  `words`: use the model's word tables (else every
 // pre-token runs the merge loop); `id_map` the output mapping.
 int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
                    const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids, int64_t ids_capacity,
-                   int64_t *d_id_off, void *d_workspace, int32_t *d_status, const uint4 *words,
+                   int64_t *d_id_off, void *d_workspace, int32_t *d_status, bool words,
                    const int32_t *id_map, hipStream_t stream) {
   if (n_bytes == 0)
     return launch_empty(d_doc_off, n_docs, BPE_STATUS_BAD_DOC_OFFSETS, d_id_off, d_status,
@@ -235,9 +238,12 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.table_seed = model->table_seed;
   a.id_map = id_map;
   a.pair_rank = model->d_pair_rank;
-  a.words = words;
-  a.word_bits = model->word_bits;
+  a.words = words ? model->d_words : nullptr;
+  a.word_mask = model->word_mask;
   a.word_seed = model->word_seed;
+  a.lwords = words ? model->d_lwords : nullptr;
+  a.lword_mask = model->lword_mask;
+  a.lword_seed = model->lword_seed;
   a.meta = (int32_t *)(ws + L.meta);
   a.tot = (int64_t *)(ws + L.tot);
   a.off = (int64_t *)(ws + L.off);
@@ -247,6 +253,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.miss = (uint32_t *)(ws + L.miss);
   a.mt = (int32_t *)(ws + L.mt);
   a.mbytes = ws + L.mbytes;
+  a.mto = ws + L.mto;
   a.res = (int32_t *)(ws + L.res);
   a.gsym = (int32_t *)(ws + L.gsym);
   a.grank = (int32_t *)(ws + L.grank);
@@ -255,6 +262,46 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   for (int k = 0; k < 4; ++k) a.win_d[k] = model->win_d[k];
   if (launch_encode(a, stream, call_events(model, BPE_OP_ENCODE)) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
+}
+
+// Two-choice cuckoo placement with one slot per bucket for entries with
+// hashes h, in order: each into its first slot when free, else its second,
+// else displacing the occupant of its second slot to that occupant's other
+// slot, and so on (bounded); then entries move back to a free first slot.
+// at[slot] = entry or -1.  False if some entry found no slot.
+bool place_words(const std::vector<uint32_t> &h, uint32_t mask, std::vector<int32_t> &at) {
+  at.assign((size_t)mask + 1, -1);
+  const int max_kicks = 500;
+  for (int32_t e = 0; e < (int32_t)h.size(); ++e) {
+    int32_t item = e;
+    const uint32_t s0 = word_slot0(h[(size_t)item], mask), s1 = word_slot1(h[(size_t)item], mask);
+    if (at[s0] < 0) { at[s0] = item; continue; }
+    if (at[s1] < 0) { at[s1] = item; continue; }
+    uint32_t cur = s1;
+    bool ok = false;
+    for (int kick = 0; kick < max_kicks && !ok; ++kick) {
+      std::swap(item, at[cur]);
+      const uint32_t a0 = word_slot0(h[(size_t)item], mask), a1 = word_slot1(h[(size_t)item], mask);
+      const uint32_t other = cur == a0 ? a1 : a0;
+      if (at[other] < 0) {
+        at[other] = item;
+        ok = true;
+      } else {
+        cur = other;
+      }
+    }
+    if (!ok) return false;
+  }
+  for (uint32_t i = 0; i <= mask; ++i) {
+    const int32_t e = at[i];
+    if (e < 0) continue;
+    const uint32_t s0 = word_slot0(h[(size_t)e], mask);
+    if (s0 != i && at[s0] < 0) {
+      at[s0] = e;
+      at[i] = -1;
+    }
+  }
+  return true;
 }
 
 // The word table: every symbol whose byte expansion (2..kWordMax bytes)
@@ -301,7 +348,7 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
                       hipMemcpyHostToDevice, stream) != hipSuccess))
     rc = BPE_EHIP;
   if (rc == BPE_OK)
-    rc = enqueue_encode(m, d_text, N, d_doc, D, d_ids, N, d_ioff, d_ws, d_status, nullptr,
+    rc = enqueue_encode(m, d_text, N, d_doc, D, d_ids, N, d_ioff, d_ws, d_status, false,
                         nullptr, stream);
   if (rc == BPE_OK &&
       (hipMemcpyAsync(ioff.data(), d_ioff, sizeof(int64_t) * (size_t)(D + 1), hipMemcpyDeviceToHost,
@@ -321,8 +368,8 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
   if (rc != BPE_OK) return rc;
   if (status != 0) return BPE_EHIP;
 
-  // the entries: {key length, symbol, key[6]}
-  std::vector<std::array<uint32_t, 8>> items;
+  // the entries, split by key length: {len, symbol, key[6]}
+  std::vector<std::array<uint32_t, 8>> items[2];
   for (int64_t k = 0; k < D; ++k) {
     if (!(ioff[(size_t)k + 1] - ioff[(size_t)k] == 1 && ids[(size_t)ioff[(size_t)k]] == cand[(size_t)k]))
       continue;
@@ -333,53 +380,72 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
       w[j >> 2] |= (uint32_t)text[(size_t)doc_off[(size_t)k] + j] << (8 * (j & 3));
     it[0] = (uint32_t)len;
     it[1] = (uint32_t)cand[(size_t)k];
-    items.push_back(it);
+    items[len <= kShortMax ? 0 : 1].push_back(it);
   }
-  const int64_t n_keep = (int64_t)items.size();
-  // two-choice cuckoo placement, capacity a power of two >= 2.5 entries;
-  // on failure another seed, then twice the capacity
-  int bits = 8;
-  while (((int64_t)1 << bits) < 5 * n_keep / 2) ++bits;
-  std::vector<int32_t> at;
-  std::vector<uint32_t> hs((size_t)n_keep);
-  uint32_t seed = 0;
-  for (int attempt = 0;; ++attempt) {
-    if (bits > 30) return BPE_ENOMEM;
-    seed = 0x9E3779B9u * (uint32_t)(attempt + 1);
-    for (int64_t e = 0; e < n_keep; ++e)
-      hs[(size_t)e] = word_hash(&items[(size_t)e][2], (int)items[(size_t)e][0], seed);
-    const uint32_t mask = (1u << bits) - 1u;
-    at.assign((size_t)1 << bits, -1);
-    const int max_kicks = 64 + 4 * bits;
-    bool ok = true;
-    for (int32_t e = 0; e < (int32_t)n_keep && ok; ++e) {
-      int32_t item = e;
-      uint32_t from = word_slot0(hs[(size_t)e], mask);
-      for (int kick = 0;; ++kick) {
-        const uint32_t a = word_slot0(hs[(size_t)item], mask);
-        const uint32_t b = word_slot1(hs[(size_t)item], mask);
-        if (at[a] < 0) { at[a] = item; break; }
-        if (at[b] < 0) { at[b] = item; break; }
-        if (kick == max_kicks) { ok = false; break; }
-        from = (from == a) ? b : a;  // the occupant of the other slot moves on
-        std::swap(item, at[from]);
+  for (int t = 0; t < 2; ++t) {
+    const std::vector<std::array<uint32_t, 8>> &its = items[t];
+    const int64_t n_keep = (int64_t)its.size();
+    if (n_keep == 0) continue;
+    // capacity a power of two >= 2.5 entries; on failure another seed, then
+    // twice the capacity; after that without this table (its pre-tokens then
+    // run the merge loop, with the same result)
+    uint32_t mask = 255;
+    while ((int64_t)mask + 1 < 5 * n_keep / 2) mask = 2 * mask + 1;
+    std::vector<int32_t> at;
+    std::vector<uint32_t> hs((size_t)n_keep);
+    uint32_t seed = 0;
+    bool placed = false;
+    for (int attempt = 0; attempt < 8 && !placed; ++attempt) {
+      seed = 0x9E3779B9u * (uint32_t)(attempt + 1);
+      for (int64_t e = 0; e < n_keep; ++e) {
+        const uint32_t *w = &its[(size_t)e][2];
+        const int len = (int)its[(size_t)e][0];
+        hs[(size_t)e] = t == 0 ? short_mix(w[0], w[1], w[2], (uint32_t)len, seed)
+                               : word_hash(w, len, seed);
+      }
+      placed = place_words(hs, mask, at);
+      if (!placed && attempt % 2 == 1) mask = 2 * mask + 1;
+    }
+    if (!placed) continue;
+    std::vector<uint32_t> flag((size_t)mask + 1, 0u);
+    for (uint32_t i = 0; i <= mask; ++i)
+      if (at[i] >= 0 && word_slot0(hs[(size_t)at[i]], mask) != i)
+        flag[word_slot0(hs[(size_t)at[i]], mask)] = kWordFlag;
+    const int words_per_slot = t == 0 ? 4 : 8;
+    std::vector<uint32_t> slots((size_t)words_per_slot * ((size_t)mask + 1), 0u);
+    for (uint32_t i = 0; i <= mask; ++i) {
+      uint32_t *o = &slots[(size_t)words_per_slot * i];
+      if (at[i] < 0) {
+        if (t == 0) o[3] = flag[i];
+        else o[1] = flag[i];
+        continue;
+      }
+      const std::array<uint32_t, 8> &it = its[(size_t)at[i]];
+      const uint32_t len = it[0], sym = it[1];
+      if (t == 0) {
+        o[0] = it[2];
+        o[1] = it[3];
+        o[2] = it[4];
+        o[3] = sym | (len << 21) | flag[i];
+      } else {
+        o[0] = word_tag(hs[(size_t)at[i]], (int)len);
+        o[1] = sym | flag[i];
+        for (int j = 0; j < 6; ++j) o[2 + j] = it[2 + (size_t)j];
       }
     }
-    if (ok) break;
-    if (attempt % 2 == 1) ++bits;
+    uint4 **dst = t == 0 ? &m->d_words : &m->d_lwords;
+    rc = upload(reinterpret_cast<uint32_t **>(dst), slots.data(), slots.size(), stream);
+    if (rc != BPE_OK) return rc;
+    if (t == 0) {
+      m->word_mask = mask;
+      m->word_seed = seed;
+    } else {
+      m->lword_mask = mask;
+      m->lword_seed = seed;
+    }
+    m->n_words += n_keep;
   }
-  for (int64_t e = 0; e < n_keep; ++e)
-    items[(size_t)e][0] = word_tag(hs[(size_t)e], (int)items[(size_t)e][0]);
-  std::vector<uint32_t> slots((size_t)8 << bits, 0u);
-  for (size_t i = 0; i < at.size(); ++i)
-    if (at[i] >= 0) std::memcpy(&slots[8 * i], items[(size_t)at[i]].data(), 32);
-  rc = upload(reinterpret_cast<uint32_t **>(&m->d_words), slots.data(), slots.size(), stream);
-  if (rc == BPE_OK) {
-    m->word_bits = bits;
-    m->word_seed = seed;
-    m->n_words = n_keep;
-  }
-  return rc;
+  return BPE_OK;
 }
 
 }  // namespace
@@ -563,7 +629,7 @@ int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_b
   hipStream_t stream = (hipStream_t)hip_stream;
   if (n_bytes > 0 && workspace_bytes < enc_layout(n_bytes, n_docs).total) return BPE_EWORKSPACE;
   return enqueue_encode(model, d_bytes, n_bytes, d_doc_off, n_docs, d_ids, ids_capacity, d_id_off,
-                        d_workspace, d_status, model->d_words, model->d_id_map, stream);
+                        d_workspace, d_status, true, model->d_id_map, stream);
 }
 
 size_t bpe_decode_workspace_bytes(const bpe_model *model, int64_t n_ids, int64_t n_docs) {

@@ -41,7 +41,6 @@ constexpr int SB_HALF = WIN / 16 + 1;       // 16-bit start masks for positions 
 constexpr int SB_WORDS = (SB_HALF + 1) / 2 + 1;
 constexpr int DB_OFF = 32;                  // document-start bit of position p is bit p + DB_OFF
 constexpr int DB_WORDS = (WIN + DB_OFF) / 32 + 2;
-constexpr int kMaxLong = kChunk / (kLaneMax + 1) + 4;  // longer pre-tokens per chunk, + the last
 
 // Merge-loop list entry: where (13 bits) | length (13 bits) << 13 | overhang
 // << 26.  `where` is the pre-token's start in the chunk for bucket 3, and its
@@ -55,17 +54,11 @@ __device__ __forceinline__ int me_start(uint32_t e) { return (int)(e & 0x1FFFu);
 __device__ __forceinline__ int me_len(uint32_t e) { return (int)((e >> 13) & 0x1FFFu); }
 __device__ __forceinline__ bool me_over(uint32_t e) { return (e >> 26) & 1u; }
 
-// Length buckets of the merge-loop list: a chunk's list holds bucket 0
-// entries first, then 1, 2, 3, each in text order.  Buckets 0-2 are merged
-// one pre-token per lane (registers for 0-1, LDS arrays for 2); bucket 3 by a
-// whole wave.
-constexpr int kBuckets = 4;
+// Length buckets of the merge-loop list (2-8, 9-16, 17-kLaneMax bytes, then
+// longer ones and a chunk's last pre-token when it runs past the window).
+// Buckets 0-2 are merged one pre-token per lane, bucket 3 by a whole wave.
 __device__ __forceinline__ int bucket_of(int len, bool over) {
   return over ? 3 : (len <= 8 ? 0 : (len <= 16 ? 1 : (len <= kLaneMax ? 2 : 3)));
-}
-// Four 16-bit bucket counts packed in one int64, for one workgroup scan.
-__device__ __forceinline__ int bfield(int64_t packed, int b) {
-  return (int)((packed >> (16 * b)) & 0xFFFF);
 }
 
 // Scratch for the workgroup reductions and the workgroup merge.
@@ -349,34 +342,17 @@ struct FindShared {
   uint32_t SB[SB_WORDS];                 // pre-token start bits, positions [0, WIN]
   uint32_t DB[DB_WORDS];                 // document start bits, positions [-32, WIN)
   uint16_t PS[kChunk + 2];               // owned pre-token starts in order, then the end
+  alignas(16) uint8_t MB[kMissBytes + 16];  // lane-merged entries' bytes, back to back
+  u32x4 LM[kShortMax + 1];               // masks of the first len bytes of three words
   Red<WG> r;
   int64_t o_lo, o_hi;
+  int e_last;
+  int cnt[kBuckets];                     // merge-loop list entries per bucket
+  int nbytes;                            // bytes of the lane-merged entries
 };
 
 __device__ __forceinline__ uint32_t sb16(const FindShared &s, int g) {
   return reinterpret_cast<const uint16_t *>(s.SB)[g];
-}
-
-__device__ __forceinline__ bool db_bit(const FindShared &s, int p) {
-  const int q = p + DB_OFF;
-  return (s.DB[q >> 5] >> (q & 31)) & 1u;
-}
-
-// Smallest start position in [from, WIN], or kNoStart.  Whole workgroup.
-__device__ int block_next_start(FindShared &s, int from) {
-  int cand = kNoStart;
-  if (from <= WIN) {
-    const int w = (from >> 5) + (int)threadIdx.x;
-    if (w <= (WIN >> 5)) {
-      uint32_t bits = s.SB[w];
-      if (w == (from >> 5)) bits &= ~0u << (from & 31);
-      if (bits) {
-        const int p = (w << 5) + __ffs(bits) - 1;
-        if (p <= WIN) cand = p;
-      }
-    }
-  }
-  return block_min<WG>(cand, s.r.red);
 }
 
 // The bytes of the pre-token at window position st (len <= kWordMax) as six
@@ -399,22 +375,50 @@ __device__ __forceinline__ void pretoken_words(const FindShared &s, int st, int 
   }
 }
 
-// Symbol stored for these bytes in the word table, or -1: both slots of
-// the key are loaded at once (two-choice cuckoo table).
-__device__ __forceinline__ int32_t word_lookup(const uint4 *__restrict__ tab, uint32_t mask,
-                                               uint32_t seed, const uint32_t w[kWordWords],
+// Symbol of a pre-token of 2..kShortMax bytes at window position st in the
+// short word table, or -1.
+__device__ __forceinline__ int32_t short_lookup(const FindShared &s, const EncodeArgs &a, int st,
+                                                int len) {
+  const int b0 = 16 + st;
+  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
+  const int q = b0 >> 2;
+  const uint32_t sh = (uint32_t)(b0 & 3);
+  const uint32_t r0 = B32[q], r1 = B32[q + 1], r2 = B32[q + 2], r3 = B32[q + 3];
+  const u32x4 m = s.LM[len];
+  const uint32_t w0 = __builtin_amdgcn_alignbyte(r1, r0, sh) & m.x;
+  const uint32_t w1 = __builtin_amdgcn_alignbyte(r2, r1, sh) & m.y;
+  const uint32_t w2 = __builtin_amdgcn_alignbyte(r3, r2, sh) & m.z;
+  const uint32_t x = short_mix(w0, w1, w2, (uint32_t)len, a.word_seed);
+  const uint32_t tl = (uint32_t)len << 21;
+  const u32x4 *tab = reinterpret_cast<const u32x4 *>(a.words);
+  u32x4 e = tab[word_slot0(x, a.word_mask)];
+  if (((e.x ^ w0) | (e.y ^ w1) | (e.z ^ w2) | ((e.w ^ tl) & (0xFu << 21))) == 0)
+    return (int32_t)(e.w & kWordSymMask);
+  if (!(e.w & kWordFlag)) return -1;
+  e = tab[word_slot1(x, a.word_mask)];
+  if (((e.x ^ w0) | (e.y ^ w1) | (e.z ^ w2) | ((e.w ^ tl) & (0xFu << 21))) == 0)
+    return (int32_t)(e.w & kWordSymMask);
+  return -1;
+}
+
+// Symbol of a pre-token of kShortMax + 1..kWordMax bytes in the long word
+// table, or -1.
+__device__ __forceinline__ int32_t long_lookup(const FindShared &s, const EncodeArgs &a, int st,
                                                int len) {
-  const uint32_t h = word_hash(w, len, seed);
+  uint32_t w[kWordWords];
+  pretoken_words(s, st, len, w);
+  const uint32_t h = word_hash(w, len, a.lword_seed);
   const uint32_t tag = word_tag(h, len);
-  const uint32_t i0 = word_slot0(h, mask), i1 = word_slot1(h, mask);
-  const uint4 x0 = tab[2 * i0], y0 = tab[2 * i0 + 1];
-  const uint4 x1 = tab[2 * i1], y1 = tab[2 * i1 + 1];
-  if (x0.x == tag && x0.z == w[0] && x0.w == w[1] && y0.x == w[2] && y0.y == w[3] &&
-      y0.z == w[4] && y0.w == w[5])
-    return (int32_t)x0.y;
-  if (x1.x == tag && x1.z == w[0] && x1.w == w[1] && y1.x == w[2] && y1.y == w[3] &&
-      y1.z == w[4] && y1.w == w[5])
-    return (int32_t)x1.y;
+  uint32_t i = word_slot0(h, a.lword_mask);
+  const u32x4 *tab = reinterpret_cast<const u32x4 *>(a.lwords);
+  for (int k = 0; k < 2; ++k) {
+    const u32x4 x = tab[2 * i], y = tab[2 * i + 1];
+    if (((x.x ^ tag) | (x.z ^ w[0]) | (x.w ^ w[1]) | (y.x ^ w[2]) | (y.y ^ w[3]) | (y.z ^ w[4]) |
+         (y.w ^ w[5])) == 0)
+      return (int32_t)(x.y & kWordSymMask);
+    if (!(x.y & kWordFlag)) return -1;
+    i = word_slot1(h, a.lword_mask);
+  }
   return -1;
 }
 
@@ -444,6 +448,17 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   const int nown = (int)min<int64_t>(kChunk, n - c0);
   const bool win_reaches_end = (c0 + nwin == n);
   for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
+  if (tid < kBuckets) s.cnt[tid] = 0;
+  if (tid == 0) s.nbytes = 0;
+  if (tid <= kShortMax) {
+    // masks of the first tid bytes of three little-endian words
+    u32x4 m;
+    m.x = tid >= 4 ? ~0u : (1u << (8 * tid)) - 1u;
+    m.y = tid >= 8 ? ~0u : (tid <= 4 ? 0u : (1u << (8 * (tid - 4))) - 1u);
+    m.z = tid >= 12 ? ~0u : (tid <= 8 ? 0u : (1u << (8 * (tid - 8))) - 1u);
+    m.w = 0;
+    s.LM[tid] = m;
+  }
 
   // 1. the window's bytes, 16 per load (group g covers positions 16g ..
   //    16g + 15; group -1 is the two bytes before the chunk), issued first so
@@ -524,109 +539,92 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   }
   __syncthreads();
 
-  // last owned start and whether its pre-token runs past the window
+  // 3. the owned pre-token starts (positions below nown) as one ordered list,
+  //    then the end of the last: the first start at or after nown, where the
+  //    window still has one (else the pre-token runs past the window)
   uint32_t own = 0;
   if (16 * tid < nown) {
     own = sb16(s, tid);
     const int lim = nown - 16 * tid;
     if (lim < 16) own &= (1u << lim) - 1;
   }
-  const int ls = block_max<WG>(own ? 16 * tid + 31 - __clz(own) : -1, s.r.red);
-  const int e_last = ls >= 0 ? block_next_start(s, ls + 1) : -1;
-  const bool overhang = ls >= 0 && e_last == kNoStart;
-
-  // 3. the owned pre-token starts as one ordered list, and the end of the last
+  if (tid == 0) {
+    int e = kNoStart;
+    for (int g = nown >> 4; g < SB_HALF && e == kNoStart; ++g) {
+      uint32_t m = sb16(s, g);
+      if (g == (nown >> 4)) m &= 0xFFFFu << (nown & 15);
+      if (m) e = 16 * g + __ffs(m) - 1;
+    }
+    s.e_last = e <= WIN ? e : kNoStart;
+  }
   int n_pt;
   {
     const int pex = block_excl_sum<int, WG>(__popc(own), s.r.red, &n_pt);
     uint32_t m = own;
     for (int k = pex; m; ++k, m &= m - 1) s.PS[k] = (uint16_t)(16 * tid + __ffs(m) - 1);
-    if (tid == 0) s.PS[n_pt] = (uint16_t)(overhang ? WIN : (ls >= 0 ? e_last : 0));
+    if (tid == 0) s.PS[n_pt] = (uint16_t)(s.e_last == kNoStart ? WIN : s.e_last);
   }
   __syncthreads();
+  const bool overhang = n_pt > 0 && s.e_last == kNoStart;
 
-  // 4. each thread resolves a contiguous block of the list: a single byte is
-  //    its own token; a pre-token that is a whole word-table entry takes its
-  //    symbol; the others go to the merge-loop list (pv = -1 - list index)
-  const int per = (n_pt + WG - 1) / WG;  // <= 16
-  const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
+  // 4. each thread resolves every WG-th pre-token: a single byte is its own
+  //    token; a pre-token that is a whole word-table entry takes its symbol;
+  //    the others go to the merge-loop list, a slot in their bucket's region
+  //    and, up to kLaneMax bytes, their bytes in the dense region (both taken
+  //    by LDS atomics: pv names the entry, so order does not matter)
   int32_t *pv = a.pv + c * kChunk;
-  int64_t bcnt = 0;    // this thread's misses per bucket, packed
-  int64_t blen = 0;    // and their bytes, buckets 0-2
-  uint64_t codes = 0;  // 3 bits per pre-token k0 + j: 0 resolved, 1 + bucket otherwise
-  const uint32_t wmask = (1u << a.word_bits) - 1u;
-  for (int k = k0; k < k1; ++k) {
-    int32_t v = -1;
+  uint32_t *ml = a.miss + c * kMissMax;
+  for (int k = tid; k < n_pt; k += WG) {
     const bool over = overhang && k == n_pt - 1;
     const int st = s.PS[k];
     const int len = over ? 0 : (int)s.PS[k + 1] - st;
+    int32_t v = -1;
     if (len == 1) {
       v = s.B[16 + st];
-    } else if (!over && a.words && len <= kWordMax) {
-      uint32_t w[kWordWords];
-      pretoken_words(s, st, len, w);
-      v = word_lookup(a.words, wmask, a.word_seed, w, len);
+    } else if (!over) {
+      if (len <= kShortMax) {
+        if (a.words) v = short_lookup(s, a, st, len);
+      } else if (len <= kWordMax && a.lwords) {
+        v = long_lookup(s, a, st, len);
+      }
     }
-    if (v < 0) {
-      const int b = bucket_of(len, over);
-      bcnt += (int64_t)1 << (16 * b);
-      if (b < 3) blen += (int64_t)len << (16 * b);
-      codes |= (uint64_t)(1 + b) << (3 * (k - k0));
-    } else {
+    if (v >= 0) {
       pv[k] = v;
+      continue;
     }
-  }
-  int64_t btot, ltot;
-  const int64_t bex = block_excl_sum<int64_t, WG>(bcnt, s.r.red64, &btot);
-  const int64_t lex = block_excl_sum<int64_t, WG>(blen, s.r.red64, &ltot);
-  {
-    uint32_t *ml = a.miss + c * kMissMax;
-    uint8_t *mb = a.mbytes + c * kMissBytes;
-    int64_t at = 0;  // next list index per bucket, packed
-    int64_t bo = 0;  // next byte offset per bucket (0-2), packed
-    int base = 0, lbase = 0;
-#pragma unroll
-    for (int b = 0; b < kBuckets; ++b) {
-      at += (int64_t)(base + bfield(bex, b)) << (16 * b);
-      base += bfield(btot, b);
-      if (b < 3) {
-        bo += (int64_t)(lbase + bfield(lex, b)) << (16 * b);
-        lbase += bfield(ltot, b);
-      }
-    }
-    for (int k = k0; codes; ++k, codes >>= 3) {
-      if (codes & 7u) {
-        const int b = (int)(codes & 7u) - 1;
-        const int st = s.PS[k];
-        const bool over = overhang && k == n_pt - 1;
-        const int len = over ? 0 : (int)s.PS[k + 1] - st;
-        const int idx = bfield(at, b);
-        if (b < 3) {
-          // lane-merged entries: their bytes go to the dense region
-          const int o = bfield(bo, b);
-          for (int j = 0; j < len; ++j) mb[o + j] = s.B[16 + st + j];
-          ml[idx] = miss_entry(o, len, false);
-          bo += (int64_t)len << (16 * b);
-        } else {
-          ml[idx] = miss_entry(st, len, over);
-        }
-        pv[k] = -1 - idx;
-        at += (int64_t)1 << (16 * b);
-      }
+    const int b = bucket_of(len, over);
+    const int idx = atomicAdd(&s.cnt[b], 1);
+    const int base = b == 0 ? kBucketBase[0] : b == 1 ? kBucketBase[1] : b == 2 ? kBucketBase[2] : kBucketBase[3];
+    if (b < 3) {
+      const int o = atomicAdd(&s.nbytes, len);
+      for (int j = 0; j < len; ++j) s.MB[o + j] = s.B[16 + st + j];
+      ml[base + idx] = miss_entry(o, len, false);
+      pv[k] = -1 - o;
+    } else {
+      ml[base + idx] = miss_entry(st, len, over);
+      pv[k] = -1 - kMissBytes - idx;
     }
   }
   const bool any_bad = __syncthreads_or(bad);
+  // the dense bytes, 16 per store
+  const int nbytes = s.nbytes;
+  {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.mbytes + c * kMissBytes);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(s.MB);
+    for (int i = tid; 16 * i < nbytes; i += WG) dst[i] = src[i];
+  }
   if (tid == 0) {
     int32_t *m = a.meta + kMetaInts * c;
     int n_miss = 0;
 #pragma unroll
     for (int b = 0; b < kBuckets; ++b) {
-      m[kMetaBucket + b] = bfield(btot, b);
-      n_miss += bfield(btot, b);
+      m[kMetaBucket + b] = s.cnt[b];
+      n_miss += s.cnt[b];
     }
     m[kMetaPretokens] = n_pt;
     m[kMetaMisses] = n_miss;
     m[kMetaStatus] = any_bad ? (int32_t)BPE_STATUS_BAD_DOC_OFFSETS : 0;
+    m[kMetaBytes] = nbytes;
     a.doc_rng[2 * c] = s.o_lo;
     a.doc_rng[2 * c + 1] = s.o_hi;
   }
@@ -694,36 +692,32 @@ __device__ __forceinline__ bool lane_group(const EncodeArgs &a, LaneGroup &G) {
 
 // Bucket b of the group's lists, one pre-token per lane with W-wide LDS
 // columns, 64 entries per batch.  An entry's bytes are read from its chunk's
-// dense mbytes region and its tokens written to res at the same offset: never
-// more tokens than bytes, so entries do not overlap.  mt gets each entry's
-// token count; the return value holds the tokens per chunk, 16 bits each.
+// dense mbytes region and its tokens written to res at the same offset (never
+// more tokens than bytes, so entries do not overlap), their count to mto at
+// that offset; the return value holds the tokens per chunk, 16 bits each.
 template <int W>
 __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b, LaneCols<W> &L) {
   const int lane = lane_id();
   const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
-  // per chunk: entries of the bucket before the chunk's, and the bucket's
-  // first list index in the chunk (uniform across the wave)
-  int pre[kGroup], first[kGroup];
+  // per chunk: entries of the bucket before the chunk's (uniform across the wave)
+  int pre[kGroup];
   int total = 0;
 #pragma unroll
   for (int f = 0; f < kGroup; ++f) {
     pre[f] = total;
     total += G.cnt[f][b];
-    first[f] = 0;
-#pragma unroll
-    for (int bb = 0; bb < kBuckets; ++bb)
-      if (bb < b) first[f] += G.cnt[f][bb];
   }
+  const int base = kBucketBase[b];
   uint64_t tok = 0;
   for (int s0 = 0; s0 < total; s0 += 64) {
     const int g = s0 + lane;
     if (g >= total) break;
-    int f = 0, idx = g + first[0];
+    int f = 0, idx = base + g;
 #pragma unroll
     for (int k = 1; k < kGroup; ++k)
       if (g >= pre[k]) {
         f = k;
-        idx = g - pre[k] + first[k];
+        idx = base + g - pre[k];
       }
     const int64_t c = G.cg + f;
     const uint32_t e = a.miss[c * kMissMax + idx];
@@ -731,7 +725,7 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
     uint32_t w[W / 4];
     load_words<W / 4>(a.mbytes + c * kMissBytes + o, w);
     const int nt = lane_merge<W>(w, me_len(e), L, t, a.pair_rank, a.res + c * kMissBytes + o);
-    a.mt[c * kMissMax + idx] = nt;
+    a.mto[c * kMissBytes + o] = (uint8_t)nt;
     tok += (uint64_t)nt << (16 * f);
   }
   return tok;
@@ -980,7 +974,7 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
   const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
   for (int f = 0; f < nf; ++f) {
     const int n3 = s.g.meta[f][kMetaBucket + 3];
-    const int base = s.g.meta[f][kMetaMisses] - n3;
+    const int base = kBucketBase[3];
     const int64_t c = cg + f, c0 = c * kChunk;
     for (int q = 0; q < n3; ++q) {
       const uint32_t e = a.miss[c * kMissMax + base + q];
@@ -1003,7 +997,7 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
         nt = wg_merge<MWG>(a.gsym + gs, a.grank + gs, len, t, a.pair_rank, s.g.r);
       }
       if (lane == 0) {
-        a.mt[c * kMissMax + base + q] = (int32_t)nt;
+        a.mt[c * kMaxLong + q] = (int32_t)nt;
         s.g.tok[f] += (int32_t)nt;
       }
       __syncthreads();
@@ -1023,102 +1017,144 @@ __global__ void __launch_bounds__(OWG) k_offsets(EncodeArgs a) {
 
 // ---- k_emit -------------------------------------------------------------------
 
-constexpr int EWG = 256;  // k_emit threads per chunk
+constexpr int EWG = 256;                 // k_emit threads per chunk
+constexpr int kOutCap = kChunk + kHalo;  // chunk-relative token positions staged in LDS
+constexpr int kEmitPasses = 4;           // passes of EWG pre-tokens per round
 
 struct EmitShared {
-  int64_t ex[EWG];        // each thread's first token, relative to the chunk
-  int64_t lw[kMaxLong];   // longer entries: output position, symbols, count
+  int32_t out[kOutCap];                  // the chunk's symbols at positions below kOutCap
+  uint16_t pos[kChunk];                  // each pre-token's first position
+  int32_t wtot[kEmitPasses][EWG / 64];   // token counts per pass and wave
+  int64_t lw[kMaxLong];                  // wave-merged entries: position, source, count
   int64_t lsrc[kMaxLong];
   int64_t lnt[kMaxLong];
   int32_t n_long;
-  Red<EWG> r;
 };
 
 // Writes a chunk's IDs at its offset, and the offsets of the documents that
-// start in it.  Each thread takes a contiguous block of the chunk's
-// pre-tokens.
+// start in it.  Pre-token k belongs to thread k % EWG; rounds of kEmitPasses
+// passes load every pv value of the round, then the token counts and the first
+// four tokens of the merge-loop entries, scan the counts and place the
+// symbols in LDS; the workgroup then writes the chunk's positions in order.
+// A position at or past kOutCap (possible only after a long pre-token that
+// runs past the window) is written directly.
 __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   __shared__ EmitShared s;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int64_t c = blockIdx.x;
   const int64_t c0 = c * kChunk;
-  const int32_t *meta = a.meta + kMetaInts * c;
-  const int n_pt = meta[kMetaPretokens];
-  const int first3 = meta[kMetaMisses] - meta[kMetaBucket + 3];  // list index of bucket 3
+  const int n_pt = a.meta[kMetaInts * c + kMetaPretokens];
   const int64_t base = a.off[c];
   const int32_t *pv = a.pv + c * kChunk;
-  const uint32_t *ml = a.miss + c * kMissMax;
-  const int32_t *mt = a.mt + c * kMissMax;
   const int32_t *res = a.res + c * kMissBytes;
+  const uint8_t *mto = a.mto + c * kMissBytes;
   if (tid == 0) s.n_long = 0;
-
-  // this thread's pre-tokens: a symbol, or -1 - the index of a list entry
-  const int per = (n_pt + EWG - 1) / EWG;
-  const int k0 = min(n_pt, tid * per), k1 = min(n_pt, k0 + per);
-  int64_t cnt = 0;
-  for (int k = k0; k < k1; ++k) {
-    const int32_t v = pv[k];
-    cnt += v >= 0 ? 1 : mt[-1 - v];
-  }
-  int64_t total;
-  const int64_t ex = block_excl_sum<int64_t, EWG>(cnt, s.r.red64, &total);
-  s.ex[tid] = ex;
   bool overflow = false;
-  {
-    int64_t w = base + ex;
-    for (int k = k0; k < k1; ++k) {
-      const int32_t x = pv[k];
+  auto put = [&](int64_t w, int32_t sym) {
+    if (w < kOutCap) {
+      s.out[w] = sym;
+    } else if (base + w < a.ids_cap) {
+      a.ids[base + w] = out_id(a.id_map, sym);
+    } else {
+      overflow = true;
+    }
+  };
+  int64_t carry = 0;
+  for (int r0 = 0; r0 < n_pt; r0 += EWG * kEmitPasses) {
+    int32_t v[kEmitPasses], cnt[kEmitPasses];
+    u32x4 first[kEmitPasses];
+#pragma unroll
+    for (int j = 0; j < kEmitPasses; ++j) {
+      const int k = r0 + j * EWG + tid;
+      v[j] = k < n_pt ? pv[k] : INT32_MIN;
+    }
+#pragma unroll
+    for (int j = 0; j < kEmitPasses; ++j) {
+      cnt[j] = v[j] >= 0 ? 1 : 0;
+      first[j] = u32x4{0, 0, 0, 0};
+      if (v[j] < 0 && v[j] != INT32_MIN) {
+        const int o = -1 - v[j];
+        if (o < kMissBytes) {
+          cnt[j] = mto[o];
+          first[j] = *reinterpret_cast<const u32x4 *>(res + o);
+        } else {
+          cnt[j] = a.mt[c * kMaxLong + (o - kMissBytes)];
+        }
+      }
+    }
+    // positions: every pass of the round is one scan over the workgroup
+    int32_t inc[kEmitPasses];
+#pragma unroll
+    for (int j = 0; j < kEmitPasses; ++j) {
+      inc[j] = wave_incl_sum(cnt[j]);
+      if (lane == 63) s.wtot[j][wave] = inc[j];
+    }
+    __syncthreads();
+    int64_t w0[kEmitPasses];
+    int64_t run = carry;
+#pragma unroll
+    for (int j = 0; j < kEmitPasses; ++j) {
+      int32_t before = 0, all = 0;
+#pragma unroll
+      for (int ww = 0; ww < EWG / 64; ++ww) {
+        const int32_t t = s.wtot[j][ww];
+        if (ww < wave) before += t;
+        all += t;
+      }
+      w0[j] = run + before + inc[j] - cnt[j];
+      run += all;
+    }
+    carry = run;
+#pragma unroll
+    for (int j = 0; j < kEmitPasses; ++j) {
+      const int k = r0 + j * EWG + tid;
+      if (k >= n_pt) continue;
+      s.pos[k] = (uint16_t)w0[j];
+      const int32_t x = v[j];
+      int64_t w = w0[j];
       if (x >= 0) {
-        if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, x);
-        else overflow = true;
-        ++w;
+        put(w, x);
         continue;
       }
-      const int i = -1 - x;
-      const uint32_t e = ml[i];
-      const int64_t nt = mt[i];
-      if (i < first3) {
-        const int32_t *src = res + me_start(e);
-        for (int j = 0; j < nt; ++j, ++w) {
-          if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, src[j]);
-          else overflow = true;
-        }
+      const int o = -1 - x;
+      if (o < kMissBytes) {
+        const int nt = cnt[j];
+        put(w, (int32_t)first[j].x);
+        if (nt > 1) put(w + 1, (int32_t)first[j].y);
+        if (nt > 2) put(w + 2, (int32_t)first[j].z);
+        if (nt > 3) put(w + 3, (int32_t)first[j].w);
+        for (int t = 4; t < nt; ++t) put(w + t, res[o + t]);
       } else {
+        const int q = o - kMissBytes;
+        const uint32_t e = a.miss[c * kMissMax + kBucketBase[3] + q];
         const int slot = atomicAdd(&s.n_long, 1);
         s.lw[slot] = w;
         s.lsrc[slot] = c0 + me_start(e);
-        s.lnt[slot] = nt;
-        w += nt;
+        s.lnt[slot] = cnt[j];
       }
     }
+    __syncthreads();  // wtot is rewritten by the next round
   }
-  __syncthreads();
-  // longer entries' symbols, copied by the whole workgroup
+  const int64_t total = carry;
+  // wave-merged entries' symbols, copied by the whole workgroup
   for (int q = 0; q < s.n_long; ++q) {
     const int64_t w0 = s.lw[q], src = s.lsrc[q], nt = s.lnt[q];
-    for (int64_t j = tid; j < nt; j += EWG) {
-      const int64_t w = w0 + j;
-      if (w < a.ids_cap) a.ids[w] = out_id(a.id_map, a.gsym[src + j]);
-      else overflow = true;
-    }
+    for (int64_t j = tid; j < nt; j += EWG) put(w0 + j, a.gsym[src + j]);
+  }
+  __syncthreads();
+  // the staged positions, in order
+  const int nst = (int)min(total, (int64_t)kOutCap);
+  for (int k = tid; k < nst; k += EWG) {
+    if (base + k < a.ids_cap) a.ids[base + k] = out_id(a.id_map, s.out[k]);
+    else overflow = true;
   }
   if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
-  // per-document offsets: a document starting at pre-token k begins after
-  // every token of the pre-tokens before k (those of k's thread before k are
-  // counted again)
+  // per-document offsets: a document starting at pre-token k begins at k's
+  // first position
   const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
   for (int64_t d = dlo + tid; d < dhi; d += EWG) {
     const int k = min(max(a.doc_pt[d], 0), n_pt);
-    int64_t o = total;
-    if (k < n_pt) {
-      const int t = k / per;
-      o = s.ex[t];
-      for (int kk = t * per; kk < k; ++kk) {
-        const int32_t v = pv[kk];
-        o += v >= 0 ? 1 : mt[-1 - v];
-      }
-    }
-    a.id_off[d] = base + o;
+    a.id_off[d] = base + (k < n_pt ? (int64_t)s.pos[k] : total);
   }
   if (c == a.n_chunks - 1) {
     const int64_t end = base + (a.tot[c] & kCountMask);

@@ -47,13 +47,18 @@ __host__ __device__ inline uint32_t mul24(uint32_t a, uint32_t b) {
   return (a & 0xFFFFFFu) * (b & 0xFFFFFFu);
 }
 
-// 32-bit mix of a pair of symbols (both below 2^21) and the table's seed.
-__host__ __device__ inline uint32_t pair_mix(uint32_t l, uint32_t r, uint32_t seed) {
-  uint32_t x = mul24(l, 0x9E3779u) ^ r ^ seed;
+// A bijection of 32-bit values: the low 24 bits times an odd constant (a
+// bijection of the low 24 bits of the product), the top byte carried over.
+__host__ __device__ inline uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
-  x = mul24(x, 0x85EBCBu);
+  x = mul24(x, 0x85EBCBu) ^ (x & 0xFF000000u);
   x ^= x >> 13;
   return x;
+}
+
+// 32-bit mix of a pair of symbols (both below 2^21) and the table's seed.
+__host__ __device__ inline uint32_t pair_mix(uint32_t l, uint32_t r, uint32_t seed) {
+  return mix32(mul24(l ^ seed, 0x9E3779u) ^ r ^ (seed >> 8));
 }
 
 // First and second bucket of a mix, for a table of mask + 1 buckets (a power
@@ -65,18 +70,38 @@ __host__ __device__ inline uint32_t pair_bucket1(uint32_t x, uint32_t mask) {
   return b1 == b0 ? b0 ^ 1u : b1;
 }
 
-// ---- word table -----------------------------------------------------------
-// Read-only table built at load time: a pre-token whose bytes equal the
-// expansion of symbol s (2..kWordMax bytes), where encoding that expansion
-// yields exactly [s], encodes to [s] without running the merge loop.  One
-// 32-byte slot per entry: {tag, symbol, key[6]}; tag = (h0 & ~0xff) | len
-// (0 = empty); key = the bytes as six little-endian words, zero padded.
-// Two-choice cuckoo hashing: an entry sits in one of two slots, both
-// derived from one seeded 32-bit hash h, so a lookup loads both slots at
-// once and never follows a chain.  Keys that share h share both slots; the
-// table's seed is chosen at load so that every key finds a slot.
+// ---- word tables ----------------------------------------------------------
+// Read-only tables built at load time ("Hugging Face Tokenizers v1", section
+// "Word caching": a pre-token seen as a whole skips the merge loop): a
+// pre-token whose bytes equal the expansion of symbol s (2..kWordMax bytes),
+// where encoding that expansion yields exactly [s], encodes to [s].  Both are
+// two-choice cuckoo tables with one slot per bucket: an entry sits in its
+// first or its second slot, and a flag in the first slot says that some
+// entry whose first slot it is sits in its second; a lookup loads the first
+// slot, and the second only when the key is not in the first and the flag is
+// set.  Keys are the bytes as little-endian words, zero padded.
+//
+// Short table (2..kShortMax bytes): 16-byte slots {w0, w1, w2, meta},
+// meta = symbol | len << 21 | flag << 31; an empty slot is all zero (its len
+// field matches no key).
+//
+// Long table (kShortMax + 1..kWordMax bytes): 32-byte slots
+// {tag, symbol | flag << 31, w0, w1}, {w2, w3, w4, w5}, tag = (h & ~0xff) |
+// len (0 = empty).
+constexpr int kShortMax = 12;
 constexpr int kWordMax = 24;
 constexpr int kWordWords = kWordMax / 4;
+constexpr uint32_t kWordFlag = 1u << 31;
+constexpr uint32_t kWordSymMask = (1u << 21) - 1;
+
+// Mix of a short key (w2:w1:w0 zero padded past len bytes), 24-bit pieces.
+__host__ __device__ inline uint32_t short_mix(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t len,
+                                              uint32_t seed) {
+  const uint32_t p1 = (w0 >> 24) | (w1 << 8);
+  const uint32_t p2 = (w1 >> 16) | (w2 << 16);
+  return mix32(mul24(w0 ^ seed, 0x9E3779u) ^ mul24(p1 ^ seed, 0x85EBCBu) ^
+               mul24(p2 ^ seed, 0xC2B2AFu) ^ mul24(w2 >> 8, 0x27D4EBu) ^ (len << 26));
+}
 
 __host__ __device__ inline uint32_t word_hash(const uint32_t *w, int len, uint32_t seed) {
   uint32_t h = 0x811C9DC5u ^ ((uint32_t)len * 0x01000193u) ^ seed;
@@ -94,8 +119,7 @@ __host__ __device__ inline uint32_t word_tag(uint32_t h, int len) {
 // The two slots of a key; the second moves off the first when they coincide.
 __host__ __device__ inline uint32_t word_slot0(uint32_t h, uint32_t mask) { return h & mask; }
 __host__ __device__ inline uint32_t word_slot1(uint32_t h, uint32_t mask) {
-  uint32_t g = h * 0x2C1B3C6Du;
-  g ^= g >> 15;
+  const uint32_t g = mul24(h >> 8, 0xC2B2AFu) ^ (h >> 19);
   const uint32_t s0 = h & mask, s1 = g & mask;
   return s1 == s0 ? s0 ^ 1u : s1;
 }
@@ -120,32 +144,48 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kWinMax = 64;
 
 // Per-chunk records of the encode pipeline.
-constexpr int kMissMax = kChunk / 2 + 16;  // merge-loop pre-tokens per chunk (each >= 2 bytes)
 constexpr int kMissBytes = kChunk + kHalo;  // bytes of a chunk's lane-merged pre-tokens, at most
+constexpr int kMaxLong = kChunk / (kLaneMax + 1) + 4;  // wave-merged pre-tokens per chunk, at most
+// The merge-loop list of a chunk: one region per length bucket (2-8, 9-16,
+// 17-32 bytes, then longer or running past the window), each sized for the
+// most entries of its least length whose bytes fit in the window.
+constexpr int kBuckets = 4;
+constexpr int kBucketCap[kBuckets] = {kMissBytes / 2, kMissBytes / 9 + 1, kMissBytes / 17 + 1,
+                                      kMaxLong};
+constexpr int kBucketBase[kBuckets] = {0, kBucketCap[0], kBucketCap[0] + kBucketCap[1],
+                                       kBucketCap[0] + kBucketCap[1] + kBucketCap[2]};
+constexpr int kMissMax = kBucketBase[3] + kBucketCap[3];
 // meta: 8 int32 per chunk
 constexpr int kMetaInts = 8;
 constexpr int kMetaPretokens = 0;  // pre-tokens that start in the chunk
 constexpr int kMetaMisses = 1;     // of which on the merge-loop list
 constexpr int kMetaStatus = 2;     // status bits found by the chunk
+constexpr int kMetaBytes = 3;      // bytes of the lane-merged entries
 constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
 
 // Encode workspace, all regions 256-byte aligned:
-//   meta      [G][8] i32  pre-tokens, merge-loop pre-tokens, status bits, -,
-//                         list entries per length bucket
+//   meta      [G][8] i32  pre-tokens, merge-loop pre-tokens, status bits,
+//                         lane-merged bytes, list entries per length bucket
 //   tot, off  [G] i64   token count per chunk with its status bits on top,
 //                       then the counts' exclusive prefix
 //   doc_rng   [G][2] i64  documents that start in the chunk
 //   doc_pt    [D] i32   index of each document's first pre-token in its chunk
-//   pv        [G][kChunk] i32    result per pre-token (symbol, or -1: see the list)
-//   miss      [G][kMissMax] u32  merge-loop list by length bucket:
-//                                start | len << 13 | overhang << 26
-//   mt        [G][kMissMax] i32  token count of each list entry
+//   pv        [G][kChunk] i32    per pre-token: its symbol; -1 - o for a
+//                                lane-merged one whose bytes start at o in
+//                                mbytes; -1 - kMissBytes - q for the q-th
+//                                wave-merged one
+//   miss      [G][kMissMax] u32  merge-loop list, a region per length bucket
+//                                (kBucketBase), in no particular order:
+//                                o | len << 13 (lane-merged), start | len << 13 |
+//                                overhang << 26 (wave-merged)
+//   mt        [G][kMaxLong] i32  token count of each wave-merged entry
 //   mbytes    [G][kMissBytes] u8   bytes of the lane-merged entries, back to back
-//   res       [G][kMissBytes] i32  their tokens, each entry's at its byte offset
+//   mto       [G][kMissBytes] u8   token count of the lane-merged entry at o
+//   res       [G][kMissBytes] i32  its tokens, from o on
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the wave merge, position-indexed
 struct EncLayout {
-  size_t meta, tot, off, doc_rng, doc_pt, pv, miss, mt, mbytes, res, gsym, grank, total;
+  size_t meta, tot, off, doc_rng, doc_pt, pv, miss, mt, mbytes, mto, res, gsym, grank, total;
 };
 inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   EncLayout L;
@@ -163,9 +203,10 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.doc_pt = take(4 * (size_t)(n_docs + 1));
   L.pv = take(4 * (size_t)kChunk * G);
   L.miss = take(4 * (size_t)kMissMax * G);
-  L.mt = take(4 * (size_t)kMissMax * G);
-  L.mbytes = take((size_t)kMissBytes * G);
-  L.res = take(4 * (size_t)kMissBytes * G);
+  L.mt = take(4 * (size_t)kMaxLong * G);
+  L.mbytes = take((size_t)kMissBytes * G + 64);  // word loads read a little past the end
+  L.mto = take((size_t)kMissBytes * G);
+  L.res = take(4 * (size_t)kMissBytes * G + 64);
   L.gsym = take(4 * (size_t)n_bytes);
   L.grank = take(4 * (size_t)n_bytes);
   L.total = o;
@@ -199,9 +240,12 @@ struct EncodeArgs {
   uint32_t table_seed;
   const int32_t *id_map;     // nullptr = identity
   const int32_t *pair_rank;  // [65536]: rank of the byte pair (a, b) at a * 256 + b
-  const uint4 *words;        // word table: 2 uint4 per slot; nullptr = none
-  int word_bits;
+  const uint4 *words;        // short word table (one uint4 per slot); nullptr = none
+  uint32_t word_mask;        // slots - 1
   uint32_t word_seed;
+  const uint4 *lwords;       // long word table (two uint4 per slot); nullptr = none
+  uint32_t lword_mask;
+  uint32_t lword_seed;
   int32_t *meta;
   int64_t *tot;
   int64_t *off;
@@ -211,6 +255,7 @@ struct EncodeArgs {
   uint32_t *miss;
   int32_t *mt;
   uint8_t *mbytes;
+  uint8_t *mto;
   int32_t *res;
   int32_t *gsym;
   int32_t *grank;
