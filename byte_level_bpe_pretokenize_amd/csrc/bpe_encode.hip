@@ -1043,11 +1043,19 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int64_t c = blockIdx.x;
   const int64_t c0 = c * kChunk;
-  const int n_pt = a.meta[kMetaInts * c + kMetaPretokens];
-  const int64_t base = a.off[c];
   const int32_t *pv = a.pv + c * kChunk;
   const int32_t *res = a.res + c * kMissBytes;
   const uint8_t *mto = a.mto + c * kMissBytes;
+  // loads that need nothing else first: the first round's pv values (pv has
+  // room for kChunk entries, so this reads inside it whatever the count), and
+  // the first pre-token of the documents that start here
+  int32_t v0[kEmitPasses];
+#pragma unroll
+  for (int j = 0; j < kEmitPasses; ++j) v0[j] = pv[j * EWG + tid];
+  const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
+  const int dk0 = dlo + tid < dhi ? a.doc_pt[dlo + tid] : 0;
+  const int n_pt = a.meta[kMetaInts * c + kMetaPretokens];
+  const int64_t base = a.off[c];
   if (tid == 0) s.n_long = 0;
   bool overflow = false;
   auto put = [&](int64_t w, int32_t sym) {
@@ -1066,7 +1074,7 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
       const int k = r0 + j * EWG + tid;
-      v[j] = k < n_pt ? pv[k] : INT32_MIN;
+      v[j] = k < n_pt ? (r0 == 0 ? v0[j] : pv[k]) : INT32_MIN;
     }
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
@@ -1151,9 +1159,8 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
   // per-document offsets: a document starting at pre-token k begins at k's
   // first position
-  const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
   for (int64_t d = dlo + tid; d < dhi; d += EWG) {
-    const int k = min(max(a.doc_pt[d], 0), n_pt);
+    const int k = min(max(d == dlo + tid ? dk0 : a.doc_pt[d], 0), n_pt);
     a.id_off[d] = base + (k < n_pt ? (int64_t)s.pos[k] : total);
   }
   if (c == a.n_chunks - 1) {
