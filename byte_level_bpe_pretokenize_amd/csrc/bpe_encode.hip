@@ -1022,7 +1022,8 @@ constexpr int kOutCap = kChunk + kHalo;  // chunk-relative token positions stage
 constexpr int kEmitPasses = 4;           // passes of EWG pre-tokens per round
 
 struct EmitShared {
-  int32_t out[kOutCap];                  // the chunk's symbols at positions below kOutCap
+  int32_t out[kOutCap + 1];              // the chunk's symbols at positions below kOutCap;
+                                         // stores that place nothing go to out[kOutCap]
   uint16_t pos[kChunk];                  // each pre-token's first position
   int32_t wtot[kEmitPasses][EWG / 64];   // token counts per pass and wave
   int64_t lw[kMaxLong];                  // wave-merged entries: position, source, count
@@ -1078,17 +1079,16 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
-      cnt[j] = v[j] >= 0 ? 1 : 0;
-      first[j] = u32x4{0, 0, 0, 0};
-      if (v[j] < 0 && v[j] != INT32_MIN) {
-        const int o = -1 - v[j];
-        if (o < kMissBytes) {
-          cnt[j] = mto[o];
-          first[j] = *reinterpret_cast<const u32x4 *>(res + o);
-        } else {
-          cnt[j] = a.mt[c * kMaxLong + (o - kMissBytes)];
-        }
-      }
+      // a merge-loop entry's count and first four tokens; other pre-tokens
+      // read entry 0 (the loads stay unconditional)
+      const int o = -1 - v[j];
+      const bool lane_merged = v[j] < 0 && v[j] != INT32_MIN && o < kMissBytes;
+      const int oo = lane_merged ? o : 0;
+      const int32_t m = mto[oo];
+      first[j] = *reinterpret_cast<const u32x4 *>(res + oo);
+      cnt[j] = v[j] >= 0 ? 1 : (lane_merged ? m : 0);
+      if (v[j] < 0 && v[j] != INT32_MIN && !lane_merged)
+        cnt[j] = a.mt[c * kMaxLong + (o - kMissBytes)];
     }
     // positions: every pass of the round is one scan over the workgroup
     int32_t inc[kEmitPasses];
@@ -1115,28 +1115,27 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
     carry = run;
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
+      // the tokens of a pre-token that does not run past the window all fall
+      // below kOutCap: its first four by unconditional stores (the unused
+      // ones to the spare slot), the rest of a longer lane-merged entry after
       const int k = r0 + j * EWG + tid;
-      if (k >= n_pt) continue;
-      s.pos[k] = (uint16_t)w0[j];
       const int32_t x = v[j];
-      int64_t w = w0[j];
-      if (x >= 0) {
-        put(w, x);
-        continue;
-      }
       const int o = -1 - x;
-      if (o < kMissBytes) {
-        const int nt = cnt[j];
-        put(w, (int32_t)first[j].x);
-        if (nt > 1) put(w + 1, (int32_t)first[j].y);
-        if (nt > 2) put(w + 2, (int32_t)first[j].z);
-        if (nt > 3) put(w + 3, (int32_t)first[j].w);
-        for (int t = 4; t < nt; ++t) put(w + t, res[o + t]);
-      } else {
+      const bool placed = k < n_pt && (x >= 0 || o < kMissBytes);
+      const int nt = placed ? cnt[j] : 0;
+      const int w = (int)w0[j];
+      const u32x4 t = x >= 0 ? u32x4{(uint32_t)x, 0u, 0u, 0u} : first[j];
+      s.out[nt > 0 ? w : kOutCap] = (int32_t)t.x;
+      s.out[nt > 1 ? w + 1 : kOutCap] = (int32_t)t.y;
+      s.out[nt > 2 ? w + 2 : kOutCap] = (int32_t)t.z;
+      s.out[nt > 3 ? w + 3 : kOutCap] = (int32_t)t.w;
+      for (int q = 4; q < nt; ++q) s.out[w + q] = res[o + q];
+      if (k < n_pt) s.pos[k] = (uint16_t)w;
+      if (k < n_pt && x < 0 && o >= kMissBytes) {
         const int q = o - kMissBytes;
         const uint32_t e = a.miss[c * kMissMax + kBucketBase[3] + q];
         const int slot = atomicAdd(&s.n_long, 1);
-        s.lw[slot] = w;
+        s.lw[slot] = w0[j];
         s.lsrc[slot] = c0 + me_start(e);
         s.lnt[slot] = cnt[j];
       }
@@ -1152,9 +1151,13 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   __syncthreads();
   // the staged positions, in order
   const int nst = (int)min(total, (int64_t)kOutCap);
-  for (int k = tid; k < nst; k += EWG) {
-    if (base + k < a.ids_cap) a.ids[base + k] = out_id(a.id_map, s.out[k]);
-    else overflow = true;
+  if (base + nst <= a.ids_cap) {
+    for (int k = tid; k < nst; k += EWG) a.ids[base + k] = out_id(a.id_map, s.out[k]);
+  } else {
+    for (int k = tid; k < nst; k += EWG) {
+      if (base + k < a.ids_cap) a.ids[base + k] = out_id(a.id_map, s.out[k]);
+      else overflow = true;
+    }
   }
   if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
   // per-document offsets: a document starting at pre-token k begins at k's
