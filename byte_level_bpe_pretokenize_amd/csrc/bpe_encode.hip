@@ -182,21 +182,6 @@ __device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, cons
   return n;
 }
 
-// The len <= 4 * NW bytes at p as NW little-endian words (bytes past len are
-// whatever follows in memory): aligned 4-byte loads and byte shifts.  Reads
-// up to 3 bytes before p and 4 after the last word.
-template <int NW>
-__device__ __forceinline__ void load_words(const uint8_t *p, uint32_t *w) {
-  const uintptr_t ad = (uintptr_t)p;
-  const uint32_t *q = reinterpret_cast<const uint32_t *>(ad & ~(uintptr_t)3);
-  const uint32_t sh = (uint32_t)(ad & 3);
-  uint32_t raw[NW + 1];
-#pragma unroll
-  for (int i = 0; i <= NW; ++i) raw[i] = q[i];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) w[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
-}
-
 // The same rounds with the whole workgroup (NT threads) on Y[0..n), RK
 // scratch (global, position-indexed).  The lowest rank r is a workgroup
 // minimum; runs of consecutive pairs with rank r (only possible for a pair
@@ -342,13 +327,12 @@ struct FindShared {
   uint32_t SB[SB_WORDS];                 // pre-token start bits, positions [0, WIN]
   uint32_t DB[DB_WORDS];                 // document start bits, positions [-32, WIN)
   uint16_t PS[kChunk + 2];               // owned pre-token starts in order, then the end
-  alignas(16) uint8_t MB[kMissBytes + 16];  // lane-merged entries' bytes, back to back
   u32x4 LM[kShortMax + 1];               // masks of the first len bytes of three words
   Red<WG> r;
   int64_t o_lo, o_hi;
   int e_last;
   int cnt[kBuckets];                     // merge-loop list entries per bucket
-  int nbytes;                            // bytes of the lane-merged entries
+  int nbytes;                            // span of the lane-merged entries' dense region
 };
 
 __device__ __forceinline__ uint32_t sb16(const FindShared &s, int g) {
@@ -375,19 +359,25 @@ __device__ __forceinline__ void pretoken_words(const FindShared &s, int st, int 
   }
 }
 
-// Symbol of a pre-token of 2..kShortMax bytes at window position st in the
-// short word table, or -1.
-__device__ __forceinline__ int32_t short_lookup(const FindShared &s, const EncodeArgs &a, int st,
-                                                int len) {
+// The first kShortMax bytes at window position st as three little-endian
+// words, the bytes past len zeroed.
+__device__ __forceinline__ void short_words(const FindShared &s, int st, int len, uint32_t &w0,
+                                            uint32_t &w1, uint32_t &w2) {
   const int b0 = 16 + st;
   const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
   const int q = b0 >> 2;
   const uint32_t sh = (uint32_t)(b0 & 3);
   const uint32_t r0 = B32[q], r1 = B32[q + 1], r2 = B32[q + 2], r3 = B32[q + 3];
-  const u32x4 m = s.LM[len];
-  const uint32_t w0 = __builtin_amdgcn_alignbyte(r1, r0, sh) & m.x;
-  const uint32_t w1 = __builtin_amdgcn_alignbyte(r2, r1, sh) & m.y;
-  const uint32_t w2 = __builtin_amdgcn_alignbyte(r3, r2, sh) & m.z;
+  const u32x4 m = s.LM[min(len, kShortMax)];
+  w0 = __builtin_amdgcn_alignbyte(r1, r0, sh) & m.x;
+  w1 = __builtin_amdgcn_alignbyte(r2, r1, sh) & m.y;
+  w2 = __builtin_amdgcn_alignbyte(r3, r2, sh) & m.z;
+}
+
+// Symbol of a pre-token of 2..kShortMax bytes (words w0..w2) in the short
+// word table, or -1.
+__device__ __forceinline__ int32_t short_lookup(const EncodeArgs &a, uint32_t w0, uint32_t w1,
+                                                uint32_t w2, int len) {
   const uint32_t x = short_mix(w0, w1, w2, (uint32_t)len, a.word_seed);
   const uint32_t tl = (uint32_t)len << 21;
   const u32x4 *tab = reinterpret_cast<const u32x4 *>(a.words);
@@ -574,16 +564,19 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   //    by LDS atomics: pv names the entry, so order does not matter)
   int32_t *pv = a.pv + c * kChunk;
   uint32_t *ml = a.miss + c * kMissMax;
+  uint32_t *mb = reinterpret_cast<uint32_t *>(a.mbytes + c * kMissSpan);
   for (int k = tid; k < n_pt; k += WG) {
     const bool over = overhang && k == n_pt - 1;
     const int st = s.PS[k];
     const int len = over ? 0 : (int)s.PS[k + 1] - st;
+    uint32_t w0, w1, w2;
+    short_words(s, st, len, w0, w1, w2);
     int32_t v = -1;
     if (len == 1) {
-      v = s.B[16 + st];
+      v = (int32_t)w0;
     } else if (!over) {
       if (len <= kShortMax) {
-        if (a.words) v = short_lookup(s, a, st, len);
+        if (a.words) v = short_lookup(a, w0, w1, w2, len);
       } else if (len <= kWordMax && a.lwords) {
         v = long_lookup(s, a, st, len);
       }
@@ -596,23 +589,29 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     const int idx = atomicAdd(&s.cnt[b], 1);
     const int base = b == 0 ? kBucketBase[0] : b == 1 ? kBucketBase[1] : b == 2 ? kBucketBase[2] : kBucketBase[3];
     if (b < 3) {
-      const int o = atomicAdd(&s.nbytes, len);
-      for (int j = 0; j < len; ++j) s.MB[o + j] = s.B[16 + st + j];
-      ml[base + idx] = miss_entry(o, len, false);
+      // the bytes, as words at a 4-byte aligned offset of the dense region
+      const int o = atomicAdd(&s.nbytes, (len + 3) & ~3);
+      uint32_t *dst = mb + (o >> 2);
+      if (len <= kShortMax) {
+        dst[0] = w0;
+        if (len > 4) dst[1] = w1;
+        if (len > 8) dst[2] = w2;
+      } else {
+        const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
+        const int q = (16 + st) >> 2;
+        const uint32_t sh = (uint32_t)((16 + st) & 3);
+        for (int i = 0; 4 * i < len; ++i)
+          dst[i] = __builtin_amdgcn_alignbyte(B32[q + i + 1], B32[q + i], sh);
+      }
+      ml[base + idx] = miss_entry(o >> 2, len, false);
       pv[k] = -1 - o;
     } else {
       ml[base + idx] = miss_entry(st, len, over);
-      pv[k] = -1 - kMissBytes - idx;
+      pv[k] = -1 - kMissSpan - idx;
     }
   }
   const bool any_bad = __syncthreads_or(bad);
-  // the dense bytes, 16 per store
   const int nbytes = s.nbytes;
-  {
-    u32x4 *dst = reinterpret_cast<u32x4 *>(a.mbytes + c * kMissBytes);
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(s.MB);
-    for (int i = tid; 16 * i < nbytes; i += WG) dst[i] = src[i];
-  }
   if (tid == 0) {
     int32_t *m = a.meta + kMetaInts * c;
     int n_miss = 0;
@@ -721,11 +720,13 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
       }
     const int64_t c = G.cg + f;
     const uint32_t e = a.miss[c * kMissMax + idx];
-    const int o = me_start(e);
+    const int o = me_start(e) << 2;  // 4-byte aligned
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(a.mbytes + c * kMissSpan + o);
     uint32_t w[W / 4];
-    load_words<W / 4>(a.mbytes + c * kMissBytes + o, w);
-    const int nt = lane_merge<W>(w, me_len(e), L, t, a.pair_rank, a.res + c * kMissBytes + o);
-    a.mto[c * kMissBytes + o] = (uint8_t)nt;
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) w[i] = src[i];
+    const int nt = lane_merge<W>(w, me_len(e), L, t, a.pair_rank, a.res + c * kMissSpan + o);
+    a.mto[c * kMissSpan + o] = (uint8_t)nt;
     tok += (uint64_t)nt << (16 * f);
   }
   return tok;
@@ -1045,8 +1046,8 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int64_t c = blockIdx.x;
   const int64_t c0 = c * kChunk;
   const int32_t *pv = a.pv + c * kChunk;
-  const int32_t *res = a.res + c * kMissBytes;
-  const uint8_t *mto = a.mto + c * kMissBytes;
+  const int32_t *res = a.res + c * kMissSpan;
+  const uint8_t *mto = a.mto + c * kMissSpan;
   // loads that need nothing else first: the first round's pv values (pv has
   // room for kChunk entries, so this reads inside it whatever the count), and
   // the first pre-token of the documents that start here
@@ -1082,13 +1083,13 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       // a merge-loop entry's count and first four tokens; other pre-tokens
       // read entry 0 (the loads stay unconditional)
       const int o = -1 - v[j];
-      const bool lane_merged = v[j] < 0 && v[j] != INT32_MIN && o < kMissBytes;
+      const bool lane_merged = v[j] < 0 && v[j] != INT32_MIN && o < kMissSpan;
       const int oo = lane_merged ? o : 0;
       const int32_t m = mto[oo];
       first[j] = *reinterpret_cast<const u32x4 *>(res + oo);
       cnt[j] = v[j] >= 0 ? 1 : (lane_merged ? m : 0);
       if (v[j] < 0 && v[j] != INT32_MIN && !lane_merged)
-        cnt[j] = a.mt[c * kMaxLong + (o - kMissBytes)];
+        cnt[j] = a.mt[c * kMaxLong + (o - kMissSpan)];
     }
     // positions: every pass of the round is one scan over the workgroup
     int32_t inc[kEmitPasses];
@@ -1121,7 +1122,7 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       const int k = r0 + j * EWG + tid;
       const int32_t x = v[j];
       const int o = -1 - x;
-      const bool placed = k < n_pt && (x >= 0 || o < kMissBytes);
+      const bool placed = k < n_pt && (x >= 0 || o < kMissSpan);
       const int nt = placed ? cnt[j] : 0;
       const int w = (int)w0[j];
       const u32x4 t = x >= 0 ? u32x4{(uint32_t)x, 0u, 0u, 0u} : first[j];
@@ -1131,8 +1132,8 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       s.out[nt > 3 ? w + 3 : kOutCap] = (int32_t)t.w;
       for (int q = 4; q < nt; ++q) s.out[w + q] = res[o + q];
       if (k < n_pt) s.pos[k] = (uint16_t)w;
-      if (k < n_pt && x < 0 && o >= kMissBytes) {
-        const int q = o - kMissBytes;
+      if (k < n_pt && x < 0 && o >= kMissSpan) {
+        const int q = o - kMissSpan;
         const uint32_t e = a.miss[c * kMissMax + kBucketBase[3] + q];
         const int slot = atomicAdd(&s.n_long, 1);
         s.lw[slot] = w0[j];

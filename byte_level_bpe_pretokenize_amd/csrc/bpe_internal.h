@@ -145,6 +145,9 @@ constexpr int kWinMax = 64;
 
 // Per-chunk records of the encode pipeline.
 constexpr int kMissBytes = kChunk + kHalo;  // bytes of a chunk's lane-merged pre-tokens, at most
+// Their dense region: each entry at a 4-byte aligned offset (at most twice
+// its bytes, entries being at least 2 bytes long).
+constexpr int kMissSpan = 2 * kMissBytes;
 constexpr int kMaxLong = kChunk / (kLaneMax + 1) + 4;  // wave-merged pre-tokens per chunk, at most
 // The merge-loop list of a chunk: one region per length bucket (2-8, 9-16,
 // 17-32 bytes, then longer or running past the window), each sized for the
@@ -160,7 +163,7 @@ constexpr int kMetaInts = 8;
 constexpr int kMetaPretokens = 0;  // pre-tokens that start in the chunk
 constexpr int kMetaMisses = 1;     // of which on the merge-loop list
 constexpr int kMetaStatus = 2;     // status bits found by the chunk
-constexpr int kMetaBytes = 3;      // bytes of the lane-merged entries
+constexpr int kMetaBytes = 3;      // span of the lane-merged entries' dense region
 constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
 
 // Encode workspace, all regions 256-byte aligned:
@@ -172,16 +175,17 @@ constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
 //   doc_pt    [D] i32   index of each document's first pre-token in its chunk
 //   pv        [G][kChunk] i32    per pre-token: its symbol; -1 - o for a
 //                                lane-merged one whose bytes start at o in
-//                                mbytes; -1 - kMissBytes - q for the q-th
+//                                mbytes; -1 - kMissSpan - q for the q-th
 //                                wave-merged one
 //   miss      [G][kMissMax] u32  merge-loop list, a region per length bucket
 //                                (kBucketBase), in no particular order:
-//                                o | len << 13 (lane-merged), start | len << 13 |
+//                                o / 4 | len << 13 (lane-merged), start | len << 13 |
 //                                overhang << 26 (wave-merged)
 //   mt        [G][kMaxLong] i32  token count of each wave-merged entry
-//   mbytes    [G][kMissBytes] u8   bytes of the lane-merged entries, back to back
-//   mto       [G][kMissBytes] u8   token count of the lane-merged entry at o
-//   res       [G][kMissBytes] i32  its tokens, from o on
+//   mbytes    [G][kMissSpan] u8   bytes of the lane-merged entries, each at a
+//                                  4-byte aligned offset o
+//   mto       [G][kMissSpan] u8   token count of the lane-merged entry at o
+//   res       [G][kMissSpan] i32  its tokens, from o on
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the wave merge, position-indexed
 struct EncLayout {
@@ -204,9 +208,9 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.pv = take(4 * (size_t)kChunk * G);
   L.miss = take(4 * (size_t)kMissMax * G);
   L.mt = take(4 * (size_t)kMaxLong * G);
-  L.mbytes = take((size_t)kMissBytes * G + 64);  // word loads read a little past the end
-  L.mto = take((size_t)kMissBytes * G);
-  L.res = take(4 * (size_t)kMissBytes * G + 64);
+  L.mbytes = take((size_t)kMissSpan * G + 64);  // word loads read a little past the end
+  L.mto = take((size_t)kMissSpan * G);
+  L.res = take(4 * (size_t)kMissSpan * G + 64);
   L.gsym = take(4 * (size_t)n_bytes);
   L.grank = take(4 * (size_t)n_bytes);
   L.total = o;
