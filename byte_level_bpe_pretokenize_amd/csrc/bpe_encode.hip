@@ -37,8 +37,7 @@ constexpr int WG = kEncThreads;             // k_find: 4 waves
 constexpr int MWG = 64;                     // k_merge: one wave per chunk
 constexpr int OWG = 1024;                   // k_offsets: one workgroup
 constexpr int WIN = kChunk + kHalo;         // window positions [0, WIN)
-constexpr int SB_HALF = WIN / 16 + 1;       // 16-bit start masks for positions [0, WIN]
-constexpr int SB_WORDS = (SB_HALF + 1) / 2 + 1;
+constexpr int SB_WORDS = kChunk / 32;       // start bits of the owned positions
 constexpr int DB_OFF = 32;                  // document-start bit of position p is bit p + DB_OFF
 constexpr int DB_WORDS = (WIN + DB_OFF) / 32 + 2;
 
@@ -269,62 +268,94 @@ __device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const RankTable 
   return n;
 }
 
-// ---- start bits, four bytes per operation --------------------------------------
-// Per-byte flags live in the high bit of each byte of a 32-bit word.
-
-__device__ __forceinline__ uint32_t spread4(uint32_t nib) {  // bit k -> bit 8k + 7
-  return (nib * 0x10204080u) & 0x80808080u;
-}
-__device__ __forceinline__ uint32_t pack4(uint32_t m) {  // bit 8k + 7 -> bit k
-  return ((((m >> 7) & 0x01010101u) * 0x01020408u) >> 24) & 0xFu;
-}
+// ---- start bits ------------------------------------------------------------------
 
 // Pre-token start bits of the positions 16g .. 16g + 15 (bit k: position
 // 16g + k) from the 20 bytes at positions 16g - 4 .. 16g + 15 (w[0]: the four
-// before) and the document-start bits doc (bit k + 1: position 16g + k, bit
-// 0: position 16g - 1).  A position starts a pre-token when it starts a
-// document, or when its class differs from the byte before's, unless it is a
-// letter after a single space that follows a non-whitespace byte (or starts
-// its document).  Classes: letters A-Z, a-z and bytes >= 0x80; digits;
-// whitespace 0x09-0x0D and 0x20; punctuation, the rest.
+// before, then four words in order) and the document-start bits doc (bit
+// k + 1: position 16g + k, bit 0: position 16g - 1).  A position starts a
+// pre-token when it starts a document, or when its class differs from the
+// byte before's, unless it is a letter after a single space that follows a
+// non-whitespace byte (or starts its document).  Classes: letters A-Z, a-z
+// and bytes >= 0x80; digits; whitespace 0x09-0x0D and 0x20; punctuation, the
+// rest.
+//
+// The 16 bytes are first transposed so that byte j of word k is position
+// 4j + k: the byte one position back is then the same byte of word k - 1.
+// Class flags live in bit 7 of each byte (range tests by byte-wise adds of
+// 7-bit values); the lower bits carry no meaning until the final mask.
 __device__ __forceinline__ uint32_t start_bits16(const uint32_t w[5], uint32_t doc) {
   constexpr uint32_t H = 0x80808080u, M7 = 0x7F7F7F7Fu;
-  uint32_t L[5], D[5], W[5], P[5], S[5];
+  const uint32_t t0 = __builtin_amdgcn_perm(w[2], w[1], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(w[2], w[1], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(w[4], w[3], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(w[4], w[3], 0x07030602u);
+  uint32_t x[5];
+  x[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  x[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  x[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  x[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+  x[4] = w[0];  // positions 16g - 4 .. 16g - 1, in order
+  uint32_t L[5], D[5], W[5], S[5];
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
-    const uint32_t x = w[k], hi = x & H, z = x & M7;
-    const uint32_t y = (x | 0x20202020u) & M7;  // ASCII letters folded to lower case
-    L[k] = hi | ((y + 0x1F1F1F1Fu) & ~(y + 0x05050505u) & H);      // 'a' <= y <= 'z'
-    D[k] = (z + 0x50505050u) & ~(z + 0x46464646u) & H & ~hi;        // '0' <= z <= '9'
-    const uint32_t tb = (z + 0x77777777u) & ~(z + 0x72727272u) & H & ~hi;  // 0x09..0x0D
-    const uint32_t v = x ^ 0x20202020u;
-    S[k] = ~(((v & M7) + M7) | v) & H;  // byte == 0x20
-    W[k] = tb | S[k];
-    P[k] = H & ~(L[k] | D[k] | W[k]);
+    const uint32_t v = x[k], z = v & M7;
+    const uint32_t y = (v | 0x20202020u) & M7;                   // letters folded to lower case
+    L[k] = ((y + 0x1F1F1F1Fu) & ~(y + 0x05050505u)) | v;         // 'a'..'z', or >= 0x80
+    D[k] = (z + 0x50505050u) & ~(z + 0x46464646u) & ~v;           // '0'..'9'
+    S[k] = (z + 0x60606060u) & ~(z + 0x5F5F5F5Fu) & ~v;           // 0x20
+    W[k] = ((z + 0x77777777u) & ~(z + 0x72727272u) & ~v) | S[k]; // 0x09..0x0D, or 0x20
   }
-  uint32_t out = 0;
+  // the flags one and two positions back: word k - 1 (k - 2), or for the
+  // first words the last word shifted up one byte, the earlier bytes first
+  uint32_t ne[4], att[4], W2[4];
 #pragma unroll
-  for (int k = 1; k < 5; ++k) {
-    // the same flags one and two bytes earlier
-#define PREV1(m) (((m)[k] << 8) | ((m)[k - 1] >> 24))
-#define PREV2(m) (((m)[k] << 16) | ((m)[k - 1] >> 16))
-    const uint32_t eq = (L[k] & PREV1(L)) | (D[k] & PREV1(D)) | (W[k] & PREV1(W)) |
-                        (P[k] & PREV1(P));
-    const uint32_t d0 = spread4((doc >> (4 * (k - 1) + 1)) & 0xFu);
-    const uint32_t d1 = spread4((doc >> (4 * (k - 1))) & 0xFu);
-    const uint32_t attach = L[k] & PREV1(S) & (d1 | (~PREV2(W) & H));
-#undef PREV1
-#undef PREV2
-    out |= pack4(d0 | (~eq & ~attach & H)) << (4 * (k - 1));
+  for (int k = 0; k < 4; ++k) {
+    uint32_t L1, D1, W1, S1;
+    if (k == 0) {
+      L1 = __builtin_amdgcn_alignbyte(L[3], L[4], 3);
+      D1 = __builtin_amdgcn_alignbyte(D[3], D[4], 3);
+      W1 = __builtin_amdgcn_alignbyte(W[3], W[4], 3);
+      S1 = __builtin_amdgcn_alignbyte(S[3], S[4], 3);
+      W2[k] = __builtin_amdgcn_alignbyte(W[2], W[4] << 8, 3);
+    } else {
+      L1 = L[k - 1];
+      D1 = D[k - 1];
+      W1 = W[k - 1];
+      S1 = S[k - 1];
+      W2[k] = k == 1 ? __builtin_amdgcn_alignbyte(W[3], W[4], 3) : W[k - 2];
+    }
+    ne[k] = (L[k] ^ L1) | (D[k] ^ D1) | (W[k] ^ W1);
+    att[k] = L[k] & S1;
   }
-  return out;
+  uint32_t F[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) F[k] = ne[k] & ~(att[k] & ~W2[k]) & H;
+  if (doc) {
+    // a document start is a start, and a space that starts its document
+    // leads the letter after it
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t d0 = 0, d1 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d0 |= ((doc >> (4 * j + k + 1)) & 1u) << (8 * j + 7);
+        d1 |= ((doc >> (4 * j + k)) & 1u) << (8 * j + 7);
+      }
+      F[k] = (d0 | (ne[k] & ~(att[k] & (d1 | ~W2[k])))) & H;
+    }
+  }
+  // bit 8j + k of X is position 4j + k; then the four nibbles side by side
+  const uint32_t X = (F[0] >> 7) | (F[1] >> 6) | (F[2] >> 5) | (F[3] >> 4);
+  const uint32_t t = X | (X >> 4);
+  return (t & 0xFFu) | ((t >> 8) & 0xFF00u);
 }
 
 // ---- k_find -------------------------------------------------------------------
 
 struct FindShared {
   alignas(16) uint8_t B[16 + WIN + 32];  // B[16 + p] = byte at window position p
-  uint32_t SB[SB_WORDS];                 // pre-token start bits, positions [0, WIN]
+  uint32_t SB[SB_WORDS];                 // pre-token start bits, positions [0, kChunk)
   uint32_t DB[DB_WORDS];                 // document start bits, positions [-32, WIN)
   uint16_t PS[kChunk + 2];               // owned pre-token starts in order, then the end
   u32x4 LM[kShortMax + 1];               // masks of the first len bytes of three words
@@ -334,6 +365,11 @@ struct FindShared {
   int cnt[kBuckets];                     // merge-loop list entries per bucket
   int nbytes;                            // span of the lane-merged entries' dense region
 };
+
+__device__ __forceinline__ bool db_bit(const FindShared &s, int p) {
+  const int q = p + DB_OFF;
+  return (s.DB[q >> 5] >> (q & 31)) & 1u;
+}
 
 __device__ __forceinline__ uint32_t sb16(const FindShared &s, int g) {
   return reinterpret_cast<const uint16_t *>(s.SB)[g];
@@ -506,10 +542,11 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   }
   __syncthreads();
 
-  // 2. start bits: a document start, or a class change unless a single space
-  //    that follows a non-whitespace byte (or opens the document) leads a
-  //    letter run.  Positions past the input end read as starts.
-  for (int g = tid; g < SB_HALF; g += WG) {
+  // 2. start bits of the owned positions: a document start, or a class
+  //    change unless a single space that follows a non-whitespace byte (or
+  //    opens the document) leads a letter run.  Positions past the input end
+  //    read as starts.
+  for (int g = tid; g < kChunk / 16; g += WG) {
     // this thread's 16 bytes, the 4 before them, and the document-start bits
     // of positions 16g - 1 .. 16g + 15, from LDS in four reads
     const u32x4 cur = *reinterpret_cast<const u32x4 *>(&s.B[16 + 16 * g]);
@@ -538,14 +575,25 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     const int lim = nown - 16 * tid;
     if (lim < 16) own &= (1u << lim) - 1;
   }
-  if (tid == 0) {
-    int e = kNoStart;
-    for (int g = nown >> 4; g < SB_HALF && e == kNoStart; ++g) {
-      uint32_t m = sb16(s, g);
-      if (g == (nown >> 4)) m &= 0xFFFFu << (nown & 15);
-      if (m) e = 16 * g + __ffs(m) - 1;
+  if (wave == 0) {
+    // one position per lane, nown .. nown + 63 (the halo), by the same rule
+    const int p = nown + lane;
+    bool st;
+    if (p >= nwin) {
+      st = win_reaches_end;
+    } else {
+      const uint32_t b0 = s.B[16 + p], b1 = s.B[16 + p - 1], b2 = s.B[16 + p - 2];
+      const uint32_t c0 = byte_class(b0), c1 = byte_class(b1);
+      const bool d0 = db_bit(s, p), d1 = db_bit(s, p - 1);
+      const bool attach = c0 == kL && b1 == 0x20u && (d1 || byte_class(b2) != kW);
+      st = d0 || (c0 != c1 && !attach);
     }
-    s.e_last = e <= WIN ? e : kNoStart;
+    const uint64_t m = __ballot(st);
+    if (lane == 0) {
+      int e = m ? nown + __ffsll((unsigned long long)m) - 1
+                : ((win_reaches_end && nwin == WIN) ? WIN : kNoStart);
+      s.e_last = e <= WIN ? e : kNoStart;
+    }
   }
   int n_pt;
   {
