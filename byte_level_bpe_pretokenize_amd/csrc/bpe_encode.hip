@@ -87,6 +87,28 @@ struct LaneCols {
   uint32_t k[W - 1][64];  // key of the pair (position, next live position)
 };
 
+// Rank of a byte pair from the direct table in device memory.
+struct GlobalPairs {
+  const int32_t *__restrict__ pair_rank;
+  __device__ __forceinline__ int32_t operator()(uint32_t x, uint32_t y) const {
+    return pair_rank[(x << 8) | y];
+  }
+};
+
+// Rank of a byte pair from a copy in LDS of the ASCII pairs' ranks (1 + rank,
+// 0 for none), the others and ranks from 0xFFFE on from device memory.
+struct AsciiPairs {
+  const uint16_t *pa;  // LDS
+  const int32_t *__restrict__ pair_rank;
+  __device__ __forceinline__ int32_t operator()(uint32_t x, uint32_t y) const {
+    if ((x | y) < 128u) {
+      const uint32_t u = pa[(x << 7) | y];
+      if (u != 0xFFFFu) return u == 0 ? kRankInf : (int32_t)u - 1;
+    }
+    return pair_rank[(x << 8) | y];
+  }
+};
+
 // Merge one pre-token of len <= W bytes (little-endian words w) by one lane
 // and write its symbols to out; returns their count.  A round takes the
 // lowest rank r and merges its pairs left to right without overlap; here the
@@ -96,9 +118,9 @@ struct LaneCols {
 // still present are exactly the rest of the round's.  Positions never move:
 // a consumed position leaves the live mask, and each pair joins a live
 // position to the next live one.
-template <int W>
+template <int W, class Pairs>
 __device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, const RankTable &t,
-                          const int32_t *__restrict__ pair_rank, int32_t *out) {
+                          const Pairs &pair_rank, int32_t *out) {
   const int lane = lane_id();
   uint32_t *S = &L.s[0][lane];
   uint32_t *K = &L.k[0][lane];
@@ -112,7 +134,7 @@ __device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, cons
   int32_t r0[W - 1];
 #pragma unroll
   for (int j = 0; j + 1 < W; ++j)
-    r0[j] = (j + 1 < len) ? pair_rank[(b[j] << 8) | b[j + 1]] : kRankInf;
+    r0[j] = (j + 1 < len) ? pair_rank(b[j], b[j + 1]) : kRankInf;
 #pragma unroll
   for (int j = 0; j + 1 < W; ++j)
     K[64 * j] = r0[j] == kRankInf ? kKeyNone : (((uint32_t)r0[j] << 5) | (uint32_t)j);
@@ -724,9 +746,9 @@ struct LaneGroup {
   int cnt[kGroup][kBuckets];
 };
 
-__device__ __forceinline__ bool lane_group(const EncodeArgs &a, LaneGroup &G) {
-  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
-  G.cg = ((int64_t)blockIdx.x * kMergeWaves + wv) * kGroup;
+// Group q (chunks kGroup q ..) of the merge-loop lists; false past the last.
+__device__ __forceinline__ bool lane_group(const EncodeArgs &a, int64_t q, LaneGroup &G) {
+  G.cg = q * kGroup;
   if (G.cg >= a.n_chunks) return false;
   G.nf = (int)min<int64_t>(kGroup, a.n_chunks - G.cg);
 #pragma unroll
@@ -737,13 +759,18 @@ __device__ __forceinline__ bool lane_group(const EncodeArgs &a, LaneGroup &G) {
   return true;
 }
 
+__device__ __forceinline__ int64_t wave_group(int64_t first) {
+  return first + __builtin_amdgcn_readfirstlane(wave_id());
+}
+
 // Bucket b of the group's lists, one pre-token per lane with W-wide LDS
 // columns, 64 entries per batch.  An entry's bytes are read from its chunk's
 // dense mbytes region and its tokens written to res at the same offset (never
 // more tokens than bytes, so entries do not overlap), their count to mto at
 // that offset; the return value holds the tokens per chunk, 16 bits each.
-template <int W>
-__device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b, LaneCols<W> &L) {
+template <int W, class Pairs>
+__device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b, LaneCols<W> &L,
+                                 const Pairs &pairs) {
   const int lane = lane_id();
   const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
   // per chunk: entries of the bucket before the chunk's (uniform across the wave)
@@ -773,7 +800,7 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
     uint32_t w[W / 4];
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) w[i] = src[i];
-    const int nt = lane_merge<W>(w, me_len(e), L, t, a.pair_rank, a.res + c * kMissSpan + o);
+    const int nt = lane_merge<W>(w, me_len(e), L, t, pairs, a.res + c * kMissSpan + o);
     a.mto[c * kMissSpan + o] = (uint8_t)nt;
     tok += (uint64_t)nt << (16 * f);
   }
@@ -785,25 +812,49 @@ __device__ __forceinline__ uint64_t wave_tok_sum(uint64_t tok) {
   return wave_sum(tok);
 }
 
+constexpr int kMergePWaves = 16;  // waves of a persistent k_merge workgroup, one per CU
+
+struct PMergeShared {
+  LaneCols<16> cols[kMergePWaves];
+  uint16_t pa[128 * 128];  // ranks of the ASCII byte pairs
+  int next;                // next group of this workgroup's share
+};
+
 // Merge-loop lists of kGroup consecutive chunks per wave, buckets 0 (2-8
 // bytes) and 1 (9-16 bytes).  The entries of one bucket are taken 64 at a
 // time across the chunks, so every lane of a batch runs the same merge width.
 // tot[c] gets the chunk's count so far (its resolved pre-tokens and these
-// buckets) with its status bits on top.
-__global__ void __launch_bounds__(MWG *kMergeWaves) k_merge(EncodeArgs a) {
-  __shared__ LaneCols<16> cols[kMergeWaves];
-  LaneGroup G;
-  if (!lane_group(a, G)) return;
-  LaneCols<16> &L = cols[wave_id()];
-  uint64_t tok = merge_bucket<8>(a, G, 0, *reinterpret_cast<LaneCols<8> *>(&L));
-  tok += merge_bucket<16>(a, G, 1, L);
-  tok = wave_tok_sum(tok);
-  const int lane = lane_id();
-  if (lane < G.nf) {
-    const int64_t c = G.cg + lane;
-    const int32_t *m = a.meta + kMetaInts * c;
-    const int64_t t = (int64_t)(m[kMetaPretokens] - m[kMetaMisses]) + (int64_t)((tok >> (16 * lane)) & 0xFFFFu);
-    a.tot[c] = t | ((int64_t)m[kMetaStatus] << kCountBits);
+// buckets) with its status bits on top.  One workgroup per compute unit,
+// kMergePWaves waves that take the groups of its share (every gridDim.x-th)
+// one at a time; the initial ranks of ASCII byte pairs come from an LDS copy.
+__global__ void __launch_bounds__(MWG *kMergePWaves) k_merge(EncodeArgs a) {
+  __shared__ PMergeShared s;
+  const int tid = threadIdx.x, lane = lane_id();
+  {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.pair_ascii);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(s.pa);
+    for (int i = tid; i < 128 * 128 * 2 / 16; i += MWG * kMergePWaves) dst[i] = src[i];
+    if (tid == 0) s.next = 0;
+  }
+  __syncthreads();
+  const AsciiPairs pairs{s.pa, a.pair_rank};
+  LaneCols<16> &L = s.cols[wave_id()];
+  for (;;) {
+    int q = 0;
+    if (lane == 0) q = atomicAdd(&s.next, 1);
+    q = __builtin_amdgcn_readfirstlane(__shfl(q, 0, 64));
+    LaneGroup G;
+    if (!lane_group(a, (int64_t)blockIdx.x + (int64_t)gridDim.x * q, G)) break;
+    uint64_t tok = merge_bucket<8>(a, G, 0, *reinterpret_cast<LaneCols<8> *>(&L), pairs);
+    tok += merge_bucket<16>(a, G, 1, L, pairs);
+    tok = wave_tok_sum(tok);
+    if (lane < G.nf) {
+      const int64_t c = G.cg + lane;
+      const int32_t *m = a.meta + kMetaInts * c;
+      const int64_t t = (int64_t)(m[kMetaPretokens] - m[kMetaMisses]) +
+                        (int64_t)((tok >> (16 * lane)) & 0xFFFFu);
+      a.tot[c] = t | ((int64_t)m[kMetaStatus] << kCountBits);
+    }
   }
 }
 
@@ -811,12 +862,12 @@ __global__ void __launch_bounds__(MWG *kMergeWaves) k_merge(EncodeArgs a) {
 __global__ void __launch_bounds__(MWG *kMergeWaves) k_merge_wide(EncodeArgs a) {
   __shared__ LaneCols<32> cols[kMergeWaves];
   LaneGroup G;
-  if (!lane_group(a, G)) return;
+  if (!lane_group(a, wave_group((int64_t)blockIdx.x * kMergeWaves), G)) return;
   int any = 0;
 #pragma unroll
   for (int f = 0; f < kGroup; ++f) any += G.cnt[f][2];
   if (any == 0) return;
-  uint64_t tok = wave_tok_sum(merge_bucket<32>(a, G, 2, cols[wave_id()]));
+  uint64_t tok = wave_tok_sum(merge_bucket<32>(a, G, 2, cols[wave_id()], GlobalPairs{a.pair_rank}));
   const int lane = lane_id();
   if (lane < G.nf) {
     const int32_t add = (int32_t)((tok >> (16 * lane)) & 0xFFFFu);
@@ -1253,7 +1304,9 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
   hipLaunchKernelGGL(k_find, dim3(G), dim3(WG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[1], stream);
   const unsigned LG = (G + kGroup * kMergeWaves - 1) / (kGroup * kMergeWaves);
-  hipLaunchKernelGGL(k_merge, dim3(LG), dim3(MWG * kMergeWaves), 0, stream, a);
+  const unsigned n_groups = (G + kGroup - 1) / kGroup;
+  hipLaunchKernelGGL(k_merge, dim3(min((unsigned)a.n_cu, n_groups)), dim3(MWG * kMergePWaves), 0,
+                     stream, a);
   if (ev) (void)hipEventRecord(ev[2], stream);
   hipLaunchKernelGGL(k_merge_wide, dim3(LG), dim3(MWG * kMergeWaves), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[3], stream);

@@ -244,6 +244,9 @@ struct EncodeArgs {
   uint32_t table_seed;
   const int32_t *id_map;     // nullptr = identity
   const int32_t *pair_rank;  // [65536]: rank of the byte pair (a, b) at a * 256 + b
+  const uint16_t *pair_ascii;  // [128 * 128]: for a, b < 128, 1 + rank of (a, b) at a * 128 + b;
+                               // 0: no merge; 0xFFFF: rank >= 0xFFFE, see pair_rank
+  int n_cu;                  // compute units (workgroups of the persistent merge kernel)
   const uint4 *words;        // short word table (one uint4 per slot); nullptr = none
   uint32_t word_mask;        // slots - 1
   uint32_t word_seed;
