@@ -710,6 +710,158 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   }
 }
 
+// Two pre-tokens per lane, merged as lane_merge does, their steps taken side
+// by side: both minimums, both pairs' symbols and all four new pairs' first
+// buckets are read before any write, so the latencies of the two overlap.
+// Entry A (words wa, la bytes) uses columns LA, entry B columns LB; an entry
+// with va / vb false is absent.  Returns the token counts in *nta, *ntb.
+template <int W, class Pairs>
+__device__ void lane_merge2(const uint32_t *wa, int la, bool va, int32_t *outa, int *nta,
+                            const uint32_t *wb, int lb, bool vb, int32_t *outb, int *ntb,
+                            LaneCols<W> &LA, LaneCols<W> &LB, const RankTable &t,
+                            const Pairs &pair_rank) {
+  const int lane = lane_id();
+  uint32_t *SA = &LA.s[0][lane], *KA = &LA.k[0][lane];
+  uint32_t *SB = &LB.s[0][lane], *KB = &LB.k[0][lane];
+  if (!va) la = 0;
+  if (!vb) lb = 0;
+  {
+    uint32_t ba[W], bb[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      ba[j] = (wa[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+      bb[j] = (wb[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+      SA[64 * j] = ba[j];
+      SB[64 * j] = bb[j];
+    }
+    int32_t ra[W - 1], rb[W - 1];
+#pragma unroll
+    for (int j = 0; j + 1 < W; ++j) {
+      ra[j] = (j + 1 < la) ? pair_rank(ba[j], ba[j + 1]) : kRankInf;
+      rb[j] = (j + 1 < lb) ? pair_rank(bb[j], bb[j + 1]) : kRankInf;
+    }
+#pragma unroll
+    for (int j = 0; j + 1 < W; ++j) {
+      KA[64 * j] = ra[j] == kRankInf ? kKeyNone : (((uint32_t)ra[j] << 5) | (uint32_t)j);
+      KB[64 * j] = rb[j] == kRankInf ? kKeyNone : (((uint32_t)rb[j] << 5) | (uint32_t)j);
+    }
+  }
+  uint32_t aliveA = la >= 32 ? ~0u : ((1u << la) - 1u);
+  uint32_t aliveB = lb >= 32 ? ~0u : ((1u << lb) - 1u);
+  uint32_t rcA = kKeyNone, rcB = kKeyNone;
+  bool defA = false, defB = false;
+  for (;;) {
+    uint32_t mA = kKeyNone, mB = kKeyNone;
+#pragma unroll
+    for (int j = 0; j + 1 < W; ++j) {
+      mA = min(mA, KA[64 * j]);
+      mB = min(mB, KB[64 * j]);
+    }
+    const bool goA = mA < kKeyDone, goB = mB < kKeyDone;
+    if (!goA && !goB) break;
+    const uint32_t rA = mA >> 5, rB = mB >> 5;
+    const bool fixA = defA && goA && rA != rcA, fixB = defB && goB && rB != rcB;
+    if (fixA || fixB) {
+      // a round is over: pairs it made join the next one
+      if (fixA) {
+#pragma unroll
+        for (int j = 0; j + 1 < W; ++j) KA[64 * j] &= ~kKeyDef;
+        defA = false;
+      }
+      if (fixB) {
+#pragma unroll
+        for (int j = 0; j + 1 < W; ++j) KB[64 * j] &= ~kKeyDef;
+        defB = false;
+      }
+      continue;
+    }
+    // positions: the merged pair (i, q), its live neighbours p and t
+    const int iA = goA ? (int)(mA & 31u) : 0, iB = goB ? (int)(mB & 31u) : 0;
+    const uint32_t abA = aliveA & (0xFFFFFFFEu << iA), abB = aliveB & (0xFFFFFFFEu << iB);
+    const int qA = goA ? __builtin_ctz(abA) : 0, qB = goB ? __builtin_ctz(abB) : 0;
+    const uint32_t reA = abA & (abA - 1u), reB = abB & (abB - 1u);
+    const uint32_t beA = aliveA & ((1u << iA) - 1u), beB = aliveB & ((1u << iB) - 1u);
+    const bool hpA = goA && beA != 0, htA = goA && reA != 0;
+    const bool hpB = goB && beB != 0, htB = goB && reB != 0;
+    const int pA = hpA ? 31 - __builtin_clz(beA) : iA, tA = htA ? __builtin_ctz(reA) : iA;
+    const int pB = hpB ? 31 - __builtin_clz(beB) : iB, tB = htB ? __builtin_ctz(reB) : iB;
+    const uint32_t spA = SA[64 * pA], stA = SA[64 * tA];
+    const uint32_t spB = SB[64 * pB], stB = SB[64 * tB];
+    const uint32_t zA = 256u + rA, zB = 256u + rB;
+    // the new pairs' ranks: four first buckets at once
+    const uint32_t xlA = pair_mix(spA, zA, t.seed), xrA = pair_mix(zA, stA, t.seed);
+    const uint32_t xlB = pair_mix(spB, zB, t.seed), xrB = pair_mix(zB, stB, t.seed);
+    const uint64_t klA = pair_key(spA, zA), krA = pair_key(zA, stA);
+    const uint64_t klB = pair_key(spB, zB), krB = pair_key(zB, stB);
+    const u64x2 none = {kEmptySlot, kEmptySlot};
+    u64x2 blA = none, brA = none, blB = none, brB = none;
+    if (hpA) blA = t.b[pair_bucket0(xlA, t.mask)];
+    if (htA) brA = t.b[pair_bucket0(xrA, t.mask)];
+    if (hpB) blB = t.b[pair_bucket0(xlB, t.mask)];
+    if (htB) brB = t.b[pair_bucket0(xrB, t.mask)];
+    int32_t rlA = bucket_rank(blA, klA), rrA = bucket_rank(brA, krA);
+    int32_t rlB = bucket_rank(blB, klB), rrB = bucket_rank(brB, krB);
+    const bool nlA = hpA && rlA == kRankInf && bucket_flag(blA);
+    const bool nrA = htA && rrA == kRankInf && bucket_flag(brA);
+    const bool nlB = hpB && rlB == kRankInf && bucket_flag(blB);
+    const bool nrB = htB && rrB == kRankInf && bucket_flag(brB);
+    if (nlA || nrA || nlB || nrB) {
+      if (nlA) blA = t.b[pair_bucket1(xlA, t.mask)];
+      if (nrA) brA = t.b[pair_bucket1(xrA, t.mask)];
+      if (nlB) blB = t.b[pair_bucket1(xlB, t.mask)];
+      if (nrB) brB = t.b[pair_bucket1(xrB, t.mask)];
+      if (nlA) rlA = bucket_rank(blA, klA);
+      if (nrA) rrA = bucket_rank(brA, krA);
+      if (nlB) rlB = bucket_rank(blB, klB);
+      if (nrB) rrB = bucket_rank(brB, krB);
+    }
+    if (goA) {
+      aliveA ^= 1u << qA;
+      SA[64 * iA] = zA;
+      if (qA < W - 1) KA[64 * qA] = kKeyNone;
+      uint32_t vl = rlA == kRankInf ? kKeyNone : (((uint32_t)rlA << 5) | (uint32_t)pA);
+      uint32_t vr = rrA == kRankInf ? kKeyNone : (((uint32_t)rrA << 5) | (uint32_t)iA);
+      if ((uint32_t)rlA < rA) {
+        vl |= kKeyDef;
+        defA = true;
+      }
+      if ((uint32_t)rrA < rA) {
+        vr |= kKeyDef;
+        defA = true;
+      }
+      if (hpA) KA[64 * pA] = vl;
+      KA[64 * iA] = vr;
+      rcA = rA;
+    }
+    if (goB) {
+      aliveB ^= 1u << qB;
+      SB[64 * iB] = zB;
+      if (qB < W - 1) KB[64 * qB] = kKeyNone;
+      uint32_t vl = rlB == kRankInf ? kKeyNone : (((uint32_t)rlB << 5) | (uint32_t)pB);
+      uint32_t vr = rrB == kRankInf ? kKeyNone : (((uint32_t)rrB << 5) | (uint32_t)iB);
+      if ((uint32_t)rlB < rB) {
+        vl |= kKeyDef;
+        defB = true;
+      }
+      if ((uint32_t)rrB < rB) {
+        vr |= kKeyDef;
+        defB = true;
+      }
+      if (hpB) KB[64 * pB] = vl;
+      KB[64 * iB] = vr;
+      rcB = rB;
+    }
+  }
+  int na = 0, nb = 0;
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    if ((aliveA >> j) & 1u) outa[na++] = (int32_t)SA[64 * j];
+    if ((aliveB >> j) & 1u) outb[nb++] = (int32_t)SB[64 * j];
+  }
+  *nta = na;
+  *ntb = nb;
+}
+
 // ---- k_merge, k_merge_wide ---------------------------------------------------
 
 constexpr int kGroup = 4;       // chunks per merge wave: batches of one bucket span them
@@ -807,6 +959,64 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
   return tok;
 }
 
+// Bucket b as merge_bucket does, two entries per lane (lane_merge2), 128
+// entries per batch; the two column sets share the W-wide region of L2.
+template <int W, class Pairs>
+__device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b,
+                                  LaneCols<2 * W> &L2, const Pairs &pairs) {
+  static_assert(2 * sizeof(LaneCols<W>) <= sizeof(LaneCols<2 * W>), "two column sets fit");
+  const int lane = lane_id();
+  const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
+  LaneCols<W> &LA = *reinterpret_cast<LaneCols<W> *>(&L2);
+  LaneCols<W> &LB = *(reinterpret_cast<LaneCols<W> *>(&L2) + 1);
+  int pre[kGroup];
+  int total = 0;
+#pragma unroll
+  for (int f = 0; f < kGroup; ++f) {
+    pre[f] = total;
+    total += G.cnt[f][b];
+  }
+  const int base = kBucketBase[b];
+  uint64_t tok = 0;
+  for (int s0 = 0; s0 < total; s0 += 128) {
+    int f[2], o[2], len[2];
+    int64_t c[2];
+    bool v[2];
+    uint32_t w[2][W / 4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g = s0 + 64 * h + lane;
+      v[h] = g < total;
+      f[h] = 0;
+      int idx = base + (v[h] ? g : 0);
+#pragma unroll
+      for (int k = 1; k < kGroup; ++k)
+        if (v[h] && g >= pre[k]) {
+          f[h] = k;
+          idx = base + g - pre[k];
+        }
+      c[h] = G.cg + f[h];
+      const uint32_t e = v[h] ? a.miss[c[h] * kMissMax + idx] : 0u;
+      o[h] = me_start(e) << 2;
+      len[h] = me_len(e);
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.mbytes + c[h] * kMissSpan + o[h]);
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) w[h][i] = v[h] ? src[i] : 0u;
+    }
+    if (!v[0]) break;
+    int nt0 = 0, nt1 = 0;
+    lane_merge2<W>(w[0], len[0], v[0], a.res + c[0] * kMissSpan + o[0], &nt0, w[1], len[1], v[1],
+                   a.res + c[1] * kMissSpan + o[1], &nt1, LA, LB, t, pairs);
+    a.mto[c[0] * kMissSpan + o[0]] = (uint8_t)nt0;
+    tok += (uint64_t)nt0 << (16 * f[0]);
+    if (v[1]) {
+      a.mto[c[1] * kMissSpan + o[1]] = (uint8_t)nt1;
+      tok += (uint64_t)nt1 << (16 * f[1]);
+    }
+  }
+  return tok;
+}
+
 // Per-chunk token sums of the wave (16 bits each in tok).
 __device__ __forceinline__ uint64_t wave_tok_sum(uint64_t tok) {
   return wave_sum(tok);
@@ -845,7 +1055,7 @@ __global__ void __launch_bounds__(MWG *kMergePWaves) k_merge(EncodeArgs a) {
     q = __builtin_amdgcn_readfirstlane(__shfl(q, 0, 64));
     LaneGroup G;
     if (!lane_group(a, (int64_t)blockIdx.x + (int64_t)gridDim.x * q, G)) break;
-    uint64_t tok = merge_bucket<8>(a, G, 0, *reinterpret_cast<LaneCols<8> *>(&L), pairs);
+    uint64_t tok = merge_bucket2<8>(a, G, 0, L, pairs);
     tok += merge_bucket<16>(a, G, 1, L, pairs);
     tok = wave_tok_sum(tok);
     if (lane < G.nf) {
