@@ -1380,15 +1380,15 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   };
   int64_t carry = 0;
   for (int r0 = 0; r0 < n_pt; r0 += EWG * kEmitPasses) {
-    int32_t v[kEmitPasses], cnt[kEmitPasses];
+    // the passes of this round that hold pre-tokens (the same for every thread)
+    const int np = min(kEmitPasses, (n_pt - r0 + EWG - 1) / EWG);
+    int32_t v[kEmitPasses], cnt[kEmitPasses], inc[kEmitPasses], w0[kEmitPasses];
     u32x4 first[kEmitPasses];
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
+      if (j >= np) continue;
       const int k = r0 + j * EWG + tid;
       v[j] = k < n_pt ? (r0 == 0 ? v0[j] : pv[k]) : INT32_MIN;
-    }
-#pragma unroll
-    for (int j = 0; j < kEmitPasses; ++j) {
       // a merge-loop entry's count and first four tokens; other pre-tokens
       // read entry 0 (the loads stay unconditional)
       const int o = -1 - v[j];
@@ -1401,17 +1401,19 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
         cnt[j] = a.mt[c * kMaxLong + (o - kMissSpan)];
     }
     // positions: every pass of the round is one scan over the workgroup
-    int32_t inc[kEmitPasses];
+    // (chunk-relative positions fit 32 bits: only the chunk's last pre-token
+    // can run past the window)
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
+      if (j >= np) continue;
       inc[j] = wave_incl_sum(cnt[j]);
       if (lane == 63) s.wtot[j][wave] = inc[j];
     }
     __syncthreads();
-    int64_t w0[kEmitPasses];
-    int64_t run = carry;
+    int32_t run = 0;
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
+      if (j >= np) continue;
       int32_t before = 0, all = 0;
 #pragma unroll
       for (int ww = 0; ww < EWG / 64; ++ww) {
@@ -1419,12 +1421,12 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
         if (ww < wave) before += t;
         all += t;
       }
-      w0[j] = run + before + inc[j] - cnt[j];
+      w0[j] = (int32_t)carry + run + before + inc[j] - cnt[j];
       run += all;
     }
-    carry = run;
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
+      if (j >= np) continue;
       // the tokens of a pre-token that does not run past the window all fall
       // below kOutCap: its first four by unconditional stores (the unused
       // ones to the spare slot), the rest of a longer lane-merged entry after
@@ -1433,7 +1435,7 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       const int o = -1 - x;
       const bool placed = k < n_pt && (x >= 0 || o < kMissSpan);
       const int nt = placed ? cnt[j] : 0;
-      const int w = (int)w0[j];
+      const int w = w0[j];
       const u32x4 t = x >= 0 ? u32x4{(uint32_t)x, 0u, 0u, 0u} : first[j];
       s.out[nt > 0 ? w : kOutCap] = (int32_t)t.x;
       s.out[nt > 1 ? w + 1 : kOutCap] = (int32_t)t.y;
@@ -1445,11 +1447,12 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
         const int q = o - kMissSpan;
         const uint32_t e = a.miss[c * kMissMax + kBucketBase[3] + q];
         const int slot = atomicAdd(&s.n_long, 1);
-        s.lw[slot] = w0[j];
+        s.lw[slot] = w;
         s.lsrc[slot] = c0 + me_start(e);
         s.lnt[slot] = cnt[j];
       }
     }
+    carry += run;
     __syncthreads();  // wtot is rewritten by the next round
   }
   const int64_t total = carry;
