@@ -255,10 +255,10 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.doc_rng = (int64_t *)(ws + L.doc_rng);
   a.doc_pt = (int32_t *)(ws + L.doc_pt);
   a.pv = (int32_t *)(ws + L.pv);
+  a.cntk = ws + L.cntk;
   a.miss = (uint32_t *)(ws + L.miss);
   a.mt = (int32_t *)(ws + L.mt);
   a.mbytes = ws + L.mbytes;
-  a.mto = ws + L.mto;
   a.res = (int32_t *)(ws + L.res);
   a.gsym = (int32_t *)(ws + L.gsym);
   a.grank = (int32_t *)(ws + L.grank);

@@ -46,6 +46,21 @@ constexpr int DB_WORDS = (WIN + DB_OFF) / 32 + 2;
 // offset in the chunk's mbytes / res regions for buckets 0-2.  An overhang
 // entry is a chunk's last pre-token that runs past the window; its length is
 // found by the merge kernel.
+// Lane-merged entries (at most kLaneMax bytes) instead: o / 4 (12 bits), the
+// entry's 4-byte aligned offset in the dense region | len << 12 | the
+// pre-token's index k in the chunk << 18.
+__device__ __forceinline__ uint32_t lane_entry(int o4, int len, int k) {
+  return (uint32_t)o4 | ((uint32_t)len << 12) | ((uint32_t)k << 18);
+}
+__device__ __forceinline__ int le_o4(uint32_t e) { return (int)(e & 0xFFFu); }
+__device__ __forceinline__ int le_len(uint32_t e) { return (int)((e >> 12) & 0x3Fu); }
+__device__ __forceinline__ int le_k(uint32_t e) { return (int)(e >> 18); }
+
+// pv value of a merge-loop pre-token: -1 - u.  A lane-merged entry at dense
+// offset 4 o4 has u = o4 (its token count goes to cntk at the pre-token's
+// index); the q-th wave-merged entry has u = kPvLong + q.
+constexpr int kPvLong = 1 << 20;
+
 __device__ __forceinline__ uint32_t miss_entry(int st, int len, bool over) {
   return (uint32_t)st | ((uint32_t)len << 13) | ((uint32_t)over << 26);
 }
@@ -673,11 +688,11 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
         for (int i = 0; 4 * i < len; ++i)
           dst[i] = __builtin_amdgcn_alignbyte(B32[q + i + 1], B32[q + i], sh);
       }
-      ml[base + idx] = miss_entry(o >> 2, len, false);
-      pv[k] = -1 - o;
+      ml[base + idx] = lane_entry(o >> 2, len, k);
+      pv[k] = -1 - (o >> 2);
     } else {
       ml[base + idx] = miss_entry(st, len, over);
-      pv[k] = -1 - kMissSpan - idx;
+      pv[k] = -1 - kPvLong - idx;
     }
   }
   const bool any_bad = __syncthreads_or(bad);
@@ -918,8 +933,9 @@ __device__ __forceinline__ int64_t wave_group(int64_t first) {
 // Bucket b of the group's lists, one pre-token per lane with W-wide LDS
 // columns, 64 entries per batch.  An entry's bytes are read from its chunk's
 // dense mbytes region and its tokens written to res at the same offset (never
-// more tokens than bytes, so entries do not overlap), their count to mto at
-// that offset; the return value holds the tokens per chunk, 16 bits each.
+// more tokens than bytes, so entries do not overlap), their count to cntk
+// at the pre-token's index; the return value holds the tokens per chunk, 16
+// bits each.
 template <int W, class Pairs>
 __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b, LaneCols<W> &L,
                                  const Pairs &pairs) {
@@ -947,13 +963,13 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
       }
     const int64_t c = G.cg + f;
     const uint32_t e = a.miss[c * kMissMax + idx];
-    const int o = me_start(e) << 2;  // 4-byte aligned
+    const int o4 = le_o4(e), o = o4 << 2;  // 4-byte aligned
     const uint32_t *src = reinterpret_cast<const uint32_t *>(a.mbytes + c * kMissSpan + o);
     uint32_t w[W / 4];
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) w[i] = src[i];
-    const int nt = lane_merge<W>(w, me_len(e), L, t, pairs, a.res + c * kMissSpan + o);
-    a.mto[c * kMissSpan + o] = (uint8_t)nt;
+    const int nt = lane_merge<W>(w, le_len(e), L, t, pairs, a.res + c * kMissSpan + o);
+    a.cntk[c * kChunk + le_k(e)] = (uint8_t)nt;
     tok += (uint64_t)nt << (16 * f);
   }
   return tok;
@@ -979,7 +995,7 @@ __device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b
   const int base = kBucketBase[b];
   uint64_t tok = 0;
   for (int s0 = 0; s0 < total; s0 += 128) {
-    int f[2], o[2], len[2];
+    int f[2], o[2], len[2], kk[2];
     int64_t c[2];
     bool v[2];
     uint32_t w[2][W / 4];
@@ -997,8 +1013,9 @@ __device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b
         }
       c[h] = G.cg + f[h];
       const uint32_t e = v[h] ? a.miss[c[h] * kMissMax + idx] : 0u;
-      o[h] = me_start(e) << 2;
-      len[h] = me_len(e);
+      o[h] = le_o4(e) << 2;
+      len[h] = le_len(e);
+      kk[h] = le_k(e);
       const uint32_t *src = reinterpret_cast<const uint32_t *>(a.mbytes + c[h] * kMissSpan + o[h]);
 #pragma unroll
       for (int i = 0; i < W / 4; ++i) w[h][i] = v[h] ? src[i] : 0u;
@@ -1007,10 +1024,10 @@ __device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b
     int nt0 = 0, nt1 = 0;
     lane_merge2<W>(w[0], len[0], v[0], a.res + c[0] * kMissSpan + o[0], &nt0, w[1], len[1], v[1],
                    a.res + c[1] * kMissSpan + o[1], &nt1, LA, LB, t, pairs);
-    a.mto[c[0] * kMissSpan + o[0]] = (uint8_t)nt0;
+    a.cntk[c[0] * kChunk + kk[0]] = (uint8_t)nt0;
     tok += (uint64_t)nt0 << (16 * f[0]);
     if (v[1]) {
-      a.mto[c[1] * kMissSpan + o[1]] = (uint8_t)nt1;
+      a.cntk[c[1] * kChunk + kk[1]] = (uint8_t)nt1;
       tok += (uint64_t)nt1 << (16 * f[1]);
     }
   }
@@ -1356,13 +1373,16 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int64_t c0 = c * kChunk;
   const int32_t *pv = a.pv + c * kChunk;
   const int32_t *res = a.res + c * kMissSpan;
-  const uint8_t *mto = a.mto + c * kMissSpan;
   // loads that need nothing else first: the first round's pv values (pv has
   // room for kChunk entries, so this reads inside it whatever the count), and
   // the first pre-token of the documents that start here
-  int32_t v0[kEmitPasses];
+  const uint8_t *cntk = a.cntk + c * kChunk;
+  int32_t v0[kEmitPasses], n0[kEmitPasses];
 #pragma unroll
-  for (int j = 0; j < kEmitPasses; ++j) v0[j] = pv[j * EWG + tid];
+  for (int j = 0; j < kEmitPasses; ++j) {
+    v0[j] = pv[j * EWG + tid];
+    n0[j] = cntk[j * EWG + tid];
+  }
   const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
   const int dk0 = dlo + tid < dhi ? a.doc_pt[dlo + tid] : 0;
   const int n_pt = a.meta[kMetaInts * c + kMetaPretokens];
@@ -1389,16 +1409,17 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       if (j >= np) continue;
       const int k = r0 + j * EWG + tid;
       v[j] = k < n_pt ? (r0 == 0 ? v0[j] : pv[k]) : INT32_MIN;
-      // a merge-loop entry's count and first four tokens; other pre-tokens
-      // read entry 0 (the loads stay unconditional)
-      const int o = -1 - v[j];
-      const bool lane_merged = v[j] < 0 && v[j] != INT32_MIN && o < kMissSpan;
-      const int oo = lane_merged ? o : 0;
-      const int32_t m = mto[oo];
+      const int nk = r0 == 0 ? n0[j] : cntk[k];
+      // a lane-merged entry's count comes from cntk, loaded beside pv; its
+      // first four tokens in one load (other pre-tokens read entry 0: the
+      // load stays unconditional)
+      const int u = -1 - v[j];
+      const bool lane_merged = v[j] < 0 && v[j] != INT32_MIN && u < kPvLong;
+      const int oo = lane_merged ? (u & 0xFFF) << 2 : 0;
       first[j] = *reinterpret_cast<const u32x4 *>(res + oo);
-      cnt[j] = v[j] >= 0 ? 1 : (lane_merged ? m : 0);
+      cnt[j] = v[j] >= 0 ? 1 : (lane_merged ? nk : 0);
       if (v[j] < 0 && v[j] != INT32_MIN && !lane_merged)
-        cnt[j] = a.mt[c * kMaxLong + (o - kMissSpan)];
+        cnt[j] = a.mt[c * kMaxLong + (u - kPvLong)];
     }
     // positions: every pass of the round is one scan over the workgroup
     // (chunk-relative positions fit 32 bits: only the chunk's last pre-token
@@ -1432,8 +1453,9 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       // ones to the spare slot), the rest of a longer lane-merged entry after
       const int k = r0 + j * EWG + tid;
       const int32_t x = v[j];
-      const int o = -1 - x;
-      const bool placed = k < n_pt && (x >= 0 || o < kMissSpan);
+      const int u = -1 - x;
+      const int o = (u & 0xFFF) << 2;
+      const bool placed = k < n_pt && (x >= 0 || u < kPvLong);
       const int nt = placed ? cnt[j] : 0;
       const int w = w0[j];
       const u32x4 t = x >= 0 ? u32x4{(uint32_t)x, 0u, 0u, 0u} : first[j];
@@ -1443,8 +1465,8 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       s.out[nt > 3 ? w + 3 : kOutCap] = (int32_t)t.w;
       for (int q = 4; q < nt; ++q) s.out[w + q] = res[o + q];
       if (k < n_pt) s.pos[k] = (uint16_t)w;
-      if (k < n_pt && x < 0 && o >= kMissSpan) {
-        const int q = o - kMissSpan;
+      if (k < n_pt && x < 0 && u >= kPvLong) {
+        const int q = u - kPvLong;
         const uint32_t e = a.miss[c * kMissMax + kBucketBase[3] + q];
         const int slot = atomicAdd(&s.n_long, 1);
         s.lw[slot] = w;

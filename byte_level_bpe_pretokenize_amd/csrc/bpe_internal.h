@@ -173,23 +173,24 @@ constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
 //                       then the counts' exclusive prefix
 //   doc_rng   [G][2] i64  documents that start in the chunk
 //   doc_pt    [D] i32   index of each document's first pre-token in its chunk
-//   pv        [G][kChunk] i32    per pre-token: its symbol; -1 - o for a
-//                                lane-merged one whose bytes start at o in
-//                                mbytes; -1 - kMissSpan - q for the q-th
+//   pv        [G][kChunk] i32    per pre-token: its symbol; -1 - o4 for a
+//                                lane-merged one whose bytes start at 4 o4 in
+//                                mbytes; -1 - 2^20 - q for the q-th
 //                                wave-merged one
+//   cntk      [G][kChunk] u8     token count of each lane-merged pre-token
 //   miss      [G][kMissMax] u32  merge-loop list, a region per length bucket
 //                                (kBucketBase), in no particular order:
-//                                o / 4 | len << 13 (lane-merged), start | len << 13 |
+//                                o / 4 | len << 12 | k << 18 (lane-merged,
+//                                k the pre-token's index), start | len << 13 |
 //                                overhang << 26 (wave-merged)
 //   mt        [G][kMaxLong] i32  token count of each wave-merged entry
 //   mbytes    [G][kMissSpan] u8   bytes of the lane-merged entries, each at a
 //                                  4-byte aligned offset o
-//   mto       [G][kMissSpan] u8   token count of the lane-merged entry at o
 //   res       [G][kMissSpan] i32  its tokens, from o on
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the wave merge, position-indexed
 struct EncLayout {
-  size_t meta, tot, off, doc_rng, doc_pt, pv, miss, mt, mbytes, mto, res, gsym, grank, total;
+  size_t meta, tot, off, doc_rng, doc_pt, pv, cntk, miss, mt, mbytes, res, gsym, grank, total;
 };
 inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   EncLayout L;
@@ -206,10 +207,10 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.doc_rng = take(16 * G);
   L.doc_pt = take(4 * (size_t)(n_docs + 1));
   L.pv = take(4 * (size_t)kChunk * G);
+  L.cntk = take((size_t)kChunk * G);
   L.miss = take(4 * (size_t)kMissMax * G);
   L.mt = take(4 * (size_t)kMaxLong * G);
   L.mbytes = take((size_t)kMissSpan * G + 64);  // word loads read a little past the end
-  L.mto = take((size_t)kMissSpan * G);
   L.res = take(4 * (size_t)kMissSpan * G + 64);
   L.gsym = take(4 * (size_t)n_bytes);
   L.grank = take(4 * (size_t)n_bytes);
@@ -259,10 +260,10 @@ struct EncodeArgs {
   int64_t *doc_rng;
   int32_t *doc_pt;
   int32_t *pv;
+  uint8_t *cntk;
   uint32_t *miss;
   int32_t *mt;
   uint8_t *mbytes;
-  uint8_t *mto;
   int32_t *res;
   int32_t *gsym;
   int32_t *grank;
