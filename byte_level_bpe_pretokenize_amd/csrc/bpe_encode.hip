@@ -60,6 +60,13 @@ __device__ __forceinline__ int le_k(uint32_t e) { return (int)(e >> 18); }
 // offset 4 o4 has u = o4 (its token count goes to cntk at the pre-token's
 // index); the q-th wave-merged entry has u = kPvLong + q.
 constexpr int kPvLong = 1 << 20;
+// pv of a lane-merged pre-token that takes the tokens of another entry with
+// the same bytes: -1 - (kPvDup + g), the tokens at res + 4 g.
+constexpr int kPvDup = 1 << 21;
+// Buckets kDedupFrom..2 go through the call's entry table (k_dedup); the
+// shorter entries below are merged wherever they occur.
+constexpr int kDedupFrom = 1;
+__device__ __forceinline__ bool deduped(int b) { return b >= kDedupFrom && b < 3; }
 
 __device__ __forceinline__ uint32_t miss_entry(int st, int len, bool over) {
   return (uint32_t)st | ((uint32_t)len << 13) | ((uint32_t)over << 26);
@@ -511,6 +518,13 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   const int nown = (int)min<int64_t>(kChunk, n - c0);
   const bool win_reaches_end = (c0 + nwin == n);
   for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
+  if (a.dedup) {
+    // this chunk's share of the call's entry table starts empty
+    const uint64_t words = 2 * ((uint64_t)a.dt_mask + 1);
+    const uint64_t per = (words + a.n_chunks - 1) / (uint64_t)a.n_chunks;
+    const uint64_t lo = (uint64_t)c * per, hi = min(lo + per, words);
+    for (uint64_t i = lo + tid; i < hi; i += WG) a.dt[i] = 0ull;
+  }
   if (tid < kBuckets) s.cnt[tid] = 0;
   if (tid == 0) s.nbytes = 0;
   if (tid <= kShortMax) {
@@ -888,16 +902,6 @@ struct MergeShared {
   Red<MWG> r;
 };
 
-// Entry g (0-based) of bucket b across the group's chunks: chunk index f and
-// list index; meta counts are in LDS.
-__device__ __forceinline__ void group_entry(const MergeShared &s, int b, int g, int &f, int &idx) {
-  int pre = 0;
-  f = 0;
-  while (g >= pre + s.meta[f][kMetaBucket + b]) pre += s.meta[f++][kMetaBucket + b];
-  idx = g - pre;
-  for (int bb = 0; bb < b; ++bb) idx += s.meta[f][kMetaBucket + bb];
-}
-
 __device__ void load_group(const EncodeArgs &a, MergeShared &s, int64_t cg, int nf) {
   const int lane = lane_id();
   if (lane < kMetaInts * nf) (&s.meta[0][0])[lane] = a.meta[kMetaInts * cg + lane];
@@ -914,6 +918,8 @@ struct LaneGroup {
 };
 
 // Group q (chunks kGroup q ..) of the merge-loop lists; false past the last.
+// The counts of buckets 0-2 are their owners' (entries the call's table
+// found first), listed in olist.
 __device__ __forceinline__ bool lane_group(const EncodeArgs &a, int64_t q, LaneGroup &G) {
   G.cg = q * kGroup;
   if (G.cg >= a.n_chunks) return false;
@@ -922,7 +928,8 @@ __device__ __forceinline__ bool lane_group(const EncodeArgs &a, int64_t q, LaneG
   for (int f = 0; f < kGroup; ++f)
 #pragma unroll
     for (int b = 0; b < kBuckets; ++b)
-      G.cnt[f][b] = f < G.nf ? a.meta[kMetaInts * (G.cg + f) + kMetaBucket + b] : 0;
+      G.cnt[f][b] = f < G.nf ? a.meta[kMetaInts * (G.cg + f) + (deduped(b) ? kMetaOwners : kMetaBucket) + b]
+                             : 0;
   return true;
 }
 
@@ -962,7 +969,9 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
         idx = base + g - pre[k];
       }
     const int64_t c = G.cg + f;
-    const uint32_t e = a.miss[c * kMissMax + idx];
+    const uint64_t ol = deduped(b) ? a.olist[c * kMissMax + idx]
+                                   : ((uint64_t)kNoSlot << 32 | a.miss[c * kMissMax + idx]);
+    const uint32_t e = (uint32_t)ol, slot = (uint32_t)(ol >> 32);
     const int o4 = le_o4(e), o = o4 << 2;  // 4-byte aligned
     const uint32_t *src = reinterpret_cast<const uint32_t *>(a.mbytes + c * kMissSpan + o);
     uint32_t w[W / 4];
@@ -970,6 +979,7 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
     for (int i = 0; i < W / 4; ++i) w[i] = src[i];
     const int nt = lane_merge<W>(w, le_len(e), L, t, pairs, a.res + c * kMissSpan + o);
     a.cntk[c * kChunk + le_k(e)] = (uint8_t)nt;
+    if (slot != kNoSlot) reinterpret_cast<uint32_t *>(a.dt)[4 * (size_t)slot + 3] = (uint32_t)nt;
     tok += (uint64_t)nt << (16 * f);
   }
   return tok;
@@ -998,6 +1008,7 @@ __device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b
     int f[2], o[2], len[2], kk[2];
     int64_t c[2];
     bool v[2];
+    uint32_t sl[2];
     uint32_t w[2][W / 4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1012,7 +1023,11 @@ __device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b
           idx = base + g - pre[k];
         }
       c[h] = G.cg + f[h];
-      const uint32_t e = v[h] ? a.miss[c[h] * kMissMax + idx] : 0u;
+      const uint64_t ol = !v[h]        ? ((uint64_t)kNoSlot << 32)
+                          : deduped(b) ? a.olist[c[h] * kMissMax + idx]
+                                       : ((uint64_t)kNoSlot << 32 | a.miss[c[h] * kMissMax + idx]);
+      const uint32_t e = (uint32_t)ol;
+      sl[h] = (uint32_t)(ol >> 32);
       o[h] = le_o4(e) << 2;
       len[h] = le_len(e);
       kk[h] = le_k(e);
@@ -1024,10 +1039,13 @@ __device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b
     int nt0 = 0, nt1 = 0;
     lane_merge2<W>(w[0], len[0], v[0], a.res + c[0] * kMissSpan + o[0], &nt0, w[1], len[1], v[1],
                    a.res + c[1] * kMissSpan + o[1], &nt1, LA, LB, t, pairs);
+    uint32_t *dt32 = reinterpret_cast<uint32_t *>(a.dt);
     a.cntk[c[0] * kChunk + kk[0]] = (uint8_t)nt0;
+    if (sl[0] != kNoSlot) dt32[4 * (size_t)sl[0] + 3] = (uint32_t)nt0;
     tok += (uint64_t)nt0 << (16 * f[0]);
     if (v[1]) {
       a.cntk[c[1] * kChunk + kk[1]] = (uint8_t)nt1;
+      if (sl[1] != kNoSlot) dt32[4 * (size_t)sl[1] + 3] = (uint32_t)nt1;
       tok += (uint64_t)nt1 << (16 * f[1]);
     }
   }
@@ -1100,6 +1118,185 @@ __global__ void __launch_bounds__(MWG *kMergeWaves) k_merge_wide(EncodeArgs a) {
     const int32_t add = (int32_t)((tok >> (16 * lane)) & 0xFFFFu);
     if (add) a.tot[G.cg + lane] += add;
   }
+}
+
+// ---- k_dedup, k_dupfill ----------------------------------------------------
+// The pages' word cache ("Hugging Face Tokenizers v1", section "Word
+// caching": a pre-token seen before skips the merge loop), built for each call
+// from nothing.  The first lane-merged entry with given bytes to claim a slot
+// of the call's table owns them and is merged; a later one with the same bytes
+// takes, once the owner is merged, the owner's token count and its tokens (pv
+// points at them).  Nothing is kept from one call to the next.
+//
+// A slot is 16 bytes: the claimed key (hash bits and the entry's length, above
+// g, the owner's offset / 4 in mbytes), then g again and, once the owner is
+// merged, its token count.  A key whose upper half matches is checked against
+// the bytes at g.
+
+constexpr int kDedupProbes = 64;
+constexpr int kDedupSeed = 256;    // chunks of the first, seeding launch
+
+// The bytes (at most 32) at 4-byte offset q of mbytes as eight words, zero
+// from byte len on.  All eight are loaded, with no branch between the loads
+// (mbytes has room past its last entry for that).
+__device__ __forceinline__ void entry_words(const uint8_t *mbytes, uint64_t q, int len,
+                                            uint32_t *w) {
+  const uint32_t *src = reinterpret_cast<const uint32_t *>(mbytes) + q;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = src[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int valid = len - 4 * i;
+    w[i] &= valid >= 4 ? ~0u : (valid <= 0 ? 0u : (1u << (8 * valid)) - 1u);
+  }
+}
+
+__device__ __forceinline__ uint32_t entry_hash(const uint32_t *w, int len) {
+  uint32_t x = mix32((uint32_t)len * 0x9E3779B9u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (4 * i < len) x = mix32(x ^ w[i]) + (uint32_t)i;
+  return x;
+}
+
+// List entries of bucket b of a chunk (meta m) that go through the table.
+__device__ __forceinline__ int dedup_count(const int32_t *m, int b) {
+  return deduped(b) ? m[kMetaBucket + b] : 0;
+}
+
+// Entry g of buckets 0-2 of a chunk, taken in bucket order: its list index.
+__device__ __forceinline__ int lane_list_index(int g, int n0, int n01, int &b) {
+  b = g < n0 ? 0 : (g < n01 ? 1 : 2);
+  return b == 0 ? g : (b == 1 ? kBucketBase[1] + g - n0 : kBucketBase[2] + g - n01);
+}
+
+// One wave per chunk of [c_lo, c_hi): every lane-merged entry becomes an
+// owner (merged itself, listed in olist by bucket) or takes the owner of its
+// bytes (dref = the slot); the owner counts go to meta.
+__global__ void __launch_bounds__(256) k_dedup(EncodeArgs a, int64_t c_lo, int64_t c_hi) {
+  const int64_t c = c_lo + (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave_id());
+  if (c >= c_hi) return;
+  const int lane = lane_id();
+  const int32_t *m = a.meta + kMetaInts * c;
+  const int n0 = dedup_count(m, 0), n01 = n0 + dedup_count(m, 1);
+  const int n = n01 + dedup_count(m, 2);
+  const uint32_t q0 = (uint32_t)c * (kMissSpan / 4);  // the chunk's mbytes, in words
+  const uint64_t below = (1ull << lane) - 1;
+  uint32_t *dt32 = reinterpret_cast<uint32_t *>(a.dt);
+  const u64x2 *dt2 = reinterpret_cast<const u64x2 *>(a.dt);
+  int own0 = 0, own1 = 0, own2 = 0;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int g = s0 + lane;
+    const bool v = g < n;
+    int b;
+    const int idx = lane_list_index(g, n0, n01, b);
+    const uint32_t e = v ? a.miss[c * kMissMax + idx] : 0u;
+    bool owner = true;
+    uint32_t slot = kNoSlot;
+    if (v && a.dedup) {
+      const int len = le_len(e);
+      const uint32_t gme = q0 + le_o4(e);
+      uint32_t w[8];
+      entry_words(a.mbytes, gme, len, w);
+      const uint32_t h = entry_hash(w, len);
+      const uint32_t khi = (h & ~63u) | 0x80000000u | (uint32_t)len;
+      const unsigned long long key = (unsigned long long)khi << 32 | gme;
+      // linear probing; an empty slot is claimed by a CAS (one that loses
+      // reads the slot again), a slot whose key matches a longer entry is
+      // checked by its bytes.  The claims and the byte loads of the other
+      // lanes are in flight together.
+      uint32_t s = mix32(h ^ 0x5BD1E995u) & a.dt_mask;
+      bool active = true, need = true;
+      unsigned long long x = 0ull;
+      for (int p = 0; p < kDedupProbes && active; ++p) {
+        if (need) x = dt2[s].x;
+        need = true;
+        const bool empty = x == 0ull;
+        const bool hit = (uint32_t)(x >> 32) == khi;
+        unsigned long long old = 1ull;
+        if (empty) old = atomicCAS(&a.dt[2 * (size_t)s], 0ull, key);
+        uint32_t w2[8];
+        if (hit) entry_words(a.mbytes, (uint32_t)x, len, w2);
+        if (empty) {
+          if (old == 0ull) {
+            slot = s;  // this entry owns its bytes
+            dt32[4 * (size_t)s + 2] = gme;
+            active = false;
+          } else {
+            x = old;  // taken meanwhile: look at the key that won
+            need = false;
+          }
+        } else if (hit) {
+          uint32_t d = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) d |= w[i] ^ w2[i];
+          if (d == 0) {
+            owner = false;
+            slot = s;
+            active = false;
+          } else {
+            s = (s + 1) & a.dt_mask;
+          }
+        } else {
+          s = (s + 1) & a.dt_mask;
+        }
+      }
+    }
+    if (v) a.dref[c * kMissMax + idx] = owner ? kDrefOwner : slot;
+    const bool ov = v && owner;
+    const uint64_t o0 = __ballot(ov && b == 0), o1 = __ballot(ov && b == 1),
+                   o2 = __ballot(ov && b == 2);
+    if (ov) {
+      const int at = b == 0 ? own0 + __popcll(o0 & below)
+                            : (b == 1 ? own1 + __popcll(o1 & below) : own2 + __popcll(o2 & below));
+      a.olist[c * kMissMax + kBucketBase[b] + at] = (uint64_t)e | ((uint64_t)slot << 32);
+    }
+    own0 += __popcll(o0);
+    own1 += __popcll(o1);
+    own2 += __popcll(o2);
+  }
+  if (lane == 0) {
+    int32_t *mm = a.meta + kMetaInts * c;
+    mm[kMetaOwners + 0] = own0;
+    mm[kMetaOwners + 1] = own1;
+    mm[kMetaOwners + 2] = own2;
+  }
+}
+
+// One wave per chunk, after the owners are merged: each entry that is not an
+// owner takes its owner's token count and tokens from the slot; the chunk's
+// count grows by theirs.
+__global__ void __launch_bounds__(256) k_dupfill(EncodeArgs a) {
+  const int64_t c = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave_id());
+  if (c >= a.n_chunks || !a.dedup) return;
+  const int lane = lane_id();
+  const int32_t *m = a.meta + kMetaInts * c;
+  const int n0 = dedup_count(m, 0), n01 = n0 + dedup_count(m, 1);
+  const int n = n01 + dedup_count(m, 2);
+  int owners = 0;
+#pragma unroll
+  for (int b = kDedupFrom; b < 3; ++b) owners += m[kMetaOwners + b];
+  if (owners == n) return;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 *dty = reinterpret_cast<const u32x2 *>(a.dt);
+  int sum = 0;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int g = s0 + lane;
+    int b;
+    const int idx = lane_list_index(g, n0, n01, b);
+    if (g < n) {
+      const uint32_t r = a.dref[c * kMissMax + idx];
+      const uint32_t e = a.miss[c * kMissMax + idx];
+      if (r != kDrefOwner) {
+        const u32x2 y = dty[2 * (size_t)r + 1];  // owner's g, token count
+        a.cntk[c * kChunk + le_k(e)] = (uint8_t)y.y;
+        a.pv[c * kChunk + le_k(e)] = -1 - (kPvDup + (int32_t)y.x);
+        sum += (int)y.y;
+      }
+    }
+  }
+  sum = wave_sum(sum);
+  if (lane == 0 && sum) a.tot[c] += sum;
 }
 
 // End (exclusive, global) of the pre-token that starts at gs and has no start
@@ -1359,6 +1556,13 @@ struct EmitShared {
   int32_t n_long;
 };
 
+// Tokens of the lane-merged pre-token with pv value -1 - u: in the chunk's
+// own res region, or (u >= kPvDup) in the owner's of the same bytes.
+__device__ __forceinline__ const int32_t *entry_res(const EncodeArgs &a, const int32_t *res,
+                                                    int u) {
+  return u >= kPvDup ? a.res + 4 * (size_t)(uint32_t)(u - kPvDup) : res + ((u & 0xFFF) << 2);
+}
+
 // Writes a chunk's IDs at its offset, and the offsets of the documents that
 // start in it.  Pre-token k belongs to thread k % EWG; rounds of kEmitPasses
 // passes load every pv value of the round, then the token counts and the first
@@ -1414,12 +1618,11 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       // first four tokens in one load (other pre-tokens read entry 0: the
       // load stays unconditional)
       const int u = -1 - v[j];
-      const bool lane_merged = v[j] < 0 && v[j] != INT32_MIN && u < kPvLong;
-      const int oo = lane_merged ? (u & 0xFFF) << 2 : 0;
-      first[j] = *reinterpret_cast<const u32x4 *>(res + oo);
+      const bool neg = v[j] < 0 && v[j] != INT32_MIN;
+      const bool lane_merged = neg && (u < kPvLong || u >= kPvDup);
+      first[j] = *reinterpret_cast<const u32x4 *>(entry_res(a, res, lane_merged ? u : 0));
       cnt[j] = v[j] >= 0 ? 1 : (lane_merged ? nk : 0);
-      if (v[j] < 0 && v[j] != INT32_MIN && !lane_merged)
-        cnt[j] = a.mt[c * kMaxLong + (u - kPvLong)];
+      if (neg && !lane_merged) cnt[j] = a.mt[c * kMaxLong + (u - kPvLong)];
     }
     // positions: every pass of the round is one scan over the workgroup
     // (chunk-relative positions fit 32 bits: only the chunk's last pre-token
@@ -1454,8 +1657,7 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       const int k = r0 + j * EWG + tid;
       const int32_t x = v[j];
       const int u = -1 - x;
-      const int o = (u & 0xFFF) << 2;
-      const bool placed = k < n_pt && (x >= 0 || u < kPvLong);
+      const bool placed = k < n_pt && (x >= 0 || u < kPvLong || u >= kPvDup);
       const int nt = placed ? cnt[j] : 0;
       const int w = w0[j];
       const u32x4 t = x >= 0 ? u32x4{(uint32_t)x, 0u, 0u, 0u} : first[j];
@@ -1463,9 +1665,12 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       s.out[nt > 1 ? w + 1 : kOutCap] = (int32_t)t.y;
       s.out[nt > 2 ? w + 2 : kOutCap] = (int32_t)t.z;
       s.out[nt > 3 ? w + 3 : kOutCap] = (int32_t)t.w;
-      for (int q = 4; q < nt; ++q) s.out[w + q] = res[o + q];
+      if (nt > 4) {
+        const int32_t *src = entry_res(a, res, u);
+        for (int q = 4; q < nt; ++q) s.out[w + q] = src[q];
+      }
       if (k < n_pt) s.pos[k] = (uint16_t)w;
-      if (k < n_pt && x < 0 && u >= kPvLong) {
+      if (k < n_pt && x < 0 && u >= kPvLong && u < kPvDup) {
         const int q = u - kPvLong;
         const uint32_t e = a.miss[c * kMissMax + kBucketBase[3] + q];
         const int slot = atomicAdd(&s.n_long, 1);
@@ -1530,27 +1735,46 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
   return hipGetLastError();
 }
 
-const char *const kEncStageNames[kEncStages] = {"k_find",       "k_merge",   "k_merge_wide",
-                                                "k_merge_long", "k_offsets", "k_emit"};
+const char *const kEncStageNames[kEncStages] = {"k_find",       "k_dedup",   "k_merge",
+                                                "k_merge_wide", "k_merge_long", "k_dupfill",
+                                                "k_offsets",    "k_emit"};
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev) {
   const unsigned G = (unsigned)a.n_chunks;
-  if (ev) (void)hipEventRecord(ev[0], stream);
+  const unsigned G4 = (G + 3) / 4;
+  int st = 0;
+  auto mark = [&]() {
+    if (ev) (void)hipEventRecord(ev[st++], stream);
+  };
+  mark();
   hipLaunchKernelGGL(k_find, dim3(G), dim3(WG), 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[1], stream);
+  mark();
+  {
+    // the first chunks claim the keys they share with most others before the
+    // rest start, so that few CAS on one slot at once
+    const int64_t seed = min((int64_t)kDedupSeed, a.n_chunks);
+    hipLaunchKernelGGL(k_dedup, dim3((unsigned)((seed + 3) / 4)), dim3(256), 0, stream, a,
+                       (int64_t)0, seed);
+    if (a.n_chunks > seed)
+      hipLaunchKernelGGL(k_dedup, dim3((unsigned)((a.n_chunks - seed + 3) / 4)), dim3(256), 0,
+                         stream, a, seed, a.n_chunks);
+  }
+  mark();
   const unsigned LG = (G + kGroup * kMergeWaves - 1) / (kGroup * kMergeWaves);
   const unsigned n_groups = (G + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(k_merge, dim3(min((unsigned)a.n_cu, n_groups)), dim3(MWG * kMergePWaves), 0,
                      stream, a);
-  if (ev) (void)hipEventRecord(ev[2], stream);
+  mark();
   hipLaunchKernelGGL(k_merge_wide, dim3(LG), dim3(MWG * kMergeWaves), 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[3], stream);
+  mark();
   hipLaunchKernelGGL(k_merge_long, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[4], stream);
+  mark();
+  hipLaunchKernelGGL(k_dupfill, dim3(G4), dim3(256), 0, stream, a);
+  mark();
   hipLaunchKernelGGL(k_offsets, dim3(1), dim3(OWG), 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[5], stream);
+  mark();
   hipLaunchKernelGGL(k_emit, dim3(G), dim3(EWG), 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[6], stream);
+  mark();
   return hipGetLastError();
 }
 

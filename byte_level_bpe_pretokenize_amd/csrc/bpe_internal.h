@@ -158,17 +158,20 @@ constexpr int kBucketCap[kBuckets] = {kMissBytes / 2, kMissBytes / 9 + 1, kMissB
 constexpr int kBucketBase[kBuckets] = {0, kBucketCap[0], kBucketCap[0] + kBucketCap[1],
                                        kBucketCap[0] + kBucketCap[1] + kBucketCap[2]};
 constexpr int kMissMax = kBucketBase[3] + kBucketCap[3];
-// meta: 8 int32 per chunk
-constexpr int kMetaInts = 8;
+// meta: 16 int32 per chunk
+constexpr int kMetaInts = 16;
 constexpr int kMetaPretokens = 0;  // pre-tokens that start in the chunk
 constexpr int kMetaMisses = 1;     // of which on the merge-loop list
 constexpr int kMetaStatus = 2;     // status bits found by the chunk
 constexpr int kMetaBytes = 3;      // span of the lane-merged entries' dense region
 constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
+constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes in the call
+                                   // (buckets 0-2)
 
 // Encode workspace, all regions 256-byte aligned:
-//   meta      [G][8] i32  pre-tokens, merge-loop pre-tokens, status bits,
-//                         lane-merged bytes, list entries per length bucket
+//   meta      [G][16] i32  pre-tokens, merge-loop pre-tokens, status bits,
+//                          lane-merged bytes, list entries per length bucket,
+//                          owners per lane-merged bucket
 //   tot, off  [G] i64   token count per chunk with its status bits on top,
 //                       then the counts' exclusive prefix
 //   doc_rng   [G][2] i64  documents that start in the chunk
@@ -176,7 +179,10 @@ constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
 //   pv        [G][kChunk] i32    per pre-token: its symbol; -1 - o4 for a
 //                                lane-merged one whose bytes start at 4 o4 in
 //                                mbytes; -1 - 2^20 - q for the q-th
-//                                wave-merged one
+//                                wave-merged one; -1 - 2^21 - g for a
+//                                lane-merged one whose tokens are those of
+//                                another entry with the same bytes, at 4 g in
+//                                res (g counted from the start of res)
 //   cntk      [G][kChunk] u8     token count of each lane-merged pre-token
 //   miss      [G][kMissMax] u32  merge-loop list, a region per length bucket
 //                                (kBucketBase), in no particular order:
@@ -184,14 +190,36 @@ constexpr int kMetaBucket = 4;     // 4 entries: list entries per length bucket
 //                                k the pre-token's index), start | len << 13 |
 //                                overhang << 26 (wave-merged)
 //   mt        [G][kMaxLong] i32  token count of each wave-merged entry
+//   dref      [G][kMissMax] u32  lane-merged entry: kDrefOwner if it is merged
+//                                itself, else the entry-table slot of its bytes
+//   olist     [G][kMissMax] u64  the entries merged themselves, per bucket
+//                                region: entry | slot << 32 (kNoSlot: none)
+//   dt        [DS][16] u8  the call's entry table, DS = dedup_slots(G): per
+//                          slot the key (u64: hash bits and length above the
+//                          owner's offset / 4 in mbytes, counted from its
+//                          start), that offset again (u32) and, once the
+//                          owner is merged, its token count (u32)
 //   mbytes    [G][kMissSpan] u8   bytes of the lane-merged entries, each at a
 //                                  4-byte aligned offset o
 //   res       [G][kMissSpan] i32  its tokens, from o on
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the wave merge, position-indexed
 struct EncLayout {
-  size_t meta, tot, off, doc_rng, doc_pt, pv, cntk, miss, mt, mbytes, res, gsym, grank, total;
+  size_t meta, tot, off, doc_rng, doc_pt, pv, cntk, miss, mt, dref, olist, dt, mbytes, res, gsym,
+      grank, total;
 };
+
+// Slots of the call's entry table: a power of two >= 32 per chunk.
+inline size_t dedup_slots(size_t G) {
+  size_t n = 4096;
+  while (n < 32 * G) n *= 2;
+  return n;
+}
+constexpr uint32_t kDrefOwner = 0xFFFFFFFFu;
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+// pv values below -2^21 address res across chunks; the entry table is used
+// only while every such value fits an int32.
+constexpr int64_t kDedupMaxChunks = ((1ll << 31) - (1ll << 21)) / (kMissSpan / 4) - 1;
 inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   EncLayout L;
   const size_t G = (size_t)enc_chunks(n_bytes);
@@ -210,6 +238,9 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.cntk = take((size_t)kChunk * G);
   L.miss = take(4 * (size_t)kMissMax * G);
   L.mt = take(4 * (size_t)kMaxLong * G);
+  L.dref = take(4 * (size_t)kMissMax * G);
+  L.olist = take(8 * (size_t)kMissMax * G);
+  L.dt = take(16 * dedup_slots(G));
   L.mbytes = take((size_t)kMissSpan * G + 64);  // word loads read a little past the end
   L.res = take(4 * (size_t)kMissSpan * G + 64);
   L.gsym = take(4 * (size_t)n_bytes);
@@ -263,6 +294,11 @@ struct EncodeArgs {
   uint8_t *cntk;
   uint32_t *miss;
   int32_t *mt;
+  uint32_t *dref;
+  uint64_t *olist;
+  unsigned long long *dt;    // the call's entry table (dedup_slots(n_chunks) slots)
+  uint32_t dt_mask;          // slots - 1
+  int dedup;                 // 0: every lane-merged entry is merged (no table)
   uint8_t *mbytes;
   int32_t *res;
   int32_t *gsym;
@@ -301,7 +337,7 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
                         int32_t *status, hipStream_t stream);
 // The encode pipeline for n_bytes > 0 (bpe_encode.hip).  ev: nullptr, or
 // kEncStages + 1 events recorded before the first kernel and after each.
-constexpr int kEncStages = 6;
+constexpr int kEncStages = 8;
 extern const char *const kEncStageNames[kEncStages];
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
 // The decode pipeline for n_ids > 0 (bpe_decode.hip), events as for encode.

@@ -294,3 +294,38 @@ def test_long_pretokens_out_of_order_table(dev):
     docs = [bytes(rng.choice([48, 49, 50], int(n)).astype(np.uint8)) for n in (40, 300, 2048, 2500)]
     data, off = batch_from_docs(docs)
     check_encode(model, table, data, off)
+
+
+def _word_docs(rng, words, n_docs, doc_bytes):
+    docs = []
+    for _ in range(n_docs):
+        parts, n = [], 0
+        while n < doc_bytes:
+            w = words[int(rng.integers(0, len(words)))]
+            parts.append(w)
+            n += len(w) + 1
+        docs.append(b" ".join(parts))
+    return docs
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_repeated_long_pretokens(dev, seed):
+    # a few dozen 8-31 letter words (pre-tokens of 9-32 bytes with their
+    # space, mostly absent from the word tables) repeated across hundreds of
+    # chunks: most lane-merged entries share their bytes with an earlier one
+    # in the same call, many of them at once; words that differ only in their
+    # last letter, or are prefixes of one another, must stay apart.  Two
+    # calls in a row, so that the second starts from the first's leftovers.
+    model, table = model_pair("multilingual")
+    rng = np.random.default_rng(seed)
+    letters = np.frombuffer(b"abcdefghijklmnopqrstuvwxyz", dtype=np.uint8)
+    words = []
+    for _ in range(40):
+        n = int(rng.integers(8, 32))
+        w = bytes(rng.choice(letters, n))
+        words += [w, w[:-1] + bytes([97 + (w[-1] - 96) % 26]), w[: max(8, n - 3)]]
+    for _ in range(2):
+        docs = _word_docs(rng, words, 160, int(rng.integers(6000, 12000)))
+        data, off = batch_from_docs(docs)
+        check_encode(model, table, data, off)
+        words = [w[::-1] for w in words]
