@@ -9,8 +9,8 @@ throughput workload: 4,096 documents of 64 KiB (256 MiB) with the
 32,000-merge table.  The CPU baseline is the oracle, single-threaded, on the
 first documents of the same batch; its IDs are checked against the GPU's.
 
-The roofline object covers one encode call: its four kernels run back to
-back on one stream, and the library's stage timing (HIP events recorded
+The roofline object covers one encode call: its kernels run back to back
+on one stream, and the library's stage timing (HIP events recorded
 between them during the timed steps) gives each kernel's average duration.
 Algorithmic bytes are the call's: the input read once, the IDs and the
 per-document offsets written once (N + 4T + 16(D + 1)).  Measured HBM
