@@ -252,6 +252,8 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.meta = (int32_t *)(ws + L.meta);
   a.tot = (int64_t *)(ws + L.tot);
   a.off = (int64_t *)(ws + L.off);
+  a.bsum = (int64_t *)(ws + L.bsum);
+  a.boff = (int64_t *)(ws + L.boff);
   a.doc_rng = (int64_t *)(ws + L.doc_rng);
   a.doc_pt = (int32_t *)(ws + L.doc_pt);
   a.pv = (int32_t *)(ws + L.pv);

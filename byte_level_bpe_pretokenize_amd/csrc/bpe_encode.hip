@@ -11,7 +11,8 @@
 //   k_merge   one wave per chunk runs the merge loop for the list: one
 //             pre-token per lane in registers for <= kLaneMax bytes, the
 //             whole wave for longer ones; writes token counts and tokens.
-//   k_offsets exclusive scan of the per-chunk token counts.
+//   k_offsets exclusive scan of the per-chunk token counts within blocks of
+//             1024 chunks; k_bscan the same over the blocks' counts.
 //   k_emit    writes each chunk's IDs at its offset, and the per-document
 //             offsets.
 //
@@ -35,7 +36,8 @@ namespace {
 
 constexpr int WG = kEncThreads;             // k_find: 4 waves
 constexpr int MWG = 64;                     // k_merge: one wave per chunk
-constexpr int OWG = 1024;                   // k_offsets: one workgroup
+constexpr int OWG = 1024;                   // k_bscan: one workgroup
+constexpr int kScanBlock = 1024;            // chunks per k_offsets workgroup
 constexpr int WIN = kChunk + kHalo;         // window positions [0, WIN)
 constexpr int SB_WORDS = kChunk / 32;       // start bits of the owned positions
 constexpr int DB_OFF = 32;                  // document-start bit of position p is bit p + DB_OFF
@@ -1532,11 +1534,33 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
 
 // ---- k_offsets ---------------------------------------------------------------
 
-// Exclusive prefix of the per-chunk token counts, and the status word from
-// the chunks' status bits (one workgroup).
-__global__ void __launch_bounds__(OWG) k_offsets(EncodeArgs a) {
+// Block b of kScanBlock chunks, one chunk per thread (coalesced): the
+// exclusive prefix of its token counts within the block, and the block's
+// count with the OR of its status bits on top.
+__global__ void __launch_bounds__(kScanBlock) k_offsets(EncodeArgs a) {
+  __shared__ int64_t red64[kScanBlock / 64];
+  __shared__ int32_t bits_w[kScanBlock / 64];
+  const int64_t c = (int64_t)blockIdx.x * kScanBlock + threadIdx.x;
+  const int64_t v = c < a.n_chunks ? a.tot[c] : 0;
+  int64_t total;
+  const int64_t ex = block_excl_sum<int64_t, kScanBlock>(v & kCountMask, red64, &total);
+  if (c < a.n_chunks) a.off[c] = ex;
+  int32_t b32 = (int32_t)(v >> kCountBits);
+  for (int d = 32; d >= 1; d >>= 1) b32 |= __shfl_xor(b32, d, 64);
+  if (lane_id() == 0) bits_w[wave_id()] = b32;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t all = 0;
+    for (int w = 0; w < kScanBlock / 64; ++w) all |= bits_w[w];
+    a.bsum[blockIdx.x] = total | ((int64_t)all << kCountBits);
+  }
+}
+
+// Exclusive prefix of the blocks' counts, and the status word from their
+// status bits (one workgroup).  A chunk's offset is off[c] + boff[c / kScanBlock].
+__global__ void __launch_bounds__(OWG) k_bscan(EncodeArgs a) {
   __shared__ int64_t red64[OWG / 64];
-  chunk_offsets<OWG>(a.tot, a.off, a.n_chunks, a.status, red64);
+  chunk_offsets<OWG>(a.bsum, a.boff, (a.n_chunks + kScanBlock - 1) / kScanBlock, a.status, red64);
 }
 
 // ---- k_emit -------------------------------------------------------------------
@@ -1590,7 +1614,7 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
   const int dk0 = dlo + tid < dhi ? a.doc_pt[dlo + tid] : 0;
   const int n_pt = a.meta[kMetaInts * c + kMetaPretokens];
-  const int64_t base = a.off[c];
+  const int64_t base = a.off[c] + a.boff[c / kScanBlock];
   if (tid == 0) s.n_long = 0;
   bool overflow = false;
   auto put = [&](int64_t w, int32_t sym) {
@@ -1735,9 +1759,9 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
   return hipGetLastError();
 }
 
-const char *const kEncStageNames[kEncStages] = {"k_find",       "k_dedup",   "k_merge",
-                                                "k_merge_wide", "k_merge_long", "k_dupfill",
-                                                "k_offsets",    "k_emit"};
+const char *const kEncStageNames[kEncStages] = {
+    "k_find", "k_dedup", "k_merge", "k_merge_wide", "k_merge_long", "k_dupfill", "k_offsets",
+    "k_bscan", "k_emit"};
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev) {
   const unsigned G = (unsigned)a.n_chunks;
@@ -1771,7 +1795,10 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
   mark();
   hipLaunchKernelGGL(k_dupfill, dim3(G4), dim3(256), 0, stream, a);
   mark();
-  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(OWG), 0, stream, a);
+  hipLaunchKernelGGL(k_offsets, dim3((unsigned)((G + kScanBlock - 1) / kScanBlock)),
+                     dim3(kScanBlock), 0, stream, a);
+  mark();
+  hipLaunchKernelGGL(k_bscan, dim3(1), dim3(OWG), 0, stream, a);
   mark();
   hipLaunchKernelGGL(k_emit, dim3(G), dim3(EWG), 0, stream, a);
   mark();

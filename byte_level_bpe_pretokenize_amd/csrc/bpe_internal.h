@@ -173,7 +173,10 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //                          lane-merged bytes, list entries per length bucket,
 //                          owners per lane-merged bucket
 //   tot, off  [G] i64   token count per chunk with its status bits on top,
-//                       then the counts' exclusive prefix
+//                       then the counts' exclusive prefix within its block of
+//                       1024 chunks
+//   bsum, boff [B] i64  per block of 1024 chunks: its count with the status
+//                       bits on top, then the blocks' exclusive prefix
 //   doc_rng   [G][2] i64  documents that start in the chunk
 //   doc_pt    [D] i32   index of each document's first pre-token in its chunk
 //   pv        [G][kChunk] i32    per pre-token: its symbol; -1 - o4 for a
@@ -205,7 +208,7 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the wave merge, position-indexed
 struct EncLayout {
-  size_t meta, tot, off, doc_rng, doc_pt, pv, cntk, miss, mt, dref, olist, dt, mbytes, res, gsym,
+  size_t meta, tot, off, bsum, boff, doc_rng, doc_pt, pv, cntk, miss, mt, dref, olist, dt, mbytes, res, gsym,
       grank, total;
 };
 
@@ -232,6 +235,9 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.meta = take(4 * kMetaInts * G);
   L.tot = take(8 * (G + 16));  // the offset scan reads whole groups of 16
   L.off = take(8 * (G + 16));
+  const size_t B = (G + 1023) / 1024;
+  L.bsum = take(8 * (B + 16));
+  L.boff = take(8 * (B + 16));
   L.doc_rng = take(16 * G);
   L.doc_pt = take(4 * (size_t)(n_docs + 1));
   L.pv = take(4 * (size_t)kChunk * G);
@@ -288,6 +294,8 @@ struct EncodeArgs {
   int32_t *meta;
   int64_t *tot;
   int64_t *off;
+  int64_t *bsum;
+  int64_t *boff;
   int64_t *doc_rng;
   int32_t *doc_pt;
   int32_t *pv;
@@ -326,6 +334,8 @@ struct DecodeArgs {
   int64_t vocab;
   int64_t *tot;
   int64_t *off;
+  int64_t *bsum;
+  int64_t *boff;
   int32_t *status;
   int64_t n_chunks;
 };
@@ -337,7 +347,7 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
                         int32_t *status, hipStream_t stream);
 // The encode pipeline for n_bytes > 0 (bpe_encode.hip).  ev: nullptr, or
 // kEncStages + 1 events recorded before the first kernel and after each.
-constexpr int kEncStages = 8;
+constexpr int kEncStages = 9;
 extern const char *const kEncStageNames[kEncStages];
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
 // The decode pipeline for n_ids > 0 (bpe_decode.hip), events as for encode.
