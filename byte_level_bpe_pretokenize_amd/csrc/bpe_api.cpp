@@ -37,6 +37,9 @@ struct bpe_model {
   int64_t max_token = 1;
   int64_t *d_exp_off = nullptr;
   uint8_t *d_exp_bytes = nullptr;
+  uint4 *d_exp16 = nullptr;     // first 16 bytes of each expansion, zero padded
+  uint4 *d_exp16b = nullptr;    // its bytes 16..31, zero padded
+  int32_t *d_exp_len = nullptr;
   int32_t *d_inv_map = nullptr;
   int64_t inv_size = 0;
   int32_t win_d[4] = {0, 0, 0, 0};  // window radii by pre-token class (EncodeArgs::win_d)
@@ -91,6 +94,9 @@ void free_model(bpe_model *m) {
   if (m->d_lwords) (void)hipFree(m->d_lwords);
   if (m->d_exp_off) (void)hipFree(m->d_exp_off);
   if (m->d_exp_bytes) (void)hipFree(m->d_exp_bytes);
+  if (m->d_exp16) (void)hipFree(m->d_exp16);
+  if (m->d_exp16b) (void)hipFree(m->d_exp16b);
+  if (m->d_exp_len) (void)hipFree(m->d_exp_len);
   if (m->d_inv_map) (void)hipFree(m->d_inv_map);
   delete m;
 }
@@ -611,6 +617,21 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
     m->max_token = *std::max_element(len.begin(), len.end());
     rc = upload(&m->d_exp_off, exp_off.data(), exp_off.size(), stream);
     if (rc == BPE_OK) rc = upload(&m->d_exp_bytes, exp_bytes.data(), exp_bytes.size(), stream);
+    if (rc == BPE_OK) {
+      std::vector<uint4> e16((size_t)V), e16b((size_t)V);
+      std::vector<int32_t> elen((size_t)V);
+      for (int64_t v = 0; v < V; ++v) {
+        uint8_t w[32] = {};
+        std::memcpy(w, &exp_bytes[(size_t)exp_off[(size_t)v]],
+                    (size_t)std::min<int64_t>(32, len[(size_t)v]));
+        std::memcpy(&e16[(size_t)v], w, 16);
+        std::memcpy(&e16b[(size_t)v], w + 16, 16);
+        elen[(size_t)v] = (int32_t)len[(size_t)v];
+      }
+      rc = upload(&m->d_exp16, e16.data(), e16.size(), stream);
+      if (rc == BPE_OK) rc = upload(&m->d_exp16b, e16b.data(), e16b.size(), stream);
+      if (rc == BPE_OK) rc = upload(&m->d_exp_len, elen.data(), elen.size(), stream);
+    }
     if (rc == BPE_OK && id_map) {
       inv.assign((size_t)max_id + 1, -1);
       for (int64_t v = 0; v < V; ++v) inv[(size_t)id_map[v]] = (int32_t)v;
@@ -694,11 +715,17 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
   a.byte_off = d_byte_off;
   a.exp_off = model->d_exp_off;
   a.exp_bytes = model->d_exp_bytes;
+  a.exp16 = model->d_exp16;
+  a.exp16b = model->d_exp16b;
+  a.exp_len = model->d_exp_len;
   a.inv_map = model->d_inv_map;
   a.inv_size = model->inv_size;
   a.vocab = model->V;
   a.tot = (int64_t *)(ws + L.tot);
   a.off = (int64_t *)(ws + L.off);
+  a.bsum = (int64_t *)(ws + L.bsum);
+  a.boff = (int64_t *)(ws + L.boff);
+  a.dlo = (int64_t *)(ws + L.dlo);
   a.status = d_status;
   a.n_chunks = dec_chunks(n_ids);
   if (launch_decode(a, stream, call_events(model, BPE_OP_DECODE)) != hipSuccess) return BPE_EHIP;

@@ -6,7 +6,9 @@
 // workgroup:
 //   k_dec_len    per chunk: the byte count of its IDs and its status bits
 //                (an ID outside the vocabulary, bad document offsets).
-//   k_dec_scan   exclusive scan of the chunk byte counts; the status word.
+//   k_dec_scan   exclusive scan of the chunk byte counts within blocks of
+//                1024 chunks; k_dec_bscan the same over the blocks' counts,
+//                and the status word.
 //   k_dec_write  per chunk: the byte offset of each ID in the chunk, the
 //                bytes, and the per-document byte offsets.
 //
@@ -48,6 +50,15 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   const int64_t c = blockIdx.x;
   const int64_t i0 = c * kDecChunk;
   const int cnt = (int)min<int64_t>(kDecChunk, a.n_ids - i0);
+  // the first document whose IDs start at or after this chunk's (and, from
+  // the last chunk, after the last ID): the documents that start in each chunk
+  if (wave_id() == 0) {
+    const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, i0);
+    if (lane_id() == 0) a.dlo[c] = d;
+  } else if (wave_id() == 1 && c == a.n_chunks - 1) {
+    const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, a.n_ids);
+    if (lane_id() == 0) a.dlo[c + 1] = d;
+  }
   bool bad_id = false;
   int64_t mine = 0;
   // consecutive threads read consecutive IDs
@@ -57,7 +68,7 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
     if (k < cnt) {
       const int32_t sym = dec_sym(a, a.ids[i0 + k]);
       if (sym < 0) bad_id = true;
-      else mine += a.exp_off[sym + 1] - a.exp_off[sym];
+      else mine += a.exp_len[sym];
     }
   }
   int64_t total;
@@ -67,9 +78,31 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   if (tid == 0) a.tot[c] = total | ((int64_t)bits << kCountBits);
 }
 
-__global__ void __launch_bounds__(SWG) k_dec_scan(DecodeArgs a) {
+__global__ void __launch_bounds__(kScanBlock) k_dec_scan(DecodeArgs a) {
+  block_offsets(a.tot, a.off, a.bsum, a.n_chunks);
+}
+
+// A chunk's output offset is off[c] + boff[c / kScanBlock].
+__global__ void __launch_bounds__(SWG) k_dec_bscan(DecodeArgs a) {
   __shared__ int64_t red64[SWG / 64];
-  chunk_offsets<SWG>(a.tot, a.off, a.n_chunks, a.status, red64);
+  chunk_offsets<SWG>(a.bsum, a.boff, (a.n_chunks + kScanBlock - 1) / kScanBlock, a.status, red64);
+}
+
+// OR the expansion bytes b (zero from byte len on, len <= 16) into the
+// zeroed LDS stage at byte offset w: up to five 32-bit words, shifted across
+// word boundaries (tokens never overlap, so every byte is ORed once).
+__device__ __forceinline__ void stage_or16(uint32_t *stage32, int w, uint4 b, int len) {
+  const uint32_t sh = 32u - 8u * (uint32_t)(w & 3);  // 32: already aligned
+  const int nw = ((w & 3) + len + 3) >> 2;
+  uint32_t *d = stage32 + (w >> 2);
+  auto word = [sh](uint32_t hi, uint32_t lo) {
+    return (uint32_t)((((uint64_t)hi << 32) | lo) >> sh);
+  };
+  atomicOr(d, word(b.x, 0u));
+  if (nw > 1) atomicOr(d + 1, word(b.y, b.x));
+  if (nw > 2) atomicOr(d + 2, word(b.z, b.y));
+  if (nw > 3) atomicOr(d + 3, word(b.w, b.z));
+  if (nw > 4) atomicOr(d + 4, word(0u, b.w));
 }
 
 constexpr int kDecStage = 16384;  // output bytes a chunk may stage in LDS
@@ -78,40 +111,39 @@ struct WriteShared {
   int32_t len[kDecChunk];
   int64_t excl[DWG];
   int64_t red64[DWG / 64];
-  int64_t o_lo, o_hi;
-  alignas(16) uint8_t stage[kDecStage + 16];
+  alignas(16) uint32_t stage32[(kDecStage + 16) / 4];
 };
 
 __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
   __shared__ WriteShared s;
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int tid = threadIdx.x;
   const int64_t c = blockIdx.x;
   const int64_t i0 = c * kDecChunk;
   const int cnt = (int)min<int64_t>(kDecChunk, a.n_ids - i0);
-  const int64_t base = a.off[c];
-  if (wave == 0) {
-    const int64_t olo = wave_lower_bound(a.id_off, a.n_docs + 1, i0);
-    const int64_t ohi = wave_lower_bound(a.id_off, a.n_docs + 1, i0 + cnt);
-    if (lane == 0) {
-      s.o_lo = olo;
-      s.o_hi = max(olo, ohi);
-    }
-  }
-  // lengths read coalesced into LDS, then each thread takes DPT in a row
+  const int64_t base = a.off[c] + a.boff[c / kScanBlock];
+  const int64_t o_lo = a.dlo[c], o_hi = max(o_lo, a.dlo[c + 1]);
+  for (int i = tid; i < (kDecStage + 16) / 4; i += DWG) s.stage32[i] = 0u;
+  // each thread takes DPT IDs in a row: their symbols, lengths and first 16
+  // bytes, all loads in flight together (lengths also to LDS for the
+  // document offsets)
+  const int k0 = tid * DPT;
+  int32_t sym[DPT], len[DPT];
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) {
-    const int k = j * DWG + tid;
-    int32_t len = 0;
-    if (k < cnt) {
-      const int32_t sym = dec_sym(a, a.ids[i0 + k]);
-      if (sym >= 0) len = (int32_t)(a.exp_off[sym + 1] - a.exp_off[sym]);
-    }
-    s.len[k] = len;
-  }
-  __syncthreads();
+  for (int j = 0; j < DPT; ++j) sym[j] = k0 + j < cnt ? dec_sym(a, a.ids[i0 + k0 + j]) : -1;
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) len[j] = sym[j] >= 0 ? a.exp_len[sym[j]] : 0;
+  // (named values, not an array: an array of them ends up in scratch)
+  auto first16 = [&a](int32_t v) { return v >= 0 ? a.exp16[v] : uint4{0u, 0u, 0u, 0u}; };
+  static_assert(DPT == 8, "eight IDs per thread");
+  const uint4 b0 = first16(sym[0]), b1 = first16(sym[1]), b2 = first16(sym[2]),
+              b3 = first16(sym[3]), b4 = first16(sym[4]), b5 = first16(sym[5]),
+              b6 = first16(sym[6]), b7 = first16(sym[7]);
   int64_t mine = 0;
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) mine += s.len[tid * DPT + j];
+  for (int j = 0; j < DPT; ++j) {
+    s.len[k0 + j] = len[j];
+    mine += len[j];
+  }
   int64_t total;
   const int64_t ex = block_excl_sum<int64_t, DWG>(mine, s.red64, &total);
   s.excl[tid] = ex;
@@ -121,27 +153,48 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
     // aligned 16-byte blocks (bytes at the two ends)
     const int lead = (int)(((uintptr_t)(a.out + base)) & 15u);
     int w = lead + (int)ex;
-    for (int j = 0; j < DPT; ++j) {
-      const int k = tid * DPT + j;
-      const int32_t len = s.len[k];
-      if (len > 0) {
-        const int32_t sym = dec_sym(a, a.ids[i0 + k]);
-        const uint8_t *src = a.exp_bytes + a.exp_off[sym];
-        for (int q = 0; q < len; ++q) s.stage[w + q] = src[q];
+    bool longer = false;
+    auto put = [&](uint4 b, int32_t n) {
+      if (n > 0 && n <= 16) stage_or16(s.stage32, w, b, n);
+      longer |= n > 16;
+      w += n;
+    };
+    put(b0, len[0]);
+    put(b1, len[1]);
+    put(b2, len[2]);
+    put(b3, len[3]);
+    put(b4, len[4]);
+    put(b5, len[5]);
+    put(b6, len[6]);
+    put(b7, len[7]);
+    if (longer) {  // expansions of more than 16 bytes: up to 32 from the two
+                   // 16-byte tables, longer ones byte by byte
+      w = lead + (int)ex;
+      for (int j = 0; j < DPT; ++j) {
+        const int32_t n = len[j];
+        if (n > 32) {
+          const uint8_t *src = a.exp_bytes + a.exp_off[sym[j]];
+          for (int q = 0; q < n; ++q)
+            atomicOr(&s.stage32[(w + q) >> 2], (uint32_t)src[q] << (8 * ((w + q) & 3)));
+        } else if (n > 16) {
+          stage_or16(s.stage32, w, a.exp16[sym[j]], 16);
+          stage_or16(s.stage32, w + 16, a.exp16b[sym[j]], n - 16);
+        }
+        w += n;
       }
-      w += len;
     }
     __syncthreads();
+    const uint8_t *stage = reinterpret_cast<const uint8_t *>(s.stage32);
     const int nblk = (lead + (int)total + 15) >> 4;
     uint8_t *g0 = a.out + base - lead;  // 16-byte aligned
     for (int blk = tid; blk < nblk; blk += DWG) {
       const int lo = 16 * blk;
       const int64_t gpos = base - lead + lo;  // output index of stage[lo]
       if (lo >= lead && lo + 16 <= lead + (int)total && gpos + 16 <= a.out_cap) {
-        *reinterpret_cast<u32x4 *>(g0 + lo) = *reinterpret_cast<const u32x4 *>(&s.stage[lo]);
+        *reinterpret_cast<u32x4 *>(g0 + lo) = *reinterpret_cast<const u32x4 *>(&stage[lo]);
       } else {
         for (int q = max(lo, lead); q < min(lo + 16, lead + (int)total); ++q) {
-          if (base - lead + q < a.out_cap) g0[q] = s.stage[q];
+          if (base - lead + q < a.out_cap) g0[q] = stage[q];
           else overflow = true;
         }
       }
@@ -164,7 +217,7 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
   }
   if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_BYTES_CAPACITY);
   __syncthreads();
-  for (int64_t d = s.o_lo + tid; d < s.o_hi; d += DWG) {
+  for (int64_t d = o_lo + tid; d < o_hi; d += DWG) {
     const int64_t k64 = a.id_off[d] - i0;
     const int k = (int)min<int64_t>(max<int64_t>(k64, 0), kDecChunk - 1);
     const int t = k / DPT;
@@ -173,22 +226,26 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
     a.byte_off[d] = base + before;
   }
   if (c == a.n_chunks - 1)
-    for (int64_t d = s.o_hi + tid; d <= a.n_docs; d += DWG) a.byte_off[d] = base + total;
+    for (int64_t d = o_hi + tid; d <= a.n_docs; d += DWG) a.byte_off[d] = base + total;
 }
 
 }  // namespace
 
-const char *const kDecStageNames[kDecStages] = {"k_dec_len", "k_dec_scan", "k_dec_write"};
+const char *const kDecStageNames[kDecStages] = {"k_dec_len", "k_dec_scan", "k_dec_bscan",
+                                                "k_dec_write"};
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t *ev) {
   const unsigned G = (unsigned)a.n_chunks;
   if (ev) (void)hipEventRecord(ev[0], stream);
   hipLaunchKernelGGL(k_dec_len, dim3(G), dim3(DWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[1], stream);
-  hipLaunchKernelGGL(k_dec_scan, dim3(1), dim3(SWG), 0, stream, a);
+  hipLaunchKernelGGL(k_dec_scan, dim3((G + kScanBlock - 1) / kScanBlock), dim3(kScanBlock), 0,
+                     stream, a);
   if (ev) (void)hipEventRecord(ev[2], stream);
-  hipLaunchKernelGGL(k_dec_write, dim3(G), dim3(DWG), 0, stream, a);
+  hipLaunchKernelGGL(k_dec_bscan, dim3(1), dim3(SWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[3], stream);
+  hipLaunchKernelGGL(k_dec_write, dim3(G), dim3(DWG), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[4], stream);
   return hipGetLastError();
 }
 

@@ -219,6 +219,31 @@ __device__ void chunk_offsets(const int64_t *__restrict__ tot, int64_t *__restri
   }
 }
 
+// First level of an offset scan: block blockIdx.x of kScanBlock chunks, one
+// chunk per thread (coalesced), of the per-chunk counts tot[0..n) (status
+// bits above kCountBits): the exclusive prefix within the block into off,
+// and the block's count with the OR of its status bits into bsum.  The
+// second level is chunk_offsets over bsum.
+__device__ void block_offsets(const int64_t *__restrict__ tot, int64_t *__restrict__ off,
+                              int64_t *__restrict__ bsum, int64_t n) {
+  __shared__ int64_t red64[kScanBlock / 64];
+  __shared__ int32_t bits_w[kScanBlock / 64];
+  const int64_t c = (int64_t)blockIdx.x * kScanBlock + threadIdx.x;
+  const int64_t v = c < n ? tot[c] : 0;
+  int64_t total;
+  const int64_t ex = block_excl_sum<int64_t, kScanBlock>(v & kCountMask, red64, &total);
+  if (c < n) off[c] = ex;
+  int32_t b32 = (int32_t)(v >> kCountBits);
+  for (int d = 32; d >= 1; d >>= 1) b32 |= __shfl_xor(b32, d, 64);
+  if (lane_id() == 0) bits_w[wave_id()] = b32;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t all = 0;
+    for (int w = 0; w < kScanBlock / 64; ++w) all |= bits_w[w];
+    bsum[blockIdx.x] = total | ((int64_t)all << kCountBits);
+  }
+}
+
 __device__ __forceinline__ int32_t out_id(const int32_t *id_map, int32_t sym) {
   return id_map ? id_map[sym] : sym;
 }

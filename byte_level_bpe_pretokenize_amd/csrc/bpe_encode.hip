@@ -37,7 +37,6 @@ namespace {
 constexpr int WG = kEncThreads;             // k_find: 4 waves
 constexpr int MWG = 64;                     // k_merge: one wave per chunk
 constexpr int OWG = 1024;                   // k_bscan: one workgroup
-constexpr int kScanBlock = 1024;            // chunks per k_offsets workgroup
 constexpr int WIN = kChunk + kHalo;         // window positions [0, WIN)
 constexpr int SB_WORDS = kChunk / 32;       // start bits of the owned positions
 constexpr int DB_OFF = 32;                  // document-start bit of position p is bit p + DB_OFF
@@ -1534,26 +1533,10 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
 
 // ---- k_offsets ---------------------------------------------------------------
 
-// Block b of kScanBlock chunks, one chunk per thread (coalesced): the
-// exclusive prefix of its token counts within the block, and the block's
-// count with the OR of its status bits on top.
+// The first level of the offset scan (block_offsets): blocks of kScanBlock
+// chunks.
 __global__ void __launch_bounds__(kScanBlock) k_offsets(EncodeArgs a) {
-  __shared__ int64_t red64[kScanBlock / 64];
-  __shared__ int32_t bits_w[kScanBlock / 64];
-  const int64_t c = (int64_t)blockIdx.x * kScanBlock + threadIdx.x;
-  const int64_t v = c < a.n_chunks ? a.tot[c] : 0;
-  int64_t total;
-  const int64_t ex = block_excl_sum<int64_t, kScanBlock>(v & kCountMask, red64, &total);
-  if (c < a.n_chunks) a.off[c] = ex;
-  int32_t b32 = (int32_t)(v >> kCountBits);
-  for (int d = 32; d >= 1; d >>= 1) b32 |= __shfl_xor(b32, d, 64);
-  if (lane_id() == 0) bits_w[wave_id()] = b32;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t all = 0;
-    for (int w = 0; w < kScanBlock / 64; ++w) all |= bits_w[w];
-    a.bsum[blockIdx.x] = total | ((int64_t)all << kCountBits);
-  }
+  block_offsets(a.tot, a.off, a.bsum, a.n_chunks);
 }
 
 // Exclusive prefix of the blocks' counts, and the status word from their

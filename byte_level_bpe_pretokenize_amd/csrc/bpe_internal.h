@@ -212,6 +212,9 @@ struct EncLayout {
       grank, total;
 };
 
+// Chunks per workgroup of the first level of the offset scans.
+constexpr int kScanBlock = 1024;
+
 // Slots of the call's entry table: a power of two >= 32 per chunk.
 inline size_t dedup_slots(size_t G) {
   size_t n = 4096;
@@ -235,7 +238,7 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.meta = take(4 * kMetaInts * G);
   L.tot = take(8 * (G + 16));  // the offset scan reads whole groups of 16
   L.off = take(8 * (G + 16));
-  const size_t B = (G + 1023) / 1024;
+  const size_t B = (G + kScanBlock - 1) / kScanBlock;
   L.bsum = take(8 * (B + 16));
   L.boff = take(8 * (B + 16));
   L.doc_rng = take(16 * G);
@@ -256,16 +259,24 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
 }
 
 // Decode workspace: tot, off [G] i64 (byte count per chunk of IDs with the
-// chunk's status bits on top, then the counts' exclusive prefix).
+// chunk's status bits on top, then the counts' exclusive prefix within its
+// block of kScanBlock chunks); dlo [G + 1] i64 (the first document whose IDs
+// start at or after chunk g's first ID, and after the last ID); bsum, boff
+// [B] i64 (per block: its count with the status bits on top, then the blocks'
+// exclusive prefix).
 struct DecLayout {
-  size_t tot, off, total;
+  size_t tot, off, dlo, bsum, boff, total;
 };
 inline DecLayout dec_layout(int64_t n_ids) {
   DecLayout L;
   const size_t G = (size_t)dec_chunks(n_ids);
-  L.tot = 0;  // the offset scan reads whole groups of 16
-  L.off = align256(8 * (G + 16));
-  L.total = L.off + align256(8 * (G + 16));
+  const size_t B = (G + kScanBlock - 1) / kScanBlock;
+  L.tot = 0;
+  L.off = align256(8 * G);
+  L.dlo = L.off + align256(8 * G);
+  L.bsum = L.dlo + align256(8 * (G + 1));
+  L.boff = L.bsum + align256(8 * (B + 16));  // the block scan reads whole groups of 16
+  L.total = L.boff + align256(8 * (B + 16));
   return L;
 }
 
@@ -329,6 +340,9 @@ struct DecodeArgs {
   int64_t *byte_off;
   const int64_t *exp_off;    // [V + 1]
   const uint8_t *exp_bytes;  // expansions back to back
+  const uint4 *exp16;        // [V]: the first 16 bytes of each expansion, zero padded
+  const uint4 *exp16b;       // [V]: its bytes 16..31, zero padded
+  const int32_t *exp_len;    // [V]: each expansion's length
   const int32_t *inv_map;    // nullptr = identity; else [inv_size], -1 = no symbol
   int64_t inv_size;
   int64_t vocab;
@@ -336,6 +350,7 @@ struct DecodeArgs {
   int64_t *off;
   int64_t *bsum;
   int64_t *boff;
+  int64_t *dlo;
   int32_t *status;
   int64_t n_chunks;
 };
@@ -351,7 +366,7 @@ constexpr int kEncStages = 9;
 extern const char *const kEncStageNames[kEncStages];
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
 // The decode pipeline for n_ids > 0 (bpe_decode.hip), events as for encode.
-constexpr int kDecStages = 3;
+constexpr int kDecStages = 4;
 extern const char *const kDecStageNames[kDecStages];
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t *ev);
 

@@ -95,7 +95,7 @@ def test_workspace_sizes():
 def test_stage_timing_queries():
     L = _lib.load()
     assert L.bpe_stage_count(_lib.OP_ENCODE) == 9
-    assert L.bpe_stage_count(_lib.OP_DECODE) == 3
+    assert L.bpe_stage_count(_lib.OP_DECODE) == 4
     assert L.bpe_stage_count(7) == -1
     names = [L.bpe_stage_name(_lib.OP_ENCODE, k).decode() for k in range(9)]
     assert names == ["k_find", "k_dedup", "k_merge", "k_merge_wide", "k_merge_long", "k_dupfill",
