@@ -1477,6 +1477,188 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
   return n;
 }
 
+// ---- run-length rounds ----------------------------------------------------
+// A pre-token made of few runs of one repeated byte (a letter repeated
+// hundreds of times, say) is merged on its runs, (symbol, count), instead of
+// symbol by symbol.  Each round is an exact R4 round: the lowest rank r of
+// the pairs present, all its occurrences left to right without overlap,
+// taken on the sequence as it was at the round's start.  The pair of rank r
+// is one pair (A, B):
+//  - A == B occurs only inside runs of A: a run of k becomes (Z, k / 2) and,
+//    for odd k, one A after it;
+//  - A != B occurs only where a run of A meets a run of B (no two such
+//    occurrences overlap): each side gives up one symbol to a Z between them.
+// Z = 256 + r.  Equal neighbouring runs are then joined.  The run list lives
+// in LongShared's arrays; a round that would leave more than kRleMax runs
+// gives up (false), and the entry is merged symbol by symbol from its bytes.
+
+constexpr int kRleMax = 512;
+
+struct RleView {
+  int32_t *sym, *cnt;    // [kRleMax] the runs
+  int32_t *rin, *rbd;    // [kRleMax] rank of (sym, sym) inside a run of 2 or more, and of
+                         //   (sym[i], sym[i + 1]); kRankInf where none
+  int32_t *esym, *ecnt;  // [2 kRleMax] the runs a round emits, before joining
+};
+
+__device__ __forceinline__ RleView rle_view(LongShared &L) {
+  static_assert(2 * kRleMax + 2 * kRleMax <= kLdsLong, "run arrays fit LongShared");
+  return RleView{L.y, L.y + kRleMax, L.r, L.r + kRleMax, L.y + 2 * kRleMax, L.r + 2 * kRleMax};
+}
+
+// Wave-wide exclusive prefix of v over the lanes, plus a carry; *all gets
+// the wave's sum.
+__device__ __forceinline__ int wave_excl(int v, int carry, int *all) {
+  const int inc = wave_incl_sum(v);
+  *all = __shfl(inc, 63, 64);
+  return carry + inc - v;
+}
+
+__device__ void rle_ranks(const RleView &V, int R, const RankTable &tab) {
+  for (int i = lane_id(); i < R; i += 64) {
+    const int32_t x = V.sym[i];
+    V.rin[i] = V.cnt[i] >= 2 ? rank_of(tab, (uint32_t)x, (uint32_t)x) : kRankInf;
+    V.rbd[i] = i + 1 < R ? rank_of(tab, (uint32_t)x, (uint32_t)V.sym[i + 1]) : kRankInf;
+  }
+}
+
+// The runs of bytes[0, n) (global), if there are at most kRleMax of them and
+// at least 8 bytes per run on average; returns their number, or -1.
+__device__ int rle_build(const RleView &V, const uint8_t *bytes, int64_t n) {
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1;
+  int R = 0;
+  int32_t prev = -1;
+  for (int64_t i0 = 0; i0 < n; i0 += 64) {
+    const int64_t i = i0 + lane;
+    const int32_t b = i < n ? (int32_t)bytes[i] : -2;
+    int32_t left = __shfl_up(b, 1, 64);
+    if (lane == 0) left = prev;
+    const bool head = i < n && b != left;
+    const uint64_t bm = __ballot(head);
+    const int k = R + __popcll(bm & below);
+    if (head && k < kRleMax) {
+      V.sym[k] = b;
+      V.cnt[k] = (int32_t)i;  // start for now
+    }
+    R += __popcll(bm);
+    prev = __shfl(b, 63, 64);
+    if (R > kRleMax || (int64_t)R * 8 > n) return -1;  // R only grows
+  }
+  for (int k = lane; k < R; k += 64)
+    V.cnt[k] = (int32_t)((k + 1 < R ? (int64_t)V.cnt[k + 1] : n) - V.cnt[k]);
+  return R;
+}
+
+// Rounds on the R runs in V until no pair has a rank; returns the final
+// number of runs, or -1 if a round would leave more than kRleMax.
+__device__ int rle_merge(const RleView &V, int R, const RankTable &tab) {
+  const int lane = lane_id();
+  rle_ranks(V, R, tab);
+  for (;;) {
+    // the lowest rank, and whether it is a pair of equal symbols
+    int32_t r = kRankInf;
+    for (int i = lane; i < R; i += 64) r = min(r, min(V.rin[i], V.rbd[i]));
+    for (int d = 32; d >= 1; d >>= 1) r = min(r, __shfl_xor(r, d, 64));
+    if (r == kRankInf) return R;
+    int32_t A = -1, B = -1;
+    for (int i0 = 0; i0 < R && A < 0; i0 += 64) {
+      const int i = i0 + lane;
+      const bool in = i < R && V.rin[i] == r, bd = i < R && V.rbd[i] == r;
+      const uint64_t m = __ballot(in || bd);
+      if (m) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        const int32_t a_l = in ? V.sym[i] : (bd ? V.sym[i] : -1);
+        const int32_t b_l = in ? V.sym[i] : (bd ? V.sym[i + 1] : -1);
+        A = __shfl(a_l, src, 64);
+        B = __shfl(b_l, src, 64);
+      }
+    }
+    const int32_t Z = 256 + r;
+    // emit: every run gives at most two
+    int E = 0;
+    for (int i0 = 0; i0 < R; i0 += 64) {
+      const int i = i0 + lane;
+      int32_t s0 = -1, c0 = 0, s1 = -1, c1 = 0;
+      if (i < R) {
+        const int32_t x = V.sym[i], k = V.cnt[i];
+        if (A == B) {
+          const bool m = x == A && k >= 2;
+          s0 = m ? Z : x;
+          c0 = m ? k / 2 : k;
+          if (m && (k & 1)) {
+            s1 = A;
+            c1 = 1;
+          }
+        } else {
+          const int dl = (i > 0 && V.sym[i - 1] == A && x == B) ? 1 : 0;
+          const int dr = (i + 1 < R && x == A && V.sym[i + 1] == B) ? 1 : 0;
+          if (k - dl - dr > 0) {
+            s0 = x;
+            c0 = k - dl - dr;
+          }
+          if (dr) {
+            s1 = Z;
+            c1 = 1;
+          }
+        }
+      }
+      const int ne = (s0 >= 0) + (s1 >= 0);
+      int all;
+      int o = wave_excl(ne, E, &all);
+      if (s0 >= 0) {
+        V.esym[o] = s0;
+        V.ecnt[o] = c0;
+        ++o;
+      }
+      if (s1 >= 0) {
+        V.esym[o] = s1;
+        V.ecnt[o] = c1;
+      }
+      E += all;
+    }
+    // join equal neighbours: heads take their symbol and the count before
+    // them; a head's count is the next head's minus its own
+    int Rn = 0, before = 0;
+    for (int j0 = 0; j0 < E; j0 += 64) {
+      const int j = j0 + lane;
+      const bool in = j < E;
+      const int32_t x = in ? V.esym[j] : -1;
+      const int32_t k = in ? V.ecnt[j] : 0;
+      const bool head = in && (j == 0 || V.esym[j - 1] != x);
+      int all_h, all_c;
+      const int h = wave_excl(head ? 1 : 0, Rn, &all_h);
+      const int p = wave_excl(k, before, &all_c);
+      if (head && h < kRleMax) {
+        V.sym[h] = x;
+        V.cnt[h] = p;
+      }
+      Rn += all_h;
+      before += all_c;
+    }
+    if (Rn > kRleMax) return -1;
+    for (int h = lane; h < Rn; h += 64) {
+      // groups run in order and every lane reads before it writes: cnt[h + 1]
+      // still holds a start here
+      const int32_t next = h + 1 < Rn ? V.cnt[h + 1] : before;
+      V.cnt[h] = next - V.cnt[h];
+    }
+    R = Rn;
+    rle_ranks(V, R, tab);
+  }
+}
+
+// The R runs in V written out as symbols to out[0 ..); returns their number.
+__device__ int64_t rle_expand(const RleView &V, int R, int32_t *out) {
+  int64_t p = 0;
+  for (int k = 0; k < R; ++k) {
+    const int32_t x = V.sym[k], n = V.cnt[k];
+    for (int q = lane_id(); q < n; q += 64) out[p + q] = x;
+    p += n;
+  }
+  return p;
+}
+
 struct LongGroupShared {
   MergeShared g;
   LongShared L;
@@ -1506,8 +1688,17 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
       const int64_t gs = c0 + me_start(e);
       const int64_t ge = me_over(e) ? wave_global_end(a, gs, c0 + WIN) : gs + me_len(e);
       const int64_t len = ge - gs;
-      int64_t nt;
-      if (len <= kLdsLong) {
+      int64_t nt = -1;
+      {
+        // few long runs of one byte: merged on the runs
+        const RleView V = rle_view(s.L);
+        const int R = rle_build(V, a.bytes + gs, len);
+        const int Rf = R > 0 ? rle_merge(V, R, t) : -1;
+        if (Rf > 0) nt = rle_expand(V, Rf, a.gsym + gs);
+      }
+      if (nt >= 0) {
+        // done
+      } else if (len <= kLdsLong) {
 #pragma unroll 8
         for (int i = lane; i < len; i += MWG) s.L.y[i] = a.bytes[gs + i];
         __syncthreads();

@@ -329,3 +329,35 @@ def test_repeated_long_pretokens(dev, seed):
         data, off = batch_from_docs(docs)
         check_encode(model, table, data, off)
         words = [w[::-1] for w in words]
+
+
+def _run_docs(rng, letters, n_docs, max_runs, lo, hi):
+    docs = []
+    for _ in range(n_docs):
+        k = int(rng.integers(1, max_runs + 1))
+        seq = rng.choice(np.frombuffer(letters, dtype=np.uint8), k)
+        docs.append(b"".join(bytes([int(c)]) * int(rng.integers(lo, hi + 1)) for c in seq))
+    return docs
+
+
+def test_run_length_rounds(dev):
+    # long pre-tokens made of runs of one letter: merged on their runs.
+    # Runs of 9 of two letters alternating split on every pair merge, so the
+    # longest ones outgrow the run list and are merged symbol by symbol
+    # instead; runs of 8-40 of three letters meet at run boundaries.
+    model, table = model_pair("adversarial")
+    rng = np.random.default_rng(41)
+    docs = [(b"a" * 9 + b"b" * 9) * n for n in (4, 30, 75, 150, 300)]
+    docs += [b" " + b"q" * 9 + (b"r" * 9 + b"q" * 9) * n for n in (10, 100, 200)]
+    docs += _run_docs(rng, b"abc", 60, 120, 8, 40)
+    data, off = batch_from_docs(docs)
+    ids, ioff = check_encode(model, table, data, off)
+    out, _, st = gpu_decode(model, ids, ioff)
+    assert st == 0 and np.array_equal(out, data)
+    # random acyclic tables over a, b, c, ranks out of creation order: the
+    # pairs at run boundaries and inside runs in every order
+    for seed in range(4):
+        rng = np.random.default_rng(100 + seed)
+        merges = _random_acyclic_table(rng, 40)
+        m, t = Model(merges), O.Table(merges)
+        check_encode(m, t, *batch_from_docs(_run_docs(rng, b"abc", 40, 60, 8, 30)))
