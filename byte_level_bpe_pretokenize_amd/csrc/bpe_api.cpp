@@ -269,6 +269,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.mbytes = ws + L.mbytes;
   a.dref = (uint32_t *)(ws + L.dref);
   a.olist = (uint64_t *)(ws + L.olist);
+  a.dstat = (uint32_t *)(ws + L.dstat);
   a.dt = (unsigned long long *)(ws + L.dt);
   a.dt_mask = (uint32_t)(dedup_slots((size_t)enc_chunks(n_bytes)) - 1);
   a.dedup = enc_chunks(n_bytes) <= kDedupMaxChunks ? 1 : 0;

@@ -724,6 +724,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     m[kMetaMisses] = n_miss;
     m[kMetaStatus] = any_bad ? (int32_t)BPE_STATUS_BAD_DOC_OFFSETS : 0;
     m[kMetaBytes] = nbytes;
+    if (c == 0) a.dstat[0] = 0u;
     a.doc_rng[2 * c] = s.o_lo;
     a.doc_rng[2 * c + 1] = s.o_hi;
   }
@@ -919,8 +920,8 @@ struct LaneGroup {
 };
 
 // Group q (chunks kGroup q ..) of the merge-loop lists; false past the last.
-// The counts of buckets 0-2 are their owners' (entries the call's table
-// found first), listed in olist.
+// The counts of buckets kDedupFrom..2 are their owners', listed in olist
+// (all their entries, in a chunk that did not go through the call's table).
 __device__ __forceinline__ bool lane_group(const EncodeArgs &a, int64_t q, LaneGroup &G) {
   G.cg = q * kGroup;
   if (G.cg >= a.n_chunks) return false;
@@ -932,6 +933,14 @@ __device__ __forceinline__ bool lane_group(const EncodeArgs &a, int64_t q, LaneG
       G.cnt[f][b] = f < G.nf ? a.meta[kMetaInts * (G.cg + f) + (deduped(b) ? kMetaOwners : kMetaBucket) + b]
                              : 0;
   return true;
+}
+
+// The list entry of bucket b, chunk c at idx: its miss entry and, for an
+// owner in the call's entry table, its slot (else kNoSlot).
+__device__ __forceinline__ uint64_t group_list_entry(const EncodeArgs &a, int b, int64_t c,
+                                                     int idx) {
+  return deduped(b) ? a.olist[c * kMissMax + idx]
+                    : ((uint64_t)kNoSlot << 32 | a.miss[c * kMissMax + idx]);
 }
 
 __device__ __forceinline__ int64_t wave_group(int64_t first) {
@@ -970,8 +979,7 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
         idx = base + g - pre[k];
       }
     const int64_t c = G.cg + f;
-    const uint64_t ol = deduped(b) ? a.olist[c * kMissMax + idx]
-                                   : ((uint64_t)kNoSlot << 32 | a.miss[c * kMissMax + idx]);
+    const uint64_t ol = group_list_entry(a, b, c, idx);
     const uint32_t e = (uint32_t)ol, slot = (uint32_t)(ol >> 32);
     const int o4 = le_o4(e), o = o4 << 2;  // 4-byte aligned
     const uint32_t *src = reinterpret_cast<const uint32_t *>(a.mbytes + c * kMissSpan + o);
@@ -1024,9 +1032,8 @@ __device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b
           idx = base + g - pre[k];
         }
       c[h] = G.cg + f[h];
-      const uint64_t ol = !v[h]        ? ((uint64_t)kNoSlot << 32)
-                          : deduped(b) ? a.olist[c[h] * kMissMax + idx]
-                                       : ((uint64_t)kNoSlot << 32 | a.miss[c[h] * kMissMax + idx]);
+      const uint64_t ol =
+          v[h] ? group_list_entry(a, b, c[h], idx) : ((uint64_t)kNoSlot << 32);
       const uint32_t e = (uint32_t)ol;
       sl[h] = (uint32_t)(ol >> 32);
       o[h] = le_o4(e) << 2;
@@ -1134,7 +1141,7 @@ __global__ void __launch_bounds__(MWG *kMergeWaves) k_merge_wide(EncodeArgs a) {
 // merged, its token count.  A key whose upper half matches is checked against
 // the bytes at g.
 
-constexpr int kDedupProbes = 64;
+constexpr int kDedupProbes = 16;  // slots tried before an entry merges itself
 constexpr int kDedupSeed = 256;    // chunks of the first, seeding launch
 
 // The bytes (at most 32) at 4-byte offset q of mbytes as eight words, zero
@@ -1174,13 +1181,30 @@ __device__ __forceinline__ int lane_list_index(int g, int n0, int n01, int &b) {
 // One wave per chunk of [c_lo, c_hi): every lane-merged entry becomes an
 // owner (merged itself, listed in olist by bucket) or takes the owner of its
 // bytes (dref = the slot); the owner counts go to meta.
-__global__ void __launch_bounds__(256) k_dedup(EncodeArgs a, int64_t c_lo, int64_t c_hi) {
+__global__ void __launch_bounds__(256) k_dedup(EncodeArgs a, int64_t c_lo, int64_t c_hi,
+                                               int seeding) {
   const int64_t c = c_lo + (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave_id());
   if (c >= c_hi) return;
   const int lane = lane_id();
   const int32_t *m = a.meta + kMetaInts * c;
+  // after the first kDedupSeed chunks: if at their rate of new byte strings
+  // the call's would overfill the table four times over, the text has few
+  // repeats, and the rest is merged without the table
+  const uint64_t slots = (uint64_t)a.dt_mask + 1;
+  const bool use = a.dedup && (seeding || (uint64_t)a.dstat[0] * (uint64_t)a.n_chunks <=
+                                              4 * slots * (uint64_t)kDedupSeed);
+  int claims = 0;
   const int n0 = dedup_count(m, 0), n01 = n0 + dedup_count(m, 1);
   const int n = n01 + dedup_count(m, 2);
+  if (!use) {  // every entry merges itself: the lists as they are
+    for (int g = lane; g < n; g += 64) {
+      int b;
+      const int idx = lane_list_index(g, n0, n01, b);
+      a.olist[c * kMissMax + idx] = (uint64_t)a.miss[c * kMissMax + idx] | ((uint64_t)kNoSlot << 32);
+    }
+    if (lane < 3) a.meta[kMetaInts * c + kMetaOwners + lane] = m[kMetaBucket + lane];
+    return;
+  }
   const uint32_t q0 = (uint32_t)c * (kMissSpan / 4);  // the chunk's mbytes, in words
   const uint64_t below = (1ull << lane) - 1;
   uint32_t *dt32 = reinterpret_cast<uint32_t *>(a.dt);
@@ -1194,7 +1218,7 @@ __global__ void __launch_bounds__(256) k_dedup(EncodeArgs a, int64_t c_lo, int64
     const uint32_t e = v ? a.miss[c * kMissMax + idx] : 0u;
     bool owner = true;
     uint32_t slot = kNoSlot;
-    if (v && a.dedup) {
+    if (v) {
       const int len = le_len(e);
       const uint32_t gme = q0 + le_o4(e);
       uint32_t w[8];
@@ -1222,6 +1246,7 @@ __global__ void __launch_bounds__(256) k_dedup(EncodeArgs a, int64_t c_lo, int64
           if (old == 0ull) {
             slot = s;  // this entry owns its bytes
             dt32[4 * (size_t)s + 2] = gme;
+            ++claims;
             active = false;
           } else {
             x = old;  // taken meanwhile: look at the key that won
@@ -1256,11 +1281,13 @@ __global__ void __launch_bounds__(256) k_dedup(EncodeArgs a, int64_t c_lo, int64
     own1 += __popcll(o1);
     own2 += __popcll(o2);
   }
+  claims = wave_sum(claims);
   if (lane == 0) {
     int32_t *mm = a.meta + kMetaInts * c;
     mm[kMetaOwners + 0] = own0;
     mm[kMetaOwners + 1] = own1;
     mm[kMetaOwners + 2] = own2;
+    if (seeding && claims) atomicAdd(&a.dstat[0], (uint32_t)claims);
   }
 }
 
@@ -1269,7 +1296,7 @@ __global__ void __launch_bounds__(256) k_dedup(EncodeArgs a, int64_t c_lo, int64
 // count grows by theirs.
 __global__ void __launch_bounds__(256) k_dupfill(EncodeArgs a) {
   const int64_t c = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave_id());
-  if (c >= a.n_chunks || !a.dedup) return;
+  if (c >= a.n_chunks) return;
   const int lane = lane_id();
   const int32_t *m = a.meta + kMetaInts * c;
   const int n0 = dedup_count(m, 0), n01 = n0 + dedup_count(m, 1);
@@ -1952,10 +1979,10 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
     // rest start, so that few CAS on one slot at once
     const int64_t seed = min((int64_t)kDedupSeed, a.n_chunks);
     hipLaunchKernelGGL(k_dedup, dim3((unsigned)((seed + 3) / 4)), dim3(256), 0, stream, a,
-                       (int64_t)0, seed);
+                       (int64_t)0, seed, 1);
     if (a.n_chunks > seed)
       hipLaunchKernelGGL(k_dedup, dim3((unsigned)((a.n_chunks - seed + 3) / 4)), dim3(256), 0,
-                         stream, a, seed, a.n_chunks);
+                         stream, a, seed, a.n_chunks, 0);
   }
   mark();
   const unsigned LG = (G + kGroup * kMergeWaves - 1) / (kGroup * kMergeWaves);

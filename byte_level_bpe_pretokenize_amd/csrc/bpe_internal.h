@@ -197,6 +197,7 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //                                itself, else the entry-table slot of its bytes
 //   olist     [G][kMissMax] u64  the entries merged themselves, per bucket
 //                                region: entry | slot << 32 (kNoSlot: none)
+//   dstat     u32       entry-table claims of the first (seeding) launch
 //   dt        [DS][16] u8  the call's entry table, DS = dedup_slots(G): per
 //                          slot the key (u64: hash bits and length above the
 //                          owner's offset / 4 in mbytes, counted from its
@@ -208,7 +209,7 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the wave merge, position-indexed
 struct EncLayout {
-  size_t meta, tot, off, bsum, boff, doc_rng, doc_pt, pv, cntk, miss, mt, dref, olist, dt, mbytes, res, gsym,
+  size_t meta, tot, off, bsum, boff, doc_rng, doc_pt, pv, cntk, miss, mt, dref, olist, dstat, dt, mbytes, res, gsym,
       grank, total;
 };
 
@@ -249,6 +250,7 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.mt = take(4 * (size_t)kMaxLong * G);
   L.dref = take(4 * (size_t)kMissMax * G);
   L.olist = take(8 * (size_t)kMissMax * G);
+  L.dstat = take(8);
   L.dt = take(16 * dedup_slots(G));
   L.mbytes = take((size_t)kMissSpan * G + 64);  // word loads read a little past the end
   L.res = take(4 * (size_t)kMissSpan * G + 64);
@@ -315,6 +317,7 @@ struct EncodeArgs {
   int32_t *mt;
   uint32_t *dref;
   uint64_t *olist;
+  uint32_t *dstat;           // entry-table claims of the seeding launch
   unsigned long long *dt;    // the call's entry table (dedup_slots(n_chunks) slots)
   uint32_t dt_mask;          // slots - 1
   int dedup;                 // 0: every lane-merged entry is merged (no table)

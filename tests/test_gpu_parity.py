@@ -361,3 +361,18 @@ def test_run_length_rounds(dev):
         merges = _random_acyclic_table(rng, 40)
         m, t = Model(merges), O.Table(merges)
         check_encode(m, t, *batch_from_docs(_run_docs(rng, b"abc", 40, 60, 8, 30)))
+
+
+def test_unique_long_pretokens(dev):
+    # 4 MiB of random 9-20 letter words, nearly all distinct: after the first
+    # 256 chunks the per-call entry table is left out (it would overfill), and
+    # every entry merges itself; the first chunks still go through it
+    model, table = model_pair("throughput")
+    rng = np.random.default_rng(57)
+    letters = np.frombuffer(b"abcdefghijklmnopqrstuvwxyz", dtype=np.uint8)
+    docs = []
+    for _ in range(64):
+        words = [bytes(rng.choice(letters, int(rng.integers(9, 21)))) for _ in range(4400)]
+        docs.append(b" ".join(words)[:65536])
+    data, off = batch_from_docs(docs)
+    check_encode(model, table, data, off)
