@@ -1,20 +1,25 @@
 // bpe_encode.hip -- byte-level BPE encode for gfx950.
 //
 // The input is cut into 4 KiB chunks; a chunk owns every pre-token whose
-// first byte lies in it.  Four kernels, none of which waits on another
-// workgroup:
-//   k_find    scan a chunk (coalesced bytes into LDS, a byte class and a
-//             start bit per byte from a 3-byte window), list its pre-tokens
-//             in order (prefix popcount), and resolve each one that is a
-//             single byte or a whole entry of the word table; the others go
-//             to the chunk's ordered merge-loop list.
-//   k_merge   one wave per chunk runs the merge loop for the list: one
-//             pre-token per lane in registers for <= kLaneMax bytes, the
-//             whole wave for longer ones; writes token counts and tokens.
-//   k_offsets exclusive scan of the per-chunk token counts within blocks of
-//             1024 chunks; k_bscan the same over the blocks' counts.
-//   k_emit    writes each chunk's IDs at its offset, and the per-document
-//             offsets.
+// first byte lies in it.  Nine kernels in order on one stream, none of which
+// waits on another workgroup:
+//   k_find        scan a chunk (coalesced bytes into LDS, a byte class and a
+//                 start bit per byte from a 3-byte window), list its
+//                 pre-tokens in order (prefix popcount), and resolve each one
+//                 that is a single byte or a whole entry of a word table; the
+//                 others go to the chunk's merge-loop list, by length bucket.
+//   k_dedup       the call's table of 9-32 byte entries: the first entry with
+//                 given bytes owns them, later ones take its result.
+//   k_merge       (persistent) the merge loop for 2-8 byte entries and the
+//                 9-16 byte owners, one pre-token per lane in LDS columns.
+//   k_merge_wide  the same for the 17-32 byte owners.
+//   k_merge_long  longer pre-tokens, one wave each (runs of one byte on
+//                 their run lengths).
+//   k_dupfill     token counts of the entries that took an owner's result.
+//   k_offsets     exclusive scan of the per-chunk token counts within blocks
+//                 of 1024 chunks; k_bscan the same over the blocks' counts.
+//   k_emit        writes each chunk's IDs at its offset, and the
+//                 per-document offsets.
 //
 // Sources: "Tokenization LLM: ... C++" (glitch4techs.com), sections
 // "Technical analysis" (the split into words, numbers, punctuation and
@@ -35,7 +40,7 @@ namespace bpe {
 namespace {
 
 constexpr int WG = kEncThreads;             // k_find: 4 waves
-constexpr int MWG = 64;                     // k_merge: one wave per chunk
+constexpr int MWG = 64;                     // threads of a merge wave
 constexpr int OWG = 1024;                   // k_bscan: one workgroup
 constexpr int WIN = kChunk + kHalo;         // window positions [0, WIN)
 constexpr int SB_WORDS = kChunk / 32;       // start bits of the owned positions
