@@ -403,11 +403,14 @@ __device__ __forceinline__ uint32_t start_bits16(const uint32_t w[5], uint32_t d
 
 // ---- k_find -------------------------------------------------------------------
 
+constexpr int kFindList = 1024;  // misses listed for the dense miss pass (more: in place)
+
 struct FindShared {
   alignas(16) uint8_t B[16 + WIN + 32];  // B[16 + p] = byte at window position p
   uint32_t SB[SB_WORDS];                 // pre-token start bits, positions [0, kChunk)
   uint32_t DB[DB_WORDS];                 // document start bits, positions [-32, WIN)
   uint16_t PS[kChunk + 2];               // owned pre-token starts in order, then the end
+  uint16_t ML[kFindList];                // the pre-tokens that missed the word tables
   u32x4 LM[kShortMax + 1];               // masks of the first len bytes of three words
   Red<WG> r;
   int64_t o_lo, o_hi;
@@ -664,13 +667,14 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
 
   // 4. each thread resolves every WG-th pre-token: a single byte is its own
   //    token; a pre-token that is a whole word-table entry takes its symbol;
-  //    the others go to the merge-loop list, a slot in their bucket's region
-  //    and, up to kLaneMax bytes, their bytes in the dense region (both taken
-  //    by LDS atomics: pv names the entry, so order does not matter)
+  //    the others are listed (bit j of `missed`: pre-token tid + j WG) and
+  //    then handled by the whole workgroup in list order, so that the
+  //    miss path runs on full waves
   int32_t *pv = a.pv + c * kChunk;
   uint32_t *ml = a.miss + c * kMissMax;
   uint32_t *mb = reinterpret_cast<uint32_t *>(a.mbytes + c * kMissSpan);
-  for (int k = tid; k < n_pt; k += WG) {
+  uint32_t missed = 0;
+  for (int k = tid, j = 0; k < n_pt; k += WG, ++j) {
     const bool over = overhang && k == n_pt - 1;
     const int st = s.PS[k];
     const int len = over ? 0 : (int)s.PS[k + 1] - st;
@@ -686,10 +690,16 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
         v = long_lookup(s, a, st, len);
       }
     }
-    if (v >= 0) {
-      pv[k] = v;
-      continue;
-    }
+    if (v >= 0) pv[k] = v;
+    else missed |= 1u << j;
+  }
+  // each miss takes a slot in its bucket's region and, up to kLaneMax bytes,
+  // its bytes in the dense region (both by LDS atomics: pv names the entry,
+  // so order does not matter)
+  auto miss = [&](int k) {
+    const bool over = overhang && k == n_pt - 1;
+    const int st = s.PS[k];
+    const int len = over ? 0 : (int)s.PS[k + 1] - st;
     const int b = bucket_of(len, over);
     const int idx = atomicAdd(&s.cnt[b], 1);
     const int base = b == 0 ? kBucketBase[0] : b == 1 ? kBucketBase[1] : b == 2 ? kBucketBase[2] : kBucketBase[3];
@@ -697,23 +707,72 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
       // the bytes, as words at a 4-byte aligned offset of the dense region
       const int o = atomicAdd(&s.nbytes, (len + 3) & ~3);
       uint32_t *dst = mb + (o >> 2);
-      if (len <= kShortMax) {
-        dst[0] = w0;
-        if (len > 4) dst[1] = w1;
-        if (len > 8) dst[2] = w2;
-      } else {
-        const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
-        const int q = (16 + st) >> 2;
-        const uint32_t sh = (uint32_t)((16 + st) & 3);
-        for (int i = 0; 4 * i < len; ++i)
-          dst[i] = __builtin_amdgcn_alignbyte(B32[q + i + 1], B32[q + i], sh);
-      }
+      const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
+      const int q = (16 + st) >> 2;
+      const uint32_t sh = (uint32_t)((16 + st) & 3);
+      for (int i = 0; 4 * i < len; ++i)
+        dst[i] = __builtin_amdgcn_alignbyte(B32[q + i + 1], B32[q + i], sh);
       ml[base + idx] = lane_entry(o >> 2, len, k);
       pv[k] = -1 - (o >> 2);
     } else {
       ml[base + idx] = miss_entry(st, len, over);
       pv[k] = -1 - kPvLong - idx;
     }
+  };
+  int n_miss;
+  const int mex = block_excl_sum<int, WG>(__popc(missed), s.r.red, &n_miss);
+  {
+    int o = mex;
+    for (uint32_t m = missed; m; m &= m - 1, ++o)
+      if (o < kFindList) s.ML[o] = (uint16_t)(tid + (__ffs(m) - 1) * WG);
+  }
+  __syncthreads();
+  // the listed misses, 64 to a wave: slots and dense offsets from wave
+  // prefix sums, one LDS atomic per bucket and wave
+  const int n_list = min(n_miss, kFindList);
+  for (int i0 = wave * 64; i0 < n_list; i0 += WG) {
+    const int i = i0 + lane;
+    const bool act = i < n_list;
+    const int k = act ? (int)s.ML[i] : 0;
+    const bool over = act && overhang && k == n_pt - 1;
+    const int st = s.PS[k];
+    const int len = act ? (over ? 0 : (int)s.PS[k + 1] - st) : 0;
+    const int b = bucket_of(len, over);
+    const uint64_t below = (1ull << lane) - 1;
+    int idx = 0;
+#pragma unroll
+    for (int bb = 0; bb < kBuckets; ++bb) {
+      const uint64_t m = __ballot(act && b == bb);
+      int first = 0;
+      if (m && lane == __ffsll((unsigned long long)m) - 1) first = atomicAdd(&s.cnt[bb], __popcll(m));
+      first = __shfl(first, m ? __ffsll((unsigned long long)m) - 1 : 0, 64);
+      if (b == bb) idx = first + __popcll(m & below);
+    }
+    const int sz = act && b < 3 ? (len + 3) & ~3 : 0;
+    const int inc = wave_incl_sum(sz);
+    int obase = 0;
+    if (lane == 63 && inc) obase = atomicAdd(&s.nbytes, inc);
+    const int o = __shfl(obase, 63, 64) + inc - sz;
+    if (!act) continue;
+    const int base = b == 0 ? kBucketBase[0] : b == 1 ? kBucketBase[1] : b == 2 ? kBucketBase[2] : kBucketBase[3];
+    if (b < 3) {
+      uint32_t *dst = mb + (o >> 2);
+      const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
+      const int q = (16 + st) >> 2;
+      const uint32_t sh = (uint32_t)((16 + st) & 3);
+      for (int w = 0; 4 * w < len; ++w)
+        dst[w] = __builtin_amdgcn_alignbyte(B32[q + w + 1], B32[q + w], sh);
+      ml[base + idx] = lane_entry(o >> 2, len, k);
+      pv[k] = -1 - (o >> 2);
+    } else {
+      ml[base + idx] = miss_entry(st, len, over);
+      pv[k] = -1 - kPvLong - idx;
+    }
+  }
+  if (n_miss > kFindList) {  // the rest, each by the thread that found it
+    int o = mex;
+    for (uint32_t m = missed; m; m &= m - 1, ++o)
+      if (o >= kFindList) miss(tid + (__ffs(m) - 1) * WG);
   }
   const bool any_bad = __syncthreads_or(bad);
   const int nbytes = s.nbytes;

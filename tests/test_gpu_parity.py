@@ -376,3 +376,19 @@ def test_unique_long_pretokens(dev):
         docs.append(b" ".join(words)[:65536])
     data, off = batch_from_docs(docs)
     check_encode(model, table, data, off)
+
+
+def test_dense_misses(dev):
+    # 3-byte groups (two random bytes >= 0x80, then a digit): about 1,365
+    # two-byte merge-loop pre-tokens per 4 KiB chunk, more than the 1,024 a
+    # chunk lists for its dense miss pass; the rest are handled in place
+    model, table = model_pair("throughput")
+    rng = np.random.default_rng(73)
+    docs = []
+    for n in (5000, 20000, 40000):
+        g = np.empty((n, 3), dtype=np.uint8)
+        g[:, :2] = rng.integers(0x80, 0x100, (n, 2))
+        g[:, 2] = rng.integers(0x30, 0x3A, n)
+        docs.append(g.tobytes())
+    data, off = batch_from_docs(docs)
+    check_encode(model, table, data, off)
