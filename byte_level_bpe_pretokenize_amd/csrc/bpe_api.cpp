@@ -261,6 +261,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.bsum = (int64_t *)(ws + L.bsum);
   a.boff = (int64_t *)(ws + L.boff);
   a.doc_rng = (int64_t *)(ws + L.doc_rng);
+  a.dfirst = (int64_t *)(ws + L.dfirst);
   a.doc_pt = (int32_t *)(ws + L.doc_pt);
   a.pv = (int32_t *)(ws + L.pv);
   a.cntk = ws + L.cntk;

@@ -1,8 +1,9 @@
 // bpe_encode.hip -- byte-level BPE encode for gfx950.
 //
 // The input is cut into 4 KiB chunks; a chunk owns every pre-token whose
-// first byte lies in it.  Nine kernels in order on one stream, none of which
+// first byte lies in it.  Ten kernels in order on one stream, none of which
 // waits on another workgroup:
+//   k_docs        each chunk's first document (a binary search per chunk).
 //   k_find        scan a chunk (coalesced bytes into LDS, a byte class and a
 //                 start bit per byte from a 3-byte window), list its
 //                 pre-tokens in order (prefix popcount), and resolve each one
@@ -503,6 +504,22 @@ __device__ __forceinline__ int32_t long_lookup(const FindShared &s, const Encode
 
 // Eight waves per SIMD (latency-bound: occupancy pays for the few registers
 // this spills).
+// The first document whose offset is at or after the byte before each
+// chunk (a binary search per chunk, one thread each): k_find starts its
+// document scan there.
+__global__ void __launch_bounds__(256) k_docs(EncodeArgs a) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.n_chunks) return;
+  const int64_t key = c * kChunk - 1;
+  int64_t lo = 0, hi = a.n_docs + 1;  // first index in [lo, hi) with doc_off >= key
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (a.doc_off[mid] < key) lo = mid + 1;
+    else hi = mid;
+  }
+  a.dfirst[c] = lo;
+}
+
 __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   __shared__ FindShared s;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -567,8 +584,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   //    document at or after the byte before the chunk, then 64 offsets per
   //    load)
   if (wave == 0) {
-    int64_t d0 = wave_lower_bound(a.doc_off, a.n_docs + 1, c0 - 1);
-    d0 = min(d0, a.n_docs);
+    int64_t d0 = min(max(a.dfirst[c], (int64_t)0), a.n_docs);  // (k_docs)
     int64_t olo = d0, ohi = d0;
     for (;;) {
       const int64_t d = d0 + lane;
@@ -2025,8 +2041,8 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
 }
 
 const char *const kEncStageNames[kEncStages] = {
-    "k_find", "k_dedup", "k_merge", "k_merge_wide", "k_merge_long", "k_dupfill", "k_offsets",
-    "k_bscan", "k_emit"};
+    "k_docs",       "k_find",    "k_dedup",   "k_merge", "k_merge_wide",
+    "k_merge_long", "k_dupfill", "k_offsets", "k_bscan", "k_emit"};
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev) {
   const unsigned G = (unsigned)a.n_chunks;
@@ -2035,6 +2051,8 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
   auto mark = [&]() {
     if (ev) (void)hipEventRecord(ev[st++], stream);
   };
+  mark();
+  hipLaunchKernelGGL(k_docs, dim3((G + 255) / 256), dim3(256), 0, stream, a);
   mark();
   hipLaunchKernelGGL(k_find, dim3(G), dim3(WG), 0, stream, a);
   mark();

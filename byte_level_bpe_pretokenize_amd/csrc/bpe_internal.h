@@ -178,6 +178,8 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //   bsum, boff [B] i64  per block of 1024 chunks: its count with the status
 //                       bits on top, then the blocks' exclusive prefix
 //   doc_rng   [G][2] i64  documents that start in the chunk
+//   dfirst    [G] i64   first document whose offset is at or after the byte
+//                       before the chunk
 //   doc_pt    [D] i32   index of each document's first pre-token in its chunk
 //   pv        [G][kChunk] i32    per pre-token: its symbol; -1 - o4 for a
 //                                lane-merged one whose bytes start at 4 o4 in
@@ -209,7 +211,7 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the wave merge, position-indexed
 struct EncLayout {
-  size_t meta, tot, off, bsum, boff, doc_rng, doc_pt, pv, cntk, miss, mt, dref, olist, dstat, dt, mbytes, res, gsym,
+  size_t meta, tot, off, bsum, boff, doc_rng, dfirst, doc_pt, pv, cntk, miss, mt, dref, olist, dstat, dt, mbytes, res, gsym,
       grank, total;
 };
 
@@ -243,6 +245,7 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.bsum = take(8 * (B + 16));
   L.boff = take(8 * (B + 16));
   L.doc_rng = take(16 * G);
+  L.dfirst = take(8 * G);
   L.doc_pt = take(4 * (size_t)(n_docs + 1));
   L.pv = take(4 * (size_t)kChunk * G);
   L.cntk = take((size_t)kChunk * G);
@@ -310,6 +313,7 @@ struct EncodeArgs {
   int64_t *bsum;
   int64_t *boff;
   int64_t *doc_rng;
+  int64_t *dfirst;
   int32_t *doc_pt;
   int32_t *pv;
   uint8_t *cntk;
@@ -365,7 +369,7 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
                         int32_t *status, hipStream_t stream);
 // The encode pipeline for n_bytes > 0 (bpe_encode.hip).  ev: nullptr, or
 // kEncStages + 1 events recorded before the first kernel and after each.
-constexpr int kEncStages = 9;
+constexpr int kEncStages = 10;
 extern const char *const kEncStageNames[kEncStages];
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
 // The decode pipeline for n_ids > 0 (bpe_decode.hip), events as for encode.

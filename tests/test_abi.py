@@ -94,18 +94,18 @@ def test_workspace_sizes():
 
 def test_stage_timing_queries():
     L = _lib.load()
-    assert L.bpe_stage_count(_lib.OP_ENCODE) == 9
+    assert L.bpe_stage_count(_lib.OP_ENCODE) == 10
     assert L.bpe_stage_count(_lib.OP_DECODE) == 4
     assert L.bpe_stage_count(7) == -1
-    names = [L.bpe_stage_name(_lib.OP_ENCODE, k).decode() for k in range(9)]
-    assert names == ["k_find", "k_dedup", "k_merge", "k_merge_wide", "k_merge_long", "k_dupfill",
-                     "k_offsets", "k_bscan", "k_emit"]
-    assert L.bpe_stage_name(_lib.OP_ENCODE, 9) is None
+    names = [L.bpe_stage_name(_lib.OP_ENCODE, k).decode() for k in range(10)]
+    assert names == ["k_docs", "k_find", "k_dedup", "k_merge", "k_merge_wide", "k_merge_long",
+                     "k_dupfill", "k_offsets", "k_bscan", "k_emit"]
+    assert L.bpe_stage_name(_lib.OP_ENCODE, 10) is None
     assert L.bpe_stage_name(_lib.OP_DECODE, -1) is None
     assert L.bpe_stage_timing(None, 1) == _lib.BPE_EINVAL
-    ms = (C.c_double * 9)()
+    ms = (C.c_double * 10)()
     n = C.c_int64()
-    assert L.bpe_stage_times(None, _lib.OP_ENCODE, ms, 9, C.byref(n)) == _lib.BPE_EINVAL
+    assert L.bpe_stage_times(None, _lib.OP_ENCODE, ms, 10, C.byref(n)) == _lib.BPE_EINVAL
 
 
 def test_strerror():
