@@ -17,8 +17,9 @@ after the timed one; `ms_per_step` comes from the pass without them.
 Algorithmic bytes are the call's: the input read once, the IDs and the
 per-document offsets written once (N + 4T + 16(D + 1)).  Measured HBM
 traffic comes from profiles/traffic_<workload>.json (rocprofv3 FETCH_SIZE and
-WRITE_SIZE per call, scaled by a plain copy's counts) and is reported only
-while the kernel sources still hash to the value recorded there.
+WRITE_SIZE per call, scaled by a plain copy's counts), as do the per-kernel
+L2 hit rates (TCC_HIT / (TCC_HIT + TCC_MISS)); both are reported only while
+the kernel sources still hash to the value recorded there.
 """
 from __future__ import annotations
 
@@ -50,9 +51,10 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per encode call from the committed counter summary, or None
-    when it is missing or the kernels changed since it was taken."""
+def measured_counters(workload: str):
+    """The committed counter summary of one encode call (HBM bytes, per-kernel
+    L2 hit rates), or None when it is missing or the kernels changed since it
+    was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -60,7 +62,7 @@ def measured_traffic(workload: str):
         rec = json.load(fh)
     if rec.get("sources_sha256") != kernel_sources_sha256():
         return None
-    return int(rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"])
+    return rec
 
 
 def parse():
@@ -273,7 +275,10 @@ def main():
     sec = ms / 1e3
     alg_bytes = N + 4 * T + 16 * (D + 1)
     achieved = alg_bytes / (path_ms / 1e3) / 1e9
-    traffic = measured_traffic(args.workload)
+    counters = measured_counters(args.workload)
+    traffic = None if counters is None else int(counters["fetch_bytes_per_call"] +
+                                                counters["write_bytes_per_call"])
+    l2_hit = None if counters is None else counters.get("l2_hit_rate")
 
     # decode of the same IDs (round trip), timed the same way
     dec = {}
@@ -339,6 +344,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "l2_hit": l2_hit,
             "scope": "one encode call: " + " + ".join(kern),
             "algorithmic_bytes": alg_bytes,
             "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
