@@ -392,3 +392,22 @@ def test_dense_misses(dev):
         docs.append(g.tobytes())
     data, off = batch_from_docs(docs)
     check_encode(model, table, data, off)
+
+
+def test_decode_long_tokens(dev):
+    # tokens of 2 to 256 bytes (a repeated letter doubled by each merge) and
+    # of 3 to 48 (a three-letter word tripled): expansions past 16 and 32
+    # bytes, and chunks whose output exceeds what a workgroup stages in LDS
+    merges = [[97, 97]] + [[256 + i, 256 + i] for i in range(7)]  # a^2 .. a^256
+    merges += [[98, 99], [264, 100]]                               # "bc", "bcd"
+    merges += [[265, 265], [266, 265], [267, 267]]                 # bcd x2, x3, x6 (18 bytes)
+    model, table = Model(merges), O.Table(merges)
+    rng = np.random.default_rng(83)
+    docs = [b"a" * int(n) for n in rng.integers(1, 700, 60)]
+    docs += [b"bcd" * int(n) for n in rng.integers(1, 40, 60)]
+    docs += [b"".join(b"a" * int(rng.integers(1, 300)) + b" " + b"bcd" * int(rng.integers(1, 20)) + b" "
+                      for _ in range(50)) for _ in range(8)]
+    data, off = batch_from_docs(docs)
+    ids, ioff = check_encode(model, table, data, off)
+    out, boff, st = gpu_decode(model, ids, ioff)
+    assert st == 0 and np.array_equal(out, data) and np.array_equal(boff, off)
