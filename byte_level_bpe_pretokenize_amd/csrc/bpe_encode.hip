@@ -1853,7 +1853,6 @@ constexpr int kEmitPasses = 3;           // passes of EWG pre-tokens per round
 struct EmitShared {
   int32_t out[kOutCap + 1];              // the chunk's symbols at positions below kOutCap;
                                          // stores that place nothing go to out[kOutCap]
-  uint16_t pos[kChunk];                  // each pre-token's first position
   int32_t wtot[kEmitPasses][EWG / 64];   // token counts per pass and wave
   int64_t lw[kMaxLong];                  // wave-merged entries: position, source, count
   int64_t lsrc[kMaxLong];
@@ -1880,7 +1879,7 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int64_t c = blockIdx.x;
   const int64_t c0 = c * kChunk;
-  const int32_t *pv = a.pv + c * kChunk;
+  int32_t *pv = a.pv + c * kChunk;
   const int32_t *res = a.res + c * kMissSpan;
   // loads that need nothing else first: the first round's pv values (pv has
   // room for kChunk entries, so this reads inside it whatever the count), and
@@ -1895,6 +1894,7 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
   const int dk0 = dlo + tid < dhi ? a.doc_pt[dlo + tid] : 0;
   const int n_pt = a.meta[kMetaInts * c + kMetaPretokens];
+  const bool docs_here = dhi > dlo;
   const int64_t base = a.off[c] + a.boff[c / kScanBlock];
   if (tid == 0) s.n_long = 0;
   bool overflow = false;
@@ -1974,7 +1974,9 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
         const int32_t *src = entry_res(a, res, u);
         for (int q = 4; q < nt; ++q) s.out[w + q] = src[q];
       }
-      if (k < n_pt) s.pos[k] = (uint16_t)w;
+      // a chunk where documents start keeps each pre-token's first position
+      // in place of its pv value (read by this thread only, and already read)
+      if (docs_here && k < n_pt) pv[k] = w;
       if (k < n_pt && x < 0 && u >= kPvLong && u < kPvDup) {
         const int q = u - kPvLong;
         const uint32_t e = a.miss[c * kMissMax + kBucketBase[3] + q];
@@ -2006,10 +2008,11 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   }
   if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
   // per-document offsets: a document starting at pre-token k begins at k's
-  // first position
+  // first position (the workgroup's own stores to pv, ordered by the barrier
+  // above), one starting after the last pre-token at the chunk's end
   for (int64_t d = dlo + tid; d < dhi; d += EWG) {
     const int k = min(max(d == dlo + tid ? dk0 : a.doc_pt[d], 0), n_pt);
-    a.id_off[d] = base + (k < n_pt ? (int64_t)s.pos[k] : total);
+    a.id_off[d] = base + (k < n_pt ? (int64_t)pv[k] : total);
   }
   if (c == a.n_chunks - 1) {
     const int64_t end = base + (a.tot[c] & kCountMask);
