@@ -64,6 +64,21 @@ __device__ __forceinline__ T wave_incl_sum(T v) {
   return v;
 }
 
+// The same for 32-bit values with every lane of the wave active, in six DPP
+// adds and no LDS traffic: prefix sums within each row of 16 lanes by row
+// shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row add 0), then
+// lane 15's sum added to row 1 and row 3 (row broadcast 15), then lane 31's
+// to rows 2 and 3 (row broadcast 31).
+__device__ __forceinline__ int32_t wave_incl_sum(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive prefix sum over the workgroup; *total gets the sum.  Barriers
 // inside: every thread must call it.
 template <typename T, int NT>
