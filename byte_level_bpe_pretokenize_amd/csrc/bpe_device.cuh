@@ -79,6 +79,47 @@ __device__ __forceinline__ int32_t wave_incl_sum(int32_t v) {
   return v;
 }
 
+// Lane l's value in every lane (l the same in every lane of the wave).
+__device__ __forceinline__ int32_t lane_value(int32_t v, int l) {
+  return __builtin_amdgcn_readlane(v, l);
+}
+__device__ __forceinline__ int64_t lane_value(int64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Each lane gets the value of the lane below it, lane 0 gets fill (DPP wave
+// shift; every lane active).
+__device__ __forceinline__ int32_t wave_shift_up1(int32_t v, int32_t fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, 0x138, 0xF, 0xF, false);  // wave_shr:1
+}
+
+// Running maximum over the lanes (lane i gets the maximum of lanes 0..i),
+// every lane active: the same DPP steps as wave_incl_sum.
+__device__ __forceinline__ int32_t wave_incl_max(int32_t v) {
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x111, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x112, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x114, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x118, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x142, 0xA, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+// Minimum and maximum over the wave in every lane (every lane active): a
+// running minimum by DPP, then lane 63's.
+__device__ __forceinline__ int32_t wave_min(int32_t v) {
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x111, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x112, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x114, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x118, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x142, 0xA, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x143, 0xC, 0xF, false));
+  return lane_value(v, 63);
+}
+__device__ __forceinline__ int32_t wave_max(int32_t v) { return lane_value(wave_incl_max(v), 63); }
+
 // Exclusive prefix sum over the workgroup; *total gets the sum.  Barriers
 // inside: every thread must call it.
 template <typename T, int NT>
@@ -100,7 +141,7 @@ __device__ T block_excl_sum(T v, T *red, T *total) {
 
 template <int NT>
 __device__ int32_t block_min(int32_t v, int32_t *red) {
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
+  v = wave_min(v);
   if (lane_id() == 0) red[wave_id()] = v;
   __syncthreads();
   int32_t m = red[0];
@@ -112,7 +153,7 @@ __device__ int32_t block_min(int32_t v, int32_t *red) {
 
 template <int NT>
 __device__ int32_t block_max(int32_t v, int32_t *red) {
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 64));
+  v = wave_max(v);
   if (lane_id() == 0) red[wave_id()] = v;
   __syncthreads();
   int32_t m = red[0];

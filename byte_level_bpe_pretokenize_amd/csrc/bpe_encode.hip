@@ -593,7 +593,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
       if (p >= -1 && p < nwin) atomicOr(&s.DB[(p + DB_OFF) >> 5], 1u << ((p + DB_OFF) & 31));
       olo += __popcll(__ballot(v < c0));
       ohi += __popcll(__ballot(v < c0 + nown));
-      if (!(__shfl(v, 63, 64) < c0 + nwin)) break;
+      if (!(lane_value(v, 63) < c0 + nwin)) break;
       d0 += 64;
     }
     if (lane == 0) {
@@ -761,14 +761,14 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
       const uint64_t m = __ballot(act && b == bb);
       int first = 0;
       if (m && lane == __ffsll((unsigned long long)m) - 1) first = atomicAdd(&s.cnt[bb], __popcll(m));
-      first = __shfl(first, m ? __ffsll((unsigned long long)m) - 1 : 0, 64);
+      first = lane_value(first, m ? __ffsll((unsigned long long)m) - 1 : 0);
       if (b == bb) idx = first + __popcll(m & below);
     }
     const int sz = act && b < 3 ? (len + 3) & ~3 : 0;
     const int inc = wave_incl_sum(sz);
     int obase = 0;
     if (lane == 63 && inc) obase = atomicAdd(&s.nbytes, inc);
-    const int o = __shfl(obase, 63, 64) + inc - sz;
+    const int o = lane_value(obase, 63) + inc - sz;
     if (!act) continue;
     const int base = b == 0 ? kBucketBase[0] : b == 1 ? kBucketBase[1] : b == 2 ? kBucketBase[2] : kBucketBase[3];
     if (b < 3) {
@@ -1175,7 +1175,7 @@ __global__ void __launch_bounds__(MWG *kMergePWaves) k_merge(EncodeArgs a) {
   for (;;) {
     int q = 0;
     if (lane == 0) q = atomicAdd(&s.next, 1);
-    q = __builtin_amdgcn_readfirstlane(__shfl(q, 0, 64));
+    q = lane_value(q, 0);
     LaneGroup G;
     if (!lane_group(a, (int64_t)blockIdx.x + (int64_t)gridDim.x * q, G)) break;
     uint64_t tok = merge_bucket2<8>(a, G, 0, L, pairs);
@@ -1429,7 +1429,7 @@ __device__ int64_t wave_global_end(const EncodeArgs &a, int64_t gs, int64_t from
         break;
       }
     }
-    for (int dd = 32; dd >= 1; dd >>= 1) cand = min(cand, __shfl_xor(cand, dd, 64));
+    cand = wave_min(cand);
     if (cand != kNoStart) return q0 + cand;
   }
   return limit;
@@ -1470,7 +1470,7 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
     int32_t gmin = kRankInf;
     if (D == 0) {
       for (int i = lane; i < n; i += MWG) gmin = min(gmin, L.r[i]);
-      for (int d = 32; d >= 1; d >>= 1) gmin = min(gmin, __shfl_xor(gmin, d, 64));
+      gmin = wave_min(gmin);
       if (gmin == kRankInf) break;
     }
     // 1. the lowest pairs of their windows
@@ -1505,12 +1505,10 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
       const bool in = i < n;
       const int32_t r = in ? L.r[i] : kRankInf;
       const int32_t y = in ? L.y[i] : 0;
-      int32_t rl = __shfl_up(r, 1, 64);
-      if (lane == 0) rl = prevr;
+      const int32_t rl = wave_shift_up1(r, prevr);
       const bool bnd = in && (i == 0 || rl != r);
       int st = bnd ? i : -1;
-      for (int d = 1; d < 64; d <<= 1) st = max(st, __shfl_up(st, d, 64) | (lane >= d ? 0 : -1));
-      st = max(st, run);
+      st = max(wave_incl_max(st), run);
       const bool c = in && ((L.cand[i >> 5] >> (i & 31)) & 1u);
       const bool cs = (L.cand[st >> 5] >> (st & 31)) & 1u;
       const bool m = c && cs && ((i - st) & 1) == 0;
@@ -1526,8 +1524,8 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
       any |= bm != 0;
       out += __popcll(bk);
       prevm = (bm >> 63) & 1u;
-      prevr = __shfl(r, 63, 64);
-      run = __shfl(st, 63, 64);
+      prevr = lane_value(r, 63);
+      run = lane_value(st, 63);
     }
     if (!any) break;
     n = out;
@@ -1617,7 +1615,7 @@ __device__ __forceinline__ RleView rle_view(LongShared &L) {
 // the wave's sum.
 __device__ __forceinline__ int wave_excl(int v, int carry, int *all) {
   const int inc = wave_incl_sum(v);
-  *all = __shfl(inc, 63, 64);
+  *all = lane_value(inc, 63);
   return carry + inc - v;
 }
 
@@ -1639,8 +1637,7 @@ __device__ int rle_build(const RleView &V, const uint8_t *bytes, int64_t n) {
   for (int64_t i0 = 0; i0 < n; i0 += 64) {
     const int64_t i = i0 + lane;
     const int32_t b = i < n ? (int32_t)bytes[i] : -2;
-    int32_t left = __shfl_up(b, 1, 64);
-    if (lane == 0) left = prev;
+    const int32_t left = wave_shift_up1(b, prev);
     const bool head = i < n && b != left;
     const uint64_t bm = __ballot(head);
     const int k = R + __popcll(bm & below);
@@ -1649,7 +1646,7 @@ __device__ int rle_build(const RleView &V, const uint8_t *bytes, int64_t n) {
       V.cnt[k] = (int32_t)i;  // start for now
     }
     R += __popcll(bm);
-    prev = __shfl(b, 63, 64);
+    prev = lane_value(b, 63);
     if (R > kRleMax || (int64_t)R * 8 > n) return -1;  // R only grows
   }
   for (int k = lane; k < R; k += 64)
@@ -1666,7 +1663,7 @@ __device__ int rle_merge(const RleView &V, int R, const RankTable &tab) {
     // the lowest rank, and whether it is a pair of equal symbols
     int32_t r = kRankInf;
     for (int i = lane; i < R; i += 64) r = min(r, min(V.rin[i], V.rbd[i]));
-    for (int d = 32; d >= 1; d >>= 1) r = min(r, __shfl_xor(r, d, 64));
+    r = wave_min(r);
     if (r == kRankInf) return R;
     int32_t A = -1, B = -1;
     for (int i0 = 0; i0 < R && A < 0; i0 += 64) {
@@ -1677,8 +1674,8 @@ __device__ int rle_merge(const RleView &V, int R, const RankTable &tab) {
         const int src = __ffsll((unsigned long long)m) - 1;
         const int32_t a_l = in ? V.sym[i] : (bd ? V.sym[i] : -1);
         const int32_t b_l = in ? V.sym[i] : (bd ? V.sym[i + 1] : -1);
-        A = __shfl(a_l, src, 64);
-        B = __shfl(b_l, src, 64);
+        A = lane_value(a_l, src);
+        B = lane_value(b_l, src);
       }
     }
     const int32_t Z = 256 + r;
