@@ -279,6 +279,8 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.grank = (int32_t *)(ws + L.grank);
   a.status = d_status;
   a.n_chunks = enc_chunks(n_bytes);
+  a.doc_per = (n_docs + 1 + a.n_chunks - 1) / a.n_chunks;
+  a.dt_per = (2 * ((uint64_t)a.dt_mask + 1) + (uint64_t)a.n_chunks - 1) / (uint64_t)a.n_chunks;
   for (int k = 0; k < 4; ++k) a.win_d[k] = model->win_d[k];
   if (launch_encode(a, stream, call_events(model, BPE_OP_ENCODE)) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
@@ -730,6 +732,7 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
   a.dlo = (int64_t *)(ws + L.dlo);
   a.status = d_status;
   a.n_chunks = dec_chunks(n_ids);
+  a.doc_per = (n_docs + 1 + a.n_chunks - 1) / a.n_chunks;
   if (launch_decode(a, stream, call_events(model, BPE_OP_DECODE)) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }

@@ -38,7 +38,7 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   const int tid = threadIdx.x;
   bool bad_off = false;
   {
-    const int64_t per = (a.n_docs + 1 + gridDim.x - 1) / gridDim.x;
+    const int64_t per = a.doc_per;
     const int64_t i0 = (int64_t)blockIdx.x * per;
     for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += DWG) {
       const int64_t v = a.id_off[i];

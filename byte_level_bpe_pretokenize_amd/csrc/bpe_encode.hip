@@ -527,7 +527,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   // document offsets check, spread over the grid
   bool bad = false;
   {
-    const int64_t per = (a.n_docs + 1 + gridDim.x - 1) / gridDim.x;
+    const int64_t per = a.doc_per;
     const int64_t i0 = (int64_t)blockIdx.x * per;
     for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += WG) {
       const int64_t v = a.doc_off[i];
@@ -547,8 +547,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   if (a.dedup) {
     // this chunk's share of the call's entry table starts empty
     const uint64_t words = 2 * ((uint64_t)a.dt_mask + 1);
-    const uint64_t per = (words + a.n_chunks - 1) / (uint64_t)a.n_chunks;
-    const uint64_t lo = (uint64_t)c * per, hi = min(lo + per, words);
+    const uint64_t lo = (uint64_t)c * a.dt_per, hi = min(lo + a.dt_per, words);
     for (uint64_t i = lo + tid; i < hi; i += WG) a.dt[i] = 0ull;
   }
   if (tid < kBuckets) s.cnt[tid] = 0;
