@@ -1995,7 +1995,21 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   // the staged positions, in order
   const int nst = (int)min(total, (int64_t)kOutCap);
   if (base + nst <= a.ids_cap) {
-    for (int k = tid; k < nst; k += EWG) a.ids[base + k] = out_id(a.id_map, s.out[k]);
+    // the positions before the first 16-byte boundary of ids one per thread,
+    // then four per thread with 16-byte stores, then the rest
+    const int head = min(nst, (int)((4 - ((reinterpret_cast<uintptr_t>(a.ids + base) >> 2) & 3)) & 3));
+    const int body = (nst - head) & ~3;
+    if (tid < head) a.ids[base + tid] = out_id(a.id_map, s.out[tid]);
+    for (int k = head + 4 * tid; k < head + body; k += 4 * EWG) {
+      uint4 q;
+      q.x = (uint32_t)out_id(a.id_map, s.out[k]);
+      q.y = (uint32_t)out_id(a.id_map, s.out[k + 1]);
+      q.z = (uint32_t)out_id(a.id_map, s.out[k + 2]);
+      q.w = (uint32_t)out_id(a.id_map, s.out[k + 3]);
+      *reinterpret_cast<uint4 *>(a.ids + base + k) = q;
+    }
+    const int k = head + body + tid;
+    if (k < nst) a.ids[base + k] = out_id(a.id_map, s.out[k]);
   } else {
     for (int k = tid; k < nst; k += EWG) {
       if (base + k < a.ids_cap) a.ids[base + k] = out_id(a.id_map, s.out[k]);
