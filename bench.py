@@ -20,6 +20,11 @@ traffic comes from profiles/traffic_<workload>.json (rocprofv3 FETCH_SIZE and
 WRITE_SIZE per call, scaled by a plain copy's counts), as do the per-kernel
 L2 hit rates (TCC_HIT / (TCC_HIT + TCC_MISS)); both are reported only while
 the kernel sources still hash to the value recorded there.
+
+Beside the timed encode the line carries the decode of the same IDs
+(`decode`, a round trip) and the encode with a BOS and an EOS ID around each
+document (`special`, bpe_encode_batch_special), each timed the same way and
+checked against the plain encode.
 """
 from __future__ import annotations
 
@@ -304,6 +309,34 @@ def main():
                "achieved_GB_per_s": round((4 * T + N + 16 * (D + 1)) / (dms / 1e3) / 1e9, 1),
                "round_trip_ok": rt}
 
+    # the same encode with reserved IDs around each document (post-processing:
+    # bpe_encode_batch_special), timed the same way; with the reserved IDs
+    # taken out its IDs must be the plain encode's
+    V = model.vocab_size
+    sp_ids = torch.empty(N + 2 * D, dtype=torch.int32, device=dev)
+    sp_off = torch.empty(D + 1, dtype=torch.int64, device=dev)
+    sws = torch.empty(model.encode_special_workspace_bytes(N, D), dtype=torch.uint8, device=dev)
+    sstat = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        model.encode_batch_special_into(data, doc_off, V, V + 1, sp_ids, sp_off, sws, sstat, stream)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        model.encode_batch_special_into(data, doc_off, V, V + 1, sp_ids, sp_off, sws, sstat, stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    sms = start.elapsed_time(stop) / args.steps
+    sp_t = sp_ids[:T + 2 * D]
+    keep = (sp_t != V) & (sp_t != V + 1)
+    sp_ok = bool(int(sstat.item()) == 0
+                 and torch.equal(sp_off, id_off + 2 * torch.arange(D + 1, device=dev))
+                 and torch.equal(sp_t[keep], ids[:T])
+                 and torch.equal(sp_ids[sp_off[:-1]], torch.full((D,), V, dtype=torch.int32, device=dev))
+                 and torch.equal(sp_ids[sp_off[1:] - 1],
+                                 torch.full((D,), V + 1, dtype=torch.int32, device=dev)))
+    special = {"ms": round(sms, 4), "bos_eos_per_document": 2, "ids_match_plain": sp_ok}
+    del sws, sp_ids, sp_t, keep
+
     ids_np = ids[:T].cpu().numpy()
     id_off_np = id_off.cpu().numpy()
     fnv = None
@@ -358,6 +391,7 @@ def main():
         "cpu_baseline_all_cores": cpu_all,
         "ids_fnv1a64": fnv,
         "decode": dec,
+        "special": special,
         "ids_sha256": hashlib.sha256(ids_np.tobytes()).hexdigest()[:16],
     }
     print(json.dumps(line), flush=True)

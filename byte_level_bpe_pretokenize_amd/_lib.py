@@ -11,7 +11,8 @@ LIB_PATH = os.path.join(PKG, "libbpe.so")
 SYMBOLS = (
     "bpe_load_merges", "bpe_free", "bpe_vocab_size", "bpe_max_token_bytes",
     "bpe_encode_workspace_bytes", "bpe_encode_batch",
-    "bpe_decode_workspace_bytes", "bpe_decode_batch",
+    "bpe_encode_special_workspace_bytes", "bpe_encode_batch_special",
+    "bpe_decode_workspace_bytes", "bpe_decode_batch", "bpe_decode_batch_special",
     "bpe_stage_timing", "bpe_stage_count", "bpe_stage_name", "bpe_stage_times",
     "bpe_strerror",
 )
@@ -49,6 +50,12 @@ def load() -> C.CDLL:
     L.bpe_encode_workspace_bytes.restype = sz
     L.bpe_encode_batch.argtypes = [p, p, i64, p, i64, p, i64, p, p, sz, p, p]
     L.bpe_encode_batch.restype = i32
+    L.bpe_encode_special_workspace_bytes.argtypes = [p, i64, i64]
+    L.bpe_encode_special_workspace_bytes.restype = sz
+    L.bpe_encode_batch_special.argtypes = [p, p, i64, p, i64, i32, i32, p, i64, p, p, sz, p, p]
+    L.bpe_encode_batch_special.restype = i32
+    L.bpe_decode_batch_special.argtypes = [p, p, i64, p, i64, i32, i32, p, i64, p, p, sz, p, p]
+    L.bpe_decode_batch_special.restype = i32
     L.bpe_decode_workspace_bytes.argtypes = [p, i64, i64]
     L.bpe_decode_workspace_bytes.restype = sz
     L.bpe_decode_batch.argtypes = [p, p, i64, p, i64, p, i64, p, p, sz, p, p]

@@ -139,13 +139,62 @@ class Model:
         T = int(id_off[-1].item())
         return ids[:T], id_off
 
+    # ---- encode with reserved IDs around each document --------------------------
+    def encode_special_workspace_bytes(self, n_bytes: int, n_docs: int) -> int:
+        return int(_lib.load().bpe_encode_special_workspace_bytes(self._h, n_bytes, n_docs))
+
+    def encode_batch_special_into(self, data: torch.Tensor, doc_off: torch.Tensor, bos_id: int,
+                                  eos_id: int, ids: torch.Tensor, id_off: torch.Tensor,
+                                  workspace: torch.Tensor, status: torch.Tensor,
+                                  stream=None) -> None:
+        """bpe_encode_batch_special on caller-owned device buffers (bos_id / eos_id:
+        -1 for none)."""
+        n_bytes = int(data.numel())
+        n_docs = int(doc_off.numel()) - 1
+        if data.dtype != torch.uint8 or doc_off.dtype != torch.int64 or ids.dtype != torch.int32 \
+                or id_off.dtype != torch.int64 or status.dtype != torch.int32:
+            raise TypeError("dtypes: data uint8, doc_off int64, ids int32, id_off int64, status int32")
+        if n_docs < 0 or id_off.numel() != n_docs + 1:
+            raise ValueError("doc_off and id_off need n_docs + 1 entries")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        rc = _lib.load().bpe_encode_batch_special(
+            self._h, _dptr(data) if n_bytes else None, n_bytes, _dptr(doc_off), n_docs,
+            int(bos_id), int(eos_id), _dptr(ids) if ids.numel() else None, int(ids.numel()),
+            _dptr(id_off), _dptr(workspace), ws_bytes, _dptr(status),
+            C.c_void_p(_stream_handle(stream)))
+        if rc != _lib.BPE_OK:
+            raise BPEError(rc, "bpe_encode_batch_special")
+
+    def encode_batch_special(self, data: torch.Tensor, doc_off: torch.Tensor, bos_id: int = -1,
+                             eos_id: int = -1, ids_capacity: int | None = None, stream=None):
+        """Allocate outputs, encode with bos_id / eos_id around each document,
+        synchronize, and return (ids[:T], id_off)."""
+        dev = data.device
+        n_bytes = int(data.numel())
+        n_docs = int(doc_off.numel()) - 1
+        per_doc = int(bos_id >= 0) + int(eos_id >= 0)
+        cap = n_bytes + n_docs * per_doc if ids_capacity is None else ids_capacity
+        ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)[:cap]
+        id_off = torch.empty(n_docs + 1, dtype=torch.int64, device=dev)
+        ws = torch.empty(max(1, self.encode_special_workspace_bytes(n_bytes, n_docs)),
+                         dtype=torch.uint8, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.encode_batch_special_into(data, doc_off, bos_id, eos_id, ids, id_off, ws, status, stream)
+        st = int(status.item())
+        if st:
+            raise RuntimeError(f"bpe_encode_batch_special device status {st:#x}")
+        T = int(id_off[-1].item())
+        return ids[:T], id_off
+
     # ---- decode -------------------------------------------------------------
     def decode_workspace_bytes(self, n_ids: int, n_docs: int) -> int:
         return int(_lib.load().bpe_decode_workspace_bytes(self._h, n_ids, n_docs))
 
     def decode_batch_into(self, ids: torch.Tensor, id_off: torch.Tensor, out: torch.Tensor,
                           byte_off: torch.Tensor, workspace: torch.Tensor | None,
-                          status: torch.Tensor, stream=None) -> None:
+                          status: torch.Tensor, stream=None, skip=(-1, -1)) -> None:
+        """bpe_decode_batch (bpe_decode_batch_special when skip names reserved
+        IDs that decode to no bytes)."""
         n_ids = int(ids.numel())
         n_docs = int(id_off.numel()) - 1
         if ids.dtype != torch.int32 or id_off.dtype != torch.int64 or out.dtype != torch.uint8 \
@@ -154,16 +203,25 @@ class Model:
         if n_docs < 0 or byte_off.numel() != n_docs + 1:
             raise ValueError("id_off and byte_off need n_docs + 1 entries")
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        rc = _lib.load().bpe_decode_batch(
-            self._h, _dptr(ids) if n_ids else None, n_ids, _dptr(id_off), n_docs,
-            _dptr(out) if out.numel() else None, int(out.numel()), _dptr(byte_off),
-            _dptr(workspace) if ws_bytes else None, ws_bytes, _dptr(status),
-            C.c_void_p(_stream_handle(stream)))
+        skip_a, skip_b = (int(x) for x in skip)
+        L = _lib.load()
+        if skip_a == -1 and skip_b == -1:
+            rc = L.bpe_decode_batch(
+                self._h, _dptr(ids) if n_ids else None, n_ids, _dptr(id_off), n_docs,
+                _dptr(out) if out.numel() else None, int(out.numel()), _dptr(byte_off),
+                _dptr(workspace) if ws_bytes else None, ws_bytes, _dptr(status),
+                C.c_void_p(_stream_handle(stream)))
+        else:
+            rc = L.bpe_decode_batch_special(
+                self._h, _dptr(ids) if n_ids else None, n_ids, _dptr(id_off), n_docs, skip_a,
+                skip_b, _dptr(out) if out.numel() else None, int(out.numel()), _dptr(byte_off),
+                _dptr(workspace) if ws_bytes else None, ws_bytes, _dptr(status),
+                C.c_void_p(_stream_handle(stream)))
         if rc != _lib.BPE_OK:
             raise BPEError(rc, "bpe_decode_batch")
 
     def decode_batch(self, ids: torch.Tensor, id_off: torch.Tensor, bytes_capacity: int | None = None,
-                     stream=None):
+                     stream=None, skip=(-1, -1)):
         """Allocate outputs, decode, synchronize, and return (bytes[:N], byte_off)."""
         dev = ids.device
         n_ids = int(ids.numel())
@@ -174,7 +232,7 @@ class Model:
         ws = torch.empty(max(1, self.decode_workspace_bytes(n_ids, n_docs)), dtype=torch.uint8,
                          device=dev)
         status = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.decode_batch_into(ids, id_off, out, byte_off, ws, status, stream)
+        self.decode_batch_into(ids, id_off, out, byte_off, ws, status, stream, skip)
         st = int(status.item())
         if st:
             raise RuntimeError(f"bpe_decode_batch device status {st:#x}")

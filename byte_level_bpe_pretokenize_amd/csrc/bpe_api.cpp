@@ -43,6 +43,7 @@ struct bpe_model {
   int32_t *d_inv_map = nullptr;
   int64_t inv_size = 0;
   int32_t win_d[4] = {0, 0, 0, 0};  // window radii by pre-token class (EncodeArgs::win_d)
+  std::vector<uint64_t> used;       // with an id_map: bit x set when x is a symbol's output ID
   // stage timing (bpe_stage_timing): events of the calls not yet read, per
   // op, stages + 1 per call; spare events for reuse
   bool timing = false;
@@ -566,6 +567,10 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
   if (!m) return BPE_ENOMEM;
   m->R = R;
   m->V = V;
+  if (id_map) {
+    m->used.assign(((size_t)max_id + 64) / 64, 0ull);
+    for (int64_t v = 0; v < V; ++v) m->used[(size_t)id_map[v] >> 6] |= 1ull << (id_map[v] & 63);
+  }
   window_radii(merges, R, len, order, m->win_d);
   m->table_mask = tmask;
   m->table_seed = tseed;
@@ -684,6 +689,75 @@ int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_b
                         d_workspace, d_status, true, model->d_id_map, stream);
 }
 
+namespace {
+
+// Whether id is the output ID of some symbol (so that encoding text can
+// produce it).
+bool symbol_id(const bpe_model *m, int64_t id) {
+  if (m->used.empty()) return id >= 0 && id < m->V;
+  return id >= 0 && (size_t)(id >> 6) < m->used.size() && ((m->used[(size_t)(id >> 6)] >> (id & 63)) & 1u);
+}
+
+// A reserved ID argument: -1 (none), or in [0, BPE_MAX_ID] and no symbol's ID.
+bool reserved_ok(const bpe_model *m, int32_t id) {
+  return id == -1 || (id >= 0 && id <= BPE_MAX_ID && !symbol_id(m, id));
+}
+
+size_t special_offsets(const bpe_model *model, int64_t n_bytes, int64_t n_docs, size_t *ids0,
+                       size_t *off0) {
+  const size_t e = align256(bpe_encode_workspace_bytes(model, n_bytes, n_docs));
+  *ids0 = e;
+  *off0 = e + align256(4 * (size_t)n_bytes);
+  return *off0 + align256(8 * ((size_t)n_docs + 1));
+}
+
+}  // namespace
+
+size_t bpe_encode_special_workspace_bytes(const bpe_model *model, int64_t n_bytes,
+                                          int64_t n_docs) {
+  if (n_bytes < 0 || n_docs < 0) return 0;
+  size_t ids0, off0;
+  return special_offsets(model, n_bytes, n_docs, &ids0, &off0);
+}
+
+int bpe_encode_batch_special(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
+                             const int64_t *d_doc_off, int64_t n_docs, int32_t bos_id,
+                             int32_t eos_id, int32_t *d_ids, int64_t ids_capacity,
+                             int64_t *d_id_off, void *d_workspace, size_t workspace_bytes,
+                             int32_t *d_status, void *hip_stream) {
+  if (!model || n_bytes < 0 || n_docs < 0 || ids_capacity < 0 || !d_doc_off || !d_id_off ||
+      !d_status || (ids_capacity > 0 && !d_ids) || !d_workspace || (n_bytes > 0 && !d_bytes))
+    return BPE_EINVAL;
+  if (!reserved_ok(model, bos_id) || !reserved_ok(model, eos_id)) return BPE_EINVAL;
+  if (enc_chunks(n_bytes) * kEncThreads > (int64_t)UINT32_MAX) return BPE_EINVAL;
+  if ((n_bytes + 1023) / 1024 + (n_docs + 1 + 255) / 256 > (int64_t)UINT32_MAX / 256)
+    return BPE_EINVAL;
+  if (!on_model_device(model)) return BPE_EINVAL;
+  size_t ids0, off0;
+  if (workspace_bytes < special_offsets(model, n_bytes, n_docs, &ids0, &off0))
+    return BPE_EWORKSPACE;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  uint8_t *ws = (uint8_t *)d_workspace;
+  // the plain encode into the workspace (its capacity n_bytes is never short)
+  const int rc = enqueue_encode(model, d_bytes, n_bytes, d_doc_off, n_docs, (int32_t *)(ws + ids0),
+                                n_bytes, (int64_t *)(ws + off0), d_workspace, d_status, true,
+                                model->d_id_map, stream);
+  if (rc != BPE_OK) return rc;
+  SpecialArgs a;
+  a.ids0 = (const int32_t *)(ws + ids0);
+  a.off0 = (const int64_t *)(ws + off0);
+  a.n_docs = n_docs;
+  a.n_bytes = n_bytes;
+  a.bos = bos_id;
+  a.eos = eos_id;
+  a.ids = d_ids;
+  a.ids_cap = ids_capacity;
+  a.id_off = d_id_off;
+  a.status = d_status;
+  a.tok_blocks = std::min<int64_t>((n_bytes + 1023) / 1024, 16 * (int64_t)model->n_cu);
+  return launch_special(a, stream) == hipSuccess ? BPE_OK : BPE_EHIP;
+}
+
 size_t bpe_decode_workspace_bytes(const bpe_model *model, int64_t n_ids, int64_t n_docs) {
   (void)model;
   (void)n_docs;
@@ -694,6 +768,17 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
                      const int64_t *d_id_off, int64_t n_docs, uint8_t *d_bytes,
                      int64_t bytes_capacity, int64_t *d_byte_off, void *d_workspace,
                      size_t workspace_bytes, int32_t *d_status, void *hip_stream) {
+  return bpe_decode_batch_special(model, d_ids, n_ids, d_id_off, n_docs, -1, -1, d_bytes,
+                                  bytes_capacity, d_byte_off, d_workspace, workspace_bytes,
+                                  d_status, hip_stream);
+}
+
+int bpe_decode_batch_special(const bpe_model *model, const int32_t *d_ids, int64_t n_ids,
+                             const int64_t *d_id_off, int64_t n_docs, int32_t skip_a,
+                             int32_t skip_b, uint8_t *d_bytes, int64_t bytes_capacity,
+                             int64_t *d_byte_off, void *d_workspace, size_t workspace_bytes,
+                             int32_t *d_status, void *hip_stream) {
+  if (model && (!reserved_ok(model, skip_a) || !reserved_ok(model, skip_b))) return BPE_EINVAL;
   if (!model || n_ids < 0 || n_docs < 0 || bytes_capacity < 0 || !d_id_off || !d_byte_off ||
       !d_status || (bytes_capacity > 0 && !d_bytes) || (n_ids > 0 && (!d_ids || !d_workspace)))
     return BPE_EINVAL;
@@ -733,6 +818,8 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
   a.status = d_status;
   a.n_chunks = dec_chunks(n_ids);
   a.doc_per = (n_docs + 1 + a.n_chunks - 1) / a.n_chunks;
+  a.skip0 = skip_a;
+  a.skip1 = skip_b;
   if (launch_decode(a, stream, call_events(model, BPE_OP_DECODE)) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }

@@ -66,9 +66,12 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   for (int j = 0; j < DPT; ++j) {
     const int k = j * DWG + tid;
     if (k < cnt) {
-      const int32_t sym = dec_sym(a, a.ids[i0 + k]);
-      if (sym < 0) bad_id = true;
-      else mine += a.exp_len[sym];
+      const int32_t id = a.ids[i0 + k];
+      const int32_t sym = dec_sym(a, id);
+      // a reserved ID given as skip0 / skip1 decodes to no bytes (k_dec_write
+      // writes none for an ID with no symbol)
+      if (sym >= 0) mine += a.exp_len[sym];
+      else if (!((a.skip0 >= 0 && id == a.skip0) || (a.skip1 >= 0 && id == a.skip1))) bad_id = true;
     }
   }
   int64_t total;

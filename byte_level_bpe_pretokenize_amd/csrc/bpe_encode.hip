@@ -2030,6 +2030,87 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   }
 }
 
+// ---- k_special ------------------------------------------------------------------
+// Reserved IDs around each document ("Characters, bytes and subwords", section
+// "Special tokens are their own IDs": reserved IDs such as BOS and EOS are
+// inserted on purpose and no text can produce them; "Hugging Face Tokenizers
+// v1", section "How v1 works": a post-processing stage adds the special
+// tokens a model expects).  With nb (0 or 1) IDs before and ne after each
+// document, document d's IDs move up by d (nb + ne) + nb and its offset by
+// d (nb + ne): no scan is needed.  Workgroups below tok_blocks take tiles of
+// 1024 consecutive IDs in turn (thread t the IDs t, t + 256, ...): their loads go
+// first; wave 0 finds the document of the first ID by a 64-way search of the
+// offsets, the ends of that document and the next 255 are staged in LDS, and
+// each ID's document is a binary search there (stepping on in the offsets
+// only past those 256 documents).  The other workgroups place one document's
+// reserved IDs and offset per thread.  Every write is checked against the
+// capacity; offsets that are not in order (already flagged by the encode)
+// only keep the reads in bounds.
+__global__ void __launch_bounds__(256) k_special(SpecialArgs a) {
+  __shared__ int64_t ends[256];
+  __shared__ int64_t first_doc;
+  const int tid = threadIdx.x;
+  const int64_t nb = a.bos >= 0 ? 1 : 0, ns = nb + (a.eos >= 0 ? 1 : 0);
+  const int64_t T = min(max(a.off0[a.n_docs], (int64_t)0), a.n_bytes);
+  bool over = false;
+  if ((int64_t)blockIdx.x < a.tok_blocks) {
+    if (a.n_docs == 0) return;
+    for (int64_t b0 = (int64_t)blockIdx.x * 1024; b0 < T; b0 += a.tok_blocks * 1024) {
+      int32_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t i = b0 + q * 256 + tid;
+        v[q] = i < T ? a.ids0[i] : 0;
+      }
+      if (wave_id() == 0) {
+        // the first document whose end off0[d + 1] is past b0
+        const int64_t d0 = min(wave_lower_bound(a.off0 + 1, a.n_docs, b0 + 1), a.n_docs - 1);
+        if (lane_id() == 0) first_doc = d0;
+      }
+      __syncthreads();
+      const int64_t d0 = first_doc;
+      ends[tid] = d0 + 1 + tid <= a.n_docs ? a.off0[d0 + 1 + tid] : INT64_MAX;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t i = b0 + q * 256 + tid;
+        if (i >= T) continue;
+        int lo = 0, hi = 256;  // first j with ends[j] > i, else 256
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (ends[mid] > i) hi = mid;
+          else lo = mid + 1;
+        }
+        int64_t d = d0 + lo;
+        while (d + 1 < a.n_docs && a.off0[d + 1] <= i) ++d;
+        d = min(d, a.n_docs - 1);
+        const int64_t o = i + d * ns + nb;
+        if (o < a.ids_cap) a.ids[o] = v[q];
+        else over = true;
+      }
+      __syncthreads();  // ends and first_doc are rewritten for the next tile
+    }
+  } else {
+    const int64_t d = ((int64_t)blockIdx.x - a.tok_blocks) * 256 + threadIdx.x;
+    if (d <= a.n_docs) {
+      const int64_t s = min(max(a.off0[d], (int64_t)0), T) + d * ns;
+      a.id_off[d] = s;
+      if (d < a.n_docs) {
+        const int64_t e = min(max(a.off0[d + 1], (int64_t)0), T) + (d + 1) * ns;
+        if (nb) {
+          if (s < a.ids_cap) a.ids[s] = a.bos;
+          else over = true;
+        }
+        if (a.eos >= 0) {
+          if (e - 1 < a.ids_cap) a.ids[e - 1] = a.eos;
+          else over = true;
+        }
+      }
+    }
+  }
+  if (over) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
+}
+
 // Empty input (one workgroup): clear the status, then check that every
 // offset is zero and write zero offsets.
 __global__ void k_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, int64_t *out_off,
@@ -2045,6 +2126,12 @@ __global__ void k_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
 }
 
 }  // namespace
+
+hipError_t launch_special(const SpecialArgs &a, hipStream_t stream) {
+  const int64_t doc_blocks = (a.n_docs + 1 + 255) / 256;
+  hipLaunchKernelGGL(k_special, dim3((unsigned)(a.tok_blocks + doc_blocks)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, int64_t *out_off,
                         int32_t *status, hipStream_t stream) {

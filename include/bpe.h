@@ -138,6 +138,39 @@ int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_b
                      int64_t ids_capacity, int64_t *d_id_off, void *d_workspace,
                      size_t workspace_bytes, int32_t *d_status, void *hip_stream);
 
+/*
+ * Reserved IDs around each document: post-processing ("Characters, bytes and
+ * subwords", section "Special tokens are their own IDs": IDs such as BOS and
+ * EOS are reserved, inserted on purpose when data is prepared, and no text
+ * can produce them; "Hugging Face Tokenizers v1", section "How v1 works": a
+ * post-processing stage adds the special tokens a model expects).
+ *
+ * Workspace bytes bpe_encode_batch_special needs (always > 0 for valid sizes).
+ */
+size_t bpe_encode_special_workspace_bytes(const bpe_model *model, int64_t n_bytes,
+                                          int64_t n_docs);
+
+/*
+ * Encode as bpe_encode_batch, then put bos_id before and eos_id after each
+ * document's IDs (also around an empty document).  Either may be -1 (none);
+ * otherwise it must lie in [0, BPE_MAX_ID] and be no symbol's output ID
+ * (with an id_map, no value of it; else not below 256 + n_merges), so that
+ * no text yields it, else BPE_EINVAL.
+ *  d_ids       receives document d's IDs as [bos] encode(d) [eos]; the count
+ *              is at most n_bytes + n_docs * (number of reserved IDs given),
+ *              and with less capacity the IDs past it are dropped and
+ *              BPE_STATUS_IDS_CAPACITY is set.
+ *  d_id_off    receives each document's offset, the reserved IDs included.
+ *  d_workspace non-null, of at least bpe_encode_special_workspace_bytes
+ *              bytes (the plain encode's workspace plus room for its output).
+ * Other arguments, the status bits and the return codes as bpe_encode_batch.
+ */
+int bpe_encode_batch_special(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
+                             const int64_t *d_doc_off, int64_t n_docs, int32_t bos_id,
+                             int32_t eos_id, int32_t *d_ids, int64_t ids_capacity,
+                             int64_t *d_id_off, void *d_workspace, size_t workspace_bytes,
+                             int32_t *d_status, void *hip_stream);
+
 /* Workspace bytes bpe_decode_batch needs (0 for n_ids <= 0). */
 size_t bpe_decode_workspace_bytes(const bpe_model *model, int64_t n_ids, int64_t n_docs);
 
@@ -159,6 +192,20 @@ int bpe_decode_batch(const bpe_model *model, const int32_t *d_ids, int64_t n_ids
                      const int64_t *d_id_off, int64_t n_docs, uint8_t *d_bytes,
                      int64_t bytes_capacity, int64_t *d_byte_off, void *d_workspace,
                      size_t workspace_bytes, int32_t *d_status, void *hip_stream);
+
+/*
+ * Decode as bpe_decode_batch, with the reserved IDs skip_a and skip_b (each
+ * -1 for none, else a valid reserved ID as for bpe_encode_batch_special,
+ * else BPE_EINVAL) decoding to no bytes instead of setting
+ * BPE_STATUS_BAD_ID: the output of bpe_encode_batch_special decodes back to
+ * the input bytes ("Special tokens are their own IDs": on output they may be
+ * skipped).  Same workspace as bpe_decode_batch.
+ */
+int bpe_decode_batch_special(const bpe_model *model, const int32_t *d_ids, int64_t n_ids,
+                             const int64_t *d_id_off, int64_t n_docs, int32_t skip_a,
+                             int32_t skip_b, uint8_t *d_bytes, int64_t bytes_capacity,
+                             int64_t *d_byte_off, void *d_workspace, size_t workspace_bytes,
+                             int32_t *d_status, void *hip_stream);
 
 /*
  * Stage timing, for benchmarks and profilers.  While it is enabled on a

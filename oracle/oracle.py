@@ -177,6 +177,37 @@ class Table:
         assert n2 == n
         return out[:n].copy(), byte_off
 
+    def encode_batch_special(self, data: np.ndarray, doc_off: np.ndarray, bos: int = -1,
+                             eos: int = -1):
+        """Post-processing with reserved IDs ("Characters, bytes and subwords",
+        section "Special tokens are their own IDs"): each document's IDs with
+        bos before and eos after them (-1: none), one document at a time."""
+        ids, id_off = self.encode_batch(data, doc_off)
+        out, off = [], [0]
+        for d in range(id_off.size - 1):
+            seq = ids[id_off[d]:id_off[d + 1]].tolist()
+            if bos >= 0:
+                seq = [bos] + seq
+            if eos >= 0:
+                seq = seq + [eos]
+            out += seq
+            off.append(off[-1] + len(seq))
+        return np.array(out, dtype=np.int32), np.array(off, dtype=np.int64)
+
+    def decode_batch_special(self, ids: np.ndarray, id_off: np.ndarray, skip=(-1, -1)):
+        """Decode with the reserved IDs in skip dropped first (on output they
+        may be skipped, same section)."""
+        ids = np.asarray(ids, dtype=np.int32)
+        id_off = np.asarray(id_off, dtype=np.int64)
+        keep = np.ones(ids.size, dtype=bool)
+        for x in skip:
+            if x >= 0:
+                keep &= ids != x
+        new_off = np.zeros(id_off.size, dtype=np.int64)
+        csum = np.concatenate([[0], np.cumsum(keep)])
+        new_off[:] = csum[id_off]
+        return self.decode_batch(ids[keep], new_off)
+
     def decode(self, ids) -> bytes:
         a = np.asarray(ids, dtype=np.int32)
         out, _ = self.decode_batch(a, np.array([0, a.size], dtype=np.int64))

@@ -78,6 +78,10 @@ def test_null_model_calls():
     assert L.bpe_max_token_bytes(None) == -1
     assert L.bpe_encode_batch(None, None, 0, None, 0, None, 0, None, None, 0, None, None) == _lib.BPE_EINVAL
     assert L.bpe_decode_batch(None, None, 0, None, 0, None, 0, None, None, 0, None, None) == _lib.BPE_EINVAL
+    assert L.bpe_encode_batch_special(None, None, 0, None, 0, -1, -1, None, 0, None, None, 0, None,
+                                      None) == _lib.BPE_EINVAL
+    assert L.bpe_decode_batch_special(None, None, 0, None, 0, -1, -1, None, 0, None, None, 0, None,
+                                      None) == _lib.BPE_EINVAL
     L.bpe_free(None)
 
 
@@ -90,6 +94,11 @@ def test_workspace_sizes():
     assert ws >= 8 * n                       # position-indexed scratch for long pre-tokens
     assert L.bpe_encode_workspace_bytes(None, n + 1, 16) > ws
     assert L.bpe_decode_workspace_bytes(None, 5000, 3) > 0
+    # the special encode: the plain encode's workspace, then its IDs and offsets
+    sp = L.bpe_encode_special_workspace_bytes(None, n, 16)
+    assert sp >= ws + 4 * n + 8 * 17
+    assert L.bpe_encode_special_workspace_bytes(None, 0, 5) >= 8 * 6
+    assert L.bpe_encode_special_workspace_bytes(None, -1, 5) == 0
 
 
 def test_stage_timing_queries():

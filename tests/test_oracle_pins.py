@@ -251,3 +251,46 @@ def test_special_token_like_text_stays_text(tiny_table):
     ids = tiny_table.encode(b"<assistant>")
     assert all(i < 256 + tiny_table.R for i in ids)
     assert tiny_table.decode(ids) == b"<assistant>"
+
+
+# ---- reserved IDs around documents ("Characters, bytes and subwords", section
+# "Special tokens are their own IDs": reserved IDs are inserted explicitly,
+# EOS marks the end of a document, and on output they may be skipped) ----
+
+def test_special_tokens_wrap_each_document(tiny_table):
+    docs = [b"Hello world!", b"", b"the 42 cats"]
+    data = np.frombuffer(b"".join(docs), dtype=np.uint8).copy()
+    off = np.array([0, 12, 12, 23], dtype=np.int64)
+    V = 256 + tiny_table.R
+    bos, eos = V + 1, V + 7
+    ids, id_off = tiny_table.encode_batch_special(data, off, bos, eos)
+    for d, doc in enumerate(docs):
+        assert ids[id_off[d]:id_off[d + 1]].tolist() == [bos] + tiny_table.encode(doc) + [eos]
+    # an empty document is [bos, eos]; offsets move by two per document
+    assert ids[id_off[1]:id_off[2]].tolist() == [bos, eos]
+    plain_ids, plain_off = tiny_table.encode_batch(data, off)
+    assert np.array_equal(id_off, plain_off + 2 * np.arange(len(docs) + 1))
+    assert ids.size == plain_ids.size + 2 * len(docs)
+
+
+@pytest.mark.parametrize("bos,eos", [(-1, -1), (1000, -1), (-1, 1001), (1000, 1001)])
+def test_special_tokens_one_side_and_round_trip(tiny_table, bos, eos):
+    docs = [b"a", b"  spaces  ", b"", b"\xf0\x9f\x90\x88 cat"]
+    data = np.frombuffer(b"".join(docs), dtype=np.uint8).copy()
+    off = np.zeros(len(docs) + 1, dtype=np.int64)
+    np.cumsum([len(x) for x in docs], out=off[1:])
+    ids, id_off = tiny_table.encode_batch_special(data, off, bos, eos)
+    plain, plain_off = tiny_table.encode_batch(data, off)
+    n = int(bos >= 0) + int(eos >= 0)
+    assert np.array_equal(id_off, plain_off + n * np.arange(len(docs) + 1))
+    for d in range(len(docs)):
+        seg = ids[id_off[d]:id_off[d + 1]].tolist()
+        body = seg[1:] if bos >= 0 else seg
+        body = body[:-1] if eos >= 0 else body
+        assert body == plain[plain_off[d]:plain_off[d + 1]].tolist()
+        if bos >= 0:
+            assert seg[0] == bos
+        if eos >= 0:
+            assert seg[-1] == eos
+    out, boff = tiny_table.decode_batch_special(ids, id_off, (bos, eos))
+    assert out.tobytes() == data.tobytes() and np.array_equal(boff, off)
