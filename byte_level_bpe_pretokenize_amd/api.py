@@ -145,7 +145,7 @@ class Model:
 
     def encode_batch_special_into(self, data: torch.Tensor, doc_off: torch.Tensor, bos_id: int,
                                   eos_id: int, ids: torch.Tensor, id_off: torch.Tensor,
-                                  workspace: torch.Tensor, status: torch.Tensor,
+                                  workspace: torch.Tensor | None, status: torch.Tensor,
                                   stream=None) -> None:
         """bpe_encode_batch_special on caller-owned device buffers (bos_id / eos_id:
         -1 for none)."""
@@ -156,11 +156,11 @@ class Model:
             raise TypeError("dtypes: data uint8, doc_off int64, ids int32, id_off int64, status int32")
         if n_docs < 0 or id_off.numel() != n_docs + 1:
             raise ValueError("doc_off and id_off need n_docs + 1 entries")
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         rc = _lib.load().bpe_encode_batch_special(
             self._h, _dptr(data) if n_bytes else None, n_bytes, _dptr(doc_off), n_docs,
             int(bos_id), int(eos_id), _dptr(ids) if ids.numel() else None, int(ids.numel()),
-            _dptr(id_off), _dptr(workspace), ws_bytes, _dptr(status),
+            _dptr(id_off), _dptr(workspace) if ws_bytes else None, ws_bytes, _dptr(status),
             C.c_void_p(_stream_handle(stream)))
         if rc != _lib.BPE_OK:
             raise BPEError(rc, "bpe_encode_batch_special")

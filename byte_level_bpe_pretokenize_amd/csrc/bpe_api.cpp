@@ -227,7 +227,8 @@ bool on_model_device(const bpe_model *m) {
 int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
                    const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids, int64_t ids_capacity,
                    int64_t *d_id_off, void *d_workspace, int32_t *d_status, bool words,
-                   const int32_t *id_map, hipStream_t stream) {
+                   const int32_t *id_map, hipStream_t stream, int32_t bos = -1,
+                   int32_t eos = -1) {
   if (n_bytes == 0)
     return launch_empty(d_doc_off, n_docs, BPE_STATUS_BAD_DOC_OFFSETS, d_id_off, d_status,
                         stream) == hipSuccess
@@ -283,6 +284,8 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.doc_per = (n_docs + 1 + a.n_chunks - 1) / a.n_chunks;
   a.dt_per = (2 * ((uint64_t)a.dt_mask + 1) + (uint64_t)a.n_chunks - 1) / (uint64_t)a.n_chunks;
   for (int k = 0; k < 4; ++k) a.win_d[k] = model->win_d[k];
+  a.bos = bos;
+  a.eos = eos;
   if (launch_encode(a, stream, call_events(model, BPE_OP_ENCODE)) != hipSuccess) return BPE_EHIP;
   return BPE_OK;
 }
@@ -703,21 +706,11 @@ bool reserved_ok(const bpe_model *m, int32_t id) {
   return id == -1 || (id >= 0 && id <= BPE_MAX_ID && !symbol_id(m, id));
 }
 
-size_t special_offsets(const bpe_model *model, int64_t n_bytes, int64_t n_docs, size_t *ids0,
-                       size_t *off0) {
-  const size_t e = align256(bpe_encode_workspace_bytes(model, n_bytes, n_docs));
-  *ids0 = e;
-  *off0 = e + align256(4 * (size_t)n_bytes);
-  return *off0 + align256(8 * ((size_t)n_docs + 1));
-}
-
 }  // namespace
 
 size_t bpe_encode_special_workspace_bytes(const bpe_model *model, int64_t n_bytes,
                                           int64_t n_docs) {
-  if (n_bytes < 0 || n_docs < 0) return 0;
-  size_t ids0, off0;
-  return special_offsets(model, n_bytes, n_docs, &ids0, &off0);
+  return bpe_encode_workspace_bytes(model, n_bytes, n_docs);
 }
 
 int bpe_encode_batch_special(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
@@ -726,35 +719,30 @@ int bpe_encode_batch_special(const bpe_model *model, const uint8_t *d_bytes, int
                              int64_t *d_id_off, void *d_workspace, size_t workspace_bytes,
                              int32_t *d_status, void *hip_stream) {
   if (!model || n_bytes < 0 || n_docs < 0 || ids_capacity < 0 || !d_doc_off || !d_id_off ||
-      !d_status || (ids_capacity > 0 && !d_ids) || !d_workspace || (n_bytes > 0 && !d_bytes))
+      !d_status || (ids_capacity > 0 && !d_ids) || (n_bytes > 0 && (!d_bytes || !d_workspace)))
     return BPE_EINVAL;
   if (!reserved_ok(model, bos_id) || !reserved_ok(model, eos_id)) return BPE_EINVAL;
   if (enc_chunks(n_bytes) * kEncThreads > (int64_t)UINT32_MAX) return BPE_EINVAL;
-  if ((n_bytes + 1023) / 1024 + (n_docs + 1 + 255) / 256 > (int64_t)UINT32_MAX / 256)
-    return BPE_EINVAL;
+  if ((n_docs + 1 + 255) / 256 > (int64_t)UINT32_MAX) return BPE_EINVAL;
   if (!on_model_device(model)) return BPE_EINVAL;
-  size_t ids0, off0;
-  if (workspace_bytes < special_offsets(model, n_bytes, n_docs, &ids0, &off0))
-    return BPE_EWORKSPACE;
   hipStream_t stream = (hipStream_t)hip_stream;
-  uint8_t *ws = (uint8_t *)d_workspace;
-  // the plain encode into the workspace (its capacity n_bytes is never short)
-  const int rc = enqueue_encode(model, d_bytes, n_bytes, d_doc_off, n_docs, (int32_t *)(ws + ids0),
-                                n_bytes, (int64_t *)(ws + off0), d_workspace, d_status, true,
-                                model->d_id_map, stream);
-  if (rc != BPE_OK) return rc;
+  if (n_bytes > 0 && workspace_bytes < enc_layout(n_bytes, n_docs).total) return BPE_EWORKSPACE;
+  if (n_bytes > 0 || (bos_id < 0 && eos_id < 0))
+    return enqueue_encode(model, d_bytes, n_bytes, d_doc_off, n_docs, d_ids, ids_capacity,
+                          d_id_off, d_workspace, d_status, true, model->d_id_map, stream, bos_id,
+                          eos_id);
+  // an empty input: the offsets checked (and zeroed), then the reserved IDs
+  if (launch_empty(d_doc_off, n_docs, BPE_STATUS_BAD_DOC_OFFSETS, d_id_off, d_status, stream) !=
+      hipSuccess)
+    return BPE_EHIP;
   SpecialArgs a;
-  a.ids0 = (const int32_t *)(ws + ids0);
-  a.off0 = (const int64_t *)(ws + off0);
   a.n_docs = n_docs;
-  a.n_bytes = n_bytes;
   a.bos = bos_id;
   a.eos = eos_id;
   a.ids = d_ids;
   a.ids_cap = ids_capacity;
   a.id_off = d_id_off;
   a.status = d_status;
-  a.tok_blocks = std::min<int64_t>((n_bytes + 1023) / 1024, 16 * (int64_t)model->n_cu);
   return launch_special(a, stream) == hipSuccess ? BPE_OK : BPE_EHIP;
 }
 

@@ -1846,6 +1846,9 @@ constexpr int EWG = 256;                 // k_emit threads per chunk
 constexpr int kOutCap = kChunk + kHalo;  // chunk-relative token positions staged in LDS
 constexpr int kEmitPasses = 3;           // passes of EWG pre-tokens per round
 
+constexpr int kDocLds = 512;             // document starts of a chunk staged in LDS (with reserved IDs)
+
+template <bool SP>
 struct EmitShared {
   int32_t out[kOutCap + 1];              // the chunk's symbols at positions below kOutCap;
                                          // stores that place nothing go to out[kOutCap]
@@ -1854,6 +1857,7 @@ struct EmitShared {
   int64_t lsrc[kMaxLong];
   int64_t lnt[kMaxLong];
   int32_t n_long;
+  int32_t dpos[SP ? kDocLds : 1];        // first position of each document that starts here
 };
 
 // Tokens of the lane-merged pre-token with pv value -1 - u: in the chunk's
@@ -1870,8 +1874,21 @@ __device__ __forceinline__ const int32_t *entry_res(const EncodeArgs &a, const i
 // symbols in LDS; the workgroup then writes the chunk's positions in order.
 // A position at or past kOutCap (possible only after a long pre-token that
 // runs past the window) is written directly.
+//
+// SP: reserved IDs around each document ("Characters, bytes and subwords",
+// section "Special tokens are their own IDs"; "Hugging Face Tokenizers v1",
+// section "How v1 works": post-processing adds the special tokens a model
+// expects).  With nb (0 or 1) reserved IDs before and ne after each document,
+// the token at plain position p of document d lands at p + d (nb + ne) + nb,
+// and document d's IDs start at its plain offset + d (nb + ne): the shift is
+// constant between document starts, so no scan changes.  The chunk's
+// document starts are placed first (their offsets, BOS and the previous
+// document's EOS), then every position is written with the shift of its
+// document (a binary search over the starts staged in LDS; a chunk where no
+// document starts has one shift for all).
+template <bool SP>
 __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
-  __shared__ EmitShared s;
+  __shared__ EmitShared<SP> s;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int64_t c = blockIdx.x;
   const int64_t c0 = c * kChunk;
@@ -1894,13 +1911,43 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int64_t base = a.off[c] + a.boff[c / kScanBlock];
   if (tid == 0) s.n_long = 0;
   bool overflow = false;
+  // SP: the reserved IDs per document, and the output position of plain
+  // chunk position w (documents dlo .. dhi - 1 start here, at s.dpos / from
+  // their first pre-token's position)
+  const int64_t nb = SP && a.bos >= 0 ? 1 : 0, ns = nb + (SP && a.eos >= 0 ? 1 : 0);
+  int64_t total = 0;
+  auto doc_pos = [&](int64_t d) -> int64_t {
+    const int k = min(max(a.doc_pt[d], 0), n_pt);
+    return k < n_pt ? (int64_t)pv[k] : total;
+  };
+  auto out_pos = [&](int64_t w) -> int64_t {
+    if (!SP) return base + w;
+    const int64_t nd = dhi - dlo;
+    int lo = 0, hi = (int)min<int64_t>(nd, kDocLds);  // starts at or before w
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s.dpos[mid] > w) hi = mid;
+      else lo = mid + 1;
+    }
+    int64_t n = lo;
+    if (lo == kDocLds && nd > kDocLds) {
+      int64_t l2 = kDocLds, h2 = nd;
+      while (l2 < h2) {
+        const int64_t mid = (l2 + h2) >> 1;
+        if (doc_pos(dlo + mid) > w) h2 = mid;
+        else l2 = mid + 1;
+      }
+      n = l2;
+    }
+    return base + w + ns * max(dlo - 1 + n, (int64_t)0) + nb;
+  };
   auto put = [&](int64_t w, int32_t sym) {
     if (w < kOutCap) {
       s.out[w] = sym;
-    } else if (base + w < a.ids_cap) {
-      a.ids[base + w] = out_id(a.id_map, sym);
     } else {
-      overflow = true;
+      const int64_t o = out_pos(w);
+      if (o < a.ids_cap) a.ids[o] = out_id(a.id_map, sym);
+      else overflow = true;
     }
   };
   int64_t carry = 0;
@@ -1985,7 +2032,26 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
     carry += run;
     __syncthreads();  // wtot is rewritten by the next round
   }
-  const int64_t total = carry;
+  total = carry;
+  if (SP) {
+    // the documents that start here: offsets, their BOS and the previous
+    // document's EOS, and their first positions for out_pos
+    for (int64_t d = dlo + tid; d < dhi; d += EWG) {
+      const int64_t p = doc_pos(d);
+      if (d - dlo < kDocLds) s.dpos[d - dlo] = (int32_t)p;
+      const int64_t o = base + p + ns * d;
+      a.id_off[d] = o;
+      if (nb) {
+        if (o < a.ids_cap) a.ids[o] = a.bos;
+        else overflow = true;
+      }
+      if (a.eos >= 0 && d >= 1) {
+        if (o - 1 < a.ids_cap) a.ids[o - 1] = a.eos;
+        else overflow = true;
+      }
+    }
+    __syncthreads();
+  }
   // wave-merged entries' symbols, copied by the whole workgroup
   for (int q = 0; q < s.n_long; ++q) {
     const int64_t w0 = s.lw[q], src = s.lsrc[q], nt = s.lnt[q];
@@ -1994,7 +2060,15 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   __syncthreads();
   // the staged positions, in order
   const int nst = (int)min(total, (int64_t)kOutCap);
-  if (base + nst <= a.ids_cap) {
+  if (SP && docs_here) {
+    for (int k = tid; k < nst; k += EWG) {
+      const int64_t o = out_pos(k);
+      if (o < a.ids_cap) a.ids[o] = out_id(a.id_map, s.out[k]);
+      else overflow = true;
+    }
+  } else if (out_pos(0) + nst <= a.ids_cap) {
+    // (one shift for the whole chunk)
+    const int64_t base = out_pos(0);
     // the positions before the first 16-byte boundary of ids one per thread,
     // then four per thread with 16-byte stores, then the rest
     const int head = min(nst, (int)((4 - ((reinterpret_cast<uintptr_t>(a.ids + base) >> 2) & 3)) & 3));
@@ -2011,102 +2085,60 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
     const int k = head + body + tid;
     if (k < nst) a.ids[base + k] = out_id(a.id_map, s.out[k]);
   } else {
+    const int64_t base = out_pos(0);
     for (int k = tid; k < nst; k += EWG) {
       if (base + k < a.ids_cap) a.ids[base + k] = out_id(a.id_map, s.out[k]);
       else overflow = true;
     }
   }
-  if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
   // per-document offsets: a document starting at pre-token k begins at k's
   // first position (the workgroup's own stores to pv, ordered by the barrier
   // above), one starting after the last pre-token at the chunk's end
-  for (int64_t d = dlo + tid; d < dhi; d += EWG) {
-    const int k = min(max(d == dlo + tid ? dk0 : a.doc_pt[d], 0), n_pt);
-    a.id_off[d] = base + (k < n_pt ? (int64_t)pv[k] : total);
+  if (!SP) {
+    for (int64_t d = dlo + tid; d < dhi; d += EWG) {
+      const int k = min(max(d == dlo + tid ? dk0 : a.doc_pt[d], 0), n_pt);
+      a.id_off[d] = base + (k < n_pt ? (int64_t)pv[k] : total);
+    }
   }
   if (c == a.n_chunks - 1) {
+    // documents that start at the input's end (empty), and the end; with
+    // reserved IDs their BOS, the EOS before each, and the last document's
     const int64_t end = base + (a.tot[c] & kCountMask);
-    for (int64_t d = dhi + tid; d <= a.n_docs; d += EWG) a.id_off[d] = end;
+    for (int64_t d = dhi + tid; d <= a.n_docs; d += EWG) {
+      const int64_t o = end + ns * d;
+      a.id_off[d] = o;
+      if (SP && nb && d < a.n_docs) {
+        if (o < a.ids_cap) a.ids[o] = a.bos;
+        else overflow = true;
+      }
+      if (SP && a.eos >= 0 && d >= 1) {
+        if (o - 1 < a.ids_cap) a.ids[o - 1] = a.eos;
+        else overflow = true;
+      }
+    }
   }
+  if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
 }
 
 // ---- k_special ------------------------------------------------------------------
-// Reserved IDs around each document ("Characters, bytes and subwords", section
-// "Special tokens are their own IDs": reserved IDs such as BOS and EOS are
-// inserted on purpose and no text can produce them; "Hugging Face Tokenizers
-// v1", section "How v1 works": a post-processing stage adds the special
-// tokens a model expects).  With nb (0 or 1) IDs before and ne after each
-// document, document d's IDs move up by d (nb + ne) + nb and its offset by
-// d (nb + ne): no scan is needed.  Workgroups below tok_blocks take tiles of
-// 1024 consecutive IDs in turn (thread t the IDs t, t + 256, ...): their loads go
-// first; wave 0 finds the document of the first ID by a 64-way search of the
-// offsets, the ends of that document and the next 255 are staged in LDS, and
-// each ID's document is a binary search there (stepping on in the offsets
-// only past those 256 documents).  The other workgroups place one document's
-// reserved IDs and offset per thread.  Every write is checked against the
-// capacity; offsets that are not in order (already flagged by the encode)
-// only keep the reads in bounds.
+// Reserved IDs around the documents of an empty input (every document
+// empty, as k_empty has checked): document d is [bos, eos] at d (nb + ne).
+// One document per thread; every write is checked against the capacity.  (A
+// non-empty input gets its reserved IDs from k_emit<true>.)
 __global__ void __launch_bounds__(256) k_special(SpecialArgs a) {
-  __shared__ int64_t ends[256];
-  __shared__ int64_t first_doc;
-  const int tid = threadIdx.x;
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (d > a.n_docs) return;
   const int64_t nb = a.bos >= 0 ? 1 : 0, ns = nb + (a.eos >= 0 ? 1 : 0);
-  const int64_t T = min(max(a.off0[a.n_docs], (int64_t)0), a.n_bytes);
+  const int64_t o = ns * d;
   bool over = false;
-  if ((int64_t)blockIdx.x < a.tok_blocks) {
-    if (a.n_docs == 0) return;
-    for (int64_t b0 = (int64_t)blockIdx.x * 1024; b0 < T; b0 += a.tok_blocks * 1024) {
-      int32_t v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t i = b0 + q * 256 + tid;
-        v[q] = i < T ? a.ids0[i] : 0;
-      }
-      if (wave_id() == 0) {
-        // the first document whose end off0[d + 1] is past b0
-        const int64_t d0 = min(wave_lower_bound(a.off0 + 1, a.n_docs, b0 + 1), a.n_docs - 1);
-        if (lane_id() == 0) first_doc = d0;
-      }
-      __syncthreads();
-      const int64_t d0 = first_doc;
-      ends[tid] = d0 + 1 + tid <= a.n_docs ? a.off0[d0 + 1 + tid] : INT64_MAX;
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t i = b0 + q * 256 + tid;
-        if (i >= T) continue;
-        int lo = 0, hi = 256;  // first j with ends[j] > i, else 256
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (ends[mid] > i) hi = mid;
-          else lo = mid + 1;
-        }
-        int64_t d = d0 + lo;
-        while (d + 1 < a.n_docs && a.off0[d + 1] <= i) ++d;
-        d = min(d, a.n_docs - 1);
-        const int64_t o = i + d * ns + nb;
-        if (o < a.ids_cap) a.ids[o] = v[q];
-        else over = true;
-      }
-      __syncthreads();  // ends and first_doc are rewritten for the next tile
-    }
-  } else {
-    const int64_t d = ((int64_t)blockIdx.x - a.tok_blocks) * 256 + threadIdx.x;
-    if (d <= a.n_docs) {
-      const int64_t s = min(max(a.off0[d], (int64_t)0), T) + d * ns;
-      a.id_off[d] = s;
-      if (d < a.n_docs) {
-        const int64_t e = min(max(a.off0[d + 1], (int64_t)0), T) + (d + 1) * ns;
-        if (nb) {
-          if (s < a.ids_cap) a.ids[s] = a.bos;
-          else over = true;
-        }
-        if (a.eos >= 0) {
-          if (e - 1 < a.ids_cap) a.ids[e - 1] = a.eos;
-          else over = true;
-        }
-      }
-    }
+  a.id_off[d] = o;
+  if (nb && d < a.n_docs) {
+    if (o < a.ids_cap) a.ids[o] = a.bos;
+    else over = true;
+  }
+  if (a.eos >= 0 && d >= 1) {
+    if (o - 1 < a.ids_cap) a.ids[o - 1] = a.eos;
+    else over = true;
   }
   if (over) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
 }
@@ -2128,8 +2160,8 @@ __global__ void k_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
 }  // namespace
 
 hipError_t launch_special(const SpecialArgs &a, hipStream_t stream) {
-  const int64_t doc_blocks = (a.n_docs + 1 + 255) / 256;
-  hipLaunchKernelGGL(k_special, dim3((unsigned)(a.tok_blocks + doc_blocks)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_special, dim3((unsigned)((a.n_docs + 1 + 255) / 256)), dim3(256), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
@@ -2183,7 +2215,8 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
   mark();
   hipLaunchKernelGGL(k_bscan, dim3(1), dim3(OWG), 0, stream, a);
   mark();
-  hipLaunchKernelGGL(k_emit, dim3(G), dim3(EWG), 0, stream, a);
+  if (a.bos >= 0 || a.eos >= 0) hipLaunchKernelGGL(k_emit<true>, dim3(G), dim3(EWG), 0, stream, a);
+  else hipLaunchKernelGGL(k_emit<false>, dim3(G), dim3(EWG), 0, stream, a);
   mark();
   return hipGetLastError();
 }

@@ -337,6 +337,9 @@ struct EncodeArgs {
   // of the pre-token's first letter/digit/space/punctuation byte: the longest
   // token whose bytes can occur in such a pre-token; 0 = one rank per round.
   int32_t win_d[4];
+  // reserved IDs put before / after each document's IDs (-1: none); with
+  // either, k_emit writes every ID at its place in the output with them
+  int32_t bos, eos;
 };
 
 struct DecodeArgs {
@@ -366,18 +369,14 @@ struct DecodeArgs {
   int32_t skip0, skip1;      // reserved IDs that decode to no bytes (-1: none)
 };
 
-// Reserved IDs around each document, from a finished encode (k_special).
+// Reserved IDs around the documents of an empty input (k_special).
 struct SpecialArgs {
-  const int32_t *ids0;       // the encode's IDs [T]
-  const int64_t *off0;       // and its document offsets [n_docs + 1]
   int64_t n_docs;
-  int64_t n_bytes;           // T <= n_bytes
   int32_t bos, eos;          // written before / after each document (-1: none)
   int32_t *ids;
   int64_t ids_cap;
   int64_t *id_off;
   int32_t *status;
-  int64_t tok_blocks;        // workgroups that move IDs (4 per thread); the rest place the reserved IDs
 };
 
 // Launchers.
@@ -390,8 +389,7 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
 constexpr int kEncStages = 10;
 extern const char *const kEncStageNames[kEncStages];
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
-// Moves a finished encode's IDs into the output with the reserved IDs around
-// each document (bpe_encode.hip).
+// The reserved IDs of an empty input, after launch_empty (bpe_encode.hip).
 hipError_t launch_special(const SpecialArgs &a, hipStream_t stream);
 // The decode pipeline for n_ids > 0 (bpe_decode.hip), events as for encode.
 constexpr int kDecStages = 4;

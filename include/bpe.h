@@ -145,7 +145,8 @@ int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_b
  * can produce them; "Hugging Face Tokenizers v1", section "How v1 works": a
  * post-processing stage adds the special tokens a model expects).
  *
- * Workspace bytes bpe_encode_batch_special needs (always > 0 for valid sizes).
+ * Workspace bytes bpe_encode_batch_special needs: the same as
+ * bpe_encode_batch (0 for n_bytes <= 0).
  */
 size_t bpe_encode_special_workspace_bytes(const bpe_model *model, int64_t n_bytes,
                                           int64_t n_docs);
@@ -161,9 +162,9 @@ size_t bpe_encode_special_workspace_bytes(const bpe_model *model, int64_t n_byte
  *              and with less capacity the IDs past it are dropped and
  *              BPE_STATUS_IDS_CAPACITY is set.
  *  d_id_off    receives each document's offset, the reserved IDs included.
- *  d_workspace non-null, of at least bpe_encode_special_workspace_bytes
- *              bytes (the plain encode's workspace plus room for its output).
- * Other arguments, the status bits and the return codes as bpe_encode_batch.
+ * Other arguments, the workspace, the status bits and the return codes as
+ * bpe_encode_batch.  The reserved IDs are written by the encode's own last
+ * kernel: the call costs about what bpe_encode_batch does.
  */
 int bpe_encode_batch_special(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
                              const int64_t *d_doc_off, int64_t n_docs, int32_t bos_id,

@@ -41,7 +41,8 @@ def gpu_encode_special(model, data, doc_off, bos, eos, cap=None, guard=64):
     d_data = torch.from_numpy(data).to(dev) if n else torch.zeros(0, dtype=torch.uint8, device=dev)
     d_off = torch.from_numpy(np.ascontiguousarray(doc_off)).to(dev)
     id_off = torch.full((nd + 1,), -7, dtype=torch.int64, device=dev)
-    ws = torch.empty(model.encode_special_workspace_bytes(n, nd), dtype=torch.uint8, device=dev)
+    wsb = model.encode_special_workspace_bytes(n, nd)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     status = torch.full((1,), -1, dtype=torch.int32, device=dev)
     model.encode_batch_special_into(d_data, d_off, bos, eos, ids, id_off, ws, status)
     torch.cuda.synchronize()
@@ -158,3 +159,26 @@ def gpu_decode_special(model, ids, id_off, skip):
 def gpu_decode_plain(model, ids, id_off):
     from gpu_util import gpu_decode
     return gpu_decode(model, ids, id_off)
+
+
+def test_special_many_documents_per_chunk(dev):
+    # more document starts in one chunk than k_emit stages in LDS (512), with
+    # empty documents among them
+    model, table = model_pair("tiny")
+    V = model.vocab_size
+    rng = np.random.default_rng(21)
+    alphabet = np.frombuffer(b"ab c1!", dtype=np.uint8)
+    docs = [rng.choice(alphabet, size=int(rng.integers(0, 4))).tobytes() for _ in range(3000)]
+    data, off = batch_from_docs(docs)
+    check_special(model, table, data, off, V, V + 1)
+    check_special(model, table, data, off, -1, V + 1)
+
+
+def test_special_long_pretokens(dev):
+    # pre-tokens that run past a chunk's window (wave-merged, written straight
+    # to the output) next to document starts
+    model, table = model_pair("adversarial")
+    V = model.vocab_size
+    docs = [b"x " + b"a" * 9000 + b" tail", b"", b"7" * 3000, b"short one", b"b" * 4100]
+    data, off = batch_from_docs(docs)
+    check_special(model, table, data, off, V + 5, V + 9)
