@@ -9,7 +9,8 @@ LIB_PATH = os.path.join(PKG, "libbpe.so")
 
 # every symbol include/bpe.h declares
 SYMBOLS = (
-    "bpe_load_merges", "bpe_free", "bpe_vocab_size", "bpe_max_token_bytes",
+    "bpe_load_merges", "bpe_parse_merges_text", "bpe_parse_vocab_json",
+    "bpe_free", "bpe_vocab_size", "bpe_max_token_bytes",
     "bpe_encode_workspace_bytes", "bpe_encode_batch",
     "bpe_encode_special_workspace_bytes", "bpe_encode_batch_special",
     "bpe_decode_workspace_bytes", "bpe_decode_batch", "bpe_decode_batch_special",
@@ -17,8 +18,8 @@ SYMBOLS = (
     "bpe_strerror",
 )
 
-BPE_OK, BPE_EINVAL, BPE_EMERGES, BPE_EIDMAP, BPE_EWORKSPACE, BPE_EHIP, BPE_ENOMEM, BPE_ENOTSUP = \
-    0, -1, -2, -3, -4, -5, -6, -7
+BPE_OK, BPE_EINVAL, BPE_EMERGES, BPE_EIDMAP, BPE_EWORKSPACE, BPE_EHIP, BPE_ENOMEM, BPE_ENOTSUP, \
+    BPE_EFORMAT = 0, -1, -2, -3, -4, -5, -6, -7, -8
 STATUS_BAD_DOC_OFFSETS, STATUS_IDS_CAPACITY, STATUS_BAD_ID, STATUS_BYTES_CAPACITY, \
     STATUS_BAD_ID_OFFSETS = 1, 2, 4, 8, 16
 OP_ENCODE, OP_DECODE = 0, 1
@@ -40,6 +41,10 @@ def load() -> C.CDLL:
     p, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int, C.c_size_t
     L.bpe_load_merges.argtypes = [p, i64, p, p, C.POINTER(p)]
     L.bpe_load_merges.restype = i32
+    L.bpe_parse_merges_text.argtypes = [p, i64, p, i64, C.POINTER(C.c_int64)]
+    L.bpe_parse_merges_text.restype = i32
+    L.bpe_parse_vocab_json.argtypes = [p, i64, p, i64, p]
+    L.bpe_parse_vocab_json.restype = i32
     L.bpe_free.argtypes = [p]
     L.bpe_free.restype = None
     L.bpe_vocab_size.argtypes = [p]

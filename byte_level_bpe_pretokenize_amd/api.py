@@ -36,8 +36,40 @@ def _dptr(t: torch.Tensor | None) -> int | None:
     return t.data_ptr()
 
 
+def parse_merges_text(text: bytes | str) -> np.ndarray:
+    """A merges file (text form) as the (R, 2) int32 table: bpe_parse_merges_text."""
+    b = text.encode() if isinstance(text, str) else bytes(text)
+    cap = b.count(b"\n") + 1
+    out = np.zeros((cap, 2), dtype=np.int32)
+    n = C.c_int64()
+    rc = _lib.load().bpe_parse_merges_text(b, len(b), out.ctypes.data_as(C.c_void_p), cap, C.byref(n))
+    if rc != _lib.BPE_OK:
+        raise BPEError(rc, "bpe_parse_merges_text")
+    return out[:n.value].copy()
+
+
+def parse_vocab_json(text: bytes | str, merges) -> np.ndarray:
+    """Each symbol's ID from a vocabulary (JSON text form): bpe_parse_vocab_json."""
+    b = text.encode() if isinstance(text, str) else bytes(text)
+    m = np.ascontiguousarray(np.asarray(merges, dtype=np.int32).reshape(-1, 2))
+    out = np.zeros(256 + m.shape[0], dtype=np.int32)
+    rc = _lib.load().bpe_parse_vocab_json(b, len(b), m.ctypes.data_as(C.c_void_p) if m.size else None,
+                                          m.shape[0], out.ctypes.data_as(C.c_void_p))
+    if rc != _lib.BPE_OK:
+        raise BPEError(rc, "bpe_parse_vocab_json")
+    return out
+
+
 class Model:
     """A merge table resident on the current GPU (bpe_load_merges)."""
+
+    @classmethod
+    def from_text(cls, merges_text: bytes | str, vocab_json: bytes | str | None = None,
+                  stream=None) -> "Model":
+        """Load a table from its text form (merges file, and optionally the
+        vocabulary that gives the output IDs)."""
+        m = parse_merges_text(merges_text)
+        return cls(m, None if vocab_json is None else parse_vocab_json(vocab_json, m), stream)
 
     def __init__(self, merges, id_map=None, stream=None):
         if not torch.cuda.is_available():

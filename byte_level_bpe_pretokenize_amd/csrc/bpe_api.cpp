@@ -859,6 +859,7 @@ const char *bpe_strerror(int code) {
     case BPE_EHIP: return "HIP runtime error";
     case BPE_ENOMEM: return "out of memory";
     case BPE_ENOTSUP: return "decode unsupported: byte expansions of this table are too large";
+    case BPE_EFORMAT: return "text form rejected (malformed line, JSON or UTF-8, or an unmapped character)";
     default: return "unknown error";
   }
 }

@@ -65,6 +65,7 @@ extern "C" {
 #define BPE_EHIP (-5)        /* a HIP runtime call failed */
 #define BPE_ENOMEM (-6)      /* host or device allocation failed while loading */
 #define BPE_ENOTSUP (-7)     /* decode: this table's byte expansions exceed BPE_MAX_EXPANSION */
+#define BPE_EFORMAT (-8)     /* text form: malformed line, JSON or UTF-8, or a character no byte prints as */
 
 /* bits of *d_status */
 #define BPE_STATUS_BAD_DOC_OFFSETS 1u   /* encode: offsets not 0 = d[0] <= ... <= d[n_docs] = n_bytes */
@@ -97,6 +98,48 @@ typedef struct bpe_model bpe_model;
  */
 int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_map,
                     void *hip_stream, bpe_model **out);
+
+/*
+ * The text form of a table ("Tokenization LLM: details of building an
+ * inference engine in C++", section "Byte-level encoding": every byte value
+ * prints as one character, e.g. 0xF0 as U+00F0, so that merges and
+ * vocabularies are stored as text; section "Vocabulary lookup": merged
+ * symbols map to IDs through the vocabulary, where " world" is "Ġworld").
+ * Printable map: bytes 0x21-0x7E, 0xA1-0xAC and 0xAE-0xFF print as the code
+ * point of the same value, the other 68 bytes as U+0100, U+0101, ... in
+ * increasing byte order (0x20 is U+0120 'Ġ').  Both calls run on the host
+ * only; their results go to bpe_load_merges.
+ *
+ * Parse a merges file: UTF-8 text, one merge per line ("left right", one
+ * space), in rank order, after an optional first line starting with
+ * "#version"; empty lines are skipped and a line may end in "
+".  Each
+ * operand is a byte or the text of an earlier line's result, and no two lines
+ * may give the same bytes.
+ *  merges_out  host int32 [max_merges][2]: row r receives line r's operands
+ *              as symbols (bytes 0..255, line r' as 256 + r').
+ *  n_merges    receives the number of merges.
+ * Returns BPE_OK; BPE_EFORMAT (malformed line or UTF-8, or a character no
+ * byte prints as); BPE_EMERGES (unknown operand, a repeated result, or more
+ * than BPE_MAX_MERGES); BPE_EINVAL (null pointer, or more than max_merges).
+ */
+int bpe_parse_merges_text(const char *text, int64_t text_len, int32_t *merges_out,
+                          int64_t max_merges, int64_t *n_merges);
+
+/*
+ * Parse a vocabulary: a JSON object from token text (in the printable map)
+ * to integer ID, e.g. {"hello": 15339, "\u0120world": 1917}.  Keys with
+ * characters outside the printable map name no symbol and are ignored (the
+ * names of reserved IDs, for instance).
+ *  merges      host int32 [n_merges][2], the table (as bpe_load_merges).
+ *  id_map_out  host int32 [256 + n_merges]: receives each symbol's ID, the
+ *              ID of the text of its bytes; ready for bpe_load_merges.
+ * Returns BPE_OK; BPE_EFORMAT (malformed JSON); BPE_EMERGES (operand out of
+ * range or a cycle); BPE_EIDMAP (a symbol's text missing, or its ID outside
+ * [0, BPE_MAX_ID]); BPE_EINVAL (null pointer or bad size).
+ */
+int bpe_parse_vocab_json(const char *json, int64_t json_len, const int32_t *merges,
+                         int64_t n_merges, int32_t *id_map_out);
 
 /* Release a model and its device tables (the caller makes sure no queued
  * work still uses it).  NULL is ignored. */

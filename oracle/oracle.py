@@ -240,3 +240,85 @@ def replay_merges(merges, w: bytes) -> list[int]:
     out = np.zeros(max(1, len(w)), dtype=np.int32)
     n = lib().ora_replay_merges(_ptr(m), m.shape[0], _ptr(a), len(w), _ptr(out))
     return out[:n].tolist()
+
+
+# ---- the text form of a table ("Tokenization LLM: details of building an
+# inference engine in C++", sections "Byte-level encoding" and "Vocabulary
+# lookup": each byte prints as one character, so merges and vocabularies are
+# stored as text; reading R8 for the character of each byte) ----
+
+def _expansions(merges) -> list[bytes]:
+    """Bytes of every symbol: a byte, or its merge's two operands' bytes."""
+    m = np.asarray(merges, dtype=np.int64).reshape(-1, 2)
+    exp: list[bytes | None] = [bytes([b]) for b in range(256)] + [None] * m.shape[0]
+    todo = True
+    while todo:
+        todo = False
+        for r, (a, b) in enumerate(m.tolist()):
+            if exp[256 + r] is None and exp[a] is not None and exp[b] is not None:
+                exp[256 + r] = exp[a] + exp[b]
+                todo = True
+    assert all(e is not None for e in exp), "operand out of range or a cycle"
+    return exp
+
+
+_printed = None
+
+
+def _print_table():
+    global _printed
+    if _printed is None:
+        chars = [byte_to_unicode(x) for x in range(256)]
+        _printed = (chars, {ch: x for x, ch in enumerate(chars)})
+    return _printed
+
+
+def bytes_to_text(b: bytes) -> str:
+    chars, _ = _print_table()
+    return "".join(chars[x] for x in b)
+
+
+def text_to_bytes(t: str) -> bytes:
+    _, inv = _print_table()
+    return bytes(inv[ch] for ch in t)
+
+
+def merges_to_text(merges) -> str:
+    """A merges file: a version line, then "left right" per merge in rank order."""
+    exp = _expansions(merges)
+    m = np.asarray(merges).reshape(-1, 2)
+    return "#version: 0.2\n" + "".join(f"{bytes_to_text(exp[a])} {bytes_to_text(exp[b])}\n"
+                                       for a, b in m.tolist())
+
+
+def parse_merges_text(text: str) -> np.ndarray:
+    """The integer table of a merges file: each line's operands looked up by
+    their bytes among the bytes and the earlier lines' results."""
+    sym = {bytes([b]): b for b in range(256)}
+    out = []
+    lines = text.split("\n")
+    for n, line in enumerate(lines):
+        line = line[:-1] if line.endswith("\r") else line
+        if not line or (n == 0 and line.startswith("#version")):
+            continue
+        left, right = line.split(" ")
+        lb, rb = text_to_bytes(left), text_to_bytes(right)
+        assert lb + rb not in sym, "two lines give the same bytes"
+        out.append((sym[lb], sym[rb]))
+        sym[lb + rb] = 256 + len(out) - 1
+    return np.array(out, dtype=np.int32).reshape(-1, 2)
+
+
+def vocab_to_json(merges, id_map, ensure_ascii: bool = True, extra: dict | None = None) -> str:
+    import json
+    exp = _expansions(merges)
+    d = {bytes_to_text(e): int(i) for e, i in zip(exp, np.asarray(id_map).tolist())}
+    d.update(extra or {})
+    return json.dumps(d, ensure_ascii=ensure_ascii)
+
+
+def parse_vocab_json(text: str, merges) -> np.ndarray:
+    """Each symbol's ID: the vocabulary's entry for the text of its bytes."""
+    import json
+    d = json.loads(text)
+    return np.array([d[bytes_to_text(e)] for e in _expansions(merges)], dtype=np.int32)
