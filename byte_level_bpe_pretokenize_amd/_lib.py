@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(PKG, "libbpe.so")
 
 # every symbol include/bpe.h declares
 SYMBOLS = (
-    "bpe_load_merges", "bpe_parse_merges_text", "bpe_parse_vocab_json",
+    "bpe_load_merges", "bpe_parse_merges_text", "bpe_parse_vocab_json", "bpe_train",
     "bpe_free", "bpe_vocab_size", "bpe_max_token_bytes",
     "bpe_encode_workspace_bytes", "bpe_encode_batch",
     "bpe_encode_special_workspace_bytes", "bpe_encode_batch_special",
@@ -45,6 +45,8 @@ def load() -> C.CDLL:
     L.bpe_parse_merges_text.restype = i32
     L.bpe_parse_vocab_json.argtypes = [p, i64, p, i64, p]
     L.bpe_parse_vocab_json.restype = i32
+    L.bpe_train.argtypes = [p, i64, p, i64, i64, p, p, C.POINTER(C.c_int64), p]
+    L.bpe_train.restype = i32
     L.bpe_free.argtypes = [p]
     L.bpe_free.restype = None
     L.bpe_vocab_size.argtypes = [p]

@@ -60,6 +60,26 @@ def parse_vocab_json(text: bytes | str, merges) -> np.ndarray:
     return out
 
 
+def train(data, doc_off, n_merges: int, stream=None):
+    """Train a merge table on the current GPU (bpe_train): data (uint8 bytes,
+    host) and doc_off (int64, host); returns (merges (R, 2) int32, counts)."""
+    if not torch.cuda.is_available():
+        raise RuntimeError("libbpe needs a HIP device; none is visible")
+    d = np.ascontiguousarray(np.frombuffer(data, dtype=np.uint8) if isinstance(data, (bytes, bytearray))
+                             else np.asarray(data, dtype=np.uint8))
+    off = np.ascontiguousarray(np.asarray(doc_off, dtype=np.int64))
+    merges = np.zeros((max(1, n_merges), 2), dtype=np.int32)
+    counts = np.zeros(max(1, n_merges), dtype=np.int64)
+    made = C.c_int64()
+    rc = _lib.load().bpe_train(d.ctypes.data_as(C.c_void_p) if d.size else None, d.size,
+                               off.ctypes.data_as(C.c_void_p), off.size - 1, int(n_merges),
+                               merges.ctypes.data_as(C.c_void_p), counts.ctypes.data_as(C.c_void_p),
+                               C.byref(made), C.c_void_p(_stream_handle(stream)))
+    if rc != _lib.BPE_OK:
+        raise BPEError(rc, "bpe_train")
+    return merges[:made.value].copy(), counts[:made.value].copy()
+
+
 class Model:
     """A merge table resident on the current GPU (bpe_load_merges)."""
 

@@ -10,6 +10,8 @@
 #include <array>
 #include <cstring>
 #include <new>
+#include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/bpe.h"
@@ -846,6 +848,127 @@ int bpe_stage_times(bpe_model *model, int op, double *ms, int max_stages, int64_
   *n_calls = (int64_t)(r.size() / n);
   model->spare.insert(model->spare.end(), r.begin(), r.end());
   r.clear();
+  return rc;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Byte classes and the pre-token start rule, as the encode kernels apply them
+// (readings R1-R3): a document start, or a class change unless a single space
+// that opens the document or follows a non-whitespace byte leads a letter.
+int host_class(uint8_t b) {
+  if ((b >= 'A' && b <= 'Z') || (b >= 'a' && b <= 'z') || b >= 0x80) return 0;  // letter
+  if (b >= '0' && b <= '9') return 1;                                          // digit
+  if ((b >= 0x09 && b <= 0x0D) || b == 0x20) return 2;                         // whitespace
+  return 3;                                                                    // punctuation
+}
+
+bool host_start(const uint8_t *d, int64_t i) {
+  if (i == 0) return true;
+  const int c0 = host_class(d[i]), c1 = host_class(d[i - 1]);
+  if (c0 == c1) return false;
+  return !(c0 == 0 && d[i - 1] == 0x20 && (i == 1 || host_class(d[i - 2]) != 2));
+}
+
+// Device copies for training, made before any kernel runs (blocking copies:
+// the host vectors may go away as soon as they return).
+template <class T>
+T *dev_copy(const std::vector<T> &v, std::vector<void *> &owned) {
+  void *p = nullptr;
+  if (hipMalloc(&p, sizeof(T) * std::max<size_t>(v.size(), 1)) != hipSuccess) return nullptr;
+  owned.push_back(p);
+  if (!v.empty() && hipMemcpy(p, v.data(), sizeof(T) * v.size(), hipMemcpyHostToDevice) != hipSuccess)
+    return nullptr;
+  return (T *)p;
+}
+
+template <class T>
+T *dev_zeros(size_t n, std::vector<void *> &owned) {
+  void *p = nullptr;
+  if (hipMalloc(&p, sizeof(T) * std::max<size_t>(n, 1)) != hipSuccess) return nullptr;
+  owned.push_back(p);
+  if (hipMemset(p, 0, sizeof(T) * std::max<size_t>(n, 1)) != hipSuccess) return nullptr;
+  return (T *)p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bpe_train(const uint8_t *bytes, int64_t n_bytes, const int64_t *doc_off, int64_t n_docs,
+              int64_t n_merges, int32_t *merges_out, int64_t *counts_out, int64_t *n_made,
+              void *hip_stream) {
+  if (n_bytes < 0 || n_docs < 0 || !doc_off || (n_bytes > 0 && !bytes) || n_merges < 0 ||
+      n_merges > BPE_MAX_MERGES || (n_merges > 0 && !merges_out) || !n_made)
+    return BPE_EINVAL;
+  if (doc_off[0] != 0 || doc_off[n_docs] != n_bytes) return BPE_EINVAL;
+  for (int64_t d = 0; d < n_docs; ++d)
+    if (doc_off[d + 1] < doc_off[d]) return BPE_EINVAL;
+  *n_made = 0;
+  // the distinct pre-tokens and their frequencies
+  std::unordered_map<std::string, int64_t> freq;
+  for (int64_t d = 0; d < n_docs; ++d) {
+    const uint8_t *doc = bytes + doc_off[d];
+    const int64_t n = doc_off[d + 1] - doc_off[d];
+    for (int64_t i = 0; i < n;) {
+      int64_t e = i + 1;
+      while (e < n && !host_start(doc, e)) ++e;
+      ++freq[std::string((const char *)doc + i, (size_t)(e - i))];
+      i = e;
+    }
+  }
+  std::vector<int32_t> sym, pos_word, word_len;
+  std::vector<int64_t> word_off, word_freq;
+  for (const auto &kv : freq) {
+    const int32_t w = (int32_t)word_off.size();
+    word_off.push_back((int64_t)sym.size());
+    word_len.push_back((int32_t)kv.first.size());
+    word_freq.push_back(kv.second);
+    for (unsigned char ch : kv.first) {
+      sym.push_back(ch);
+      pos_word.push_back(w);
+    }
+  }
+  if (n_merges == 0 || sym.empty()) return BPE_OK;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  std::vector<void *> owned;
+  int rc = BPE_OK;
+  TrainArgs a;
+  a.n_words = (int64_t)word_off.size();
+  a.n_pos = (int64_t)sym.size();
+  uint64_t slots = 2;
+  while (slots < 2 * (uint64_t)a.n_pos) slots *= 2;
+  a.mask = slots - 1;
+  a.sym = dev_copy(sym, owned);
+  a.word_off = dev_copy(word_off, owned);
+  a.word_len = dev_copy(word_len, owned);
+  a.word_freq = dev_copy(word_freq, owned);
+  a.pos_word = dev_copy(pos_word, owned);
+  a.keys = dev_zeros<uint64_t>((size_t)slots, owned);
+  a.counts = dev_zeros<uint64_t>((size_t)slots, owned);
+  a.best = dev_zeros<uint64_t>(2, owned);
+  a.stop = dev_zeros<int32_t>(1, owned);
+  a.merges = dev_zeros<int32_t>((size_t)(2 * n_merges), owned);
+  a.out_counts = dev_zeros<int64_t>((size_t)n_merges, owned);
+  a.made = dev_zeros<int64_t>(1, owned);
+  if (!a.sym || !a.word_off || !a.word_len || !a.word_freq || !a.pos_word || !a.keys ||
+      !a.counts || !a.best || !a.stop || !a.merges || !a.out_counts || !a.made)
+    rc = BPE_ENOMEM;
+  for (int64_t r = 0; rc == BPE_OK && r < n_merges; ++r)
+    if (launch_train_step(a, r, stream) != hipSuccess) rc = BPE_EHIP;
+  int64_t made = 0;
+  if (rc == BPE_OK &&
+      (hipMemcpyAsync(&made, a.made, sizeof(int64_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+       hipMemcpyAsync(merges_out, a.merges, sizeof(int32_t) * 2 * (size_t)n_merges,
+                      hipMemcpyDeviceToHost, stream) != hipSuccess ||
+       (counts_out && hipMemcpyAsync(counts_out, a.out_counts, sizeof(int64_t) * (size_t)n_merges,
+                                     hipMemcpyDeviceToHost, stream) != hipSuccess)))
+    rc = BPE_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess && rc == BPE_OK) rc = BPE_EHIP;
+  for (void *p : owned) (void)hipFree(p);
+  if (rc == BPE_OK) *n_made = made;
   return rc;
 }
 

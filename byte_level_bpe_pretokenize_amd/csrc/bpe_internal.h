@@ -389,6 +389,26 @@ hipError_t launch_empty(const int64_t *offs, int64_t n_docs, uint32_t bad_bit, i
 constexpr int kEncStages = 10;
 extern const char *const kEncStageNames[kEncStages];
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
+// Training (bpe_train.hip): the distinct pre-tokens of the corpus with their
+// frequencies, their current symbols, and the pair table of one merge.
+struct TrainArgs {
+  int32_t *sym;              // symbols of pre-token w from word_off[w], word_len[w] of them
+  const int64_t *word_off;
+  int32_t *word_len;
+  const int64_t *word_freq;
+  const int32_t *pos_word;   // the pre-token of each original position
+  int64_t n_words, n_pos;
+  uint64_t *keys;            // pair table: (left << 32 | right) + 1, 0 = empty
+  uint64_t *counts;
+  uint64_t mask;             // slots - 1 (a power of two, at least 2 n_pos)
+  uint64_t *best;            // [2]: the merge's best count, then its smallest key
+  int32_t *stop;             // set once the best count is below 2
+  int32_t *merges;           // [n_merges][2] out
+  int64_t *out_counts;       // [n_merges] out
+  int64_t *made;             // merges made
+};
+hipError_t launch_train_step(const TrainArgs &a, int64_t r, hipStream_t stream);
+
 // The reserved IDs of an empty input, after launch_empty (bpe_encode.hip).
 hipError_t launch_special(const SpecialArgs &a, hipStream_t stream);
 // The decode pipeline for n_ids > 0 (bpe_decode.hip), events as for encode.

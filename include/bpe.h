@@ -141,6 +141,29 @@ int bpe_parse_merges_text(const char *text, int64_t text_len, int32_t *merges_ou
 int bpe_parse_vocab_json(const char *json, int64_t json_len, const int32_t *merges,
                          int64_t n_merges, int32_t *id_map_out);
 
+/*
+ * Train a merge table on the current device ("Characters, bytes and
+ * subwords", section "BPE step by step": count the adjacent pairs, the most
+ * frequent one merges into a new symbol (ties: the smallest IDs), replace its
+ * occurrences, count again, until n_merges merges or no pair occurs twice;
+ * "Hugging Face Tokenizers v1", section "How v1 works": merges stay inside
+ * pre-tokens).  Readings: pairs are counted at every position, weighted by
+ * the pre-token's frequency in the corpus; ties go to the smallest (left,
+ * right); replacement is encoding's left-to-right pass without overlap.
+ *  bytes, doc_off  host memory: the corpus as for bpe_encode_batch (offsets
+ *                  that are not 0 = d[0] <= ... <= d[n_docs] = n_bytes give
+ *                  BPE_EINVAL).
+ *  merges_out      host int32 [n_merges][2]: merge r, rank order.
+ *  counts_out      host int64 [n_merges] or NULL: each merge's pair count.
+ *  n_made          receives the number of merges made (<= n_merges).
+ * The pre-tokens are collected on the host, then each merge runs as kernels
+ * on hip_stream; the call allocates its own device memory and waits for the
+ * result.  Returns BPE_OK, BPE_EINVAL, BPE_ENOMEM or BPE_EHIP.
+ */
+int bpe_train(const uint8_t *bytes, int64_t n_bytes, const int64_t *doc_off, int64_t n_docs,
+              int64_t n_merges, int32_t *merges_out, int64_t *counts_out, int64_t *n_made,
+              void *hip_stream);
+
 /* Release a model and its device tables (the caller makes sure no queued
  * work still uses it).  NULL is ignored. */
 void bpe_free(bpe_model *model);
