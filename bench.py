@@ -24,7 +24,8 @@ the kernel sources still hash to the value recorded there.
 Beside the timed encode the line carries the decode of the same IDs
 (`decode`, a round trip) and the encode with a BOS and an EOS ID around each
 document (`special`, bpe_encode_batch_special), each timed the same way and
-checked against the plain encode.
+checked against the plain encode, and (`train`) bpe_train on the workload's
+training corpus, its table checked against the one stored in assets/.
 """
 from __future__ import annotations
 
@@ -81,6 +82,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip timing bpe_train on the workload's training corpus")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of the input (for counter scaling)")
     return ap.parse_args()
@@ -337,6 +340,21 @@ def main():
     special = {"ms": round(sms, 4), "bos_eos_per_document": 2, "ids_match_plain": sp_ok}
     del sws, sp_ids, sp_t, keep
 
+    # the GPU trainer on the workload's training corpus (the throughput and
+    # tiny workloads), its table checked against the one stored in assets/
+    train_info = None
+    if not args.no_train and args.workload in ("throughput", "tiny"):
+        from byte_level_bpe_pretokenize_amd import train as bpe_train
+        from workloads import training_corpus
+        tc = training_corpus(cfg, make_lexicon(cfg))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tm, _ = bpe_train(tc.data, tc.doc_off, cfg.n_merges)
+        train_s = time.perf_counter() - t0
+        train_info = {"s": round(train_s, 3), "merges": int(tm.shape[0]),
+                      "corpus_bytes": int(tc.data.size),
+                      "matches_stored_table": bool(np.array_equal(tm, merges))}
+
     ids_np = ids[:T].cpu().numpy()
     id_off_np = id_off.cpu().numpy()
     fnv = None
@@ -392,6 +410,7 @@ def main():
         "ids_fnv1a64": fnv,
         "decode": dec,
         "special": special,
+        "train": train_info,
         "ids_sha256": hashlib.sha256(ids_np.tobytes()).hexdigest()[:16],
     }
     print(json.dumps(line), flush=True)
