@@ -182,3 +182,25 @@ def test_special_long_pretokens(dev):
     docs = [b"x " + b"a" * 9000 + b" tail", b"", b"7" * 3000, b"short one", b"b" * 4100]
     data, off = batch_from_docs(docs)
     check_special(model, table, data, off, V + 5, V + 9)
+
+
+@pytest.mark.parametrize("name", ["throughput", "serving"])
+def test_special_full_size(dev, name):
+    # the whole batch at its full size, in the launch configuration bench.py
+    # times: with the reserved IDs taken out the IDs are the plain encode's,
+    # and every document is [bos] ... [eos] at the plain offset + 2 d
+    from workloads import encode_batch_input
+    cfg = WORKLOADS[name]
+    batch = encode_batch_input(cfg, make_lexicon(cfg))
+    model, _ = model_pair(name)
+    V = model.vocab_size
+    data = torch.from_numpy(batch.data).to(dev)
+    off = torch.from_numpy(batch.doc_off).to(dev)
+    plain, plain_off = model.encode_batch(data, off)
+    ids, id_off = model.encode_batch_special(data, off, V, V + 1)
+    D = batch.n_docs
+    assert torch.equal(id_off, plain_off + 2 * torch.arange(D + 1, device=dev))
+    keep = (ids != V) & (ids != V + 1)
+    assert torch.equal(ids[keep], plain)
+    assert bool((ids[id_off[:-1]] == V).all()) and bool((ids[id_off[1:] - 1] == V + 1).all())
+    assert int((~keep).sum()) == 2 * D
