@@ -62,8 +62,10 @@ __global__ void __launch_bounds__(TWG) k_tcount(TrainArgs a) {
   const unsigned long long f = (unsigned long long)a.word_freq[w];
   uint64_t s = tslot(key, a.mask);
   for (uint64_t probe = 0; probe <= a.mask; ++probe) {
-    const unsigned long long old =
-        atomicCAS((unsigned long long *)&a.keys[s], 0ull, (unsigned long long)key);
+    // a slot goes from empty to its key once per merge: a plain read that
+    // finds the key needs no CAS (the frequent pairs' slots are the hot ones)
+    unsigned long long old = a.keys[s];
+    if (old == 0ull) old = atomicCAS((unsigned long long *)&a.keys[s], 0ull, (unsigned long long)key);
     if (old == 0ull || old == key) {
       atomicAdd((unsigned long long *)&a.counts[s], f);
       return;
