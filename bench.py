@@ -173,8 +173,9 @@ def cpu_baseline_all_cores(merges, batch, rate1, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(documents shard independently across GPUs, see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(documents are independent: a batch shards by document ranges, one process per GPU)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -21,7 +21,7 @@
  *       (dothoosh.com): How v1 works (BPE definition, merges never cross a
  *       pre-token boundary), Benchmarks (FNV-1a over output IDs).
  *
- * Readings where the pages are silent (the same list is in the design notes):
+ * Readings where the pages are silent:
  *  R1 byte classes: L = A-Z a-z and every byte >= 0x80; D = 0-9;
  *     W = 0x09-0x0D and 0x20; P = every other byte.
  *  R2 split: leftmost-first alternation of greedy runs ` ?L+ | D+ | P+ | W+`,
