@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(PKG, "libbpe.so")
 SYMBOLS = (
     "bpe_load_merges", "bpe_parse_merges_text", "bpe_parse_vocab_json", "bpe_train",
     "bpe_free", "bpe_vocab_size", "bpe_max_token_bytes",
-    "bpe_encode_workspace_bytes", "bpe_encode_batch",
+    "bpe_encode_workspace_bytes", "bpe_encode_batch", "bpe_encode_batch_noalloc",
     "bpe_encode_special_workspace_bytes", "bpe_encode_batch_special",
     "bpe_decode_workspace_bytes", "bpe_decode_batch", "bpe_decode_batch_special",
     "bpe_stage_timing", "bpe_stage_count", "bpe_stage_name", "bpe_stage_times",
@@ -19,7 +19,8 @@ SYMBOLS = (
 )
 
 BPE_OK, BPE_EINVAL, BPE_EMERGES, BPE_EIDMAP, BPE_EWORKSPACE, BPE_EHIP, BPE_ENOMEM, BPE_ENOTSUP, \
-    BPE_EFORMAT = 0, -1, -2, -3, -4, -5, -6, -7, -8
+    BPE_EFORMAT, BPE_ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+NOALLOC_SCRATCH_BYTES = 128 << 20
 STATUS_BAD_DOC_OFFSETS, STATUS_IDS_CAPACITY, STATUS_BAD_ID, STATUS_BYTES_CAPACITY, \
     STATUS_BAD_ID_OFFSETS = 1, 2, 4, 8, 16
 OP_ENCODE, OP_DECODE = 0, 1
@@ -57,6 +58,8 @@ def load() -> C.CDLL:
     L.bpe_encode_workspace_bytes.restype = sz
     L.bpe_encode_batch.argtypes = [p, p, i64, p, i64, p, i64, p, p, sz, p, p]
     L.bpe_encode_batch.restype = i32
+    L.bpe_encode_batch_noalloc.argtypes = [p, p, i64, p, i64, p, i64, p, p, p]
+    L.bpe_encode_batch_noalloc.restype = i32
     L.bpe_encode_special_workspace_bytes.argtypes = [p, i64, i64]
     L.bpe_encode_special_workspace_bytes.restype = sz
     L.bpe_encode_batch_special.argtypes = [p, p, i64, p, i64, i32, i32, p, i64, p, p, sz, p, p]

@@ -172,6 +172,26 @@ class Model:
         if rc != _lib.BPE_OK:
             raise BPEError(rc, "bpe_encode_batch")
 
+    def encode_batch_noalloc_into(self, data: torch.Tensor, doc_off: torch.Tensor,
+                                  ids: torch.Tensor, id_off: torch.Tensor, status: torch.Tensor,
+                                  stream=None) -> None:
+        """bpe_encode_batch_noalloc: as encode_batch_into, with the library's
+        static scratch as the workspace (inputs up to NOALLOC_SCRATCH_BYTES of
+        workspace; calls on one GPU must not overlap)."""
+        n_bytes = int(data.numel())
+        n_docs = int(doc_off.numel()) - 1
+        if data.dtype != torch.uint8 or doc_off.dtype != torch.int64 or ids.dtype != torch.int32 \
+                or id_off.dtype != torch.int64 or status.dtype != torch.int32:
+            raise TypeError("dtypes: data uint8, doc_off int64, ids int32, id_off int64, status int32")
+        if n_docs < 0 or id_off.numel() != n_docs + 1:
+            raise ValueError("doc_off and id_off need n_docs + 1 entries")
+        rc = _lib.load().bpe_encode_batch_noalloc(
+            self._h, _dptr(data) if n_bytes else None, n_bytes, _dptr(doc_off), n_docs,
+            _dptr(ids) if ids.numel() else None, int(ids.numel()), _dptr(id_off), _dptr(status),
+            C.c_void_p(_stream_handle(stream)))
+        if rc != _lib.BPE_OK:
+            raise BPEError(rc, "bpe_encode_batch_noalloc")
+
     def encode_batch(self, data: torch.Tensor, doc_off: torch.Tensor, ids_capacity: int | None = None,
                      stream=None):
         """Allocate outputs, encode, synchronize, and return (ids[:T], id_off)."""

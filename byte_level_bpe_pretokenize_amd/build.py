@@ -13,8 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbpe.so")
 SOURCES = [os.path.join(CSRC, f)
-           for f in ("bpe_encode.hip", "bpe_decode.hip", "bpe_train.hip", "bpe_api.cpp",
-                     "bpe_text.cpp")]
+           for f in ("bpe_encode.hip", "bpe_decode.hip", "bpe_train.hip", "bpe_noalloc.hip",
+                     "bpe_api.cpp", "bpe_text.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

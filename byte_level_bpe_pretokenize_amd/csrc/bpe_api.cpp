@@ -230,7 +230,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
                    const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids, int64_t ids_capacity,
                    int64_t *d_id_off, void *d_workspace, int32_t *d_status, bool words,
                    const int32_t *id_map, hipStream_t stream, int32_t bos = -1,
-                   int32_t eos = -1) {
+                   int32_t eos = -1, bool timed = true) {
   if (n_bytes == 0)
     return launch_empty(d_doc_off, n_docs, BPE_STATUS_BAD_DOC_OFFSETS, d_id_off, d_status,
                         stream) == hipSuccess
@@ -288,9 +288,36 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   for (int k = 0; k < 4; ++k) a.win_d[k] = model->win_d[k];
   a.bos = bos;
   a.eos = eos;
-  if (launch_encode(a, stream, call_events(model, BPE_OP_ENCODE)) != hipSuccess) return BPE_EHIP;
+  if (launch_encode(a, stream, timed ? call_events(model, BPE_OP_ENCODE) : nullptr) != hipSuccess)
+    return BPE_EHIP;
   return BPE_OK;
 }
+
+}  // namespace
+
+namespace bpe {
+
+int encode_checked(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
+                   const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids, int64_t ids_capacity,
+                   int64_t *d_id_off, void *d_workspace, size_t workspace_bytes, int32_t *d_status,
+                   void *hip_stream, bool timed) {
+  if (!model || n_bytes < 0 || n_docs < 0 || ids_capacity < 0 || !d_doc_off || !d_id_off ||
+      !d_status || (ids_capacity > 0 && !d_ids) || (n_bytes > 0 && (!d_bytes || !d_workspace)))
+    return BPE_EINVAL;
+  // a launch holds at most 2^32 - 1 work-items
+  if (enc_chunks(n_bytes) * kEncThreads > (int64_t)UINT32_MAX) return BPE_EINVAL;
+  if (!on_model_device(model)) return BPE_EINVAL;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (n_bytes > 0 && workspace_bytes < enc_layout(n_bytes, n_docs).total) return BPE_EWORKSPACE;
+  return enqueue_encode(model, d_bytes, n_bytes, d_doc_off, n_docs, d_ids, ids_capacity, d_id_off,
+                        d_workspace, d_status, true, model->d_id_map, stream, -1, -1, timed);
+}
+
+int model_device(const bpe_model *model) { return model ? model->device : -1; }
+
+}  // namespace bpe
+
+namespace {
 
 // Two-choice cuckoo placement with one slot per bucket for entries with
 // hashes h, in order: each into its first slot when free, else its second,
@@ -682,16 +709,8 @@ int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_b
                      const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids,
                      int64_t ids_capacity, int64_t *d_id_off, void *d_workspace,
                      size_t workspace_bytes, int32_t *d_status, void *hip_stream) {
-  if (!model || n_bytes < 0 || n_docs < 0 || ids_capacity < 0 || !d_doc_off || !d_id_off ||
-      !d_status || (ids_capacity > 0 && !d_ids) || (n_bytes > 0 && (!d_bytes || !d_workspace)))
-    return BPE_EINVAL;
-  // a launch holds at most 2^32 - 1 work-items
-  if (enc_chunks(n_bytes) * kEncThreads > (int64_t)UINT32_MAX) return BPE_EINVAL;
-  if (!on_model_device(model)) return BPE_EINVAL;
-  hipStream_t stream = (hipStream_t)hip_stream;
-  if (n_bytes > 0 && workspace_bytes < enc_layout(n_bytes, n_docs).total) return BPE_EWORKSPACE;
-  return enqueue_encode(model, d_bytes, n_bytes, d_doc_off, n_docs, d_ids, ids_capacity, d_id_off,
-                        d_workspace, d_status, true, model->d_id_map, stream);
+  return bpe::encode_checked(model, d_bytes, n_bytes, d_doc_off, n_docs, d_ids, ids_capacity,
+                             d_id_off, d_workspace, workspace_bytes, d_status, hip_stream, true);
 }
 
 namespace {
@@ -983,6 +1002,7 @@ const char *bpe_strerror(int code) {
     case BPE_ENOMEM: return "out of memory";
     case BPE_ENOTSUP: return "decode unsupported: byte expansions of this table are too large";
     case BPE_EFORMAT: return "text form rejected (malformed line, JSON or UTF-8, or an unmapped character)";
+    case BPE_ESCRATCH: return "input too large for the library's static scratch (BPE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error";
   }
 }

@@ -4,7 +4,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct bpe_model;
+
 namespace bpe {
+
+// bpe_encode_batch's argument checks and launches (bpe_api.cpp); `timed`:
+// record stage-timing events when the model has them enabled.
+int encode_checked(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
+                   const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids, int64_t ids_capacity,
+                   int64_t *d_id_off, void *d_workspace, size_t workspace_bytes, int32_t *d_status,
+                   void *hip_stream, bool timed);
+// The device a model was loaded on (-1 for NULL).
+int model_device(const bpe_model *model);
 
 // ---- byte classes ---------------------------------------------------------
 // The fixed split rule's classes: letters (A-Z, a-z and every byte from 0x80

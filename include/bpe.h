@@ -66,6 +66,7 @@ extern "C" {
 #define BPE_ENOMEM (-6)      /* host or device allocation failed while loading */
 #define BPE_ENOTSUP (-7)     /* decode: this table's byte expansions exceed BPE_MAX_EXPANSION */
 #define BPE_EFORMAT (-8)     /* text form: malformed line, JSON or UTF-8, or a character no byte prints as */
+#define BPE_ESCRATCH (-9)    /* bpe_encode_batch_noalloc: the input needs more than BPE_NOALLOC_SCRATCH_BYTES */
 
 /* bits of *d_status */
 #define BPE_STATUS_BAD_DOC_OFFSETS 1u   /* encode: offsets not 0 = d[0] <= ... <= d[n_docs] = n_bytes */
@@ -112,8 +113,8 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
  *
  * Parse a merges file: UTF-8 text, one merge per line ("left right", one
  * space), in rank order, after an optional first line starting with
- * "#version"; empty lines are skipped and a line may end in "
-".  Each
+ * "#version"; empty lines are skipped and a line may end in a carriage
+ * return (0x0D) before its line feed.  Each
  * operand is a byte or the text of an earlier line's result, and no two lines
  * may give the same bytes.
  *  merges_out  host int32 [max_merges][2]: row r receives line r's operands
@@ -203,6 +204,32 @@ int bpe_encode_batch(const bpe_model *model, const uint8_t *d_bytes, int64_t n_b
                      const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids,
                      int64_t ids_capacity, int64_t *d_id_off, void *d_workspace,
                      size_t workspace_bytes, int32_t *d_status, void *hip_stream);
+
+/*
+ * Encode with no allocation and no caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array of
+ * BPE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, which each GPU
+ * holds from the first such call on it until the process ends; its device
+ * address is looked up once per device, on that first call.  The call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine, and
+ * no stage-timing events).
+ *  Arguments, outputs, status bits and the operation are bpe_encode_batch's,
+ *  without d_workspace / workspace_bytes.
+ *  Inputs whose bpe_encode_workspace_bytes(model, n_bytes, n_docs) exceeds
+ *  BPE_NOALLOC_SCRATCH_BYTES are rejected with BPE_ESCRATCH before anything is
+ *  queued.
+ *  Every call on one GPU shares that GPU's array: calls that may overlap on one
+ *  GPU (several streams or host threads) race and must be serialized by the
+ *  caller.  The array keeps the last call's contents; the kernels clear what
+ *  they need cleared themselves.
+ * Returns BPE_OK, BPE_EINVAL, BPE_ESCRATCH or BPE_EHIP.
+ */
+#define BPE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int bpe_encode_batch_noalloc(const bpe_model *model, const uint8_t *d_bytes, int64_t n_bytes,
+                             const int64_t *d_doc_off, int64_t n_docs, int32_t *d_ids,
+                             int64_t ids_capacity, int64_t *d_id_off, int32_t *d_status,
+                             void *hip_stream);
 
 /*
  * Reserved IDs around each document: post-processing ("Characters, bytes and

@@ -78,6 +78,8 @@ def test_null_model_calls():
     assert L.bpe_max_token_bytes(None) == -1
     assert L.bpe_encode_batch(None, None, 0, None, 0, None, 0, None, None, 0, None, None) == _lib.BPE_EINVAL
     assert L.bpe_decode_batch(None, None, 0, None, 0, None, 0, None, None, 0, None, None) == _lib.BPE_EINVAL
+    assert L.bpe_encode_batch_noalloc(None, None, 0, None, 0, None, 0, None, None, None) == _lib.BPE_EINVAL
+    assert b"scratch" in L.bpe_strerror(_lib.BPE_ESCRATCH)
     assert L.bpe_encode_batch_special(None, None, 0, None, 0, -1, -1, None, 0, None, None, 0, None,
                                       None) == _lib.BPE_EINVAL
     assert L.bpe_decode_batch_special(None, None, 0, None, 0, -1, -1, None, 0, None, None, 0, None,
