@@ -281,11 +281,6 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.res = (int32_t *)(ws + L.res);
   a.gsym = (int32_t *)(ws + L.gsym);
   a.grank = (int32_t *)(ws + L.grank);
-  a.cstate = (unsigned long long *)(ws + L.cstate);
-  a.tick = (uint32_t *)(ws + L.tick);
-  a.stage = (int32_t *)(ws + L.stage);
-  a.lw = (int32_t *)(ws + L.lw);
-  a.doc_w = (int32_t *)(ws + L.doc_w);
   a.status = d_status;
   a.n_chunks = enc_chunks(n_bytes);
   a.doc_per = (n_docs + 1 + a.n_chunks - 1) / a.n_chunks;

@@ -148,8 +148,8 @@ struct AsciiPairs {
 // a consumed position leaves the live mask, and each pair joins a live
 // position to the next live one.
 template <int W, class Pairs>
-__device__ uint32_t lane_merge_cols(const uint32_t *w, const int len, LaneCols<W> &L,
-                                    const RankTable &t, const Pairs &pair_rank) {
+__device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, const RankTable &t,
+                          const Pairs &pair_rank, int32_t *out) {
   const int lane = lane_id();
   uint32_t *S = &L.s[0][lane];
   uint32_t *K = &L.k[0][lane];
@@ -225,16 +225,6 @@ __device__ uint32_t lane_merge_cols(const uint32_t *w, const int len, LaneCols<W
     if (hp) K[64 * p] = vl;
     K[64 * i] = vr;  // i < q <= W - 1
   }
-  return alive;
-}
-
-// lane_merge_cols, then the symbols left written to out in order; returns
-// their count.
-template <int W, class Pairs>
-__device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, const RankTable &t,
-                          const Pairs &pair_rank, int32_t *out) {
-  const uint32_t alive = lane_merge_cols<W>(w, len, L, t, pair_rank);
-  const uint32_t *S = &L.s[0][lane_id()];
   int n = 0;
 #pragma unroll
   for (int j = 0; j < W; ++j)
@@ -441,10 +431,10 @@ __device__ __forceinline__ uint32_t sb16(const FindShared &s, int g) {
 
 // The bytes of the pre-token at window position st (len <= kWordMax) as six
 // little-endian words, zero padded.
-__device__ __forceinline__ void pretoken_words(const uint8_t *B, int st, int len,
+__device__ __forceinline__ void pretoken_words(const FindShared &s, int st, int len,
                                                uint32_t w[kWordWords]) {
   const int b0 = 16 + st;
-  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(B);
+  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
   const int q = b0 >> 2;
   const uint32_t sh = (uint32_t)(b0 & 3);
   uint32_t raw[kWordWords + 1];
@@ -461,14 +451,14 @@ __device__ __forceinline__ void pretoken_words(const uint8_t *B, int st, int len
 
 // The first kShortMax bytes at window position st as three little-endian
 // words, the bytes past len zeroed.
-__device__ __forceinline__ void short_words(const uint8_t *B, const u32x4 *LM, int st, int len,
-                                            uint32_t &w0, uint32_t &w1, uint32_t &w2) {
+__device__ __forceinline__ void short_words(const FindShared &s, int st, int len, uint32_t &w0,
+                                            uint32_t &w1, uint32_t &w2) {
   const int b0 = 16 + st;
-  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(B);
+  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
   const int q = b0 >> 2;
   const uint32_t sh = (uint32_t)(b0 & 3);
   const uint32_t r0 = B32[q], r1 = B32[q + 1], r2 = B32[q + 2], r3 = B32[q + 3];
-  const u32x4 m = LM[min(len, kShortMax)];
+  const u32x4 m = s.LM[min(len, kShortMax)];
   w0 = __builtin_amdgcn_alignbyte(r1, r0, sh) & m.x;
   w1 = __builtin_amdgcn_alignbyte(r2, r1, sh) & m.y;
   w2 = __builtin_amdgcn_alignbyte(r3, r2, sh) & m.z;
@@ -493,10 +483,10 @@ __device__ __forceinline__ int32_t short_lookup(const EncodeArgs &a, uint32_t w0
 
 // Symbol of a pre-token of kShortMax + 1..kWordMax bytes in the long word
 // table, or -1.
-__device__ __forceinline__ int32_t long_lookup(const uint8_t *B, const EncodeArgs &a, int st,
+__device__ __forceinline__ int32_t long_lookup(const FindShared &s, const EncodeArgs &a, int st,
                                                int len) {
   uint32_t w[kWordWords];
-  pretoken_words(B, st, len, w);
+  pretoken_words(s, st, len, w);
   const uint32_t h = word_hash(w, len, a.lword_seed);
   const uint32_t tag = word_tag(h, len);
   uint32_t i = word_slot0(h, a.lword_mask);
@@ -519,15 +509,7 @@ __device__ __forceinline__ int32_t long_lookup(const uint8_t *B, const EncodeArg
 // document scan there.
 __global__ void __launch_bounds__(256) k_docs(EncodeArgs a) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c == 0) {
-    // a new call: the status word, the tickets, no staged chunk yet
-    *a.status = 0;
-    a.tick[0] = 0;
-    a.tick[1] = 0;
-    a.tick[2] = (uint32_t)a.n_chunks;
-  }
   if (c >= a.n_chunks) return;
-  a.cstate[c] = 0ull;
   const int64_t key = c * kChunk - 1;
   int64_t lo = 0, hi = a.n_docs + 1;  // first index in [lo, hi) with doc_off >= key
   while (lo < hi) {
@@ -712,7 +694,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     const int st = s.PS[k];
     const int len = over ? 0 : (int)s.PS[k + 1] - st;
     uint32_t w0, w1, w2;
-    short_words(s.B, s.LM, st, len, w0, w1, w2);
+    short_words(s, st, len, w0, w1, w2);
     int32_t v = -1;
     if (len == 1) {
       v = (int32_t)w0;
@@ -720,7 +702,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
       if (len <= kShortMax) {
         if (a.words) v = short_lookup(a, w0, w1, w2, len);
       } else if (len <= kWordMax && a.lwords) {
-        v = long_lookup(s.B, a, st, len);
+        v = long_lookup(s, a, st, len);
       }
     }
     if (v >= 0) pv[k] = v;
@@ -844,9 +826,10 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
 // Entry A (words wa, la bytes) uses columns LA, entry B columns LB; an entry
 // with va / vb false is absent.  Returns the token counts in *nta, *ntb.
 template <int W, class Pairs>
-__device__ void lane_merge2_cols(const uint32_t *wa, int la, bool va, const uint32_t *wb, int lb,
-                                 bool vb, LaneCols<W> &LA, LaneCols<W> &LB, const RankTable &t,
-                                 const Pairs &pair_rank, uint32_t &alive_a, uint32_t &alive_b) {
+__device__ void lane_merge2(const uint32_t *wa, int la, bool va, int32_t *outa, int *nta,
+                            const uint32_t *wb, int lb, bool vb, int32_t *outb, int *ntb,
+                            LaneCols<W> &LA, LaneCols<W> &LB, const RankTable &t,
+                            const Pairs &pair_rank) {
   const int lane = lane_id();
   uint32_t *SA = &LA.s[0][lane], *KA = &LA.k[0][lane];
   uint32_t *SB = &LB.s[0][lane], *KB = &LB.k[0][lane];
@@ -979,21 +962,6 @@ __device__ void lane_merge2_cols(const uint32_t *wa, int la, bool va, const uint
       rcB = rB;
     }
   }
-  alive_a = va ? aliveA : 0u;
-  alive_b = vb ? aliveB : 0u;
-}
-
-// lane_merge2_cols, then both entries' symbols written to outa / outb;
-// their counts in *nta, *ntb.
-template <int W, class Pairs>
-__device__ void lane_merge2(const uint32_t *wa, int la, bool va, int32_t *outa, int *nta,
-                            const uint32_t *wb, int lb, bool vb, int32_t *outb, int *ntb,
-                            LaneCols<W> &LA, LaneCols<W> &LB, const RankTable &t,
-                            const Pairs &pair_rank) {
-  uint32_t aliveA, aliveB;
-  lane_merge2_cols<W>(wa, la, va, wb, lb, vb, LA, LB, t, pair_rank, aliveA, aliveB);
-  const int lane = lane_id();
-  const uint32_t *SA = &LA.s[0][lane], *SB = &LB.s[0][lane];
   int na = 0, nb = 0;
 #pragma unroll
   for (int j = 0; j < W; ++j) {
@@ -1875,6 +1843,7 @@ __global__ void __launch_bounds__(OWG) k_bscan(EncodeArgs a) {
 // ---- k_emit -------------------------------------------------------------------
 
 constexpr int EWG = 256;                 // k_emit threads per chunk
+constexpr int kOutCap = kChunk + kHalo;  // chunk-relative token positions staged in LDS
 constexpr int kEmitPasses = 3;           // passes of EWG pre-tokens per round
 
 constexpr int kDocLds = 512;             // document starts of a chunk staged in LDS (with reserved IDs)
@@ -2151,683 +2120,6 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
 }
 
-// ---- k_one, k_fix: a chunk in one pass ----------------------------------------
-//
-// k_one takes each chunk through every step in one workgroup: the window's
-// start bits and ordered pre-token list (as k_find), the word tables, the
-// merge loop of its 2-32 byte misses by lanes (tokens kept in LDS), its token
-// count, its output offset by a single-pass scan over the chunks (decoupled
-// look-back), and its IDs and document offsets written at their final place.
-// A chunk with a pre-token longer than kLaneMax bytes cannot know its count
-// before k_merge_long has merged it: it writes its other IDs to its stage
-// region instead, and so does every chunk after it (their offsets depend on
-// its count); k_fix then places those chunks once k_merge_long is done.
-
-constexpr int kOneWaves = WG / 64;
-constexpr int kOneRegPasses = 4;                   // pre-tokens below kOneRegK keep their value in registers
-constexpr int kOneRegK = kOneRegPasses * WG;       // (the others in the chunk's pv region)
-constexpr int kOneMlCap = kChunk / 2;              // 2-32 byte merge-loop entries of a chunk, at most
-constexpr int kOneTokCap = 1024;                   // their tokens in LDS (the rest in the chunk's res region)
-constexpr int kOneDocCap = 256;                    // documents starting in a chunk with their first pre-token in LDS
-constexpr int kOneMergeWaves = 2;                  // waves that run the 2-16 byte merges
-
-// Chunk states of the single-pass offset scan: a 64-bit word, state << 62 |
-// value, written and read whole.
-constexpr unsigned long long kStAgg = 1ull << 62;  // value: the chunk's token count
-constexpr unsigned long long kStInc = 2ull << 62;  // value: tokens of all chunks up to and including it
-constexpr unsigned long long kStBlk = 3ull << 62;  // its count or offset waits for k_fix
-constexpr unsigned long long kStVal = (1ull << 62) - 1;
-
-__device__ __forceinline__ void state_put(unsigned long long *p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned long long state_get(const unsigned long long *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The offset of chunk c from the states of the chunks before it, by one wave
-// (every lane active): 64 chunks per step, nearest first.  A state of 0 (not
-// yet written) or, when `wait_blk`, kStBlk is waited for; the walk ends at
-// the first kStInc (its value added) or, unless `wait_blk`, kStBlk (the
-// result is then -1); kStAgg values are added on the way.  Before chunk 0
-// the offset is 0.
-// The wait is bounded: after kLookSpins sleeps the chunk gives up, sets
-// BPE_STATUS_SCAN_STALL and takes offset 0 (the outputs are then not valid),
-// so that the kernel still ends.
-constexpr int kLookSpins = 1 << 23;
-
-__device__ int64_t look_back(const unsigned long long *cs, int64_t c, bool wait_blk,
-                             int32_t *status) {
-  const int lane = lane_id();
-  int64_t p = c - 1;
-  unsigned long long sum = 0;
-  int spins = 0;
-  for (;;) {
-    const int64_t q = p - lane;
-    const unsigned long long v = q >= 0 ? state_get(cs + q) : kStInc;
-    const unsigned long long st = v >> 62;
-    const bool busy = st == 0 || (wait_blk && st == 3);
-    const uint64_t term = __ballot(!busy && st >= 2);
-    const uint64_t wait = __ballot(busy);
-    const uint64_t first = term & (~term + 1);  // the nearest terminal chunk (0: none)
-    const uint64_t before = first ? first - 1 : ~0ull;
-    if (wait & before) {
-      if (++spins > kLookSpins) {
-        if (lane == 0) atomicOr(status, (int32_t)BPE_STATUS_SCAN_STALL);
-        return 0;
-      }
-      __builtin_amdgcn_s_sleep(2);
-      continue;
-    }
-    const unsigned long long add = ((1ull << lane) & (before | first)) ? (v & kStVal) : 0ull;
-    sum += wave_sum(add);
-    if (first) {
-      const int tl = __ffsll((unsigned long long)first) - 1;
-      const unsigned long long vt = __shfl(v, tl, 64);
-      return (vt >> 62) == 2 ? (int64_t)sum : -1;
-    }
-    p -= 64;
-  }
-}
-
-// The bytes at window position st as NW little-endian words, zero past len.
-template <int NW>
-__device__ __forceinline__ void window_words(const uint8_t *B, int st, int len, uint32_t *w) {
-  const int b0 = 16 + st;
-  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(B);
-  const int q = b0 >> 2;
-  const uint32_t sh = (uint32_t)(b0 & 3);
-  uint32_t raw[NW + 1];
-#pragma unroll
-  for (int i = 0; i <= NW; ++i) raw[i] = B32[q + i];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t v = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
-    const int valid = len - 4 * i;
-    const uint32_t m = valid >= 4 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : ((1u << (8 * valid)) - 1u));
-    w[i] = v & m;
-  }
-}
-
-struct OneShared {
-  alignas(16) uint8_t B[16 + WIN + 32];  // B[16 + p] = byte at window position p
-  uint32_t DB[DB_WORDS];                 // document start bits, positions [-32, WIN)
-  union {
-    struct {
-      uint32_t SB[SB_WORDS];             // pre-token start bits of the owned positions
-      uint16_t PS[kChunk + 2];           // owned pre-token starts in order, then the end
-    } a;                                 // scan and lookups
-    LaneCols<16> c16[kOneMergeWaves];    // 2-16 byte merges, one column set per wave
-    LaneCols<32> c32;                    // 17-32 byte merges (one wave)
-    uint16_t W[kChunk + 2];              // output: each pre-token's first token position
-  } u;
-  uint32_t ML[kOneMlCap];                // 2-32 byte merge-loop entries, by length bucket:
-                                         // st | len << 12, then tokens at | count << 16
-  int32_t TOK[kOneTokCap];               // their tokens
-  int32_t DK[kOneDocCap];                // first pre-token of each document starting here
-  u32x4 LM[kShortMax + 1];
-  int32_t wtot[kOneRegPasses][kOneWaves];
-  Red<WG> r;
-  int64_t o_lo, o_hi;
-  int64_t base;                          // output offset, or -1: staged
-  int chunk, e_last, ntok;
-};
-
-template <class F>
-__device__ __forceinline__ void for_tokens(const OneShared &s, const int32_t *resc, int at, int n,
-                                           F &&f) {
-  for (int q = 0; q < n; ++q) {
-    const int t = at + q;
-    f(q, t < kOneTokCap ? s.TOK[t] : resc[t - kOneTokCap]);
-  }
-}
-
-__global__ void __launch_bounds__(WG, 4) k_one(EncodeArgs a) {
-  __shared__ OneShared s;
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-
-  // document offsets check, spread over the grid
-  bool bad = false;
-  {
-    const int64_t per = a.doc_per;
-    const int64_t i0 = (int64_t)blockIdx.x * per;
-    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += WG) {
-      const int64_t v = a.doc_off[i];
-      if (i == 0 && v != 0) bad = true;
-      if (i == a.n_docs && v != a.n_bytes) bad = true;
-      if (i < a.n_docs && a.doc_off[i + 1] < v) bad = true;
-    }
-  }
-  // chunks are taken in ticket order, so every chunk before this one has
-  // started when it looks back
-  if (tid == 0) {
-    s.chunk = (int)atomicAdd(&a.tick[0], 1u);
-    s.ntok = 0;
-  }
-  for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
-  if (tid <= kShortMax) {
-    u32x4 m;
-    m.x = tid >= 4 ? ~0u : (1u << (8 * tid)) - 1u;
-    m.y = tid >= 8 ? ~0u : (tid <= 4 ? 0u : (1u << (8 * (tid - 4))) - 1u);
-    m.z = tid >= 12 ? ~0u : (tid <= 8 ? 0u : (1u << (8 * (tid - 8))) - 1u);
-    m.w = 0;
-    s.LM[tid] = m;
-  }
-  __syncthreads();
-  const int64_t c = s.chunk;
-  const int64_t c0 = c * kChunk;
-  const int64_t n = a.n_bytes;
-  const int nwin = (int)min<int64_t>(WIN, n - c0);
-  const int nown = (int)min<int64_t>(kChunk, n - c0);
-  const bool win_reaches_end = (c0 + nwin == n);
-
-  // 1. the window's bytes (16 per load), and the document starts in it
-  const bool aligned = (((uintptr_t)a.bytes) & 15u) == 0;
-  constexpr int NG = WIN / 16 + 1;
-  u32x4 reg[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int g = tid - 1 + r * WG;
-    reg[r] = u32x4{0, 0, 0, 0};
-    const int64_t gp = c0 + 16 * (int64_t)g;
-    if (g + 1 < NG && aligned && gp >= 0 && gp + 16 <= n)
-      reg[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.bytes + gp));
-  }
-  if (wave == 0) {
-    int64_t d0 = min(max(a.dfirst[c], (int64_t)0), a.n_docs);  // (k_docs)
-    int64_t olo = d0, ohi = d0;
-    for (;;) {
-      const int64_t d = d0 + lane;
-      const int64_t v = d < a.n_docs ? a.doc_off[d] : INT64_MAX;
-      const int64_t p = v - c0;
-      if (p >= -1 && p < nwin) atomicOr(&s.DB[(p + DB_OFF) >> 5], 1u << ((p + DB_OFF) & 31));
-      olo += __popcll(__ballot(v < c0));
-      ohi += __popcll(__ballot(v < c0 + nown));
-      if (!(lane_value(v, 63) < c0 + nwin)) break;
-      d0 += 64;
-    }
-    if (lane == 0) {
-      s.o_lo = olo;
-      s.o_hi = ohi;
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int g = tid - 1 + r * WG;
-    if (g + 1 >= NG) continue;
-    const int64_t gp = c0 + 16 * (int64_t)g;
-    uint8_t *dst = &s.B[16 + 16 * g];
-    if (aligned && gp >= 0 && gp + 16 <= n) {
-      *reinterpret_cast<u32x4 *>(dst) = reg[r];
-    } else {
-      for (int k = 0; k < 16; ++k) {
-        const int64_t q = gp + k;
-        dst[k] = (q >= 0 && q < n) ? a.bytes[q] : 0;
-      }
-    }
-  }
-  __syncthreads();
-
-  // 2. start bits of the owned positions (as k_find)
-  for (int g = tid; g < kChunk / 16; g += WG) {
-    const u32x4 cur = *reinterpret_cast<const u32x4 *>(&s.B[16 + 16 * g]);
-    const uint32_t before = *reinterpret_cast<const uint32_t *>(&s.B[16 + 16 * g - 4]);
-    const int q = 16 * g - 1 + DB_OFF;
-    const uint64_t dw = (uint64_t)s.DB[q >> 5] | ((uint64_t)s.DB[(q >> 5) + 1] << 32);
-    const uint32_t doc = (uint32_t)(dw >> (q & 31));
-    const uint32_t w[5] = {before, cur.x, cur.y, cur.z, cur.w};
-    uint32_t m = start_bits16(w, doc);
-    const int lim = nwin - 16 * g;
-    if (lim < 16) {
-      const uint32_t past = lim <= 0 ? 0xFFFFu : (0xFFFFu << lim) & 0xFFFFu;
-      m = (m & ~past) | (win_reaches_end ? past : 0u);
-    }
-    reinterpret_cast<uint16_t *>(s.u.a.SB)[g] = (uint16_t)m;
-  }
-  __syncthreads();
-
-  // 3. the owned pre-token starts in order, then the end of the last
-  uint32_t own = 0;
-  if (16 * tid < nown) {
-    own = reinterpret_cast<const uint16_t *>(s.u.a.SB)[tid];
-    const int lim = nown - 16 * tid;
-    if (lim < 16) own &= (1u << lim) - 1;
-  }
-  if (wave == 0) {
-    const int p = nown + lane;
-    bool st;
-    if (p >= nwin) {
-      st = win_reaches_end;
-    } else {
-      const uint32_t b0 = s.B[16 + p], b1 = s.B[16 + p - 1], b2 = s.B[16 + p - 2];
-      const uint32_t k0 = byte_class(b0), k1 = byte_class(b1);
-      const int q0 = p + DB_OFF, q1 = p - 1 + DB_OFF;
-      const bool d0 = (s.DB[q0 >> 5] >> (q0 & 31)) & 1u, d1 = (s.DB[q1 >> 5] >> (q1 & 31)) & 1u;
-      const bool attach = k0 == kL && b1 == 0x20u && (d1 || byte_class(b2) != kW);
-      st = d0 || (k0 != k1 && !attach);
-    }
-    const uint64_t m = __ballot(st);
-    if (lane == 0) {
-      int e = m ? nown + __ffsll((unsigned long long)m) - 1
-                : ((win_reaches_end && nwin == WIN) ? WIN : kNoStart);
-      s.e_last = e <= WIN ? e : kNoStart;
-    }
-  }
-  int n_pt;
-  {
-    const int pex = block_excl_sum<int, WG>(__popc(own), s.r.red, &n_pt);
-    uint32_t m = own;
-    for (int k = pex; m; ++k, m &= m - 1) s.u.a.PS[k] = (uint16_t)(16 * tid + __ffs(m) - 1);
-    if (tid == 0) s.u.a.PS[n_pt] = (uint16_t)(s.e_last == kNoStart ? WIN : s.e_last);
-  }
-  __syncthreads();
-  const bool overhang = n_pt > 0 && s.e_last == kNoStart;
-
-  // 4. every pre-token: a single byte, a word-table entry, or a merge-loop
-  //    entry of length bucket 0 (2-8 bytes), 1 (9-16), 2 (17-32) or 3 (longer,
-  //    or running past the window); pre-token k belongs to thread k % WG
-  int32_t *pvc = a.pv + c * kChunk;
-  auto lookup = [&](int k, int32_t &v) -> int {
-    const bool over = overhang && k == n_pt - 1;
-    const int st = s.u.a.PS[k];
-    const int len = over ? 0 : (int)s.u.a.PS[k + 1] - st;
-    uint32_t w0, w1, w2;
-    short_words(s.B, s.LM, st, len, w0, w1, w2);
-    v = -1;
-    if (len == 1) {
-      v = (int32_t)w0;
-    } else if (!over) {
-      if (len <= kShortMax) {
-        if (a.words) v = short_lookup(a, w0, w1, w2, len);
-      } else if (len <= kWordMax && a.lwords) {
-        v = long_lookup(s.B, a, st, len);
-      }
-    }
-    if (v >= 0) return -1;
-    return bucket_of(len, over);
-  };
-  int32_t vr[kOneRegPasses];
-  uint32_t bk = 0;      // 2 bits per register pass: the bucket of a merge-loop entry
-  uint32_t missed = 0;  // bit j: pre-token tid + j WG is a merge-loop entry
-  uint32_t cnt01 = 0, cnt23 = 0;  // this thread's entries per bucket, 16 bits each
-#pragma unroll
-  for (int j = 0; j < kOneRegPasses; ++j) {
-    const int k = tid + j * WG;
-    vr[j] = 0;
-    if (k < n_pt) {
-      int32_t v;
-      const int b = lookup(k, v);
-      vr[j] = v;
-      if (b >= 0) {
-        missed |= 1u << j;
-        bk |= (uint32_t)b << (2 * j);
-        if (b < 2) cnt01 += 1u << (16 * b);
-        else cnt23 += 1u << (16 * (b - 2));
-      }
-    }
-  }
-  for (int k = tid + kOneRegK, j = kOneRegPasses; k < n_pt; k += WG, ++j) {
-    int32_t v;
-    const int b = lookup(k, v);
-    if (b >= 0) {
-      missed |= 1u << j;
-      pvc[k] = -1 - b;  // the bucket, until the entry has its slot
-      if (b < 2) cnt01 += 1u << (16 * b);
-      else cnt23 += 1u << (16 * (b - 2));
-    } else {
-      pvc[k] = v;
-    }
-  }
-  // slots: buckets 0-2 side by side in ML, bucket 3 in the chunk's list of
-  // long entries (k_merge_long)
-  int t01, t23;
-  const int e01 = block_excl_sum<int, WG>((int)cnt01, s.r.red, &t01);
-  const int e23 = block_excl_sum<int, WG>((int)cnt23, s.r.red, &t23);
-  const int n0 = t01 & 0xFFFF, n1 = (int)((uint32_t)t01 >> 16), n2 = t23 & 0xFFFF,
-            n3 = (int)((uint32_t)t23 >> 16);
-  uint32_t r0 = (uint32_t)e01 & 0xFFFFu, r1 = (uint32_t)n0 + ((uint32_t)e01 >> 16),
-           r2 = (uint32_t)(n0 + n1) + ((uint32_t)e23 & 0xFFFFu), r3 = (uint32_t)e23 >> 16;
-  uint32_t *lng = a.miss + c * kMissMax + kBucketBase[3];
-  auto place = [&](int k, int b) -> int32_t {
-    const bool over = overhang && k == n_pt - 1;
-    const int st = s.u.a.PS[k];
-    const int len = over ? 0 : (int)s.u.a.PS[k + 1] - st;
-    uint32_t slot;
-    if (b == 0) slot = r0++;
-    else if (b == 1) slot = r1++;
-    else if (b == 2) slot = r2++;
-    else slot = r3++;
-    if (b < 3) {
-      s.ML[slot] = (uint32_t)st | ((uint32_t)len << 12);
-      return -1 - (int32_t)slot;
-    }
-    lng[slot] = miss_entry(st, len, over);
-    return -1 - kPvLong - (int32_t)slot;
-  };
-#pragma unroll
-  for (int j = 0; j < kOneRegPasses; ++j)
-    if ((missed >> j) & 1u) vr[j] = place(tid + j * WG, (int)((bk >> (2 * j)) & 3u));
-  for (int k = tid + kOneRegK, j = kOneRegPasses; k < n_pt; k += WG, ++j)
-    if ((missed >> j) & 1u) pvc[k] = place(k, -1 - pvc[k]);
-  // each document that starts here: its first pre-token
-  for (int64_t d = s.o_lo + tid; d < s.o_hi; d += WG) {
-    const int p = (int)min(max(a.doc_off[d] - c0, (int64_t)0), (int64_t)kChunk - 1);
-    int lo = 0, hi = n_pt;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if ((int)s.u.a.PS[mid] < p) lo = mid + 1;
-      else hi = mid;
-    }
-    if (d - s.o_lo < kOneDocCap) s.DK[d - s.o_lo] = lo;
-    else a.doc_pt[d] = lo;
-  }
-  __syncthreads();  // the starts are no longer needed: their LDS holds merge columns next
-
-  // 5. merge-loop entries of 2-16 bytes: batches of 128 2-8 byte entries (two
-  //    per lane) and of 64 9-16 byte entries, one batch per wave at a time;
-  //    then 17-32 byte entries by one wave.  Each batch's tokens take the next
-  //    positions of the chunk's token area.
-  const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
-  const GlobalPairs gp{a.pair_rank};
-  int32_t *resc = a.res + c * kMissSpan;
-  auto tok_put = [&](int at, int32_t v) {
-    if (at < kOneTokCap) s.TOK[at] = v;
-    else resc[at - kOneTokCap] = v;
-  };
-  // token area positions for this lane's entries (nt tokens), whole wave
-  auto tok_take = [&](int nt) -> int {
-    const int inc = wave_incl_sum(nt);
-    int b = 0;
-    if (lane == 63 && inc) b = atomicAdd(&s.ntok, inc);
-    return lane_value(b, 63) + inc - nt;
-  };
-  const int nb0 = (n0 + 127) / 128, nb1 = (n1 + 63) / 64;
-  if (wave < kOneMergeWaves) {
-    LaneCols<16> &L = s.u.c16[wave];
-    for (int bi = wave; bi < nb0 + nb1; bi += kOneMergeWaves) {
-      if (bi < nb0) {
-        LaneCols<8> &LA = *reinterpret_cast<LaneCols<8> *>(&L);
-        LaneCols<8> &LB = *(reinterpret_cast<LaneCols<8> *>(&L) + 1);
-        const int ia = bi * 128 + lane, ib = ia + 64;
-        const bool va = ia < n0, vb = ib < n0;
-        const uint32_t ea = va ? s.ML[ia] : 0u, eb = vb ? s.ML[ib] : 0u;
-        const int la = (int)(ea >> 12), lb = (int)(eb >> 12);
-        uint32_t wa[2], wb[2];
-        window_words<2>(s.B, (int)(ea & 0xFFFu), la, wa);
-        window_words<2>(s.B, (int)(eb & 0xFFFu), lb, wb);
-        uint32_t aa, ab;
-        lane_merge2_cols<8>(wa, la, va, wb, lb, vb, LA, LB, t, gp, aa, ab);
-        const int na = __popc(aa), nb = __popc(ab);
-        const int o = tok_take(na + nb);
-        const uint32_t *SA = &LA.s[0][lane], *SB = &LB.s[0][lane];
-        int q = o;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if ((aa >> j) & 1u) tok_put(q++, (int32_t)SA[64 * j]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if ((ab >> j) & 1u) tok_put(q++, (int32_t)SB[64 * j]);
-        if (va) s.ML[ia] = (uint32_t)o | ((uint32_t)na << 16);
-        if (vb) s.ML[ib] = (uint32_t)(o + na) | ((uint32_t)nb << 16);
-      } else {
-        const int g = (bi - nb0) * 64 + lane;
-        const bool v = g < n1;
-        const int i = n0 + g;
-        const uint32_t e = v ? s.ML[i] : 0u;
-        const int len = v ? (int)(e >> 12) : 0;
-        uint32_t w[4];
-        window_words<4>(s.B, (int)(e & 0xFFFu), len, w);
-        const uint32_t al = lane_merge_cols<16>(w, len, L, t, gp);
-        const int nt = v ? __popc(al) : 0;
-        const int o = tok_take(nt);
-        const uint32_t *S = &L.s[0][lane];
-        int q = o;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (v && ((al >> j) & 1u)) tok_put(q++, (int32_t)S[64 * j]);
-        if (v) s.ML[i] = (uint32_t)o | ((uint32_t)nt << 16);
-      }
-    }
-  }
-  if (n2 > 0) {
-    __syncthreads();  // the 17-32 byte columns cover both column sets
-    if (wave == 0) {
-      LaneCols<32> &L = s.u.c32;
-      for (int g0 = 0; g0 < n2; g0 += 64) {
-        const int g = g0 + lane;
-        const bool v = g < n2;
-        const int i = n0 + n1 + g;
-        const uint32_t e = v ? s.ML[i] : 0u;
-        const int len = v ? (int)(e >> 12) : 0;
-        uint32_t w[8];
-        window_words<8>(s.B, (int)(e & 0xFFFu), len, w);
-        const uint32_t al = lane_merge_cols<32>(w, len, L, t, gp);
-        const int nt = v ? __popc(al) : 0;
-        const int o = tok_take(nt);
-        const uint32_t *S = &L.s[0][lane];
-        int q = o;
-        for (int j = 0; j < 32; ++j)
-          if (v && ((al >> j) & 1u)) tok_put(q++, (int32_t)S[64 * j]);
-        if (v) s.ML[i] = (uint32_t)o | ((uint32_t)nt << 16);
-      }
-    }
-  }
-  __syncthreads();
-
-  // 6. the chunk's count, then its offset: from the chunks before it, unless
-  //    it has a long entry or one of them waits for k_fix (then staged)
-  const int n_miss = n0 + n1 + n2 + n3;
-  const int64_t count = (int64_t)(n_pt - n_miss) + s.ntok;  // without the long entries' tokens
-  const bool any_bad = __syncthreads_or(bad);
-  if (tid == 0) {
-    int32_t *m = a.meta + kMetaInts * c;
-    m[kMetaPretokens] = n_pt;
-    m[kMetaBucket + 3] = n3;
-    a.tot[c] = count;  // k_merge_long adds the long entries' counts
-    a.doc_rng[2 * c] = s.o_lo;
-    a.doc_rng[2 * c + 1] = s.o_hi;
-  }
-  if (wave == 0) {
-    unsigned long long *cs = a.cstate;
-    int64_t base = -1;
-    if (n3 == 0) {
-      if (c == 0) {
-        base = 0;
-        if (lane == 0) state_put(cs, kStInc | (unsigned long long)count);
-      } else {
-        if (lane == 0) state_put(cs + c, kStAgg | (unsigned long long)count);
-        base = look_back(cs, c, false, a.status);
-        if (lane == 0)
-          state_put(cs + c, base >= 0 ? (kStInc | (unsigned long long)(base + count)) : kStBlk);
-      }
-    } else if (lane == 0) {
-      state_put(cs + c, kStBlk);
-    }
-    if (lane == 0) {
-      s.base = base;
-      if (base < 0) atomicMin(&a.tick[2], (uint32_t)c);
-    }
-  }
-  __syncthreads();
-
-  // 7. the IDs, in rounds of kOneRegPasses passes of WG pre-tokens: each
-  //    pass's token counts scanned over the workgroup, then each pre-token's
-  //    tokens written at their place (or staged)
-  const int64_t base = s.base;
-  const bool direct = base >= 0;
-  const bool docs_here = s.o_hi > s.o_lo;
-  int32_t *stg = a.stage + c * kOutCap;
-  int32_t *lwc = a.lw + c * kMaxLong;
-  bool overflow = false;
-  auto put = [&](int w, int32_t sym) {
-    if (direct) {
-      const int64_t o = base + w;
-      if (o < a.ids_cap) a.ids[o] = out_id(a.id_map, sym);
-      else overflow = true;
-    } else {
-      stg[w] = sym;
-    }
-  };
-  int carry = 0;
-  for (int rr = 0; rr < n_pt; rr += kOneRegK) {
-    const int np = min(kOneRegPasses, (n_pt - rr + WG - 1) / WG);
-    int32_t v[kOneRegPasses], cnt[kOneRegPasses], inc[kOneRegPasses];
-    uint32_t e[kOneRegPasses];
-#pragma unroll
-    for (int j = 0; j < kOneRegPasses; ++j) {
-      if (j >= np) continue;
-      const int k = rr + j * WG + tid;
-      v[j] = k < n_pt ? (rr == 0 ? vr[j] : pvc[k]) : INT32_MIN;
-      const int u = -1 - v[j];
-      e[j] = (v[j] < 0 && v[j] != INT32_MIN && u < kPvLong) ? s.ML[u] : 0u;
-      cnt[j] = v[j] >= 0 ? 1 : (int)(e[j] >> 16);
-      inc[j] = wave_incl_sum(cnt[j]);
-      if (lane == 63) s.wtot[j][wave] = inc[j];
-    }
-    __syncthreads();
-    int run = 0;
-#pragma unroll
-    for (int j = 0; j < kOneRegPasses; ++j) {
-      if (j >= np) continue;
-      int before = 0, all = 0;
-#pragma unroll
-      for (int ww = 0; ww < kOneWaves; ++ww) {
-        const int x = s.wtot[j][ww];
-        if (ww < wave) before += x;
-        all += x;
-      }
-      const int w = carry + run + before + inc[j] - cnt[j];
-      run += all;
-      const int k = rr + j * WG + tid;
-      if (k >= n_pt) continue;
-      const int32_t x = v[j];
-      if (x >= 0) {
-        put(w, x);
-      } else {
-        const int u = -1 - x;
-        if (u < kPvLong) for_tokens(s, resc, (int)(e[j] & 0xFFFFu), cnt[j], [&](int q, int32_t y) { put(w + q, y); });
-        else lwc[u - kPvLong] = w;
-      }
-      if (docs_here) s.u.W[k] = (uint16_t)w;
-    }
-    carry += run;
-    __syncthreads();
-  }
-
-  // 8. offsets of the documents that start here (the first token of their
-  //    first pre-token); past the last chunk, the empty documents at the end
-  for (int64_t d = s.o_lo + tid; d < s.o_hi; d += WG) {
-    const int kd = d - s.o_lo < kOneDocCap ? s.DK[d - s.o_lo] : a.doc_pt[d];
-    const int w = kd < n_pt ? (int)s.u.W[kd] : carry;
-    if (direct) a.id_off[d] = base + w;
-    else a.doc_w[d] = w;
-  }
-  if (direct && c == a.n_chunks - 1)
-    for (int64_t d = s.o_hi + tid; d <= a.n_docs; d += WG) a.id_off[d] = base + carry;
-  if (tid == 0 && (any_bad)) atomicOr(a.status, (int32_t)BPE_STATUS_BAD_DOC_OFFSETS);
-  if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
-}
-
-// The staged chunks, from the first one on, in ticket order: each chunk's
-// count now includes its long entries (k_merge_long), so its offset follows
-// from the states before it (a staged chunk before it is waited for); then
-// its staged IDs are written with the long entries' tokens between them, and
-// its documents' offsets moved by the long entries before them.
-constexpr int kFixThreads = 256;
-
-struct FixShared {
-  int32_t st[kMaxLong];     // long entries: start in the chunk, position among the staged IDs,
-  int32_t w[kMaxLong];      // token count, in start order
-  int32_t nt[kMaxLong];
-  int32_t pre[kMaxLong + 1];  // tokens of the long entries before each
-  int64_t base;
-  int chunk;
-};
-
-__global__ void __launch_bounds__(kFixThreads) k_fix(EncodeArgs a) {
-  __shared__ FixShared s;
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const uint32_t first = a.tick[2];  // the first staged chunk (n_chunks: none)
-  if ((int64_t)blockIdx.x >= a.n_chunks - (int64_t)first) return;
-  if (tid == 0) s.chunk = (int)(first + atomicAdd(&a.tick[1], 1u));
-  __syncthreads();
-  const int64_t c = s.chunk, c0 = c * kChunk;
-  const int n3 = a.meta[kMetaInts * c + kMetaBucket + 3];
-  const int64_t total = a.tot[c];
-  // the long entries in start order (they were listed in no particular order)
-  const uint32_t *lng = a.miss + c * kMissMax + kBucketBase[3];
-  for (int q = tid; q < n3; q += kFixThreads) {
-    const int st = me_start(lng[q]);
-    int r = 0;
-    for (int q2 = 0; q2 < n3; ++q2) r += me_start(lng[q2]) < st ? 1 : 0;
-    s.st[r] = st;
-    s.w[r] = a.lw[c * kMaxLong + q];
-    s.nt[r] = a.mt[c * kMaxLong + q];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int r = 0; r < n3; ++r) {
-      s.pre[r] = run;
-      run += s.nt[r];
-    }
-    s.pre[n3] = run;
-  }
-  if (wave == 0) {
-    unsigned long long *cs = a.cstate;
-    int64_t base;
-    if (c == 0) {
-      base = 0;
-      if (lane == 0) state_put(cs, kStInc | (unsigned long long)total);
-    } else {
-      if (lane == 0) state_put(cs + c, kStAgg | (unsigned long long)total);
-      base = look_back(cs, c, true, a.status);
-      if (lane == 0) state_put(cs + c, kStInc | (unsigned long long)(base + total));
-    }
-    if (lane == 0) s.base = base;
-  }
-  __syncthreads();
-  const int64_t base = s.base;
-  const int64_t nshort = total - s.pre[n3];
-  bool overflow = false;
-  auto put = [&](int64_t o, int32_t sym) {
-    if (o < a.ids_cap) a.ids[o] = out_id(a.id_map, sym);
-    else overflow = true;
-  };
-  // staged IDs: moved by the tokens of the long entries at or before them
-  const int32_t *stg = a.stage + c * kOutCap;
-  for (int64_t w = tid; w < nshort; w += kFixThreads) {
-    int lo = 0, hi = n3;  // long entries with position <= w
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (s.w[mid] <= w) lo = mid + 1;
-      else hi = mid;
-    }
-    put(base + w + s.pre[lo], stg[w]);
-  }
-  // the long entries' tokens
-  for (int r = 0; r < n3; ++r) {
-    const int64_t o = base + s.w[r] + s.pre[r];
-    const int32_t *src = a.gsym + c0 + s.st[r];
-    for (int q = tid; q < s.nt[r]; q += kFixThreads) put(o + q, src[q]);
-  }
-  // documents that start here
-  const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
-  for (int64_t d = dlo + tid; d < dhi; d += kFixThreads) {
-    const int64_t p = a.doc_off[d] - c0;
-    int lo = 0, hi = n3;  // long entries that start before the document
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (s.st[mid] < p) lo = mid + 1;
-      else hi = mid;
-    }
-    a.id_off[d] = base + a.doc_w[d] + s.pre[lo];
-  }
-  if (c == a.n_chunks - 1)
-    for (int64_t d = dhi + tid; d <= a.n_docs; d += kFixThreads) a.id_off[d] = base + total;
-  if (overflow) atomicOr(a.status, (int32_t)BPE_STATUS_IDS_CAPACITY);
-}
-
 // ---- k_special ------------------------------------------------------------------
 // Reserved IDs around the documents of an empty input (every document
 // empty, as k_empty has checked): document d is [bos, eos] at d (nb + ne).
@@ -2892,18 +2184,6 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
     if (ev) (void)hipEventRecord(ev[st++], stream);
   };
   mark();
-  if (a.bos < 0 && a.eos < 0) {
-    hipLaunchKernelGGL(k_docs, dim3((G + 255) / 256), dim3(256), 0, stream, a);
-    mark();
-    hipLaunchKernelGGL(k_one, dim3(G), dim3(WG), 0, stream, a);
-    mark();
-    hipLaunchKernelGGL(k_merge_long, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
-    mark();
-    hipLaunchKernelGGL(k_fix, dim3(G), dim3(kFixThreads), 0, stream, a);
-    if (ev)
-      while (st <= kEncStages) mark();
-    return hipGetLastError();
-  }
   hipLaunchKernelGGL(k_docs, dim3((G + 255) / 256), dim3(256), 0, stream, a);
   mark();
   hipLaunchKernelGGL(k_find, dim3(G), dim3(WG), 0, stream, a);

@@ -221,20 +221,10 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //   res       [G][kMissSpan] i32  its tokens, from o on
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
 //   grank     [N] i32   pair ranks of the wave merge, position-indexed
-//   cstate    [G] u64   single-pass offset scan: each chunk's state << 62 | value
-//   tick      [4] u32   tickets of k_one and k_fix, the first chunk whose
-//                       output waits for the long pre-tokens' pass
-//   stage     [G][kOutCap] i32  that chunk's IDs before the long pre-tokens'
-//                               tokens are put between them
-//   lw        [G][kMaxLong] i32 position of each long pre-token's first token
-//                               among the chunk's staged IDs
-//   doc_w     [D] i32   position of each document's first token among its
-//                       chunk's staged IDs
 struct EncLayout {
   size_t meta, tot, off, bsum, boff, doc_rng, dfirst, doc_pt, pv, cntk, miss, mt, dref, olist, dstat, dt, mbytes, res, gsym,
-      grank, cstate, tick, stage, lw, doc_w, total;
+      grank, total;
 };
-constexpr int kOutCap = kChunk + kHalo;  // a chunk's IDs before its long pre-tokens' tokens, at most
 
 // Chunks per workgroup of the first level of the offset scans.
 constexpr int kScanBlock = 1024;
@@ -280,11 +270,6 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.res = take(4 * (size_t)kMissSpan * G + 64);
   L.gsym = take(4 * (size_t)n_bytes);
   L.grank = take(4 * (size_t)n_bytes);
-  L.cstate = take(8 * G);
-  L.tick = take(16);
-  L.stage = take(4 * (size_t)kOutCap * G);
-  L.lw = take(4 * (size_t)kMaxLong * G);
-  L.doc_w = take(4 * (size_t)(n_docs + 1));
   L.total = o;
   return L;
 }
@@ -355,11 +340,6 @@ struct EncodeArgs {
   int32_t *res;
   int32_t *gsym;
   int32_t *grank;
-  unsigned long long *cstate;  // single-pass offset scan states
-  uint32_t *tick;            // [0]: k_one tickets, [1]: k_fix tickets, [2]: first chunk waiting for k_fix
-  int32_t *stage;
-  int32_t *lw;
-  int32_t *doc_w;
   int32_t *status;
   int64_t n_chunks;
   int64_t doc_per;           // document offsets checked per k_find workgroup: ceil((n_docs + 1) / n_chunks)

@@ -74,8 +74,6 @@ extern "C" {
 #define BPE_STATUS_BAD_ID 4u            /* decode: an ID that no symbol maps to */
 #define BPE_STATUS_BYTES_CAPACITY 8u    /* decode: more bytes than bytes_capacity (extra dropped) */
 #define BPE_STATUS_BAD_ID_OFFSETS 16u   /* decode: offsets not 0 = o[0] <= ... <= o[n_docs] = n_ids */
-#define BPE_STATUS_SCAN_STALL 32u       /* encode: a chunk's wait for the chunks before it gave up (not
-                                           expected; the outputs are then not valid) */
 
 /* limits */
 #define BPE_MAX_MERGES (1 << 20)               /* merges per table */
