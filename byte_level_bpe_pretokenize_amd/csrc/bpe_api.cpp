@@ -11,7 +11,6 @@
 #include <cstring>
 #include <new>
 #include <string>
-#include <unordered_map>
 #include <vector>
 
 #include "../../include/bpe.h"
@@ -874,7 +873,7 @@ int bpe_stage_times(bpe_model *model, int op, double *ms, int max_stages, int64_
 
 namespace {
 
-// Byte classes and the pre-token start rule, as the encode kernels apply them
+// Byte classes of the pre-token start rule, as the encode kernels apply it
 // (readings R1-R3): a document start, or a class change unless a single space
 // that opens the document or follows a non-whitespace byte leads a letter.
 int host_class(uint8_t b) {
@@ -884,11 +883,96 @@ int host_class(uint8_t b) {
   return 3;                                                                    // punctuation
 }
 
-bool host_start(const uint8_t *d, int64_t i) {
-  if (i == 0) return true;
-  const int c0 = host_class(d[i]), c1 = host_class(d[i - 1]);
-  if (c0 == c1) return false;
-  return !(c0 == 0 && d[i - 1] == 0x20 && (i == 1 || host_class(d[i - 2]) != 2));
+// The distinct pre-tokens of the documents with their frequencies (words in
+// order of first appearance): each pre-token's bytes as symbols in sym from
+// word_off[w], word_len[w] of them, and the pre-token of each position.  An
+// open-addressing table of byte spans (a multiplicative hash of 8-byte
+// words, compared with memcmp) finds a pre-token seen before.
+void collect_pretokens(const uint8_t *bytes, const int64_t *doc_off, int64_t n_docs,
+                       std::vector<int32_t> &sym, std::vector<int32_t> &pos_word,
+                       std::vector<int64_t> &word_off, std::vector<int32_t> &word_len,
+                       std::vector<int64_t> &word_freq) {
+  uint8_t cls[256];
+  for (int b = 0; b < 256; ++b) cls[b] = (uint8_t)host_class((uint8_t)b);
+  std::vector<const uint8_t *> first;  // each word's bytes (its first occurrence)
+  std::vector<uint64_t> hashes;
+  std::vector<int32_t> table(1 << 16, -1);
+  uint64_t mask = table.size() - 1;
+  auto hash_of = [](const uint8_t *p, int64_t n) {
+    uint64_t h = 0x9E3779B97F4A7C15ull ^ (uint64_t)n;
+    int64_t i = 0;
+    for (; i + 8 <= n; i += 8) {
+      uint64_t x;
+      std::memcpy(&x, p + i, 8);
+      h = (h ^ x) * 0xFF51AFD7ED558CCDull;
+      h ^= h >> 32;
+    }
+    uint64_t x = 0;
+    for (int64_t k = 0; i + k < n; ++k) x |= (uint64_t)p[i + k] << (8 * k);
+    h = (h ^ x) * 0xC4CEB9FE1A85EC53ull;
+    return h ^ (h >> 29);
+  };
+  auto insert = [&](const uint8_t *p, int64_t n, uint64_t h) {
+    uint64_t s = h & mask;
+    for (;;) {
+      const int32_t w = table[s];
+      if (w < 0) {
+        table[s] = (int32_t)first.size();
+        first.push_back(p);
+        hashes.push_back(h);
+        word_len.push_back((int32_t)n);
+        word_freq.push_back(1);
+        return;
+      }
+      if (hashes[(size_t)w] == h && word_len[(size_t)w] == n &&
+          std::memcmp(first[(size_t)w], p, (size_t)n) == 0) {
+        ++word_freq[(size_t)w];
+        return;
+      }
+      s = (s + 1) & mask;
+    }
+  };
+  for (int64_t d = 0; d < n_docs; ++d) {
+    const uint8_t *doc = bytes + doc_off[d];
+    const int64_t n = doc_off[d + 1] - doc_off[d];
+    for (int64_t i = 0; i < n;) {
+      int64_t e = i + 1;
+      // the next start: a class change, unless a single space after a
+      // non-whitespace byte (or at the document start) leads a letter
+      while (e < n) {
+        const int c0 = cls[doc[e]], c1 = cls[doc[e - 1]];
+        if (c0 != c1 && !(c0 == 0 && doc[e - 1] == 0x20 && (e == 1 || cls[doc[e - 2]] != 2))) break;
+        ++e;
+      }
+      insert(doc + i, e - i, hash_of(doc + i, e - i));
+      i = e;
+      if (2 * first.size() > table.size()) {
+        // grow: twice the slots, every word placed again
+        std::vector<int32_t> bigger(2 * table.size(), -1);
+        mask = bigger.size() - 1;
+        for (size_t w = 0; w < first.size(); ++w) {
+          uint64_t s2 = hashes[w] & mask;
+          while (bigger[s2] >= 0) s2 = (s2 + 1) & mask;
+          bigger[s2] = (int32_t)w;
+        }
+        table.swap(bigger);
+      }
+    }
+  }
+  word_off.resize(first.size());
+  int64_t total = 0;
+  for (size_t w = 0; w < first.size(); ++w) {
+    word_off[w] = total;
+    total += word_len[w];
+  }
+  sym.resize((size_t)total);
+  pos_word.resize((size_t)total);
+  for (size_t w = 0; w < first.size(); ++w) {
+    for (int32_t k = 0; k < word_len[w]; ++k) {
+      sym[(size_t)(word_off[w] + k)] = first[w][k];
+      pos_word[(size_t)(word_off[w] + k)] = (int32_t)w;
+    }
+  }
 }
 
 // Device copies for training, made before any kernel runs (blocking copies:
@@ -912,6 +996,58 @@ T *dev_zeros(size_t n, std::vector<void *> &owned) {
   return (T *)p;
 }
 
+// The merges, kTrainGraph at a time: the three kernels of a merge take no
+// argument that changes from merge to merge (the merge index is in device
+// memory), so kTrainGraph merges are captured once as a HIP graph and the
+// graph is launched until n merges are made or training stops (a step past
+// either does nothing); the stop flag is read back every kTrainCheck
+// launches.
+constexpr int kTrainGraph = 64;
+constexpr int kTrainCheck = 16;
+
+int run_train_steps(const TrainArgs &a, int64_t n, hipStream_t stream) {
+  const int64_t launches = (n + kTrainGraph - 1) / kTrainGraph;
+  hipStream_t cs = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int rc = BPE_OK;
+  // the capture runs on a stream of its own, ordered after the caller's work
+  if (hipStreamCreate(&cs) != hipSuccess) return BPE_EHIP;
+  hipEvent_t ready = nullptr;
+  if (hipEventCreateWithFlags(&ready, hipEventDisableTiming) != hipSuccess ||
+      hipEventRecord(ready, stream) != hipSuccess || hipStreamWaitEvent(cs, ready, 0) != hipSuccess)
+    rc = BPE_EHIP;
+  if (rc == BPE_OK && hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess) {
+    bool ok = true;
+    for (int k = 0; k < kTrainGraph && ok; ++k) ok = launch_train_step(a, cs) == hipSuccess;
+    if (hipStreamEndCapture(cs, &graph) != hipSuccess || !ok) rc = BPE_EHIP;
+  } else {
+    rc = BPE_EHIP;
+  }
+  if (rc == BPE_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
+    rc = BPE_EHIP;
+  for (int64_t l = 0; rc == BPE_OK && l < launches; ++l) {
+    if (hipGraphLaunch(exec, cs) != hipSuccess) {
+      rc = BPE_EHIP;
+      break;
+    }
+    if ((l + 1) % kTrainCheck == 0 && l + 1 < launches) {
+      int32_t stop = 0;
+      if (hipMemcpyAsync(&stop, a.stop, sizeof(stop), hipMemcpyDeviceToHost, cs) != hipSuccess ||
+          hipStreamSynchronize(cs) != hipSuccess)
+        rc = BPE_EHIP;
+      else if (stop)
+        break;
+    }
+  }
+  if (hipStreamSynchronize(cs) != hipSuccess && rc == BPE_OK) rc = BPE_EHIP;
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (ready) (void)hipEventDestroy(ready);
+  (void)hipStreamDestroy(cs);
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -923,60 +1059,106 @@ int bpe_train(const uint8_t *bytes, int64_t n_bytes, const int64_t *doc_off, int
       n_merges > BPE_MAX_MERGES || (n_merges > 0 && !merges_out) || !n_made)
     return BPE_EINVAL;
   if (doc_off[0] != 0 || doc_off[n_docs] != n_bytes) return BPE_EINVAL;
+  if ((uint64_t)n_bytes >= ((uint64_t)1 << 32)) return BPE_EINVAL;  // pair counts are 32-bit
   for (int64_t d = 0; d < n_docs; ++d)
     if (doc_off[d + 1] < doc_off[d]) return BPE_EINVAL;
   *n_made = 0;
   // the distinct pre-tokens and their frequencies
-  std::unordered_map<std::string, int64_t> freq;
-  for (int64_t d = 0; d < n_docs; ++d) {
-    const uint8_t *doc = bytes + doc_off[d];
-    const int64_t n = doc_off[d + 1] - doc_off[d];
-    for (int64_t i = 0; i < n;) {
-      int64_t e = i + 1;
-      while (e < n && !host_start(doc, e)) ++e;
-      ++freq[std::string((const char *)doc + i, (size_t)(e - i))];
-      i = e;
-    }
-  }
   std::vector<int32_t> sym, pos_word, word_len;
   std::vector<int64_t> word_off, word_freq;
-  for (const auto &kv : freq) {
-    const int32_t w = (int32_t)word_off.size();
-    word_off.push_back((int64_t)sym.size());
-    word_len.push_back((int32_t)kv.first.size());
-    word_freq.push_back(kv.second);
-    for (unsigned char ch : kv.first) {
-      sym.push_back(ch);
-      pos_word.push_back(w);
-    }
-  }
+  collect_pretokens(bytes, doc_off, n_docs, sym, pos_word, word_off, word_len, word_freq);
   if (n_merges == 0 || sym.empty()) return BPE_OK;
+  // the pre-tokens' symbols and the occurrence lists are indexed by 32 bits
+  if (sym.size() >= ((size_t)1 << 30)) return BPE_EINVAL;
   hipStream_t stream = (hipStream_t)hip_stream;
   std::vector<void *> owned;
   int rc = BPE_OK;
   TrainArgs a;
   a.n_words = (int64_t)word_off.size();
   a.n_pos = (int64_t)sym.size();
-  uint64_t slots = 2;
-  while (slots < 2 * (uint64_t)a.n_pos) slots *= 2;
+  // keys are never removed: at most the initial pairs plus two per merged
+  // occurrence (at most one occurrence per position), so 4 n_pos slots keep
+  // the table at most three quarters full
+  uint64_t slots = kTrainBlock;
+  while (slots < 4 * (uint64_t)a.n_pos) slots *= 2;
   a.mask = slots - 1;
+  a.nblocks = (int64_t)std::min<uint64_t>(slots / kTrainBlock, kTrainLoopBlocks);
+  a.bsize = slots / (uint64_t)a.nblocks;
+  a.n_target = n_merges;
+  a.n_grid = std::min<int64_t>(n_merges, kTrainGridMerges);
   a.sym = dev_copy(sym, owned);
-  a.word_off = dev_copy(word_off, owned);
-  a.word_len = dev_copy(word_len, owned);
-  a.word_freq = dev_copy(word_freq, owned);
+  {
+    std::vector<uint4> wrec(word_off.size());
+    for (size_t w = 0; w < word_off.size(); ++w)
+      wrec[w] = uint4{(uint32_t)word_off[w], (uint32_t)word_len[w], (uint32_t)word_freq[w],
+                      (uint32_t)((uint64_t)word_freq[w] >> 32)};
+    a.wrec = dev_copy(wrec, owned);
+  }
   a.pos_word = dev_copy(pos_word, owned);
   a.keys = dev_zeros<uint64_t>((size_t)slots, owned);
-  a.counts = dev_zeros<uint64_t>((size_t)slots, owned);
-  a.best = dev_zeros<uint64_t>(2, owned);
+  a.counts = dev_zeros<uint32_t>((size_t)slots, owned);
+  a.bmax = dev_zeros<uint32_t>((size_t)a.nblocks, owned);
+  a.bkey = dev_zeros<unsigned long long>((size_t)a.nblocks, owned);
+  a.dirty = dev_zeros<uint32_t>((size_t)a.nblocks, owned);
+  a.dlist = dev_zeros<uint32_t>((size_t)a.nblocks, owned);
+  a.ndirty = dev_zeros<uint32_t>(1, owned);
+  {
+    // occurrence lists of the bytes: each pre-token once per distinct byte;
+    // the pool also holds one entry per pre-token a merge changes (at most
+    // one per position in all)
+    std::vector<int64_t> cnt(256, 0), off(256 + (size_t)n_merges, 0);
+    std::vector<int32_t> len(256 + (size_t)n_merges, 0);
+    std::vector<uint8_t> seen(256, 0);
+    for (size_t w = 0; w < word_off.size(); ++w) {
+      for (int32_t k = 0; k < word_len[w]; ++k) {
+        const int b = sym[(size_t)(word_off[w] + k)];
+        if (!seen[b]) {
+          seen[b] = 1;
+          ++cnt[b];
+        }
+      }
+      for (int32_t k = 0; k < word_len[w]; ++k) seen[sym[(size_t)(word_off[w] + k)]] = 0;
+    }
+    int64_t total = 0;
+    for (int b = 0; b < 256; ++b) {
+      off[b] = total;
+      len[b] = (int32_t)cnt[b];
+      total += cnt[b];
+    }
+    std::vector<int32_t> pool((size_t)(total + a.n_pos));
+    std::vector<int64_t> at(off.begin(), off.begin() + 256);
+    for (size_t w = 0; w < word_off.size(); ++w) {
+      for (int32_t k = 0; k < word_len[w]; ++k) {
+        const int b = sym[(size_t)(word_off[w] + k)];
+        if (!seen[b]) {
+          seen[b] = 1;
+          pool[(size_t)at[b]++] = (int32_t)w;
+        }
+      }
+      for (int32_t k = 0; k < word_len[w]; ++k) seen[sym[(size_t)(word_off[w] + k)]] = 0;
+    }
+    a.pool = dev_copy(pool, owned);
+    std::vector<uint2> lrec(off.size());
+    for (size_t x = 0; x < off.size(); ++x) lrec[x] = uint2{(uint32_t)off[x], (uint32_t)len[x]};
+    a.lrec = dev_copy(lrec, owned);
+    std::vector<unsigned long long> top(1, (unsigned long long)total);
+    a.pool_top = dev_copy(top, owned);
+    a.zcount = dev_zeros<uint32_t>(1, owned);
+  }
+  a.best = dev_zeros<uint64_t>(3, owned);
   a.stop = dev_zeros<int32_t>(1, owned);
   a.merges = dev_zeros<int32_t>((size_t)(2 * n_merges), owned);
   a.out_counts = dev_zeros<int64_t>((size_t)n_merges, owned);
   a.made = dev_zeros<int64_t>(1, owned);
-  if (!a.sym || !a.word_off || !a.word_len || !a.word_freq || !a.pos_word || !a.keys ||
-      !a.counts || !a.best || !a.stop || !a.merges || !a.out_counts || !a.made)
+  if (!a.sym || !a.wrec || !a.pos_word || !a.keys ||
+      !a.counts || !a.bmax || !a.bkey || !a.dirty || !a.dlist || !a.ndirty || !a.best ||
+      !a.pool || !a.lrec || !a.pool_top || !a.zcount ||
+      !a.stop || !a.merges || !a.out_counts || !a.made)
     rc = BPE_ENOMEM;
-  for (int64_t r = 0; rc == BPE_OK && r < n_merges; ++r)
-    if (launch_train_step(a, r, stream) != hipSuccess) rc = BPE_EHIP;
+  if (rc == BPE_OK && launch_train_init(a, stream) != hipSuccess) rc = BPE_EHIP;
+  if (rc == BPE_OK) rc = run_train_steps(a, a.n_grid, stream);
+  if (rc == BPE_OK && n_merges > kTrainGridMerges && launch_train_loop(a, stream) != hipSuccess)
+    rc = BPE_EHIP;
   int64_t made = 0;
   if (rc == BPE_OK &&
       (hipMemcpyAsync(&made, a.made, sizeof(int64_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||

@@ -401,24 +401,52 @@ constexpr int kEncStages = 10;
 extern const char *const kEncStageNames[kEncStages];
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev);
 // Training (bpe_train.hip): the distinct pre-tokens of the corpus with their
-// frequencies, their current symbols, and the pair table of one merge.
+// frequencies, their current symbols, and a pair table whose counts are kept
+// up to date merge by merge.  The table's slots are summarized in blocks of
+// kTrainBlock: each block's largest count and the smallest key with it, kept
+// exact for every block a merge touched before the next pick.
+constexpr int kTrainBlock = 1024;       // slots per block, at least
+constexpr int kTrainLoopBlocks = 8192;  // blocks, at most (the one-workgroup loop keeps them in LDS)
+constexpr int kTrainGridMerges = 256;   // merges run as grid-wide kernels before the loop
 struct TrainArgs {
-  int32_t *sym;              // symbols of pre-token w from word_off[w], word_len[w] of them
-  const int64_t *word_off;
-  int32_t *word_len;
-  const int64_t *word_freq;
+  int32_t *sym;              // the pre-tokens' current symbols
+  uint4 *wrec;               // per pre-token: its first symbol's index in sym, its
+                             // symbol count, its frequency (low, high 32 bits)
   const int32_t *pos_word;   // the pre-token of each original position
   int64_t n_words, n_pos;
   uint64_t *keys;            // pair table: (left << 32 | right) + 1, 0 = empty
-  uint64_t *counts;
-  uint64_t mask;             // slots - 1 (a power of two, at least 2 n_pos)
-  uint64_t *best;            // [2]: the merge's best count, then its smallest key
-  int32_t *stop;             // set once the best count is below 2
+  uint32_t *counts;          // its counts (a corpus has fewer than 2^32 bytes)
+  uint64_t mask;             // slots - 1 (a power of two, at least 4 n_pos: keys are never removed)
+  uint32_t *bmax;            // [nblocks] each block's largest count
+  unsigned long long *bkey;  // [nblocks] the smallest key with that count (~0: none)
+  uint32_t *dirty;           // [nblocks] 1 while the block is listed in dlist
+  uint32_t *dlist;           // [nblocks] blocks touched since their summary
+  uint32_t *ndirty;          // [1] entries of dlist
+  int64_t nblocks;           // a power of two, at most kTrainLoopBlocks
+  uint64_t bsize;            // slots per block: (mask + 1) / nblocks
+  // occurrence lists: symbol x's list, pool[lrec[x].x .. + lrec[x].y),
+  // holds every pre-token that contains x (and perhaps some that no longer
+  // do): for a byte, the pre-tokens with that byte; for 256 + r, the
+  // pre-tokens merge r changed, appended at pool_top during the merge
+  int32_t *pool;
+  uint2 *lrec;               // per symbol: its list's first pool entry, its length
+  unsigned long long *pool_top;  // [1] the pool's first free entry
+  uint32_t *zcount;          // [1] pre-tokens the last merge changed
+  uint64_t *best;            // [3]: the picked count, its key, and the merge's index
+  int64_t n_target;          // merges asked for
+  int64_t n_grid;            // of which made by the grid-wide kernels (the rest by k_tloop)
+  int32_t *stop;             // set once the best count is below 2 or n_target merges are made
   int32_t *merges;           // [n_merges][2] out
   int64_t *out_counts;       // [n_merges] out
   int64_t *made;             // merges made
 };
-hipError_t launch_train_step(const TrainArgs &a, int64_t r, hipStream_t stream);
+// The initial pair counts and every block's summary.
+hipError_t launch_train_init(const TrainArgs &a, hipStream_t stream);
+// One merge as grid-wide kernels: pick the best pair, apply it, summarize
+// the touched blocks.
+hipError_t launch_train_step(const TrainArgs &a, hipStream_t stream);
+// The remaining merges in one workgroup.
+hipError_t launch_train_loop(const TrainArgs &a, hipStream_t stream);
 
 // The reserved IDs of an empty input, after launch_empty (bpe_encode.hip).
 hipError_t launch_special(const SpecialArgs &a, hipStream_t stream);

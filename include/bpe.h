@@ -153,13 +153,17 @@ int bpe_parse_vocab_json(const char *json, int64_t json_len, const int32_t *merg
  * right); replacement is encoding's left-to-right pass without overlap.
  *  bytes, doc_off  host memory: the corpus as for bpe_encode_batch (offsets
  *                  that are not 0 = d[0] <= ... <= d[n_docs] = n_bytes give
- *                  BPE_EINVAL).
+ *                  BPE_EINVAL); n_bytes below 2^32, and the distinct
+ *                  pre-tokens' bytes below 2^30, else BPE_EINVAL.
  *  merges_out      host int32 [n_merges][2]: merge r, rank order.
  *  counts_out      host int64 [n_merges] or NULL: each merge's pair count.
  *  n_made          receives the number of merges made (<= n_merges).
- * The pre-tokens are collected on the host, then each merge runs as kernels
- * on hip_stream; the call allocates its own device memory and waits for the
- * result.  Returns BPE_OK, BPE_EINVAL, BPE_ENOMEM or BPE_EHIP.
+ * The distinct pre-tokens are collected on the host; the device counts the
+ * pairs once, then keeps the counts up to date merge by merge (a merge
+ * changes only the pre-tokens that hold its pair).  The call allocates its
+ * own device memory, runs on hip_stream (and a stream of its own, ordered
+ * after it) and waits for the result.  Returns BPE_OK, BPE_EINVAL,
+ * BPE_ENOMEM or BPE_EHIP.
  */
 int bpe_train(const uint8_t *bytes, int64_t n_bytes, const int64_t *doc_off, int64_t n_docs,
               int64_t n_merges, int32_t *merges_out, int64_t *counts_out, int64_t *n_made,

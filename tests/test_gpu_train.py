@@ -71,3 +71,18 @@ def test_train_throughput_corpus():
     dt = time.perf_counter() - t0
     print(f"bpe_train: {tc.data.size} bytes, {m.shape[0]} merges in {dt:.2f} s")
     assert np.array_equal(m, np.load(os.path.join(ROOT, "assets", "merges_throughput.npy")))
+
+
+@pytest.mark.parametrize("name", ["multilingual", "serving", "adversarial"])
+def test_train_reproduces_stored_tables(name):
+    # the larger workloads' training corpora (32-64 MiB, 50,000-128,000
+    # merges): the tables the oracle's trainer stored in assets/
+    cfg = WORKLOADS[name]
+    tc = training_corpus(cfg, make_lexicon(cfg))
+    t0 = time.perf_counter()
+    m, c = train(tc.data, tc.doc_off, cfg.n_merges)
+    dt = time.perf_counter() - t0
+    print(f"bpe_train {name}: {tc.data.size} bytes, {m.shape[0]} merges in {dt:.2f} s")
+    assert np.array_equal(m, np.load(os.path.join(ROOT, "assets", f"merges_{name}.npy")))
+    # the chosen counts never increase
+    assert np.all(np.diff(c) <= 0) and c[-1] >= 2
