@@ -18,7 +18,7 @@
 // to token); "Hugging Face Tokenizers v1" (dothoosh.com), section "Road to
 // 1.0.0" (GPU batch decode).
 #include "../../include/bpe.h"
-#include "bpe_device.cuh"
+#include "bpe_device.h"
 
 namespace bpe {
 namespace {

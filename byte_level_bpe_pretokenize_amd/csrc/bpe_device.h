@@ -1,4 +1,4 @@
-// bpe_device.cuh -- device helpers shared by the encode and decode kernels:
+// bpe_device.h -- device helpers shared by the encode and decode kernels:
 // byte classes, rank probes, wave / workgroup reductions and scans, a wave-wide
 // binary search and the per-chunk offset scan.
 #pragma once

@@ -35,7 +35,7 @@
 // batches) and "Road to 1.0.0" (GPU batch encode, output positions in
 // parallel).
 #include "../../include/bpe.h"
-#include "bpe_device.cuh"
+#include "bpe_device.h"
 
 namespace bpe {
 namespace {
@@ -1417,16 +1417,21 @@ __device__ int64_t wave_global_end(const EncodeArgs &a, int64_t gs, int64_t from
   // from > gs + 1 always (the pre-token fills the window), so q - 1 > gs is
   // inside the document and is not a document start
   for (int64_t q0 = max(from, gs + 2); q0 < limit; q0 += 64 * 16) {
+    // the lane's 16 positions and the two bytes before them, loaded together
+    const int64_t p0 = q0 + 16 * (int64_t)lane;
+    uint32_t v[18];
+#pragma unroll
+    for (int j = 0; j < 18; ++j) {
+      const int64_t q = p0 - 2 + j;
+      v[j] = q < limit ? (uint32_t)b[q] : 0u;
+    }
     int cand = kNoStart;
-    for (int j = 0; j < 16; ++j) {
-      const int64_t q = q0 + 16 * (int64_t)lane + j;
-      if (q >= limit) break;
-      const uint32_t c0 = byte_class(b[q]), b1 = b[q - 1], c1 = byte_class(b1);
-      const bool attach = c0 == kL && b1 == 0x20u && byte_class(b[q - 2]) != kW;
-      if (c0 != c1 && !attach) {
-        cand = 16 * lane + j;
-        break;
-      }
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      const int64_t q = p0 + j;
+      const uint32_t c0 = byte_class(v[j + 2]), b1 = v[j + 1], c1 = byte_class(b1);
+      const bool attach = c0 == kL && b1 == 0x20u && byte_class(v[j]) != kW;
+      if (q < limit && c0 != c1 && !attach) cand = 16 * lane + j;
     }
     cand = wave_min(cand);
     if (cand != kNoStart) return q0 + cand;
@@ -1479,7 +1484,15 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
       if (i < n) {
         const int32_t r = L.r[i];
         int32_t w = gmin;
-        if (D > 0) {
+        if (D > 0 && D <= 8) {
+          // the 17 reads are independent: issued together
+          w = r;
+#pragma unroll
+          for (int dj = -8; dj <= 8; ++dj) {
+            const int j = i + dj;
+            if (dj != 0 && dj >= -D && dj <= D && j >= 0 && j < n) w = min(w, L.r[j]);
+          }
+        } else if (D > 8) {
           w = r;
           const int j1 = min(n - 1, i + D);
           for (int j = max(0, i - D); j <= j1; ++j) w = min(w, L.r[j]);
@@ -1628,24 +1641,41 @@ __device__ void rle_ranks(const RleView &V, int R, const RankTable &tab) {
 
 // The runs of bytes[0, n) (global), if there are at most kRleMax of them and
 // at least 8 bytes per run on average; returns their number, or -1.
+// The bytes come 16 per lane per step (1 KiB per wave, all loads of a step in
+// flight together); a run starts where a byte differs from the one before.
 __device__ int rle_build(const RleView &V, const uint8_t *bytes, int64_t n) {
   const int lane = lane_id();
-  const uint64_t below = (1ull << lane) - 1;
   int R = 0;
   int32_t prev = -1;
-  for (int64_t i0 = 0; i0 < n; i0 += 64) {
-    const int64_t i = i0 + lane;
-    const int32_t b = i < n ? (int32_t)bytes[i] : -2;
-    const int32_t left = wave_shift_up1(b, prev);
-    const bool head = i < n && b != left;
-    const uint64_t bm = __ballot(head);
-    const int k = R + __popcll(bm & below);
-    if (head && k < kRleMax) {
-      V.sym[k] = b;
-      V.cnt[k] = (int32_t)i;  // start for now
+  for (int64_t i0 = 0; i0 < n; i0 += 64 * 16) {
+    const int64_t p0 = i0 + 16 * (int64_t)lane;
+    int32_t b[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) b[j] = p0 + j < n ? (int32_t)bytes[p0 + j] : -2;
+    const int32_t left = wave_shift_up1(b[15], prev);  // the byte before this lane's first
+    uint32_t hm = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (p0 + j < n && b[j] != (j ? b[j - 1] : left)) hm |= 1u << j;
+    // the 16 bytes packed (a head's byte is taken by a shift, not by a
+    // register index)
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)(b[4 * q] & 0xFF) | ((uint32_t)(b[4 * q + 1] & 0xFF) << 8) |
+             ((uint32_t)(b[4 * q + 2] & 0xFF) << 16) | ((uint32_t)(b[4 * q + 3] & 0xFF) << 24);
+    int all;
+    int k = wave_excl(__popc(hm), R, &all);
+    for (uint32_t m = hm; m; m &= m - 1, ++k) {
+      const int j = __ffs(m) - 1;
+      const uint32_t wq = j < 8 ? (j < 4 ? w[0] : w[1]) : (j < 12 ? w[2] : w[3]);
+      if (k < kRleMax) {
+        V.sym[k] = (int32_t)((wq >> (8 * (j & 3))) & 0xFFu);
+        V.cnt[k] = (int32_t)(p0 + j);  // start for now
+      }
     }
-    R += __popcll(bm);
-    prev = lane_value(b, 63);
+    R += all;
+    prev = lane_value(b[15], 63);
     if (R > kRleMax || (int64_t)R * 8 > n) return -1;  // R only grows
   }
   for (int k = lane; k < R; k += 64)

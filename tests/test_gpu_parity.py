@@ -262,6 +262,32 @@ def test_determinism(dev):
     assert s1 == 0 and s2 == 0 and np.array_equal(a1, a2) and np.array_equal(o1, o2)
 
 
+def test_determinism_across_launch_geometries(dev):
+    # the same documents encoded alone, behind a prefix document that moves
+    # every chunk boundary (another grid, other chunks, other entry-table
+    # owners), and from an unaligned address (the byte-wise window loads):
+    # each document's IDs are the same, and the oracle's
+    model, table = model_pair("throughput")
+    cfg = WORKLOADS["throughput"]
+    lex = make_lexicon(cfg)
+    b = small_batch(cfg, 48, 20000, seed=13, lex=lex)
+    want, want_off = table.encode_batch(b.data, b.doc_off)
+    runs = []
+    for prefix_len, data_offset in [(0, 0), (1234, 0), (4095, 0), (0, 3)]:
+        pre = small_batch(cfg, 1, prefix_len, seed=99, lex=lex).data if prefix_len else \
+            np.zeros(0, np.uint8)
+        data = np.concatenate([pre, b.data])
+        off = np.concatenate([[0], b.doc_off + prefix_len]) if prefix_len else b.doc_off
+        ids, ioff, st = gpu_encode(model, data, off, data_offset=data_offset)
+        assert st == 0
+        k = 1 if prefix_len else 0
+        got = ids[ioff[k]:ioff[-1]]
+        assert np.array_equal(ioff[k:] - ioff[k], want_off)
+        assert np.array_equal(got, want), (prefix_len, data_offset)
+        runs.append(got)
+    assert all(np.array_equal(r, runs[0]) for r in runs)
+
+
 def test_long_pretokens_windowed_rounds(dev):
     # pre-tokens longer than 32 bytes go to the wave merge (multi-rank rounds
     # for tables in rank order): random digit runs up to 2048, single-letter
