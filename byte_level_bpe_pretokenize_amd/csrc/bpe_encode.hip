@@ -73,6 +73,7 @@ constexpr int kPvDup = 1 << 21;
 // Buckets kDedupFrom..2 go through the call's entry table (k_dedup); the
 // shorter entries below are merged wherever they occur.
 constexpr int kDedupFrom = 1;
+static_assert(kBucketBase[kDedupFrom] == kDrefBase, "dref covers the deduplicated buckets");
 __device__ __forceinline__ bool deduped(int b) { return b >= kDedupFrom && b < 3; }
 
 __device__ __forceinline__ uint32_t miss_entry(int st, int len, bool over) {
@@ -1347,7 +1348,7 @@ __global__ void __launch_bounds__(256) k_dedup(EncodeArgs a, int64_t c_lo, int64
         }
       }
     }
-    if (v) a.dref[c * kMissMax + idx] = owner ? kDrefOwner : slot;
+    if (v) a.dref[c * kDrefCap + idx - kDrefBase] = owner ? kDrefOwner : slot;
     const bool ov = v && owner;
     const uint64_t o0 = __ballot(ov && b == 0), o1 = __ballot(ov && b == 1),
                    o2 = __ballot(ov && b == 2);
@@ -1392,7 +1393,7 @@ __global__ void __launch_bounds__(256) k_dupfill(EncodeArgs a) {
     int b;
     const int idx = lane_list_index(g, n0, n01, b);
     if (g < n) {
-      const uint32_t r = a.dref[c * kMissMax + idx];
+      const uint32_t r = a.dref[c * kDrefCap + idx - kDrefBase];
       const uint32_t e = a.miss[c * kMissMax + idx];
       if (r != kDrefOwner) {
         const u32x2 y = dty[2 * (size_t)r + 1];  // owner's g, token count

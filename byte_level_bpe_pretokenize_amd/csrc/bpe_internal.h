@@ -169,6 +169,10 @@ constexpr int kBucketCap[kBuckets] = {kMissBytes / 2, kMissBytes / 9 + 1, kMissB
 constexpr int kBucketBase[kBuckets] = {0, kBucketCap[0], kBucketCap[0] + kBucketCap[1],
                                        kBucketCap[0] + kBucketCap[1] + kBucketCap[2]};
 constexpr int kMissMax = kBucketBase[3] + kBucketCap[3];
+// The call's entry table covers buckets 1 and 2: their entries' references
+// (dref), per chunk.
+constexpr int kDrefBase = kBucketBase[1];
+constexpr int kDrefCap = kBucketCap[1] + kBucketCap[2];
 // meta: 16 int32 per chunk
 constexpr int kMetaInts = 16;
 constexpr int kMetaPretokens = 0;  // pre-tokens that start in the chunk
@@ -206,8 +210,9 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //                                k the pre-token's index), start | len << 13 |
 //                                overhang << 26 (wave-merged)
 //   mt        [G][kMaxLong] i32  token count of each wave-merged entry
-//   dref      [G][kMissMax] u32  lane-merged entry: kDrefOwner if it is merged
-//                                itself, else the entry-table slot of its bytes
+//   dref      [G][kDrefCap] u32  entry of bucket 1 or 2 (list index minus
+//                                kDrefBase): kDrefOwner if it is merged itself,
+//                                else the entry-table slot of its bytes
 //   olist     [G][kMissMax] u64  the entries merged themselves, per bucket
 //                                region: entry | slot << 32 (kNoSlot: none)
 //   dstat     u32       entry-table claims of the first (seeding) launch
@@ -220,7 +225,8 @@ constexpr int kMetaOwners = 8;     // 3 entries: of which first of their bytes i
 //                                  4-byte aligned offset o
 //   res       [G][kMissSpan] i32  its tokens, from o on
 //   gsym      [N] i32   tokens of a wave-merged entry that starts at byte g, from gsym[g] on
-//   grank     [N] i32   pair ranks of the wave merge, position-indexed
+//   grank     [N] i32   pair ranks of the wave merge, position-indexed (in olist's
+//                       memory: olist is dead by then)
 struct EncLayout {
   size_t meta, tot, off, bsum, boff, doc_rng, dfirst, doc_pt, pv, cntk, miss, mt, dref, olist, dstat, dt, mbytes, res, gsym,
       grank, total;
@@ -262,14 +268,17 @@ inline EncLayout enc_layout(int64_t n_bytes, int64_t n_docs) {
   L.cntk = take((size_t)kChunk * G);
   L.miss = take(4 * (size_t)kMissMax * G);
   L.mt = take(4 * (size_t)kMaxLong * G);
-  L.dref = take(4 * (size_t)kMissMax * G);
+  L.dref = take(4 * (size_t)kDrefCap * G);
   L.olist = take(8 * (size_t)kMissMax * G);
   L.dstat = take(8);
   L.dt = take(16 * dedup_slots(G));
   L.mbytes = take((size_t)kMissSpan * G + 64);  // word loads read a little past the end
   L.res = take(4 * (size_t)kMissSpan * G + 64);
   L.gsym = take(4 * (size_t)n_bytes);
-  L.grank = take(4 * (size_t)n_bytes);
+  // grank is only used by k_merge_long, after the last reader of olist
+  // (k_merge_wide): it takes olist's memory
+  static_assert(8 * kMissMax >= 4 * kChunk, "olist holds grank");
+  L.grank = L.olist;
   L.total = o;
   return L;
 }

@@ -181,7 +181,9 @@ int64_t bpe_vocab_size(const bpe_model *model);
 int64_t bpe_max_token_bytes(const bpe_model *model);
 
 /* Workspace bytes bpe_encode_batch needs for this input size (0 for
- * n_bytes <= 0). */
+ * n_bytes <= 0): about 28.7 bytes per input byte plus 4 per document, since
+ * every intermediate region is sized for the worst case of each 4 KiB chunk
+ * (for example 7.5 GiB for a 256 MiB batch). */
 size_t bpe_encode_workspace_bytes(const bpe_model *model, int64_t n_bytes, int64_t n_docs);
 
 /*

@@ -94,6 +94,10 @@ def test_workspace_sizes():
     n = 1 << 20
     ws = L.bpe_encode_workspace_bytes(None, n, 16)
     assert ws >= 8 * n                       # position-indexed scratch for long pre-tokens
+    # about 28.7 bytes per input byte (the regions are sized for each chunk's
+    # worst case)
+    for big in (1 << 20, 1 << 28):
+        assert L.bpe_encode_workspace_bytes(None, big, 4096) <= 29 * big
     assert L.bpe_encode_workspace_bytes(None, n + 1, 16) > ws
     assert L.bpe_decode_workspace_bytes(None, 5000, 3) > 0
     # the special encode writes its reserved IDs in the encode's own kernels
