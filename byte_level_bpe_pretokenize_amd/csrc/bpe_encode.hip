@@ -405,7 +405,7 @@ __device__ __forceinline__ uint32_t start_bits16(const uint32_t w[5], uint32_t d
 
 // ---- k_find -------------------------------------------------------------------
 
-constexpr int kFindList = 1024;  // misses listed for the dense miss pass (more: in place)
+constexpr int kFindList = 1024;  // byte copies listed for full waves (more: by their own thread)
 
 struct FindShared {
   alignas(16) uint8_t B[16 + WIN + 32];  // B[16 + p] = byte at window position p
@@ -417,9 +417,50 @@ struct FindShared {
   Red<WG> r;
   int64_t o_lo, o_hi;
   int e_last;
-  int cnt[kBuckets];                     // merge-loop list entries per bucket
-  int nbytes;                            // span of the lane-merged entries' dense region
+  uint64_t tally;                        // the entries placed so far (tally_add, hi:lo)
 };
+
+// A merge-loop entry's place, as two 32-bit tallies whose fields never carry
+// into each other (the bounds hold for any chunk: the owned pre-tokens start
+// at distinct positions below kChunk and are disjoint):
+//   lo: entries of 2-8 bytes (bits 0-11, at most kChunk / 2), of 9-16 bytes
+//       (bits 12-23, at most kChunk / 9 + 1), of 17-kLaneMax bytes (bits
+//       24-31, at most kChunk / 17 + 1 < 256)
+//   hi: longer entries and the one past the window (bits 0-15), dense-region
+//       bytes of the lane-merged ones, each rounded up to 4 (bits 16-31, at
+//       most kMissSpan)
+// One 64-bit LDS add of a wave's tallies (hi:lo) places all its entries:
+// their slots in their buckets' regions and their dense offsets.
+__device__ __forceinline__ void tally_add(uint32_t &lo, uint32_t &hi, int b, int len) {
+  if (b < 3) {
+    lo += 1u << (12 * b);
+    hi += (uint32_t)((len + 3) & ~3) << 16;
+  } else {
+    hi += 1u;
+  }
+}
+__device__ __forceinline__ int tally_count(uint32_t lo, uint32_t hi, int b) {
+  return b == 0 ? (int)(lo & 0xFFFu)
+       : b == 1 ? (int)((lo >> 12) & 0xFFFu)
+       : b == 2 ? (int)(lo >> 24)
+                : (int)(hi & 0xFFFFu);
+}
+static_assert(kChunk / 2 < 4096 && kChunk / 9 + 1 < 4096 && kChunk / 17 + 1 < 256 &&
+              kMissSpan < 65536, "tally fields hold a chunk's counts");
+
+// The len bytes at window position st as words at dst (the last word's bytes
+// past len are the window's next bytes: readers take len bytes).
+__device__ __forceinline__ void copy_words(const FindShared &s, int st, int len, uint32_t *dst) {
+  const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
+  const int q = (16 + st) >> 2;
+  const uint32_t sh = (uint32_t)((16 + st) & 3);
+  uint32_t prev = B32[q];
+  for (int i = 0; 4 * i < len; ++i) {
+    const uint32_t next = B32[q + i + 1];
+    dst[i] = __builtin_amdgcn_alignbyte(next, prev, sh);
+    prev = next;
+  }
+}
 
 __device__ __forceinline__ bool db_bit(const FindShared &s, int p) {
   const int q = p + DB_OFF;
@@ -551,8 +592,6 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     const uint64_t lo = (uint64_t)c * a.dt_per, hi = min(lo + a.dt_per, words);
     for (uint64_t i = lo + tid; i < hi; i += WG) a.dt[i] = 0ull;
   }
-  if (tid < kBuckets) s.cnt[tid] = 0;
-  if (tid == 0) s.nbytes = 0;
   if (tid <= kShortMax) {
     // masks of the first tid bytes of three little-endian words
     u32x4 m;
@@ -683,9 +722,9 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
 
   // 4. each thread resolves every WG-th pre-token: a single byte is its own
   //    token; a pre-token that is a whole word-table entry takes its symbol;
-  //    the others are listed (bit j of `missed`: pre-token tid + j WG) and
-  //    then handled by the whole workgroup in list order, so that the
-  //    miss path runs on full waves
+  //    the others (bit j of `missed`: pre-token tid + j WG) are listed and
+  //    then placed 64 to a wave, so that the merge-loop path runs on full
+  //    waves
   int32_t *pv = a.pv + c * kChunk;
   uint32_t *ml = a.miss + c * kMissMax;
   uint32_t *mb = reinterpret_cast<uint32_t *>(a.mbytes + c * kMissSpan);
@@ -709,27 +748,21 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     if (v >= 0) pv[k] = v;
     else missed |= 1u << j;
   }
-  // each miss takes a slot in its bucket's region and, up to kLaneMax bytes,
-  // its bytes in the dense region (both by LDS atomics: pv names the entry,
-  // so order does not matter)
-  auto miss = [&](int k) {
+  if (tid == 0) s.tally = 0;
+  // an entry's slot and dense offset from the tallies before it (elo, ehi):
+  // its entry, its pv value, and its bytes
+  auto place = [&](int k, uint32_t elo, uint32_t ehi) {
     const bool over = overhang && k == n_pt - 1;
     const int st = s.PS[k];
     const int len = over ? 0 : (int)s.PS[k + 1] - st;
     const int b = bucket_of(len, over);
-    const int idx = atomicAdd(&s.cnt[b], 1);
+    const int idx = tally_count(elo, ehi, b);
     const int base = b == 0 ? kBucketBase[0] : b == 1 ? kBucketBase[1] : b == 2 ? kBucketBase[2] : kBucketBase[3];
     if (b < 3) {
-      // the bytes, as words at a 4-byte aligned offset of the dense region
-      const int o = atomicAdd(&s.nbytes, (len + 3) & ~3);
-      uint32_t *dst = mb + (o >> 2);
-      const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
-      const int q = (16 + st) >> 2;
-      const uint32_t sh = (uint32_t)((16 + st) & 3);
-      for (int i = 0; 4 * i < len; ++i)
-        dst[i] = __builtin_amdgcn_alignbyte(B32[q + i + 1], B32[q + i], sh);
-      ml[base + idx] = lane_entry(o >> 2, len, k);
-      pv[k] = -1 - (o >> 2);
+      const int o4 = (int)(ehi >> 18);
+      copy_words(s, st, len, mb + o4);
+      ml[base + idx] = lane_entry(o4, len, k);
+      pv[k] = -1 - o4;
     } else {
       ml[base + idx] = miss_entry(st, len, over);
       pv[k] = -1 - kPvLong - idx;
@@ -743,67 +776,56 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
       if (o < kFindList) s.ML[o] = (uint16_t)(tid + (__ffs(m) - 1) * WG);
   }
   __syncthreads();
-  // the listed misses, 64 to a wave: slots and dense offsets from wave
-  // prefix sums, one LDS atomic per bucket and wave
+  // the listed entries, 64 to a wave: the wave's tallies by two prefix sums,
+  // placed by one LDS add
   const int n_list = min(n_miss, kFindList);
   for (int i0 = wave * 64; i0 < n_list; i0 += WG) {
     const int i = i0 + lane;
     const bool act = i < n_list;
     const int k = act ? (int)s.ML[i] : 0;
-    const bool over = act && overhang && k == n_pt - 1;
-    const int st = s.PS[k];
-    const int len = act ? (over ? 0 : (int)s.PS[k + 1] - st) : 0;
-    const int b = bucket_of(len, over);
-    const uint64_t below = (1ull << lane) - 1;
-    int idx = 0;
-#pragma unroll
-    for (int bb = 0; bb < kBuckets; ++bb) {
-      const uint64_t m = __ballot(act && b == bb);
-      int first = 0;
-      if (m && lane == __ffsll((unsigned long long)m) - 1) first = atomicAdd(&s.cnt[bb], __popcll(m));
-      first = lane_value(first, m ? __ffsll((unsigned long long)m) - 1 : 0);
-      if (b == bb) idx = first + __popcll(m & below);
+    uint32_t tlo = 0, thi = 0;
+    if (act) {
+      const bool over = overhang && k == n_pt - 1;
+      const int st = s.PS[k];
+      const int len = over ? 0 : (int)s.PS[k + 1] - st;
+      tally_add(tlo, thi, bucket_of(len, over), len);
     }
-    const int sz = act && b < 3 ? (len + 3) & ~3 : 0;
-    const int inc = wave_incl_sum(sz);
-    int obase = 0;
-    if (lane == 63 && inc) obase = atomicAdd(&s.nbytes, inc);
-    const int o = lane_value(obase, 63) + inc - sz;
-    if (!act) continue;
-    const int base = b == 0 ? kBucketBase[0] : b == 1 ? kBucketBase[1] : b == 2 ? kBucketBase[2] : kBucketBase[3];
-    if (b < 3) {
-      uint32_t *dst = mb + (o >> 2);
-      const uint32_t *B32 = reinterpret_cast<const uint32_t *>(s.B);
-      const int q = (16 + st) >> 2;
-      const uint32_t sh = (uint32_t)((16 + st) & 3);
-      for (int w = 0; 4 * w < len; ++w)
-        dst[w] = __builtin_amdgcn_alignbyte(B32[q + w + 1], B32[q + w], sh);
-      ml[base + idx] = lane_entry(o >> 2, len, k);
-      pv[k] = -1 - (o >> 2);
-    } else {
-      ml[base + idx] = miss_entry(st, len, over);
-      pv[k] = -1 - kPvLong - idx;
-    }
+    const uint32_t ilo = (uint32_t)wave_incl_sum((int32_t)tlo);
+    const uint32_t ihi = (uint32_t)wave_incl_sum((int32_t)thi);
+    uint64_t wb = 0;
+    if (lane == 63) wb = atomicAdd(&s.tally, ((uint64_t)ihi << 32) | ilo);
+    const uint32_t blo = (uint32_t)lane_value((int32_t)(uint32_t)wb, 63);
+    const uint32_t bhi = (uint32_t)lane_value((int32_t)(uint32_t)(wb >> 32), 63);
+    if (act) place(k, blo + ilo - tlo, bhi + ihi - thi);
   }
   if (n_miss > kFindList) {  // the rest, each by the thread that found it
     int o = mex;
-    for (uint32_t m = missed; m; m &= m - 1, ++o)
-      if (o >= kFindList) miss(tid + (__ffs(m) - 1) * WG);
+    for (uint32_t m = missed; m; m &= m - 1, ++o) {
+      if (o < kFindList) continue;
+      const int k = tid + (__ffs(m) - 1) * WG;
+      const bool over = overhang && k == n_pt - 1;
+      const int len = over ? 0 : (int)s.PS[k + 1] - (int)s.PS[k];
+      uint32_t tlo = 0, thi = 0;
+      tally_add(tlo, thi, bucket_of(len, over), len);
+      const uint64_t e = atomicAdd(&s.tally, ((uint64_t)thi << 32) | tlo);
+      place(k, (uint32_t)e, (uint32_t)(e >> 32));
+    }
   }
   const bool any_bad = __syncthreads_or(bad);
-  const int nbytes = s.nbytes;
+  const uint32_t nlo = (uint32_t)s.tally, nhi = (uint32_t)(s.tally >> 32);
   if (tid == 0) {
     int32_t *m = a.meta + kMetaInts * c;
     int n_miss = 0;
 #pragma unroll
     for (int b = 0; b < kBuckets; ++b) {
-      m[kMetaBucket + b] = s.cnt[b];
-      n_miss += s.cnt[b];
+      const int nb = tally_count(nlo, nhi, b);
+      m[kMetaBucket + b] = nb;
+      n_miss += nb;
     }
     m[kMetaPretokens] = n_pt;
     m[kMetaMisses] = n_miss;
     m[kMetaStatus] = any_bad ? (int32_t)BPE_STATUS_BAD_DOC_OFFSETS : 0;
-    m[kMetaBytes] = nbytes;
+    m[kMetaBytes] = (int)(nhi >> 16);
     if (c == 0) a.dstat[0] = 0u;
     a.doc_rng[2 * c] = s.o_lo;
     a.doc_rng[2 * c + 1] = s.o_hi;
