@@ -1467,11 +1467,40 @@ __device__ int64_t wave_global_end(const EncodeArgs &a, int64_t gs, int64_t from
 constexpr int kLdsLong = 2048;    // longest bucket-3 pre-token merged in LDS
 constexpr int kProbeGroups = 8;   // groups of 64 positions whose rank probes go together
 
+constexpr int kRPad = 8;          // sentinel ranks on each side of r (window radii up to 8)
+
 struct LongShared {
-  int32_t y[kLdsLong];              // symbols
-  int32_t r[kLdsLong];              // rank of the pair (y[i], y[i + 1]); -1 = to be found
-  uint32_t cand[kLdsLong / 32];     // bit i: the pair is the lowest in its window
+  int32_t y[kLdsLong];                          // symbols
+  int32_t rpad[kRPad + kLdsLong + kRPad];       // r(): rank of the pair (y[i], y[i + 1]);
+                                                //   -1 = to be found
+  uint32_t cand[kLdsLong / 32];                 // bit i: the pair is the lowest in its window
+  __device__ __forceinline__ int32_t *r() { return rpad + kRPad; }
 };
+
+// Bits of the pairs whose rank is the lowest within D positions on each side
+// (D a compile-time radius up to kRPad): the ranks r[-kRPad .. -1] and
+// r[n .. n + kRPad - 1] read as kRankInf, so no window needs a bounds test.
+template <int D>
+__device__ __forceinline__ void lowest_in_window(LongShared &L, const int32_t *r, int n) {
+  static_assert(D >= 1 && D <= kRPad, "radius within the sentinels");
+  const int lane = lane_id();
+  for (int i0 = 0; i0 < n; i0 += MWG) {
+    const int i = i0 + lane;
+    bool c = false;
+    if (i < n) {
+      const int32_t x = r[i];
+      int32_t w = x;
+#pragma unroll
+      for (int dj = 1; dj <= D; ++dj) w = min(w, min(r[i - dj], r[i + dj]));
+      c = x < kRankInf && x == w;
+    }
+    const uint64_t bc = __ballot(c);
+    if (lane == 0) {
+      L.cand[i0 >> 5] = (uint32_t)bc;
+      L.cand[(i0 >> 5) + 1] = (uint32_t)(bc >> 32);
+    }
+  }
+}
 
 // The rounds for one pre-token of n <= kLdsLong symbols (bytes on entry) in
 // LDS, by one wave; returns the final count, the symbols left in y.
@@ -1490,43 +1519,51 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
                          const int32_t *__restrict__ pair_rank) {
   const int lane = lane_id();
   const uint64_t below = (1ull << lane) - 1;
+  int32_t *const R = L.r();
 #pragma unroll 8
   for (int i = lane; i < n; i += MWG)
-    L.r[i] = (i + 1 < n) ? pair_rank[(L.y[i] << 8) | L.y[i + 1]] : kRankInf;
+    R[i] = (i + 1 < n) ? pair_rank[(L.y[i] << 8) | L.y[i + 1]] : kRankInf;
+  if (lane < kRPad) {
+    R[-1 - lane] = kRankInf;
+    R[n + lane] = kRankInf;
+  }
   while (n > 1) {
     int32_t gmin = kRankInf;
     if (D == 0) {
-      for (int i = lane; i < n; i += MWG) gmin = min(gmin, L.r[i]);
+      for (int i = lane; i < n; i += MWG) gmin = min(gmin, R[i]);
       gmin = wave_min(gmin);
       if (gmin == kRankInf) break;
     }
     // 1. the lowest pairs of their windows
-    for (int i0 = 0; i0 < n; i0 += MWG) {
-      const int i = i0 + lane;
-      bool c = false;
-      if (i < n) {
-        const int32_t r = L.r[i];
-        int32_t w = gmin;
-        if (D > 0 && D <= 8) {
-          // the 17 reads are independent: issued together
-          w = r;
-#pragma unroll
-          for (int dj = -8; dj <= 8; ++dj) {
-            const int j = i + dj;
-            if (dj != 0 && dj >= -D && dj <= D && j >= 0 && j < n) w = min(w, L.r[j]);
+    switch (D) {
+      case 1: lowest_in_window<1>(L, R, n); break;
+      case 2: lowest_in_window<2>(L, R, n); break;
+      case 3: lowest_in_window<3>(L, R, n); break;
+      case 4: lowest_in_window<4>(L, R, n); break;
+      case 5: lowest_in_window<5>(L, R, n); break;
+      case 6: lowest_in_window<6>(L, R, n); break;
+      case 7: lowest_in_window<7>(L, R, n); break;
+      case 8: lowest_in_window<8>(L, R, n); break;
+      default:
+        for (int i0 = 0; i0 < n; i0 += MWG) {
+          const int i = i0 + lane;
+          bool c = false;
+          if (i < n) {
+            const int32_t r = R[i];
+            int32_t w = gmin;
+            if (D > 0) {
+              w = r;
+              const int j1 = min(n - 1, i + D);
+              for (int j = max(0, i - D); j <= j1; ++j) w = min(w, R[j]);
+            }
+            c = r < kRankInf && r == w;
           }
-        } else if (D > 8) {
-          w = r;
-          const int j1 = min(n - 1, i + D);
-          for (int j = max(0, i - D); j <= j1; ++j) w = min(w, L.r[j]);
+          const uint64_t bc = __ballot(c);
+          if (lane == 0) {
+            L.cand[i0 >> 5] = (uint32_t)bc;
+            L.cand[(i0 >> 5) + 1] = (uint32_t)(bc >> 32);
+          }
         }
-        c = r < kRankInf && r == w;
-      }
-      const uint64_t bc = __ballot(c);
-      if (lane == 0) {
-        L.cand[i0 >> 5] = (uint32_t)bc;
-        L.cand[(i0 >> 5) + 1] = (uint32_t)(bc >> 32);
-      }
     }
     // 2. merge flags (run starts by a running maximum) and compaction: a
     //    symbol whose left neighbour merged is consumed
@@ -1538,7 +1575,7 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
     for (int i0 = 0; i0 < n; i0 += MWG) {
       const int i = i0 + lane;
       const bool in = i < n;
-      const int32_t r = in ? L.r[i] : kRankInf;
+      const int32_t r = in ? R[i] : kRankInf;
       const int32_t y = in ? L.y[i] : 0;
       const int32_t rl = wave_shift_up1(r, prevr);
       const bool bnd = in && (i == 0 || rl != r);
@@ -1554,7 +1591,7 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
       const int o = out + __popcll(bk & below);
       if (keep) {
         L.y[o] = m ? 256 + r : y;
-        L.r[o] = m ? -1 : r;
+        R[o] = m ? -1 : r;
       }
       any |= bm != 0;
       out += __popcll(bk);
@@ -1564,6 +1601,7 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
     }
     if (!any) break;
     n = out;
+    if (lane < kRPad) R[n + lane] = kRankInf;
     // 3. ranks of the pairs that touch a new symbol, the probes of kProbeGroups
     //    groups of 64 positions issued together
     for (int i0 = 0; i0 < n; i0 += MWG * kProbeGroups) {
@@ -1580,9 +1618,9 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
         xs[g] = 0;
         bk[g] = u64x2{kEmptySlot, kEmptySlot};
         if (i + 1 < n) {
-          const int32_t r = L.r[i];
+          const int32_t r = R[i];
           nv[g] = r;
-          if (r == -1 || L.r[i + 1] == -1) {
+          if (r == -1 || R[i + 1] == -1) {
             need |= 1u << g;
             const uint32_t l = (uint32_t)L.y[i], rt = (uint32_t)L.y[i + 1];
             key[g] = pair_key(l, rt);
@@ -1610,7 +1648,7 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
 #pragma unroll
       for (int g = 0; g < kProbeGroups; ++g) {
         const int i = i0 + MWG * g + lane;
-        if (i < n) L.r[i] = nv[g];
+        if (i < n) R[i] = nv[g];
       }
     }
   }
@@ -1643,7 +1681,7 @@ struct RleView {
 
 __device__ __forceinline__ RleView rle_view(LongShared &L) {
   static_assert(2 * kRleMax + 2 * kRleMax <= kLdsLong, "run arrays fit LongShared");
-  return RleView{L.y, L.y + kRleMax, L.r, L.r + kRleMax, L.y + 2 * kRleMax, L.r + 2 * kRleMax};
+  return RleView{L.y, L.y + kRleMax, L.r(), L.r() + kRleMax, L.y + 2 * kRleMax, L.r() + 2 * kRleMax};
 }
 
 // Wave-wide exclusive prefix of v over the lanes, plus a carry; *all gets
