@@ -1468,12 +1468,14 @@ constexpr int kLdsLong = 2048;    // longest bucket-3 pre-token merged in LDS
 constexpr int kProbeGroups = 8;   // groups of 64 positions whose rank probes go together
 
 constexpr int kRPad = 8;          // sentinel ranks on each side of r (window radii up to 8)
+constexpr int kFreshMax = 128;    // new symbols of a round listed for their probes (more: a scan)
 
 struct LongShared {
   int32_t y[kLdsLong];                          // symbols
   int32_t rpad[kRPad + kLdsLong + kRPad];       // r(): rank of the pair (y[i], y[i + 1]);
                                                 //   -1 = to be found
   uint32_t cand[kLdsLong / 32];                 // bit i: the pair is the lowest in its window
+  uint16_t fresh[kFreshMax];                    // positions of a round's new symbols
   __device__ __forceinline__ int32_t *r() { return rpad + kRPad; }
 };
 
@@ -1566,23 +1568,37 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
         }
     }
     // 2. merge flags (run starts by a running maximum) and compaction: a
-    //    symbol whose left neighbour merged is consumed
+    //    symbol whose left neighbour merged is consumed.  The next group's
+    //    symbols, ranks and candidate bits are read before this group's
+    //    writes (those land at or before this group's positions, never in
+    //    the next group), so each group's reads overlap the one before.
     int run = 0;                // run start in force before this group
+    bool run_c = false;         // its candidate bit
     bool prevm = false;         // the position before this group merged
     int32_t prevr = kRankInf;   // and its rank (its slot may already be rewritten)
     int out = 0;                // symbols kept so far
+    int nnew = 0;               // new symbols so far
     bool any = false;
+    int32_t nr = lane < n ? R[lane] : kRankInf;
+    int32_t ny = lane < n ? L.y[lane] : 0;
+    uint64_t ncm = ((uint64_t)L.cand[1] << 32) | L.cand[0];
     for (int i0 = 0; i0 < n; i0 += MWG) {
       const int i = i0 + lane;
       const bool in = i < n;
-      const int32_t r = in ? R[i] : kRankInf;
-      const int32_t y = in ? L.y[i] : 0;
+      const int32_t r = nr, y = ny;
+      const uint64_t cm = ncm;  // candidate bits of positions i0 .. i0 + 63
+      if (i0 + MWG < n) {
+        const int j = i + MWG;
+        nr = j < n ? R[j] : kRankInf;
+        ny = j < n ? L.y[j] : 0;
+        ncm = ((uint64_t)L.cand[(i0 >> 5) + 3] << 32) | L.cand[(i0 >> 5) + 2];
+      }
       const int32_t rl = wave_shift_up1(r, prevr);
       const bool bnd = in && (i == 0 || rl != r);
       int st = bnd ? i : -1;
       st = max(wave_incl_max(st), run);
-      const bool c = in && ((L.cand[i >> 5] >> (i & 31)) & 1u);
-      const bool cs = (L.cand[st >> 5] >> (st & 31)) & 1u;
+      const bool c = in && ((cm >> lane) & 1u);
+      const bool cs = st >= i0 ? ((cm >> (st - i0)) & 1u) : run_c;
       const bool m = c && cs && ((i - st) & 1) == 0;
       const uint64_t bm = __ballot(m);
       const bool cons = lane == 0 ? prevm : ((bm >> (lane - 1)) & 1u);
@@ -1593,17 +1609,57 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
         L.y[o] = m ? 256 + r : y;
         R[o] = m ? -1 : r;
       }
+      // (a merging position is never consumed: its left neighbour would
+      // belong to the same run at an odd offset)
+      if (m) {
+        const int q = nnew + __popcll(bm & below);
+        if (q < kFreshMax) L.fresh[q] = (uint16_t)o;
+      }
+      nnew += __popcll(bm);
       any |= bm != 0;
       out += __popcll(bk);
       prevm = (bm >> 63) & 1u;
       prevr = lane_value(r, 63);
-      run = lane_value(st, 63);
+      const int nrun = lane_value(st, 63);
+      run_c = nrun >= i0 ? ((cm >> (nrun - i0)) & 1u) : run_c;
+      run = nrun;
     }
     if (!any) break;
     n = out;
     if (lane < kRPad) R[n + lane] = kRankInf;
-    // 3. ranks of the pairs that touch a new symbol, the probes of kProbeGroups
-    //    groups of 64 positions issued together
+    // 3. ranks of the pairs that touch a new symbol.  Listed new symbols: a
+    //    lane probes both pairs of one, (left neighbour, new) unless the left
+    //    neighbour is new too (its own right pair is that pair) and (new,
+    //    right neighbour), the two probes in flight together.
+    if (nnew <= kFreshMax) {
+      for (int k0 = 0; k0 < nnew; k0 += MWG) {
+        const int k = k0 + lane;
+        const bool act = k < nnew;
+        const int o = act ? (int)L.fresh[k] : 0;
+        const bool hl = act && o > 0 && R[o - 1] != -1;
+        const bool hr = act && o + 1 < n;
+        const uint32_t yo = (uint32_t)L.y[o];
+        const uint32_t yl = hl ? (uint32_t)L.y[o - 1] : 0u, yr = hr ? (uint32_t)L.y[o + 1] : 0u;
+        const uint64_t kl = pair_key(yl, yo), kr = pair_key(yo, yr);
+        const uint32_t xl = pair_mix(yl, yo, tab.seed), xr = pair_mix(yo, yr, tab.seed);
+        u64x2 bl = u64x2{kEmptySlot, kEmptySlot}, br = bl;
+        if (hl) bl = tab.b[pair_bucket0(xl, tab.mask)];
+        if (hr) br = tab.b[pair_bucket0(xr, tab.mask)];
+        int32_t rl = hl ? bucket_rank(bl, kl) : kRankInf;
+        int32_t rr = hr ? bucket_rank(br, kr) : kRankInf;
+        const bool l2 = hl && rl == kRankInf && bucket_flag(bl);
+        const bool r2 = hr && rr == kRankInf && bucket_flag(br);
+        if (l2) bl = tab.b[pair_bucket1(xl, tab.mask)];
+        if (r2) br = tab.b[pair_bucket1(xr, tab.mask)];
+        if (l2) rl = bucket_rank(bl, kl);
+        if (r2) rr = bucket_rank(br, kr);
+        if (hl) R[o - 1] = rl;
+        if (act) R[o] = rr;
+      }
+      continue;
+    }
+    //    More new symbols: every position scanned, the probes of kProbeGroups
+    //    groups of 64 positions issued together.
     for (int i0 = 0; i0 < n; i0 += MWG * kProbeGroups) {
       int32_t nv[kProbeGroups];
       uint32_t xs[kProbeGroups];
