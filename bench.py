@@ -25,11 +25,13 @@ them) gives each kernel's average duration.  Those events cost time of their
 own, so they are recorded in a second pass of the same number of steps right
 after the timed one; `ms_per_step` comes from the pass without them.
 Algorithmic bytes are the call's: the input read once, the IDs and the
-per-document offsets written once (N + 4T + 16(D + 1)).  Measured HBM
-traffic comes from profiles/traffic_<workload>.json (rocprofv3 FETCH_SIZE and
-WRITE_SIZE per call, scaled by a plain copy's counts), as do the per-kernel
-L2 hit rates (TCC_HIT / (TCC_HIT + TCC_MISS)); both are reported only while
-the kernel sources still hash to the value recorded there.
+per-document offsets written once (N + 4T + 16(D + 1)).  Measured memory
+traffic comes from profiles/traffic_<workload>.json: the L2's read requests
+to memory (rocprofv3 TCC_EA0_RDREQ, 128 bytes each on this chip, as a copy, a
+reduction and an elementwise kernel of known size show) and its write
+requests (WRITE_SIZE), summed over the encode kernels of one call, with the
+per-kernel L2 hit rates (TCC_HIT / (TCC_HIT + TCC_MISS)); both are reported
+only while the kernel sources still hash to the value recorded there.
 
 Beside the timed encode the line carries the decode of the same IDs
 (`decode`, a round trip) and the encode with a BOS and an EOS ID around each
@@ -95,7 +97,8 @@ def parse():
     ap.add_argument("--no-train", action="store_true",
                     help="skip timing bpe_train on the workload's training corpus")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain device copy of the input (for counter scaling)")
+                    help="also run kernels of known traffic on the input (copy, reduction, "
+                         "elementwise, fill) for the counter runs")
     return ap.parse_args()
 
 
@@ -312,11 +315,16 @@ def main():
     del copy
 
     if args.copy_calibration:
-        # a plain copy kernel of known size: reads and writes n_bytes once
+        # kernels of known traffic for the counter runs: a device copy (reads
+        # and writes N bytes), a reduction with 16-byte loads (reads N), an
+        # elementwise kernel (reads and writes N) and a fill (writes N)
         copy = torch.empty_like(data)
         copy.copy_(data)
+        _ = data[:N & ~7].view(torch.int64).sum()
+        _ = data[:N & ~3].view(torch.float32) * 2.0
+        copy.zero_()
         torch.cuda.synchronize()
-        del copy
+        del copy, _
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
