@@ -25,7 +25,7 @@ struct bpe_model {
   uint32_t table_mask = 0, table_seed = 0;
   int32_t *d_id_map = nullptr;
   int32_t *d_pair_rank = nullptr;   // [65536] ranks of byte pairs
-  uint16_t *d_pair_ascii = nullptr; // [128 * 128] 1 + rank of ASCII byte pairs (EncodeArgs::pair_ascii)
+  uint32_t *d_pair_filter = nullptr;  // [kPairFilterWords] bit set of the merges' pairs
   int n_cu = 1;                     // compute units of the device
   uint4 *d_words = nullptr;         // short word table (one uint4 per slot), or nullptr
   uint32_t word_mask = 0;
@@ -91,7 +91,7 @@ void free_model(bpe_model *m) {
   if (m->d_table) (void)hipFree(m->d_table);
   if (m->d_id_map) (void)hipFree(m->d_id_map);
   if (m->d_pair_rank) (void)hipFree(m->d_pair_rank);
-  if (m->d_pair_ascii) (void)hipFree(m->d_pair_ascii);
+  if (m->d_pair_filter) (void)hipFree(m->d_pair_filter);
   if (m->d_words) (void)hipFree(m->d_words);
   if (m->d_lwords) (void)hipFree(m->d_lwords);
   if (m->d_exp_off) (void)hipFree(m->d_exp_off);
@@ -250,7 +250,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.table_seed = model->table_seed;
   a.id_map = id_map;
   a.pair_rank = model->d_pair_rank;
-  a.pair_ascii = model->d_pair_ascii;
+  a.pair_filter = model->d_pair_filter;
   a.n_cu = model->n_cu;
   a.words = words ? model->d_words : nullptr;
   a.word_mask = model->word_mask;
@@ -618,13 +618,13 @@ int bpe_load_merges(const int32_t *merges, int64_t n_merges, const int32_t *id_m
         pr[(size_t)(merges[2 * r] * 256 + merges[2 * r + 1])] = (int32_t)r;
     rc = upload(&m->d_pair_rank, pr.data(), pr.size(), stream);
     if (rc == BPE_OK) {
-      std::vector<uint16_t> pa((size_t)128 * 128, 0);
-      for (int x = 0; x < 128; ++x)
-        for (int y = 0; y < 128; ++y) {
-          const int32_t r = pr[(size_t)(x * 256 + y)];
-          if (r != kRankInf) pa[(size_t)(x * 128 + y)] = (uint16_t)std::min<int32_t>(r + 1, 0xFFFF);
-        }
-      rc = upload(&m->d_pair_ascii, pa.data(), pa.size(), stream);
+      std::vector<uint32_t> pf((size_t)kPairFilterWords, 0u);
+      for (int64_t r = 0; r < R; ++r) {
+        const uint32_t k = pair_filter_bit(
+            pair_mix((uint32_t)merges[2 * r], (uint32_t)merges[2 * r + 1], tseed));
+        pf[k >> 5] |= 1u << (k & 31);
+      }
+      rc = upload(&m->d_pair_filter, pf.data(), pf.size(), stream);
     }
   }
   if (rc == BPE_OK) {

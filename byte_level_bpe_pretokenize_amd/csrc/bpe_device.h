@@ -21,10 +21,18 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 // The rank table as seen by the kernels.
 struct RankTable {
-  const u64x2 *b;  // buckets
-  uint32_t mask;   // buckets - 1
+  const u64x2 *b;             // buckets
+  uint32_t mask;              // buckets - 1
   uint32_t seed;
+  const uint32_t *filt = nullptr;  // the pair filter (pair_filter_bit), nullptr = none
 };
+
+// False when the pair with mix x certainly has no rank (its filter bit is clear).
+__device__ __forceinline__ bool pair_maybe(const RankTable &t, uint32_t x) {
+  if (!t.filt) return true;
+  const uint32_t k = pair_filter_bit(x);
+  return (t.filt[k >> 5] >> (k & 31)) & 1u;
+}
 
 // Rank held by a loaded bucket for key, or kRankInf.
 __device__ __forceinline__ int32_t bucket_rank(u64x2 b, uint64_t key) {

@@ -125,20 +125,6 @@ struct GlobalPairs {
   }
 };
 
-// Rank of a byte pair from a copy in LDS of the ASCII pairs' ranks (1 + rank,
-// 0 for none), the others and ranks from 0xFFFE on from device memory.
-struct AsciiPairs {
-  const uint16_t *pa;  // LDS
-  const int32_t *__restrict__ pair_rank;
-  __device__ __forceinline__ int32_t operator()(uint32_t x, uint32_t y) const {
-    if ((x | y) < 128u) {
-      const uint32_t u = pa[(x << 7) | y];
-      if (u != 0xFFFFu) return u == 0 ? kRankInf : (int32_t)u - 1;
-    }
-    return pair_rank[(x << 8) | y];
-  }
-};
-
 // Merge one pre-token of len <= W bytes (little-endian words w) by one lane
 // and write its symbols to out; returns their count.  A round takes the
 // lowest rank r and merges its pairs left to right without overlap; here the
@@ -202,8 +188,8 @@ __device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, cons
     const uint32_t xl = pair_mix(sp, z, t.seed), xr = pair_mix(z, st, t.seed);
     const uint64_t kl = pair_key(sp, z), kr = pair_key(z, st);
     u64x2 bl = {kEmptySlot, kEmptySlot}, br = {kEmptySlot, kEmptySlot};
-    if (hp) bl = t.b[pair_bucket0(xl, t.mask)];
-    if (ht) br = t.b[pair_bucket0(xr, t.mask)];
+    if (hp && pair_maybe(t, xl)) bl = t.b[pair_bucket0(xl, t.mask)];
+    if (ht && pair_maybe(t, xr)) br = t.b[pair_bucket0(xr, t.mask)];
     int32_t rl = bucket_rank(bl, kl), rr = bucket_rank(br, kr);
     const bool nl = hp && rl == kRankInf && bucket_flag(bl);
     const bool nr = ht && rr == kRankInf && bucket_flag(br);
@@ -928,10 +914,10 @@ __device__ void lane_merge2(const uint32_t *wa, int la, bool va, int32_t *outa, 
     const uint64_t klB = pair_key(spB, zB), krB = pair_key(zB, stB);
     const u64x2 none = {kEmptySlot, kEmptySlot};
     u64x2 blA = none, brA = none, blB = none, brB = none;
-    if (hpA) blA = t.b[pair_bucket0(xlA, t.mask)];
-    if (htA) brA = t.b[pair_bucket0(xrA, t.mask)];
-    if (hpB) blB = t.b[pair_bucket0(xlB, t.mask)];
-    if (htB) brB = t.b[pair_bucket0(xrB, t.mask)];
+    if (hpA && pair_maybe(t, xlA)) blA = t.b[pair_bucket0(xlA, t.mask)];
+    if (htA && pair_maybe(t, xrA)) brA = t.b[pair_bucket0(xrA, t.mask)];
+    if (hpB && pair_maybe(t, xlB)) blB = t.b[pair_bucket0(xlB, t.mask)];
+    if (htB && pair_maybe(t, xrB)) brB = t.b[pair_bucket0(xrB, t.mask)];
     int32_t rlA = bucket_rank(blA, klA), rrA = bucket_rank(brA, krA);
     int32_t rlB = bucket_rank(blB, klB), rrB = bucket_rank(brB, krB);
     const bool nlA = hpA && rlA == kRankInf && bucket_flag(blA);
@@ -1057,9 +1043,9 @@ __device__ __forceinline__ int64_t wave_group(int64_t first) {
 // bits each.
 template <int W, class Pairs>
 __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b, LaneCols<W> &L,
-                                 const Pairs &pairs) {
+                                 const Pairs &pairs, const uint32_t *filt = nullptr) {
   const int lane = lane_id();
-  const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
+  const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed, filt};
   // per chunk: entries of the bucket before the chunk's (uniform across the wave)
   int pre[kGroup];
   int total = 0;
@@ -1100,10 +1086,11 @@ __device__ uint64_t merge_bucket(const EncodeArgs &a, const LaneGroup &G, int b,
 // entries per batch; the two column sets share the W-wide region of L2.
 template <int W, class Pairs>
 __device__ uint64_t merge_bucket2(const EncodeArgs &a, const LaneGroup &G, int b,
-                                  LaneCols<2 * W> &L2, const Pairs &pairs) {
+                                  LaneCols<2 * W> &L2, const Pairs &pairs,
+                                  const uint32_t *filt = nullptr) {
   static_assert(2 * sizeof(LaneCols<W>) <= sizeof(LaneCols<2 * W>), "two column sets fit");
   const int lane = lane_id();
-  const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed};
+  const RankTable t{reinterpret_cast<const u64x2 *>(a.table), a.table_mask, a.table_seed, filt};
   LaneCols<W> &LA = *reinterpret_cast<LaneCols<W> *>(&L2);
   LaneCols<W> &LB = *(reinterpret_cast<LaneCols<W> *>(&L2) + 1);
   int pre[kGroup];
@@ -1171,8 +1158,8 @@ constexpr int kMergePWaves = 16;  // waves of a persistent k_merge workgroup, on
 
 struct PMergeShared {
   LaneCols<16> cols[kMergePWaves];
-  uint16_t pa[128 * 128];  // ranks of the ASCII byte pairs
-  int next;                // next group of this workgroup's share
+  uint32_t filt[kPairFilterWords];  // the pair filter: most pairs without a rank stay in the CU
+  int next;                         // next group of this workgroup's share
 };
 
 // Merge-loop lists of kGroup consecutive chunks per wave, buckets 0 (2-8
@@ -1181,18 +1168,19 @@ struct PMergeShared {
 // tot[c] gets the chunk's count so far (its resolved pre-tokens and these
 // buckets) with its status bits on top.  One workgroup per compute unit,
 // kMergePWaves waves that take the groups of its share (every gridDim.x-th)
-// one at a time; the initial ranks of ASCII byte pairs come from an LDS copy.
+// one at a time.  The merges' pair filter is copied to LDS: a new pair whose
+// filter bit is clear skips its rank probe.
 __global__ void __launch_bounds__(MWG *kMergePWaves) k_merge(EncodeArgs a) {
   __shared__ PMergeShared s;
   const int tid = threadIdx.x, lane = lane_id();
   {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.pair_ascii);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(s.pa);
-    for (int i = tid; i < 128 * 128 * 2 / 16; i += MWG * kMergePWaves) dst[i] = src[i];
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.pair_filter);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(s.filt);
+    for (int i = tid; i < kPairFilterWords / 4; i += MWG * kMergePWaves) dst[i] = src[i];
     if (tid == 0) s.next = 0;
   }
   __syncthreads();
-  const AsciiPairs pairs{s.pa, a.pair_rank};
+  const GlobalPairs pairs{a.pair_rank};
   LaneCols<16> &L = s.cols[wave_id()];
   for (;;) {
     int q = 0;
@@ -1200,8 +1188,8 @@ __global__ void __launch_bounds__(MWG *kMergePWaves) k_merge(EncodeArgs a) {
     q = lane_value(q, 0);
     LaneGroup G;
     if (!lane_group(a, (int64_t)blockIdx.x + (int64_t)gridDim.x * q, G)) break;
-    uint64_t tok = merge_bucket2<8>(a, G, 0, L, pairs);
-    tok += merge_bucket<16>(a, G, 1, L, pairs);
+    uint64_t tok = merge_bucket2<8>(a, G, 0, L, pairs, s.filt);
+    tok += merge_bucket<16>(a, G, 1, L, pairs, s.filt);
     tok = wave_tok_sum(tok);
     if (lane < G.nf) {
       const int64_t c = G.cg + lane;

@@ -72,6 +72,14 @@ __host__ __device__ inline uint32_t pair_mix(uint32_t l, uint32_t r, uint32_t se
   return mix32(mul24(l ^ seed, 0x9E3779u) ^ r ^ (seed >> 8));
 }
 
+// A bit set of the merges' pairs (a one-hash Bloom filter over pair_mix): a
+// pair whose bit is clear has no rank, so its probe of the rank table can be
+// skipped.  2^18 bits (32 KiB): for 32,000 merges about one clear-pair probe
+// in eight still goes to the table.
+constexpr int kPairFilterLog2 = 18;
+constexpr int kPairFilterWords = (1 << kPairFilterLog2) / 32;
+__host__ __device__ inline uint32_t pair_filter_bit(uint32_t x) { return x >> (32 - kPairFilterLog2); }
+
 // First and second bucket of a mix, for a table of mask + 1 buckets (a power
 // of two, at least 2); the second differs from the first.
 __host__ __device__ inline uint32_t pair_bucket0(uint32_t x, uint32_t mask) { return x & mask; }
@@ -318,8 +326,8 @@ struct EncodeArgs {
   uint32_t table_seed;
   const int32_t *id_map;     // nullptr = identity
   const int32_t *pair_rank;  // [65536]: rank of the byte pair (a, b) at a * 256 + b
-  const uint16_t *pair_ascii;  // [128 * 128]: for a, b < 128, 1 + rank of (a, b) at a * 128 + b;
-                               // 0: no merge; 0xFFFF: rank >= 0xFFFE, see pair_rank
+  const uint32_t *pair_filter;  // [kPairFilterWords] bit pair_filter_bit(pair_mix(l, r, table_seed))
+                                // set for every merge (l, r)
   int n_cu;                  // compute units (workgroups of the persistent merge kernel)
   const uint4 *words;        // short word table (one uint4 per slot); nullptr = none
   uint32_t word_mask;        // slots - 1
