@@ -252,6 +252,7 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.pair_rank = model->d_pair_rank;
   a.pair_filter = model->d_pair_filter;
   a.n_cu = model->n_cu;
+  a.lgroup = 1;  // the launch picks the merge kernels' group size
   a.words = words ? model->d_words : nullptr;
   a.word_mask = model->word_mask;
   a.word_seed = model->word_seed;

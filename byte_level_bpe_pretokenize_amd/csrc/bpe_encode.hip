@@ -1007,13 +1007,14 @@ struct LaneGroup {
   int cnt[kGroup][kBuckets];
 };
 
-// Group q (chunks kGroup q ..) of the merge-loop lists; false past the last.
+// Group q (chunks lgroup q .., lgroup <= kGroup) of the merge-loop lists;
+// false past the last.
 // The counts of buckets kDedupFrom..2 are their owners', listed in olist
 // (all their entries, in a chunk that did not go through the call's table).
 __device__ __forceinline__ bool lane_group(const EncodeArgs &a, int64_t q, LaneGroup &G) {
-  G.cg = q * kGroup;
+  G.cg = q * a.lgroup;
   if (G.cg >= a.n_chunks) return false;
-  G.nf = (int)min<int64_t>(kGroup, a.n_chunks - G.cg);
+  G.nf = (int)min<int64_t>(a.lgroup, a.n_chunks - G.cg);
 #pragma unroll
   for (int f = 0; f < kGroup; ++f)
 #pragma unroll
@@ -2334,12 +2335,19 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream, hipEvent_t *ev
                          stream, a, seed, a.n_chunks, 0);
   }
   mark();
-  const unsigned LG = (G + kGroup * kMergeWaves - 1) / (kGroup * kMergeWaves);
-  const unsigned n_groups = (G + kGroup - 1) / kGroup;
+  // chunks per lane-merge group: kGroup fills a batch's lanes from several
+  // chunks; fewer where that would leave most waves of the persistent
+  // k_merge without a group (a small input)
+  EncodeArgs m = a;
+  m.lgroup = kGroup;
+  while (m.lgroup > 1 && 4 * ((G + m.lgroup - 1) / m.lgroup) < (unsigned)a.n_cu * kMergePWaves)
+    m.lgroup /= 2;
+  const unsigned n_groups = (G + m.lgroup - 1) / m.lgroup;
+  const unsigned LG = (n_groups + kMergeWaves - 1) / kMergeWaves;
   hipLaunchKernelGGL(k_merge, dim3(min((unsigned)a.n_cu, n_groups)), dim3(MWG * kMergePWaves), 0,
-                     stream, a);
+                     stream, m);
   mark();
-  hipLaunchKernelGGL(k_merge_wide, dim3(LG), dim3(MWG * kMergeWaves), 0, stream, a);
+  hipLaunchKernelGGL(k_merge_wide, dim3(LG), dim3(MWG * kMergeWaves), 0, stream, m);
   mark();
   hipLaunchKernelGGL(k_merge_long, dim3((G + kGroup - 1) / kGroup), dim3(MWG), 0, stream, a);
   mark();

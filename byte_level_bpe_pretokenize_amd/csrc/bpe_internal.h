@@ -329,6 +329,7 @@ struct EncodeArgs {
   const uint32_t *pair_filter;  // [kPairFilterWords] bit pair_filter_bit(pair_mix(l, r, table_seed))
                                 // set for every merge (l, r)
   int n_cu;                  // compute units (workgroups of the persistent merge kernel)
+  int lgroup;                // chunks per lane-merge group (set by the launch)
   const uint4 *words;        // short word table (one uint4 per slot); nullptr = none
   uint32_t word_mask;        // slots - 1
   uint32_t word_seed;
