@@ -125,6 +125,27 @@ struct GlobalPairs {
   }
 };
 
+// The live symbols of a lane's column S (bit j of alive: position j), in
+// order, to out; returns their count.  They are first packed to the front of
+// the column (in place: the k-th live position is at or after k), then
+// stored four to a 16-byte store.  out is 16-byte aligned and has room for
+// the pre-token's length rounded up to 4 (an entry's tokens sit at 4 times its
+// 4-byte aligned dense offset, in a span four times its rounded length), so
+// the stores stay inside it; slots past the count hold leftovers.
+template <int W>
+__device__ __forceinline__ int emit_alive(uint32_t *S, uint32_t alive, int32_t *out) {
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < W; ++j)
+    if ((alive >> j) & 1u) S[64 * n++] = S[64 * j];
+#pragma unroll
+  for (int q = 0; q < W / 4; ++q)
+    if (n > 4 * q)
+      *reinterpret_cast<u32x4 *>(out + 4 * q) =
+          u32x4{S[64 * (4 * q)], S[64 * (4 * q + 1)], S[64 * (4 * q + 2)], S[64 * (4 * q + 3)]};
+  return n;
+}
+
 // Merge one pre-token of len <= W bytes (little-endian words w) by one lane
 // and write its symbols to out; returns their count.  A round takes the
 // lowest rank r and merges its pairs left to right without overlap; here the
@@ -212,11 +233,7 @@ __device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, cons
     if (hp) K[64 * p] = vl;
     K[64 * i] = vr;  // i < q <= W - 1
   }
-  int n = 0;
-#pragma unroll
-  for (int j = 0; j < W; ++j)
-    if ((alive >> j) & 1u) out[n++] = (int32_t)S[64 * j];
-  return n;
+  return emit_alive<W>(S, alive, out);
 }
 
 // The same rounds with the whole workgroup (NT threads) on Y[0..n), RK
@@ -971,14 +988,8 @@ __device__ void lane_merge2(const uint32_t *wa, int la, bool va, int32_t *outa, 
       rcB = rB;
     }
   }
-  int na = 0, nb = 0;
-#pragma unroll
-  for (int j = 0; j < W; ++j) {
-    if ((aliveA >> j) & 1u) outa[na++] = (int32_t)SA[64 * j];
-    if ((aliveB >> j) & 1u) outb[nb++] = (int32_t)SB[64 * j];
-  }
-  *nta = na;
-  *ntb = nb;
+  *nta = emit_alive<W>(SA, aliveA, outa);
+  *ntb = emit_alive<W>(SB, aliveB, outb);
 }
 
 // ---- k_merge, k_merge_wide ---------------------------------------------------
