@@ -2221,13 +2221,21 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
     const int head = min(nst, (int)((4 - ((reinterpret_cast<uintptr_t>(a.ids + base) >> 2) & 3)) & 3));
     const int body = (nst - head) & ~3;
     if (tid < head) a.ids[base + tid] = out_id(a.id_map, s.out[tid]);
-    for (int k = head + 4 * tid; k < head + body; k += 4 * EWG) {
-      uint4 q;
-      q.x = (uint32_t)out_id(a.id_map, s.out[k]);
-      q.y = (uint32_t)out_id(a.id_map, s.out[k + 1]);
-      q.z = (uint32_t)out_id(a.id_map, s.out[k + 2]);
-      q.w = (uint32_t)out_id(a.id_map, s.out[k + 3]);
-      *reinterpret_cast<uint4 *>(a.ids + base + k) = q;
+    if (a.id_map) {
+      for (int k = head + 4 * tid; k < head + body; k += 4 * EWG) {
+        uint4 q;
+        q.x = (uint32_t)a.id_map[s.out[k]];
+        q.y = (uint32_t)a.id_map[s.out[k + 1]];
+        q.z = (uint32_t)a.id_map[s.out[k + 2]];
+        q.w = (uint32_t)a.id_map[s.out[k + 3]];
+        *reinterpret_cast<uint4 *>(a.ids + base + k) = q;
+      }
+    } else {
+      // (the symbols are the IDs: the four reads need no branch between them)
+      for (int k = head + 4 * tid; k < head + body; k += 4 * EWG)
+        *reinterpret_cast<uint4 *>(a.ids + base + k) =
+            uint4{(uint32_t)s.out[k], (uint32_t)s.out[k + 1], (uint32_t)s.out[k + 2],
+                  (uint32_t)s.out[k + 3]};
     }
     const int k = head + body + tid;
     if (k < nst) a.ids[base + k] = out_id(a.id_map, s.out[k]);
