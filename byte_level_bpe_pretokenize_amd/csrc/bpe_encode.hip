@@ -1568,60 +1568,94 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
         }
     }
     // 2. merge flags (run starts by a running maximum) and compaction: a
-    //    symbol whose left neighbour merged is consumed.  The next group's
-    //    symbols, ranks and candidate bits are read before this group's
-    //    writes (those land at or before this group's positions, never in
-    //    the next group), so each group's reads overlap the one before.
-    int run = 0;                // run start in force before this group
+    //    symbol whose left neighbour merged is consumed.  Two groups of 64
+    //    positions per step, A then B: their scans and ballots do not wait on
+    //    each other, only the carries from A into B do.  The next two
+    //    groups' symbols, ranks and candidate bits are read before this
+    //    step's writes (those land at or before this step's positions), so
+    //    each step's reads overlap the one before.
+    int run = 0;                // run start in force before this step
     bool run_c = false;         // its candidate bit
-    bool prevm = false;         // the position before this group merged
+    bool prevm = false;         // the position before this step merged
     int32_t prevr = kRankInf;   // and its rank (its slot may already be rewritten)
     int out = 0;                // symbols kept so far
     int nnew = 0;               // new symbols so far
     bool any = false;
-    int32_t nr = lane < n ? R[lane] : kRankInf;
-    int32_t ny = lane < n ? L.y[lane] : 0;
-    uint64_t ncm = ((uint64_t)L.cand[1] << 32) | L.cand[0];
-    for (int i0 = 0; i0 < n; i0 += MWG) {
-      const int i = i0 + lane;
-      const bool in = i < n;
-      const int32_t r = nr, y = ny;
-      const uint64_t cm = ncm;  // candidate bits of positions i0 .. i0 + 63
-      if (i0 + MWG < n) {
-        const int j = i + MWG;
-        nr = j < n ? R[j] : kRankInf;
-        ny = j < n ? L.y[j] : 0;
-        ncm = ((uint64_t)L.cand[(i0 >> 5) + 3] << 32) | L.cand[(i0 >> 5) + 2];
+    int32_t nrA = lane < n ? R[lane] : kRankInf;
+    int32_t nyA = lane < n ? L.y[lane] : 0;
+    int32_t nrB = lane + MWG < n ? R[lane + MWG] : kRankInf;
+    int32_t nyB = lane + MWG < n ? L.y[lane + MWG] : 0;
+    uint64_t ncmA = ((uint64_t)L.cand[1] << 32) | L.cand[0];
+    uint64_t ncmB = ((uint64_t)L.cand[3] << 32) | L.cand[2];
+    for (int i0 = 0; i0 < n; i0 += 2 * MWG) {
+      const int iA = i0 + lane, iB = iA + MWG;
+      const bool inA = iA < n, inB = iB < n;
+      const int32_t rA = nrA, yA = nyA, rB = nrB, yB = nyB;
+      const uint64_t cmA = ncmA, cmB = ncmB;  // candidate bits of positions i0 .., i0 + 64 ..
+      if (i0 + 2 * MWG < n) {
+        const int jA = iA + 2 * MWG, jB = iB + 2 * MWG;
+        nrA = jA < n ? R[jA] : kRankInf;
+        nyA = jA < n ? L.y[jA] : 0;
+        nrB = jB < n ? R[jB] : kRankInf;
+        nyB = jB < n ? L.y[jB] : 0;
+        const int w = (i0 >> 5) + 4;  // the word of position i0 + 128
+        ncmA = ((uint64_t)L.cand[w + 1] << 32) | L.cand[w];
+        ncmB = ((uint64_t)L.cand[w + 3] << 32) | L.cand[w + 2];
       }
-      const int32_t rl = wave_shift_up1(r, prevr);
-      const bool bnd = in && (i == 0 || rl != r);
-      int st = bnd ? i : -1;
-      st = max(wave_incl_max(st), run);
-      const bool c = in && ((cm >> lane) & 1u);
-      const bool cs = st >= i0 ? ((cm >> (st - i0)) & 1u) : run_c;
-      const bool m = c && cs && ((i - st) & 1) == 0;
-      const uint64_t bm = __ballot(m);
-      const bool cons = lane == 0 ? prevm : ((bm >> (lane - 1)) & 1u);
-      const bool keep = in && !cons;
-      const uint64_t bk = __ballot(keep);
-      const int o = out + __popcll(bk & below);
-      if (keep) {
-        L.y[o] = m ? 256 + r : y;
-        R[o] = m ? -1 : r;
+      const int32_t rAl = wave_shift_up1(rA, prevr);
+      const int32_t rBl = wave_shift_up1(rB, lane_value(rA, 63));
+      const bool bA = inA && (iA == 0 || rAl != rA);
+      const bool bB = inB && rBl != rB;
+      const bool cA = inA && ((cmA >> lane) & 1u), cB = inB && ((cmB >> lane) & 1u);
+      // where every position starts a run (no pair repeats its neighbour's
+      // rank) each is its own run start
+      int stA = iA, stB = iB;
+      bool csA = cA, csB = cB;
+      if (__ballot((inA && !bA) || (inB && !bB)) != 0) {
+        const int sA = wave_incl_max(bA ? iA : -1), sB = wave_incl_max(bB ? iB : -1);
+        stA = max(sA, run);
+        const int runA = lane_value(stA, 63);
+        const bool rcA = runA >= i0 ? ((cmA >> (runA - i0)) & 1u) : run_c;
+        stB = max(sB, runA);
+        csA = stA >= i0 ? ((cmA >> (stA - i0)) & 1u) : run_c;
+        csB = stB >= i0 + MWG ? ((cmB >> (stB - i0 - MWG)) & 1u) : rcA;
+      }
+      const bool mA = cA && csA && ((iA - stA) & 1) == 0;
+      const bool mB = cB && csB && ((iB - stB) & 1) == 0;
+      const uint64_t bmA = __ballot(mA), bmB = __ballot(mB);
+      const bool consA = lane == 0 ? prevm : ((bmA >> (lane - 1)) & 1u);
+      const bool consB = lane == 0 ? ((bmA >> 63) & 1u) : ((bmB >> (lane - 1)) & 1u);
+      const bool kA = inA && !consA, kB = inB && !consB;
+      const uint64_t bkA = __ballot(kA), bkB = __ballot(kB);
+      const int oA = out + __popcll(bkA & below);
+      const int oB = out + __popcll(bkA) + __popcll(bkB & below);
+      if (kA) {
+        L.y[oA] = mA ? 256 + rA : yA;
+        R[oA] = mA ? -1 : rA;
+      }
+      if (kB) {
+        L.y[oB] = mB ? 256 + rB : yB;
+        R[oB] = mB ? -1 : rB;
       }
       // (a merging position is never consumed: its left neighbour would
       // belong to the same run at an odd offset)
-      if (m) {
-        const int q = nnew + __popcll(bm & below);
-        if (q < kFreshMax) L.fresh[q] = (uint16_t)o;
+      if (mA) {
+        const int q = nnew + __popcll(bmA & below);
+        if (q < kFreshMax) L.fresh[q] = (uint16_t)oA;
       }
-      nnew += __popcll(bm);
-      any |= bm != 0;
-      out += __popcll(bk);
-      prevm = (bm >> 63) & 1u;
-      prevr = lane_value(r, 63);
-      const int nrun = lane_value(st, 63);
-      run_c = nrun >= i0 ? ((cm >> (nrun - i0)) & 1u) : run_c;
+      if (mB) {
+        const int q = nnew + __popcll(bmA) + __popcll(bmB & below);
+        if (q < kFreshMax) L.fresh[q] = (uint16_t)oB;
+      }
+      nnew += __popcll(bmA) + __popcll(bmB);
+      any |= (bmA | bmB) != 0;
+      out += __popcll(bkA) + __popcll(bkB);
+      prevm = (bmB >> 63) & 1u;
+      prevr = lane_value(rB, 63);
+      const int nrun = lane_value(stB, 63);
+      run_c = nrun >= i0 + MWG ? ((cmB >> (nrun - i0 - MWG)) & 1u)
+            : nrun >= i0       ? ((cmA >> (nrun - i0)) & 1u)
+                               : run_c;
       run = nrun;
     }
     if (!any) break;
