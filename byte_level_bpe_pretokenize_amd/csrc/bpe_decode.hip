@@ -50,15 +50,6 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   const int64_t c = blockIdx.x;
   const int64_t i0 = c * kDecChunk;
   const int cnt = (int)min<int64_t>(kDecChunk, a.n_ids - i0);
-  // the first document whose IDs start at or after this chunk's (and, from
-  // the last chunk, after the last ID): the documents that start in each chunk
-  if (wave_id() == 0) {
-    const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, i0);
-    if (lane_id() == 0) a.dlo[c] = d;
-  } else if (wave_id() == 1 && c == a.n_chunks - 1) {
-    const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, a.n_ids);
-    if (lane_id() == 0) a.dlo[c + 1] = d;
-  }
   bool bad_id = false;
   int64_t mine = 0;
   // consecutive threads read consecutive IDs
@@ -79,6 +70,16 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   const int bits = (__syncthreads_or(bad_id) ? (int)BPE_STATUS_BAD_ID : 0) |
                    (__syncthreads_or(bad_off) ? (int)BPE_STATUS_BAD_ID_OFFSETS : 0);
   if (tid == 0) a.tot[c] = total | ((int64_t)bits << kCountBits);
+  // the first document whose IDs start at or after this chunk's (and, from
+  // the last chunk, after the last ID): the documents that start in each
+  // chunk.  Searched last: nothing above waits on it.
+  if (wave_id() == 0) {
+    const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, i0);
+    if (lane_id() == 0) a.dlo[c] = d;
+  } else if (wave_id() == 1 && c == a.n_chunks - 1) {
+    const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, a.n_ids);
+    if (lane_id() == 0) a.dlo[c + 1] = d;
+  }
 }
 
 __global__ void __launch_bounds__(kScanBlock) k_dec_scan(DecodeArgs a) {
@@ -131,8 +132,17 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
   // document offsets)
   const int k0 = tid * DPT;
   int32_t sym[DPT], len[DPT];
+  if (k0 + DPT <= cnt && ((reinterpret_cast<uintptr_t>(a.ids + i0 + k0) & 15u) == 0)) {
+    // the thread's eight IDs in two 16-byte loads
+    const int4 p = *reinterpret_cast<const int4 *>(a.ids + i0 + k0);
+    const int4 q = *reinterpret_cast<const int4 *>(a.ids + i0 + k0 + 4);
+    const int32_t v[DPT] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) sym[j] = k0 + j < cnt ? dec_sym(a, a.ids[i0 + k0 + j]) : -1;
+    for (int j = 0; j < DPT; ++j) sym[j] = dec_sym(a, v[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) sym[j] = k0 + j < cnt ? dec_sym(a, a.ids[i0 + k0 + j]) : -1;
+  }
 #pragma unroll
   for (int j = 0; j < DPT; ++j) len[j] = sym[j] >= 0 ? a.exp_len[sym[j]] : 0;
   // (named values, not an array: an array of them ends up in scratch)
