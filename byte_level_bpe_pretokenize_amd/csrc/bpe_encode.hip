@@ -2195,8 +2195,16 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
       s.out[nt > 2 ? w + 2 : kOutCap] = (int32_t)t.z;
       s.out[nt > 3 ? w + 3 : kOutCap] = (int32_t)t.w;
       if (nt > 4) {
+        // the rest four to a 16-byte load: an entry's token span is 16-byte
+        // aligned and covers its tokens rounded up to four
         const int32_t *src = entry_res(a, res, u);
-        for (int q = 4; q < nt; ++q) s.out[w + q] = src[q];
+        for (int q = 4; q < nt; q += 4) {
+          const u32x4 r4 = *reinterpret_cast<const u32x4 *>(src + q);
+          s.out[w + q] = (int32_t)r4.x;
+          if (q + 1 < nt) s.out[w + q + 1] = (int32_t)r4.y;
+          if (q + 2 < nt) s.out[w + q + 2] = (int32_t)r4.z;
+          if (q + 3 < nt) s.out[w + q + 3] = (int32_t)r4.w;
+        }
       }
       // a chunk where documents start keeps each pre-token's first position
       // in place of its pv value (read by this thread only, and already read)
