@@ -547,13 +547,28 @@ __device__ __forceinline__ int32_t long_lookup(const FindShared &s, const Encode
   return -1;
 }
 
-// Eight waves per SIMD (latency-bound: occupancy pays for the few registers
-// this spills).
 // The first document whose offset is at or after the byte before each
 // chunk (a binary search per chunk, one thread each): k_find starts its
-// document scan there.
+// document scan there.  The same grid checks the document offsets (start at
+// 0, never decrease, end at the input's length), each block its share, and
+// flags a block's first chunk (kDocFirstBad) where the share breaks a rule;
+// the check's loads are issued before the search's, so that their latencies
+// overlap.
+constexpr int64_t kDocFirstBad = (int64_t)1 << 62;
 __global__ void __launch_bounds__(256) k_docs(EncodeArgs a) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  bool bad = false;
+  {
+    const int64_t i0 = (int64_t)blockIdx.x * 256 * a.doc_per;
+    const int64_t i1 = min(i0 + 256 * a.doc_per, a.n_docs + 1);
+    for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) {
+      const int64_t v = a.doc_off[i];
+      if (i == 0 && v != 0) bad = true;
+      if (i == a.n_docs && v != a.n_bytes) bad = true;
+      if (i < a.n_docs && a.doc_off[i + 1] < v) bad = true;
+    }
+  }
+  bad = __syncthreads_or(bad);
   if (c >= a.n_chunks) return;
   const int64_t key = c * kChunk - 1;
   int64_t lo = 0, hi = a.n_docs + 1;  // first index in [lo, hi) with doc_off >= key
@@ -562,27 +577,16 @@ __global__ void __launch_bounds__(256) k_docs(EncodeArgs a) {
     if (a.doc_off[mid] < key) lo = mid + 1;
     else hi = mid;
   }
-  a.dfirst[c] = lo;
+  a.dfirst[c] = lo | ((bad && threadIdx.x == 0) ? kDocFirstBad : 0);
 }
 
+// Eight waves per SIMD.
 __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   __shared__ FindShared s;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
 
-  // document offsets check, spread over the grid
-  bool bad = false;
-  {
-    const int64_t per = a.doc_per;
-    const int64_t i0 = (int64_t)blockIdx.x * per;
-    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += WG) {
-      const int64_t v = a.doc_off[i];
-      if (i == 0 && v != 0) bad = true;
-      if (i == a.n_docs && v != a.n_bytes) bad = true;
-      if (i < a.n_docs && a.doc_off[i + 1] < v) bad = true;
-    }
-  }
-
   const int64_t c = blockIdx.x;
+  const int64_t dfirst = a.dfirst[c];  // (k_docs) loaded early: used after the window loads
   const int64_t c0 = c * kChunk;
   const int64_t n = a.n_bytes;
   const int nwin = (int)min<int64_t>(WIN, n - c0);
@@ -607,18 +611,21 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
 
   // 1. the window's bytes, 16 per load (group g covers positions 16g ..
   //    16g + 15; group -1 is the two bytes before the chunk), issued first so
-  //    that their latency overlaps the document search
-  const bool aligned = (((uintptr_t)a.bytes) & 15u) == 0;
+  //    that their latency overlaps the document search.  Every thread loads
+  //    from an address clamped into the input, so that no lane is masked off
+  //    and nothing waits for these loads before the search; a group that is
+  //    not wholly inside the input is copied byte by byte below.
+  const bool vec = (((uintptr_t)a.bytes) & 15u) == 0 && n >= 16;
   constexpr int NG = WIN / 16 + 1;  // groups -1 .. WIN / 16 - 1
   u32x4 reg[2];
+  if (vec) {
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int g = tid - 1 + r * WG;
-    reg[r] = u32x4{0, 0, 0, 0};
-    const int64_t gp = c0 + 16 * (int64_t)g;
-    if (g + 1 < NG && aligned && gp >= 0 && gp + 16 <= n)
+    for (int r = 0; r < 2; ++r) {
+      const int64_t gp = c0 + 16 * (int64_t)(tid - 1 + r * WG);
+      const int64_t q = min(max(gp, (int64_t)0), (n - 16) & ~(int64_t)15);
       // streamed once: keep it out of the way of the tables in L2
-      reg[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.bytes + gp));
+      reg[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.bytes + q));
+    }
   }
   __syncthreads();
 
@@ -626,7 +633,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   //    document at or after the byte before the chunk, then 64 offsets per
   //    load)
   if (wave == 0) {
-    int64_t d0 = min(max(a.dfirst[c], (int64_t)0), a.n_docs);  // (k_docs)
+    int64_t d0 = min(dfirst & (kDocFirstBad - 1), a.n_docs);
     int64_t olo = d0, ohi = d0;
     for (;;) {
       const int64_t d = d0 + lane;
@@ -649,7 +656,7 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
     if (g + 1 >= NG) continue;
     const int64_t gp = c0 + 16 * (int64_t)g;
     uint8_t *dst = &s.B[16 + 16 * g];
-    if (aligned && gp >= 0 && gp + 16 <= n) {
+    if (vec && gp >= 0 && gp + 16 <= n) {
       *reinterpret_cast<u32x4 *>(dst) = reg[r];
     } else {
       for (int k = 0; k < 16; ++k) {
@@ -814,7 +821,8 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
       place(k, (uint32_t)e, (uint32_t)(e >> 32));
     }
   }
-  const bool any_bad = __syncthreads_or(bad);
+  __syncthreads();
+  const bool any_bad = (dfirst & kDocFirstBad) != 0;
   const uint32_t nlo = (uint32_t)s.tally, nhi = (uint32_t)(s.tally >> 32);
   if (tid == 0) {
     int32_t *m = a.meta + kMetaInts * c;
@@ -2137,21 +2145,30 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
     const int np = min(kEmitPasses, (n_pt - r0 + EWG - 1) / EWG);
     int32_t v[kEmitPasses], cnt[kEmitPasses], inc[kEmitPasses], w0[kEmitPasses];
     u32x4 first[kEmitPasses];
+    // a lane-merged entry's count comes from cntk, loaded beside pv, a
+    // wave-merged one's from mt; then the first four tokens of each
+    // lane-merged entry in one load (other pre-tokens read entry 0: the load
+    // stays unconditional), issued last so that the scan below waits for the
+    // counts only
 #pragma unroll
     for (int j = 0; j < kEmitPasses; ++j) {
+      v[j] = INT32_MIN;
+      cnt[j] = 0;
       if (j >= np) continue;
       const int k = r0 + j * EWG + tid;
       v[j] = k < n_pt ? (r0 == 0 ? v0[j] : pv[k]) : INT32_MIN;
       const int nk = r0 == 0 ? n0[j] : cntk[k];
-      // a lane-merged entry's count comes from cntk, loaded beside pv; its
-      // first four tokens in one load (other pre-tokens read entry 0: the
-      // load stays unconditional)
       const int u = -1 - v[j];
       const bool neg = v[j] < 0 && v[j] != INT32_MIN;
       const bool lane_merged = neg && (u < kPvLong || u >= kPvDup);
-      first[j] = *reinterpret_cast<const u32x4 *>(entry_res(a, res, lane_merged ? u : 0));
       cnt[j] = v[j] >= 0 ? 1 : (lane_merged ? nk : 0);
       if (neg && !lane_merged) cnt[j] = a.mt[c * kMaxLong + (u - kPvLong)];
+    }
+#pragma unroll
+    for (int j = 0; j < kEmitPasses; ++j) {
+      const int u = -1 - v[j];
+      const bool lane_merged = v[j] < 0 && v[j] != INT32_MIN && (u < kPvLong || u >= kPvDup);
+      first[j] = *reinterpret_cast<const u32x4 *>(entry_res(a, res, lane_merged ? u : 0));
     }
     // positions: every pass of the round is one scan over the workgroup
     // (chunk-relative positions fit 32 bits: only the chunk's last pre-token
