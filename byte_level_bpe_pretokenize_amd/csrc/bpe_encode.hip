@@ -2033,7 +2033,7 @@ __global__ void __launch_bounds__(OWG) k_bscan(EncodeArgs a) {
 
 constexpr int EWG = 256;                 // k_emit threads per chunk
 constexpr int kOutCap = kChunk + kHalo;  // chunk-relative token positions staged in LDS
-constexpr int kEmitPasses = 3;           // passes of EWG pre-tokens per round
+constexpr int kEmitPasses = 4;           // passes of EWG pre-tokens per round
 
 constexpr int kDocLds = 512;             // document starts of a chunk staged in LDS (with reserved IDs)
 
