@@ -284,7 +284,6 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.status = d_status;
   a.n_chunks = enc_chunks(n_bytes);
   a.doc_per = (n_docs + 1 + a.n_chunks - 1) / a.n_chunks;
-  a.dt_per = (2 * ((uint64_t)a.dt_mask + 1) + (uint64_t)a.n_chunks - 1) / (uint64_t)a.n_chunks;
   for (int k = 0; k < 4; ++k) a.win_d[k] = model->win_d[k];
   a.bos = bos;
   a.eos = eos;

@@ -553,7 +553,7 @@ __device__ __forceinline__ int32_t long_lookup(const FindShared &s, const Encode
 // 0, never decrease, end at the input's length), each block its share, and
 // flags a block's first chunk (kDocFirstBad) where the share breaks a rule;
 // the check's loads are issued before the search's, so that their latencies
-// overlap.
+// overlap.  It also clears the call's entry table (k_dedup).
 constexpr int64_t kDocFirstBad = (int64_t)1 << 62;
 __global__ void __launch_bounds__(256) k_docs(EncodeArgs a) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -569,6 +569,13 @@ __global__ void __launch_bounds__(256) k_docs(EncodeArgs a) {
     }
   }
   bad = __syncthreads_or(bad);
+  if (a.dedup) {
+    // the call's entry table starts empty (one 16-byte slot per store,
+    // spread over the grid)
+    u64x2 *dt = reinterpret_cast<u64x2 *>(a.dt);
+    const uint64_t slots = (uint64_t)a.dt_mask + 1, step = (uint64_t)gridDim.x * 256;
+    for (uint64_t i = (uint64_t)c; i < slots; i += step) dt[i] = u64x2{0ull, 0ull};
+  }
   if (c >= a.n_chunks) return;
   const int64_t key = c * kChunk - 1;
   int64_t lo = 0, hi = a.n_docs + 1;  // first index in [lo, hi) with doc_off >= key
@@ -593,12 +600,6 @@ __global__ void __launch_bounds__(WG, 8) k_find(EncodeArgs a) {
   const int nown = (int)min<int64_t>(kChunk, n - c0);
   const bool win_reaches_end = (c0 + nwin == n);
   for (int i = tid; i < DB_WORDS; i += WG) s.DB[i] = 0;
-  if (a.dedup) {
-    // this chunk's share of the call's entry table starts empty
-    const uint64_t words = 2 * ((uint64_t)a.dt_mask + 1);
-    const uint64_t lo = (uint64_t)c * a.dt_per, hi = min(lo + a.dt_per, words);
-    for (uint64_t i = lo + tid; i < hi; i += WG) a.dt[i] = 0ull;
-  }
   if (tid <= kShortMax) {
     // masks of the first tid bytes of three little-endian words
     u32x4 m;

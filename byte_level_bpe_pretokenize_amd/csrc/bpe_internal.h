@@ -361,7 +361,6 @@ struct EncodeArgs {
   int32_t *status;
   int64_t n_chunks;
   int64_t doc_per;           // document offsets checked per chunk (k_docs): ceil((n_docs + 1) / n_chunks)
-  uint64_t dt_per;           // entry-table words cleared per k_find workgroup: ceil(2 slots / n_chunks)
   // Window radius of the multi-rank rounds for long pre-tokens, by the class
   // of the pre-token's first letter/digit/space/punctuation byte: the longest
   // token whose bytes can occur in such a pre-token; 0 = one rank per round.
