@@ -2086,12 +2086,14 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int32_t *res = a.res + c * kMissSpan;
   // loads that need nothing else first: the first round's pv values (pv has
   // room for kChunk entries, so this reads inside it whatever the count), and
-  // the first pre-token of the documents that start here
+  // the first pre-token of the documents that start here.  pv (read once
+  // here) and the IDs (written once) are streamed with non-temporal
+  // accesses.
   const uint8_t *cntk = a.cntk + c * kChunk;
   int32_t v0[kEmitPasses], n0[kEmitPasses];
 #pragma unroll
   for (int j = 0; j < kEmitPasses; ++j) {
-    v0[j] = pv[j * EWG + tid];
+    v0[j] = __builtin_nontemporal_load(&pv[j * EWG + tid]);
     n0[j] = cntk[j * EWG + tid];
   }
   const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
@@ -2288,14 +2290,15 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
         q.y = (uint32_t)a.id_map[s.out[k + 1]];
         q.z = (uint32_t)a.id_map[s.out[k + 2]];
         q.w = (uint32_t)a.id_map[s.out[k + 3]];
-        *reinterpret_cast<uint4 *>(a.ids + base + k) = q;
+        __builtin_nontemporal_store(u32x4{q.x, q.y, q.z, q.w},
+                                    reinterpret_cast<u32x4 *>(a.ids + base + k));
       }
     } else {
       // (the symbols are the IDs: the four reads need no branch between them)
       for (int k = head + 4 * tid; k < head + body; k += 4 * EWG)
-        *reinterpret_cast<uint4 *>(a.ids + base + k) =
-            uint4{(uint32_t)s.out[k], (uint32_t)s.out[k + 1], (uint32_t)s.out[k + 2],
-                  (uint32_t)s.out[k + 3]};
+        __builtin_nontemporal_store(u32x4{(uint32_t)s.out[k], (uint32_t)s.out[k + 1],
+                                          (uint32_t)s.out[k + 2], (uint32_t)s.out[k + 3]},
+                                    reinterpret_cast<u32x4 *>(a.ids + base + k));
     }
     const int k = head + body + tid;
     if (k < nst) a.ids[base + k] = out_id(a.id_map, s.out[k]);
