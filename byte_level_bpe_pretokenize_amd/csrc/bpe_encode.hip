@@ -2086,14 +2086,13 @@ __global__ void __launch_bounds__(EWG) k_emit(EncodeArgs a) {
   const int32_t *res = a.res + c * kMissSpan;
   // loads that need nothing else first: the first round's pv values (pv has
   // room for kChunk entries, so this reads inside it whatever the count), and
-  // the first pre-token of the documents that start here.  pv (read once
-  // here) and the IDs (written once) are streamed with non-temporal
-  // accesses.
+  // the first pre-token of the documents that start here.  The IDs (written
+  // once) are streamed out with non-temporal stores.
   const uint8_t *cntk = a.cntk + c * kChunk;
   int32_t v0[kEmitPasses], n0[kEmitPasses];
 #pragma unroll
   for (int j = 0; j < kEmitPasses; ++j) {
-    v0[j] = __builtin_nontemporal_load(&pv[j * EWG + tid]);
+    v0[j] = pv[j * EWG + tid];
     n0[j] = cntk[j * EWG + tid];
   }
   const int64_t dlo = a.doc_rng[2 * c], dhi = a.doc_rng[2 * c + 1];
