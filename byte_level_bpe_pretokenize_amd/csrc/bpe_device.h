@@ -147,56 +147,6 @@ __device__ T block_excl_sum(T v, T *red, T *total) {
   return wp + inc - v;
 }
 
-template <int NT>
-__device__ int32_t block_min(int32_t v, int32_t *red) {
-  v = wave_min(v);
-  if (lane_id() == 0) red[wave_id()] = v;
-  __syncthreads();
-  int32_t m = red[0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) m = min(m, red[w]);
-  __syncthreads();
-  return m;
-}
-
-template <int NT>
-__device__ int32_t block_max(int32_t v, int32_t *red) {
-  v = wave_max(v);
-  if (lane_id() == 0) red[wave_id()] = v;
-  __syncthreads();
-  int32_t m = red[0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) m = max(m, red[w]);
-  __syncthreads();
-  return m;
-}
-
-// Exclusive running maximum over the workgroup (identity `lowest`);
-// *total gets the maximum of all values.
-template <int NT>
-__device__ int64_t block_excl_max64(int64_t v, int64_t lowest, int64_t *red, int64_t *total) {
-  const int lane = lane_id();
-  int64_t inc = v;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t o = __shfl_up(inc, d, 64);
-    if (lane >= d) inc = max(inc, o);
-  }
-  int64_t ex = __shfl_up(inc, 1, 64);
-  if (lane == 0) ex = lowest;
-  if (lane == 63) red[wave_id()] = inc;
-  __syncthreads();
-  int64_t wp = lowest, tot = lowest;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int64_t x = red[w];
-    if (w < wave_id()) wp = max(wp, x);
-    tot = max(tot, x);
-  }
-  __syncthreads();
-  *total = tot;
-  return max(wp, ex);
-}
-
 // First index i in [0, n) with a[i] >= key (n if none), for a sorted array.
 // Called by all 64 lanes of one wave; 64-way split per step.  For an array
 // that is not sorted the result is still in [0, n].

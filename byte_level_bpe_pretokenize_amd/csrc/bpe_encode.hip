@@ -94,8 +94,6 @@ __device__ __forceinline__ int bucket_of(int len, bool over) {
 template <int NT>
 struct Red {
   int32_t red[NT / 64 + 4];
-  int64_t red64[NT / 64 + 4];
-  uint8_t mflag[NT];
 };
 
 // ---- merge loops ----------------------------------------------------------
@@ -236,87 +234,101 @@ __device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, cons
   return emit_alive<W>(S, alive, out);
 }
 
-// The same rounds with the whole workgroup (NT threads) on Y[0..n), RK
-// scratch (global, position-indexed).  The lowest rank r is a workgroup
-// minimum; runs of consecutive pairs with rank r (only possible for a pair
-// (x, x)) merge at even offsets from the run start; survivors are compacted
-// in place tile by tile.  Returns the final symbol count.
-template <int NT>
-__device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, const RankTable &tab,
-                            const int32_t *__restrict__ pair_rank, Red<NT> &s) {
-  constexpr int PER = 4;
-  constexpr int TILE = NT * PER;
-  const int tid = threadIdx.x;
-  for (int64_t i = tid; i < n; i += NT)
+// The rounds of lds_merge (multi-rank rounds with window radius D; D == 0:
+// the lowest rank of the whole pre-token per round) for a pre-token longer
+// than the LDS path takes, by one wave on Y[0..n) and RK (global,
+// position-indexed), in place.  Each round:
+//  1. a pair that is the lowest within D positions on each side gets the
+//     sign bit of its RK entry (the windows read RK without that bit, and
+//     each step's reads come before its writes);
+//  2. merge flags by the run rule (a run of one pair (x, x) merges at even
+//     offsets from its first pair, and only if that first pair is a lowest
+//     pair) and compaction, 64 positions per step: every read of a step
+//     comes before its writes, which land at or before its positions;
+//  3. the pairs that touch a new symbol (RK == -1) are probed.
+// Returns the final symbol count.
+__device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, int D, const RankTable &tab,
+                            const int32_t *__restrict__ pair_rank) {
+  constexpr int32_t kRankBits = 0x7FFFFFFF;  // RK without the candidate bit
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1;
+  for (int64_t i = lane; i < n; i += MWG)
     RK[i] = (i + 1 < n) ? pair_rank[(Y[i] << 8) | Y[i + 1]] : kRankInf;
   __syncthreads();
-  for (;;) {
-    int32_t r = kRankInf;
-    for (int64_t i = tid; i < n; i += NT) r = min(r, RK[i]);
-    r = block_min<NT>(r, s.red);
-    if (r == kRankInf) break;
-    const int32_t z = 256 + r;
-    int64_t out_base = 0;
-    int64_t anchor = -1;  // last position before the tile whose pair rank is not r
-    bool prev_m = false;  // the pair just before the tile merged
-    for (int64_t t0 = 0; t0 < n; t0 += TILE) {
-      const int64_t p0 = t0 + PER * (int64_t)tid;
-      int32_t y[PER], rk[PER];
-      uint32_t f = 0;
-      int64_t my_anchor = -1;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int64_t p = p0 + j;
-        const bool v = p < n;
-        rk[j] = v ? RK[p] : kRankInf;
-        y[j] = v ? Y[p] : 0;
-        if (v && rk[j] == r) f |= 1u << j;
-        else my_anchor = p;
-      }
-      int64_t tile_anchor;
-      int64_t za = block_excl_max64<NT>(my_anchor, -1, s.red64, &tile_anchor);
-      za = max(za, anchor);
-      uint32_t m = 0;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int64_t p = p0 + j;
-        if (!((f >> j) & 1u)) za = p;
-        else if (((p - 1 - za) & 1) == 0) m |= 1u << j;
-      }
-      s.mflag[tid] = (m >> (PER - 1)) & 1u;
-      __syncthreads();
-      const uint32_t mprev = tid ? (uint32_t)s.mflag[tid - 1] : (uint32_t)prev_m;
-      const bool tile_last_m = s.mflag[NT - 1] != 0;
-      // position p is consumed when the pair at p - 1 merged
-      const uint32_t consumed = ((m << 1) | mprev) & ((1u << PER) - 1u);
-      uint32_t keep = 0;
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (p0 + j < n && !((consumed >> j) & 1u)) keep |= 1u << j;
-      int tile_kept;
-      const int kex = block_excl_sum<int, NT>(__popc(keep), s.red, &tile_kept);
-      int64_t o = out_base + kex;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if ((keep >> j) & 1u) {
-          Y[o] = ((m >> j) & 1u) ? z : y[j];
-          RK[o] = rk[j];
-          ++o;
-        }
-      }
-      anchor = max(anchor, tile_anchor);
-      prev_m = tile_last_m;
-      out_base += tile_kept;
-      __syncthreads();
+  while (n > 1) {
+    int32_t gmin = kRankInf;
+    if (D == 0) {
+      for (int64_t i = lane; i < n; i += MWG) gmin = min(gmin, RK[i]);
+      gmin = wave_min(gmin);
+      if (gmin == kRankInf) break;
     }
-    n = out_base;
-    for (int64_t i = tid; i < n; i += NT) {
-      if (i + 1 < n) {
-        const int32_t l = Y[i], rr = Y[i + 1];
-        if (l == z || rr == z) RK[i] = rank_of(tab, l, rr);
-      } else {
-        RK[i] = kRankInf;
+    // 1. the lowest pairs of their windows
+    for (int64_t i0 = 0; i0 < n; i0 += MWG) {
+      const int64_t i = i0 + lane;
+      if (i >= n) continue;
+      const int32_t r = RK[i] & kRankBits;
+      int32_t w = gmin;
+      if (D > 0) {
+        w = r;
+        const int64_t j1 = min(i + D, n - 1);
+        for (int64_t j = max(i - D, (int64_t)0); j <= j1; ++j) w = min(w, RK[j] & kRankBits);
       }
+      if (r < kRankInf && r == w) RK[i] = r | (int32_t)0x80000000;
+    }
+    __syncthreads();
+    // 2. merge flags and compaction (the carries: the run start in force,
+    //    its candidate bit, whether the position before the step merged, and
+    //    its rank)
+    int64_t run = 0, out = 0;
+    bool run_c = false, prevm = false, any = false;
+    int32_t prevr = kRankInf;
+    for (int64_t i0 = 0; i0 < n; i0 += MWG) {
+      const int64_t i = i0 + lane;
+      const bool in = i < n;
+      const int32_t raw = in ? RK[i] : kRankInf;
+      const int32_t y = in ? Y[i] : 0;
+      const int32_t r = raw & kRankBits;
+      const bool c = in && raw < 0;
+      const uint64_t cm = __ballot(c);
+      const int32_t rl = wave_shift_up1(r, prevr);
+      const bool b = in && (i == 0 || rl != r);
+      int64_t st = i;
+      bool cs = c;
+      if (__ballot(in && !b) != 0) {
+        const int sl = wave_incl_max(b ? lane : -1);  // the step's last run start at or before
+        st = sl >= 0 ? i0 + sl : run;
+        cs = sl >= 0 ? ((cm >> sl) & 1u) != 0 : run_c;
+      }
+      const bool m = c && cs && ((i - st) & 1) == 0;
+      const uint64_t bm = __ballot(m);
+      const bool cons = lane == 0 ? prevm : ((bm >> (lane - 1)) & 1u) != 0;
+      const bool k = in && !cons;
+      const uint64_t bk = __ballot(k);
+      if (k) {
+        const int64_t o = out + __popcll(bk & below);
+        Y[o] = m ? 256 + r : y;
+        RK[o] = m ? -1 : r;
+      }
+      any |= bm != 0;
+      out += __popcll(bk);
+      prevm = ((bm >> 63) & 1u) != 0;
+      prevr = lane_value(r, 63);
+      run = lane_value(st, 63);
+      run_c = lane_value((int32_t)cs, 63) != 0;
+    }
+    __syncthreads();
+    if (!any) break;
+    n = out;
+    // 3. ranks of the pairs that touch a new symbol
+    for (int64_t i0 = 0; i0 < n; i0 += MWG) {
+      const int64_t i = i0 + lane;
+      if (i >= n) continue;
+      const int32_t r = RK[i];
+      const int32_t rn = i + 1 < n ? RK[i + 1] : 0;
+      int32_t v = r;
+      if (i + 1 >= n) v = kRankInf;
+      else if (r == -1 || rn == -1) v = rank_of(tab, (uint32_t)Y[i], (uint32_t)Y[i + 1]);
+      RK[i] = v;
     }
     __syncthreads();
   }
@@ -1009,7 +1021,6 @@ constexpr int kMergeWaves = 4;  // waves per merge workgroup, each on its own gr
 struct MergeShared {
   int32_t meta[kGroup][kMetaInts];
   int32_t tok[kGroup];
-  Red<MWG> r;
 };
 
 __device__ void load_group(const EncodeArgs &a, MergeShared &s, int64_t cg, int nf) {
@@ -1957,10 +1968,11 @@ struct LongGroupShared {
   LongShared L;
 };
 
-// Bucket 3 of the same groups: one wave per entry, in turn.  An entry of at
-// most kLdsLong bytes is merged in LDS (lds_merge) with the window radius of
-// its class; a longer one in place in the position-indexed gsym / grank
-// (wg_merge).  The tokens end in gsym at the entry's position; adds the
+// Bucket 3 of the same groups: one wave per entry, in turn.  An entry made
+// of few runs of one byte is merged on its runs; otherwise one of at most
+// kLdsLong bytes is merged in LDS (lds_merge) and a longer one in place in
+// the position-indexed gsym / grank (wg_merge), both with the window radius
+// of its class.  The tokens end in gsym at the entry's position; adds the
 // token counts to tot.
 __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
   __shared__ LongGroupShared s;
@@ -2003,7 +2015,9 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
       } else {
         for (int64_t p = gs + lane; p < ge; p += MWG) a.gsym[p] = a.bytes[p];
         __syncthreads();
-        nt = wg_merge<MWG>(a.gsym + gs, a.grank + gs, len, t, a.pair_rank, s.g.r);
+        uint32_t b = a.bytes[gs];
+        if (b == 0x20u) b = a.bytes[gs + 1];  // (len > kLdsLong)
+        nt = wg_merge(a.gsym + gs, a.grank + gs, len, a.win_d[byte_class(b)], t, a.pair_rank);
       }
       if (lane == 0) {
         a.mt[c * kMaxLong + q] = (int32_t)nt;
