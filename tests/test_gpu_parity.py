@@ -312,6 +312,32 @@ def test_long_pretokens_windowed_rounds(dev):
     assert st == 0 and np.array_equal(out, data)
 
 
+def test_long_pretokens_past_lds_limit(dev):
+    # pre-tokens above 2048 bytes that are not a few runs of one byte take
+    # the rounds on the position-indexed scratch: every class (random
+    # letters, with a leading space, multi-byte letters, digits, punctuation,
+    # whitespace), each with its own window radius, on two tables
+    rng = np.random.default_rng(47)
+    letters = [chr(c) for c in range(ord("a"), ord("z") + 1)]
+    wide = list("éüßжщ中文字节")
+    punct = list("!?.,;:-_()[]{}<>/|\\'\"@#$%^&*+=~`")
+    ws = ["\t", "\n", "\r", "\x0b", "\x0c", " "]
+    docs = []
+    for n in (2049, 3000, 7000):
+        docs.append("".join(rng.choice(letters, n)).encode())
+        docs.append((" " + "".join(rng.choice(letters[:4], n))).encode())
+        docs.append(rng.integers(48, 58, n).astype(np.uint8).tobytes())
+        docs.append("".join(rng.choice(punct, n)).encode())
+        docs.append(("x" + "".join(rng.choice(ws, n)) + "y").encode())
+    docs.append("".join(rng.choice(wide, 1500)).encode())  # 2-3 bytes per letter
+    data, off = batch_from_docs(docs)
+    for k in ("adversarial", "throughput"):
+        model, table = model_pair(k)
+        ids, ioff = check_encode(model, table, data, off)
+        out, _, st = gpu_decode(model, ids, ioff)
+        assert st == 0 and np.array_equal(out, data)
+
+
 def test_long_pretokens_out_of_order_table(dev):
     # a table whose ranks are not in creation order: one rank per round
     rng = np.random.default_rng(17)
