@@ -28,7 +28,8 @@ struct bpe_model {
   uint32_t *d_pair_filter = nullptr;  // [kPairFilterWords] bit set of the merges' pairs
   int n_cu = 1;                     // compute units of the device
   uint4 *d_words = nullptr;         // short word table (one uint4 per slot), or nullptr
-  uint32_t word_mask = 0;
+  uint8_t *d_word_disp = nullptr;   // its displacements, one per bucket of keys
+  uint32_t word_mask = 0, word_dshift = 32;
   uint4 *d_lwords = nullptr;        // long word table (two uint4 per slot), or nullptr
   uint32_t lword_mask = 0, lword_seed = 0;
   uint32_t word_seed = 0;
@@ -93,6 +94,7 @@ void free_model(bpe_model *m) {
   if (m->d_pair_rank) (void)hipFree(m->d_pair_rank);
   if (m->d_pair_filter) (void)hipFree(m->d_pair_filter);
   if (m->d_words) (void)hipFree(m->d_words);
+  if (m->d_word_disp) (void)hipFree(m->d_word_disp);
   if (m->d_lwords) (void)hipFree(m->d_lwords);
   if (m->d_exp_off) (void)hipFree(m->d_exp_off);
   if (m->d_exp_bytes) (void)hipFree(m->d_exp_bytes);
@@ -254,8 +256,10 @@ int enqueue_encode(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
   a.n_cu = model->n_cu;
   a.lgroup = 1;  // the launch picks the merge kernels' group size
   a.words = words ? model->d_words : nullptr;
+  a.word_disp = model->d_word_disp;
   a.word_mask = model->word_mask;
   a.word_seed = model->word_seed;
+  a.word_dshift = model->word_dshift;
   a.lwords = words ? model->d_lwords : nullptr;
   a.lword_mask = model->lword_mask;
   a.lword_seed = model->lword_seed;
@@ -358,6 +362,49 @@ bool place_words(const std::vector<uint32_t> &h, uint32_t mask, std::vector<int3
   return true;
 }
 
+// Displacement placement for keys with hashes h and steps st (the short
+// table): the keys are grouped by h >> (32 - dbits); the largest groups
+// first, each takes the first displacement d < 256 under which all its keys
+// land on distinct free slots short_slot(h, d, st, mask).  at[slot] = key or
+// -1, disp[group] = d.  False if some group found no displacement.
+bool place_displaced(const std::vector<uint32_t> &h, const std::vector<uint32_t> &st,
+                     uint32_t mask, int dbits, std::vector<int32_t> &at,
+                     std::vector<uint8_t> &disp) {
+  const size_t nb = (size_t)1 << dbits;
+  at.assign((size_t)mask + 1, -1);
+  disp.assign(nb, 0);
+  std::vector<std::vector<int32_t>> group(nb);
+  for (int32_t e = 0; e < (int32_t)h.size(); ++e) group[h[(size_t)e] >> (32 - dbits)].push_back(e);
+  std::vector<uint32_t> order(nb);
+  for (size_t b = 0; b < nb; ++b) order[b] = (uint32_t)b;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](uint32_t x, uint32_t y) { return group[x].size() > group[y].size(); });
+  std::vector<uint32_t> sl;
+  for (uint32_t b : order) {
+    const std::vector<int32_t> &g = group[b];
+    if (g.empty()) break;
+    bool ok = false;
+    for (uint32_t d = 0; d < 256 && !ok; ++d) {
+      sl.clear();
+      ok = true;
+      for (int32_t e : g) {
+        const uint32_t s = short_slot(h[(size_t)e], d, st[(size_t)e], mask);
+        if (at[s] >= 0 || std::find(sl.begin(), sl.end(), s) != sl.end()) {
+          ok = false;
+          break;
+        }
+        sl.push_back(s);
+      }
+      if (ok) {
+        for (size_t i = 0; i < g.size(); ++i) at[sl[i]] = g[i];
+        disp[b] = (uint8_t)d;
+      }
+    }
+    if (!ok) return false;
+  }
+  return true;
+}
+
 // The word table: every symbol whose byte expansion (2..kWordMax bytes)
 // encodes to exactly that symbol.  The expansions are encoded on the device
 // by the same kernels, with the merge loop for every pre-token; the host only
@@ -440,14 +487,17 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
     const std::vector<std::array<uint32_t, 8>> &its = items[t];
     const int64_t n_keep = (int64_t)its.size();
     if (n_keep == 0) continue;
-    // capacity a power of two >= 2.5 entries; on failure another seed, then
-    // twice the capacity; after that without this table (its pre-tokens then
-    // run the merge loop, with the same result)
+    // capacity a power of two >= 2 entries (short table) or >= 2.5 (long
+    // table); on failure another seed, then twice the capacity; after that
+    // without this table (its pre-tokens then run the merge loop, with the
+    // same result)
     uint32_t mask = 255;
-    while ((int64_t)mask + 1 < 5 * n_keep / 2) mask = 2 * mask + 1;
+    while ((int64_t)mask + 1 < (t == 0 ? 2 * n_keep : 5 * n_keep / 2)) mask = 2 * mask + 1;
     std::vector<int32_t> at;
-    std::vector<uint32_t> hs((size_t)n_keep);
+    std::vector<uint8_t> disp;
+    std::vector<uint32_t> hs((size_t)n_keep), st((size_t)n_keep);
     uint32_t seed = 0;
+    int dbits = 0;
     bool placed = false;
     for (int attempt = 0; attempt < 8 && !placed; ++attempt) {
       seed = 0x9E3779B9u * (uint32_t)(attempt + 1);
@@ -456,15 +506,23 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
         const int len = (int)its[(size_t)e][0];
         hs[(size_t)e] = t == 0 ? short_mix(w[0], w[1], w[2], (uint32_t)len, seed)
                                : word_hash(w, len, seed);
+        st[(size_t)e] = short_step(w[0], w[1], w[2]);
       }
-      placed = place_words(hs, mask, at);
+      if (t == 0) {
+        dbits = 0;
+        while (((uint64_t)kShortSlotsPerDisp << dbits) < (uint64_t)mask + 1) ++dbits;
+        placed = place_displaced(hs, st, mask, dbits, at, disp);
+      } else {
+        placed = place_words(hs, mask, at);
+      }
       if (!placed && attempt % 2 == 1) mask = 2 * mask + 1;
     }
     if (!placed) continue;
     std::vector<uint32_t> flag((size_t)mask + 1, 0u);
-    for (uint32_t i = 0; i <= mask; ++i)
-      if (at[i] >= 0 && word_slot0(hs[(size_t)at[i]], mask) != i)
-        flag[word_slot0(hs[(size_t)at[i]], mask)] = kWordFlag;
+    if (t == 1)
+      for (uint32_t i = 0; i <= mask; ++i)
+        if (at[i] >= 0 && word_slot0(hs[(size_t)at[i]], mask) != i)
+          flag[word_slot0(hs[(size_t)at[i]], mask)] = kWordFlag;
     const int words_per_slot = t == 0 ? 4 : 8;
     std::vector<uint32_t> slots((size_t)words_per_slot * ((size_t)mask + 1), 0u);
     for (uint32_t i = 0; i <= mask; ++i) {
@@ -491,8 +549,11 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
     rc = upload(reinterpret_cast<uint32_t **>(dst), slots.data(), slots.size(), stream);
     if (rc != BPE_OK) return rc;
     if (t == 0) {
+      rc = upload(&m->d_word_disp, disp.data(), disp.size(), stream);
+      if (rc != BPE_OK) return rc;
       m->word_mask = mask;
       m->word_seed = seed;
+      m->word_dshift = (uint32_t)(32 - dbits);
     } else {
       m->lword_mask = mask;
       m->lword_seed = seed;

@@ -522,20 +522,18 @@ __device__ __forceinline__ void short_words(const FindShared &s, int st, int len
 }
 
 // Symbol of a pre-token of 2..kShortMax bytes (words w0..w2) in the short
-// word table, or -1.
+// word table, or -1: the key's bucket displacement, then its one slot (no
+// branch: every lane of a wave takes the same two loads).
 __device__ __forceinline__ int32_t short_lookup(const EncodeArgs &a, uint32_t w0, uint32_t w1,
                                                 uint32_t w2, int len) {
   const uint32_t x = short_mix(w0, w1, w2, (uint32_t)len, a.word_seed);
+  const uint32_t d = a.word_disp[x >> a.word_dshift];
+  const u32x4 e = reinterpret_cast<const u32x4 *>(
+      a.words)[short_slot(x, d, short_step(w0, w1, w2), a.word_mask)];
   const uint32_t tl = (uint32_t)len << 21;
-  const u32x4 *tab = reinterpret_cast<const u32x4 *>(a.words);
-  u32x4 e = tab[word_slot0(x, a.word_mask)];
-  if (((e.x ^ w0) | (e.y ^ w1) | (e.z ^ w2) | ((e.w ^ tl) & (0xFu << 21))) == 0)
-    return (int32_t)(e.w & kWordSymMask);
-  if (!(e.w & kWordFlag)) return -1;
-  e = tab[word_slot1(x, a.word_mask)];
-  if (((e.x ^ w0) | (e.y ^ w1) | (e.z ^ w2) | ((e.w ^ tl) & (0xFu << 21))) == 0)
-    return (int32_t)(e.w & kWordSymMask);
-  return -1;
+  return ((e.x ^ w0) | (e.y ^ w1) | (e.z ^ w2) | ((e.w ^ tl) & (0xFu << 21))) == 0
+             ? (int32_t)(e.w & kWordSymMask)
+             : -1;
 }
 
 // Symbol of a pre-token of kShortMax + 1..kWordMax bytes in the long word

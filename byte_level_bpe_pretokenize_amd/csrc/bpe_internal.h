@@ -93,20 +93,23 @@ __host__ __device__ inline uint32_t pair_bucket1(uint32_t x, uint32_t mask) {
 // Read-only tables built at load time ("Hugging Face Tokenizers v1", section
 // "Word caching": a pre-token seen as a whole skips the merge loop): a
 // pre-token whose bytes equal the expansion of symbol s (2..kWordMax bytes),
-// where encoding that expansion yields exactly [s], encodes to [s].  Both are
-// two-choice cuckoo tables with one slot per bucket: an entry sits in its
-// first or its second slot, and a flag in the first slot says that some
-// entry whose first slot it is sits in its second; a lookup loads the first
-// slot, and the second only when the key is not in the first and the flag is
-// set.  Keys are the bytes as little-endian words, zero padded.
+// where encoding that expansion yields exactly [s], encodes to [s].  Keys are
+// the bytes as little-endian words, zero padded.
 //
-// Short table (2..kShortMax bytes): 16-byte slots {w0, w1, w2, meta},
-// meta = symbol | len << 21 | flag << 31; an empty slot is all zero (its len
-// field matches no key).
+// Short table (2..kShortMax bytes): one probe per lookup.  The keys are
+// grouped by the top bits of their hash h into buckets of about four; each
+// bucket has a one-byte displacement d, chosen at load so that every key of
+// the bucket lands on its own free slot short_slot(h, d, step) with step an
+// odd value from the key's words (keys with equal hashes still part).  The
+// table has at least two slots per key.  16-byte slots {w0, w1, w2, symbol |
+// len << 21}; an empty slot is all zero (its len field matches no key).
 //
-// Long table (kShortMax + 1..kWordMax bytes): 32-byte slots
-// {tag, symbol | flag << 31, w0, w1}, {w2, w3, w4, w5}, tag = (h & ~0xff) |
-// len (0 = empty).
+// Long table (kShortMax + 1..kWordMax bytes): a two-choice cuckoo table with
+// one slot per bucket: an entry sits in its first or its second slot, and a
+// flag in the first slot says that some entry whose first slot it is sits in
+// its second; a lookup loads the first slot, and the second only when the
+// key is not in the first and the flag is set.  32-byte slots {tag, symbol |
+// flag << 31, w0, w1}, {w2, w3, w4, w5}, tag = (h & ~0xff) | len (0 = empty).
 constexpr int kShortMax = 12;
 constexpr int kWordMax = 24;
 constexpr int kWordWords = kWordMax / 4;
@@ -120,6 +123,19 @@ __host__ __device__ inline uint32_t short_mix(uint32_t w0, uint32_t w1, uint32_t
   const uint32_t p2 = (w1 >> 16) | (w2 << 16);
   return mix32(mul24(w0 ^ seed, 0x9E3779u) ^ mul24(p1 ^ seed, 0x85EBCBu) ^
                mul24(p2 ^ seed, 0xC2B2AFu) ^ mul24(w2 >> 8, 0x27D4EBu) ^ (len << 26));
+}
+
+// The short table's slots per displacement (about four keys per bucket at
+// two slots per key), the step of a key (odd, below 2^24), and its slot for
+// displacement d < 256 (the product stays below 2^32: one 24-bit
+// multiply-add on the device).
+constexpr uint32_t kShortSlotsPerDisp = 8;
+__host__ __device__ inline uint32_t short_step(uint32_t w0, uint32_t w1, uint32_t w2) {
+  return (mul24(w1 ^ (w2 << 7) ^ (w0 >> 9), 0x27D4EBu) >> 8) | 1u;
+}
+__host__ __device__ inline uint32_t short_slot(uint32_t h, uint32_t d, uint32_t step,
+                                               uint32_t mask) {
+  return (d * step + h) & mask;
 }
 
 __host__ __device__ inline uint32_t word_hash(const uint32_t *w, int len, uint32_t seed) {
@@ -331,8 +347,10 @@ struct EncodeArgs {
   int n_cu;                  // compute units (workgroups of the persistent merge kernel)
   int lgroup;                // chunks per lane-merge group (set by the launch)
   const uint4 *words;        // short word table (one uint4 per slot); nullptr = none
+  const uint8_t *word_disp;  // its displacement per bucket of keys (hash >> word_dshift)
   uint32_t word_mask;        // slots - 1
   uint32_t word_seed;
+  uint32_t word_dshift;
   const uint4 *lwords;       // long word table (two uint4 per slot); nullptr = none
   uint32_t lword_mask;
   uint32_t lword_seed;
