@@ -506,7 +506,7 @@ int build_word_table(bpe_model *m, const std::vector<int64_t> &exp_off,
         const int len = (int)its[(size_t)e][0];
         hs[(size_t)e] = t == 0 ? short_mix(w[0], w[1], w[2], (uint32_t)len, seed)
                                : word_hash(w, len, seed);
-        st[(size_t)e] = short_step(w[0], w[1], w[2]);
+        if (t == 0) st[(size_t)e] = short_step(w[0], w[1], w[2]);
       }
       if (t == 0) {
         dbits = 0;
