@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbpe.so")
 SOURCES = [os.path.join(CSRC, f)
            for f in ("bpe_encode.hip", "bpe_decode.hip", "bpe_train.hip", "bpe_noalloc.hip",
-                     "bpe_api.cpp", "bpe_text.cpp")]
+                     "bpe_api.cpp", "bpe_tables.cpp", "bpe_text.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

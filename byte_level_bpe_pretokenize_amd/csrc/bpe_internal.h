@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 struct bpe_model;
 
 namespace bpe {
@@ -16,6 +18,26 @@ int encode_checked(const bpe_model *model, const uint8_t *d_bytes, int64_t n_byt
                    void *hip_stream, bool timed);
 // The device a model was loaded on (-1 for NULL).
 int model_device(const bpe_model *model);
+
+// Host-side table placement (bpe_tables.cpp).
+// The rank table: keys in rank order (pair_key), buckets = mask + 1 of two
+// 64-bit slots {key << kSymBits | rank}, the kSlotFlag of a key's first
+// bucket set when the key sits in its second.
+bool build_rank_table(const std::vector<uint64_t> &keys, uint32_t mask, uint32_t seed,
+                      std::vector<uint64_t> &slots);
+// The long word table: a two-choice cuckoo placement of hashes h over mask + 1
+// slots (word_slot0, word_slot1); at[slot] = entry or -1.
+bool place_words(const std::vector<uint32_t> &h, uint32_t mask, std::vector<int32_t> &at);
+// The short word table: a displacement per bucket of keys (h >> (32 - dbits))
+// under which every key sits at short_slot(h, disp, st, mask), all distinct.
+bool place_displaced(const std::vector<uint32_t> &h, const std::vector<uint32_t> &st,
+                     uint32_t mask, int dbits, std::vector<int32_t> &at,
+                     std::vector<uint8_t> &disp);
+// Window radii of the long pre-tokens' rounds by class (0: one rank per
+// round); len[v] = bytes of symbol v, order = the symbols >= 256 with their
+// operands first.
+void window_radii(const int32_t *merges, int64_t R, const std::vector<int64_t> &len,
+                  const std::vector<int64_t> &order, int32_t win_d[4]);
 
 // ---- byte classes ---------------------------------------------------------
 // The fixed split rule's classes: letters (A-Z, a-z and every byte from 0x80

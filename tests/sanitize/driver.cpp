@@ -1,18 +1,23 @@
 // Host-code check under AddressSanitizer and UndefinedBehaviorSanitizer (CPU
-// only): the oracle (oracle/bpe_oracle.c) and the library's text-form parsers
-// (bpe_text.cpp) on seeded random tables and inputs, their error paths
-// included.  Built and run by tests/test_sanitizers.py; any report of either
-// sanitizer aborts with a non-zero status.
+// only): the oracle (oracle/bpe_oracle.c), the library's text-form parsers
+// (bpe_text.cpp) and its hash-table placement (bpe_tables.cpp) on seeded
+// random tables and inputs, their error paths included.  Every placed key
+// must be found by the rule the kernels probe with.  Built and run by
+// tests/test_sanitizers.py; any report of either sanitizer aborts with a
+// non-zero status.
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <random>
 #include <string>
+#include <unordered_set>
 #include <vector>
 
 #include "bpe.h"
+#include "bpe_internal.h"
 
 extern "C" {
 int64_t ora_split(const uint8_t *s, int64_t n, int64_t *starts);
@@ -67,7 +72,94 @@ static std::string sym_text(const std::vector<std::string> &exp, int32_t v) {
   return t;
 }
 
+// The word tables' and the rank table's placement: every key is found where
+// the kernels look for it (short table: its one slot; long table: its first
+// or second slot; rank table: its first bucket, or its second when the first
+// bucket's flag is set), and no slot holds two keys.
+static void check_tables() {
+  for (int n : {1, 7, 300, 5000, 40000}) {
+    uint32_t mask = 255;
+    while ((int64_t)mask + 1 < 2 * (int64_t)n) mask = 2 * mask + 1;
+    int dbits = 0;
+    while (((uint64_t)bpe::kShortSlotsPerDisp << dbits) < (uint64_t)mask + 1) ++dbits;
+    std::vector<uint32_t> h((size_t)n), st((size_t)n);
+    for (int i = 0; i < n; ++i) {
+      h[(size_t)i] = (uint32_t)rng();
+      st[(size_t)i] = bpe::short_step((uint32_t)rng(), (uint32_t)rng(), (uint32_t)rng());
+    }
+    std::vector<int32_t> at;
+    std::vector<uint8_t> disp;
+    CHECK(bpe::place_displaced(h, st, mask, dbits, at, disp));
+    CHECK(at.size() == (size_t)mask + 1 && disp.size() == (size_t)1 << dbits);
+    int64_t used = 0;
+    for (int32_t e : at) used += e >= 0;
+    CHECK(used == n);
+    for (int i = 0; i < n; ++i) {
+      const uint32_t d = disp[h[(size_t)i] >> (32 - dbits)];
+      CHECK(at[bpe::short_slot(h[(size_t)i], d, st[(size_t)i], mask)] == i);
+    }
+    // the long table's two choices, at 2.5 slots per key
+    uint32_t lmask = 255;
+    while ((int64_t)lmask + 1 < 5 * (int64_t)n / 2) lmask = 2 * lmask + 1;
+    CHECK(bpe::place_words(h, lmask, at));
+    used = 0;
+    for (int32_t e : at) used += e >= 0;
+    CHECK(used == n);
+    for (int i = 0; i < n; ++i)
+      CHECK(at[bpe::word_slot0(h[(size_t)i], lmask)] == i ||
+            at[bpe::word_slot1(h[(size_t)i], lmask)] == i);
+  }
+  // the rank table: distinct pair keys in rank order, at most half full
+  for (int n : {1, 100, 20000}) {
+    std::vector<uint64_t> keys;
+    std::unordered_set<uint64_t> seen;
+    while ((int)keys.size() < n) {
+      const uint32_t l = (uint32_t)(rng() % 70000), r = (uint32_t)(rng() % 70000);
+      const uint64_t k = bpe::pair_key(l, r);
+      if (seen.insert(k).second) keys.push_back(k);
+    }
+    uint32_t mask = 63;
+    while ((int64_t)mask + 1 < (int64_t)n) mask = 2 * mask + 1;
+    const uint32_t seed = 0x9E3779B9u;
+    std::vector<uint64_t> slots;
+    CHECK(bpe::build_rank_table(keys, mask, seed, slots));
+    for (int r = 0; r < n; ++r) {
+      const uint64_t k = keys[(size_t)r];
+      const uint32_t x = bpe::pair_mix((uint32_t)(k >> bpe::kSymBits),
+                                       (uint32_t)(k & ((1u << bpe::kSymBits) - 1)), seed);
+      auto find = [&](uint32_t b) {
+        for (int j = 0; j < 2; ++j) {
+          const uint64_t v = slots[2 * (size_t)b + j];
+          if (v != bpe::kEmptySlot && (v >> bpe::kSymBits) == k)
+            return (int64_t)(v & ((1u << 20) - 1));
+        }
+        return (int64_t)-1;
+      };
+      const uint32_t b0 = bpe::pair_bucket0(x, mask);
+      int64_t got = find(b0);
+      if (got < 0 && (slots[2 * (size_t)b0] & bpe::kSlotFlag)) got = find(bpe::pair_bucket1(x, mask));
+      CHECK(got == r);
+    }
+  }
+  // window radii: digits '1' '2' -> 256, (256, '3') -> 257 give the digit
+  // class radius 3 and the others 1; a merge that uses a later symbol
+  // gives 0 everywhere
+  {
+    const int32_t m[4] = {'1', '2', 256, '3'};
+    std::vector<int64_t> len(258, 1);
+    len[256] = 2;
+    len[257] = 3;
+    int32_t wd[4];
+    bpe::window_radii(m, 2, len, {256, 257}, wd);
+    CHECK(wd[bpe::kD] == 3 && wd[bpe::kL] == 1 && wd[bpe::kW] == 1 && wd[bpe::kP] == 1);
+    const int32_t bad[4] = {'1', 257, '2', '3'};
+    bpe::window_radii(bad, 2, len, {257, 256}, wd);
+    CHECK(wd[0] == 0 && wd[1] == 0 && wd[2] == 0 && wd[3] == 0);
+  }
+}
+
 int main() {
+  check_tables();
   for (int round = 0; round < 40; ++round) {
     // a table trained by the oracle on a random corpus
     std::vector<uint8_t> data;
