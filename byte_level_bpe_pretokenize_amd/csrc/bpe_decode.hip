@@ -33,36 +33,58 @@ __device__ __forceinline__ int32_t dec_sym(const DecodeArgs &a, int32_t id) {
   return (id >= 0 && id < a.vocab) ? id : -1;
 }
 
+// The symbols of DPT IDs (dec_sym): the map's loads unconditional (entry 0
+// for an ID outside it) and issued together, so that no lane is masked off
+// around them and no load waits on another.
+__device__ __forceinline__ void dec_syms(const DecodeArgs &a, const int32_t *id, int32_t *sym) {
+  if (a.inv_map) {
+    int32_t m[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) m[j] = a.inv_map[(id[j] >= 0 && id[j] < a.inv_size) ? id[j] : 0];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) sym[j] = (id[j] >= 0 && id[j] < a.inv_size) ? m[j] : -1;
+  } else {
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) sym[j] = (id[j] >= 0 && id[j] < a.vocab) ? id[j] : -1;
+  }
+}
+
 __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   __shared__ int64_t red64[DWG / 64];
   const int tid = threadIdx.x;
-  bool bad_off = false;
-  {
-    const int64_t per = a.doc_per;
-    const int64_t i0 = (int64_t)blockIdx.x * per;
-    for (int64_t i = i0 + tid; i < min(i0 + per, a.n_docs + 1); i += DWG) {
-      const int64_t v = a.id_off[i];
-      if (i == 0 && v != 0) bad_off = true;
-      if (i == a.n_docs && v != a.n_ids) bad_off = true;
-      if (i < a.n_docs && a.id_off[i + 1] < v) bad_off = true;
-    }
-  }
   const int64_t c = blockIdx.x;
   const int64_t i0 = c * kDecChunk;
   const int cnt = (int)min<int64_t>(kDecChunk, a.n_ids - i0);
   bool bad_id = false;
   int64_t mine = 0;
-  // consecutive threads read consecutive IDs
+  // consecutive threads read consecutive IDs; every load is unconditional
+  // (the chunk's last ID again past its end, symbol 0 for an ID with none),
+  // so that the loads of all DPT IDs are in flight together
+  int32_t id[DPT], sym[DPT], len[DPT];
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) id[j] = a.ids[i0 + min(j * DWG + tid, cnt - 1)];
+  dec_syms(a, id, sym);
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) len[j] = a.exp_len[max(sym[j], 0)];
 #pragma unroll
   for (int j = 0; j < DPT; ++j) {
-    const int k = j * DWG + tid;
-    if (k < cnt) {
-      const int32_t id = a.ids[i0 + k];
-      const int32_t sym = dec_sym(a, id);
-      // a reserved ID given as skip0 / skip1 decodes to no bytes (k_dec_write
-      // writes none for an ID with no symbol)
-      if (sym >= 0) mine += a.exp_len[sym];
-      else if (!((a.skip0 >= 0 && id == a.skip0) || (a.skip1 >= 0 && id == a.skip1))) bad_id = true;
+    if (j * DWG + tid >= cnt) continue;
+    // a reserved ID given as skip0 / skip1 decodes to no bytes (k_dec_write
+    // writes none for an ID with no symbol)
+    if (sym[j] >= 0) mine += len[j];
+    else if (!((a.skip0 >= 0 && id[j] == a.skip0) || (a.skip1 >= 0 && id[j] == a.skip1)))
+      bad_id = true;
+  }
+  // the ID offsets check, spread over the grid (after the loads above)
+  bool bad_off = false;
+  {
+    const int64_t per = a.doc_per;
+    const int64_t d0 = (int64_t)blockIdx.x * per;
+    for (int64_t i = d0 + tid; i < min(d0 + per, a.n_docs + 1); i += DWG) {
+      const int64_t v = a.id_off[i];
+      if (i == 0 && v != 0) bad_off = true;
+      if (i == a.n_docs && v != a.n_ids) bad_off = true;
+      if (i < a.n_docs && a.id_off[i + 1] < v) bad_off = true;
     }
   }
   int64_t total;
@@ -131,21 +153,31 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
   // bytes, all loads in flight together (lengths also to LDS for the
   // document offsets)
   const int k0 = tid * DPT;
-  int32_t sym[DPT], len[DPT];
+  int32_t id[DPT], sym[DPT], len[DPT];
   if (k0 + DPT <= cnt && ((reinterpret_cast<uintptr_t>(a.ids + i0 + k0) & 15u) == 0)) {
     // the thread's eight IDs in two 16-byte loads
     const int4 p = *reinterpret_cast<const int4 *>(a.ids + i0 + k0);
     const int4 q = *reinterpret_cast<const int4 *>(a.ids + i0 + k0 + 4);
-    const int32_t v[DPT] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int j = 0; j < DPT; ++j) sym[j] = dec_sym(a, v[j]);
+    id[0] = p.x, id[1] = p.y, id[2] = p.z, id[3] = p.w;
+    id[4] = q.x, id[5] = q.y, id[6] = q.z, id[7] = q.w;
   } else {
 #pragma unroll
-    for (int j = 0; j < DPT; ++j) sym[j] = k0 + j < cnt ? dec_sym(a, a.ids[i0 + k0 + j]) : -1;
+    for (int j = 0; j < DPT; ++j) id[j] = a.ids[i0 + min(k0 + j, cnt - 1)];
   }
+  dec_syms(a, id, sym);
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) len[j] = sym[j] >= 0 ? a.exp_len[sym[j]] : 0;
-  // (named values, not an array: an array of them ends up in scratch)
+  for (int j = 0; j < DPT; ++j)
+    if (k0 + j >= cnt) sym[j] = -1;
+  // (unconditional loads, symbol 0 for an ID with none: they stay in flight
+  // together)
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int32_t n = a.exp_len[max(sym[j], 0)];
+    len[j] = sym[j] >= 0 ? n : 0;
+  }
+  // (named values, not an array: an array of them ends up in scratch; these
+  // loads stay conditional: unconditional ones took the kernel past 128
+  // VGPRs, to three waves per SIMD)
   auto first16 = [&a](int32_t v) { return v >= 0 ? a.exp16[v] : uint4{0u, 0u, 0u, 0u}; };
   static_assert(DPT == 8, "eight IDs per thread");
   const uint4 b0 = first16(sym[0]), b1 = first16(sym[1]), b2 = first16(sym[2]),
