@@ -1044,12 +1044,19 @@ __device__ __forceinline__ bool lane_group(const EncodeArgs &a, int64_t q, LaneG
   G.cg = q * a.lgroup;
   if (G.cg >= a.n_chunks) return false;
   G.nf = (int)min<int64_t>(a.lgroup, a.n_chunks - G.cg);
+  // every count loaded (the group's last chunk again past its end), so that
+  // all the loads are in flight together
+#pragma unroll
+  for (int f = 0; f < kGroup; ++f) {
+    const int32_t *m = a.meta + kMetaInts * (G.cg + min(f, G.nf - 1));
+#pragma unroll
+    for (int b = 0; b < kBuckets; ++b) G.cnt[f][b] = m[(deduped(b) ? kMetaOwners : kMetaBucket) + b];
+  }
 #pragma unroll
   for (int f = 0; f < kGroup; ++f)
 #pragma unroll
     for (int b = 0; b < kBuckets; ++b)
-      G.cnt[f][b] = f < G.nf ? a.meta[kMetaInts * (G.cg + f) + (deduped(b) ? kMetaOwners : kMetaBucket) + b]
-                             : 0;
+      if (f >= G.nf) G.cnt[f][b] = 0;
   return true;
 }
 
