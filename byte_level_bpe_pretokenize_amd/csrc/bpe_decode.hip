@@ -4,7 +4,8 @@
 // expansion; the concatenation is the original text.  IDs are cut into
 // chunks of kDecChunk; three kernels, none of which waits on another
 // workgroup:
-//   k_dec_len    per chunk: the byte count of its IDs and its status bits
+//   k_dec_len    per chunk (two a workgroup): the byte count of its IDs and
+//                its status bits
 //                (an ID outside the vocabulary, bad document offsets).
 //   k_dec_scan   exclusive scan of the chunk byte counts within blocks of
 //                1024 chunks; k_dec_bscan the same over the blocks' counts,
@@ -49,29 +50,33 @@ __device__ __forceinline__ void dec_syms(const DecodeArgs &a, const int32_t *id,
   }
 }
 
+// kLenChunks chunks per workgroup: DPT IDs per thread and chunk, all loaded
+// together.
+constexpr int kLenChunks = 2;
 __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
-  __shared__ int64_t red64[DWG / 64];
+  constexpr int LPT = kLenChunks * DPT;  // IDs per thread: chunk j / DPT
   const int tid = threadIdx.x;
-  const int64_t c = blockIdx.x;
-  const int64_t i0 = c * kDecChunk;
-  const int cnt = (int)min<int64_t>(kDecChunk, a.n_ids - i0);
+  const int64_t c0 = (int64_t)blockIdx.x * kLenChunks;
+  const int64_t i0 = c0 * kDecChunk;
+  const int cnt = (int)min<int64_t>(kLenChunks * kDecChunk, a.n_ids - i0);
   bool bad_id = false;
-  int64_t mine = 0;
+  int64_t mine[kLenChunks] = {};
   // consecutive threads read consecutive IDs; every load is unconditional
-  // (the chunk's last ID again past its end, symbol 0 for an ID with none),
-  // so that the loads of all DPT IDs are in flight together
-  int32_t id[DPT], sym[DPT], len[DPT];
+  // (the workgroup's last ID again past its end, symbol 0 for an ID with
+  // none), so that the loads of all LPT IDs are in flight together
+  int32_t id[LPT], sym[LPT], len[LPT];
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) id[j] = a.ids[i0 + min(j * DWG + tid, cnt - 1)];
-  dec_syms(a, id, sym);
+  for (int j = 0; j < LPT; ++j) id[j] = a.ids[i0 + min(j * DWG + tid, cnt - 1)];
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) len[j] = a.exp_len[max(sym[j], 0)];
+  for (int f = 0; f < kLenChunks; ++f) dec_syms(a, id + f * DPT, sym + f * DPT);
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) {
+  for (int j = 0; j < LPT; ++j) len[j] = a.exp_len[max(sym[j], 0)];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
     if (j * DWG + tid >= cnt) continue;
     // a reserved ID given as skip0 / skip1 decodes to no bytes (k_dec_write
     // writes none for an ID with no symbol)
-    if (sym[j] >= 0) mine += len[j];
+    if (sym[j] >= 0) mine[j / DPT] += len[j];
     else if (!((a.skip0 >= 0 && id[j] == a.skip0) || (a.skip1 >= 0 && id[j] == a.skip1)))
       bad_id = true;
   }
@@ -79,28 +84,48 @@ __global__ void __launch_bounds__(DWG) k_dec_len(DecodeArgs a) {
   bool bad_off = false;
   {
     const int64_t per = a.doc_per;
-    const int64_t d0 = (int64_t)blockIdx.x * per;
-    for (int64_t i = d0 + tid; i < min(d0 + per, a.n_docs + 1); i += DWG) {
+    const int64_t d0 = c0 * per;
+    for (int64_t i = d0 + tid; i < min(d0 + kLenChunks * per, a.n_docs + 1); i += DWG) {
       const int64_t v = a.id_off[i];
       if (i == 0 && v != 0) bad_off = true;
       if (i == a.n_docs && v != a.n_ids) bad_off = true;
       if (i < a.n_docs && a.id_off[i + 1] < v) bad_off = true;
     }
   }
-  int64_t total;
-  (void)block_excl_sum<int64_t, DWG>(mine, red64, &total);
-  const int bits = (__syncthreads_or(bad_id) ? (int)BPE_STATUS_BAD_ID : 0) |
-                   (__syncthreads_or(bad_off) ? (int)BPE_STATUS_BAD_ID_OFFSETS : 0);
-  if (tid == 0) a.tot[c] = total | ((int64_t)bits << kCountBits);
-  // the first document whose IDs start at or after this chunk's (and, from
+  // per chunk: the wave totals (lane 63 of each inclusive sum) and the
+  // waves' status bits through LDS, one barrier
+  __shared__ int64_t wtot[DWG / 64][kLenChunks];
+  __shared__ int32_t wbits[DWG / 64];
+  const int wv = wave_id();
+  int64_t inc[kLenChunks];
+#pragma unroll
+  for (int f = 0; f < kLenChunks; ++f) inc[f] = wave_incl_sum(mine[f]);
+  const int bits = (__ballot(bad_id) ? (int)BPE_STATUS_BAD_ID : 0) |
+                   (__ballot(bad_off) ? (int)BPE_STATUS_BAD_ID_OFFSETS : 0);
+  if (lane_id() == 63) {
+#pragma unroll
+    for (int f = 0; f < kLenChunks; ++f) wtot[wv][f] = inc[f];
+    wbits[wv] = bits;
+  }
+  __syncthreads();
+  if (tid < kLenChunks && c0 + tid < a.n_chunks) {
+    int64_t t = 0;
+    int b = 0;
+#pragma unroll
+    for (int w = 0; w < DWG / 64; ++w) t += wtot[w][tid], b |= wbits[w];
+    a.tot[c0 + tid] = t | ((int64_t)(tid == 0 ? b : 0) << kCountBits);
+  }
+  // the first document whose IDs start at or after each chunk's (and, after
   // the last chunk, after the last ID): the documents that start in each
   // chunk.  Searched last: nothing above waits on it.
-  if (wave_id() == 0) {
-    const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, i0);
-    if (lane_id() == 0) a.dlo[c] = d;
-  } else if (wave_id() == 1 && c == a.n_chunks - 1) {
+  if (wv < kLenChunks) {
+    if (c0 + wv < a.n_chunks) {
+      const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, (c0 + wv) * kDecChunk);
+      if (lane_id() == 0) a.dlo[c0 + wv] = d;
+    }
+  } else if (wv == kLenChunks && c0 + kLenChunks >= a.n_chunks) {
     const int64_t d = wave_lower_bound(a.id_off, a.n_docs + 1, a.n_ids);
-    if (lane_id() == 0) a.dlo[c + 1] = d;
+    if (lane_id() == 0) a.dlo[a.n_chunks] = d;
   }
 }
 
@@ -131,7 +156,7 @@ __device__ __forceinline__ void stage_or16(uint32_t *stage32, int w, uint4 b, in
   if (nw > 4) atomicOr(d + 4, word(0u, b.w));
 }
 
-constexpr int kDecStage = 16384;  // output bytes a chunk may stage in LDS
+constexpr int kDecStage = 8192;   // output bytes a chunk may stage in LDS
 
 struct WriteShared {
   int32_t len[kDecChunk];
@@ -155,11 +180,9 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
   const int k0 = tid * DPT;
   int32_t id[DPT], sym[DPT], len[DPT];
   if (k0 + DPT <= cnt && ((reinterpret_cast<uintptr_t>(a.ids + i0 + k0) & 15u) == 0)) {
-    // the thread's eight IDs in two 16-byte loads
+    // the thread's four IDs in one 16-byte load
     const int4 p = *reinterpret_cast<const int4 *>(a.ids + i0 + k0);
-    const int4 q = *reinterpret_cast<const int4 *>(a.ids + i0 + k0 + 4);
     id[0] = p.x, id[1] = p.y, id[2] = p.z, id[3] = p.w;
-    id[4] = q.x, id[5] = q.y, id[6] = q.z, id[7] = q.w;
   } else {
 #pragma unroll
     for (int j = 0; j < DPT; ++j) id[j] = a.ids[i0 + min(k0 + j, cnt - 1)];
@@ -179,10 +202,9 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
   // loads stay conditional: unconditional ones took the kernel past 128
   // VGPRs, to three waves per SIMD)
   auto first16 = [&a](int32_t v) { return v >= 0 ? a.exp16[v] : uint4{0u, 0u, 0u, 0u}; };
-  static_assert(DPT == 8, "eight IDs per thread");
+  static_assert(DPT == 4, "four IDs per thread");
   const uint4 b0 = first16(sym[0]), b1 = first16(sym[1]), b2 = first16(sym[2]),
-              b3 = first16(sym[3]), b4 = first16(sym[4]), b5 = first16(sym[5]),
-              b6 = first16(sym[6]), b7 = first16(sym[7]);
+              b3 = first16(sym[3]);
   int64_t mine = 0;
 #pragma unroll
   for (int j = 0; j < DPT; ++j) {
@@ -208,10 +230,6 @@ __global__ void __launch_bounds__(DWG) k_dec_write(DecodeArgs a) {
     put(b1, len[1]);
     put(b2, len[2]);
     put(b3, len[3]);
-    put(b4, len[4]);
-    put(b5, len[5]);
-    put(b6, len[6]);
-    put(b7, len[7]);
     if (longer) {  // expansions of more than 16 bytes: up to 32 from the two
                    // 16-byte tables, longer ones byte by byte
       w = lead + (int)ex;
@@ -282,7 +300,7 @@ const char *const kDecStageNames[kDecStages] = {"k_dec_len", "k_dec_scan", "k_de
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t *ev) {
   const unsigned G = (unsigned)a.n_chunks;
   if (ev) (void)hipEventRecord(ev[0], stream);
-  hipLaunchKernelGGL(k_dec_len, dim3(G), dim3(DWG), 0, stream, a);
+  hipLaunchKernelGGL(k_dec_len, dim3((G + kLenChunks - 1) / kLenChunks), dim3(DWG), 0, stream, a);
   if (ev) (void)hipEventRecord(ev[1], stream);
   hipLaunchKernelGGL(k_dec_scan, dim3((G + kScanBlock - 1) / kScanBlock), dim3(kScanBlock), 0,
                      stream, a);

@@ -87,6 +87,25 @@ __device__ __forceinline__ int32_t wave_incl_sum(int32_t v) {
   return v;
 }
 
+// The same for 64-bit values: each DPP step moves both 32-bit halves, then
+// one 64-bit add.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int64_t dpp64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)v >> 32), CTRL,
+                                                            ROW_MASK, 0xF, false);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int64_t wave_incl_sum(int64_t v) {
+  v += dpp64<0x111, 0xF>(v);
+  v += dpp64<0x112, 0xF>(v);
+  v += dpp64<0x114, 0xF>(v);
+  v += dpp64<0x118, 0xF>(v);
+  v += dpp64<0x142, 0xA>(v);
+  v += dpp64<0x143, 0xC>(v);
+  return v;
+}
+
 // Lane l's value in every lane (l the same in every lane of the wave).
 __device__ __forceinline__ int32_t lane_value(int32_t v, int l) {
   return __builtin_amdgcn_readlane(v, l);

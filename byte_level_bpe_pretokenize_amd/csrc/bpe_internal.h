@@ -189,7 +189,7 @@ constexpr int kLaneMax = 32;         // longest pre-token one lane merges alone
 
 // ---- decode geometry ----------------------------------------------------
 constexpr int kDecThreads = 256;
-constexpr int kDecPerThread = 8;
+constexpr int kDecPerThread = 4;
 constexpr int kDecChunk = kDecThreads * kDecPerThread;  // IDs per workgroup
 
 inline int64_t enc_chunks(int64_t n_bytes) { return (n_bytes + kChunk - 1) / kChunk; }
@@ -433,7 +433,7 @@ struct DecodeArgs {
   int64_t *dlo;
   int32_t *status;
   int64_t n_chunks;
-  int64_t doc_per;           // document offsets checked per k_dec_len workgroup: ceil((n_docs + 1) / n_chunks)
+  int64_t doc_per;           // document offsets checked per chunk (k_dec_len): ceil((n_docs + 1) / n_chunks)
   int32_t skip0, skip1;      // reserved IDs that decode to no bytes (-1: none)
 };
 
