@@ -122,6 +122,12 @@ __device__ __forceinline__ int32_t wave_shift_up1(int32_t v, int32_t fill) {
   return __builtin_amdgcn_update_dpp(fill, v, 0x138, 0xF, 0xF, false);  // wave_shr:1
 }
 
+// Each lane gets the value of the lane above it, lane 63 gets fill (DPP
+// wave shift; every lane active).
+__device__ __forceinline__ int32_t wave_shift_down1(int32_t v, int32_t fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, 0x130, 0xF, 0xF, false);  // wave_shl:1
+}
+
 // Running maximum over the lanes (lane i gets the maximum of lanes 0..i),
 // every lane active: the same DPP steps as wave_incl_sum.
 __device__ __forceinline__ int32_t wave_incl_max(int32_t v) {

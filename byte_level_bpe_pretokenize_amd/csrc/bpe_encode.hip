@@ -1770,6 +1770,300 @@ __device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
   return n;
 }
 
+// ---- segmented rounds -----------------------------------------------------
+// The rounds of lds_merge for a window radius 1 <= D <= kRPad, with each
+// lane owning a contiguous segment of the symbols instead of every 64th
+// position.  A lane walks its own segment one symbol after another, so the
+// run rule and the compaction need no scan over the wave; only the segment
+// edges are exchanged, once per round:
+//  - the window of a symbol near an edge reads the neighbouring lane's
+//    ranks (every segment holds at least D symbols, so the window never
+//    reaches two lanes away);
+//  - a run of one pair that enters a segment from the left takes its start
+//    (and that start's window bit) from the nearest lane on the left with a
+//    run start, by a running maximum over the lanes;
+//  - a merge of a segment's last pair consumes the next segment's first
+//    symbol.
+// Segments compact in place; when one falls below D symbols, the symbols are
+// spread again through the entry's position-indexed scratch (gy, gr).
+// Lane l's segment sits at l * kSegStride in LDS (an odd stride: the lanes'
+// k-th symbols fall in different banks).
+
+constexpr int kSegCap = 32;              // symbols a lane holds
+constexpr int kSegStride = kSegCap + 1;  // LDS words from one lane's segment to the next
+constexpr int kSegShare = 16;            // fewest symbols per lane when spread (if n allows)
+constexpr int kSegFrom = 256;            // entries this long or longer take the segmented rounds
+
+__device__ __forceinline__ int seg_lanes(int n) { return min(MWG, max(1, n / kSegShare)); }
+
+// Lane l's share of n symbols over Ln lanes: [n l / Ln, n (l + 1) / Ln).
+__device__ __forceinline__ void seg_share(int n, int Ln, int lane, int &lo, int &len) {
+  lo = lane < Ln ? n * lane / Ln : n;
+  len = (lane < Ln ? n * (lane + 1) / Ln : n) - lo;
+}
+
+// The positions of m's lowest kSegBatch set bits, lowest first (-1 where m
+// has fewer); m loses them.
+constexpr int kSegBatch = 8;  // symbols a lane loads together; probes in flight per lane
+
+__device__ __forceinline__ void take_bits(uint32_t &m, int (&k)[kSegBatch]) {
+#pragma unroll
+  for (int g = 0; g < kSegBatch; ++g) {
+    k[g] = m ? __builtin_ctz(m) : -1;
+    m &= m - 1;
+  }
+}
+
+template <int D>
+__device__ int seg_merge(LongShared &LS, const uint8_t *__restrict__ bytes, int n,
+                         const RankTable &tab, const int32_t *__restrict__ pair_rank,
+                         int32_t *__restrict__ gy, int32_t *__restrict__ gr) {
+  static_assert(D >= 1 && D <= kRPad, "radius");
+  static_assert(sizeof(LongShared) >= 2 * MWG * kSegStride * sizeof(int32_t), "segments fit");
+  static_assert(MWG * kSegCap >= kLdsLong && MWG * kSegStride >= kLdsLong, "every entry fits");
+  static_assert(kSegCap % kSegBatch == 0, "whole batches");
+  int32_t *const Y = reinterpret_cast<int32_t *>(&LS);
+  int32_t *const R = Y + MWG * kSegStride;
+  const int lane = lane_id();
+  const int base = lane * kSegStride;
+  const int baseL = max(base - kSegStride, 0), baseR = min(base + kSegStride, (MWG - 1) * kSegStride);
+  int Ln = seg_lanes(n);
+  int lo, len;
+  seg_share(n, Ln, lane, lo, len);
+  // the bytes in position order (in R, as staging), then each lane's share
+  // into its segment, then the pairs' ranks by the byte-pair table
+#pragma unroll 8
+  for (int i = lane; i < n; i += MWG) R[i] = bytes[i];
+  __syncthreads();
+  const int32_t nb = lo + len < n ? R[lo + len] : 0;  // the byte after the segment
+  for (int c = 0; c < len; c += kSegBatch) {
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j)
+      if (c + j < len) Y[base + c + j] = R[lo + c + j];
+  }
+  __syncthreads();
+  for (int c = 0; c < len; c += kSegBatch) {
+    int32_t rk[kSegBatch];
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j) {
+      const int k = c + j;
+      // (bytes here; masked so that a slot past the segment indexes the table too)
+      const uint32_t b0 = (uint32_t)Y[base + min(k, kSegCap - 1)] & 0xFFu;
+      const uint32_t b1 = (k + 1 < len ? (uint32_t)Y[base + min(k + 1, kSegCap - 1)] : (uint32_t)nb) & 0xFFu;
+      rk[j] = pair_rank[(b0 << 8) | b1];
+    }
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j) {
+      const int k = c + j;
+      if (k < len) R[base + k] = lo + k + 1 < n ? rk[j] : kRankInf;
+    }
+  }
+  __syncthreads();
+  while (true) {
+    const int incl = wave_incl_sum(len);
+    const int P = incl - len;  // global index of the segment's first symbol
+    const int lenL = wave_shift_up1(len, 0);
+    const int lenR = wave_shift_down1(len, 0);
+    // rank of pair k of this segment, k in [-D, len + D) (before the round):
+    // an index always inside the arrays, and whether the value counts
+    auto rank_at = [&](int k) -> int32_t {
+      int idx;
+      bool ok;
+      if (k < 0) {
+        idx = baseL + max(lenL + k, 0);
+        ok = lane > 0;
+      } else if (k < len) {
+        idx = base + k;
+        ok = true;
+      } else {
+        idx = baseR + min(k - len, kSegCap - 1);
+        ok = k - len < lenR;
+      }
+      const int32_t v = R[idx];
+      return ok ? v : kRankInf;
+    };
+    // 1. window bits cm (bit k: pair k is the lowest within D on each side),
+    //    and the last run start kls in the segment (-1: none); kSegBatch
+    //    pairs at a time, their windows' ranks loaded together
+    const int32_t left1 = rank_at(-1);
+    const bool cont0 = lane > 0 && len > 0 && rank_at(0) == left1;  // a run enters from the left
+    uint32_t cm = 0;
+    int kls = -1;
+    // w[q]: rank of pair c - D + q; the first 2D carried over from the
+    // batch before
+    int32_t w[kSegBatch + 2 * D];
+#pragma unroll
+    for (int q = 0; q < 2 * D; ++q) w[q] = rank_at(q - D);
+    for (int c = 0; c < len; c += kSegBatch) {
+#pragma unroll
+      for (int j = 0; j < kSegBatch; ++j) w[2 * D + j] = rank_at(c + D + j);
+#pragma unroll
+      for (int j = 0; j < kSegBatch; ++j) {
+        const int k = c + j;
+        const int32_t x = w[D + j];
+        int32_t mn = x;
+#pragma unroll
+        for (int q = 0; q <= 2 * D; ++q) mn = min(mn, w[j + q]);
+        if (k < len) {
+          if (x < kRankInf && x == mn) cm |= 1u << k;
+          if (k == 0 ? !cont0 : x != w[D + j - 1]) kls = k;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 2 * D; ++q) w[q] = w[q + kSegBatch];
+    }
+    // 2. the run start in force at the segment's first symbol, from the
+    //    nearest lane on the left with a start: (global index << 1) | window bit
+    const int key = kls >= 0 ? ((P + kls) << 1) | (int)((cm >> kls) & 1u) : -1;
+    const int carried = wave_incl_max(wave_shift_up1(key, -1));
+    int st_last = carried >> 1, cst_last = carried & 1;
+    if (kls >= 0) st_last = P + kls, cst_last = (int)((cm >> kls) & 1u);
+    const bool m_last = len > 0 && ((cm >> (len - 1)) & 1u) && cst_last &&
+                        ((P + len - 1 - st_last) & 1) == 0;
+    const bool prevm = wave_shift_up1((int32_t)m_last, 0) != 0;  // my first symbol is consumed
+    // 3. merge flags and compaction in place, kSegBatch symbols loaded
+    //    together (the writes land at or before them); need: the pairs whose
+    //    rank the new symbols change (a new symbol's own pair and the one
+    //    before it)
+    int st = carried >> 1, cst = carried & 1;
+    bool pm = prevm, anym = false, first_new = false;
+    int32_t pr = left1;
+    int out = 0;
+    uint32_t need = 0;
+    for (int c = 0; c < len; c += kSegBatch) {
+      int32_t xr[kSegBatch], xy[kSegBatch];
+#pragma unroll
+      for (int j = 0; j < kSegBatch; ++j) {
+        xr[j] = R[base + c + j];
+        xy[j] = Y[base + c + j];
+      }
+#pragma unroll
+      for (int j = 0; j < kSegBatch; ++j) {
+        const int k = c + j;
+        if (k < len) {
+          const int32_t x = xr[j];
+          const int cb = (int)((cm >> k) & 1u);
+          if (k == 0 ? !cont0 : x != pr) st = P + k, cst = cb;
+          const bool m = cb && cst && ((P + k - st) & 1) == 0;
+          if (!pm) {
+            Y[base + out] = m ? 256 + x : xy[j];
+            R[base + out] = m ? -1 : x;
+            if (m) {
+              need |= 1u << out;
+              if (out > 0) need |= 1u << (out - 1);
+              else first_new = true;
+            }
+            ++out;
+          }
+          anym |= m;
+          pm = m;
+          pr = x;
+        }
+      }
+    }
+    if (__ballot(anym) == 0) break;
+    // the pair before a segment's new first symbol is the last of the lane
+    // on the left
+    if (wave_shift_down1((int32_t)first_new, 0) != 0 && out > 0) need |= 1u << (out - 1);
+    len = out;
+    n = lane_value(wave_incl_sum(len), MWG - 1);
+    __syncthreads();
+    // 4. spread again when a segment is too short for the windows; the new
+    //    symbols (rank -1) then mark the pairs to probe
+    if (__ballot(lane < Ln && len < (Ln > 1 ? D : 1)) != 0) {
+      const int Q = wave_incl_sum(len) - len;
+      for (int k = 0; k < len; ++k) {
+        gy[Q + k] = Y[base + k];
+        gr[Q + k] = R[base + k];
+      }
+      __syncthreads();
+      Ln = seg_lanes(n);
+      seg_share(n, Ln, lane, lo, len);
+      for (int k = 0; k < len; ++k) {
+        Y[base + k] = gy[lo + k];
+        R[base + k] = gr[lo + k];
+      }
+      __syncthreads();
+      need = 0;
+      const int32_t r0n = lane + 1 < Ln ? R[baseR] : kRankInf;
+      for (int k = 0; k < len; ++k) {
+        const int32_t rn = k + 1 < len ? R[base + k + 1] : r0n;
+        if (R[base + k] == -1 || rn == -1) need |= 1u << k;
+      }
+      __syncthreads();
+    }
+    // 5. ranks of the marked pairs, kSegBatch probes in flight per lane; the
+    //    next segment's first symbol is read before any lane rewrites it
+    //    (the barrier keeps the read ahead of the writes)
+    const int32_t ny0 = Y[baseR];
+    const bool glast = lane == Ln - 1;
+    if (glast && len > 0 && ((need >> (len - 1)) & 1u)) {
+      need &= ~(1u << (len - 1));
+      R[base + len - 1] = kRankInf;  // the last pair has no right symbol
+    }
+    __syncthreads();
+    while (__ballot(need != 0) != 0) {
+      int ks[kSegBatch];
+      take_bits(need, ks);
+      uint32_t xs[kSegBatch];
+      uint64_t kk[kSegBatch];
+      u64x2 bk[kSegBatch];
+      int32_t nv[kSegBatch];
+#pragma unroll
+      for (int g = 0; g < kSegBatch; ++g) {
+        const int k = max(ks[g], 0);
+        const uint32_t l = (uint32_t)Y[base + k];
+        const uint32_t rt = k + 1 < len ? (uint32_t)Y[base + min(k + 1, kSegCap - 1)] : (uint32_t)ny0;
+        kk[g] = pair_key(l, rt);
+        xs[g] = pair_mix(l, rt, tab.seed);
+      }
+#pragma unroll
+      for (int g = 0; g < kSegBatch; ++g)
+        bk[g] = ks[g] >= 0 ? tab.b[pair_bucket0(xs[g], tab.mask)] : u64x2{kEmptySlot, kEmptySlot};
+      uint32_t need2 = 0;
+#pragma unroll
+      for (int g = 0; g < kSegBatch; ++g) {
+        nv[g] = bucket_rank(bk[g], kk[g]);
+        if (ks[g] >= 0 && nv[g] == kRankInf && bucket_flag(bk[g])) need2 |= 1u << g;
+      }
+      if (need2) {
+#pragma unroll
+        for (int g = 0; g < kSegBatch; ++g)
+          if ((need2 >> g) & 1u) bk[g] = tab.b[pair_bucket1(xs[g], tab.mask)];
+#pragma unroll
+        for (int g = 0; g < kSegBatch; ++g)
+          if ((need2 >> g) & 1u) nv[g] = bucket_rank(bk[g], kk[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < kSegBatch; ++g)
+        if (ks[g] >= 0) R[base + ks[g]] = nv[g];
+    }
+    __syncthreads();
+  }
+  // the symbols in order, at the entry's positions: gathered in position
+  // order in R's memory, then stored by consecutive lanes
+  const int P = wave_incl_sum(len) - len;
+  for (int k = 0; k < len; ++k) R[P + k] = Y[base + k];
+  __syncthreads();
+#pragma unroll 8
+  for (int i = lane; i < n; i += MWG) gy[i] = R[i];
+  return n;
+}
+
+__device__ int seg_merge_d(LongShared &LS, const uint8_t *bytes, int n, int D, const RankTable &tab,
+                           const int32_t *pair_rank, int32_t *gy, int32_t *gr) {
+  switch (D) {
+    case 1: return seg_merge<1>(LS, bytes, n, tab, pair_rank, gy, gr);
+    case 2: return seg_merge<2>(LS, bytes, n, tab, pair_rank, gy, gr);
+    case 3: return seg_merge<3>(LS, bytes, n, tab, pair_rank, gy, gr);
+    case 4: return seg_merge<4>(LS, bytes, n, tab, pair_rank, gy, gr);
+    case 5: return seg_merge<5>(LS, bytes, n, tab, pair_rank, gy, gr);
+    case 6: return seg_merge<6>(LS, bytes, n, tab, pair_rank, gy, gr);
+    case 7: return seg_merge<7>(LS, bytes, n, tab, pair_rank, gy, gr);
+    default: return seg_merge<8>(LS, bytes, n, tab, pair_rank, gy, gr);
+  }
+}
+
 // ---- run-length rounds ----------------------------------------------------
 // A pre-token made of few runs of one repeated byte (a letter repeated
 // hundreds of times, say) is merged on its runs, (symbol, count), instead of
@@ -1968,6 +2262,16 @@ __device__ int64_t rle_expand(const RleView &V, int R, int32_t *out) {
   return p;
 }
 
+// The window radius of the entry at gs if the segmented rounds take it
+// (1 .. kRPad), else 0.  The class is the first byte's, or the letter's
+// after a leading space.
+__device__ __forceinline__ int seg_radius(const EncodeArgs &a, int64_t gs) {
+  uint32_t b = a.bytes[gs];
+  if (b == 0x20u) b = a.bytes[gs + 1];
+  const int D = a.win_d[byte_class(b)];
+  return D >= 1 && D <= kRPad ? D : 0;
+}
+
 struct LongGroupShared {
   MergeShared g;
   LongShared L;
@@ -1999,7 +2303,11 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
       const int64_t ge = me_over(e) ? wave_global_end(a, gs, c0 + WIN) : gs + me_len(e);
       const int64_t len = ge - gs;
       int64_t nt = -1;
-      {
+      // a first look at 64 bytes: more than 8 runs there rules out the
+      // run-length path for an entry that the LDS paths take
+      const int32_t hb = lane < len ? (int32_t)a.bytes[gs + lane] : -1;
+      const bool many = __popcll(__ballot(lane < len && hb != wave_shift_up1(hb, -1))) > 8;
+      if (!(many && len <= kLdsLong)) {
         // few long runs of one byte: merged on the runs
         const RleView V = rle_view(s.L);
         const int R = rle_build(V, a.bytes + gs, len);
@@ -2008,6 +2316,9 @@ __global__ void __launch_bounds__(MWG) k_merge_long(EncodeArgs a) {
       }
       if (nt >= 0) {
         // done
+      } else if (len >= kSegFrom && len <= kLdsLong && seg_radius(a, gs)) {
+        nt = seg_merge_d(s.L, a.bytes + gs, (int)len, seg_radius(a, gs), t, a.pair_rank,
+                         a.gsym + gs, a.grank + gs);
       } else if (len <= kLdsLong) {
 #pragma unroll 8
         for (int i = lane; i < len; i += MWG) s.L.y[i] = a.bytes[gs + i];

@@ -338,6 +338,43 @@ def test_long_pretokens_past_lds_limit(dev):
         assert st == 0 and np.array_equal(out, data)
 
 
+def test_segmented_rounds(dev):
+    # long pre-tokens of 256..2048 bytes with a window radius of 1..8 take the
+    # rounds in which each lane owns a segment of the symbols: runs of one pair
+    # that cross segment edges (random binary digits, digits in short runs),
+    # merges across edges, and the lengths at the limits of the path
+    rng = np.random.default_rng(59)
+    docs = []
+    for n in (255, 256, 257, 300, 640, 1023, 1024, 1025, 1500, 2047, 2048, 2049):
+        docs.append(rng.integers(48, 58, n).astype(np.uint8).tobytes())
+        docs.append(rng.integers(48, 50, n).astype(np.uint8).tobytes())
+        docs.append((48 + (rng.random(n) < 0.9)).astype(np.uint8).tobytes())
+        runs = np.repeat(rng.integers(48, 58, n), rng.integers(2, 8, n))[:n]
+        docs.append(runs.astype(np.uint8).tobytes())
+    data, off = batch_from_docs(docs)
+    model, table = model_pair("adversarial")
+    check_encode(model, table, data, off)
+
+
+def test_segmented_rounds_respread(dev):
+    # a table whose digit tokens reach 8 bytes (window radius 8): segments fall
+    # below the radius and the symbols are spread over the lanes again
+    merges = np.array([(48, 49), (50, 51), (52, 53), (54, 55), (256, 257), (258, 259),
+                       (260, 261), (56, 57), (57, 56), (48, 48)], dtype=np.int32)
+    model, table = Model(merges), O.Table(merges)
+    rng = np.random.default_rng(61)
+    docs = []
+    for n in (256, 700, 1337, 2048):
+        for _ in range(3):
+            parts = []
+            while sum(map(len, parts)) < n:
+                parts.append(b"01234567" if rng.random() < 0.8
+                             else rng.integers(48, 58, int(rng.integers(1, 4))).astype(np.uint8).tobytes())
+            docs.append(b"".join(parts)[:n])
+    data, off = batch_from_docs(docs)
+    check_encode(model, table, data, off)
+
+
 def test_long_pretokens_out_of_order_table(dev):
     # a table whose ranks are not in creation order: one rank per round
     rng = np.random.default_rng(17)
