@@ -138,13 +138,15 @@ constexpr int kWordWords = kWordMax / 4;
 constexpr uint32_t kWordFlag = 1u << 31;
 constexpr uint32_t kWordSymMask = (1u << 21) - 1;
 
-// Mix of a short key (w2:w1:w0 zero padded past len bytes), 24-bit pieces.
+// Mix of a short key (w2:w1:w0 zero padded past len bytes): its twelve
+// bytes as four 24-bit pieces, each times an odd constant, summed with the
+// length and the seed (24-bit multiply-adds on the device), then mixed.
 __host__ __device__ inline uint32_t short_mix(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t len,
                                               uint32_t seed) {
   const uint32_t p1 = (w0 >> 24) | (w1 << 8);
   const uint32_t p2 = (w1 >> 16) | (w2 << 16);
-  return mix32(mul24(w0 ^ seed, 0x9E3779u) ^ mul24(p1 ^ seed, 0x85EBCBu) ^
-               mul24(p2 ^ seed, 0xC2B2AFu) ^ mul24(w2 >> 8, 0x27D4EBu) ^ (len << 26));
+  return mix32(mul24(w0, 0x9E3779u) + mul24(p1, 0x85EBCBu) + mul24(p2, 0xC2B2AFu) +
+               mul24(w2 >> 8, 0x27D4EBu) + (len << 26) + seed);
 }
 
 // The short table's slots per displacement (about four keys per bucket at
