@@ -375,6 +375,24 @@ def test_segmented_rounds_respread(dev):
     check_encode(model, table, data, off)
 
 
+def test_segmented_rounds_letters_after_space(dev):
+    # a letter pre-token with its leading space (the class is the letter's),
+    # on a table whose letter tokens are at most 4 bytes; and punctuation and
+    # whitespace runs of radius 1 (no merges at all)
+    merges = np.array([(97, 98), (99, 100), (256, 257), (32, 97), (259, 98), (97, 97)],
+                      dtype=np.int32)
+    model, table = Model(merges), O.Table(merges)
+    rng = np.random.default_rng(67)
+    punct = np.frombuffer(b"!?.,;:-_()[]{}<>/|@#$%^&*+=~", dtype=np.uint8)
+    docs = []
+    for n in (255, 256, 300, 1000, 2047, 2048):
+        docs.append(b"x " + rng.integers(97, 101, n).astype(np.uint8).tobytes())
+        docs.append(rng.choice(punct, n).tobytes())
+        docs.append(b"x" + rng.choice(np.array([9, 10, 13], dtype=np.uint8), n).tobytes() + b"y")
+    data, off = batch_from_docs(docs)
+    check_encode(model, table, data, off)
+
+
 def test_long_pretokens_out_of_order_table(dev):
     # a table whose ranks are not in creation order: one rank per round
     rng = np.random.default_rng(17)
