@@ -247,7 +247,7 @@ __device__ int lane_merge(const uint32_t *w, const int len, LaneCols<W> &L, cons
 //     comes before its writes, which land at or before its positions;
 //  3. the pairs that touch a new symbol (RK == -1) are probed.
 // Returns the final symbol count.
-__device__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, int D, const RankTable &tab,
+__device__ __noinline__ int64_t wg_merge(int32_t *Y, int32_t *RK, int64_t n, int D, const RankTable &tab,
                             const int32_t *__restrict__ pair_rank) {
   constexpr int32_t kRankBits = 0x7FFFFFFF;  // RK without the candidate bit
   const int lane = lane_id();
@@ -1542,7 +1542,7 @@ __device__ __forceinline__ void lowest_in_window(LongShared &L, const int32_t *r
 // Position i belongs to lane i % 64; scans run 64 positions at a time with
 // a carry.  One wave does all the work, so LDS accesses stay in program
 // order and the arrays are rewritten in place.
-__device__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
+__device__ __noinline__ int lds_merge(LongShared &L, int n, int D, const RankTable &tab,
                          const int32_t *__restrict__ pair_rank) {
   const int lane = lane_id();
   const uint64_t below = (1ull << lane) - 1;
@@ -1802,13 +1802,16 @@ __device__ __forceinline__ void seg_share(int n, int Ln, int lane, int &lo, int 
   len = (lane < Ln ? n * (lane + 1) / Ln : n) - lo;
 }
 
-// The positions of m's lowest kSegBatch set bits, lowest first (-1 where m
+// The positions of m's lowest kSegProbe set bits, lowest first (-1 where m
 // has fewer); m loses them.
-constexpr int kSegBatch = 8;  // symbols a lane loads together; probes in flight per lane
+constexpr int kSegBatch = 8;  // symbols a lane loads together
+// probes in flight per lane: with 4, the kernel fits in 168 registers (3
+// waves per SIMD; LDS then allows 9 per CU); 8 took 243 (2 waves per SIMD)
+constexpr int kSegProbe = 4;
 
-__device__ __forceinline__ void take_bits(uint32_t &m, int (&k)[kSegBatch]) {
+__device__ __forceinline__ void take_bits(uint32_t &m, int (&k)[kSegProbe]) {
 #pragma unroll
-  for (int g = 0; g < kSegBatch; ++g) {
+  for (int g = 0; g < kSegProbe; ++g) {
     k[g] = m ? __builtin_ctz(m) : -1;
     m &= m - 1;
   }
@@ -1992,7 +1995,7 @@ __device__ int seg_merge(LongShared &LS, const uint8_t *__restrict__ bytes, int 
       }
       __syncthreads();
     }
-    // 5. ranks of the marked pairs, kSegBatch probes in flight per lane; the
+    // 5. ranks of the marked pairs, kSegProbe probes in flight per lane; the
     //    next segment's first symbol is read before any lane rewrites it
     //    (the barrier keeps the read ahead of the writes)
     const int32_t ny0 = Y[baseR];
@@ -2003,14 +2006,14 @@ __device__ int seg_merge(LongShared &LS, const uint8_t *__restrict__ bytes, int 
     }
     __syncthreads();
     while (__ballot(need != 0) != 0) {
-      int ks[kSegBatch];
+      int ks[kSegProbe];
       take_bits(need, ks);
-      uint32_t xs[kSegBatch];
-      uint64_t kk[kSegBatch];
-      u64x2 bk[kSegBatch];
-      int32_t nv[kSegBatch];
+      uint32_t xs[kSegProbe];
+      uint64_t kk[kSegProbe];
+      u64x2 bk[kSegProbe];
+      int32_t nv[kSegProbe];
 #pragma unroll
-      for (int g = 0; g < kSegBatch; ++g) {
+      for (int g = 0; g < kSegProbe; ++g) {
         const int k = max(ks[g], 0);
         const uint32_t l = (uint32_t)Y[base + k];
         const uint32_t rt = k + 1 < len ? (uint32_t)Y[base + min(k + 1, kSegCap - 1)] : (uint32_t)ny0;
@@ -2018,24 +2021,24 @@ __device__ int seg_merge(LongShared &LS, const uint8_t *__restrict__ bytes, int 
         xs[g] = pair_mix(l, rt, tab.seed);
       }
 #pragma unroll
-      for (int g = 0; g < kSegBatch; ++g)
+      for (int g = 0; g < kSegProbe; ++g)
         bk[g] = ks[g] >= 0 ? tab.b[pair_bucket0(xs[g], tab.mask)] : u64x2{kEmptySlot, kEmptySlot};
       uint32_t need2 = 0;
 #pragma unroll
-      for (int g = 0; g < kSegBatch; ++g) {
+      for (int g = 0; g < kSegProbe; ++g) {
         nv[g] = bucket_rank(bk[g], kk[g]);
         if (ks[g] >= 0 && nv[g] == kRankInf && bucket_flag(bk[g])) need2 |= 1u << g;
       }
       if (need2) {
 #pragma unroll
-        for (int g = 0; g < kSegBatch; ++g)
+        for (int g = 0; g < kSegProbe; ++g)
           if ((need2 >> g) & 1u) bk[g] = tab.b[pair_bucket1(xs[g], tab.mask)];
 #pragma unroll
-        for (int g = 0; g < kSegBatch; ++g)
+        for (int g = 0; g < kSegProbe; ++g)
           if ((need2 >> g) & 1u) nv[g] = bucket_rank(bk[g], kk[g]);
       }
 #pragma unroll
-      for (int g = 0; g < kSegBatch; ++g)
+      for (int g = 0; g < kSegProbe; ++g)
         if (ks[g] >= 0) R[base + ks[g]] = nv[g];
     }
     __syncthreads();
@@ -2113,7 +2116,7 @@ __device__ void rle_ranks(const RleView &V, int R, const RankTable &tab) {
 // at least 8 bytes per run on average; returns their number, or -1.
 // The bytes come 16 per lane per step (1 KiB per wave, all loads of a step in
 // flight together); a run starts where a byte differs from the one before.
-__device__ int rle_build(const RleView &V, const uint8_t *bytes, int64_t n) {
+__device__ __noinline__ int rle_build(const RleView &V, const uint8_t *bytes, int64_t n) {
   const int lane = lane_id();
   int R = 0;
   int32_t prev = -1;
@@ -2155,7 +2158,7 @@ __device__ int rle_build(const RleView &V, const uint8_t *bytes, int64_t n) {
 
 // Rounds on the R runs in V until no pair has a rank; returns the final
 // number of runs, or -1 if a round would leave more than kRleMax.
-__device__ int rle_merge(const RleView &V, int R, const RankTable &tab) {
+__device__ __noinline__ int rle_merge(const RleView &V, int R, const RankTable &tab) {
   const int lane = lane_id();
   rle_ranks(V, R, tab);
   for (;;) {
@@ -2252,7 +2255,7 @@ __device__ int rle_merge(const RleView &V, int R, const RankTable &tab) {
 }
 
 // The R runs in V written out as symbols to out[0 ..); returns their number.
-__device__ int64_t rle_expand(const RleView &V, int R, int32_t *out) {
+__device__ __noinline__ int64_t rle_expand(const RleView &V, int R, int32_t *out) {
   int64_t p = 0;
   for (int k = 0; k < R; ++k) {
     const int32_t x = V.sym[k], n = V.cnt[k];
@@ -2277,7 +2280,9 @@ struct LongGroupShared {
   LongShared L;
 };
 
-// Bucket 3 of the same groups: one wave per entry, in turn.  An entry made
+// Bucket 3 of the same groups: one wave per entry, in turn (each merge path
+// a function of its own, so that each is given its own registers and the
+// kernel's stay within 3 waves per SIMD).  An entry made
 // of few runs of one byte is merged on its runs; otherwise one of at most
 // kLdsLong bytes is merged in LDS (lds_merge) and a longer one in place in
 // the position-indexed gsym / grank (wg_merge), both with the window radius
