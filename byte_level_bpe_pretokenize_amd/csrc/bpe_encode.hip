@@ -14,8 +14,10 @@
 //   k_merge       (persistent) the merge loop for 2-8 byte entries and the
 //                 9-16 byte owners, one pre-token per lane in LDS columns.
 //   k_merge_wide  the same for the 17-32 byte owners.
-//   k_merge_long  longer pre-tokens, one wave each (runs of one byte on
-//                 their run lengths).
+//   k_merge_long  longer pre-tokens, one wave each: runs of one byte on
+//                 their run lengths; up to 2048 bytes in LDS, with each lane
+//                 owning a segment of the symbols (256 bytes on) or every
+//                 64th position; longer ones in global scratch.
 //   k_dupfill     token counts of the entries that took an owner's result.
 //   k_offsets     exclusive scan of the per-chunk token counts within blocks
 //                 of 1024 chunks; k_bscan the same over the blocks' counts.
@@ -1791,7 +1793,10 @@ __device__ __noinline__ int lds_merge(LongShared &L, int n, int D, const RankTab
 
 constexpr int kSegCap = 32;              // symbols a lane holds
 constexpr int kSegStride = kSegCap + 1;  // LDS words from one lane's segment to the next
-constexpr int kSegShare = 16;            // fewest symbols per lane when spread (if n allows)
+// fewest symbols per lane when spread (if n allows): at least the largest
+// radius, so that a spread leaves every segment long enough for its windows
+constexpr int kSegShare = 8;
+static_assert(kSegShare >= kRPad, "a spread segment holds a window's radius");
 constexpr int kSegFrom = 256;            // entries this long or longer take the segmented rounds
 
 __device__ __forceinline__ int seg_lanes(int n) { return min(MWG, max(1, n / kSegShare)); }
