@@ -1807,13 +1807,13 @@ __device__ __forceinline__ void seg_share(int n, int Ln, int lane, int &lo, int 
   len = (lane < Ln ? n * (lane + 1) / Ln : n) - lo;
 }
 
-// The positions of m's lowest kSegProbe set bits, lowest first (-1 where m
-// has fewer); m loses them.
 constexpr int kSegBatch = 8;  // symbols a lane loads together
 // probes in flight per lane: with 4, the kernel fits in 168 registers (3
 // waves per SIMD; LDS then allows 9 per CU); 8 took 243 (2 waves per SIMD)
 constexpr int kSegProbe = 4;
 
+// The positions of m's lowest kSegProbe set bits, lowest first (-1 where m
+// has fewer); m loses them.
 __device__ __forceinline__ void take_bits(uint32_t &m, int (&k)[kSegProbe]) {
 #pragma unroll
   for (int g = 0; g < kSegProbe; ++g) {
@@ -1872,8 +1872,9 @@ __device__ int seg_merge(LongShared &LS, const uint8_t *__restrict__ bytes, int 
     const int P = incl - len;  // global index of the segment's first symbol
     const int lenL = wave_shift_up1(len, 0);
     const int lenR = wave_shift_down1(len, 0);
-    // rank of pair k of this segment, k in [-D, len + D) (before the round):
-    // an index always inside the arrays, and whether the value counts
+    // rank of pair k of this segment, k >= -D (before the round): an index
+    // always inside the arrays, and whether the value counts (kRankInf past
+    // either end of the symbols)
     auto rank_at = [&](int k) -> int32_t {
       int idx;
       bool ok;
